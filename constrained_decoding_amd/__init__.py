@@ -1,0 +1,14 @@
+"""MI355X (gfx950) batched per-request sampling step.
+
+[B, V] logits + per-row temperature / top-k / top-p / min-p / penalties /
+sparse logit bias / grammar bitmask -> one token id and one logprob per row,
+in hand-written HIP kernels behind the C ABI of libcd_sampler.so
+(include/cd_sampler.h).  This package is the thin Python binding.
+"""
+from ._binding import (  # noqa: F401
+    DTYPE_BF16, DTYPE_F32, EXPORTS, FLAG_ALL_GREEDY, FLAG_ANY_GREEDY, FLAG_HAS_BIAS,
+    FLAG_NEED_MIN_P, FLAG_NEED_PENALTY, FLAG_NEED_TOP_K, FLAG_NEED_TOP_P, LIB_PATH,
+    STATUS_INVALID, STATUS_OK, STATUS_OVERFLOW, Batch, HostParams, PackedBatch, SamplerError,
+    Workspace, apply_bitmask, apply_transforms, bias_from_dict, csr, lib, pack_host, sample,
+    set_algo, strerror, time_next, version,
+)

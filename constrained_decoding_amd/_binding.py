@@ -1,0 +1,318 @@
+"""ctypes binding of libcd_sampler.so -- argument marshalling only.
+
+Every step of the sampling path runs in the library's HIP kernels; this
+module converts numpy arrays / torch tensors into the plain pointers and
+sizes of the C ABI (include/cd_sampler.h).  PyTorch supplies device memory and
+the current stream.  If the library is missing the import fails: there is no
+fallback implementation.
+"""
+import ctypes as ct
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libcd_sampler.so")
+
+OK, EINVAL, ERANGE, ENOSPC, EUNSUPPORTED, EHIP = 0, -1, -2, -3, -4, -5
+DTYPE_F32, DTYPE_BF16 = 0, 1
+STATUS_OK, STATUS_OVERFLOW, STATUS_INVALID = 0, 1, 2
+FLAG_ALL_GREEDY, FLAG_ANY_GREEDY = 1 << 0, 1 << 1
+FLAG_NEED_TOP_K, FLAG_NEED_TOP_P, FLAG_NEED_MIN_P = 1 << 2, 1 << 3, 1 << 4
+FLAG_NEED_PENALTY, FLAG_HAS_BIAS = 1 << 5, 1 << 6
+OPT_ALGO = 1
+
+EXPORTS = [
+    "sampler_strerror", "sampler_version", "sampler_params_bytes", "sampler_pack_params",
+    "sampler_pack_host", "sampler_apply_transforms", "sampler_apply_bitmask",
+    "sampler_workspace_bytes", "sampler_workspace_init", "sampler_sample",
+    "sampler_set_option", "sampler_time_next",
+]
+
+
+class HostParams(ct.Structure):
+    _fields_ = [
+        ("B", ct.c_int32), ("V", ct.c_int32),
+        ("temperature", ct.c_void_p), ("top_k", ct.c_void_p), ("top_p", ct.c_void_p),
+        ("min_p", ct.c_void_p), ("repetition_penalty", ct.c_void_p),
+        ("frequency_penalty", ct.c_void_p), ("presence_penalty", ct.c_void_p),
+        ("hist_indptr", ct.c_void_p), ("hist_ids", ct.c_void_p),
+        ("bias_indptr", ct.c_void_p), ("bias_ids", ct.c_void_p), ("bias_vals", ct.c_void_p),
+        ("seed", ct.c_void_p), ("offset", ct.c_void_p),
+    ]
+
+
+class Batch(ct.Structure):
+    _fields_ = [
+        ("B", ct.c_int32), ("V", ct.c_int32), ("flags", ct.c_uint32),
+        ("max_top_k", ct.c_int32), ("n_pen", ct.c_int64), ("n_bias", ct.c_int64),
+        ("d_rows", ct.c_void_p), ("d_pen", ct.c_void_p), ("d_bias", ct.c_void_p),
+        ("bytes", ct.c_size_t),
+    ]
+
+
+class SamplerError(RuntimeError):
+    def __init__(self, code, what):
+        self.code = code
+        super().__init__(f"{what}: {strerror(code)} ({code})")
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run __graft_entry__.build() or "
+                          "python constrained_decoding_amd/build.py")
+    lib = ct.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ct.c_void_p, ct.c_int32, ct.c_int64, ct.c_size_t
+    sig = {
+        "sampler_strerror": ([ct.c_int], ct.c_char_p),
+        "sampler_version": ([], ct.c_char_p),
+        "sampler_params_bytes": ([I32, I64, I64], SZ),
+        "sampler_pack_params": ([P, P, SZ, P, P, P], ct.c_int),
+        "sampler_pack_host": ([P, P, SZ, P], ct.c_int),
+        "sampler_apply_transforms": ([P, P, I64, P], ct.c_int),
+        "sampler_apply_bitmask": ([P, ct.c_int, I64, I32, I32, P, I64, P, P], ct.c_int),
+        "sampler_workspace_bytes": ([I32, I32], SZ),
+        "sampler_workspace_init": ([P, SZ, P], ct.c_int),
+        "sampler_sample": ([P, P, ct.c_int, I64, P, I64, P, P, P, P, P, SZ, P], ct.c_int),
+        "sampler_set_option": ([ct.c_int, I64], ct.c_int),
+        "sampler_time_next": ([ct.c_int, P, P], ct.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+lib = _load()
+
+
+def strerror(code: int) -> str:
+    return lib.sampler_strerror(int(code)).decode()
+
+
+def version() -> str:
+    return lib.sampler_version().decode()
+
+
+def _check(rc, what):
+    if rc != OK:
+        raise SamplerError(rc, what)
+
+
+def _arr(x, dtype, n=None):
+    if x is None:
+        return None
+    a = np.ascontiguousarray(np.asarray(x, dtype=dtype))
+    if n is not None and a.shape[0] != n:
+        raise ValueError(f"expected length {n}, got {a.shape[0]}")
+    return a
+
+
+def _p(a):
+    return None if a is None else a.ctypes.data
+
+
+def bias_from_dict(d):
+    """{token-id string or int: value} in insertion order -> (ids, values).
+    String keys are converted with int() ("1" and "01" both name token 1);
+    duplicates are kept in order and resolved by the pack (later wins)."""
+    ids = np.array([int(k) for k in d], dtype=np.int32)
+    vals = np.array([float(v) for v in d.values()], dtype=np.float32)
+    return ids, vals
+
+
+def csr(rows, dtype=np.int32):
+    """List of per-row sequences -> (indptr int64 [B+1], flat values)."""
+    lens = [0 if r is None else len(r) for r in rows]
+    indptr = np.zeros(len(rows) + 1, np.int64)
+    indptr[1:] = np.cumsum(lens)
+    flat = np.concatenate([np.asarray(r, dtype) for r in rows if r is not None and len(r)]) \
+        if indptr[-1] else np.zeros(0, dtype)
+    return indptr, flat
+
+
+class _HostArrays:
+    """Owns the contiguous numpy arrays a HostParams points into."""
+
+    def __init__(self, B, V, temperature, top_k=None, top_p=None, min_p=None,
+                 repetition_penalty=None, frequency_penalty=None, presence_penalty=None,
+                 hist_indptr=None, hist_ids=None, bias_indptr=None, bias_ids=None,
+                 bias_vals=None, seed=None, offset=None):
+        self.a = dict(
+            temperature=_arr(temperature, np.float32, B), top_k=_arr(top_k, np.int32, B),
+            top_p=_arr(top_p, np.float32, B), min_p=_arr(min_p, np.float32, B),
+            repetition_penalty=_arr(repetition_penalty, np.float32, B),
+            frequency_penalty=_arr(frequency_penalty, np.float32, B),
+            presence_penalty=_arr(presence_penalty, np.float32, B),
+            hist_indptr=_arr(hist_indptr, np.int64, None if hist_indptr is None else B + 1),
+            hist_ids=_arr(hist_ids, np.int32),
+            bias_indptr=_arr(bias_indptr, np.int64, None if bias_indptr is None else B + 1),
+            bias_ids=_arr(bias_ids, np.int32), bias_vals=_arr(bias_vals, np.float32),
+            seed=_arr(seed, np.uint64, B), offset=_arr(offset, np.uint64, B))
+        self.hp = HostParams(B=B, V=V, **{k: _p(v) for k, v in self.a.items()})
+        self.B, self.V = B, V
+        self.n_hist = 0 if self.a["hist_ids"] is None else self.a["hist_ids"].shape[0]
+        self.n_bias = 0 if self.a["bias_ids"] is None else self.a["bias_ids"].shape[0]
+
+    def bytes_bound(self):
+        return int(lib.sampler_params_bytes(self.B, self.n_hist, self.n_bias))
+
+
+def pack_host(B, V, temperature, **kw):
+    """Validate and pack on the host only (no HIP call).  Returns
+    (packed bytes as a uint8 array, Batch)."""
+    h = _HostArrays(B, V, temperature, **kw)
+    buf = np.zeros(max(h.bytes_bound(), 1), np.uint8)
+    out = Batch()
+    _check(lib.sampler_pack_host(ct.byref(h.hp), buf.ctypes.data, buf.nbytes, ct.byref(out)),
+           "sampler_pack_host")
+    return buf[:out.bytes], out
+
+
+def _stream_ptr(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+class _StagingRing:
+    """Pinned host buffers for the parameter copy.  A slot is reused only after
+    the event recorded behind its copy has completed, so a later pack never
+    overwrites bytes an earlier, still-queued copy has yet to read."""
+
+    def __init__(self, n=8):
+        self.slots = [None] * n   # (tensor, event)
+        self.i = 0
+
+    def acquire(self, nbytes):
+        import torch
+        k = self.i
+        self.i = (self.i + 1) % len(self.slots)
+        slot = self.slots[k]
+        if slot is not None:
+            slot[1].synchronize()
+        if slot is None or slot[0].numel() < nbytes:
+            buf = torch.empty(max(nbytes, 4096), dtype=torch.uint8, pin_memory=True)
+            slot = (buf, torch.cuda.Event())
+            self.slots[k] = slot
+        return slot
+
+
+_ring = None
+
+
+class PackedBatch:
+    """Device-side parameters of one step (sampler_pack_params)."""
+
+    def __init__(self, B, V, temperature, *, device="cuda", stream=None, **kw):
+        import torch
+        global _ring
+        if _ring is None:
+            _ring = _StagingRing()
+        h = _HostArrays(B, V, temperature, **kw)
+        nbytes = max(h.bytes_bound(), 64)
+        self.d_buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        staging, ev = _ring.acquire(nbytes)
+        self.batch = Batch()
+        s = torch.cuda.current_stream() if stream is None else stream
+        _check(lib.sampler_pack_params(ct.byref(h.hp), self.d_buf.data_ptr(), nbytes,
+                                       staging.data_ptr(), s.cuda_stream,
+                                       ct.byref(self.batch)), "sampler_pack_params")
+        ev.record(s)
+        self.B, self.V = B, V
+
+    @property
+    def flags(self):
+        return int(self.batch.flags)
+
+    @property
+    def max_top_k(self):
+        return int(self.batch.max_top_k)
+
+
+class Workspace:
+    """Device scratch of sampler_sample, zeroed once on creation."""
+
+    def __init__(self, B, V, *, device="cuda", stream=None):
+        import torch
+        n = int(lib.sampler_workspace_bytes(B, V))
+        if n == 0:
+            raise SamplerError(ERANGE, "sampler_workspace_bytes")
+        n = (n + 255) // 256 * 256
+        self.buf = torch.empty(n + 256, dtype=torch.uint8, device=device)
+        off = (-self.buf.data_ptr()) % 256
+        self.ptr = self.buf.data_ptr() + off
+        self.nbytes = n
+        _check(lib.sampler_workspace_init(self.ptr, n, _stream_ptr(stream)),
+               "sampler_workspace_init")
+        self.B, self.V = B, V
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.float32:
+        return DTYPE_F32
+    if t.dtype == torch.bfloat16:
+        return DTYPE_BF16
+    raise ValueError(f"logits must be float32 or bfloat16, got {t.dtype}")
+
+
+def apply_transforms(packed: PackedBatch, logits, stream=None):
+    """Penalties then bias, in place on float32 logits [B, ld]."""
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be 2-D with unit column stride")
+    if _dtype_code(logits) != DTYPE_F32:
+        raise SamplerError(EUNSUPPORTED, "sampler_apply_transforms (bf16)")
+    _check(lib.sampler_apply_transforms(ct.byref(packed.batch), logits.data_ptr(),
+                                        logits.stride(0), _stream_ptr(stream)),
+           "sampler_apply_transforms")
+
+
+def apply_bitmask(logits, bitmask, row_has_mask=None, stream=None):
+    """Disallowed tokens -> -inf, in place (float32 or bfloat16 logits)."""
+    B, V = logits.shape
+    _check(lib.sampler_apply_bitmask(
+        logits.data_ptr(), _dtype_code(logits), logits.stride(0), B, V, bitmask.data_ptr(),
+        bitmask.stride(0), None if row_has_mask is None else row_has_mask.data_ptr(),
+        _stream_ptr(stream)), "sampler_apply_bitmask")
+
+
+def sample(packed: PackedBatch, logits, *, bitmask=None, row_has_mask=None, workspace=None,
+           out=None, stream=None):
+    """The sampling step.  Returns (ids int32 [B], logprobs float32 [B],
+    status int32 [B]) as device tensors (``out`` may supply them)."""
+    import torch
+    B, V = logits.shape
+    if (B, V) != (packed.B, packed.V):
+        raise ValueError("logits shape does not match the packed batch")
+    if logits.stride(1) != 1:
+        raise ValueError("logits must have unit column stride")
+    if workspace is None:
+        workspace = Workspace(B, V, device=logits.device, stream=stream)
+    if out is None:
+        ids = torch.empty(B, dtype=torch.int32, device=logits.device)
+        lp = torch.empty(B, dtype=torch.float32, device=logits.device)
+        st = torch.empty(B, dtype=torch.int32, device=logits.device)
+    else:
+        ids, lp, st = out
+    _check(lib.sampler_sample(
+        ct.byref(packed.batch), logits.data_ptr(), _dtype_code(logits), logits.stride(0),
+        None if bitmask is None else bitmask.data_ptr(),
+        0 if bitmask is None else bitmask.stride(0),
+        None if row_has_mask is None else row_has_mask.data_ptr(),
+        ids.data_ptr(), None if lp is None else lp.data_ptr(),
+        None if st is None else st.data_ptr(), workspace.ptr, workspace.nbytes,
+        _stream_ptr(stream)), "sampler_sample")
+    return ids, lp, st
+
+
+def set_algo(algo: int):
+    """0: fast path (default); 1: row-serial exact path for every row."""
+    _check(lib.sampler_set_option(OPT_ALGO, int(algo)), "sampler_set_option")
+
+
+def time_next(kernel: int, start_event, stop_event):
+    """Record torch.cuda.Event pair around kernel `kernel` of the next sample()."""
+    _check(lib.sampler_time_next(int(kernel), start_event.cuda_event, stop_event.cuda_event),
+           "sampler_time_next")

@@ -1,0 +1,362 @@
+// device_common.h -- device helpers of libcd_sampler.so: order keys, Philox,
+// the race key, row loads with the fused bitmask, and workgroup reductions.
+// Wave size is 64 (CDNA); every workgroup size used here is a multiple of 64.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <climits>
+#include <cmath>
+#include <cstdint>
+
+#include "layout.h"
+
+namespace cds {
+
+#define CDS_NEG_INF (-__builtin_inff())
+#define CDS_POS_INF (__builtin_inff())
+
+// ---- order-preserving uint32 key of a float (larger key = larger value) ----
+__device__ __forceinline__ uint32_t okey(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float from_okey(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+// ---- Philox-4x32-10 --------------------------------------------------------
+// Salmon, Moraes, Dror, Shaw, "Parallel Random Numbers: As Easy as 1, 2, 3"
+// (SC'11), section 3.2: each round multiplies counter words 0 and 2 by the two
+// round multipliers; the high halves, xored with words 1 / 3 and the round key,
+// and the low halves form the next counter; the key advances by the Weyl
+// constants (golden ratio and sqrt(3) fraction bits) between rounds.
+__device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1) {
+#pragma unroll
+  for (int round = 0; round < 10; ++round) {
+    if (round) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
+    const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
+    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+  }
+  return c;
+}
+
+// ---- the race ----------------------------------------------------------------
+// Token t of a row draws x = word (t & 3) of Philox(counter = (t>>2, lo(off),
+// hi(off), 0), key = (lo(seed), hi(seed))), U = (2*(x>>9)+1) * 2^-24 (exact in
+// fp32), and its key is (s_t - m) - ln(-ln U) with s = z/T, m = max s.  The
+// largest key wins (lowest index on an exact tie); maximising s_t + Gumbel
+// noise draws t with probability proportional to exp(s_t) over the candidate
+// set, i.e. from the renormalised distribution.
+//
+// Bounds used for pruning: U lies in [2^-24, 1-2^-24], so -ln(-ln U) lies in
+// [-2.8094, 16.6355].  The row maximum is always a candidate, so the winning
+// key is >= -2.8094 and a token with s_t - m < -19.45 can never win.
+struct RaceCtx {
+  double Td;        // T as double
+  double m;         // zmax / T
+  float zmax;
+  float invT32;     // (float)(1 / T)
+  uint32_t k0, k1;  // Philox key
+  uint32_t off_lo, off_hi;
+};
+
+__device__ __forceinline__ RaceCtx make_race_ctx(const RowParams& rp, float zmax) {
+  RaceCtx c;
+  c.Td = (double)rp.temperature;
+  c.m = (double)zmax / c.Td;
+  c.zmax = zmax;
+  c.invT32 = (float)(1.0 / c.Td);
+  c.k0 = (uint32_t)rp.seed;
+  c.k1 = (uint32_t)(rp.seed >> 32);
+  c.off_lo = (uint32_t)rp.offset;
+  c.off_hi = (uint32_t)(rp.offset >> 32);
+  return c;
+}
+
+__device__ __forceinline__ uint4 race_block(const RaceCtx& c, int64_t t0) {
+  return philox4x32_10(make_uint4((uint32_t)(t0 >> 2), c.off_lo, c.off_hi, 0u), c.k0, c.k1);
+}
+
+// fp32 estimate of -ln(-ln U); |error| < 1e-5 (used only to prune).
+__device__ __forceinline__ float gumbel32(uint32_t x) {
+  const uint32_t j = x >> 9;
+  const uint32_t n = 2u * j + 1u;  // odd, < 2^24: exact in fp32
+  float e;
+  if (j >= (1u << 22)) {  // U > 1/2: -ln U = -log1p(-(1-U)), 1-U exact
+    const float d = (float)((1u << 24) - n) * 0x1p-24f;
+    e = -log1pf(-d);
+  } else {
+    e = -logf((float)n * 0x1p-24f);
+  }
+  return -logf(e);
+}
+
+// The exact key, in fp64 with the same operation order as the definition.
+__device__ __forceinline__ double race_key64(float z, const RaceCtx& c, uint32_t x) {
+  const double u = (double)(2u * (x >> 9) + 1u) * 0x1p-24;
+  const double s = (double)z / c.Td;
+  return (s - c.m) - log(-log(u));
+}
+
+struct Best {
+  double key;
+  int32_t t;
+  float key32;  // fp32 copy of key for pruning
+  float z;      // logit of the best token
+};
+
+__device__ __forceinline__ Best best_init() {
+  Best b;
+  b.key = CDS_NEG_INF;
+  b.t = INT_MAX;
+  b.key32 = CDS_NEG_INF;
+  b.z = CDS_NEG_INF;
+  return b;
+}
+
+__device__ __forceinline__ bool better(double k1, int t1, double k2, int t2) {
+  return k1 > k2 || (k1 == k2 && t1 < t2);
+}
+
+// Cheap test before drawing bits: can token value z still beat b?
+__device__ __forceinline__ bool race_hopeful(const Best& b, float z, const RaceCtx& c) {
+  const float sd = (z - c.zmax) * c.invT32;
+  return sd >= -19.5f && sd + 16.7f >= b.key32;
+}
+
+__device__ __forceinline__ void race_consider(Best& b, float z, int32_t t, uint32_t x,
+                                              const RaceCtx& c) {
+  const float sd = (z - c.zmax) * c.invT32;
+  if (sd < -19.5f || sd + 16.7f < b.key32) return;
+  const float k32 = sd + gumbel32(x);
+  if (k32 + 1e-3f < b.key32) return;
+  const double k64 = race_key64(z, c, x);
+  if (better(k64, t, b.key, b.t)) {
+    b.key = k64;
+    b.t = t;
+    b.key32 = (float)k64;
+    b.z = z;
+  }
+}
+
+// ---- loads -------------------------------------------------------------------
+struct RowView {
+  const float* f32;
+  const uint16_t* b16;
+  const int32_t* mrow;  // bitmask words of the row, or nullptr
+};
+
+// Four consecutive tokens t0..t0+3 (t0 % 4 == 0, t0 < hi).  Disallowed and
+// out-of-range tokens read as -inf; a NaN or +inf among allowed tokens sets
+// `nonfin` and reads as -inf; -0 is canonicalised to +0 so that value
+// comparisons and value order agree.
+template <bool BF16, bool VEC>
+__device__ __forceinline__ void load4(const RowView& rv, int64_t t0, int64_t hi, float x[4],
+                                      uint32_t& nonfin) {
+  if (VEC && t0 + 3 < hi) {
+    if (BF16) {
+      const uint2 u = *reinterpret_cast<const uint2*>(rv.b16 + t0);
+      x[0] = __uint_as_float(u.x << 16);
+      x[1] = __uint_as_float(u.x & 0xFFFF0000u);
+      x[2] = __uint_as_float(u.y << 16);
+      x[3] = __uint_as_float(u.y & 0xFFFF0000u);
+    } else {
+      const float4 f = *reinterpret_cast<const float4*>(rv.f32 + t0);
+      x[0] = f.x;
+      x[1] = f.y;
+      x[2] = f.z;
+      x[3] = f.w;
+    }
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t t = t0 + q;
+      if (t < hi)
+        x[q] = BF16 ? __uint_as_float((uint32_t)rv.b16[t] << 16) : rv.f32[t];
+      else
+        x[q] = CDS_NEG_INF;
+    }
+  }
+  uint32_t bits = 0xFu;
+  if (rv.mrow) bits = ((uint32_t)rv.mrow[t0 >> 5] >> (uint32_t)(t0 & 31)) & 0xFu;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    if (!((bits >> q) & 1u) || t0 + q >= hi) {
+      x[q] = CDS_NEG_INF;
+    } else {
+      if (x[q] != x[q] || x[q] == CDS_POS_INF) {
+        nonfin = 1u;
+        x[q] = CDS_NEG_INF;
+      }
+      x[q] = x[q] + 0.0f;
+    }
+  }
+}
+
+// ---- workgroup reductions (fixed trees: deterministic) -------------------------
+template <int NT>
+struct RedScratch {
+  double d[NT / 64];
+  float f[NT / 64];
+  int32_t i[NT / 64];
+  uint64_t u[NT / 64];
+};
+
+template <int NT>
+__device__ __forceinline__ double block_sum_f64(double v, RedScratch<NT>& s) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s.d[w] = v;
+  __syncthreads();
+  double tot = 0.0;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) tot += s.d[k];
+  return tot;
+}
+
+template <int NT>
+__device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, RedScratch<NT>& s) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s.u[w] = v;
+  __syncthreads();
+  uint64_t tot = 0;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) tot += s.u[k];
+  return tot;
+}
+
+template <int NT>
+__device__ __forceinline__ int32_t block_sum_i32(int32_t v, RedScratch<NT>& s) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s.i[w] = v;
+  __syncthreads();
+  int32_t tot = 0;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) tot += s.i[k];
+  return tot;
+}
+
+template <int NT>
+__device__ __forceinline__ uint32_t block_or_u32(uint32_t v, RedScratch<NT>& s) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, 64);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s.i[w] = (int32_t)v;
+  __syncthreads();
+  uint32_t tot = 0;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) tot |= (uint32_t)s.i[k];
+  return tot;
+}
+
+// max value, lowest index among equal maxima
+template <int NT>
+__device__ __forceinline__ void block_argmax(float& z, int32_t& t, RedScratch<NT>& s) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const float z2 = __shfl_xor(z, o, 64);
+    const int32_t t2 = __shfl_xor(t, o, 64);
+    if (z2 > z || (z2 == z && t2 < t)) {
+      z = z2;
+      t = t2;
+    }
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    s.f[w] = z;
+    s.i[w] = t;
+  }
+  __syncthreads();
+  z = s.f[0];
+  t = s.i[0];
+#pragma unroll
+  for (int k = 1; k < NT / 64; ++k)
+    if (s.f[k] > z || (s.f[k] == z && s.i[k] < t)) {
+      z = s.f[k];
+      t = s.i[k];
+    }
+}
+
+template <int NT>
+__device__ __forceinline__ void block_best(Best& b, RedScratch<NT>& s) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    const double k2 = __shfl_xor(b.key, o, 64);
+    const int32_t t2 = __shfl_xor(b.t, o, 64);
+    const float z2 = __shfl_xor(b.z, o, 64);
+    if (better(k2, t2, b.key, b.t)) {
+      b.key = k2;
+      b.t = t2;
+      b.z = z2;
+    }
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    s.d[w] = b.key;
+    s.i[w] = b.t;
+    s.f[w] = b.z;
+  }
+  __syncthreads();
+  b.key = s.d[0];
+  b.t = s.i[0];
+  b.z = s.f[0];
+#pragma unroll
+  for (int k = 1; k < NT / 64; ++k)
+    if (better(s.d[k], s.i[k], b.key, b.t)) {
+      b.key = s.d[k];
+      b.t = s.i[k];
+      b.z = s.f[k];
+    }
+  b.key32 = (float)b.key;
+}
+
+// Inclusive scan over n values held in LDS array `v` (in place): serial
+// within contiguous per-thread chunks, then wave shuffles and per-wave totals
+// -- a fixed combination order, so results are bit-reproducible.
+// `wtot` is LDS scratch of NT/64 elements.  All NT threads must call it.
+template <int NT, typename T, typename Op>
+__device__ void block_scan_inplace(T* v, int n, T ident, Op op, T* wtot) {
+  const int chunk = (n + NT - 1) / NT;
+  const int lo = min((int)threadIdx.x * chunk, n);
+  const int hi = min(lo + chunk, n);
+  T acc = ident;
+  for (int i = lo; i < hi; ++i) acc = op(acc, v[i]);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  T s = acc;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const T y = __shfl_up(s, o, 64);
+    if (lane >= o) s = op(y, s);
+  }
+  T ex = __shfl_up(s, 1, 64);
+  if (lane == 0) ex = ident;
+  __syncthreads();
+  if (lane == 63) wtot[w] = s;
+  __syncthreads();
+  T run = ident;
+  for (int k = 0; k < w; ++k) run = op(run, wtot[k]);
+  run = op(run, ex);
+  for (int i = lo; i < hi; ++i) {
+    run = op(run, v[i]);
+    v[i] = run;
+  }
+  __syncthreads();
+}
+
+}  // namespace cds

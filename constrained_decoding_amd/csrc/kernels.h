@@ -1,0 +1,49 @@
+// kernels.h -- launch interface between the host ABI code (sampler_abi.cpp)
+// and the HIP kernels (kernels.hip) of libcd_sampler.so.
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "layout.h"
+
+namespace cds {
+
+struct SampleArgs {
+  const RowParams* rows;
+  const void* logits;
+  int64_t ld;
+  int32_t B, V;
+  const int32_t* mask;  // bitmask words or nullptr
+  int64_t mask_ld;
+  const uint8_t* row_has_mask;
+  int32_t* out_ids;
+  float* out_lp;
+  int32_t* out_st;
+  RowSync* sync;
+  Plan* plans;
+  SliceHead* heads;
+  uint32_t* hcnt;   // [B*P][NBINS]
+  uint64_t* hmass;  // [B*P][NBINS]
+  SliceBest* bests; // [B*P]
+  uint64_t* ulist;  // [B][UCAP]
+  int32_t P;
+  int64_t S;
+};
+
+struct KernelEvents {
+  hipEvent_t start[2];
+  hipEvent_t stop[2];
+};
+
+hipError_t launch_transforms(const RowParams* rows, const PenEntry* pen, const BiasEntry* bias,
+                             float* logits, int64_t ld, int32_t B, hipStream_t stream);
+hipError_t launch_bitmask(void* logits, bool bf16, int64_t ld, int32_t B, int32_t V,
+                          const int32_t* mask, int64_t mask_ld, const uint8_t* row_has_mask,
+                          hipStream_t stream);
+hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
+// algo 0: scan -> race -> finish (fast path); algo 1: row-serial exact path.
+hipError_t launch_sample(const SampleArgs& a, bool bf16, bool vec, int algo, bool need_race,
+                         const KernelEvents* ev, hipStream_t stream);
+
+}  // namespace cds

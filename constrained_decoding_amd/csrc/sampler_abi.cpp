@@ -1,0 +1,361 @@
+// sampler_abi.cpp -- the C ABI of libcd_sampler.so (declared and documented in
+// include/cd_sampler.h): parameter validation and packing on the host, and the
+// kernel launches of the sampling step.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <atomic>
+#include <cmath>
+#include <cstring>
+#include <utility>
+#include <vector>
+
+#include "cd_sampler.h"
+#include "kernels.h"
+#include "layout.h"
+
+using namespace cds;
+
+namespace {
+
+constexpr int32_t kMaxV = 1 << 24;
+constexpr int32_t kMaxB = kMaxRows;
+
+std::atomic<int> g_algo{0};
+// one-shot kernel timing hook (see sampler_time_next)
+std::atomic<void*> g_ev_start[2] = {{nullptr}, {nullptr}};
+std::atomic<void*> g_ev_stop[2] = {{nullptr}, {nullptr}};
+
+inline bool finite_f(float x) { return std::isfinite(x); }
+
+size_t params_bytes_exact(int32_t B, int64_t n_pen, int64_t n_bias) {
+  return sizeof(RowParams) * (size_t)B + sizeof(PenEntry) * (size_t)n_pen +
+         sizeof(BiasEntry) * (size_t)n_bias;
+}
+
+// Validate and pack into `out_buf` (host memory).  Returns a SAMPLER_* code.
+int pack_into(const sampler_host_params* h, std::vector<unsigned char>& out_buf,
+              sampler_batch* out) {
+  if (!h || !out) return SAMPLER_EINVAL;
+  const int32_t B = h->B, V = h->V;
+  if (B <= 0 || V <= 0) return SAMPLER_EINVAL;
+  if (B > kMaxB || V > kMaxV) return SAMPLER_ERANGE;
+  if (!h->temperature) return SAMPLER_EINVAL;
+  if ((h->hist_indptr == nullptr) != (h->hist_ids == nullptr)) return SAMPLER_EINVAL;
+  if ((h->bias_indptr == nullptr) != (h->bias_ids == nullptr) ||
+      (h->bias_ids == nullptr) != (h->bias_vals == nullptr))
+    return SAMPLER_EINVAL;
+
+  // CSR structure
+  if (h->hist_indptr) {
+    if (h->hist_indptr[0] != 0) return SAMPLER_EINVAL;
+    for (int32_t r = 0; r < B; ++r)
+      if (h->hist_indptr[r + 1] < h->hist_indptr[r]) return SAMPLER_EINVAL;
+    for (int64_t i = 0; i < h->hist_indptr[B]; ++i)
+      if (h->hist_ids[i] < 0 || h->hist_ids[i] >= V) return SAMPLER_EINVAL;
+  }
+  if (h->bias_indptr) {
+    if (h->bias_indptr[0] != 0) return SAMPLER_EINVAL;
+    for (int32_t r = 0; r < B; ++r)
+      if (h->bias_indptr[r + 1] < h->bias_indptr[r]) return SAMPLER_EINVAL;
+    for (int64_t i = 0; i < h->bias_indptr[B]; ++i) {
+      if (h->bias_ids[i] < 0 || h->bias_ids[i] >= V) return SAMPLER_EINVAL;
+      const float v = h->bias_vals[i];
+      if (std::isnan(v) || v == INFINITY) return SAMPLER_EINVAL;
+    }
+  }
+
+  std::vector<RowParams> rows((size_t)B);
+  std::vector<PenEntry> pen;
+  std::vector<BiasEntry> bias;
+  uint32_t flags = SAMPLER_FLAG_ALL_GREEDY;
+  bool all_nongreedy_have_k = true;
+  int32_t max_k = 0;
+  std::vector<int32_t> scratch_ids;
+  std::vector<std::pair<int32_t, int64_t>> scratch_bias;
+
+  for (int32_t r = 0; r < B; ++r) {
+    RowParams rp;
+    std::memset(&rp, 0, sizeof rp);
+    const float T = h->temperature[r];
+    if (!finite_f(T) || T < 0.0f) return SAMPLER_EINVAL;
+    const int32_t k = h->top_k ? h->top_k[r] : 0;
+    const float p = h->top_p ? h->top_p[r] : 1.0f;
+    const float mp = h->min_p ? h->min_p[r] : 0.0f;
+    const float rep = h->repetition_penalty ? h->repetition_penalty[r] : 1.0f;
+    const float fr = h->frequency_penalty ? h->frequency_penalty[r] : 0.0f;
+    const float pr = h->presence_penalty ? h->presence_penalty[r] : 0.0f;
+    if (!(p > 0.0f && p <= 1.0f)) return SAMPLER_EINVAL;   // also rejects NaN
+    if (!(mp >= 0.0f && mp <= 1.0f)) return SAMPLER_EINVAL;
+    if (!finite_f(rep) || !(rep > 0.0f)) return SAMPLER_EINVAL;
+    if (!finite_f(fr) || !finite_f(pr)) return SAMPLER_EINVAL;
+
+    rp.temperature = T;
+    rp.top_p = p;
+    rp.min_p = mp;
+    rp.rep = rep;
+    rp.freq = fr;
+    rp.pres = pr;
+    rp.seed = h->seed ? h->seed[r] : 0ull;
+    rp.offset = h->offset ? h->offset[r] : (uint64_t)r;
+    const bool greedy = (T < 1e-5f) || (k == 1);
+    if (greedy) {
+      rp.flags |= ROW_GREEDY;
+      flags |= SAMPLER_FLAG_ANY_GREEDY;
+    } else {
+      flags &= ~SAMPLER_FLAG_ALL_GREEDY;
+      if (k > 1 && k < V) {
+        rp.flags |= ROW_TOPK;
+        rp.top_k = k;
+        flags |= SAMPLER_FLAG_NEED_TOP_K;
+        max_k = std::max(max_k, k);
+      } else {
+        all_nongreedy_have_k = false;
+      }
+      if (p < 1.0f) {
+        rp.flags |= ROW_TOPP;
+        flags |= SAMPLER_FLAG_NEED_TOP_P;
+      }
+      if (mp > 0.0f) {
+        rp.flags |= ROW_MINP;
+        flags |= SAMPLER_FLAG_NEED_MIN_P;
+      }
+    }
+
+    // penalties: (token, count) from the row's history
+    rp.pen_lo = rp.pen_hi = (int32_t)pen.size();
+    const bool pen_active = (rep != 1.0f) || (fr != 0.0f) || (pr != 0.0f);
+    if (h->hist_indptr && pen_active) {
+      const int64_t lo = h->hist_indptr[r], hi = h->hist_indptr[r + 1];
+      if (hi > lo) {
+        scratch_ids.assign(h->hist_ids + lo, h->hist_ids + hi);
+        std::sort(scratch_ids.begin(), scratch_ids.end());
+        for (size_t i = 0; i < scratch_ids.size();) {
+          size_t j = i;
+          while (j < scratch_ids.size() && scratch_ids[j] == scratch_ids[i]) ++j;
+          pen.push_back(PenEntry{scratch_ids[i], (int32_t)(j - i)});
+          i = j;
+        }
+        rp.pen_hi = (int32_t)pen.size();
+        rp.flags |= ROW_PEN;
+        flags |= SAMPLER_FLAG_NEED_PENALTY;
+      }
+    }
+    // bias: duplicates of a token keep the later entry
+    rp.bias_lo = rp.bias_hi = (int32_t)bias.size();
+    if (h->bias_indptr) {
+      const int64_t lo = h->bias_indptr[r], hi = h->bias_indptr[r + 1];
+      if (hi > lo) {
+        scratch_bias.clear();
+        for (int64_t i = lo; i < hi; ++i) scratch_bias.emplace_back(h->bias_ids[i], i);
+        std::sort(scratch_bias.begin(), scratch_bias.end());
+        for (size_t i = 0; i < scratch_bias.size(); ++i) {
+          if (i + 1 < scratch_bias.size() && scratch_bias[i + 1].first == scratch_bias[i].first)
+            continue;  // a later duplicate follows
+          bias.push_back(BiasEntry{scratch_bias[i].first, h->bias_vals[scratch_bias[i].second]});
+        }
+        rp.bias_hi = (int32_t)bias.size();
+        rp.flags |= ROW_BIAS;
+        flags |= SAMPLER_FLAG_HAS_BIAS;
+      }
+    }
+    rows[(size_t)r] = rp;
+  }
+  if (pen.size() > (size_t)INT32_MAX || bias.size() > (size_t)INT32_MAX) return SAMPLER_ERANGE;
+
+  const size_t bytes = params_bytes_exact(B, (int64_t)pen.size(), (int64_t)bias.size());
+  out_buf.resize(bytes);
+  unsigned char* p = out_buf.data();
+  std::memcpy(p, rows.data(), sizeof(RowParams) * rows.size());
+  std::memcpy(p + sizeof(RowParams) * (size_t)B, pen.data(), sizeof(PenEntry) * pen.size());
+  std::memcpy(p + sizeof(RowParams) * (size_t)B + sizeof(PenEntry) * pen.size(), bias.data(),
+              sizeof(BiasEntry) * bias.size());
+
+  std::memset(out, 0, sizeof *out);
+  out->B = B;
+  out->V = V;
+  out->flags = flags;
+  out->max_top_k = ((flags & SAMPLER_FLAG_ALL_GREEDY) || !all_nongreedy_have_k) ? 0 : max_k;
+  out->n_pen = (int64_t)pen.size();
+  out->n_bias = (int64_t)bias.size();
+  out->bytes = bytes;
+  return SAMPLER_OK;
+}
+
+void set_pointers(sampler_batch* out, const void* base) {
+  const unsigned char* b = static_cast<const unsigned char*>(base);
+  out->d_rows = b;
+  out->d_pen = b + sizeof(RowParams) * (size_t)out->B;
+  out->d_bias = b + sizeof(RowParams) * (size_t)out->B + sizeof(PenEntry) * (size_t)out->n_pen;
+}
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+}  // namespace
+
+extern "C" {
+
+const char* sampler_strerror(int code) {
+  switch (code) {
+    case SAMPLER_OK: return "ok";
+    case SAMPLER_EINVAL: return "invalid argument or parameter value";
+    case SAMPLER_ERANGE: return "size outside the supported range";
+    case SAMPLER_ENOSPC: return "buffer or workspace too small";
+    case SAMPLER_EUNSUPPORTED: return "unsupported request";
+    case SAMPLER_EHIP: return "HIP runtime error";
+    default: return "unknown error";
+  }
+}
+
+const char* sampler_version(void) { return "cd_sampler 0.1 (gfx950)"; }
+
+size_t sampler_params_bytes(int32_t B, int64_t n_hist, int64_t n_bias) {
+  if (B < 0 || n_hist < 0 || n_bias < 0) return 0;
+  return params_bytes_exact(B, n_hist, n_bias);
+}
+
+int sampler_pack_host(const sampler_host_params* h, void* host_buf, size_t bytes,
+                      sampler_batch* out) {
+  std::vector<unsigned char> buf;
+  sampler_batch tmp;
+  const int rc = pack_into(h, buf, &tmp);
+  if (rc != SAMPLER_OK) return rc;
+  if (!host_buf || bytes < buf.size()) return SAMPLER_ENOSPC;
+  std::memcpy(host_buf, buf.data(), buf.size());
+  set_pointers(&tmp, host_buf);
+  *out = tmp;
+  return SAMPLER_OK;
+}
+
+int sampler_pack_params(const sampler_host_params* h, void* d_buf, size_t d_bytes,
+                        void* h_staging, void* stream, sampler_batch* out) {
+  std::vector<unsigned char> buf;
+  sampler_batch tmp;
+  const int rc = pack_into(h, buf, &tmp);
+  if (rc != SAMPLER_OK) return rc;
+  if (!d_buf || d_bytes < buf.size()) return SAMPLER_ENOSPC;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (h_staging) {
+    std::memcpy(h_staging, buf.data(), buf.size());
+    if (hipMemcpyAsync(d_buf, h_staging, buf.size(), hipMemcpyHostToDevice, s) != hipSuccess)
+      return SAMPLER_EHIP;
+  } else {
+    if (hipMemcpyAsync(d_buf, buf.data(), buf.size(), hipMemcpyHostToDevice, s) != hipSuccess)
+      return SAMPLER_EHIP;
+    if (hipStreamSynchronize(s) != hipSuccess) return SAMPLER_EHIP;
+  }
+  set_pointers(&tmp, d_buf);
+  *out = tmp;
+  return SAMPLER_OK;
+}
+
+int sampler_apply_transforms(const sampler_batch* b, float* logits, int64_t ld, void* stream) {
+  if (!b || !logits || ld < b->V || b->B <= 0) return SAMPLER_EINVAL;
+  if (!aligned(logits, 4)) return SAMPLER_EINVAL;
+  if (!(b->flags & (SAMPLER_FLAG_NEED_PENALTY | SAMPLER_FLAG_HAS_BIAS))) return SAMPLER_OK;
+  const hipError_t e = launch_transforms(
+      static_cast<const RowParams*>(b->d_rows), static_cast<const PenEntry*>(b->d_pen),
+      static_cast<const BiasEntry*>(b->d_bias), logits, ld, b->B,
+      static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SAMPLER_OK : SAMPLER_EHIP;
+}
+
+int sampler_apply_bitmask(void* logits, int dtype, int64_t ld, int32_t B, int32_t V,
+                          const int32_t* bitmask, int64_t mask_ld, const uint8_t* row_has_mask,
+                          void* stream) {
+  if (!logits || !bitmask || B <= 0 || V <= 0 || ld < V) return SAMPLER_EINVAL;
+  if (dtype != SAMPLER_DTYPE_F32 && dtype != SAMPLER_DTYPE_BF16) return SAMPLER_EINVAL;
+  if (B > kMaxB || V > kMaxV) return SAMPLER_ERANGE;
+  if (mask_ld < ((int64_t)V + 31) / 32) return SAMPLER_EINVAL;
+  const hipError_t e = launch_bitmask(logits, dtype == SAMPLER_DTYPE_BF16, ld, B, V, bitmask,
+                                      mask_ld, row_has_mask, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SAMPLER_OK : SAMPLER_EHIP;
+}
+
+size_t sampler_workspace_bytes(int32_t B, int32_t V) {
+  if (B <= 0 || V <= 0 || B > kMaxB || V > kMaxV) return 0;
+  return workspace_layout(B, V).total;
+}
+
+int sampler_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
+  if (!workspace || ws_bytes % 4 != 0) return SAMPLER_EINVAL;
+  const hipError_t e = launch_fill_zero(workspace, ws_bytes, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SAMPLER_OK : SAMPLER_EHIP;
+}
+
+int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_t ld,
+                   const int32_t* bitmask, int64_t mask_ld, const uint8_t* row_has_mask,
+                   int32_t* out_ids, float* out_logprobs, int32_t* out_status, void* workspace,
+                   size_t ws_bytes, void* stream) {
+  if (!b || !logits || !out_ids || !b->d_rows) return SAMPLER_EINVAL;
+  const int32_t B = b->B, V = b->V;
+  if (B <= 0 || V <= 0 || ld < V) return SAMPLER_EINVAL;
+  if (B > kMaxB || V > kMaxV) return SAMPLER_ERANGE;
+  if (dtype != SAMPLER_DTYPE_F32 && dtype != SAMPLER_DTYPE_BF16) return SAMPLER_EINVAL;
+  const bool bf16 = dtype == SAMPLER_DTYPE_BF16;
+  if (!aligned(logits, bf16 ? 2 : 4)) return SAMPLER_EINVAL;
+  if (bitmask && mask_ld < ((int64_t)V + 31) / 32) return SAMPLER_EINVAL;
+  const WorkspaceLayout L = workspace_layout(B, V);
+  if (!workspace || ws_bytes < L.total) return SAMPLER_ENOSPC;
+  if (!aligned(workspace, 256)) return SAMPLER_EINVAL;
+
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  SampleArgs a;
+  a.rows = static_cast<const RowParams*>(b->d_rows);
+  a.logits = logits;
+  a.ld = ld;
+  a.B = B;
+  a.V = V;
+  a.mask = bitmask;
+  a.mask_ld = mask_ld;
+  a.row_has_mask = row_has_mask;
+  a.out_ids = out_ids;
+  a.out_lp = out_logprobs;
+  a.out_st = out_status;
+  a.sync = reinterpret_cast<RowSync*>(ws + L.sync_off);
+  a.plans = reinterpret_cast<Plan*>(ws + L.plan_off);
+  a.heads = reinterpret_cast<SliceHead*>(ws + L.head_off);
+  a.hcnt = reinterpret_cast<uint32_t*>(ws + L.hist_off);
+  a.hmass = reinterpret_cast<uint64_t*>(ws + L.hist_off +
+                                        sizeof(uint32_t) * NBINS * (size_t)B * L.P);
+  a.bests = reinterpret_cast<SliceBest*>(ws + L.best_off);
+  a.ulist = reinterpret_cast<uint64_t*>(ws + L.ulist_off);
+  a.P = L.P;
+  a.S = L.S;
+
+  // 16-byte vector loads need every row start (and the base) 16-byte aligned
+  const size_t elem = bf16 ? 2 : 4;
+  const bool vec = aligned(logits, 4 * elem) && ((ld * (int64_t)elem) % (4 * (int64_t)elem) == 0);
+  int algo = g_algo.load();
+  if (L.S > 16384) algo = 1;  // slices beyond the register-resident size
+
+  KernelEvents ev;
+  bool have_ev = false;
+  for (int k = 0; k < 2; ++k) {
+    ev.start[k] = static_cast<hipEvent_t>(g_ev_start[k].exchange(nullptr));
+    ev.stop[k] = static_cast<hipEvent_t>(g_ev_stop[k].exchange(nullptr));
+    have_ev = have_ev || ev.start[k] || ev.stop[k];
+  }
+  const bool need_race = !(b->flags & SAMPLER_FLAG_ALL_GREEDY);
+  const hipError_t e = launch_sample(a, bf16, vec, algo, need_race, have_ev ? &ev : nullptr,
+                                     static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SAMPLER_OK : SAMPLER_EHIP;
+}
+
+int sampler_set_option(int option, int64_t value) {
+  if (option == SAMPLER_OPT_ALGO) {
+    if (value != 0 && value != 1) return SAMPLER_EINVAL;
+    g_algo.store((int)value);
+    return SAMPLER_OK;
+  }
+  return SAMPLER_EINVAL;
+}
+
+int sampler_time_next(int kernel, void* start_event, void* stop_event) {
+  if (kernel < 0 || kernel > 1) return SAMPLER_EINVAL;
+  g_ev_start[kernel].store(start_event);
+  g_ev_stop[kernel].store(stop_event);
+  return SAMPLER_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,257 @@
+/*
+ * cd_sampler.h -- C ABI of libcd_sampler.so, the MI355X (gfx950) batched
+ * per-request sampling step: [B, V] logits + per-row parameters -> one token
+ * id and one logprob per row.
+ *
+ * Sources, cited by page title and section:
+ *   [SGL] "SGLang 源码完全拆解(十): Sampling、Grammar 与结构化输出"
+ *         (pinghaoyang.com.cn)
+ *   [VLP] vLLM design document "Logits Processors" (Chinese translation)
+ *   [SO]  "04 · 结构化输出: 在采样器上强制合法"
+ *   [GLM] "GLM-5.3 推理全链路(七): 输出侧的最后一公里" (pinghaoyang.com.cn)
+ *   [PHX] Salmon et al., "Parallel Random Numbers: As Easy as 1, 2, 3", SC'11
+ *
+ * Pipeline (order fixed by [SGL] "惩罚项的顺序语义" and [GLM] "采样"):
+ *   1. sampler_pack_params      host: validate, batch flags, dedup, CSR, H2D
+ *   2. sampler_apply_transforms penalties then logit bias, in place (fp32)
+ *   3. sampler_apply_bitmask    grammar bitmask -> -inf, in place (optional:
+ *                               sampler_sample can take the mask fused)
+ *   4. sampler_sample           greedy rows: argmax; other rows: temperature,
+ *                               min-p, top-k, top-p, seeded exponential race
+ *
+ * Conventions
+ *   - Every call returns int: SAMPLER_OK (0) or a negative SAMPLER_E* code;
+ *     sampler_strerror() describes it.  Nothing throws across the ABI.
+ *   - "dev" pointers are device memory, "host" pointers host memory.  All
+ *     device memory is allocated and owned by the caller; the library keeps
+ *     no device allocation and no mutable global state (except the optional
+ *     one-shot timing hook below), so calls on different streams and
+ *     workspaces may run concurrently.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     No call synchronises the stream, except sampler_pack_params without a
+ *     staging buffer (documented there).  Device inputs must stay alive and
+ *     unmodified until the stream reaches the call.
+ *   - A call that returns an error has launched nothing and written nothing.
+ *   - Data-dependent failures never return an error: they come back per row
+ *     in out_status (OK=0 < OVERFLOW=1 < INVALID=2, ordered by severity as
+ *     [SGL] "LogitsProcessorOutput" orders its mask statuses).
+ */
+#ifndef CD_SAMPLER_H
+#define CD_SAMPLER_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- return codes ------------------------------------------------------ */
+#define SAMPLER_OK 0
+#define SAMPLER_EINVAL (-1)       /* invalid argument or parameter value     */
+#define SAMPLER_ERANGE (-2)       /* size outside the supported range        */
+#define SAMPLER_ENOSPC (-3)       /* caller buffer or workspace too small    */
+#define SAMPLER_EUNSUPPORTED (-4) /* valid request the library does not do  */
+#define SAMPLER_EHIP (-5)         /* a HIP runtime call failed               */
+
+/* ---- dtypes of the logits ----------------------------------------------- */
+#define SAMPLER_DTYPE_F32 0
+#define SAMPLER_DTYPE_BF16 1 /* upcast exactly (bits << 16) on load; [GLM]
+                                "从最后一层 hidden 到 token id": sampling runs
+                                on fp32 values                              */
+
+/* ---- per-row output status ---------------------------------------------- */
+#define SAMPLER_STATUS_OK 0
+#define SAMPLER_STATUS_OVERFLOW 1 /* a NaN or +inf among the allowed logits:
+                                     id = -1, logprob = NaN                  */
+#define SAMPLER_STATUS_INVALID 2  /* no finite allowed logit (e.g. the mask
+                                     allows nothing): id = -1, logprob = -inf
+                                     (takes precedence over OVERFLOW)        */
+
+/* ---- batch flags (sampler_batch.flags), computed by sampler_pack_params --
+ * Host-side booleans that let whole kernels be skipped ([SGL] "字段分组":
+ * is_all_greedy / need_top_k_sampling / ...; [VLP] "将 Logits Processors
+ * 应用于模型输出的 Logits": argmax-invariant work skipped for all-greedy
+ * batches).  NEED_* are evaluated over the non-greedy rows only.          */
+#define SAMPLER_FLAG_ALL_GREEDY (1u << 0)
+#define SAMPLER_FLAG_ANY_GREEDY (1u << 1)
+#define SAMPLER_FLAG_NEED_TOP_K (1u << 2)
+#define SAMPLER_FLAG_NEED_TOP_P (1u << 3)
+#define SAMPLER_FLAG_NEED_MIN_P (1u << 4)
+#define SAMPLER_FLAG_NEED_PENALTY (1u << 5)
+#define SAMPLER_FLAG_HAS_BIAS (1u << 6)
+
+/* ---- host-side per-request parameters ------------------------------------
+ * All arrays are host memory, [B] unless noted; NULL selects the default.
+ *   temperature  required. Row is greedy if temperature < 1e-5 ([GLM] "采样":
+ *                the sampling epsilon) or top_k == 1 ([SGL] "字段分组":
+ *                top_k <= 1 rows are argmax; top_k <= 0 here means "off").
+ *                Must be finite and >= 0.
+ *   top_k        int32; <= 0 or >= V: off (the pages' "-1 / whole vocab").
+ *   top_p        (0, 1]; 1: off.                     default 1
+ *   min_p        [0, 1]; 0: off.                     default 0
+ *   repetition_penalty  > 0, finite; 1: off.         default 1
+ *   frequency_penalty   finite; 0: off.              default 0
+ *   presence_penalty    finite; 0: off.              default 0
+ *   hist_indptr  int64 [B+1], hist_ids int32: each row's generated-token
+ *                history (CSR); counts are taken from it for the
+ *                frequency / presence / repetition penalties.  NULL: none.
+ *   bias_indptr  int64 [B+1], bias_ids int32, bias_vals float: sparse
+ *                logit bias (CSR).  Duplicate ids in a row: the later entry
+ *                wins ([SGL] "logit_bias 为什么用三元组构造").  Values may be
+ *                -inf (ban a token) but not NaN or +inf.  NULL: none.
+ *   seed         uint64: Philox key of the row's draw.      default 0
+ *   offset       uint64: Philox counter words 1-2 of the row's draw, e.g.
+ *                the decode position ([SGL] "调用点": positions seed the
+ *                draw, so a request's stream does not depend on the batch).
+ *                default: the row index.
+ * -------------------------------------------------------------------------- */
+typedef struct sampler_host_params {
+  int32_t B;
+  int32_t V;
+  const float *temperature;
+  const int32_t *top_k;
+  const float *top_p;
+  const float *min_p;
+  const float *repetition_penalty;
+  const float *frequency_penalty;
+  const float *presence_penalty;
+  const int64_t *hist_indptr;
+  const int32_t *hist_ids;
+  const int64_t *bias_indptr;
+  const int32_t *bias_ids;
+  const float *bias_vals;
+  const uint64_t *seed;
+  const uint64_t *offset;
+} sampler_host_params;
+
+/* ---- packed batch descriptor (plain data, returned by value) ------------- */
+typedef struct sampler_batch {
+  int32_t B;
+  int32_t V;
+  uint32_t flags;       /* SAMPLER_FLAG_*                                      */
+  int32_t max_top_k;    /* max top_k over non-greedy rows if every one of them
+                           has 1 < top_k < V, else 0 ([SGL] "max_top_k")      */
+  int64_t n_pen;        /* packed (token, count) penalty entries             */
+  int64_t n_bias;       /* packed (token, value) bias entries after dedup    */
+  const void *d_rows;   /* dev: per-row records inside the caller's d_buf    */
+  const void *d_pen;    /* dev: penalty entries inside d_buf                 */
+  const void *d_bias;   /* dev: bias entries inside d_buf                    */
+  size_t bytes;         /* bytes of d_buf in use                             */
+} sampler_batch;
+
+/* Message for a SAMPLER_* return code (static storage). */
+const char *sampler_strerror(int code);
+
+/* Library version string (static storage). */
+const char *sampler_version(void);
+
+/* Upper bound of the device bytes sampler_pack_params needs for B rows,
+ * n_hist history ids and n_bias bias entries in total. */
+size_t sampler_params_bytes(int32_t B, int64_t n_hist, int64_t n_bias);
+
+/* Validate `h`, compute the batch flags and max_top_k, count each row's
+ * history into (token, count) entries, deduplicate the bias, and copy the
+ * packed block to d_buf (dev, >= sampler_params_bytes(...) bytes) on
+ * `stream`.  h_staging: pinned host memory of >= the same size used as the
+ * copy source (it must stay untouched until the copy has run), or NULL:
+ * then the call copies from a temporary host buffer and synchronises
+ * `stream` before returning.  Validation follows the fail-fast rule of
+ * [SGL] "后端分支" and vLLM's validate_params ([VLP] "Logits Processor 编程
+ * 模型"): any invalid value -> SAMPLER_EINVAL and nothing is copied.
+ * d_bytes too small -> SAMPLER_ENOSPC.  On success *out describes the batch;
+ * its device pointers point into d_buf. */
+int sampler_pack_params(const sampler_host_params *h, void *d_buf,
+                        size_t d_bytes, void *h_staging, void *stream,
+                        sampler_batch *out);
+
+/* Host-only variant for inspection and CPU tests: packs into `host_buf`
+ * (host memory, >= sampler_params_bytes(...)) with the same validation;
+ * out->d_* then point into host_buf.  Makes no HIP call. */
+int sampler_pack_host(const sampler_host_params *h, void *host_buf,
+                      size_t bytes, sampler_batch *out);
+
+/* Pre-grammar penalties and post-grammar bias, in place on fp32 logits
+ * (dev, row stride `ld` >= V elements, 4-byte aligned).  Per penalised
+ * token with history count c > 0, in fp32 without contraction:
+ *   z -= frequency*c + presence;  then if repetition != 1:
+ *   z = z > 0 ? z / repetition : z * repetition
+ * ([SGL] "惩罚项的顺序语义": additive before scaling), then z += bias for
+ * each deduplicated bias entry ([SGL] same section: bias after the mask;
+ * applying it before a later mask is identical because -inf + b = -inf).
+ * Tokens outside history and bias are not touched.  Skipped (no launch) when
+ * the batch has neither NEED_PENALTY nor HAS_BIAS.  bf16 logits would round
+ * the transformed values, so only fp32 is accepted here. */
+int sampler_apply_transforms(const sampler_batch *b, float *logits, int64_t ld,
+                             void *stream);
+
+/* Grammar bitmask in place ([SGL] "位掩码"; [SO] 4.2): token t of row r is
+ * allowed iff bit (t & 31) of word bitmask[r*mask_ld + (t >> 5)] is 1;
+ * disallowed tokens become exactly -inf.  bitmask: dev int32 [B, mask_ld],
+ * mask_ld >= ceil(V/32); a word of -1 allows all its tokens; bits at
+ * positions >= V are ignored.  row_has_mask: dev uint8 [B] or NULL (every
+ * row has a mask row); rows with 0 are untouched.  dtype: SAMPLER_DTYPE_*. */
+int sampler_apply_bitmask(void *logits, int dtype, int64_t ld, int32_t B,
+                          int32_t V, const int32_t *bitmask, int64_t mask_ld,
+                          const uint8_t *row_has_mask, void *stream);
+
+/* Device workspace bytes sampler_sample needs for B rows of V tokens. */
+size_t sampler_workspace_bytes(int32_t B, int32_t V);
+
+/* Zero a workspace on `stream` (a fill kernel, safe under graph capture).
+ * A workspace must be zero before its first sampler_sample; every
+ * sampler_sample leaves its synchronisation counters zero again, so one init
+ * per allocation is enough, also for later calls with other B or V that fit
+ * in it.  Two calls that share a workspace must not overlap. */
+int sampler_workspace_init(void *workspace, size_t ws_bytes, void *stream);
+
+/* The sampling step.
+ *   logits      dev [B, ld] (ld >= V), dtype SAMPLER_DTYPE_*; read only.
+ *   bitmask     dev int32 [B, mask_ld] or NULL: applied on the fly with the
+ *               semantics of sampler_apply_bitmask (nothing is written).
+ *   row_has_mask dev uint8 [B] or NULL.
+ *   out_ids     dev int32 [B] (required); out_logprobs dev float [B] or NULL;
+ *               out_status dev int32 [B] or NULL.
+ *   workspace   dev, >= sampler_workspace_bytes(B, V), zeroed once.
+ * Per row, on the transformed (and masked) logits z:
+ *   greedy rows: id = lowest index of max z; logprob = log_softmax(z)[id]
+ *     ([SGL] "贪心路径"; [GLM] "采样": greedy rows use the logits before
+ *     the temperature).
+ *   other rows: s = z/T ([SGL] "采样主路径的骨架"); S1 = min-p set
+ *     {p_t >= min_p * p_max}; S2 = top-k of S1 (ties at the k-th value all
+ *     kept); S3 = top-p of S2 {t : mass of S2 strictly above t < top_p *
+ *     mass(S2)} (ties all in or all out) ([SGL] "概率裁剪的数学"; order
+ *     min-p -> top-k -> top-p as vLLM applies its argmax-invariant processors
+ *     after the temperature, [GLM] "采样"); the drawn token maximises
+ *     (s_t - max s) - ln(-ln U_t) over S3, an exponential race equivalent to a
+ *     draw from the renormalised distribution ([GLM] "采样" formula for p'),
+ *     with U_t = (2*(x>>9)+1) * 2^-24 and x word (t&3) of Philox-4x32-10
+ *     [PHX] at counter (t>>2, lo(offset), hi(offset), 0), key (lo(seed),
+ *     hi(seed)); logprob = log_softmax(s)[id] over all allowed tokens, before
+ *     truncation ([SGL] "logprobs 的数值一致性").
+ * Errors: B or V mismatch with `b`, bad dtype or strides -> EINVAL;
+ * workspace too small -> ENOSPC; launch failure -> EHIP. */
+int sampler_sample(const sampler_batch *b, const void *logits, int dtype,
+                   int64_t ld, const int32_t *bitmask, int64_t mask_ld,
+                   const uint8_t *row_has_mask, int32_t *out_ids,
+                   float *out_logprobs, int32_t *out_status, void *workspace,
+                   size_t ws_bytes, void *stream);
+
+/* ---- options and instrumentation ------------------------------------------
+ * sampler_set_option(SAMPLER_OPT_ALGO, v): 0 = fast path (default),
+ * 1 = the row-serial exact path for every row (one workgroup per row, many
+ * passes; used to test the fast path and the fallback it takes for rows whose
+ * boundary sets do not fit on chip).  Process-wide; not for concurrent use.
+ *
+ * sampler_time_next(k, start, stop): on the next sampler_sample call, record
+ * hipEvent_t `start` / `stop` (passed as void*) on the call's stream right
+ * before and after its kernel k (0 = the streaming scan kernel, 1 = the race
+ * kernel).  One-shot; used by the benchmark to time the dominant kernel. */
+#define SAMPLER_OPT_ALGO 1
+int sampler_set_option(int option, int64_t value);
+int sampler_time_next(int kernel, void *start_event, void *stop_event);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,149 @@
+"""Host-side checks of the C ABI: the library loads and exports every function
+include/cd_sampler.h declares; sampler_pack_host validates and packs as
+documented.  No GPU call is made."""
+import ctypes as ct
+import os
+import re
+
+import numpy as np
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def cds():
+    import constrained_decoding_amd as m
+    return m
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "cd_sampler.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(sampler_[a-z_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol(cds):
+    declared = _declared_functions()
+    assert len(declared) >= 10
+    lib = ct.CDLL(cds.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(cds.EXPORTS) == declared
+
+
+def test_strerror_and_version(cds):
+    assert cds.strerror(0) == "ok"
+    for code in (-1, -2, -3, -4, -5):
+        assert cds.strerror(code) != "unknown error"
+    assert "gfx950" in cds.version()
+
+
+def _rowparams(buf, B):
+    dt = np.dtype([("T", "<f4"), ("top_p", "<f4"), ("min_p", "<f4"), ("top_k", "<i4"),
+                   ("rep", "<f4"), ("freq", "<f4"), ("pres", "<f4"), ("flags", "<u4"),
+                   ("pen_lo", "<i4"), ("pen_hi", "<i4"), ("bias_lo", "<i4"), ("bias_hi", "<i4"),
+                   ("seed", "<u8"), ("offset", "<u8")])
+    assert dt.itemsize == 64
+    return np.frombuffer(buf[:64 * B].tobytes(), dt)
+
+
+def test_flags_greedy_and_max_top_k(cds):
+    T = np.array([0.0, 0.7, 1.0, 1e-6, 0.9], np.float32)
+    k = np.array([0, 50, 1, 0, 20], np.int32)
+    p = np.array([1.0, 0.9, 1.0, 0.5, 1.0], np.float32)
+    mp = np.array([0.3, 0.0, 0.0, 0.0, 0.05], np.float32)
+    buf, b = cds.pack_host(5, 1000, T, top_k=k, top_p=p, min_p=mp)
+    rows = _rowparams(buf, 5)
+    greedy = rows["flags"] & 1
+    np.testing.assert_array_equal(greedy, [1, 0, 1, 1, 0])   # T<1e-5 or top_k==1
+    assert b.flags & cds.FLAG_ANY_GREEDY and not b.flags & cds.FLAG_ALL_GREEDY
+    assert b.flags & cds.FLAG_NEED_TOP_K and b.flags & cds.FLAG_NEED_TOP_P
+    assert b.flags & cds.FLAG_NEED_MIN_P                       # row 4 (row 0 is greedy)
+    assert b.max_top_k == 50                                  # every sampled row has k
+    np.testing.assert_array_equal(rows["offset"], np.arange(5))  # default offset = row
+    # greedy rows do not raise NEED_* flags
+    _, b2 = cds.pack_host(2, 1000, np.array([0.0, 0.0], np.float32),
+                          top_p=np.array([0.5, 0.5], np.float32),
+                          min_p=np.array([0.2, 0.2], np.float32))
+    assert b2.flags & cds.FLAG_ALL_GREEDY
+    assert not b2.flags & (cds.FLAG_NEED_TOP_P | cds.FLAG_NEED_MIN_P | cds.FLAG_NEED_TOP_K)
+    # top_k off (0 or >= V) on a sampled row -> no max_top_k
+    _, b3 = cds.pack_host(2, 1000, np.array([1.0, 1.0], np.float32),
+                          top_k=np.array([20, 1000], np.int32))
+    assert b3.max_top_k == 0
+
+
+def test_penalty_counts_and_bias_dedup(cds):
+    hist = [[3, 3, 7, 3], [], [5]]
+    hp, hi = cds.csr(hist)
+    ids, vals = cds.bias_from_dict({"1": 5.0, "01": -3.0, "7": 2.0})
+    bp = np.array([0, 3, 3, 3], np.int64)
+    buf, b = cds.pack_host(3, 100, np.ones(3, np.float32),
+                           repetition_penalty=np.array([1.1, 1.1, 1.0], np.float32),
+                           frequency_penalty=np.array([0.5, 0.5, 0.0], np.float32),
+                           presence_penalty=np.zeros(3, np.float32),
+                           hist_indptr=hp, hist_ids=hi, bias_indptr=bp, bias_ids=ids,
+                           bias_vals=vals)
+    rows = _rowparams(buf, 3)
+    pen = np.frombuffer(buf[64 * 3:64 * 3 + 8 * b.n_pen].tobytes(), "<i4").reshape(-1, 2)
+    np.testing.assert_array_equal(pen, [[3, 3], [7, 1]])      # row 2 has no active penalty
+    assert (rows["pen_lo"][0], rows["pen_hi"][0]) == (0, 2)
+    assert b.flags & cds.FLAG_NEED_PENALTY and b.flags & cds.FLAG_HAS_BIAS
+    off = 64 * 3 + 8 * b.n_pen
+    bias = np.frombuffer(buf[off:off + 8 * b.n_bias].tobytes(),
+                         [("id", "<i4"), ("val", "<f4")])
+    assert bias["id"].tolist() == [1, 7]
+    assert bias["val"].tolist() == [-3.0, 2.0]                # "01" came later: it wins
+
+
+@pytest.mark.parametrize("field,value", [
+    ("temperature", -0.1), ("temperature", np.nan), ("temperature", np.inf),
+    ("top_p", 0.0), ("top_p", 1.5), ("top_p", np.nan),
+    ("min_p", -0.1), ("min_p", 1.1), ("min_p", np.nan),
+    ("repetition_penalty", 0.0), ("repetition_penalty", np.nan),
+    ("frequency_penalty", np.nan), ("presence_penalty", np.inf),
+])
+def test_invalid_parameters_rejected(cds, field, value):
+    kw = dict(temperature=np.ones(2, np.float32))
+    arr = np.ones(2, np.float32) if field != "frequency_penalty" and field != "presence_penalty" \
+        and field != "min_p" else np.zeros(2, np.float32)
+    if field == "top_p":
+        arr = np.ones(2, np.float32)
+    arr[1] = value
+    kw[field] = arr
+    with pytest.raises(cds.SamplerError) as e:
+        cds.pack_host(2, 100, **kw)
+    assert e.value.code == -1
+
+
+def test_invalid_ids_and_sizes_rejected(cds):
+    T = np.ones(2, np.float32)
+    with pytest.raises(cds.SamplerError) as e:
+        cds.pack_host(2, 100, T, hist_indptr=np.array([0, 1, 2]), hist_ids=np.array([3, 100]))
+    assert e.value.code == -1
+    with pytest.raises(cds.SamplerError):
+        cds.pack_host(2, 100, T, bias_indptr=np.array([0, 1, 1]), bias_ids=np.array([-1]),
+                      bias_vals=np.array([1.0]))
+    with pytest.raises(cds.SamplerError):   # +inf bias is not a valid value
+        cds.pack_host(2, 100, T, bias_indptr=np.array([0, 1, 1]), bias_ids=np.array([1]),
+                      bias_vals=np.array([np.inf]))
+    cds.pack_host(2, 100, T, bias_indptr=np.array([0, 1, 1]), bias_ids=np.array([1]),
+                  bias_vals=np.array([-np.inf]))           # -inf bans a token: allowed
+    with pytest.raises(cds.SamplerError):   # non-monotone indptr
+        cds.pack_host(2, 100, T, hist_indptr=np.array([0, 2, 1]), hist_ids=np.array([1, 2]))
+    with pytest.raises(cds.SamplerError) as e:
+        cds.pack_host(1, 1 << 25, np.ones(1, np.float32))
+    assert e.value.code == -2
+    buf = np.zeros(8, np.uint8)
+    out = cds.Batch()
+    h = cds._binding._HostArrays(2, 100, T)
+    rc = cds.lib.sampler_pack_host(ct.byref(h.hp), buf.ctypes.data, 8, ct.byref(out))
+    assert rc == -3                           # ENOSPC
+
+
+def test_workspace_size_closed_form(cds):
+    n = cds.lib.sampler_workspace_bytes(192, 151936)
+    assert n > 192 * 151936 // 64                    # holds histograms and lists
+    assert cds.lib.sampler_workspace_bytes(0, 10) == 0
+    assert cds.lib.sampler_workspace_bytes(4, 1024) > 0

@@ -1,0 +1,216 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Bar (the benchmark spec): token ids bit-exact except on rows the oracle flags as
+near-ties (top-p prefix mass within 1e-6 of top_p, race keys within 1e-6, or
+a weight within 1e-6 relative of min_p); logprobs within 1e-5 absolute;
+transformed logits within 1e-6 relative (floored at 1) -- bit-exact expected.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_harness import compare, run_gpu, run_oracle, to_device, pack
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import constrained_decoding_amd  # noqa: F401  (must load: no fallback)
+
+
+def _report(label, stats):
+    n, nf, nfm = stats
+    print(f"[parity] {label}: rows={n} flagged={nf} ({nf / max(n, 1):.3%}) "
+          f"flagged-mismatch={nfm}", flush=True)
+
+
+SMALL = [
+    ("c1", lambda: workloads.c1_tiny()),
+    ("c2-24x3000", lambda: workloads.c2_decode(B=24, V=3000)),
+    ("c2-64x20000", lambda: workloads.c2_decode(B=64, V=20000, salt=1)),
+    ("c2-32x40001", lambda: workloads.c2_decode(B=32, V=40001, salt=2)),   # ragged tail
+    ("c3-16x20000", lambda: workloads.c3_penalties(B=16, V=20000)),
+    ("c4-24x20000", lambda: workloads.c4_grammar(B=24, V=20000, sizes=(1, 50, 500, 6000))),
+    ("c5a-4x8x5000", lambda: workloads.c5_spec("a", n_req=4, V=5000)),
+    ("c5b-4x8x5000", lambda: workloads.c5_spec("b", n_req=4, V=5000)),
+]
+
+
+@pytest.mark.parametrize("algo", [0, 1])
+@pytest.mark.parametrize("name,make", SMALL, ids=[s[0] for s in SMALL])
+def test_parity_small(name, make, algo):
+    b = make()
+    print(f"[case] {name} algo={algo} B={b.B} V={b.V}", flush=True)
+    gpu = run_gpu(b, algo=algo)
+    ref, _ = run_oracle(b)
+    _report(f"{name}/algo{algo}", compare(b, gpu, ref, label=name))
+
+
+def test_fused_mask_equals_inplace_mask():
+    b = workloads.c4_grammar(B=16, V=9000, sizes=(1, 50, 500, 3000), salt=3)
+    fused = run_gpu(b, fused_mask=True)
+    inplace = run_gpu(b, fused_mask=False)
+    for x, y in zip(fused, inplace):
+        np.testing.assert_array_equal(x, y)
+
+
+def test_masked_tokens_never_drawn():
+    b = workloads.c4_grammar(B=48, V=12000, sizes=(1, 50, 500, 5000), salt=4)
+    for off in range(4):
+        b.offset[:] = off
+        ids, _, st = run_gpu(b)
+        for r in range(b.B):
+            allowed = b.meta["allowed"][r]
+            if allowed is not None:
+                assert ids[r] in set(allowed.tolist())
+
+
+@pytest.mark.parametrize("name", ["c2", "c3", "c4", "c5a", "c5b"])
+def test_parity_full_size_sampled_rows(name):
+    """Full sizes, the launch configuration the benchmark times; the oracle
+    checks a sample of rows one by one."""
+    b = workloads.CONFIGS[name]()
+    print(f"[case] full {name} B={b.B} V={b.V}", flush=True)
+    gpu = run_gpu(b)
+    rng = np.random.default_rng(7)
+    rows = np.sort(rng.choice(b.B, size=min(b.B, 40), replace=False))
+    ref, _ = run_oracle(b, rows=rows)
+    _report(f"full-{name}", compare(b, gpu, ref, rows=rows, label=name))
+
+
+def test_transformed_logits_bit_exact():
+    import torch
+    import constrained_decoding_amd as cds
+    b = workloads.c3_penalties(B=32, V=30000, salt=5)
+    x = to_device(b)
+    pk = pack(b)
+    cds.apply_transforms(pk, x)
+    torch.cuda.synchronize()
+    got = x.cpu().numpy()
+    for r in range(b.B):
+        ref = oracle.transform_row(b.logits[r], hist_ids=b.hist(r), rep=float(b.rep[r]),
+                                   freq=float(b.freq[r]), pres=float(b.pres[r]),
+                                   bias_ids=b.bias_ids[b.bias_indptr[r]:b.bias_indptr[r + 1]],
+                                   bias_vals=b.bias_vals[b.bias_indptr[r]:b.bias_indptr[r + 1]])
+        np.testing.assert_array_equal(got[r].view(np.uint32), ref.view(np.uint32))
+
+
+def test_bitmask_inplace_matches_oracle_fp32_and_bf16():
+    import torch
+    import constrained_decoding_amd as cds
+    for bf16 in (False, True):
+        b = workloads.c4_grammar(B=12, V=7001, sizes=(1, 33, 700, 4000), salt=6)
+        if not bf16:
+            b.logits = (b.logits.astype(np.uint32) << 16).view(np.float32)
+            b.bf16 = False
+        x = to_device(b)
+        cds.apply_bitmask(x, torch.from_numpy(b.masks).cuda(),
+                          torch.from_numpy(b.row_has_mask).cuda())
+        torch.cuda.synchronize()
+        got = x.float().cpu().numpy()
+        for r in range(b.B):
+            ref = oracle.transform_row(b.logits[r], bf16=bf16,
+                                       mask=b.masks[r] if b.row_has_mask[r] else None)
+            np.testing.assert_array_equal(got[r], ref)
+
+
+def _edge_batch(z, **kw):
+    B, V = z.shape
+    f = lambda v, dt=np.float32: np.full(B, v, dt)
+    return workloads.Batch("edge", z.astype(np.float32), False, kw.get("T", f(1.0)),
+                           kw.get("k", f(0, np.int32)), kw.get("p", f(1.0)),
+                           kw.get("mp", f(0.0)), kw.get("seed", np.arange(B, dtype=np.uint64)),
+                           np.zeros(B, np.uint64), masks=kw.get("masks"),
+                           row_has_mask=kw.get("rhm"))
+
+
+@pytest.mark.parametrize("algo", [0, 1])
+def test_edge_cases(algo):
+    rng = np.random.default_rng(11)
+    V = 1030                       # not a multiple of 4 or 32
+    z = (rng.standard_normal((10, V)) * 2).astype(np.float32)
+    z[0, :] = -np.inf              # nothing finite -> INVALID
+    z[1, 17] = np.nan              # OVERFLOW
+    z[2, 900] = np.inf             # OVERFLOW
+    z[3, [5, 600, 1029]] = 50.0    # tied maxima -> lowest index for greedy
+    z[4, :] = 0.25                 # all equal
+    z[5, :-1] = -np.inf            # a single finite token, the last one
+    z[6, ::2] = -np.inf
+    z[7, :] = np.round(z[7] * 2) / 2   # many ties
+    masks = np.full((10, (V + 31) // 32), -1, np.int32)
+    masks[8] = 0                   # mask allows nothing -> INVALID
+    masks[9] = 0
+    masks[9, 3] = 1 << 7           # exactly token 103 allowed
+    T = np.array([1, 1, 0.5, 0, 0.8, 0.7, 1.2, 0.9, 1, 2], np.float32)
+    k = np.array([0, 0, 0, 0, 5, 3, 0, 7, 0, 4], np.int32)
+    p = np.array([1, 1, 1, 1, 0.5, 0.9, 0.8, 0.85, 1, 0.3], np.float32)
+    mp = np.array([0, 0, 0, 0, 0, 0.1, 0.02, 0.05, 0, 0.5], np.float32)
+    b = _edge_batch(z, T=T, k=k, p=p, mp=mp, masks=masks)
+    ids, lp, st = run_gpu(b, algo=algo)
+    ref, _ = run_oracle(b)
+    compare(b, (ids, lp, st), ref, label="edge")
+    assert st[0] == 2 and st[1] == 1 and st[2] == 1 and st[8] == 2
+    assert ids[3] == 5 and ids[5] == V - 1 and ids[9] == 103 and lp[9] == 0.0
+
+
+def test_strided_and_unaligned_rows():
+    """ld > V (padded rows) and an odd ld (no 16-byte alignment: scalar loads)."""
+    import torch
+    import constrained_decoding_amd as cds
+    for ld_extra in (12, 3):
+        b = workloads.c2_decode(B=16, V=5000, salt=8)
+        pad = np.zeros((b.B, b.V + ld_extra), np.float32)
+        pad[:, :b.V] = b.logits
+        x = torch.from_numpy(pad).cuda()[:, :b.V]
+        assert x.stride(0) == b.V + ld_extra
+        pk = pack(b)
+        ids, lp, st = cds.sample(pk, x)
+        torch.cuda.synchronize()
+        ref, _ = run_oracle(b)
+        compare(b, (ids.cpu().numpy(), lp.cpu().numpy(), st.cpu().numpy()), ref,
+                label=f"ld+{ld_extra}")
+
+
+def test_boundary_overflow_takes_exact_fallback():
+    """Near-uniform logits put > 4096 tokens into the top-p boundary bins: the
+    plan switches the row to the exact path; results still match."""
+    rng = np.random.default_rng(12)
+    z = (rng.standard_normal((6, 60000)) * 1e-3).astype(np.float32)
+    T = np.full(6, 1.0, np.float32)
+    b = _edge_batch(z, T=T, p=np.full(6, 0.5, np.float32),
+                    k=np.array([0, 0, 30000, 0, 0, 0], np.int32))
+    gpu = run_gpu(b)
+    ref, _ = run_oracle(b)
+    _report("overflow-fallback", compare(b, gpu, ref, label="overflow"))
+
+
+def test_deterministic_and_batch_invariant():
+    b = workloads.c2_decode(B=48, V=20000, salt=9)
+    first = run_gpu(b)
+    again = run_gpu(b)
+    for x, y in zip(first, again):
+        np.testing.assert_array_equal(x, y)
+    perm = np.random.default_rng(3).permutation(b.B)[:17]
+    sub = run_gpu(b.subset(perm))
+    for x, y in zip(first, sub):
+        np.testing.assert_array_equal(x[perm], y)
+
+
+def test_workspace_reuse_across_calls_and_shapes():
+    """One workspace serves consecutive calls (it is left zeroed)."""
+    import constrained_decoding_amd as cds
+    big = workloads.c2_decode(B=32, V=30000, salt=10)
+    ws = cds.Workspace(big.B, big.V)
+    r1 = run_gpu(big, workspace=ws)
+    small = workloads.c2_decode(B=8, V=30000, salt=11)
+    r2 = run_gpu(small, workspace=ws)
+    r3 = run_gpu(big, workspace=ws)
+    for x, y in zip(r1, r3):
+        np.testing.assert_array_equal(x, y)
+    ref, _ = run_oracle(small)
+    compare(small, r2, ref, label="ws-reuse")
