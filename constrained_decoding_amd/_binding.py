@@ -314,5 +314,8 @@ def set_algo(algo: int):
 
 def time_next(kernel: int, start_event, stop_event):
     """Record torch.cuda.Event pair around kernel `kernel` of the next sample()."""
+    for e in (start_event, stop_event):
+        if not e.cuda_event:   # torch creates the HIP event on first record
+            e.record()
     _check(lib.sampler_time_next(int(kernel), start_event.cuda_event, stop_event.cuda_event),
            "sampler_time_next")

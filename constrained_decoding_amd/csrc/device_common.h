@@ -144,6 +144,118 @@ __device__ __forceinline__ void race_consider(Best& b, float z, int32_t t, uint3
   }
 }
 
+// ---- fp32 race with a top-two margin ------------------------------------------
+// The fast path ranks candidates by an fp32 key; |key32 - exact key| < 1e-5 for
+// every token that can win (sd error <= 20 * 1.8e-7, Gumbel term < 3e-6, final
+// rounding 1.2e-6), so when the best fp32 key beats the second by more than
+// 2 * kRaceEps the fp32 winner is the exact winner.  Otherwise the row is
+// re-raced in fp64 (finish kernel).
+constexpr float kRaceEps = 1e-4f;
+
+// -ln(-ln U) in fp32: -ln U by a degree-5 series in d = 1-U when d < 1/16
+// (relative error < 2e-7; U near 1 would lose -ln U to cancellation in a
+// log), by the hardware log otherwise.
+__device__ __forceinline__ float gumbel_fast(uint32_t x) {
+  const uint32_t n = 2u * (x >> 9) + 1u;                  // U = n * 2^-24
+  const float d = (float)((1u << 24) - n) * 0x1p-24f;     // 1 - U, exact
+  float e;
+  if (d < 0.0625f) {
+    e = d * (1.0f + d * (0.5f + d * (0.33333334f + d * (0.25f + d * 0.2f))));
+  } else {
+    e = -__logf((float)n * 0x1p-24f);
+  }
+  return -__logf(e);
+}
+
+struct Top2 {
+  float k1;    // best key
+  int32_t t1;  // its token (lowest index on an exact fp32 tie)
+  float z1;    // its logit
+  float k2;    // second-best key
+};
+
+__device__ __forceinline__ Top2 top2_init() {
+  Top2 b;
+  b.k1 = CDS_NEG_INF;
+  b.t1 = INT_MAX;
+  b.z1 = CDS_NEG_INF;
+  b.k2 = CDS_NEG_INF;
+  return b;
+}
+
+__device__ __forceinline__ void top2_add(Top2& b, float k, int32_t t, float z) {
+  if (k > b.k1 || (k == b.k1 && t < b.t1)) {
+    b.k2 = b.k1;
+    b.k1 = k;
+    b.t1 = t;
+    b.z1 = z;
+  } else if (k > b.k2) {
+    b.k2 = k;
+  }
+}
+
+__device__ __forceinline__ void top2_merge(Top2& a, const Top2& o) {
+  if (o.k1 > a.k1 || (o.k1 == a.k1 && o.t1 < a.t1)) {
+    a.k2 = fmaxf(fmaxf(a.k1, a.k2), o.k2);
+    a.k1 = o.k1;
+    a.t1 = o.t1;
+    a.z1 = o.z1;
+  } else {
+    a.k2 = fmaxf(a.k2, fmaxf(o.k1, o.k2));
+  }
+}
+
+// Can a token with value z still enter the top two?
+__device__ __forceinline__ bool race32_hopeful(const Top2& b, float z, float zmax, float invT32) {
+  const float sd = (z - zmax) * invT32;
+  return sd >= -19.5f && sd + 16.7f >= b.k2;
+}
+
+__device__ __forceinline__ void race32(Top2& b, float z, int32_t t, uint32_t x, float zmax,
+                                       float invT32) {
+  const float sd = (z - zmax) * invT32;
+  if (sd < -19.5f || sd + 16.7f < b.k2) return;
+  top2_add(b, sd + gumbel_fast(x), t, z);
+}
+
+// ---- histogram bins ------------------------------------------------------------
+struct BinGeom {
+  float delta;      // 2^floor(log2(T/8))
+  float inv_delta;  // 1 / delta (exact)
+  float c_bin;      // delta * log2(e) / T: exp2((off - 1) * c_bin) = mass vs bin top
+};
+
+__device__ __forceinline__ BinGeom bin_geom(float T) {
+  int e;
+  (void)frexpf(T * 0.125f, &e);  // T/8 = f * 2^e, f in [0.5, 1)
+  BinGeom g;
+  g.delta = ldexpf(1.0f, e - 1);
+  g.inv_delta = ldexpf(1.0f, 1 - e);
+  g.c_bin = (float)((double)g.delta * 1.4426950408889634 / (double)T);
+  return g;
+}
+
+// ---- wave-parallel search ------------------------------------------------------
+// Smallest order key k in (lo, hi] with pred(k) true, for a predicate that is
+// monotone in k, given pred(lo) false and pred(hi) true.  64 probes per step:
+// six steps for a 32-bit range.  Called by all 64 lanes of one wave.
+template <typename Pred>
+__device__ uint32_t wave_first_true(uint32_t lo, uint32_t hi, Pred pred) {
+  const int lane = threadIdx.x & 63;
+  while (hi - lo > 1u) {
+    const uint64_t span = (uint64_t)(hi - lo);
+    const uint32_t probe = lo + (uint32_t)((span * (uint64_t)(lane + 1)) >> 6);
+    const bool ok = (lane == 63) || (probe > lo && pred(probe));
+    const unsigned long long msk = __ballot(ok);
+    const int first = __ffsll((long long)msk) - 1;
+    const uint32_t nhi = __shfl(probe, first, 64);
+    const uint32_t nlo = first > 0 ? __shfl(probe, first - 1, 64) : lo;
+    hi = nhi;
+    lo = (nlo < nhi) ? nlo : lo;
+  }
+  return hi;
+}
+
 // ---- loads -------------------------------------------------------------------
 struct RowView {
   const float* f32;
@@ -196,6 +308,78 @@ __device__ __forceinline__ void load4(const RowView& rv, int64_t t0, int64_t hi,
       x[q] = x[q] + 0.0f;
     }
   }
+}
+
+// N chunks of four tokens, chunk i at t0 = lo + 4*((first+i)*NT + tid).
+// Vector path (VEC: row starts aligned and V % 4 == 0, so every chunk below
+// hi is whole): every load -- logits, then mask words -- is issued before any
+// value is used, with no branch between them; chunks at or beyond hi load
+// chunk `lo` (in bounds) and are discarded.  Otherwise guarded scalar loads.
+template <int NT, int N, bool BF16, bool VEC>
+__device__ __forceinline__ void load_chunks(const RowView& rv, int64_t lo, int64_t hi, int first,
+                                            float x[N][4], uint32_t& nonfin) {
+  if (!VEC) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int64_t t0 = lo + 4 * ((int64_t)(first + i) * NT + threadIdx.x);
+      if (t0 < hi) {
+        load4<BF16, false>(rv, t0, hi, x[i], nonfin);
+      } else {
+        x[i][0] = x[i][1] = x[i][2] = x[i][3] = CDS_NEG_INF;
+      }
+    }
+    return;
+  }
+  int64_t ta[N];
+  bool in[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    const int64_t t0 = lo + 4 * ((int64_t)(first + i) * NT + threadIdx.x);
+    in[i] = t0 < hi;
+    ta[i] = in[i] ? t0 : lo;
+  }
+  uint32_t raw[N][4];
+  if (BF16) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const uint2 u = *reinterpret_cast<const uint2*>(rv.b16 + ta[i]);
+      raw[i][0] = u.x << 16;
+      raw[i][1] = u.x & 0xFFFF0000u;
+      raw[i][2] = u.y << 16;
+      raw[i][3] = u.y & 0xFFFF0000u;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const uint4 u = *reinterpret_cast<const uint4*>(rv.f32 + ta[i]);
+      raw[i][0] = u.x;
+      raw[i][1] = u.y;
+      raw[i][2] = u.z;
+      raw[i][3] = u.w;
+    }
+  }
+  // Masking is applied per chunk, only where some token of the chunk is
+  // disallowed or out of range; the non-finite test (NaN or +inf among allowed
+  // tokens) is one class test per token.  Non-finite values are left in place:
+  // such a row ends with status OVERFLOW whatever the kernels compute for it,
+  // so consumers only have to keep their indexing in bounds for them.
+  uint32_t nf = 0u;
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    uint32_t bits = 0xFu;
+    if (rv.mrow) bits = ((uint32_t)rv.mrow[ta[i] >> 5] >> (uint32_t)(ta[i] & 31)) & 0xFu;
+    if (!in[i]) bits = 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) x[i][q] = __uint_as_float(raw[i][q]);
+    if (bits != 0xFu) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (!((bits >> q) & 1u)) x[i][q] = CDS_NEG_INF;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) nf |= __builtin_amdgcn_class(x[i][q], 0x203) ? 1u : 0u;
+  }
+  nonfin |= nf;
 }
 
 // ---- workgroup reductions (fixed trees: deterministic) -------------------------
@@ -261,6 +445,67 @@ __device__ __forceinline__ uint32_t block_or_u32(uint32_t v, RedScratch<NT>& s) 
 #pragma unroll
   for (int k = 0; k < NT / 64; ++k) tot |= (uint32_t)s.i[k];
   return tot;
+}
+
+template <int NT>
+__device__ __forceinline__ float block_max_f32(float v, RedScratch<NT>& s) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s.f[w] = v;
+  __syncthreads();
+  float tot = s.f[0];
+#pragma unroll
+  for (int k = 1; k < NT / 64; ++k) tot = fmaxf(tot, s.f[k]);
+  return tot;
+}
+
+template <int NT>
+__device__ __forceinline__ int32_t block_min_i32(int32_t v, RedScratch<NT>& s) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) s.i[w] = v;
+  __syncthreads();
+  int32_t tot = s.i[0];
+#pragma unroll
+  for (int k = 1; k < NT / 64; ++k) tot = min(tot, s.i[k]);
+  return tot;
+}
+
+template <int NT>
+__device__ __forceinline__ void block_top2(Top2& b, RedScratch<NT>& s) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    Top2 p;
+    p.k1 = __shfl_xor(b.k1, o, 64);
+    p.t1 = __shfl_xor(b.t1, o, 64);
+    p.z1 = __shfl_xor(b.z1, o, 64);
+    p.k2 = __shfl_xor(b.k2, o, 64);
+    top2_merge(b, p);
+  }
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    s.f[w] = b.k1;
+    s.i[w] = b.t1;
+    s.d[w] = (double)b.z1;
+    s.u[w] = (uint64_t)__float_as_uint(b.k2);
+  }
+  __syncthreads();
+  Top2 r = top2_init();
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) {
+    Top2 p;
+    p.k1 = s.f[k];
+    p.t1 = s.i[k];
+    p.z1 = (float)s.d[k];
+    p.k2 = __uint_as_float((uint32_t)s.u[k]);
+    top2_merge(r, p);
+  }
+  b = r;
 }
 
 // max value, lowest index among equal maxima

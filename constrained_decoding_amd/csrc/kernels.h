@@ -23,17 +23,19 @@ struct SampleArgs {
   RowSync* sync;
   Plan* plans;
   SliceHead* heads;
-  uint32_t* hcnt;   // [B*P][NBINS]
-  uint64_t* hmass;  // [B*P][NBINS]
+  unsigned long long* hist;  // [B*P][NBINS]: count << kCountShift | mass
   SliceBest* bests; // [B*P]
   uint64_t* ulist;  // [B][UCAP]
   int32_t P;
   int64_t S;
 };
 
+// Optional timing events recorded around kernel k: 0 scan, 1 race, 2 finish
+// (3: the plan kernel).
+constexpr int kTimedKernels = 4;
 struct KernelEvents {
-  hipEvent_t start[2];
-  hipEvent_t stop[2];
+  hipEvent_t start[kTimedKernels];
+  hipEvent_t stop[kTimedKernels];
 };
 
 hipError_t launch_transforms(const RowParams* rows, const PenEntry* pen, const BiasEntry* bias,

@@ -88,25 +88,6 @@ __device__ float minp_cut(float zmax, double Td, double m, float min_p) {
   return from_okey(hi);
 }
 
-// Histogram coordinate of a value: s16 = (z * (1/T)) * 16 in fp64; bin j =
-// floor(s16).  zlo(J) = smallest fp32 value whose s16 >= J, so {z >= zlo(J)}
-// is exactly the set of tokens in bins >= J.
-__device__ __forceinline__ double s16_of(float z, double invT) {
-  return ((double)z * invT) * 16.0;
-}
-__device__ float zlo_of(double J, double invT) {
-  if (s16_of(CDS_NEG_INF, invT) >= J) return CDS_NEG_INF;
-  uint32_t lo = okey(CDS_NEG_INF), hi = okey(CDS_POS_INF);
-  while (hi - lo > 1u) {
-    const uint32_t mid = lo + (hi - lo) / 2u;
-    if (s16_of(from_okey(mid), invT) >= J)
-      hi = mid;
-    else
-      lo = mid;
-  }
-  return from_okey(hi);
-}
-
 // ============================================================================
 // transforms and bitmask (in place)
 // ============================================================================
@@ -358,106 +339,224 @@ __global__ __launch_bounds__(NT) void exact_kernel(const SampleArgs a) {
 }
 
 // ============================================================================
-// fast path, kernel 1: scan (+ per-row plan by the last slice to finish)
+// fast path, kernel 1: scan (one HBM pass per slice, register resident)
+// ============================================================================
+template <int NT, int E4, bool BF16, bool VEC>
+__global__ __launch_bounds__(NT) void scan_kernel(const SampleArgs a) {
+  __shared__ RedScratch<NT> red;
+  __shared__ unsigned long long s_hist[NBINS + 32];
+  const int r = blockIdx.y, sl = blockIdx.x, tid = threadIdx.x;
+  const RowParams rp = a.rows[r];
+  const bool greedy = (rp.flags & ROW_GREEDY) != 0;
+  const bool hist = !greedy && (rp.flags & (ROW_TOPK | ROW_TOPP));
+  const int64_t lo = (int64_t)sl * a.S;
+  const int64_t hi = min(lo + a.S, (int64_t)a.V);
+  const RowView rv = row_view<BF16>(a, r);
+
+  float x[E4][4];
+  uint32_t nonfin = 0;
+  load_chunks<NT, E4, BF16, VEC>(rv, lo, hi, 0, x, nonfin);
+
+  // max, then the lowest index holding it (searched only by threads that hold it)
+  float lm = CDS_NEG_INF;
+#pragma unroll
+  for (int i = 0; i < E4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lm = fmaxf(lm, x[i][q]);
+  const float zm = block_max_f32<NT>(lm, red);
+  int32_t am = INT_MAX;
+  if (zm != CDS_NEG_INF && lm == zm) {
+#pragma unroll
+    for (int i = E4 - 1; i >= 0; --i)
+#pragma unroll
+      for (int q = 3; q >= 0; --q)
+        if (x[i][q] == zm) am = (int32_t)(lo + 4 * ((int64_t)i * NT + tid) + q);
+  }
+  am = block_min_i32<NT>(am, red);
+  nonfin = block_or_u32<NT>(nonfin, red);
+
+  const int64_t slot = (int64_t)r * a.P + sl;
+  uint32_t flags = nonfin ? SLICE_NONFINITE : 0u;
+  double se = 0.0;
+  float kmax = 0.0f;
+  if (!hist) {
+    // sum exp((z - zmax) / T_eff): the row's log-partition for the logprob
+    const float c = (greedy ? 1.0f : (float)(1.0 / (double)rp.temperature)) * kLog2e;
+    if (zm != CDS_NEG_INF) {
+#pragma unroll
+      for (int i = 0; i < E4; ++i) {
+        float part = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) part += __builtin_amdgcn_exp2f((x[i][q] - zm) * c);
+        se += (double)part;
+      }
+    }
+    se = block_sum_f64<NT>(se, red);
+  } else if (zm != CDS_NEG_INF) {
+    // histogram of the values below the slice maximum, bins aligned to delta
+    const BinGeom g = bin_geom(rp.temperature);
+    kmax = floorf(zm * g.inv_delta);
+    if (!(fabsf(kmax) < 4194304.0f)) {
+      flags |= SLICE_BINS_LOST;  // bin indices would not be exact: row takes the exact path
+    } else {
+      for (int b = tid; b < NBINS + 32; b += NT) s_hist[b] = 0ull;
+      __syncthreads();
+      // tokens outside the window (and -inf) land in 32 per-lane sink bins:
+      // no branch per token
+      const int sink = NBINS + (tid & 31);
+#pragma unroll
+      for (int i = 0; i < E4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float y = x[i][q] * g.inv_delta;
+          const float kf = floorf(y);
+          const float rbf = kmax - kf;
+          const int rb = (rbf >= 0.0f && rbf < (float)NBINS) ? (int)rbf : sink;
+          const float w = __builtin_amdgcn_exp2f(fmaf(y - kf, g.c_bin, -g.c_bin));
+          const uint32_t fix = (uint32_t)(w * 2147483648.0f);
+          atomicAdd(&s_hist[rb], (1ull << kCountShift) | (unsigned long long)fix);
+        }
+      __syncthreads();
+      unsigned long long* gh = a.hist + slot * NBINS;
+      for (int b = tid; b < NBINS; b += NT) gh[b] = s_hist[b];
+    }
+  }
+  if (tid == 0) {
+    SliceHead h;
+    h.zmax = zm;
+    h.arg = (zm == CDS_NEG_INF) ? -1 : am;
+    h.flags = flags;
+    h.kmax = kmax;
+    h.sumexp = se;
+    h.pad[0] = h.pad[1] = 0u;
+    a.heads[slot] = h;
+  }
+}
+
+// ============================================================================
+// fast path, kernel 2: plan (one workgroup per row)
 // ============================================================================
 template <int NT>
 struct PlanShared {
   SliceHead head[kMaxSlices];
-  double md[NBINS];      // merged per-bin mass relative to exp(m), then scanned
-  uint32_t cumc[NBINS];  // merged per-bin count, then scanned
+  double md[NBINS];                 // per-bin mass relative to exp(m), then scanned
+  uint32_t cumc[NBINS];             // per-bin count, then scanned
+  unsigned long long accm[NBINS];   // merge accumulators
+  uint32_t accc[NBINS];
   double wtot_d[NT / 64];
   uint32_t wtot_u[NT / 64];
-  double J[6];
-  float thr[6];
   int idx[3];
-  int mode, rb1, rb2, rb12, inK, k_rank, rb3_lo, rb3_hi, umin;
-  float zmax, zcut1;
+  int mode, inK, k_rank, rb12;
+  uint32_t lost;
+  float zmax, zcut1, kmax;
   int32_t arg;
-  double m, log_z, jmax, tlo, thi;
+  double m, log_z, tlo, thi;
 };
 
 template <int NT>
-__device__ void plan_row(const SampleArgs& a, int r, const RowParams& rp, PlanShared<NT>& ps) {
-  const int P = a.P, tid = threadIdx.x;
+__global__ __launch_bounds__(NT) void plan_kernel(const SampleArgs a) {
+  __shared__ PlanShared<NT> ps;
+  const int r = blockIdx.x, tid = threadIdx.x, P = a.P;
+  const RowParams rp = a.rows[r];
+  const bool greedy = (rp.flags & ROW_GREEDY) != 0;
+  const bool topk = (rp.flags & ROW_TOPK) != 0, topp = (rp.flags & ROW_TOPP) != 0;
+  const bool hist = !greedy && (topk || topp);
+  const double Td = (double)rp.temperature;
   if (tid < P) ps.head[tid] = a.heads[(int64_t)r * P + tid];
   __syncthreads();
-  const bool greedy = (rp.flags & ROW_GREEDY) != 0;
-  const double invTe = greedy ? 1.0 : 1.0 / (double)rp.temperature;
-  const double Td = (double)rp.temperature;
   if (tid == 0) {
     float zm = CDS_NEG_INF;
     int32_t am = INT_MAX;
-    uint32_t nonfin = 0;
-    int64_t nf = 0;
+    uint32_t fl = 0;
     for (int j = 0; j < P; ++j) {
       const SliceHead& h = ps.head[j];
-      nonfin |= h.nonfinite;
-      nf += h.nfin;
-      if (h.nfin > 0 && (h.zmax > zm || (h.zmax == zm && h.arg < am))) {
+      fl |= h.flags;
+      if (h.zmax != CDS_NEG_INF && (h.zmax > zm || (h.zmax == zm && h.arg < am))) {
         zm = h.zmax;
         am = h.arg;
       }
     }
+    const double invTe = greedy ? 1.0 : 1.0 / Td;
     double Z = 0.0;
-    for (int j = 0; j < P; ++j)
-      if (ps.head[j].nfin > 0)
-        Z += ps.head[j].sumexp * exp(((double)ps.head[j].zmax - (double)zm) * invTe);
+    if (!hist)
+      for (int j = 0; j < P; ++j)
+        if (ps.head[j].zmax != CDS_NEG_INF)
+          Z += ps.head[j].sumexp * exp(((double)ps.head[j].zmax - (double)zm) * invTe);
     int mode = PLAN_FAST;
-    if (nf == 0) {
+    if (zm == CDS_NEG_INF) {
       write_out(a, r, -1, CDS_NEG_INF, 2);
       mode = PLAN_DONE;
-    } else if (nonfin) {
+    } else if (fl & SLICE_NONFINITE) {
       write_out(a, r, -1, __builtin_nanf(""), 1);
       mode = PLAN_DONE;
     } else if (greedy) {
       write_out(a, r, am, (float)(-log(Z)), 0);
       mode = PLAN_DONE;
+    } else if (fl & SLICE_BINS_LOST) {
+      mode = PLAN_SLOW;
     }
     ps.mode = mode;
     ps.zmax = zm;
     ps.arg = am;
     ps.m = (double)zm / Td;
     ps.log_z = log(Z);
-    ps.zcut1 = (mode == PLAN_FAST && (rp.flags & ROW_MINP)) ? minp_cut(zm, Td, ps.m, rp.min_p)
-                                                           : CDS_NEG_INF;
-    ps.jmax = floor(s16_of(zm, invTe));
-    a.sync[r].scan_ticket = 0u;  // ready for the next call
   }
   __syncthreads();
-  const bool topk = (rp.flags & ROW_TOPK) != 0, topp = (rp.flags & ROW_TOPP) != 0;
-  if (ps.mode != PLAN_FAST || !(topk || topp)) {
-    if (tid == 0) {
-      Plan pl = {};
-      pl.mode = ps.mode;
-      pl.arg = ps.arg;
-      pl.zmax = ps.zmax;
-      pl.zcut1 = ps.zcut1;
-      pl.m = ps.m;
-      pl.log_z = ps.log_z;
-      pl.z_win = CDS_NEG_INF;
-      pl.z_sure = CDS_NEG_INF;
-      pl.a_lo = pl.a_hi = pl.k_lo = pl.k_hi = CDS_POS_INF;
-      pl.p = (double)rp.top_p;
-      a.plans[r] = pl;
+  // min-p: the smallest fp32 value whose weight reaches min_p (wave 0)
+  if (tid < 64) {
+    float zc = CDS_NEG_INF;
+    if (ps.mode == PLAN_FAST && (rp.flags & ROW_MINP)) {
+      const double m = ps.m, mp = (double)rp.min_p;
+      auto pred = [&](uint32_t k) { return exp((double)from_okey(k) / Td - m) >= mp; };
+      if (!pred(okey(-FLT_MAX))) zc = from_okey(wave_first_true(okey(-FLT_MAX), okey(ps.zmax), pred));
     }
+    if (tid == 0) ps.zcut1 = zc;
+  }
+  __syncthreads();
+
+  auto write_plan = [&](int mode) {
+    Plan pl = {};
+    pl.mode = mode;
+    pl.arg = ps.arg;
+    pl.zmax = ps.zmax;
+    pl.zcut1 = ps.zcut1;
+    pl.m = ps.m;
+    pl.log_z = ps.log_z;
+    pl.z_sure = CDS_NEG_INF;
+    pl.a_lo = pl.a_hi = pl.k_lo = pl.k_hi = CDS_POS_INF;
+    pl.p = (double)rp.top_p;
+    return pl;
+  };
+  if (ps.mode != PLAN_FAST || !hist) {
+    if (tid == 0) a.plans[r] = write_plan(ps.mode);
     return;
   }
 
-  // merge the slices' histograms (aligned bins: row bin = slice bin + offset)
-  const double jmax = ps.jmax, m = ps.m;
+  // merge the slices' histograms: row bin = slice bin + (row kmax - slice kmax)
+  const BinGeom g = bin_geom(rp.temperature);
+  const float kmax = floorf(ps.zmax * g.inv_delta);
   for (int b = tid; b < NBINS; b += NT) {
-    uint32_t c = 0;
-    unsigned long long mf = 0;
-    for (int j = 0; j < P; ++j) {
-      if (ps.head[j].nfin <= 0) continue;
-      const double o = jmax - ps.head[j].jmax;
-      if (o > (double)b) continue;
-      const int64_t idx = ((int64_t)r * P + j) * NBINS + (b - (int)o);
-      c += a.hcnt[idx];
-      mf += a.hmass[idx];
-    }
-    ps.cumc[b] = c;
-    ps.md[b] = (double)mf * 0x1p-40 * exp((jmax + 1.0 - (double)b) * 0.0625 - m);
+    ps.accm[b] = 0ull;
+    ps.accc[b] = 0u;
+  }
+  __syncthreads();
+#pragma unroll 4
+  for (int e = tid; e < P * NBINS; e += NT) {
+    const int j = e / NBINS, sb = e - j * NBINS;
+    const unsigned long long v = a.hist[((int64_t)r * P + j) * NBINS + sb];
+    if (v == 0ull || ps.head[j].zmax == CDS_NEG_INF) continue;
+    const float rowbin = (kmax - ps.head[j].kmax) + (float)sb;
+    if (rowbin >= (float)NBINS) continue;
+    atomicAdd(&ps.accc[(int)rowbin], (uint32_t)(v >> kCountShift));
+    atomicAdd(&ps.accm[(int)rowbin], v & ((1ull << kCountShift) - 1ull));
+  }
+  __syncthreads();
+  const double m = ps.m;
+  for (int b = tid; b < NBINS; b += NT) {
+    ps.cumc[b] = ps.accc[b];
+    // bin b spans [(kmax-b)*delta, (kmax-b+1)*delta); masses are relative to its top
+    const double top = ((double)kmax + 1.0 - (double)b) * (double)g.delta;
+    ps.md[b] = (double)ps.accm[b] * 0x1p-31 * exp(top / Td - m);
   }
   __syncthreads();
   block_scan_inplace<NT>(ps.cumc, NBINS, 0u, [](uint32_t x, uint32_t y) { return x + y; },
@@ -471,11 +570,12 @@ __device__ void plan_row(const SampleArgs& a, int r, const RowParams& rp, PlanSh
       if (ps.cumc[b] >= (uint32_t)rp.top_k) atomicMin(&ps.idx[0], b);
   __syncthreads();
   if (tid == 0) {
+    ps.log_z = log(ps.md[NBINS - 1]);
     const int rb2 = ps.idx[0];
     int rb1 = NBINS;
     if (ps.zcut1 != CDS_NEG_INF) {
-      const double rbd = jmax - floor(s16_of(ps.zcut1, invTe));
-      rb1 = rbd >= (double)NBINS ? NBINS : (int)rbd;
+      const float rbf = kmax - floorf(ps.zcut1 * g.inv_delta);
+      rb1 = rbf >= (float)NBINS ? NBINS : (int)rbf;
     }
     int inK = -1, k_rank = 0;
     if (rb2 < NBINS && rb2 <= rb1) {
@@ -487,11 +587,9 @@ __device__ void plan_row(const SampleArgs& a, int r, const RowParams& rp, PlanSh
     const int rb12 = min(rb1, rb2);
     const double M_lo = rb12 > 0 ? ps.md[min(rb12, NBINS) - 1] : 0.0;
     const double M_hi = rb12 < NBINS ? ps.md[rb12] : M_lo;
-    ps.rb1 = rb1;
-    ps.rb2 = rb2;
-    ps.rb12 = rb12;
     ps.inK = inK;
     ps.k_rank = k_rank;
+    ps.rb12 = rb12;
     ps.tlo = (double)rp.top_p * M_lo * (1.0 - 1e-9);
     ps.thi = (double)rp.top_p * M_hi * (1.0 + 1e-9);
   }
@@ -504,179 +602,41 @@ __device__ void plan_row(const SampleArgs& a, int r, const RowParams& rp, PlanSh
   __syncthreads();
   if (tid == 0) {
     const int cap = ps.rb12 < NBINS ? ps.rb12 : NBINS - 1;
-    int rb3_hi = min(ps.idx[2], cap);
-    int rb3_lo = min(ps.idx[1], rb3_hi);
+    const int rb3_hi = min(ps.idx[2], cap);
+    const int rb3_lo = min(ps.idx[1], rb3_hi);
     const int inK = ps.inK;
     int umin = NBINS;
     if (topp) umin = rb3_lo;
     if (inK >= 0) umin = min(umin, inK);
-    auto cnt_range = [&](int lo, int hi) -> uint32_t {  // bins [lo, hi]
-      return ps.cumc[hi] - (lo > 0 ? ps.cumc[lo - 1] : 0u);
+    auto cnt_range = [&](int lo_b, int hi_b) -> uint32_t {
+      return ps.cumc[hi_b] - (lo_b > 0 ? ps.cumc[lo_b - 1] : 0u);
     };
     uint32_t uexp = topp ? cnt_range(rb3_lo, rb3_hi) : 0u;
     if (inK >= 0 && !(topp && inK >= rb3_lo && inK <= rb3_hi)) uexp += cnt_range(inK, inK);
-    ps.rb3_lo = rb3_lo;
-    ps.rb3_hi = rb3_hi;
-    ps.umin = umin;
-    ps.J[0] = jmax - (double)(NBINS - 1);
-    ps.J[1] = umin < NBINS ? jmax - (double)umin + 1.0 : ps.J[0];
-    ps.J[2] = jmax - (double)rb3_hi;
-    ps.J[3] = jmax - (double)rb3_lo + 1.0;
-    ps.J[4] = jmax - (double)inK;
-    ps.J[5] = jmax - (double)inK + 1.0;
-    ps.mode = uexp > (uint32_t)UCAP ? PLAN_SLOW : PLAN_FAST;
-    ps.idx[0] = (int)uexp;
-  }
-  __syncthreads();
-  if (tid < 6) {
-    const bool valid = tid < 2 || (tid < 4 ? topp : ps.inK >= 0);
-    ps.thr[tid] = valid ? zlo_of(ps.J[tid], invTe) : CDS_POS_INF;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    Plan pl = {};
-    pl.mode = ps.mode;
-    pl.arg = ps.arg;
-    pl.zmax = ps.zmax;
-    pl.zcut1 = ps.zcut1;
-    pl.m = m;
-    pl.log_z = ps.log_z;
-    pl.z_win = ps.thr[0];
-    pl.z_sure = ps.thr[1];
-    pl.a_lo = ps.thr[2];
-    pl.a_hi = ps.thr[3];
-    pl.k_lo = ps.thr[4];
-    pl.k_hi = ps.thr[5];
+    auto edge = [&](int b) { return (kmax - (float)b) * g.delta; };  // bottom of bin b (exact)
+    Plan pl = write_plan(uexp > (uint32_t)UCAP ? PLAN_SLOW : PLAN_FAST);
+    pl.z_sure = umin < NBINS ? edge(umin - 1) : edge(NBINS - 1);
+    if (topp) {
+      pl.a_lo = edge(rb3_hi);
+      pl.a_hi = edge(rb3_lo - 1);
+    }
+    if (inK >= 0) {
+      pl.k_lo = edge(inK);
+      pl.k_hi = edge(inK - 1);
+    }
     pl.k_rank = ps.k_rank;
     pl.topp = topp ? 1 : 0;
-    pl.u_expected = (uint32_t)ps.idx[0];
-    pl.m_sure = (topp && ps.umin > 0) ? ps.md[ps.umin - 1] : 0.0;
-    const int end = ps.inK >= 0 ? ps.inK - 1 : NBINS - 1;
-    pl.m_mid = (topp && end > ps.rb3_hi) ? ps.md[end] - ps.md[ps.rb3_hi] : 0.0;
-    pl.p = (double)rp.top_p;
+    pl.u_expected = uexp;
+    pl.m_sure = (topp && umin > 0) ? ps.md[umin - 1] : 0.0;
+    const int end = inK >= 0 ? inK - 1 : NBINS - 1;
+    pl.m_mid = (topp && end > rb3_hi) ? ps.md[end] - ps.md[rb3_hi] : 0.0;
+    pl.log_z = ps.log_z;
     a.plans[r] = pl;
   }
 }
 
-template <int NT, int E4, bool BF16, bool VEC>
-__global__ __launch_bounds__(NT) void scan_kernel(const SampleArgs a) {
-  __shared__ RedScratch<NT> red;
-  __shared__ uint32_t s_cnt[NBINS];
-  __shared__ unsigned long long s_mass[NBINS];
-  __shared__ PlanShared<NT> ps;
-  __shared__ int s_last;
-  const int r = blockIdx.y, sl = blockIdx.x, tid = threadIdx.x;
-  const RowParams rp = a.rows[r];
-  const bool greedy = (rp.flags & ROW_GREEDY) != 0;
-  const bool hist = !greedy && (rp.flags & (ROW_TOPK | ROW_TOPP));
-  const int64_t lo = (int64_t)sl * a.S;
-  const int64_t hi = min(lo + a.S, (int64_t)a.V);
-  const RowView rv = row_view<BF16>(a, r);
-
-  float x[E4][4];
-  uint32_t nonfin = 0;
-#pragma unroll
-  for (int i = 0; i < E4; ++i) {
-    const int64_t t0 = lo + 4 * ((int64_t)i * NT + tid);
-    if (t0 < hi) {
-      load4<BF16, VEC>(rv, t0, hi, x[i], nonfin);
-    } else {
-      x[i][0] = x[i][1] = x[i][2] = x[i][3] = CDS_NEG_INF;
-    }
-  }
-
-  float zm = CDS_NEG_INF;
-  int32_t am = INT_MAX;
-  int32_t nf = 0;
-#pragma unroll
-  for (int i = 0; i < E4; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const float v = x[i][q];
-      if (v > zm) {
-        zm = v;
-        am = (int32_t)(lo + 4 * ((int64_t)i * NT + tid) + q);
-      }
-      nf += (v != CDS_NEG_INF);
-    }
-  block_argmax<NT>(zm, am, red);
-  nf = block_sum_i32<NT>(nf, red);
-  nonfin = block_or_u32<NT>(nonfin, red);
-
-  const double invTe = greedy ? 1.0 : 1.0 / (double)rp.temperature;
-  const float invTe32 = (float)invTe;
-  double se = 0.0;
-  if (zm != CDS_NEG_INF) {
-#pragma unroll
-    for (int i = 0; i < E4; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (x[i][q] != CDS_NEG_INF) se += (double)exp2f((x[i][q] - zm) * invTe32 * kLog2e);
-  }
-  se = block_sum_f64<NT>(se, red);
-
-  const int64_t slot = (int64_t)r * a.P + sl;
-  double jmax_loc = 0.0;
-  int32_t under = 0;
-  if (hist && zm != CDS_NEG_INF) {
-    for (int b = tid; b < NBINS; b += NT) {
-      s_cnt[b] = 0u;
-      s_mass[b] = 0ull;
-    }
-    __syncthreads();
-    jmax_loc = floor(s16_of(zm, invTe));
-#pragma unroll
-    for (int i = 0; i < E4; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float v = x[i][q];
-        if (v == CDS_NEG_INF) continue;
-        const double s16 = s16_of(v, invTe);
-        const double j = floor(s16);
-        const double rbd = jmax_loc - j;
-        if (rbd < (double)NBINS) {
-          const int rb = (int)rbd;
-          const float wr = expf((float)((s16 - (j + 1.0)) * 0.0625));
-          atomicAdd(&s_cnt[rb], 1u);
-          atomicAdd(&s_mass[rb], (unsigned long long)((double)wr * 0x1p40));
-        } else {
-          ++under;
-        }
-      }
-    __syncthreads();
-    for (int b = tid; b < NBINS; b += NT) {
-      a.hcnt[slot * NBINS + b] = s_cnt[b];
-      a.hmass[slot * NBINS + b] = s_mass[b];
-    }
-  }
-  under = block_sum_i32<NT>(under, red);
-  if (tid == 0) {
-    SliceHead h;
-    h.zmax = zm;
-    h.arg = (zm == CDS_NEG_INF) ? -1 : am;
-    h.nonfinite = nonfin;
-    h.nfin = nf;
-    h.sumexp = se;
-    h.jmax = jmax_loc;
-    h.under = (uint32_t)under;
-    h.pad[0] = h.pad[1] = h.pad[2] = 0u;
-    a.heads[slot] = h;
-  }
-  // publish, then take a ticket; the last slice of the row plans it
-  __threadfence();
-  __syncthreads();
-  if (tid == 0) {
-    const uint32_t old = atomicAdd(&a.sync[r].scan_ticket, 1u);
-    s_last = (old == (uint32_t)(a.P - 1)) ? 1 : 0;
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  plan_row<NT>(a, r, rp, ps);
-}
-
 // ============================================================================
-// fast path, kernel 2: race over the sure tokens, compact the boundary tokens
+// fast path, kernel 3: race over the sure tokens, compact the boundary tokens
 // ============================================================================
 template <int NT, int E4, bool BF16, bool VEC>
 __global__ __launch_bounds__(NT) void race_kernel(const SampleArgs a) {
@@ -690,72 +650,69 @@ __global__ __launch_bounds__(NT) void race_kernel(const SampleArgs a) {
   const RowView rv = row_view<BF16>(a, r);
   const RaceCtx c = make_race_ctx(rp, pl.zmax);
   const float zs = fmaxf(pl.z_sure, pl.zcut1);
-  Best b = best_init();
+  const bool has_u = pl.a_lo < pl.a_hi || pl.k_lo < pl.k_hi;
+  Top2 b = top2_init();
   uint64_t* ul = a.ulist + (int64_t)r * UCAP;
   uint32_t* ucount = &a.sync[r].ucount;
   const int lane = tid & 63;
   uint32_t nonfin = 0;
-  // groups of G chunks: G loads in flight, then the (heavy) race body
   constexpr int G = E4 < 4 ? E4 : 4;
 #pragma unroll 1
   for (int g = 0; g < E4; g += G) {
     float x[G][4];
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const int64_t t0 = lo + 4 * ((int64_t)(g + i) * NT + tid);
-      if (t0 < hi) {
-        load4<BF16, VEC>(rv, t0, hi, x[i], nonfin);
-      } else {
-        x[i][0] = x[i][1] = x[i][2] = x[i][3] = CDS_NEG_INF;
-      }
-    }
+    load_chunks<NT, G, BF16, VEC>(rv, lo, hi, g, x, nonfin);
 #pragma unroll
     for (int i = 0; i < G; ++i) {
       const int64_t t0 = lo + 4 * ((int64_t)(g + i) * NT + tid);
       bool need = false;
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        need |= (x[i][q] != CDS_NEG_INF && x[i][q] >= zs && race_hopeful(b, x[i][q], c));
+        need |= (x[i][q] >= zs && x[i][q] != CDS_NEG_INF &&
+                 race32_hopeful(b, x[i][q], c.zmax, c.invT32));
       if (need) {
         const uint4 blk = race_block(c, t0);
         const uint32_t xs[4] = {blk.x, blk.y, blk.z, blk.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (x[i][q] != CDS_NEG_INF && x[i][q] >= zs)
-            race_consider(b, x[i][q], (int32_t)(t0 + q), xs[q], c);
+          if (x[i][q] >= zs && x[i][q] != CDS_NEG_INF)
+            race32(b, x[i][q], (int32_t)(t0 + q), xs[q], c.zmax, c.invT32);
       }
+      if (has_u) {
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const float v = x[i][q];
-        const bool isU = v != CDS_NEG_INF && v < zs && v >= pl.zcut1 &&
-                         ((v >= pl.a_lo && v < pl.a_hi) || (v >= pl.k_lo && v < pl.k_hi));
-        const unsigned long long msk = __ballot(isU);
-        if (msk) {
-          const int leader = __ffsll((long long)msk) - 1;
-          uint32_t base = 0;
-          if (lane == leader) base = atomicAdd(ucount, (uint32_t)__popcll(msk));
-          base = __shfl(base, leader, 64);
-          if (isU) {
-            const uint32_t pos = base + (uint32_t)__popcll(msk & __lanemask_lt());
-            if (pos < (uint32_t)UCAP)
-              ul[pos] = ((uint64_t)okey(v) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)(t0 + q));
+        for (int q = 0; q < 4; ++q) {
+          const float v = x[i][q];
+          const bool isU = v < zs && v >= pl.zcut1 &&
+                           ((v >= pl.a_lo && v < pl.a_hi) || (v >= pl.k_lo && v < pl.k_hi));
+          const unsigned long long msk = __ballot(isU);
+          if (msk) {
+            const int leader = __ffsll((long long)msk) - 1;
+            uint32_t base = 0;
+            if (lane == leader) base = atomicAdd(ucount, (uint32_t)__popcll(msk));
+            base = __shfl(base, leader, 64);
+            if (isU) {
+              const uint32_t pos = base + (uint32_t)__popcll(msk & __lanemask_lt());
+              if (pos < (uint32_t)UCAP)
+                ul[pos] = ((uint64_t)okey(v + 0.0f) << 32) |
+                          (uint64_t)(0xFFFFFFFFu - (uint32_t)(t0 + q));
+            }
           }
         }
       }
     }
   }
-  block_best<NT>(b, red);
+  block_top2<NT>(b, red);
   if (tid == 0) {
     SliceBest sb;
-    sb.key = b.key;
-    sb.t = b.t;
-    sb.z = b.z;
+    sb.k1 = b.k1;
+    sb.t1 = b.t1;
+    sb.z1 = b.z1;
+    sb.k2 = b.k2;
     a.bests[(int64_t)r * a.P + sl] = sb;
   }
 }
 
 // ============================================================================
-// fast path, kernel 3: exact cuts on the boundary list, race it, merge, output
+// fast path, kernel 4: exact cuts on the boundary list, race it, merge, output
 // ============================================================================
 template <int NT>
 struct FinishShared {
@@ -769,11 +726,52 @@ struct FinishShared {
   int32_t lastA;
   int32_t has3;
   int32_t fail;
+  int32_t ambiguous;
+  float zfinal;
+  float k1;
 };
 
 __device__ __forceinline__ float ukey_z(unsigned long long k) { return from_okey((uint32_t)(k >> 32)); }
 __device__ __forceinline__ int32_t ukey_t(unsigned long long k) {
   return (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+}
+
+// fp64 race over {z >= zfinal} for tokens whose fp32 key reaches k_floor: the
+// tie-breaker when the fp32 top two are within the fp32 error.
+template <int NT, bool BF16, bool VEC>
+__device__ Best exact_rerace(const SampleArgs& a, int r, float zfinal, float k_floor,
+                             RedScratch<NT>& red) {
+  const RowParams rp = a.rows[r];
+  const RowView rv = row_view<BF16>(a, r);
+  const Plan pl = a.plans[r];
+  const RaceCtx c = make_race_ctx(rp, pl.zmax);
+  Best b = best_init();
+  uint32_t nonfin = 0;
+  for_row4<NT, BF16, VEC>(rv, a.V, nonfin, [&](const float* x, int64_t t0) {
+    bool need = false;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      need |= (x[q] != CDS_NEG_INF && x[q] >= zfinal &&
+               (x[q] - c.zmax) * c.invT32 + 16.7f >= k_floor);
+    if (!need) return;
+    const uint4 blk = race_block(c, t0);
+    const uint32_t xs[4] = {blk.x, blk.y, blk.z, blk.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (x[q] == CDS_NEG_INF || x[q] < zfinal) continue;
+      const float k32 = (x[q] - c.zmax) * c.invT32 + gumbel_fast(xs[q]);
+      if (k32 < k_floor) continue;
+      const double k64 = race_key64(x[q], c, xs[q]);
+      const int32_t t = (int32_t)(t0 + q);
+      if (better(k64, t, b.key, b.t)) {
+        b.key = k64;
+        b.t = t;
+        b.z = x[q];
+      }
+    }
+  });
+  block_best<NT>(b, red);
+  return b;
 }
 
 template <int NT, bool BF16, bool VEC>
@@ -788,6 +786,7 @@ __global__ __launch_bounds__(NT) void finish_kernel(const SampleArgs a) {
   if (tid == 0) a.sync[r].ucount = 0u;  // ready for the next call
   if (pl.mode == PLAN_SLOW || n_raw > (uint32_t)UCAP) {
     row_exact<NT, BF16, VEC>(a, r, es);
+    if (tid == 0) a.plans[r].path = PATH_EXACT;
     return;
   }
   const RowParams rp = a.rows[r];
@@ -801,6 +800,7 @@ __global__ __launch_bounds__(NT) void finish_kernel(const SampleArgs a) {
     fs.lastA = -1;
     fs.has3 = 0;
     fs.fail = 0;
+    fs.ambiguous = 0;
   }
   __syncthreads();
   // bitonic sort, descending: larger value first, then lower token index
@@ -873,38 +873,59 @@ __global__ __launch_bounds__(NT) void finish_kernel(const SampleArgs a) {
     __syncthreads();
     if (!fs.fail) zfin = fmaxf(zfin, from_okey(fs.z3key));
   }
-
-  Best b = best_init();
-  if (!fs.fail) {
-    const RaceCtx c = make_race_ctx(rp, pl.zmax);
-    for (int i = tid; i < n; i += NT) {
-      const float z = ukey_z(fs.key[i]);
-      if (!(z >= zfin)) continue;
-      const int32_t t = ukey_t(fs.key[i]);
-      if (!race_hopeful(b, z, c)) continue;
-      const uint4 blk = race_block(c, (int64_t)(t & ~3));
-      const int w = t & 3;
-      const uint32_t xw = w == 0 ? blk.x : (w == 1 ? blk.y : (w == 2 ? blk.z : blk.w));
-      race_consider(b, z, t, xw, c);
-    }
+  if (fs.fail) {
+    row_exact<NT, BF16, VEC>(a, r, es);
+    if (tid == 0) a.plans[r].path = PATH_EXACT;
+    return;
   }
-  block_best<NT>(b, fs.red);
-  if (tid == 0 && !fs.fail) {
+
+  // race the boundary tokens that survive, merge with the slices' top two
+  const RaceCtx c = make_race_ctx(rp, pl.zmax);
+  Top2 b = top2_init();
+  for (int i = tid; i < n; i += NT) {
+    const float z = ukey_z(fs.key[i]);
+    if (!(z >= zfin)) continue;
+    const int32_t t = ukey_t(fs.key[i]);
+    if (!race32_hopeful(b, z, c.zmax, c.invT32)) continue;
+    const uint4 blk = race_block(c, (int64_t)(t & ~3));
+    const int w = t & 3;
+    const uint32_t xw = w == 0 ? blk.x : (w == 1 ? blk.y : (w == 2 ? blk.z : blk.w));
+    race32(b, z, t, xw, c.zmax, c.invT32);
+  }
+  block_top2<NT>(b, fs.red);
+  if (tid == 0) {
     for (int j = 0; j < a.P; ++j) {
       const SliceBest sb = a.bests[(int64_t)r * a.P + j];
-      if (better(sb.key, sb.t, b.key, b.t)) {
-        b.key = sb.key;
-        b.t = sb.t;
-        b.z = sb.z;
-      }
+      Top2 o;
+      o.k1 = sb.k1;
+      o.t1 = sb.t1;
+      o.z1 = sb.z1;
+      o.k2 = sb.k2;
+      top2_merge(b, o);
     }
-    if (b.t == INT_MAX)
+    const float zs = fmaxf(pl.z_sure, pl.zcut1);
+    fs.zfinal = (pl.topp || pl.k_rank > 0) ? zfin : zs;
+    fs.k1 = b.k1;
+    if (b.t1 == INT_MAX) {
       fs.fail = 1;
-    else
-      write_out(a, r, b.t, (float)((double)b.z / Td - pl.m - pl.log_z), 0);
+    } else if (!(b.k1 - b.k2 > 2.0f * kRaceEps)) {
+      fs.ambiguous = 1;
+    } else {
+      write_out(a, r, b.t1, (float)((double)b.z1 / Td - pl.m - pl.log_z), 0);
+      a.plans[r].path = PATH_FAST;
+    }
   }
   __syncthreads();
-  if (fs.fail) row_exact<NT, BF16, VEC>(a, r, es);
+  if (fs.fail) {
+    row_exact<NT, BF16, VEC>(a, r, es);
+    if (tid == 0) a.plans[r].path = PATH_EXACT;
+  } else if (fs.ambiguous) {
+    const Best e = exact_rerace<NT, BF16, VEC>(a, r, fs.zfinal, fs.k1 - 2.0f * kRaceEps, fs.red);
+    if (tid == 0) {
+      write_out(a, r, e.t, (float)((double)e.z / Td - pl.m - pl.log_z), 0);
+      a.plans[r].path = PATH_RERACE;
+    }
+  }
 }
 
 // ============================================================================
@@ -941,22 +962,35 @@ hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream) {
   return hipGetLastError();
 }
 
-constexpr int kScanNT = 256;
+constexpr int kPlanNT = 256;
 constexpr int kFinishNT = 512;
+
+static inline void rec(const KernelEvents* ev, bool start, int k, hipStream_t s) {
+  if (!ev) return;
+  hipEvent_t e = start ? ev->start[k] : ev->stop[k];
+  if (e) (void)hipEventRecord(e, s);
+}
 
 template <int E4, bool BF16, bool VEC>
 static hipError_t launch_fast(const SampleArgs& a, bool need_race, const KernelEvents* ev,
                               hipStream_t s) {
   const dim3 grid((unsigned)a.P, (unsigned)a.B);
-  if (ev && ev->start[0]) (void)hipEventRecord(ev->start[0], s);
-  hipLaunchKernelGGL((scan_kernel<kScanNT, E4, BF16, VEC>), grid, dim3(kScanNT), 0, s, a);
-  if (ev && ev->stop[0]) (void)hipEventRecord(ev->stop[0], s);
+  rec(ev, true, 0, s);
+  hipLaunchKernelGGL((scan_kernel<kScanThreads, E4, BF16, VEC>), grid, dim3(kScanThreads), 0, s,
+                     a);
+  rec(ev, false, 0, s);
+  rec(ev, true, 3, s);
+  hipLaunchKernelGGL((plan_kernel<kPlanNT>), dim3((unsigned)a.B), dim3(kPlanNT), 0, s, a);
+  rec(ev, false, 3, s);
   if (need_race) {
-    if (ev && ev->start[1]) (void)hipEventRecord(ev->start[1], s);
-    hipLaunchKernelGGL((race_kernel<kScanNT, E4, BF16, VEC>), grid, dim3(kScanNT), 0, s, a);
-    if (ev && ev->stop[1]) (void)hipEventRecord(ev->stop[1], s);
+    rec(ev, true, 1, s);
+    hipLaunchKernelGGL((race_kernel<kScanThreads, E4, BF16, VEC>), grid, dim3(kScanThreads), 0,
+                       s, a);
+    rec(ev, false, 1, s);
+    rec(ev, true, 2, s);
     hipLaunchKernelGGL((finish_kernel<kFinishNT, BF16, VEC>), dim3((unsigned)a.B),
                        dim3(kFinishNT), 0, s, a);
+    rec(ev, false, 2, s);
   }
   return hipGetLastError();
 }
@@ -964,12 +998,14 @@ static hipError_t launch_fast(const SampleArgs& a, bool need_race, const KernelE
 template <bool BF16, bool VEC>
 static hipError_t launch_fast_e4(const SampleArgs& a, bool need_race, const KernelEvents* ev,
                                  hipStream_t s) {
-  const int64_t e4 = (a.S + 4 * kScanNT - 1) / (4 * kScanNT);
+  const int64_t e4 = (a.S + 4 * kScanThreads - 1) / (4 * kScanThreads);
   if (e4 <= 1) return launch_fast<1, BF16, VEC>(a, need_race, ev, s);
   if (e4 <= 2) return launch_fast<2, BF16, VEC>(a, need_race, ev, s);
   if (e4 <= 4) return launch_fast<4, BF16, VEC>(a, need_race, ev, s);
   if (e4 <= 8) return launch_fast<8, BF16, VEC>(a, need_race, ev, s);
+  if (e4 <= 12) return launch_fast<12, BF16, VEC>(a, need_race, ev, s);
   if (e4 <= 16) return launch_fast<16, BF16, VEC>(a, need_race, ev, s);
+  if (e4 <= 20) return launch_fast<20, BF16, VEC>(a, need_race, ev, s);
   return hipErrorInvalidValue;
 }
 
@@ -977,10 +1013,10 @@ template <bool BF16, bool VEC>
 static hipError_t launch_any(const SampleArgs& a, int algo, bool need_race,
                              const KernelEvents* ev, hipStream_t s) {
   if (algo == 1) {
-    if (ev && ev->start[0]) (void)hipEventRecord(ev->start[0], s);
+    rec(ev, true, 0, s);
     hipLaunchKernelGGL((exact_kernel<kFinishNT, BF16, VEC>), dim3((unsigned)a.B),
                        dim3(kFinishNT), 0, s, a);
-    if (ev && ev->stop[0]) (void)hipEventRecord(ev->stop[0], s);
+    rec(ev, false, 0, s);
     return hipGetLastError();
   }
   return launch_fast_e4<BF16, VEC>(a, need_race, ev, s);

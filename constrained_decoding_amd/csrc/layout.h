@@ -41,41 +41,53 @@ struct BiasEntry {
 };
 
 // ---- sampling geometry ------------------------------------------------------
-// A row is split into P slices of S tokens (S a multiple of 4); one workgroup
-// per slice.  The histogram window covers s = z/T within NBINS/16 of the row
-// maximum in bins of width 1/16; tokens further below can neither win the race
-// (the exponential race key is bounded, see kernels.hip) nor carry mass that
-// matters at the 1e-9 level.
-constexpr int kBinsPerUnit = 16;
-constexpr int NBINS = 560;        // 35 units of s
+// A row is split into P slices (S tokens each, S a multiple of 4), one
+// workgroup of kScanThreads per slice, each thread holding up to kMaxChunks
+// chunks of four tokens in registers.
+//
+// Histogram bins are aligned to a power-of-two grid in z: width
+// delta = 2^floor(log2(T/8)), i.e. between 1/16 and 1/8 in s = z/T.  Bin
+// index floor(z/delta) and the offset inside the bin are exact fp32
+// operations, bins of different slices line up, and the value range of a bin
+// is exactly [k*delta, (k+1)*delta).  The window holds the NBINS bins below the
+// row maximum (at least 35 units of s); tokens further down can neither win
+// the race (the exponential-race key is bounded, see device_common.h) nor carry
+// mass that matters at the 1e-10 level.
+constexpr int NBINS = 560;
+constexpr int kScanThreads = 256;
+constexpr int kMaxChunks = 20;
+constexpr int64_t kSliceMax = (int64_t)kScanThreads * 4 * kMaxChunks;  // 20480 tokens
+constexpr int kCountShift = 48;   // histogram word: count << 48 | fixed-point mass
 constexpr int UCAP = 4096;        // boundary tokens the refinement holds on chip
 constexpr int kMaxSlices = 64;
 constexpr int kMaxRows = 65535;
 
 // ---- workspace ------------------------------------------------------------
-struct RowSync {        // zero between calls; restored by the last arrivers
-  uint32_t scan_ticket;
-  uint32_t race_ticket;
+struct RowSync {        // zero between calls (restored by the finish kernel)
   uint32_t ucount;
-  uint32_t pad;
+  uint32_t pad[3];
+};
+
+enum SliceFlag : uint32_t {
+  SLICE_NONFINITE = 1u,   // a NaN or +inf among the slice's allowed tokens
+  SLICE_BINS_LOST = 2u,   // |zmax / delta| too large for exact fp32 bin indices
 };
 
 struct SliceHead {
-  float zmax;           // max finite allowed z of the slice (-inf if none)
+  float zmax;           // max allowed finite z of the slice (-inf if none)
   int32_t arg;          // its lowest index (-1 if none)
-  uint32_t nonfinite;   // any NaN / +inf among allowed tokens
-  int32_t nfin;         // finite allowed tokens
-  double sumexp;        // sum exp((z - zmax) * invT_eff)
-  double jmax;          // floor(zmax * invT * 16) (histogram rows)
-  uint32_t under;       // tokens below the slice window
-  uint32_t pad[3];
+  uint32_t flags;       // SliceFlag
+  float kmax;           // floor(zmax / delta) (histogram rows)
+  double sumexp;        // sum exp((z - zmax) / T_eff) (rows without histogram)
+  uint32_t pad[2];
 };
-static_assert(sizeof(SliceHead) == 48, "SliceHead layout");
+static_assert(sizeof(SliceHead) == 32, "SliceHead layout");
 
-struct SliceBest {
-  double key;  // race key of the slice's winner (-inf if it had no candidate)
-  int32_t t;   // its token (INT_MAX if none)
-  float z;     // its logit
+struct SliceBest {  // fp32 race keys: the slice's best two
+  float k1;         // best key (-inf if the slice had no candidate)
+  int32_t t1;       // its token
+  float z1;         // its logit
+  float k2;         // second-best key
 };
 
 enum PlanMode : int32_t { PLAN_NONE = 0, PLAN_DONE = 1, PLAN_FAST = 2, PLAN_SLOW = 3 };
@@ -87,17 +99,26 @@ struct alignas(16) Plan {
   float zcut1;       // min-p value cut, -inf when inactive
   double m;          // zmax / T
   double log_z;      // log sum exp(s - m) over allowed finite tokens
-  float z_win;       // tokens below lie outside the histogram window
   float z_sure;      // tokens >= max(z_sure, zcut1) are raced by the slices
   float a_lo, a_hi;  // top-p boundary value range [a_lo, a_hi)
   float k_lo, k_hi;  // top-k / min-p boundary bin [k_lo, k_hi)
   int32_t k_rank;    // > 0: zcut2 is the k_rank-th largest U value in [k_lo,k_hi)
   int32_t topp;      // top-p cut lies in [a_lo, a_hi)
   uint32_t u_expected;
-  uint32_t pad;
   double m_sure;     // mass (relative to exp(m)) of tokens >= z_sure
-  double m_mid;      // mass of tokens between a_lo (excl.) and k_hi (excl.)
+  double m_mid;      // mass of tokens below a_lo and at or above k_hi
   double p;          // top_p
+  int32_t path;      // how the finish kernel resolved the row (FinishPath)
+  int32_t pad;
+};
+static_assert(sizeof(Plan) == 96, "Plan layout");
+
+// Written back into Plan::path by the finish kernel (diagnostics and tests).
+enum FinishPath : int32_t {
+  PATH_NONE = 0,
+  PATH_FAST = 1,       // fp32 race margin decided the winner
+  PATH_RERACE = 2,     // fp32 top two within the error bound: fp64 re-race
+  PATH_EXACT = 3,      // row-serial exact path (plan SLOW, list overflow, cut outside range)
 };
 
 struct WorkspaceLayout {
@@ -108,9 +129,9 @@ struct WorkspaceLayout {
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
-// Slices per row: as many as keep a slice <= 16384 tokens, at most kMaxSlices.
+// Slices per row: the fewest that keep a slice register-resident.
 inline int choose_slices(int32_t V) {
-  int64_t p = (V + 16383) / 16384;
+  int64_t p = (V + kSliceMax - 1) / kSliceMax;
   if (p < 1) p = 1;
   if (p > kMaxSlices) p = kMaxSlices;
   return (int)p;
@@ -133,7 +154,7 @@ inline WorkspaceLayout workspace_layout(int32_t B, int32_t V) {
   L.sync_off = take(sizeof(RowSync) * (size_t)kMaxRows);
   L.plan_off = take(sizeof(Plan) * (size_t)B);
   L.head_off = take(sizeof(SliceHead) * (size_t)B * L.P);
-  L.hist_off = take((sizeof(uint32_t) + sizeof(uint64_t)) * NBINS * (size_t)B * L.P);
+  L.hist_off = take(sizeof(uint64_t) * NBINS * (size_t)B * L.P);
   L.best_off = take(sizeof(SliceBest) * (size_t)B * L.P);
   L.ulist_off = take(sizeof(uint64_t) * UCAP * (size_t)B);
   L.total = off;

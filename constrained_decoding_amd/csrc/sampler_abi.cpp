@@ -23,8 +23,8 @@ constexpr int32_t kMaxB = kMaxRows;
 
 std::atomic<int> g_algo{0};
 // one-shot kernel timing hook (see sampler_time_next)
-std::atomic<void*> g_ev_start[2] = {{nullptr}, {nullptr}};
-std::atomic<void*> g_ev_stop[2] = {{nullptr}, {nullptr}};
+std::atomic<void*> g_ev_start[kTimedKernels] = {};
+std::atomic<void*> g_ev_stop[kTimedKernels] = {};
 
 inline bool finite_f(float x) { return std::isfinite(x); }
 
@@ -315,9 +315,7 @@ int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_
   a.sync = reinterpret_cast<RowSync*>(ws + L.sync_off);
   a.plans = reinterpret_cast<Plan*>(ws + L.plan_off);
   a.heads = reinterpret_cast<SliceHead*>(ws + L.head_off);
-  a.hcnt = reinterpret_cast<uint32_t*>(ws + L.hist_off);
-  a.hmass = reinterpret_cast<uint64_t*>(ws + L.hist_off +
-                                        sizeof(uint32_t) * NBINS * (size_t)B * L.P);
+  a.hist = reinterpret_cast<unsigned long long*>(ws + L.hist_off);
   a.bests = reinterpret_cast<SliceBest*>(ws + L.best_off);
   a.ulist = reinterpret_cast<uint64_t*>(ws + L.ulist_off);
   a.P = L.P;
@@ -325,13 +323,13 @@ int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_
 
   // 16-byte vector loads need every row start (and the base) 16-byte aligned
   const size_t elem = bf16 ? 2 : 4;
-  const bool vec = aligned(logits, 4 * elem) && ((ld * (int64_t)elem) % (4 * (int64_t)elem) == 0);
+  const bool vec = aligned(logits, 4 * elem) && (ld % 4 == 0) && (V % 4 == 0);
   int algo = g_algo.load();
-  if (L.S > 16384) algo = 1;  // slices beyond the register-resident size
+  if (L.S > kSliceMax) algo = 1;  // slices beyond the register-resident size
 
   KernelEvents ev;
   bool have_ev = false;
-  for (int k = 0; k < 2; ++k) {
+  for (int k = 0; k < kTimedKernels; ++k) {
     ev.start[k] = static_cast<hipEvent_t>(g_ev_start[k].exchange(nullptr));
     ev.stop[k] = static_cast<hipEvent_t>(g_ev_stop[k].exchange(nullptr));
     have_ev = have_ev || ev.start[k] || ev.stop[k];
@@ -352,7 +350,7 @@ int sampler_set_option(int option, int64_t value) {
 }
 
 int sampler_time_next(int kernel, void* start_event, void* stop_event) {
-  if (kernel < 0 || kernel > 1) return SAMPLER_EINVAL;
+  if (kernel < 0 || kernel >= kTimedKernels) return SAMPLER_EINVAL;
   g_ev_start[kernel].store(start_event);
   g_ev_stop[kernel].store(stop_event);
   return SAMPLER_OK;

@@ -246,7 +246,8 @@ int sampler_sample(const sampler_batch *b, const void *logits, int dtype,
  * sampler_time_next(k, start, stop): on the next sampler_sample call, record
  * hipEvent_t `start` / `stop` (passed as void*) on the call's stream right
  * before and after its kernel k (0 = the streaming scan kernel, 1 = the race
- * kernel).  One-shot; used by the benchmark to time the dominant kernel. */
+ * kernel, 2 = the finish kernel, 3 = the plan kernel).  One-shot; used by the
+ * benchmark to time the dominant kernel. */
 #define SAMPLER_OPT_ALGO 1
 int sampler_set_option(int option, int64_t value);
 int sampler_time_next(int kernel, void *start_event, void *stop_event);
