@@ -35,11 +35,59 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5a", "c5b"])
     ap.add_argument("--sets", type=int, default=3, help="rotating input sets")
-    ap.add_argument("--cpu-rows", type=int, default=768,
+    ap.add_argument("--cpu-rows", type=int, default=2304,
                     help="rows of the workload the oracle is timed on (cpu_baseline)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--algo", type=int, default=0)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB a few times (the "
+                         "reference point for the FETCH_SIZE / WRITE_SIZE counters)")
     return ap.parse_args()
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * (1 << 20) // 4
+    src = torch.arange(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n * 4, "launches": 5}), flush=True)
+
+
+WORKLOAD_FILES = {"c2": "c2_decode", "c3": "c3_penalties", "c4": "c4_grammar",
+                  "c5a": "c5a_spec_greedy", "c5b": "c5b_spec_topk"}
+
+
+def kernel_sources_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("kernels.hip", "device_common.h", "layout.h"):
+        with open(os.path.join(ROOT, "constrained_decoding_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(config):
+    """HBM bytes per scan_kernel launch from the committed FETCH_SIZE /
+    WRITE_SIZE summary of this workload, or None when that summary is missing
+    or was taken on different kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{WORKLOAD_FILES[config]}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for ln in fh:
+            if ln.startswith("scan_kernel ") and ":" in ln:
+                k, v = ln.split(":", 1)
+                fields[k.split()[1]] = v.strip()
+    if fields.get("traffic_sources_sha256") != kernel_sources_digest():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def algorithmic_bytes(batch):
@@ -70,10 +118,14 @@ def main():
 
     import torch
 
+    torch.cuda.set_device(0)
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+
     import constrained_decoding_amd as cds
     import workloads
 
-    torch.cuda.set_device(0)
     make = workloads.CONFIGS[args.config]
     sets = []
     for s in range(args.sets):
@@ -195,7 +247,8 @@ def main():
         "pipeline_gbs": round(alg / (ms_per_step * 1e-3) / 1e9, 1),
         "roofline": {"bound": "hbm", "kernel": "scan_kernel", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(args.config),
                      "kernel_us": round(kern_ms * 1e3, 2), "bytes_per_launch": scan_bytes},
         "cpu_baseline": cpu,
     }
