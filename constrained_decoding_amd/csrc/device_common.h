@@ -240,7 +240,7 @@ __device__ __forceinline__ BinGeom bin_geom(float T) {
 // monotone in k, given pred(lo) false and pred(hi) true.  64 probes per step:
 // six steps for a 32-bit range.  Called by all 64 lanes of one wave.
 template <typename Pred>
-__device__ uint32_t wave_first_true(uint32_t lo, uint32_t hi, Pred pred) {
+__device__ __forceinline__ uint32_t wave_first_true(uint32_t lo, uint32_t hi, Pred pred) {
   const int lane = threadIdx.x & 63;
   while (hi - lo > 1u) {
     const uint64_t span = (uint64_t)(hi - lo);
@@ -382,7 +382,111 @@ __device__ __forceinline__ void load_chunks(const RowView& rv, int64_t lo, int64
   nonfin |= nf;
 }
 
-// ---- workgroup reductions (fixed trees: deterministic) -------------------------
+// ---- wave-level inclusive prefix sums by DPP (no LDS, no barrier) --------------
+// Hillis-Steele within each row of 16 lanes (row_shr 1, 2, 4, 8), then the
+// last lane of a row is added into the rows above it (row_bcast 15 and 31).
+// Fixed combination order: bit-reproducible.  All 64 lanes must call it.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROWS, 0xf, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  return (uint64_t)dpp_u32<CTRL, ROWS>((uint32_t)v) |
+         ((uint64_t)dpp_u32<CTRL, ROWS>((uint32_t)(v >> 32)) << 32);
+}
+template <typename T, typename Mov>
+__device__ __forceinline__ T wave_incl_sum_impl(T v, Mov mov) {
+  const int lane = threadIdx.x & 63;
+  T t;
+  t = mov(v, 0);
+  if ((lane & 15) >= 1) v = v + t;
+  t = mov(v, 1);
+  if ((lane & 15) >= 2) v = v + t;
+  t = mov(v, 2);
+  if ((lane & 15) >= 4) v = v + t;
+  t = mov(v, 3);
+  if ((lane & 15) >= 8) v = v + t;
+  t = mov(v, 4);
+  if ((lane & 31) >= 16) v = v + t;
+  t = mov(v, 5);
+  if (lane >= 32) v = v + t;
+  return v;
+}
+
+__device__ __forceinline__ unsigned long long wave_incl_sum(unsigned long long v) {
+  return wave_incl_sum_impl(v, [](unsigned long long x, int k) -> unsigned long long {
+    switch (k) {
+      case 0: return dpp_u64<0x111, 0xf>(x);
+      case 1: return dpp_u64<0x112, 0xf>(x);
+      case 2: return dpp_u64<0x114, 0xf>(x);
+      case 3: return dpp_u64<0x118, 0xf>(x);
+      case 4: return dpp_u64<0x142, 0xa>(x);
+      default: return dpp_u64<0x143, 0xc>(x);
+    }
+  });
+}
+__device__ __forceinline__ uint32_t wave_incl_sum(uint32_t v) {
+  return wave_incl_sum_impl(v, [](uint32_t x, int k) -> uint32_t {
+    switch (k) {
+      case 0: return dpp_u32<0x111, 0xf>(x);
+      case 1: return dpp_u32<0x112, 0xf>(x);
+      case 2: return dpp_u32<0x114, 0xf>(x);
+      case 3: return dpp_u32<0x118, 0xf>(x);
+      case 4: return dpp_u32<0x142, 0xa>(x);
+      default: return dpp_u32<0x143, 0xc>(x);
+    }
+  });
+}
+__device__ __forceinline__ double wave_incl_sum(double v) {
+  return wave_incl_sum_impl(v, [](double x, int k) -> double {
+    uint64_t u = (uint64_t)__double_as_longlong(x);
+    switch (k) {
+      case 0: u = dpp_u64<0x111, 0xf>(u); break;
+      case 1: u = dpp_u64<0x112, 0xf>(u); break;
+      case 2: u = dpp_u64<0x114, 0xf>(u); break;
+      case 3: u = dpp_u64<0x118, 0xf>(u); break;
+      case 4: u = dpp_u64<0x142, 0xa>(u); break;
+      default: u = dpp_u64<0x143, 0xc>(u); break;
+    }
+    return __longlong_as_double((long long)u);
+  });
+}
+
+// Value of lane l-1 (0 for lane 0): the exclusive prefix from an inclusive one.
+__device__ __forceinline__ uint32_t wave_shift_up(uint32_t v) { return dpp_u32<0x138, 0xf>(v); }
+__device__ __forceinline__ unsigned long long wave_shift_up(unsigned long long v) {
+  return dpp_u64<0x138, 0xf>(v);
+}
+__device__ __forceinline__ double wave_shift_up(double v) {
+  return __longlong_as_double((long long)dpp_u64<0x138, 0xf>((uint64_t)__double_as_longlong(v)));
+}
+
+// Inclusive prefix sum, in place, over n <= 64*K values of an LDS array, by
+// wave 0 alone: lane l owns elements [K*l, K*l + K).  The caller
+// synchronises the workgroup before (values written) and after (results read).
+template <int K, typename T>
+__device__ __forceinline__ void wave0_scan_inplace(T* v, int n) {
+  if (threadIdx.x >= 64) return;
+  const int l = threadIdx.x;
+  T loc[K];
+  T run = T(0);
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int i = K * l + j;
+    run = run + (i < n ? v[i] : T(0));
+    loc[j] = run;
+  }
+  const T incl = wave_incl_sum(run);
+  const T ex = wave_shift_up(incl);
+#pragma unroll
+  for (int j = 0; j < K; ++j) {
+    const int i = K * l + j;
+    if (i < n) v[i] = ex + loc[j];
+  }
+}
+
+
 template <int NT>
 struct RedScratch {
   double d[NT / 64];
@@ -576,7 +680,7 @@ __device__ __forceinline__ void block_best(Best& b, RedScratch<NT>& s) {
 // -- a fixed combination order, so results are bit-reproducible.
 // `wtot` is LDS scratch of NT/64 elements.  All NT threads must call it.
 template <int NT, typename T, typename Op>
-__device__ void block_scan_inplace(T* v, int n, T ident, Op op, T* wtot) {
+__device__ __forceinline__ void block_scan_inplace(T* v, int n, T ident, Op op, T* wtot) {
   const int chunk = (n + NT - 1) / NT;
   const int lo = min((int)threadIdx.x * chunk, n);
   const int hi = min(lo + chunk, n);

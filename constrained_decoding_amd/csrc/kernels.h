@@ -25,17 +25,17 @@ struct SampleArgs {
   SliceHead* heads;
   unsigned long long* hist;  // [B*P][NBINS]: count << kCountShift | mass
   SliceBest* bests; // [B*P]
-  uint64_t* ulist;  // [B][UCAP]
+  uint64_t* ulist;  // [B][P][SCAP] boundary tokens: okey(z) << 32 | ~t
   int32_t P;
   int64_t S;
+  uint64_t spin_limit;  // wall-clock ticks a race task waits for its row's plan
+  uint32_t gen;         // call generation (nonzero, differs from the previous call's)
 };
 
-// Optional timing events recorded around kernel k: 0 scan, 1 race, 2 finish
-// (3: the plan kernel).
-constexpr int kTimedKernels = 4;
+// Optional timing events recorded around the sampling kernel.
 struct KernelEvents {
-  hipEvent_t start[kTimedKernels];
-  hipEvent_t stop[kTimedKernels];
+  hipEvent_t start;
+  hipEvent_t stop;
 };
 
 hipError_t launch_transforms(const RowParams* rows, const PenEntry* pen, const BiasEntry* bias,
@@ -44,8 +44,8 @@ hipError_t launch_bitmask(void* logits, bool bf16, int64_t ld, int32_t B, int32_
                           const int32_t* mask, int64_t mask_ld, const uint8_t* row_has_mask,
                           hipStream_t stream);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
-// algo 0: scan -> race -> finish (fast path); algo 1: row-serial exact path.
-hipError_t launch_sample(const SampleArgs& a, bool bf16, bool vec, int algo, bool need_race,
+// algo 0: the fused fast path; algo 1: the row-serial exact path.
+hipError_t launch_sample(const SampleArgs& a, bool bf16, bool vec, int algo,
                          const KernelEvents* ev, hipStream_t stream);
 
 }  // namespace cds

@@ -74,7 +74,7 @@ __device__ __forceinline__ RowView row_view(const SampleArgs& a, int r) {
 // Smallest fp32 value v with exp(v/T - m) >= min_p (the min-p set is then
 // {z >= v}); -inf when every finite value qualifies.  Same expression as the
 // set definition, evaluated on fp32 values by bisection over order keys.
-__device__ float minp_cut(float zmax, double Td, double m, float min_p) {
+__device__ __forceinline__ float minp_cut(float zmax, double Td, double m, float min_p) {
   const double mp = (double)min_p;
   if (exp((double)(-FLT_MAX) / Td - m) >= mp) return CDS_NEG_INF;
   uint32_t lo = okey(-FLT_MAX), hi = okey(zmax);
@@ -153,8 +153,7 @@ template <int NT>
 struct ExactShared {
   RedScratch<NT> red;
   unsigned long long hist[256];
-  unsigned long long scan[256];
-  unsigned long long wtot[NT / 64];
+  unsigned long long pick_above;
   int32_t pick;
   float fshare;
 };
@@ -171,27 +170,43 @@ __device__ __forceinline__ void for_row4(const RowView& rv, int64_t V, uint32_t&
 
 // hist[256] holds per-digit totals (digit = bucket of values, larger digit =
 // larger values).  Returns the largest digit d with base + (total over digits
-// >= d) >= need, and sets *above = base + total over digits > d.
+// >= d) >= need (digit 0 if there is none), and sets *above = base + total
+// over digits > d.  Wave 0 scans by DPP; lane l owns digits 255-4l .. 252-4l.
+// Called by all NT threads after the histogram is complete.
 template <int NT>
-__device__ int pick_digit(ExactShared<NT>& sh, double need, unsigned long long base,
-                          unsigned long long* above) {
-  if (threadIdx.x < 256) sh.scan[threadIdx.x] = sh.hist[255 - threadIdx.x];
-  if (threadIdx.x == 0) sh.pick = 256;
+__device__ __forceinline__ int pick_digit(ExactShared<NT>& sh, double need,
+                                          unsigned long long base,
+                                          unsigned long long* above) {
+  if (threadIdx.x < 64) {
+    const int l = threadIdx.x;
+    const unsigned long long c1 = sh.hist[255 - 4 * l];
+    const unsigned long long c2 = c1 + sh.hist[254 - 4 * l];
+    const unsigned long long c3 = c2 + sh.hist[253 - 4 * l];
+    const unsigned long long c4 = c3 + sh.hist[252 - 4 * l];
+    const unsigned long long incl = wave_incl_sum(c4);
+    const unsigned long long ex = base + (incl - c4);
+    const unsigned long long hit = __ballot((double)(base + incl) >= need);
+    const int first = hit ? __ffsll((long long)hit) - 1 : 63;
+    if (l == first) {
+      int j;
+      unsigned long long ab;
+      if ((double)(ex + c1) >= need) { j = 0; ab = ex; }
+      else if ((double)(ex + c2) >= need) { j = 1; ab = ex + c1; }
+      else if ((double)(ex + c3) >= need) { j = 2; ab = ex + c2; }
+      else { j = 3; ab = ex + c3; }
+      sh.pick = 255 - 4 * l - j;
+      sh.pick_above = ab;
+    }
+  }
   __syncthreads();
-  block_scan_inplace<NT>(
-      sh.scan, 256, 0ull, [](unsigned long long x, unsigned long long y) { return x + y; },
-      sh.wtot);
-  if (threadIdx.x < 256 && (double)(base + sh.scan[threadIdx.x]) >= need)
-    atomicMin(&sh.pick, (int)threadIdx.x);
+  const int d = sh.pick;
+  *above = sh.pick_above;
   __syncthreads();
-  const int i = sh.pick < 256 ? sh.pick : 255;
-  *above = base + (i > 0 ? sh.scan[i - 1] : 0ull);
-  __syncthreads();
-  return 255 - i;
+  return d;
 }
 
 template <int NT, bool BF16, bool VEC>
-__device__ void row_exact(const SampleArgs& a, int r, ExactShared<NT>& sh) {
+__device__ __forceinline__ void row_exact(const SampleArgs& a, int r, ExactShared<NT>& sh) {
   const RowParams rp = a.rows[r];
   const RowView rv = row_view<BF16>(a, r);
   const int64_t V = a.V;
@@ -339,103 +354,114 @@ __global__ __launch_bounds__(NT) void exact_kernel(const SampleArgs a) {
 }
 
 // ============================================================================
-// fast path, kernel 1: scan (one HBM pass per slice, register resident)
+// fast path: one kernel, 2*B*P workgroups, two kinds of task
 // ============================================================================
-template <int NT, int E4, bool BF16, bool VEC>
-__global__ __launch_bounds__(NT) void scan_kernel(const SampleArgs a) {
-  __shared__ RedScratch<NT> red;
-  __shared__ unsigned long long s_hist[NBINS + 32];
-  const int r = blockIdx.y, sl = blockIdx.x, tid = threadIdx.x;
-  const RowParams rp = a.rows[r];
-  const bool greedy = (rp.flags & ROW_GREEDY) != 0;
-  const bool hist = !greedy && (rp.flags & (ROW_TOPK | ROW_TOPP));
-  const int64_t lo = (int64_t)sl * a.S;
-  const int64_t hi = min(lo + a.S, (int64_t)a.V);
-  const RowView rv = row_view<BF16>(a, r);
+//
+// Blocks [0, B*P): scan task for slice (block % P) of row (block / P).  Streams
+//   the slice into registers; reduces max, argmax and the non-finite flag;
+//   builds either the histogram (rows with a top-k or top-p cut) or sum exp;
+//   writes the slice summary and takes the row's arrival ticket.  The last
+//   slice of a row to arrive merges the summaries into the row's plan (greedy,
+//   invalid and overflow rows get their output here) and raises the row's
+//   ready flag.
+// Blocks [B*P, 2*B*P): race task for the same slice of row block/P - B
+//   (sampled rows only).  Waits for the row's plan, re-reads the slice (just
+//   read by the scan task, so it comes from the caches), races the tokens
+//   that are surely in the final set, stages the boundary-bin tokens in LDS
+//   and copies them to the slice's own list; then takes the row's done
+//   ticket.  The last race task of a row resolves the boundary list
+//   (exact top-k value and top-p cut by radix selects), races the surviving
+//   boundary tokens, merges the slices' top two and writes the output; rows
+//   the plan could not handle take the row-serial exact path there.
+//
+// Race tasks follow every scan task in dispatch order, so while early rows
+// race, later rows still stream from HBM, and a race task's wait ends once
+// the scans of its row, dispatched before it, complete.  The wait is still
+// bounded by wall-clock time: a task that gives up marks the row and the
+// finisher then runs the exact path, so results never depend on timing.
+//
+// The row's counters carry the call's generation number in their high half:
+// a counter left by another call reads as zero, so nothing needs resetting
+// between calls (and a task that gave up cannot disturb a later call).
 
-  float x[E4][4];
-  uint32_t nonfin = 0;
-  load_chunks<NT, E4, BF16, VEC>(rv, lo, hi, 0, x, nonfin);
+// ---- cross-workgroup data and counters ----------------------------------------
+// Everything one workgroup hands to another goes through agent-coherent
+// accesses (relaxed agent-scope atomic loads and stores: "sc1" on gfx950),
+// never through plain stores that could sit in one XCD's L2.  A producer
+// waits for its own stores to complete (vm_drain) before the ticket or flag
+// that publishes them, and a consumer issues its loads only after it has seen
+// that ticket or flag.  This avoids agent-scope release / acquire fences,
+// which write back or invalidate a whole L2 each time.
+__device__ __forceinline__ void st_u32(void* p, uint32_t v) {
+  __hip_atomic_store(static_cast<uint32_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void st_u64(void* p, uint64_t v) {
+  __hip_atomic_store(static_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_u32(const void* p) {
+  return __hip_atomic_load(static_cast<const uint32_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_u64(const void* p) {
+  return __hip_atomic_load(static_cast<uint64_t*>(const_cast<void*>(p)), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+template <typename T>
+__device__ __forceinline__ void st_obj(T* dst, const T& v) {
+  static_assert(sizeof(T) % 8 == 0, "8-byte words");
+  uint64_t w[sizeof(T) / 8];
+  __builtin_memcpy(w, &v, sizeof(T));
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(T) / 8); ++k) st_u64(reinterpret_cast<uint64_t*>(dst) + k, w[k]);
+}
+template <typename T>
+__device__ __forceinline__ T ld_obj(const T* src) {
+  static_assert(sizeof(T) % 8 == 0, "8-byte words");
+  uint64_t w[sizeof(T) / 8];
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(T) / 8); ++k) w[k] = ld_u64(reinterpret_cast<const uint64_t*>(src) + k);
+  T v;
+  __builtin_memcpy(&v, w, sizeof(T));
+  return v;
+}
+// Wait until this wave's memory operations have completed.
+__device__ __forceinline__ void vm_drain() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
 
-  // max, then the lowest index holding it (searched only by threads that hold it)
-  float lm = CDS_NEG_INF;
-#pragma unroll
-  for (int i = 0; i < E4; ++i)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) lm = fmaxf(lm, x[i][q]);
-  const float zm = block_max_f32<NT>(lm, red);
-  int32_t am = INT_MAX;
-  if (zm != CDS_NEG_INF && lm == zm) {
-#pragma unroll
-    for (int i = E4 - 1; i >= 0; --i)
-#pragma unroll
-      for (int q = 3; q >= 0; --q)
-        if (x[i][q] == zm) am = (int32_t)(lo + 4 * ((int64_t)i * NT + tid) + q);
-  }
-  am = block_min_i32<NT>(am, red);
-  nonfin = block_or_u32<NT>(nonfin, red);
-
-  const int64_t slot = (int64_t)r * a.P + sl;
-  uint32_t flags = nonfin ? SLICE_NONFINITE : 0u;
-  double se = 0.0;
-  float kmax = 0.0f;
-  if (!hist) {
-    // sum exp((z - zmax) / T_eff): the row's log-partition for the logprob
-    const float c = (greedy ? 1.0f : (float)(1.0 / (double)rp.temperature)) * kLog2e;
-    if (zm != CDS_NEG_INF) {
-#pragma unroll
-      for (int i = 0; i < E4; ++i) {
-        float part = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) part += __builtin_amdgcn_exp2f((x[i][q] - zm) * c);
-        se += (double)part;
-      }
-    }
-    se = block_sum_f64<NT>(se, red);
-  } else if (zm != CDS_NEG_INF) {
-    // histogram of the values below the slice maximum, bins aligned to delta
-    const BinGeom g = bin_geom(rp.temperature);
-    kmax = floorf(zm * g.inv_delta);
-    if (!(fabsf(kmax) < 4194304.0f)) {
-      flags |= SLICE_BINS_LOST;  // bin indices would not be exact: row takes the exact path
-    } else {
-      for (int b = tid; b < NBINS + 32; b += NT) s_hist[b] = 0ull;
-      __syncthreads();
-      // tokens outside the window (and -inf) land in 32 per-lane sink bins:
-      // no branch per token
-      const int sink = NBINS + (tid & 31);
-#pragma unroll
-      for (int i = 0; i < E4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float y = x[i][q] * g.inv_delta;
-          const float kf = floorf(y);
-          const float rbf = kmax - kf;
-          const int rb = (rbf >= 0.0f && rbf < (float)NBINS) ? (int)rbf : sink;
-          const float w = __builtin_amdgcn_exp2f(fmaf(y - kf, g.c_bin, -g.c_bin));
-          const uint32_t fix = (uint32_t)(w * 2147483648.0f);
-          atomicAdd(&s_hist[rb], (1ull << kCountShift) | (unsigned long long)fix);
-        }
-      __syncthreads();
-      unsigned long long* gh = a.hist + slot * NBINS;
-      for (int b = tid; b < NBINS; b += NT) gh[b] = s_hist[b];
-    }
-  }
-  if (tid == 0) {
-    SliceHead h;
-    h.zmax = zm;
-    h.arg = (zm == CDS_NEG_INF) ? -1 : am;
-    h.flags = flags;
-    h.kmax = kmax;
-    h.sumexp = se;
-    h.pad[0] = h.pad[1] = 0u;
-    a.heads[slot] = h;
+// Add `n` to the generation-tagged counter *w (high half: generation, low
+// half: count; another generation's count reads as zero); returns the count
+// before the addition.
+__device__ __forceinline__ uint32_t gen_add(unsigned long long* w, uint32_t gen, uint32_t n) {
+  unsigned long long old = ld_u64(w);
+  while (true) {
+    const uint32_t cnt = (uint32_t)(old >> 32) == gen ? (uint32_t)old : 0u;
+    const unsigned long long nw = ((unsigned long long)gen << 32) | (unsigned long long)(cnt + n);
+    if (__hip_atomic_compare_exchange_weak(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT))
+      return cnt;
   }
 }
 
-// ============================================================================
-// fast path, kernel 2: plan (one workgroup per row)
-// ============================================================================
+__device__ __forceinline__ uint32_t gen_count(const unsigned long long* w, uint32_t gen) {
+  const unsigned long long v = ld_u64(w);
+  return (uint32_t)(v >> 32) == gen ? (uint32_t)v : 0u;
+}
+
+// Spin until *p == gen, at most `limit` ticks of the constant-rate wall
+// clock; false on timeout.
+__device__ __forceinline__ bool gen_wait(const uint32_t* p, uint32_t gen, uint64_t limit) {
+  const uint64_t t0 = wall_clock64();
+  while (ld_u32(p) != gen) {
+    if (wall_clock64() - t0 > limit) return false;
+    __builtin_amdgcn_s_sleep(4);
+  }
+  return true;
+}
+
+// ---- phase 2: the plan ----------------------------------------------------------
 template <int NT>
 struct PlanShared {
   SliceHead head[kMaxSlices];
@@ -447,59 +473,71 @@ struct PlanShared {
   uint32_t wtot_u[NT / 64];
   int idx[3];
   int mode, inK, k_rank, rb12;
-  uint32_t lost;
-  float zmax, zcut1, kmax;
+  float zmax, zcut1;
   int32_t arg;
   double m, log_z, tlo, thi;
 };
 
+// Merge the slice summaries of row r into its plan (all NT threads).  Writes
+// the output of rows that end here (greedy, no finite token, non-finite
+// token) and the plan to a.plans[r] and to *out (LDS).
 template <int NT>
-__global__ __launch_bounds__(NT) void plan_kernel(const SampleArgs a) {
-  __shared__ PlanShared<NT> ps;
-  const int r = blockIdx.x, tid = threadIdx.x, P = a.P;
+__device__ __forceinline__ void plan_row(const SampleArgs& a, int r, PlanShared<NT>& ps, Plan* out) {
+  const int tid = threadIdx.x, P = a.P;
   const RowParams rp = a.rows[r];
   const bool greedy = (rp.flags & ROW_GREEDY) != 0;
   const bool topk = (rp.flags & ROW_TOPK) != 0, topp = (rp.flags & ROW_TOPP) != 0;
   const bool hist = !greedy && (topk || topp);
   const double Td = (double)rp.temperature;
-  if (tid < P) ps.head[tid] = a.heads[(int64_t)r * P + tid];
-  __syncthreads();
-  if (tid == 0) {
+  // merge the slice heads: wave 0, lane j holds slice j (P <= 64)
+  if (tid < 64) {
     float zm = CDS_NEG_INF;
     int32_t am = INT_MAX;
     uint32_t fl = 0;
-    for (int j = 0; j < P; ++j) {
-      const SliceHead& h = ps.head[j];
-      fl |= h.flags;
-      if (h.zmax != CDS_NEG_INF && (h.zmax > zm || (h.zmax == zm && h.arg < am))) {
-        zm = h.zmax;
-        am = h.arg;
+    double hs = 0.0;
+    if (tid < P) {
+      const SliceHead h = ld_obj(&a.heads[(int64_t)r * P + tid]);
+      ps.head[tid] = h;
+      zm = h.zmax;
+      am = h.zmax == CDS_NEG_INF ? INT_MAX : h.arg;
+      fl = h.flags;
+      hs = h.sumexp;
+    }
+    const float hz = zm;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float z2 = __shfl_xor(zm, o, 64);
+      const int32_t a2 = __shfl_xor(am, o, 64);
+      if (z2 > zm || (z2 == zm && a2 < am)) {
+        zm = z2;
+        am = a2;
       }
+      fl |= __shfl_xor(fl, o, 64);
     }
     const double invTe = greedy ? 1.0 : 1.0 / Td;
-    double Z = 0.0;
-    if (!hist)
-      for (int j = 0; j < P; ++j)
-        if (ps.head[j].zmax != CDS_NEG_INF)
-          Z += ps.head[j].sumexp * exp(((double)ps.head[j].zmax - (double)zm) * invTe);
-    int mode = PLAN_FAST;
-    if (zm == CDS_NEG_INF) {
-      write_out(a, r, -1, CDS_NEG_INF, 2);
-      mode = PLAN_DONE;
-    } else if (fl & SLICE_NONFINITE) {
-      write_out(a, r, -1, __builtin_nanf(""), 1);
-      mode = PLAN_DONE;
-    } else if (greedy) {
-      write_out(a, r, am, (float)(-log(Z)), 0);
-      mode = PLAN_DONE;
-    } else if (fl & SLICE_BINS_LOST) {
-      mode = PLAN_SLOW;
+    double Z = (!hist && hz != CDS_NEG_INF) ? hs * exp(((double)hz - (double)zm) * invTe) : 0.0;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) Z += __shfl_xor(Z, o, 64);
+    if (tid == 0) {
+      int mode = PLAN_FAST;
+      if (zm == CDS_NEG_INF) {
+        write_out(a, r, -1, CDS_NEG_INF, 2);
+        mode = PLAN_DONE;
+      } else if (fl & SLICE_NONFINITE) {
+        write_out(a, r, -1, __builtin_nanf(""), 1);
+        mode = PLAN_DONE;
+      } else if (greedy) {
+        write_out(a, r, am, (float)(-log(Z)), 0);
+        mode = PLAN_DONE;
+      } else if (fl & SLICE_BINS_LOST) {
+        mode = PLAN_SLOW;
+      }
+      ps.mode = mode;
+      ps.zmax = zm;
+      ps.arg = am;
+      ps.m = (double)zm / Td;
+      ps.log_z = hist ? 0.0 : log(Z);
     }
-    ps.mode = mode;
-    ps.zmax = zm;
-    ps.arg = am;
-    ps.m = (double)zm / Td;
-    ps.log_z = log(Z);
   }
   __syncthreads();
   // min-p: the smallest fp32 value whose weight reaches min_p (wave 0)
@@ -514,7 +552,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(const SampleArgs a) {
   }
   __syncthreads();
 
-  auto write_plan = [&](int mode) {
+  auto base_plan = [&](int mode) {
     Plan pl = {};
     pl.mode = mode;
     pl.arg = ps.arg;
@@ -528,7 +566,11 @@ __global__ __launch_bounds__(NT) void plan_kernel(const SampleArgs a) {
     return pl;
   };
   if (ps.mode != PLAN_FAST || !hist) {
-    if (tid == 0) a.plans[r] = write_plan(ps.mode);
+    if (tid == 0) {
+      const Plan pl = base_plan(ps.mode);
+      st_obj(&a.plans[r], pl);
+      *out = pl;
+    }
     return;
   }
 
@@ -540,15 +582,30 @@ __global__ __launch_bounds__(NT) void plan_kernel(const SampleArgs a) {
     ps.accc[b] = 0u;
   }
   __syncthreads();
-#pragma unroll 4
-  for (int e = tid; e < P * NBINS; e += NT) {
-    const int j = e / NBINS, sb = e - j * NBINS;
-    const unsigned long long v = a.hist[((int64_t)r * P + j) * NBINS + sb];
-    if (v == 0ull || ps.head[j].zmax == CDS_NEG_INF) continue;
-    const float rowbin = (kmax - ps.head[j].kmax) + (float)sb;
-    if (rowbin >= (float)NBINS) continue;
-    atomicAdd(&ps.accc[(int)rowbin], (uint32_t)(v >> kCountShift));
-    atomicAdd(&ps.accm[(int)rowbin], v & ((1ull << kCountShift) - 1ull));
+  {
+    // up to 18 loads in flight per thread (all of them for P <= 8)
+    constexpr int U = 18;
+    const int total = P * NBINS;
+    const unsigned long long* gh = a.hist + (int64_t)r * P * NBINS;
+    for (int e0 = tid; e0 < total; e0 += U * NT) {
+      unsigned long long v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * NT;
+        v[u] = e < total ? ld_u64(gh + e) : 0ull;
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int e = e0 + u * NT;
+        if (e >= total || v[u] == 0ull) continue;
+        const int j = e / NBINS, sb = e - j * NBINS;
+        if (ps.head[j].zmax == CDS_NEG_INF) continue;
+        const float rowbin = (kmax - ps.head[j].kmax) + (float)sb;
+        if (!(rowbin >= 0.0f && rowbin < (float)NBINS)) continue;
+        atomicAdd(&ps.accc[(int)rowbin], (uint32_t)(v[u] >> kCountShift));
+        atomicAdd(&ps.accm[(int)rowbin], v[u] & ((1ull << kCountShift) - 1ull));
+      }
+    }
   }
   __syncthreads();
   const double m = ps.m;
@@ -559,10 +616,11 @@ __global__ __launch_bounds__(NT) void plan_kernel(const SampleArgs a) {
     ps.md[b] = (double)ps.accm[b] * 0x1p-31 * exp(top / Td - m);
   }
   __syncthreads();
-  block_scan_inplace<NT>(ps.cumc, NBINS, 0u, [](uint32_t x, uint32_t y) { return x + y; },
-                         ps.wtot_u);
-  block_scan_inplace<NT>(ps.md, NBINS, 0.0, [](double x, double y) { return x + y; },
-                         ps.wtot_d);
+  // cumulative counts and masses from the top, both by wave 0
+  constexpr int KB = (NBINS + 63) / 64;
+  wave0_scan_inplace<KB>(ps.cumc, NBINS);
+  wave0_scan_inplace<KB>(ps.md, NBINS);
+  __syncthreads();
   if (tid < 3) ps.idx[tid] = NBINS;
   __syncthreads();
   if (topk)
@@ -614,7 +672,7 @@ __global__ __launch_bounds__(NT) void plan_kernel(const SampleArgs a) {
     uint32_t uexp = topp ? cnt_range(rb3_lo, rb3_hi) : 0u;
     if (inK >= 0 && !(topp && inK >= rb3_lo && inK <= rb3_hi)) uexp += cnt_range(inK, inK);
     auto edge = [&](int b) { return (kmax - (float)b) * g.delta; };  // bottom of bin b (exact)
-    Plan pl = write_plan(uexp > (uint32_t)UCAP ? PLAN_SLOW : PLAN_FAST);
+    Plan pl = base_plan(uexp > (uint32_t)UCAP ? PLAN_SLOW : PLAN_FAST);
     pl.z_sure = umin < NBINS ? edge(umin - 1) : edge(NBINS - 1);
     if (topp) {
       pl.a_lo = edge(rb3_hi);
@@ -631,106 +689,12 @@ __global__ __launch_bounds__(NT) void plan_kernel(const SampleArgs a) {
     const int end = inK >= 0 ? inK - 1 : NBINS - 1;
     pl.m_mid = (topp && end > rb3_hi) ? ps.md[end] - ps.md[rb3_hi] : 0.0;
     pl.log_z = ps.log_z;
-    a.plans[r] = pl;
+    st_obj(&a.plans[r], pl);
+    *out = pl;
   }
 }
 
-// ============================================================================
-// fast path, kernel 3: race over the sure tokens, compact the boundary tokens
-// ============================================================================
-template <int NT, int E4, bool BF16, bool VEC>
-__global__ __launch_bounds__(NT) void race_kernel(const SampleArgs a) {
-  __shared__ RedScratch<NT> red;
-  const int r = blockIdx.y, sl = blockIdx.x, tid = threadIdx.x;
-  const Plan pl = a.plans[r];
-  if (pl.mode != PLAN_FAST) return;
-  const RowParams rp = a.rows[r];
-  const int64_t lo = (int64_t)sl * a.S;
-  const int64_t hi = min(lo + a.S, (int64_t)a.V);
-  const RowView rv = row_view<BF16>(a, r);
-  const RaceCtx c = make_race_ctx(rp, pl.zmax);
-  const float zs = fmaxf(pl.z_sure, pl.zcut1);
-  const bool has_u = pl.a_lo < pl.a_hi || pl.k_lo < pl.k_hi;
-  Top2 b = top2_init();
-  uint64_t* ul = a.ulist + (int64_t)r * UCAP;
-  uint32_t* ucount = &a.sync[r].ucount;
-  const int lane = tid & 63;
-  uint32_t nonfin = 0;
-  constexpr int G = E4 < 4 ? E4 : 4;
-#pragma unroll 1
-  for (int g = 0; g < E4; g += G) {
-    float x[G][4];
-    load_chunks<NT, G, BF16, VEC>(rv, lo, hi, g, x, nonfin);
-#pragma unroll
-    for (int i = 0; i < G; ++i) {
-      const int64_t t0 = lo + 4 * ((int64_t)(g + i) * NT + tid);
-      bool need = false;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        need |= (x[i][q] >= zs && x[i][q] != CDS_NEG_INF &&
-                 race32_hopeful(b, x[i][q], c.zmax, c.invT32));
-      if (need) {
-        const uint4 blk = race_block(c, t0);
-        const uint32_t xs[4] = {blk.x, blk.y, blk.z, blk.w};
-#pragma unroll
-        for (int q = 0; q < 4; ++q)
-          if (x[i][q] >= zs && x[i][q] != CDS_NEG_INF)
-            race32(b, x[i][q], (int32_t)(t0 + q), xs[q], c.zmax, c.invT32);
-      }
-      if (has_u) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float v = x[i][q];
-          const bool isU = v < zs && v >= pl.zcut1 &&
-                           ((v >= pl.a_lo && v < pl.a_hi) || (v >= pl.k_lo && v < pl.k_hi));
-          const unsigned long long msk = __ballot(isU);
-          if (msk) {
-            const int leader = __ffsll((long long)msk) - 1;
-            uint32_t base = 0;
-            if (lane == leader) base = atomicAdd(ucount, (uint32_t)__popcll(msk));
-            base = __shfl(base, leader, 64);
-            if (isU) {
-              const uint32_t pos = base + (uint32_t)__popcll(msk & __lanemask_lt());
-              if (pos < (uint32_t)UCAP)
-                ul[pos] = ((uint64_t)okey(v + 0.0f) << 32) |
-                          (uint64_t)(0xFFFFFFFFu - (uint32_t)(t0 + q));
-            }
-          }
-        }
-      }
-    }
-  }
-  block_top2<NT>(b, red);
-  if (tid == 0) {
-    SliceBest sb;
-    sb.k1 = b.k1;
-    sb.t1 = b.t1;
-    sb.z1 = b.z1;
-    sb.k2 = b.k2;
-    a.bests[(int64_t)r * a.P + sl] = sb;
-  }
-}
-
-// ============================================================================
-// fast path, kernel 4: exact cuts on the boundary list, race it, merge, output
-// ============================================================================
-template <int NT>
-struct FinishShared {
-  unsigned long long key[UCAP];
-  double w[UCAP];
-  int32_t g[UCAP];
-  double wtot_d[NT / 64];
-  int32_t wtot_i[NT / 64];
-  RedScratch<NT> red;
-  uint32_t z3key;
-  int32_t lastA;
-  int32_t has3;
-  int32_t fail;
-  int32_t ambiguous;
-  float zfinal;
-  float k1;
-};
-
+// ---- phase 4: the boundary list --------------------------------------------------
 __device__ __forceinline__ float ukey_z(unsigned long long k) { return from_okey((uint32_t)(k >> 32)); }
 __device__ __forceinline__ int32_t ukey_t(unsigned long long k) {
   return (int32_t)(0xFFFFFFFFu - (uint32_t)k);
@@ -739,11 +703,10 @@ __device__ __forceinline__ int32_t ukey_t(unsigned long long k) {
 // fp64 race over {z >= zfinal} for tokens whose fp32 key reaches k_floor: the
 // tie-breaker when the fp32 top two are within the fp32 error.
 template <int NT, bool BF16, bool VEC>
-__device__ Best exact_rerace(const SampleArgs& a, int r, float zfinal, float k_floor,
-                             RedScratch<NT>& red) {
+__device__ __forceinline__ Best exact_rerace(const SampleArgs& a, int r, const Plan& pl, float zfinal,
+                             float k_floor, RedScratch<NT>& red) {
   const RowParams rp = a.rows[r];
   const RowView rv = row_view<BF16>(a, r);
-  const Plan pl = a.plans[r];
   const RaceCtx c = make_race_ctx(rp, pl.zmax);
   Best b = best_init();
   uint32_t nonfin = 0;
@@ -774,158 +737,447 @@ __device__ Best exact_rerace(const SampleArgs& a, int r, float zfinal, float k_f
   return b;
 }
 
+// Resolve the boundary list of row r and write its output (all NT threads of
+// the finisher).  The row's list is gathered from the slices' lists into LDS.
+// Returns false when the row must take the exact path.
 template <int NT, bool BF16, bool VEC>
-__global__ __launch_bounds__(NT) void finish_kernel(const SampleArgs a) {
-  __shared__ FinishShared<NT> fs;
-  __shared__ ExactShared<NT> es;
-  const int r = blockIdx.x, tid = threadIdx.x;
-  const Plan pl = a.plans[r];
-  if (pl.mode != PLAN_FAST && pl.mode != PLAN_SLOW) return;
-  const uint32_t n_raw = a.sync[r].ucount;
-  __syncthreads();
-  if (tid == 0) a.sync[r].ucount = 0u;  // ready for the next call
-  if (pl.mode == PLAN_SLOW || n_raw > (uint32_t)UCAP) {
-    row_exact<NT, BF16, VEC>(a, r, es);
-    if (tid == 0) a.plans[r].path = PATH_EXACT;
-    return;
-  }
+__device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Plan& pl,
+                                           ExactShared<NT>& sh, uint64_t* ul, int32_t* off,
+                                           RedScratch<NT>& red) {
+  const int tid = threadIdx.x, P = a.P;
   const RowParams rp = a.rows[r];
   const double Td = (double)rp.temperature;
-  const int n = (int)n_raw;
-  int N = 1;
-  while (N < n) N <<= 1;
-  for (int i = tid; i < N; i += NT) fs.key[i] = i < n ? a.ulist[(int64_t)r * UCAP + i] : 0ull;
-  if (tid == 0) {
-    fs.z3key = 0xFFFFFFFFu;
-    fs.lastA = -1;
-    fs.has3 = 0;
-    fs.fail = 0;
-    fs.ambiguous = 0;
+  // the slices' top two and list lengths; list offsets by a prefix sum
+  Top2 b = top2_init();
+  if (tid < 64) {  // P <= 64: one wave
+    uint32_t cnt = 0;
+    if (tid < P) {
+      const SliceBest sb = ld_obj(&a.bests[(int64_t)r * P + tid]);
+      b.k1 = sb.k1;
+      b.t1 = sb.t1;
+      b.z1 = sb.z1;
+      b.k2 = sb.k2;
+      cnt = sb.ucnt > (uint32_t)SCAP ? (uint32_t)UCAP + 1u : sb.ucnt;
+    }
+    uint32_t incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      const uint32_t y = __shfl_up(incl, o, 64);
+      if (tid >= o) incl += y;
+    }
+    off[tid + 1] = (int32_t)min(incl, (uint32_t)UCAP + 1u);
+    if (tid == 0) off[0] = 0;
   }
   __syncthreads();
-  // bitonic sort, descending: larger value first, then lower token index
-  for (int k = 2; k <= N; k <<= 1)
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < N; i += NT) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const unsigned long long p = fs.key[i], q = fs.key[ixj];
-          const bool desc = (i & k) == 0;
-          if (desc ? (p < q) : (p > q)) {
-            fs.key[i] = q;
-            fs.key[ixj] = p;
-          }
-        }
+  const int n = off[P];
+  if (n > UCAP) return false;
+  // gather the slices' lists into LDS, every load in flight at once
+#pragma unroll
+  for (int k = 0; k < UCAP / NT; ++k) {
+    const int i = tid + k * NT;
+    if (i < n) {
+      int lo = 0, hi = P;  // the slice j with off[j] <= i < off[j+1]
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (off[mid] <= i) lo = mid; else hi = mid;
       }
-      __syncthreads();
+      ul[i] = ld_u64(a.ulist + ((int64_t)r * P + lo) * SCAP + (i - off[lo]));
     }
+  }
+  __syncthreads();
 
-  // exact top-k value: the k_rank-th largest token of the boundary bin
+  // exact top-k value: the k_rank-th largest list value inside [k_lo, k_hi)
   float zc12 = pl.zcut1;
   if (pl.k_rank > 0) {
-    int ch = 0, cl = 0;
-    for (int i = tid; i < n; i += NT) {
-      const float z = ukey_z(fs.key[i]);
-      ch += (z >= pl.k_hi);
-      cl += (z >= pl.k_lo);
+    const float k_lo = pl.k_lo, k_hi = pl.k_hi;
+    auto inK = [&](unsigned long long e) {
+      const float z = ukey_z(e);
+      return z >= k_lo && z < k_hi;
+    };
+    int cnt = 0;
+#pragma unroll 1
+    for (int i = tid; i < n; i += NT) cnt += inK(ul[i]) ? 1 : 0;
+    cnt = block_sum_i32<NT>(cnt, red);
+    if (cnt < pl.k_rank) return false;
+    uint32_t prefix = 0, pmask = 0;
+    unsigned long long krem = (unsigned long long)pl.k_rank;
+#pragma unroll 1
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      if (tid < 256) sh.hist[tid] = 0ull;
+      __syncthreads();
+#pragma unroll 1
+      for (int i = tid; i < n; i += NT) {
+        const unsigned long long e = ul[i];
+        const uint32_t u = (uint32_t)(e >> 32);
+        if (inK(e) && (u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & 255u], 1ull);
+      }
+      __syncthreads();
+      unsigned long long above;
+      const int d = pick_digit<NT>(sh, (double)krem, 0ull, &above);
+      krem -= above;
+      prefix |= (uint32_t)d << shift;
+      pmask |= 255u << shift;
     }
-    ch = block_sum_i32<NT>(ch, fs.red);
-    cl = block_sum_i32<NT>(cl, fs.red);
-    const int idx = ch + pl.k_rank - 1;
-    if (idx < cl) zc12 = fmaxf(zc12, ukey_z(fs.key[idx]));
+    zc12 = fmaxf(zc12, from_okey(prefix));
   }
   float zfin = zc12;
 
-  // exact top-p cut: fp64 masses in sorted order, tie groups all in or out
+  // exact top-p cut: the largest value v in [a_lo, a_hi) whose cumulative mass
+  // (the sure region, plus every list token >= v that survived top-k) reaches
+  // top_p * M2.  List masses are exp((z - a_hi)/T) (arguments <= 0, fp32)
+  // times one fp64 factor, summed in fixed point (exact in any order).
   if (pl.topp) {
+    const float zref = pl.a_hi, a_lo = pl.a_lo, zc = zc12;
+    const float c32 = (float)(1.4426950408889634 / Td);
+    const double F = exp((double)zref / Td - pl.m);
+    constexpr double kFix = 0x1p46;  // <= 4096 weights <= 1 fit in 64 bits
+    auto wfix = [=](float z) -> unsigned long long {
+      return z >= zc ? (unsigned long long)((double)__builtin_amdgcn_exp2f((z - zref) * c32) * kFix)
+                     : 0ull;
+    };
+    unsigned long long mu = 0, m_in = 0;
+#pragma unroll 1
     for (int i = tid; i < n; i += NT) {
-      const float z = ukey_z(fs.key[i]);
-      fs.w[i] = (z >= zc12) ? exp((double)z / Td - pl.m) : 0.0;
-      fs.g[i] = (i == 0 || z != ukey_z(fs.key[i - 1])) ? i : 0;
+      const float z = ukey_z(ul[i]);
+      const unsigned long long w = wfix(z);
+      mu += w;
+      if (z >= a_lo) m_in += w;
     }
-    __syncthreads();
-    block_scan_inplace<NT>(fs.w, n, 0.0, [](double x, double y) { return x + y; }, fs.wtot_d);
-    block_scan_inplace<NT>(fs.g, n, 0, [](int32_t x, int32_t y) { return max(x, y); },
-                           fs.wtot_i);
-    const double M2 = pl.m_sure + pl.m_mid + (n > 0 ? fs.w[n - 1] : 0.0);
-    const double target = pl.p * M2;
-    for (int i = tid; i < n; i += NT) {
-      const float z = ukey_z(fs.key[i]);
-      if (!(z >= pl.a_lo && z < pl.a_hi && z >= zc12)) continue;
-      atomicMax(&fs.lastA, i);
-      const int g = fs.g[i];
-      const double above = pl.m_sure + (g > 0 ? fs.w[g - 1] : 0.0);
-      if (above < target) {
-        atomicMin(&fs.z3key, okey(z));
-        fs.has3 = 1;
+    mu = block_sum_u64<NT>(mu, red);
+    m_in = block_sum_u64<NT>(m_in, red);
+    const double M2 = pl.m_sure + pl.m_mid + F * ((double)mu / kFix);
+    // the list mass (in fixed units) the cut must reach above the sure region
+    const double need = (pl.p * M2 - pl.m_sure) / F * kFix;
+    if (!(need > 0.0)) return false;         // the cut lies above the range
+    if ((double)m_in < need) return false;   // ... or below it
+    uint32_t prefix = 0, pmask = 0;
+    unsigned long long base = 0;
+#pragma unroll 1
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      if (tid < 256) sh.hist[tid] = 0ull;
+      __syncthreads();
+#pragma unroll 1
+      for (int i = tid; i < n; i += NT) {
+        const unsigned long long e = ul[i];
+        const uint32_t u = (uint32_t)(e >> 32);
+        const float z = ukey_z(e);
+        if (z >= a_lo && (u & pmask) == prefix) {
+          const unsigned long long w = wfix(z);
+          if (w) atomicAdd(&sh.hist[(u >> shift) & 255u], w);
+        }
       }
+      __syncthreads();
+      unsigned long long above;
+      const int d = pick_digit<NT>(sh, need, base, &above);
+      base = above;
+      prefix |= (uint32_t)d << shift;
+      pmask |= 255u << shift;
     }
-    __syncthreads();
-    if (tid == 0) {
-      if (!fs.has3) {
-        fs.fail = 1;  // the cut lies above the boundary range
-      } else if (fs.lastA >= 0) {
-        const float zl = ukey_z(fs.key[fs.lastA]);
-        if (zl >= from_okey(fs.z3key) && pl.m_sure + fs.w[fs.lastA] < target)
-          fs.fail = 1;  // ... or below it
-      }
-    }
-    __syncthreads();
-    if (!fs.fail) zfin = fmaxf(zfin, from_okey(fs.z3key));
-  }
-  if (fs.fail) {
-    row_exact<NT, BF16, VEC>(a, r, es);
-    if (tid == 0) a.plans[r].path = PATH_EXACT;
-    return;
+    zfin = fmaxf(zfin, from_okey(prefix));
   }
 
-  // race the boundary tokens that survive, merge with the slices' top two
+  // race the list tokens that survive, merge with the slices' top two
   const RaceCtx c = make_race_ctx(rp, pl.zmax);
-  Top2 b = top2_init();
+#pragma unroll 1
   for (int i = tid; i < n; i += NT) {
-    const float z = ukey_z(fs.key[i]);
+    const unsigned long long e = ul[i];
+    const float z = ukey_z(e);
     if (!(z >= zfin)) continue;
-    const int32_t t = ukey_t(fs.key[i]);
+    const int32_t t = ukey_t(e);
     if (!race32_hopeful(b, z, c.zmax, c.invT32)) continue;
     const uint4 blk = race_block(c, (int64_t)(t & ~3));
     const int w = t & 3;
     const uint32_t xw = w == 0 ? blk.x : (w == 1 ? blk.y : (w == 2 ? blk.z : blk.w));
     race32(b, z, t, xw, c.zmax, c.invT32);
   }
-  block_top2<NT>(b, fs.red);
-  if (tid == 0) {
-    for (int j = 0; j < a.P; ++j) {
-      const SliceBest sb = a.bests[(int64_t)r * a.P + j];
-      Top2 o;
-      o.k1 = sb.k1;
-      o.t1 = sb.t1;
-      o.z1 = sb.z1;
-      o.k2 = sb.k2;
-      top2_merge(b, o);
-    }
-    const float zs = fmaxf(pl.z_sure, pl.zcut1);
-    fs.zfinal = (pl.topp || pl.k_rank > 0) ? zfin : zs;
-    fs.k1 = b.k1;
-    if (b.t1 == INT_MAX) {
-      fs.fail = 1;
-    } else if (!(b.k1 - b.k2 > 2.0f * kRaceEps)) {
-      fs.ambiguous = 1;
-    } else {
+  block_top2<NT>(b, red);
+  if (b.t1 == INT_MAX) return false;
+  if (b.k1 - b.k2 > 2.0f * kRaceEps) {
+    if (tid == 0) {
       write_out(a, r, b.t1, (float)((double)b.z1 / Td - pl.m - pl.log_z), 0);
       a.plans[r].path = PATH_FAST;
     }
+    return true;
   }
-  __syncthreads();
-  if (fs.fail) {
-    row_exact<NT, BF16, VEC>(a, r, es);
-    if (tid == 0) a.plans[r].path = PATH_EXACT;
-  } else if (fs.ambiguous) {
-    const Best e = exact_rerace<NT, BF16, VEC>(a, r, fs.zfinal, fs.k1 - 2.0f * kRaceEps, fs.red);
-    if (tid == 0) {
-      write_out(a, r, e.t, (float)((double)e.z / Td - pl.m - pl.log_z), 0);
-      a.plans[r].path = PATH_RERACE;
+  // fp32 top two too close: decide in fp64 over the final set
+  const float zs = fmaxf(pl.z_sure, pl.zcut1);
+  const float zfinal = (pl.topp || pl.k_rank > 0) ? zfin : zs;
+  const Best e = exact_rerace<NT, BF16, VEC>(a, r, pl, zfinal, b.k1 - 2.0f * kRaceEps, red);
+  if (tid == 0) {
+    write_out(a, r, e.t, (float)((double)e.z / Td - pl.m - pl.log_z), 0);
+    a.plans[r].path = PATH_RERACE;
+  }
+  return true;
+}
+
+__device__ __forceinline__ bool is_boundary(float v, float zs, float zc1, float a_lo, float a_hi,
+                                            float k_lo, float k_hi) {
+  return v < zs && v >= zc1 && ((v >= a_lo && v < a_hi) || (v >= k_lo && v < k_hi));
+}
+
+template <int NT>
+union FusedLds {
+  unsigned long long hist[NBINS + 32];
+  PlanShared<NT> plan;
+  struct {
+    ExactShared<NT> ex;
+    uint64_t list[UCAP];
+    int32_t off[kMaxSlices + 1];
+  } fin;
+  uint64_t stage[SCAP];
+};
+
+template <int NT, int E4, bool BF16, bool VEC>
+__device__ __forceinline__ void scan_task(const SampleArgs& a, int r, int sl, FusedLds<NT>& sh,
+                          RedScratch<NT>& red, Plan* s_plan, uint32_t* s_word) {
+  const int tid = threadIdx.x, P = a.P;
+  const RowParams rp = a.rows[r];
+  const bool greedy = (rp.flags & ROW_GREEDY) != 0;
+  const bool hist = !greedy && (rp.flags & (ROW_TOPK | ROW_TOPP));
+  const int64_t lo = (int64_t)sl * a.S;
+  const int64_t hi = min(lo + a.S, (int64_t)a.V);
+  const RowView rv = row_view<BF16>(a, r);
+
+  float x[E4][4];
+  uint32_t nonfin = 0;
+  load_chunks<NT, E4, BF16, VEC>(rv, lo, hi, 0, x, nonfin);
+
+  // max, then the lowest index holding it (searched only by threads that hold it)
+  float lm = CDS_NEG_INF;
+#pragma unroll
+  for (int i = 0; i < E4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) lm = fmaxf(lm, x[i][q]);
+  const float zm = block_max_f32<NT>(lm, red);
+  int32_t am = INT_MAX;
+  if (zm != CDS_NEG_INF && lm == zm) {
+#pragma unroll
+    for (int i = E4 - 1; i >= 0; --i)
+#pragma unroll
+      for (int q = 3; q >= 0; --q)
+        if (x[i][q] == zm) am = (int32_t)(lo + 4 * ((int64_t)i * NT + tid) + q);
+  }
+  am = block_min_i32<NT>(am, red);
+  nonfin = block_or_u32<NT>(nonfin, red);
+
+  const int64_t slot = (int64_t)r * P + sl;
+  uint32_t flags = nonfin ? SLICE_NONFINITE : 0u;
+  double se = 0.0;
+  float kmax = 0.0f;
+  if (!hist) {
+    // sum exp((z - zmax) / T_eff): the row's log-partition for the logprob
+    const float cexp = (greedy ? 1.0f : (float)(1.0 / (double)rp.temperature)) * kLog2e;
+    if (zm != CDS_NEG_INF) {
+#pragma unroll
+      for (int i = 0; i < E4; ++i) {
+        float part = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) part += __builtin_amdgcn_exp2f((x[i][q] - zm) * cexp);
+        se += (double)part;
+      }
+    }
+    se = block_sum_f64<NT>(se, red);
+  } else if (zm != CDS_NEG_INF) {
+    // histogram of the values below the slice maximum, bins aligned to delta
+    const BinGeom g = bin_geom(rp.temperature);
+    kmax = floorf(zm * g.inv_delta);
+    if (!(fabsf(kmax) < 4194304.0f)) {
+      flags |= SLICE_BINS_LOST;  // bin indices would not be exact: row takes the exact path
+    } else {
+      for (int b = tid; b < NBINS + 32; b += NT) sh.hist[b] = 0ull;
+      __syncthreads();
+      // tokens outside the window (and -inf) land in 32 per-lane sink bins:
+      // no branch per token
+      const int sink = NBINS + (tid & 31);
+#pragma unroll
+      for (int i = 0; i < E4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float y = x[i][q] * g.inv_delta;
+          const float kf = floorf(y);
+          const float rbf = kmax - kf;
+          const int rb = (rbf >= 0.0f && rbf < (float)NBINS) ? (int)rbf : sink;
+          const float w = __builtin_amdgcn_exp2f(fmaf(y - kf, g.c_bin, -g.c_bin));
+          const uint32_t fix = (uint32_t)(w * 2147483648.0f);
+          atomicAdd(&sh.hist[rb], (1ull << kCountShift) | (unsigned long long)fix);
+        }
+      __syncthreads();
+      unsigned long long* gh = a.hist + slot * NBINS;
+      for (int b = tid; b < NBINS; b += NT) st_u64(gh + b, sh.hist[b]);
     }
   }
+  if (tid == 0) {
+    SliceHead h;
+    h.zmax = zm;
+    h.arg = (zm == CDS_NEG_INF) ? -1 : am;
+    h.flags = flags;
+    h.kmax = kmax;
+    h.sumexp = se;
+    h.pad[0] = h.pad[1] = 0u;
+    st_obj(&a.heads[slot], h);
+  }
+  vm_drain();
+  __syncthreads();
+  RowSync* sy = &a.sync[r];
+  if (tid == 0) s_word[0] = gen_add(&sy->arrive, a.gen, 1u);
+  __syncthreads();
+  if (s_word[0] != (uint32_t)(P - 1)) return;
+  // the last slice of the row: the plan
+  plan_row<NT>(a, r, sh.plan, s_plan);
+  if (tid == 0 && !greedy) {
+    vm_drain();  // the plan (written by this thread) before its flag
+    st_u32(&sy->ready, a.gen);
+  }
+}
+
+template <int NT, int E4, bool BF16, bool VEC>
+__device__ __forceinline__ void race_task(const SampleArgs& a, int r, int sl, FusedLds<NT>& sh,
+                          RedScratch<NT>& red, Plan* s_plan, uint32_t* s_word) {
+  const int tid = threadIdx.x, P = a.P;
+  const RowParams rp = a.rows[r];
+  if (rp.flags & ROW_GREEDY) return;  // answered by the scan tasks
+  RowSync* sy = &a.sync[r];
+  if (tid == 0) {
+    if (gen_wait(&sy->ready, a.gen, a.spin_limit)) {
+      *s_plan = ld_obj(&a.plans[r]);
+    } else {
+      s_plan->mode = PLAN_NONE;
+      st_u32(&sy->failed, a.gen);
+    }
+  }
+  __syncthreads();
+  const int64_t lo = (int64_t)sl * a.S;
+  const int64_t hi = min(lo + a.S, (int64_t)a.V);
+  const int64_t slot = (int64_t)r * P + sl;
+
+  if (s_plan->mode == PLAN_FAST) {
+    const RowView rv = row_view<BF16>(a, r);
+    const RaceCtx c = make_race_ctx(rp, s_plan->zmax);
+    const float zc1 = s_plan->zcut1;
+    const float zs = fmaxf(fmaxf(s_plan->z_sure, zc1), -FLT_MAX);
+    const float a_lo = s_plan->a_lo, a_hi = s_plan->a_hi;
+    const float k_lo = s_plan->k_lo, k_hi = s_plan->k_hi;
+    const bool has_u = a_lo < a_hi || k_lo < k_hi;
+    const int lane = tid & 63;
+    Top2 b = top2_init();
+    uint32_t nonfin = 0;
+    // groups of G chunks, the next group's loads in flight while one is
+    // raced (the slice was just streamed by the scan task, so it comes from
+    // the caches); boundary tokens are staged in LDS, one reservation per wave
+    constexpr int G = E4 < 4 ? E4 : 4;
+    if (tid == 0) s_word[1] = 0u;
+    __syncthreads();
+    float x[G][4], xn[G][4];
+    load_chunks<NT, G, BF16, VEC>(rv, lo, hi, 0, x, nonfin);
+#pragma unroll 1
+    for (int g0 = 0; g0 < E4; g0 += G) {
+      if (g0 + G < E4) load_chunks<NT, G, BF16, VEC>(rv, lo, hi, g0 + G, xn, nonfin);
+      int32_t ucnt = 0;
+#pragma unroll
+      for (int i = 0; i < G; ++i) {
+        const int64_t t0 = lo + 4 * ((int64_t)(g0 + i) * NT + tid);
+        bool need = false;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          need |= x[i][q] >= zs && race32_hopeful(b, x[i][q], c.zmax, c.invT32);
+        if (need) {
+          const uint4 blk = race_block(c, t0);
+          const uint32_t xs[4] = {blk.x, blk.y, blk.z, blk.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (x[i][q] >= zs) race32(b, x[i][q], (int32_t)(t0 + q), xs[q], c.zmax, c.invT32);
+        }
+        if (has_u) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            ucnt += is_boundary(x[i][q], zs, zc1, a_lo, a_hi, k_lo, k_hi) ? 1 : 0;
+        }
+      }
+      if (has_u && __any(ucnt)) {
+        int32_t incl = ucnt;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          const int32_t y = __shfl_up(incl, o, 64);
+          if (lane >= o) incl += y;
+        }
+        uint32_t base = 0;
+        if (lane == 63) base = atomicAdd(&s_word[1], (uint32_t)incl);
+        base = __shfl(base, 63, 64);
+        uint32_t pos = base + (uint32_t)(incl - ucnt);
+        if (ucnt) {
+#pragma unroll
+          for (int i = 0; i < G; ++i)
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const float v = x[i][q];
+              if (is_boundary(v, zs, zc1, a_lo, a_hi, k_lo, k_hi)) {
+                if (pos < (uint32_t)SCAP)
+                  sh.stage[pos] = ((uint64_t)okey(v + 0.0f) << 32) |
+                                  (uint64_t)(0xFFFFFFFFu -
+                                             (uint32_t)(lo + 4 * ((int64_t)(g0 + i) * NT + tid) + q));
+                ++pos;
+              }
+            }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < G; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) x[i][q] = xn[i][q];
+    }
+    __syncthreads();
+    const uint32_t nst = s_word[1];
+    if (nst && nst <= (uint32_t)SCAP) {
+      uint64_t* ul = a.ulist + slot * SCAP;
+      for (uint32_t i = tid; i < nst; i += NT) st_u64(ul + i, sh.stage[i]);
+    }
+    block_top2<NT>(b, red);
+    if (tid == 0) {
+      SliceBest sb;
+      sb.k1 = b.k1;
+      sb.t1 = b.t1;
+      sb.z1 = b.z1;
+      sb.k2 = b.k2;
+      sb.ucnt = nst;
+      sb.pad[0] = sb.pad[1] = sb.pad[2] = 0u;
+      st_obj(&a.bests[slot], sb);
+    }
+  }
+
+  // the last race task of the row finishes it
+  vm_drain();
+  __syncthreads();
+  if (tid == 0) s_word[0] = gen_add(&sy->done, a.gen, 1u);
+  __syncthreads();
+  if (s_word[0] != (uint32_t)(P - 1)) return;
+  if (tid == 0) s_word[0] = ld_u32(&sy->failed) == a.gen;
+  __syncthreads();
+  const bool failed = s_word[0] != 0u;
+  const Plan pl = *s_plan;
+  if (failed || pl.mode == PLAN_SLOW ||
+      (pl.mode == PLAN_FAST &&
+       !finish_row<NT, BF16, VEC>(a, r, pl, sh.fin.ex, sh.fin.list, sh.fin.off, red))) {
+    __syncthreads();
+    row_exact<NT, BF16, VEC>(a, r, sh.fin.ex);
+    if (tid == 0) a.plans[r].path = PATH_EXACT;
+  }
+}
+
+// Four waves per SIMD (<= 128 VGPRs): 4 workgroups of 256 threads per CU.
+template <int NT, int E4, bool BF16, bool VEC>
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sample_kernel(
+    const SampleArgs a) {
+  __shared__ RedScratch<NT> red;
+  __shared__ FusedLds<NT> sh;
+  __shared__ Plan s_plan;
+  __shared__ uint32_t s_word[2];
+  // blocks [0, B*P) scan, [B*P, 2*B*P) race; slice = block % P
+  const int y = (int)(blockIdx.x / (unsigned)a.P);
+  const int sl = (int)(blockIdx.x - (unsigned)y * (unsigned)a.P);
+  if (y < a.B)
+    scan_task<NT, E4, BF16, VEC>(a, y, sl, sh, red, &s_plan, s_word);
+  else
+    race_task<NT, E4, BF16, VEC>(a, y - a.B, sl, sh, red, &s_plan, s_word);
 }
 
 // ============================================================================
@@ -962,73 +1214,56 @@ hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream) {
   return hipGetLastError();
 }
 
-constexpr int kPlanNT = 256;
-constexpr int kFinishNT = 512;
+constexpr int kExactNT = 512;
 
-static inline void rec(const KernelEvents* ev, bool start, int k, hipStream_t s) {
+static inline void rec(const KernelEvents* ev, bool start, hipStream_t s) {
   if (!ev) return;
-  hipEvent_t e = start ? ev->start[k] : ev->stop[k];
+  hipEvent_t e = start ? ev->start : ev->stop;
   if (e) (void)hipEventRecord(e, s);
 }
 
 template <int E4, bool BF16, bool VEC>
-static hipError_t launch_fast(const SampleArgs& a, bool need_race, const KernelEvents* ev,
-                              hipStream_t s) {
-  const dim3 grid((unsigned)a.P, (unsigned)a.B);
-  rec(ev, true, 0, s);
-  hipLaunchKernelGGL((scan_kernel<kScanThreads, E4, BF16, VEC>), grid, dim3(kScanThreads), 0, s,
-                     a);
-  rec(ev, false, 0, s);
-  rec(ev, true, 3, s);
-  hipLaunchKernelGGL((plan_kernel<kPlanNT>), dim3((unsigned)a.B), dim3(kPlanNT), 0, s, a);
-  rec(ev, false, 3, s);
-  if (need_race) {
-    rec(ev, true, 1, s);
-    hipLaunchKernelGGL((race_kernel<kScanThreads, E4, BF16, VEC>), grid, dim3(kScanThreads), 0,
-                       s, a);
-    rec(ev, false, 1, s);
-    rec(ev, true, 2, s);
-    hipLaunchKernelGGL((finish_kernel<kFinishNT, BF16, VEC>), dim3((unsigned)a.B),
-                       dim3(kFinishNT), 0, s, a);
-    rec(ev, false, 2, s);
-  }
+static hipError_t launch_fused(const SampleArgs& a, const KernelEvents* ev, hipStream_t s) {
+  rec(ev, true, s);
+  hipLaunchKernelGGL((sample_kernel<kScanThreads, E4, BF16, VEC>),
+                     dim3(2u * (unsigned)a.B * (unsigned)a.P), dim3(kScanThreads), 0, s, a);
+  rec(ev, false, s);
   return hipGetLastError();
 }
 
 template <bool BF16, bool VEC>
-static hipError_t launch_fast_e4(const SampleArgs& a, bool need_race, const KernelEvents* ev,
-                                 hipStream_t s) {
+static hipError_t launch_fused_e4(const SampleArgs& a, const KernelEvents* ev, hipStream_t s) {
   const int64_t e4 = (a.S + 4 * kScanThreads - 1) / (4 * kScanThreads);
-  if (e4 <= 1) return launch_fast<1, BF16, VEC>(a, need_race, ev, s);
-  if (e4 <= 2) return launch_fast<2, BF16, VEC>(a, need_race, ev, s);
-  if (e4 <= 4) return launch_fast<4, BF16, VEC>(a, need_race, ev, s);
-  if (e4 <= 8) return launch_fast<8, BF16, VEC>(a, need_race, ev, s);
-  if (e4 <= 12) return launch_fast<12, BF16, VEC>(a, need_race, ev, s);
-  if (e4 <= 16) return launch_fast<16, BF16, VEC>(a, need_race, ev, s);
-  if (e4 <= 20) return launch_fast<20, BF16, VEC>(a, need_race, ev, s);
+  if (e4 <= 1) return launch_fused<1, BF16, VEC>(a, ev, s);
+  if (e4 <= 2) return launch_fused<2, BF16, VEC>(a, ev, s);
+  if (e4 <= 4) return launch_fused<4, BF16, VEC>(a, ev, s);
+  if (e4 <= 8) return launch_fused<8, BF16, VEC>(a, ev, s);
+  if (e4 <= 12) return launch_fused<12, BF16, VEC>(a, ev, s);
+  if (e4 <= 16) return launch_fused<16, BF16, VEC>(a, ev, s);
+  if (e4 <= 20) return launch_fused<20, BF16, VEC>(a, ev, s);
   return hipErrorInvalidValue;
 }
 
 template <bool BF16, bool VEC>
-static hipError_t launch_any(const SampleArgs& a, int algo, bool need_race,
-                             const KernelEvents* ev, hipStream_t s) {
+static hipError_t launch_any(const SampleArgs& a, int algo, const KernelEvents* ev,
+                             hipStream_t s) {
   if (algo == 1) {
-    rec(ev, true, 0, s);
-    hipLaunchKernelGGL((exact_kernel<kFinishNT, BF16, VEC>), dim3((unsigned)a.B),
-                       dim3(kFinishNT), 0, s, a);
-    rec(ev, false, 0, s);
+    rec(ev, true, s);
+    hipLaunchKernelGGL((exact_kernel<kExactNT, BF16, VEC>), dim3((unsigned)a.B), dim3(kExactNT),
+                       0, s, a);
+    rec(ev, false, s);
     return hipGetLastError();
   }
-  return launch_fast_e4<BF16, VEC>(a, need_race, ev, s);
+  return launch_fused_e4<BF16, VEC>(a, ev, s);
 }
 
-hipError_t launch_sample(const SampleArgs& a, bool bf16, bool vec, int algo, bool need_race,
+hipError_t launch_sample(const SampleArgs& a, bool bf16, bool vec, int algo,
                          const KernelEvents* ev, hipStream_t stream) {
   if (bf16)
-    return vec ? launch_any<true, true>(a, algo, need_race, ev, stream)
-               : launch_any<true, false>(a, algo, need_race, ev, stream);
-  return vec ? launch_any<false, true>(a, algo, need_race, ev, stream)
-             : launch_any<false, false>(a, algo, need_race, ev, stream);
+    return vec ? launch_any<true, true>(a, algo, ev, stream)
+               : launch_any<true, false>(a, algo, ev, stream);
+  return vec ? launch_any<false, true>(a, algo, ev, stream)
+             : launch_any<false, false>(a, algo, ev, stream);
 }
 
 }  // namespace cds

@@ -1,6 +1,6 @@
 // layout.h -- device-memory layouts shared by the host code and the kernels
 // of libcd_sampler.so: the packed per-row parameter records and the
-// workspace used between the two sampling kernels.
+// workspace the sampling kernel's workgroups share.
 #pragma once
 #include <stddef.h>
 #include <stdint.h>
@@ -58,15 +58,23 @@ constexpr int kScanThreads = 256;
 constexpr int kMaxChunks = 20;
 constexpr int64_t kSliceMax = (int64_t)kScanThreads * 4 * kMaxChunks;  // 20480 tokens
 constexpr int kCountShift = 48;   // histogram word: count << 48 | fixed-point mass
-constexpr int UCAP = 4096;        // boundary tokens the refinement holds on chip
+constexpr int UCAP = 4096;        // boundary tokens of a row the finisher holds on chip
+constexpr int SCAP = 2048;        // boundary tokens one slice can hand over
 constexpr int kMaxSlices = 64;
 constexpr int kMaxRows = 65535;
 
 // ---- workspace ------------------------------------------------------------
-struct RowSync {        // zero between calls (restored by the finish kernel)
-  uint32_t ucount;
-  uint32_t pad[3];
+// Per-row meeting point of the row's workgroups.  Counters hold the call's
+// generation in the high half and a count in the low half (a counter of
+// another generation counts as zero); flags hold the generation that set them.
+struct RowSync {
+  unsigned long long arrive;  // scan tasks done
+  unsigned long long done;    // race tasks done
+  uint32_t ready;             // generation whose plan is published
+  uint32_t failed;            // generation in which a race task gave up waiting
+  uint32_t pad[2];
 };
+static_assert(sizeof(RowSync) == 32, "RowSync layout");
 
 enum SliceFlag : uint32_t {
   SLICE_NONFINITE = 1u,   // a NaN or +inf among the slice's allowed tokens
@@ -83,12 +91,15 @@ struct SliceHead {
 };
 static_assert(sizeof(SliceHead) == 32, "SliceHead layout");
 
-struct SliceBest {  // fp32 race keys: the slice's best two
+struct SliceBest {  // fp32 race keys: the slice's best two, and its boundary tokens
   float k1;         // best key (-inf if the slice had no candidate)
   int32_t t1;       // its token
   float z1;         // its logit
   float k2;         // second-best key
+  uint32_t ucnt;    // boundary tokens in the slice's list (> SCAP: overflowed)
+  uint32_t pad[3];
 };
+static_assert(sizeof(SliceBest) == 32, "SliceBest layout");
 
 enum PlanMode : int32_t { PLAN_NONE = 0, PLAN_DONE = 1, PLAN_FAST = 2, PLAN_SLOW = 3 };
 
@@ -156,7 +167,7 @@ inline WorkspaceLayout workspace_layout(int32_t B, int32_t V) {
   L.head_off = take(sizeof(SliceHead) * (size_t)B * L.P);
   L.hist_off = take(sizeof(uint64_t) * NBINS * (size_t)B * L.P);
   L.best_off = take(sizeof(SliceBest) * (size_t)B * L.P);
-  L.ulist_off = take(sizeof(uint64_t) * UCAP * (size_t)B);
+  L.ulist_off = take(sizeof(uint64_t) * SCAP * (size_t)B * L.P);
   L.total = off;
   return L;
 }

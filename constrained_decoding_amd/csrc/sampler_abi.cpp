@@ -23,8 +23,9 @@ constexpr int32_t kMaxB = kMaxRows;
 
 std::atomic<int> g_algo{0};
 // one-shot kernel timing hook (see sampler_time_next)
-std::atomic<void*> g_ev_start[kTimedKernels] = {};
-std::atomic<void*> g_ev_stop[kTimedKernels] = {};
+std::atomic<uint32_t> g_gen{0u};  // call generations (see sampler_sample)
+std::atomic<void*> g_ev_start{nullptr};
+std::atomic<void*> g_ev_stop{nullptr};
 
 inline bool finite_f(float x) { return std::isfinite(x); }
 
@@ -327,15 +328,25 @@ int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_
   int algo = g_algo.load();
   if (L.S > kSliceMax) algo = 1;  // slices beyond the register-resident size
 
+  // A slice waits at most ~5 ms of wall clock for its row's plan (then the
+  // row takes the exact path); the wall clock's rate is a device attribute.
+  int dev = 0, rate_khz = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
+      rate_khz <= 0)
+    rate_khz = 100000;
+  a.spin_limit = (uint64_t)rate_khz * 5u;
+  // Generation of this call: tags the workspace's row counters, so counters
+  // left by any earlier call read as zero.  Never 0 (a zeroed workspace).
+  uint32_t gen = g_gen.fetch_add(1u) + 1u;
+  if (gen == 0u) gen = g_gen.fetch_add(1u) + 1u;
+  a.gen = gen;
+
   KernelEvents ev;
-  bool have_ev = false;
-  for (int k = 0; k < kTimedKernels; ++k) {
-    ev.start[k] = static_cast<hipEvent_t>(g_ev_start[k].exchange(nullptr));
-    ev.stop[k] = static_cast<hipEvent_t>(g_ev_stop[k].exchange(nullptr));
-    have_ev = have_ev || ev.start[k] || ev.stop[k];
-  }
-  const bool need_race = !(b->flags & SAMPLER_FLAG_ALL_GREEDY);
-  const hipError_t e = launch_sample(a, bf16, vec, algo, need_race, have_ev ? &ev : nullptr,
+  ev.start = static_cast<hipEvent_t>(g_ev_start.exchange(nullptr));
+  ev.stop = static_cast<hipEvent_t>(g_ev_stop.exchange(nullptr));
+  const bool have_ev = ev.start || ev.stop;
+  const hipError_t e = launch_sample(a, bf16, vec, algo, have_ev ? &ev : nullptr,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SAMPLER_OK : SAMPLER_EHIP;
 }
@@ -350,9 +361,9 @@ int sampler_set_option(int option, int64_t value) {
 }
 
 int sampler_time_next(int kernel, void* start_event, void* stop_event) {
-  if (kernel < 0 || kernel >= kTimedKernels) return SAMPLER_EINVAL;
-  g_ev_start[kernel].store(start_event);
-  g_ev_stop[kernel].store(stop_event);
+  if (kernel != 0) return SAMPLER_EINVAL;
+  g_ev_start.store(start_event);
+  g_ev_stop.store(stop_event);
   return SAMPLER_OK;
 }
 

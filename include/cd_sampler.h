@@ -243,11 +243,10 @@ int sampler_sample(const sampler_batch *b, const void *logits, int dtype,
  * passes; used to test the fast path and the fallback it takes for rows whose
  * boundary sets do not fit on chip).  Process-wide; not for concurrent use.
  *
- * sampler_time_next(k, start, stop): on the next sampler_sample call, record
+ * sampler_time_next(0, start, stop): on the next sampler_sample call, record
  * hipEvent_t `start` / `stop` (passed as void*) on the call's stream right
- * before and after its kernel k (0 = the streaming scan kernel, 1 = the race
- * kernel, 2 = the finish kernel, 3 = the plan kernel).  One-shot; used by the
- * benchmark to time the dominant kernel. */
+ * before and after its sampling kernel.  One-shot; used by the benchmark to
+ * time the kernel.  Any other first argument -> EINVAL. */
 #define SAMPLER_OPT_ALGO 1
 int sampler_set_option(int option, int64_t value);
 int sampler_time_next(int kernel, void *start_event, void *stop_event);
