@@ -487,6 +487,23 @@ __device__ __forceinline__ void wave0_scan_inplace(T* v, int n) {
 }
 
 
+// First index i < n with v[i] >= x in an LDS array that is non-decreasing
+// (n if none), by wave 0 alone with one ballot: lane l owns [K*l, K*l + K).
+// Every lane of wave 0 gets the result.
+template <int K, typename T>
+__device__ __forceinline__ int wave0_first_ge(const T* v, int n, T x) {
+  const int l = threadIdx.x & 63;
+  const int last = min(K * l + K, n) - 1;
+  const bool any = K * l < n && v[last] >= x;
+  const unsigned long long m = __ballot(any);
+  if (!m) return n;
+  const int f = __ffsll((long long)m) - 1;
+  int i = K * f;
+  while (!(v[i] >= x)) ++i;  // stops inside lane f's range, whose last value is >= x
+  return i;
+}
+
+// ---- workgroup reductions (fixed trees: deterministic) -------------------------
 template <int NT>
 struct RedScratch {
   double d[NT / 64];

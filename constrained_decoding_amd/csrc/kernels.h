@@ -11,6 +11,8 @@ namespace cds {
 
 struct SampleArgs {
   const RowParams* rows;
+  const int32_t* sampled;  // the rows that are not greedy, ascending
+  int32_t n_sampled;
   const void* logits;
   int64_t ld;
   int32_t B, V;

@@ -354,17 +354,17 @@ __global__ __launch_bounds__(NT) void exact_kernel(const SampleArgs a) {
 }
 
 // ============================================================================
-// fast path: one kernel, 2*B*P workgroups, two kinds of task
+// fast path: one kernel, (B + sampled rows)*P workgroups, two kinds of task
 // ============================================================================
 //
-// Blocks [0, B*P): scan task for slice (block % P) of row (block / P).  Streams
+// Scan task for slice s of row r.  Streams
 //   the slice into registers; reduces max, argmax and the non-finite flag;
 //   builds either the histogram (rows with a top-k or top-p cut) or sum exp;
 //   writes the slice summary and takes the row's arrival ticket.  The last
 //   slice of a row to arrive merges the summaries into the row's plan (greedy,
 //   invalid and overflow rows get their output here) and raises the row's
 //   ready flag.
-// Blocks [B*P, 2*B*P): race task for the same slice of row block/P - B
+// Race task for slice s of row r
 //   (sampled rows only).  Waits for the row's plan, re-reads the slice (just
 //   read by the scan task, so it comes from the caches), races the tokens
 //   that are surely in the final set, stages the boundary-bin tokens in LDS
@@ -376,7 +376,8 @@ __global__ __launch_bounds__(NT) void exact_kernel(const SampleArgs a) {
 //
 // Race tasks follow every scan task in dispatch order, so while early rows
 // race, later rows still stream from HBM, and a race task's wait ends once
-// the scans of its row, dispatched before it, complete.  The wait is still
+// the scans of its row, dispatched before it, complete.  Greedy rows get no
+// race tasks.  The wait is still
 // bounded by wall-clock time: a task that gives up marks the row and the
 // finisher then runs the exact path, so results never depend on timing.
 //
@@ -471,7 +472,6 @@ struct PlanShared {
   uint32_t accc[NBINS];
   double wtot_d[NT / 64];
   uint32_t wtot_u[NT / 64];
-  int idx[3];
   int mode, inK, k_rank, rb12;
   float zmax, zcut1;
   int32_t arg;
@@ -621,15 +621,11 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, PlanShared<
   wave0_scan_inplace<KB>(ps.cumc, NBINS);
   wave0_scan_inplace<KB>(ps.md, NBINS);
   __syncthreads();
-  if (tid < 3) ps.idx[tid] = NBINS;
-  __syncthreads();
-  if (topk)
-    for (int b = tid; b < NBINS; b += NT)
-      if (ps.cumc[b] >= (uint32_t)rp.top_k) atomicMin(&ps.idx[0], b);
-  __syncthreads();
+  // the rest is searches over the monotone cumulative arrays: wave 0 only
+  if (tid >= 64) return;
+  const int rb2 = topk ? wave0_first_ge<KB>(ps.cumc, NBINS, (uint32_t)rp.top_k) : NBINS;
   if (tid == 0) {
     ps.log_z = log(ps.md[NBINS - 1]);
-    const int rb2 = ps.idx[0];
     int rb1 = NBINS;
     if (ps.zcut1 != CDS_NEG_INF) {
       const float rbf = kmax - floorf(ps.zcut1 * g.inv_delta);
@@ -651,17 +647,13 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, PlanShared<
     ps.tlo = (double)rp.top_p * M_lo * (1.0 - 1e-9);
     ps.thi = (double)rp.top_p * M_hi * (1.0 + 1e-9);
   }
-  __syncthreads();
-  if (topp)
-    for (int b = tid; b < NBINS; b += NT) {
-      if (ps.md[b] >= ps.tlo) atomicMin(&ps.idx[1], b);
-      if (ps.md[b] >= ps.thi) atomicMin(&ps.idx[2], b);
-    }
-  __syncthreads();
+  __builtin_amdgcn_wave_barrier();
+  const int i_lo = topp ? wave0_first_ge<KB>(ps.md, NBINS, ps.tlo) : NBINS;
+  const int i_hi = topp ? wave0_first_ge<KB>(ps.md, NBINS, ps.thi) : NBINS;
   if (tid == 0) {
     const int cap = ps.rb12 < NBINS ? ps.rb12 : NBINS - 1;
-    const int rb3_hi = min(ps.idx[2], cap);
-    const int rb3_lo = min(ps.idx[1], rb3_hi);
+    const int rb3_hi = min(i_hi, cap);
+    const int rb3_lo = min(i_lo, rb3_hi);
     const int inK = ps.inK;
     int umin = NBINS;
     if (topp) umin = rb3_lo;
@@ -915,9 +907,11 @@ __device__ __forceinline__ bool is_boundary(float v, float zs, float zc1, float 
   return v < zs && v >= zc1 && ((v >= a_lo && v < a_hi) || (v >= k_lo && v < k_hi));
 }
 
+constexpr int kHistCopies = 4;
+
 template <int NT>
 union FusedLds {
-  unsigned long long hist[NBINS + 32];
+  unsigned long long hist[kHistCopies * (NBINS + 32)];
   PlanShared<NT> plan;
   struct {
     ExactShared<NT> ex;
@@ -984,11 +978,13 @@ __device__ __forceinline__ void scan_task(const SampleArgs& a, int r, int sl, Fu
     if (!(fabsf(kmax) < 4194304.0f)) {
       flags |= SLICE_BINS_LOST;  // bin indices would not be exact: row takes the exact path
     } else {
-      for (int b = tid; b < NBINS + 32; b += NT) sh.hist[b] = 0ull;
+      for (int b = tid; b < kHistCopies * (NBINS + 32); b += NT) sh.hist[b] = 0ull;
       __syncthreads();
       // tokens outside the window (and -inf) land in 32 per-lane sink bins:
-      // no branch per token
+      // no branch per token.  kHistCopies interleaved copies (lane % copies)
+      // spread the atomics of one instruction over more addresses.
       const int sink = NBINS + (tid & 31);
+      const int copy = tid & (kHistCopies - 1);
 #pragma unroll
       for (int i = 0; i < E4; ++i)
 #pragma unroll
@@ -999,11 +995,17 @@ __device__ __forceinline__ void scan_task(const SampleArgs& a, int r, int sl, Fu
           const int rb = (rbf >= 0.0f && rbf < (float)NBINS) ? (int)rbf : sink;
           const float w = __builtin_amdgcn_exp2f(fmaf(y - kf, g.c_bin, -g.c_bin));
           const uint32_t fix = (uint32_t)(w * 2147483648.0f);
-          atomicAdd(&sh.hist[rb], (1ull << kCountShift) | (unsigned long long)fix);
+          atomicAdd(&sh.hist[rb * kHistCopies + copy],
+                    (1ull << kCountShift) | (unsigned long long)fix);
         }
       __syncthreads();
       unsigned long long* gh = a.hist + slot * NBINS;
-      for (int b = tid; b < NBINS; b += NT) st_u64(gh + b, sh.hist[b]);
+      for (int b = tid; b < NBINS; b += NT) {
+        unsigned long long v = 0ull;
+#pragma unroll
+        for (int c = 0; c < kHistCopies; ++c) v += sh.hist[b * kHistCopies + c];
+        st_u64(gh + b, v);
+      }
     }
   }
   if (tid == 0) {
@@ -1171,13 +1173,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sa
   __shared__ FusedLds<NT> sh;
   __shared__ Plan s_plan;
   __shared__ uint32_t s_word[2];
-  // blocks [0, B*P) scan, [B*P, 2*B*P) race; slice = block % P
-  const int y = (int)(blockIdx.x / (unsigned)a.P);
-  const int sl = (int)(blockIdx.x - (unsigned)y * (unsigned)a.P);
-  if (y < a.B)
-    scan_task<NT, E4, BF16, VEC>(a, y, sl, sh, red, &s_plan, s_word);
+  // Blocks [0, B*P): scan tasks (row block/P); then race tasks for the rows
+  // that are not greedy (the i-th of them for block/P - B = i); slice =
+  // block % P.  Every race task follows its row's scan tasks.
+  const int grp = (int)(blockIdx.x / (unsigned)a.P);
+  const int sl = (int)(blockIdx.x - (unsigned)grp * (unsigned)a.P);
+  if (grp < a.B)
+    scan_task<NT, E4, BF16, VEC>(a, grp, sl, sh, red, &s_plan, s_word);
   else
-    race_task<NT, E4, BF16, VEC>(a, y - a.B, sl, sh, red, &s_plan, s_word);
+    race_task<NT, E4, BF16, VEC>(a, a.sampled[grp - a.B], sl, sh, red, &s_plan, s_word);
 }
 
 // ============================================================================
@@ -1226,7 +1230,8 @@ template <int E4, bool BF16, bool VEC>
 static hipError_t launch_fused(const SampleArgs& a, const KernelEvents* ev, hipStream_t s) {
   rec(ev, true, s);
   hipLaunchKernelGGL((sample_kernel<kScanThreads, E4, BF16, VEC>),
-                     dim3(2u * (unsigned)a.B * (unsigned)a.P), dim3(kScanThreads), 0, s, a);
+                     dim3((unsigned)(a.B + a.n_sampled) * (unsigned)a.P), dim3(kScanThreads), 0, s,
+                     a);
   rec(ev, false, s);
   return hipGetLastError();
 }

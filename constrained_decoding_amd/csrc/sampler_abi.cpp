@@ -29,8 +29,12 @@ std::atomic<void*> g_ev_stop{nullptr};
 
 inline bool finite_f(float x) { return std::isfinite(x); }
 
+// Device parameter block: RowParams[B] | int32 sampled-row list, room for B
+// (padded to 16 bytes) | PenEntry[n_pen] | BiasEntry[n_bias].
+size_t list_bytes(int32_t B) { return ((size_t)B * sizeof(int32_t) + 15) / 16 * 16; }
+
 size_t params_bytes_exact(int32_t B, int64_t n_pen, int64_t n_bias) {
-  return sizeof(RowParams) * (size_t)B + sizeof(PenEntry) * (size_t)n_pen +
+  return sizeof(RowParams) * (size_t)B + list_bytes(B) + sizeof(PenEntry) * (size_t)n_pen +
          sizeof(BiasEntry) * (size_t)n_bias;
 }
 
@@ -67,6 +71,7 @@ int pack_into(const sampler_host_params* h, std::vector<unsigned char>& out_buf,
   }
 
   std::vector<RowParams> rows((size_t)B);
+  std::vector<int32_t> sampled;
   std::vector<PenEntry> pen;
   std::vector<BiasEntry> bias;
   uint32_t flags = SAMPLER_FLAG_ALL_GREEDY;
@@ -105,6 +110,7 @@ int pack_into(const sampler_host_params* h, std::vector<unsigned char>& out_buf,
       flags |= SAMPLER_FLAG_ANY_GREEDY;
     } else {
       flags &= ~SAMPLER_FLAG_ALL_GREEDY;
+      sampled.push_back(r);
       if (k > 1 && k < V) {
         rp.flags |= ROW_TOPK;
         rp.top_k = k;
@@ -165,11 +171,14 @@ int pack_into(const sampler_host_params* h, std::vector<unsigned char>& out_buf,
   if (pen.size() > (size_t)INT32_MAX || bias.size() > (size_t)INT32_MAX) return SAMPLER_ERANGE;
 
   const size_t bytes = params_bytes_exact(B, (int64_t)pen.size(), (int64_t)bias.size());
-  out_buf.resize(bytes);
+  out_buf.assign(bytes, 0);
   unsigned char* p = out_buf.data();
+  const size_t off_list = sizeof(RowParams) * (size_t)B;
+  const size_t off_pen = off_list + list_bytes(B);
   std::memcpy(p, rows.data(), sizeof(RowParams) * rows.size());
-  std::memcpy(p + sizeof(RowParams) * (size_t)B, pen.data(), sizeof(PenEntry) * pen.size());
-  std::memcpy(p + sizeof(RowParams) * (size_t)B + sizeof(PenEntry) * pen.size(), bias.data(),
+  std::memcpy(p + off_list, sampled.data(), sizeof(int32_t) * sampled.size());
+  std::memcpy(p + off_pen, pen.data(), sizeof(PenEntry) * pen.size());
+  std::memcpy(p + off_pen + sizeof(PenEntry) * pen.size(), bias.data(),
               sizeof(BiasEntry) * bias.size());
 
   std::memset(out, 0, sizeof *out);
@@ -180,14 +189,18 @@ int pack_into(const sampler_host_params* h, std::vector<unsigned char>& out_buf,
   out->n_pen = (int64_t)pen.size();
   out->n_bias = (int64_t)bias.size();
   out->bytes = bytes;
+  out->n_sampled = (int32_t)sampled.size();
   return SAMPLER_OK;
 }
 
 void set_pointers(sampler_batch* out, const void* base) {
   const unsigned char* b = static_cast<const unsigned char*>(base);
+  const size_t off_list = sizeof(RowParams) * (size_t)out->B;
+  const size_t off_pen = off_list + list_bytes(out->B);
   out->d_rows = b;
-  out->d_pen = b + sizeof(RowParams) * (size_t)out->B;
-  out->d_bias = b + sizeof(RowParams) * (size_t)out->B + sizeof(PenEntry) * (size_t)out->n_pen;
+  out->d_sampled = b + off_list;
+  out->d_pen = b + off_pen;
+  out->d_bias = b + off_pen + sizeof(PenEntry) * (size_t)out->n_pen;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -302,7 +315,11 @@ int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   SampleArgs a;
+  if (b->n_sampled < 0 || b->n_sampled > B || (b->n_sampled > 0 && !b->d_sampled))
+    return SAMPLER_EINVAL;
   a.rows = static_cast<const RowParams*>(b->d_rows);
+  a.sampled = static_cast<const int32_t*>(b->d_sampled);
+  a.n_sampled = b->n_sampled;
   a.logits = logits;
   a.ld = ld;
   a.B = B;

@@ -138,6 +138,10 @@ typedef struct sampler_batch {
   const void *d_pen;    /* dev: penalty entries inside d_buf                 */
   const void *d_bias;   /* dev: bias entries inside d_buf                    */
   size_t bytes;         /* bytes of d_buf in use                             */
+  int32_t n_sampled;    /* rows that are not greedy                          */
+  int32_t reserved;
+  const void *d_sampled; /* dev: int32 indices of those rows, ascending,
+                            inside d_buf                                     */
 } sampler_batch;
 
 /* Message for a SAMPLER_* return code (static storage). */

@@ -86,11 +86,14 @@ def test_penalty_counts_and_bias_dedup(cds):
                            hist_indptr=hp, hist_ids=hi, bias_indptr=bp, bias_ids=ids,
                            bias_vals=vals)
     rows = _rowparams(buf, 3)
-    pen = np.frombuffer(buf[64 * 3:64 * 3 + 8 * b.n_pen].tobytes(), "<i4").reshape(-1, 2)
+    assert b.n_sampled == 3
+    assert np.frombuffer(buf[64 * 3:64 * 3 + 12].tobytes(), "<i4").tolist() == [0, 1, 2]
+    pen_off = 64 * 3 + 16        # the sampled-row list: room for B int32, 16-byte padded
+    pen = np.frombuffer(buf[pen_off:pen_off + 8 * b.n_pen].tobytes(), "<i4").reshape(-1, 2)
     np.testing.assert_array_equal(pen, [[3, 3], [7, 1]])      # row 2 has no active penalty
     assert (rows["pen_lo"][0], rows["pen_hi"][0]) == (0, 2)
     assert b.flags & cds.FLAG_NEED_PENALTY and b.flags & cds.FLAG_HAS_BIAS
-    off = 64 * 3 + 8 * b.n_pen
+    off = pen_off + 8 * b.n_pen
     bias = np.frombuffer(buf[off:off + 8 * b.n_bias].tobytes(),
                          [("id", "<i4"), ("val", "<f4")])
     assert bias["id"].tolist() == [1, 7]
@@ -147,3 +150,15 @@ def test_workspace_size_closed_form(cds):
     assert n > 192 * 151936 // 64                    # holds histograms and lists
     assert cds.lib.sampler_workspace_bytes(0, 10) == 0
     assert cds.lib.sampler_workspace_bytes(4, 1024) > 0
+
+
+def test_sampled_row_list(cds):
+    """The packed block lists the rows that are not greedy (T >= 1e-5 and
+    top_k != 1), ascending; greedy rows get no race work."""
+    T = np.array([0.0, 0.7, 1e-6, 1.0, 0.9], np.float32)
+    k = np.array([0, 0, 0, 1, 50], np.int32)
+    buf, b = cds.pack_host(5, 1000, T, top_k=k)
+    assert b.n_sampled == 2
+    assert np.frombuffer(buf[64 * 5:64 * 5 + 8].tobytes(), "<i4").tolist() == [1, 4]
+    buf, b = cds.pack_host(2, 1000, np.zeros(2, np.float32))
+    assert b.n_sampled == 0 and b.flags & cds.FLAG_ALL_GREEDY
