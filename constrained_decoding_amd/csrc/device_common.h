@@ -315,7 +315,7 @@ __device__ __forceinline__ void load4(const RowView& rv, int64_t t0, int64_t hi,
 // hi is whole): every load -- logits, then mask words -- is issued before any
 // value is used, with no branch between them; chunks at or beyond hi load
 // chunk `lo` (in bounds) and are discarded.  Otherwise guarded scalar loads.
-template <int NT, int N, bool BF16, bool VEC>
+template <int NT, int N, bool BF16, bool VEC, bool STREAM = false>
 __device__ __forceinline__ void load_chunks(const RowView& rv, int64_t lo, int64_t hi, int first,
                                             float x[N][4], uint32_t& nonfin) {
   if (!VEC) {
@@ -338,11 +338,15 @@ __device__ __forceinline__ void load_chunks(const RowView& rv, int64_t lo, int64
     in[i] = t0 < hi;
     ta[i] = in[i] ? t0 : lo;
   }
+  // STREAM: non-temporal loads, for data no later pass reads again
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   uint32_t raw[N][4];
   if (BF16) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const uint2 u = *reinterpret_cast<const uint2*>(rv.b16 + ta[i]);
+      const u32x2* src = reinterpret_cast<const u32x2*>(rv.b16 + ta[i]);
+      const u32x2 u = STREAM ? __builtin_nontemporal_load(src) : *src;
       raw[i][0] = u.x << 16;
       raw[i][1] = u.x & 0xFFFF0000u;
       raw[i][2] = u.y << 16;
@@ -351,7 +355,8 @@ __device__ __forceinline__ void load_chunks(const RowView& rv, int64_t lo, int64
   } else {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const uint4 u = *reinterpret_cast<const uint4*>(rv.f32 + ta[i]);
+      const u32x4* src = reinterpret_cast<const u32x4*>(rv.f32 + ta[i]);
+      const u32x4 u = STREAM ? __builtin_nontemporal_load(src) : *src;
       raw[i][0] = u.x;
       raw[i][1] = u.y;
       raw[i][2] = u.z;

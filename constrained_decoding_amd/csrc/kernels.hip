@@ -921,7 +921,9 @@ union FusedLds {
   uint64_t stage[SCAP];
 };
 
-template <int NT, int E4, bool BF16, bool VEC>
+// STREAM: non-temporal loads, for slices no race task reads again (greedy
+// rows); the slices of other rows should stay in the caches for their race.
+template <int NT, int E4, bool BF16, bool VEC, bool STREAM>
 __device__ __forceinline__ void scan_task(const SampleArgs& a, int r, int sl, FusedLds<NT>& sh,
                           RedScratch<NT>& red, Plan* s_plan, uint32_t* s_word) {
   const int tid = threadIdx.x, P = a.P;
@@ -934,7 +936,7 @@ __device__ __forceinline__ void scan_task(const SampleArgs& a, int r, int sl, Fu
 
   float x[E4][4];
   uint32_t nonfin = 0;
-  load_chunks<NT, E4, BF16, VEC>(rv, lo, hi, 0, x, nonfin);
+  load_chunks<NT, E4, BF16, VEC, STREAM>(rv, lo, hi, 0, x, nonfin);
 
   // max, then the lowest index holding it (searched only by threads that hold it)
   float lm = CDS_NEG_INF;
@@ -1178,10 +1180,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sa
   // block % P.  Every race task follows its row's scan tasks.
   const int grp = (int)(blockIdx.x / (unsigned)a.P);
   const int sl = (int)(blockIdx.x - (unsigned)grp * (unsigned)a.P);
-  if (grp < a.B)
-    scan_task<NT, E4, BF16, VEC>(a, grp, sl, sh, red, &s_plan, s_word);
-  else
+  if (grp < a.B) {
+    if (a.rows[grp].flags & ROW_GREEDY)
+      scan_task<NT, E4, BF16, VEC, true>(a, grp, sl, sh, red, &s_plan, s_word);
+    else
+      scan_task<NT, E4, BF16, VEC, false>(a, grp, sl, sh, red, &s_plan, s_word);
+  }
+  else {
     race_task<NT, E4, BF16, VEC>(a, a.sampled[grp - a.B], sl, sh, red, &s_plan, s_word);
+  }
 }
 
 // ============================================================================
