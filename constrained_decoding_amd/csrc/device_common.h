@@ -149,8 +149,8 @@ __device__ __forceinline__ void race_consider(Best& b, float z, int32_t t, uint3
 // every token that can win (sd error <= 20 * 1.8e-7, Gumbel term < 3e-6, final
 // rounding 1.2e-6), so when the best fp32 key beats the second by more than
 // 2 * kRaceEps the fp32 winner is the exact winner.  Otherwise the row is
-// re-raced in fp64 (finish kernel).
-constexpr float kRaceEps = 1e-4f;
+// re-raced in fp64 by the row's finisher.
+constexpr float kRaceEps = 2e-5f;
 
 // -ln(-ln U) in fp32: -ln U by a degree-5 series in d = 1-U when d < 1/16
 // (relative error < 2e-7; U near 1 would lose -ln U to cancellation in a

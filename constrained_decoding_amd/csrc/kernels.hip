@@ -159,12 +159,18 @@ struct ExactShared {
 };
 
 // Visit every token of the row in groups of four (t0 % 4 == 0).
-template <int NT, bool BF16, bool VEC, typename F>
+// K chunks per thread are loaded per round, all loads in flight at once.
+template <int NT, bool BF16, bool VEC, typename F, int K = 4>
 __device__ __forceinline__ void for_row4(const RowView& rv, int64_t V, uint32_t& nonfin, F f) {
-  for (int64_t t0 = 4 * (int64_t)threadIdx.x; t0 < V; t0 += 4 * (int64_t)NT) {
-    float x[4];
-    load4<BF16, VEC>(rv, t0, V, x, nonfin);
-    f(x, t0);
+#pragma unroll 1
+  for (int g = 0; (int64_t)g * 4 * NT < V; g += K) {
+    float x[K][4];
+    load_chunks<NT, K, BF16, VEC>(rv, 0, V, g, x, nonfin);
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      const int64_t t0 = 4 * ((int64_t)(g + i) * NT + threadIdx.x);
+      if (t0 < V) f(x[i], t0);
+    }
   }
 }
 
