@@ -10,5 +10,5 @@ from ._binding import (  # noqa: F401
     FLAG_NEED_MIN_P, FLAG_NEED_PENALTY, FLAG_NEED_TOP_K, FLAG_NEED_TOP_P, LIB_PATH,
     STATUS_INVALID, STATUS_OK, STATUS_OVERFLOW, Batch, HostParams, PackedBatch, SamplerError,
     Workspace, apply_bitmask, apply_transforms, bias_from_dict, csr, lib, pack_host, sample,
-    set_algo, strerror, time_next, version,
+    set_algo, set_trace, strerror, time_next, version,
 )

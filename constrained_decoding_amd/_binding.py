@@ -21,6 +21,7 @@ FLAG_ALL_GREEDY, FLAG_ANY_GREEDY = 1 << 0, 1 << 1
 FLAG_NEED_TOP_K, FLAG_NEED_TOP_P, FLAG_NEED_MIN_P = 1 << 2, 1 << 3, 1 << 4
 FLAG_NEED_PENALTY, FLAG_HAS_BIAS = 1 << 5, 1 << 6
 OPT_ALGO = 1
+OPT_TRACE = 2
 
 EXPORTS = [
     "sampler_strerror", "sampler_version", "sampler_params_bytes", "sampler_pack_params",
@@ -311,6 +312,13 @@ def sample(packed: PackedBatch, logits, *, bitmask=None, row_has_mask=None, work
 def set_algo(algo: int):
     """0: fast path (default); 1: row-serial exact path for every row."""
     _check(lib.sampler_set_option(OPT_ALGO, int(algo)), "sampler_set_option")
+
+
+def set_trace(buf=None):
+    """Diagnostic phase timestamps: ``buf`` is a device int64 tensor of 8 words
+    per workgroup of the sampling kernel (see SAMPLER_OPT_TRACE), or None."""
+    _check(lib.sampler_set_option(OPT_TRACE, 0 if buf is None else int(buf.data_ptr())),
+           "sampler_set_option")
 
 
 def time_next(kernel: int, start_event, stop_event):

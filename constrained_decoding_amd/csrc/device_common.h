@@ -330,14 +330,17 @@ __device__ __forceinline__ void load_chunks(const RowView& rv, int64_t lo, int64
     }
     return;
   }
-  int64_t ta[N];
-  bool in[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) {
-    const int64_t t0 = lo + 4 * ((int64_t)(first + i) * NT + threadIdx.x);
-    in[i] = t0 < hi;
-    ta[i] = in[i] ? t0 : lo;
-  }
+  // 32-bit unsigned byte offsets (V < 2^24) from the row base, which is the
+  // same for the whole workgroup: loads take the scalar-base + 32-bit vector
+  // offset form, and no 64-bit address per chunk stays live
+  const uint32_t tb = (uint32_t)lo + 4u * (uint32_t)threadIdx.x + 4u * (uint32_t)(NT * first);
+  const uint32_t hi32 = (uint32_t)hi, lo32 = (uint32_t)lo;
+  auto tok = [&](int i) {
+    const uint32_t t = tb + 4u * (uint32_t)(NT * i);
+    return t < hi32 ? t : lo32;
+  };
+  const unsigned char* base = BF16 ? reinterpret_cast<const unsigned char*>(rv.b16)
+                                   : reinterpret_cast<const unsigned char*>(rv.f32);
   // STREAM: non-temporal loads, for data no later pass reads again
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
@@ -345,7 +348,7 @@ __device__ __forceinline__ void load_chunks(const RowView& rv, int64_t lo, int64
   if (BF16) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const u32x2* src = reinterpret_cast<const u32x2*>(rv.b16 + ta[i]);
+      const u32x2* src = reinterpret_cast<const u32x2*>(base + tok(i) * 2u);
       const u32x2 u = STREAM ? __builtin_nontemporal_load(src) : *src;
       raw[i][0] = u.x << 16;
       raw[i][1] = u.x & 0xFFFF0000u;
@@ -355,7 +358,7 @@ __device__ __forceinline__ void load_chunks(const RowView& rv, int64_t lo, int64
   } else {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(rv.f32 + ta[i]);
+      const u32x4* src = reinterpret_cast<const u32x4*>(base + tok(i) * 4u);
       const u32x4 u = STREAM ? __builtin_nontemporal_load(src) : *src;
       raw[i][0] = u.x;
       raw[i][1] = u.y;
@@ -369,11 +372,20 @@ __device__ __forceinline__ void load_chunks(const RowView& rv, int64_t lo, int64
   // such a row ends with status OVERFLOW whatever the kernels compute for it,
   // so consumers only have to keep their indexing in bounds for them.
   uint32_t nf = 0u;
+  // token offsets again, from an opaque copy of the base: the compiler would
+  // otherwise keep every chunk's offset live from the loads to here
+  uint32_t tb2 = tb;
+  asm volatile("" : "+v"(tb2));
 #pragma unroll
   for (int i = 0; i < N; ++i) {
+    const uint32_t t = tb2 + 4u * (uint32_t)(NT * i);
     uint32_t bits = 0xFu;
-    if (rv.mrow) bits = ((uint32_t)rv.mrow[ta[i] >> 5] >> (uint32_t)(ta[i] & 31)) & 0xFu;
-    if (!in[i]) bits = 0u;
+    if (rv.mrow) {
+      const uint32_t tc = t < hi32 ? t : lo32;
+      bits = (*reinterpret_cast<const uint32_t*>(reinterpret_cast<const unsigned char*>(rv.mrow) +
+                                                  ((tc >> 5) << 2)) >> (t & 31u)) & 0xFu;
+    }
+    if (t >= hi32) bits = 0u;
 #pragma unroll
     for (int q = 0; q < 4; ++q) x[i][q] = __uint_as_float(raw[i][q]);
     if (bits != 0xFu) {

@@ -11,8 +11,7 @@ namespace cds {
 
 struct SampleArgs {
   const RowParams* rows;
-  const int32_t* sampled;  // the rows that are not greedy, ascending
-  int32_t n_sampled;
+  const int32_t* order;  // dispatch order of the B rows (sampler_batch.d_sampled)
   const void* logits;
   int64_t ld;
   int32_t B, V;
@@ -32,6 +31,7 @@ struct SampleArgs {
   int64_t S;
   uint64_t spin_limit;  // wall-clock ticks a race task waits for its row's plan
   uint32_t gen;         // call generation (nonzero, differs from the previous call's)
+  unsigned long long* trace;  // 8 words per workgroup of phase timestamps, or nullptr
 };
 
 // Optional timing events recorded around the sampling kernel.

@@ -468,6 +468,11 @@ __device__ __forceinline__ bool gen_wait(const uint32_t* p, uint32_t gen, uint64
   return true;
 }
 
+// A value every lane of the wave holds, moved to a scalar register.
+__device__ __forceinline__ float sgpr_f(float v) {
+  return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(v)));
+}
+
 // ---- phase 2: the plan ----------------------------------------------------------
 template <int NT>
 struct PlanShared {
@@ -488,12 +493,12 @@ struct PlanShared {
 // the output of rows that end here (greedy, no finite token, non-finite
 // token) and the plan to a.plans[r] and to *out (LDS).
 template <int NT>
-__device__ __forceinline__ void plan_row(const SampleArgs& a, int r, PlanShared<NT>& ps, Plan* out) {
+__device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, PlanShared<NT>& ps,
+                                         Plan* out) {
   const int tid = threadIdx.x, P = a.P;
   const RowParams rp = a.rows[r];
   const bool greedy = (rp.flags & ROW_GREEDY) != 0;
   const bool topk = (rp.flags & ROW_TOPK) != 0, topp = (rp.flags & ROW_TOPP) != 0;
-  const bool hist = !greedy && (topk || topp);
   const double Td = (double)rp.temperature;
   // merge the slice heads: wave 0, lane j holds slice j (P <= 64)
   if (tid < 64) {
@@ -755,6 +760,12 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Pla
       b.t1 = sb.t1;
       b.z1 = sb.z1;
       b.k2 = sb.k2;
+      if (sb.pad[0]) {  // keys relative to the slice maximum: shift to the row's
+        const float sh_k = (__uint_as_float(sb.pad[1]) - pl.zmax) *
+                           (float)(1.0 / (double)rp.temperature);
+        b.k1 += sh_k;
+        b.k2 += sh_k;
+      }
       cnt = sb.ucnt > (uint32_t)SCAP ? (uint32_t)UCAP + 1u : sb.ucnt;
     }
     uint32_t incl = cnt;
@@ -796,27 +807,32 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Pla
 #pragma unroll 1
     for (int i = tid; i < n; i += NT) cnt += inK(ul[i]) ? 1 : 0;
     cnt = block_sum_i32<NT>(cnt, red);
-    if (cnt < pl.k_rank) return false;
-    uint32_t prefix = 0, pmask = 0;
-    unsigned long long krem = (unsigned long long)pl.k_rank;
+    // A boundary list short of k_rank contradicts the plan.  A candidate list
+    // (list_mode) holds every token of the min-p set when that set has at most
+    // k tokens; top-k then cuts nothing.
+    if (cnt < pl.k_rank && !pl.list_mode) return false;
+    if (cnt >= pl.k_rank) {
+      uint32_t prefix = 0, pmask = 0;
+      unsigned long long krem = (unsigned long long)pl.k_rank;
 #pragma unroll 1
-    for (int shift = 24; shift >= 0; shift -= 8) {
-      if (tid < 256) sh.hist[tid] = 0ull;
-      __syncthreads();
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        if (tid < 256) sh.hist[tid] = 0ull;
+        __syncthreads();
 #pragma unroll 1
-      for (int i = tid; i < n; i += NT) {
-        const unsigned long long e = ul[i];
-        const uint32_t u = (uint32_t)(e >> 32);
-        if (inK(e) && (u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & 255u], 1ull);
+        for (int i = tid; i < n; i += NT) {
+          const unsigned long long e = ul[i];
+          const uint32_t u = (uint32_t)(e >> 32);
+          if (inK(e) && (u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & 255u], 1ull);
+        }
+        __syncthreads();
+        unsigned long long above;
+        const int d = pick_digit<NT>(sh, (double)krem, 0ull, &above);
+        krem -= above;
+        prefix |= (uint32_t)d << shift;
+        pmask |= 255u << shift;
       }
-      __syncthreads();
-      unsigned long long above;
-      const int d = pick_digit<NT>(sh, (double)krem, 0ull, &above);
-      krem -= above;
-      prefix |= (uint32_t)d << shift;
-      pmask |= 255u << shift;
+      zc12 = fmaxf(zc12, from_okey(prefix));
     }
-    zc12 = fmaxf(zc12, from_okey(prefix));
   }
   float zfin = zc12;
 
@@ -924,21 +940,104 @@ union FusedLds {
     uint64_t list[UCAP];
     int32_t off[kMaxSlices + 1];
   } fin;
+  struct {
+    ExactShared<NT> ex;
+    uint32_t gm[kMaxChunks * NT];  // group maxima (order keys)
+  } sel;
   uint64_t stage[SCAP];
 };
 
-// STREAM: non-temporal loads, for slices no race task reads again (greedy
-// rows); the slices of other rows should stay in the caches for their race.
+
+__device__ __forceinline__ int row_class(const RowParams& rp) {
+  return (int)row_class_of(rp.flags, rp.top_k);
+}
+
+// Appends the slice's tokens whose value passes keep() to the LDS stage as
+// okey(v) << 32 | ~t: one LDS reservation per wave and chunk, only where some
+// lane holds such a token.  *cnt (LDS) counts them all (stage holds SCAP).
+template <int NT, int E4, typename Keep>
+__device__ __forceinline__ void stage_tokens(const float (&x)[E4][4], int32_t tbase,
+                                             uint64_t* stage, uint32_t* cnt, Keep keep) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int i = 0; i < E4; ++i) {
+    uint32_t um = 0u;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) um |= keep(x[i][q]) ? (1u << q) : 0u;
+    if (__any(um)) {
+      int32_t tb = tbase;
+      asm volatile("" : "+v"(tb));
+      const int32_t t0 = tb + 4 * NT * i;
+      const uint32_t c = (uint32_t)__popc(um);
+      const uint32_t incl = wave_incl_sum(c);
+      uint32_t base = 0;
+      if (lane == 63) base = atomicAdd(cnt, incl);
+      base = (uint32_t)__builtin_amdgcn_readlane((int)base, 63);
+      uint32_t pos = base + incl - c;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if ((um >> q) & 1u) {
+          if (pos < (uint32_t)SCAP)
+            stage[pos] = ((uint64_t)okey(x[i][q] + 0.0f) << 32) |
+                         (uint64_t)(0xFFFFFFFFu - (uint32_t)(t0 + q));
+          ++pos;
+        }
+    }
+  }
+}
+
+// Smallest fp32 value v with exp(v/T - zmax/T) >= min_p (the min-p set
+// relative to zmax is {z >= v}); -inf when every finite value qualifies.  Wave
+// 0 only; every lane of it gets the result.
+__device__ __forceinline__ float minp_cut_wave(float zmax, double Td, float min_p) {
+  const double m = (double)zmax / Td, mp = (double)min_p;
+  auto pred = [&](uint32_t k) { return exp((double)from_okey(k) / Td - m) >= mp; };
+  if (pred(okey(-FLT_MAX))) return CDS_NEG_INF;
+  return from_okey(wave_first_true(okey(-FLT_MAX), okey(zmax), pred));
+}
+
+// One workgroup per slice of a row.  The slice is streamed once into
+// registers (bf16 upcast and the grammar bitmask fused into the load) and is
+// never read again from memory.  Every slice reduces max, lowest argmax and the
+// non-finite flag, then by row class:
+//   GREEDY  sum exp((z - max)) for the logprob;
+//   RACE    sum exp((z - max)/T), and the race over all its tokens (keys
+//           relative to the slice maximum);
+//   LIST    sum exp((z - max)/T), and a list of its tokens that may survive:
+//           for top-k rows every token at or above the top_k-th largest of a
+//           set of group maxima (which is at most the slice's own top_k-th
+//           value), for min-p rows every token at or above the min-p cut
+//           relative to the slice maximum (at most the row's cut);
+//   HOLD    a histogram of s = z/T on a power-of-two grid (counts and masses).
+// The slice publishes its summary and takes the row's arrival ticket; the last
+// slice of the row (the planner) merges the summaries.  GREEDY, RACE and LIST
+// rows are then resolved by the planner alone: the other slices have exited.
+// HOLD rows need the row's top-p cut before the race: the planner publishes a
+// plan (min-p cut, the value range of sure tokens, the top-p boundary bins),
+// the other slices wait for it with their slice still in registers, race their
+// sure tokens, list their boundary tokens and take the done ticket; the last
+// one resolves the boundary list.  A wait that times out marks the row, whose
+// finisher then takes the exact path, so results never depend on timing.
+// STREAM: non-temporal loads, for greedy rows (read once).
+// Diagnostic phase timestamp k of this workgroup (SAMPLER_OPT_TRACE).
+#define CDS_TRACE(k)                                                             \
+  do {                                                                           \
+    if (a.trace && threadIdx.x == 0) a.trace[(size_t)blockIdx.x * 8 + (k)] = wall_clock64(); \
+  } while (0)
+
 template <int NT, int E4, bool BF16, bool VEC, bool STREAM>
-__device__ __forceinline__ void scan_task(const SampleArgs& a, int r, int sl, FusedLds<NT>& sh,
-                          RedScratch<NT>& red, Plan* s_plan, uint32_t* s_word) {
+__device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, FusedLds<NT>& sh,
+                                           RedScratch<NT>& red, Plan* s_plan, uint32_t* s_word) {
   const int tid = threadIdx.x, P = a.P;
   const RowParams rp = a.rows[r];
-  const bool greedy = (rp.flags & ROW_GREEDY) != 0;
-  const bool hist = !greedy && (rp.flags & (ROW_TOPK | ROW_TOPP));
+  const int cls = row_class(rp);
+  const bool greedy = cls == CLS_GREEDY;
   const int64_t lo = (int64_t)sl * a.S;
   const int64_t hi = min(lo + a.S, (int64_t)a.V);
+  const int32_t tbase = (int32_t)lo + 4 * tid;  // token of chunk i: tbase + 4*NT*i
   const RowView rv = row_view<BF16>(a, r);
+  const int64_t slot = (int64_t)r * P + sl;
+  CDS_TRACE(1);
 
   float x[E4][4];
   uint32_t nonfin = 0;
@@ -957,16 +1056,16 @@ __device__ __forceinline__ void scan_task(const SampleArgs& a, int r, int sl, Fu
     for (int i = E4 - 1; i >= 0; --i)
 #pragma unroll
       for (int q = 3; q >= 0; --q)
-        if (x[i][q] == zm) am = (int32_t)(lo + 4 * ((int64_t)i * NT + tid) + q);
+        if (x[i][q] == zm) am = tbase + 4 * NT * i + q;
   }
+  CDS_TRACE(2);
   am = block_min_i32<NT>(am, red);
   nonfin = block_or_u32<NT>(nonfin, red);
 
-  const int64_t slot = (int64_t)r * P + sl;
   uint32_t flags = nonfin ? SLICE_NONFINITE : 0u;
   double se = 0.0;
   float kmax = 0.0f;
-  if (!hist) {
+  if (cls != CLS_HOLD) {
     // sum exp((z - zmax) / T_eff): the row's log-partition for the logprob
     const float cexp = (greedy ? 1.0f : (float)(1.0 / (double)rp.temperature)) * kLog2e;
     if (zm != CDS_NEG_INF) {
@@ -1016,6 +1115,162 @@ __device__ __forceinline__ void scan_task(const SampleArgs& a, int r, int sl, Fu
       }
     }
   }
+
+  CDS_TRACE(3);
+  if (cls == CLS_RACE && zm != CDS_NEG_INF && !nonfin) {
+    // the race over every allowed token, keys relative to the slice maximum
+    const float invT32 = sgpr_f((float)(1.0 / (double)rp.temperature));
+    const uint32_t k0 = (uint32_t)rp.seed, k1 = (uint32_t)(rp.seed >> 32);
+    const uint32_t off_lo = (uint32_t)rp.offset, off_hi = (uint32_t)(rp.offset >> 32);
+    Top2 b = top2_init();
+#pragma unroll
+    for (int i = 0; i < E4; ++i) {
+      int32_t tb = tbase;
+      asm volatile("" : "+v"(tb));
+      const int32_t t0 = tb + 4 * NT * i;
+      bool need = false;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) need |= race32_hopeful(b, x[i][q], zm, invT32);
+      if (need) {
+        const uint4 blk =
+            philox4x32_10(make_uint4((uint32_t)t0 >> 2, off_lo, off_hi, 0u), k0, k1);
+        const uint32_t xs[4] = {blk.x, blk.y, blk.z, blk.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (x[i][q] != CDS_NEG_INF) race32(b, x[i][q], t0 + q, xs[q], zm, invT32);
+      }
+    }
+    block_top2<NT>(b, red);
+    if (tid == 0) {
+      SliceBest sb;
+      sb.k1 = b.k1;
+      sb.t1 = b.t1;
+      sb.z1 = b.z1;
+      sb.k2 = b.k2;
+      sb.ucnt = 0u;
+      sb.pad[0] = 1u;
+      sb.pad[1] = __float_as_uint(zm);
+      sb.pad[2] = 0u;
+      st_obj(&a.bests[slot], sb);
+    }
+  } else if (cls == CLS_LIST && zm != CDS_NEG_INF && !nonfin) {
+    // a superset of the slice's candidates, listed
+    float cut = CDS_NEG_INF;
+    if (rp.flags & ROW_TOPK) {
+      // L = the q-th largest of NT*h group maxima (group g of thread tid =
+      // chunks [g*E4/h, (g+1)*E4/h)): at least q tokens lie at or above it, so
+      // it is at most the slice's own q-th largest value.  With about 4q
+      // groups few tokens beyond the q largest pass it.
+      const int q = min(rp.top_k, SCAP);
+      const int h = min(E4, (4 * q + NT - 1) / NT);
+      const int n = h * NT;
+#pragma unroll
+      for (int g = 0; g < E4; ++g) {
+        if (g < h) {
+          float gmx = CDS_NEG_INF;
+#pragma unroll
+          for (int i = 0; i < E4; ++i)
+            if ((i * h) / E4 == g)
+              gmx = fmaxf(gmx, fmaxf(fmaxf(x[i][0], x[i][1]), fmaxf(x[i][2], x[i][3])));
+          sh.sel.gm[g * NT + tid] = okey(gmx + 0.0f);
+        }
+      }
+      __syncthreads();
+      uint32_t prefix = 0, pmask = 0;
+      unsigned long long krem = (unsigned long long)q;
+#pragma unroll 1
+      for (int shift = 24; shift >= 0; shift -= 8) {
+        if (tid < 256) sh.sel.ex.hist[tid] = 0ull;
+        __syncthreads();
+        for (int i = tid; i < n; i += NT) {
+          const uint32_t u = sh.sel.gm[i];
+          if ((u & pmask) == prefix) atomicAdd(&sh.sel.ex.hist[(u >> shift) & 255u], 1ull);
+        }
+        __syncthreads();
+        unsigned long long above;
+        const int d = pick_digit<NT>(sh.sel.ex, (double)krem, 0ull, &above);
+        krem -= above;
+        prefix |= (uint32_t)d << shift;
+        pmask |= 255u << shift;
+      }
+      cut = from_okey(prefix);
+      // more than SCAP tokens at or above L: cut at the exact q-th largest
+      // value instead (a radix select over the tokens >= L, in registers)
+      const float lcut = sgpr_f(cut);
+      int c = 0;
+#pragma unroll
+      for (int i = 0; i < E4; ++i)
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) c += (x[i][qq] >= lcut && x[i][qq] != CDS_NEG_INF) ? 1 : 0;
+      c = block_sum_i32<NT>(c, red);
+      if (c > SCAP) {
+        uint32_t pfx = 0, pm = 0;
+        unsigned long long kr = (unsigned long long)q;
+#pragma unroll 1
+        for (int shift = 24; shift >= 0; shift -= 8) {
+          if (tid < 256) sh.sel.ex.hist[tid] = 0ull;
+          __syncthreads();
+#pragma unroll
+          for (int i = 0; i < E4; ++i)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              const float v = x[i][qq];
+              const uint32_t u = okey(v + 0.0f);
+              if (v >= lcut && v != CDS_NEG_INF && (u & pm) == pfx)
+                atomicAdd(&sh.sel.ex.hist[(u >> shift) & 255u], 1ull);
+            }
+          __syncthreads();
+          unsigned long long above;
+          const int d = pick_digit<NT>(sh.sel.ex, (double)kr, 0ull, &above);
+          kr -= above;
+          pfx |= (uint32_t)d << shift;
+          pm |= 255u << shift;
+        }
+        cut = from_okey(pfx);
+      }
+    }
+    if (rp.flags & ROW_MINP) {
+      if (tid < 64) {
+        const float c = minp_cut_wave(zm, (double)rp.temperature, rp.min_p);
+        if (tid == 0) sh.sel.ex.fshare = c;
+      }
+      __syncthreads();
+      cut = fmaxf(cut, sh.sel.ex.fshare);
+    }
+    if (tid == 0) s_word[1] = 0u;
+    __syncthreads();
+    const float cutv = sgpr_f(cut);
+    stage_tokens<NT, E4>(x, tbase, sh.stage, &s_word[1],
+                         [&](float v) { return v >= cutv && v != CDS_NEG_INF; });
+    __syncthreads();
+    const uint32_t nst = s_word[1];
+    if (nst <= (uint32_t)SCAP) {
+      uint64_t* ul = a.ulist + slot * SCAP;
+      for (uint32_t i = tid; i < nst; i += NT) st_u64(ul + i, sh.stage[i]);
+    }
+    if (tid == 0) {
+      SliceBest sb;
+      sb.k1 = CDS_NEG_INF;
+      sb.t1 = INT_MAX;
+      sb.z1 = CDS_NEG_INF;
+      sb.k2 = CDS_NEG_INF;
+      sb.ucnt = nst;
+      sb.pad[0] = sb.pad[1] = sb.pad[2] = 0u;
+      st_obj(&a.bests[slot], sb);
+    }
+  } else if ((cls == CLS_RACE || cls == CLS_LIST) && tid == 0) {
+    // nothing allowed or a non-finite value: the planner answers the row
+    SliceBest sb;
+    sb.k1 = CDS_NEG_INF;
+    sb.t1 = INT_MAX;
+    sb.z1 = CDS_NEG_INF;
+    sb.k2 = CDS_NEG_INF;
+    sb.ucnt = 0u;
+    sb.pad[0] = sb.pad[1] = sb.pad[2] = 0u;
+    st_obj(&a.bests[slot], sb);
+  }
+
+  CDS_TRACE(4);
   if (tid == 0) {
     SliceHead h;
     h.zmax = zm;
@@ -1031,23 +1286,61 @@ __device__ __forceinline__ void scan_task(const SampleArgs& a, int r, int sl, Fu
   RowSync* sy = &a.sync[r];
   if (tid == 0) s_word[0] = gen_add(&sy->arrive, a.gen, 1u);
   __syncthreads();
-  if (s_word[0] != (uint32_t)(P - 1)) return;
-  // the last slice of the row: the plan
-  plan_row<NT>(a, r, sh.plan, s_plan);
-  if (tid == 0 && !greedy) {
-    vm_drain();  // the plan (written by this thread) before its flag
-    st_u32(&sy->ready, a.gen);
+  const bool planner = s_word[0] == (uint32_t)(P - 1);
+  if (a.trace && tid == 0)
+    a.trace[(size_t)blockIdx.x * 8] = (unsigned long long)r | ((unsigned long long)sl << 20) |
+                                      ((unsigned long long)cls << 28) |
+                                      ((unsigned long long)planner << 31);
+  CDS_TRACE(5);
+  if (cls != CLS_HOLD) {
+    if (!planner) {
+      CDS_TRACE(7);
+      return;
+    }
+    // the last slice of the row resolves it from the summaries and lists
+    plan_row<NT>(a, r, false, sh.plan, s_plan);
+    __syncthreads();
+    CDS_TRACE(6);
+    if (greedy) {
+      CDS_TRACE(7);
+      return;
+    }
+    Plan pl = *s_plan;
+    if (pl.mode != PLAN_FAST) return;  // answered (no finite token, non-finite)
+    pl.list_mode = 1;
+    pl.z_sure = CDS_NEG_INF;
+    pl.m_sure = pl.m_mid = 0.0;
+    pl.p = (double)rp.top_p;
+    pl.k_rank = 0;
+    pl.topp = 0;
+    pl.a_lo = pl.a_hi = pl.k_lo = pl.k_hi = CDS_POS_INF;
+    if (rp.flags & ROW_TOPK) {
+      pl.k_rank = rp.top_k;
+      pl.k_lo = pl.zcut1;  // the k-th largest within the min-p set
+      pl.k_hi = CDS_POS_INF;
+    }
+    if (rp.flags & ROW_TOPP) {
+      pl.topp = 1;
+      pl.a_lo = -FLT_MAX;
+      pl.a_hi = pl.zmax;   // masses exp((z - zmax)/T) <= 1
+    }
+    if (!finish_row<NT, BF16, VEC>(a, r, pl, sh.fin.ex, sh.fin.list, sh.fin.off, red)) {
+      __syncthreads();
+      row_exact<NT, BF16, VEC>(a, r, sh.fin.ex);
+      if (tid == 0) a.plans[r].path = PATH_EXACT;
+    }
+    CDS_TRACE(7);
+    return;
   }
-}
 
-template <int NT, int E4, bool BF16, bool VEC>
-__device__ __forceinline__ void race_task(const SampleArgs& a, int r, int sl, FusedLds<NT>& sh,
-                          RedScratch<NT>& red, Plan* s_plan, uint32_t* s_word) {
-  const int tid = threadIdx.x, P = a.P;
-  const RowParams rp = a.rows[r];
-  if (rp.flags & ROW_GREEDY) return;  // answered by the scan tasks
-  RowSync* sy = &a.sync[r];
-  if (tid == 0) {
+  // ---- HOLD rows: the plan, then the race from registers ----
+  if (planner) {
+    plan_row<NT>(a, r, true, sh.plan, s_plan);
+    if (tid == 0) {
+      vm_drain();  // the plan (written by this thread) before its flag
+      st_u32(&sy->ready, a.gen);
+    }
+  } else if (tid == 0) {
     if (gen_wait(&sy->ready, a.gen, a.spin_limit)) {
       *s_plan = ld_obj(&a.plans[r]);
     } else {
@@ -1055,86 +1348,47 @@ __device__ __forceinline__ void race_task(const SampleArgs& a, int r, int sl, Fu
       st_u32(&sy->failed, a.gen);
     }
   }
+  if (tid == 0) s_word[1] = 0u;
   __syncthreads();
-  const int64_t lo = (int64_t)sl * a.S;
-  const int64_t hi = min(lo + a.S, (int64_t)a.V);
-  const int64_t slot = (int64_t)r * P + sl;
+  CDS_TRACE(6);
 
   if (s_plan->mode == PLAN_FAST) {
-    const RowView rv = row_view<BF16>(a, r);
-    const RaceCtx c = make_race_ctx(rp, s_plan->zmax);
-    const float zc1 = s_plan->zcut1;
-    const float zs = fmaxf(fmaxf(s_plan->z_sure, zc1), -FLT_MAX);
-    const float a_lo = s_plan->a_lo, a_hi = s_plan->a_hi;
-    const float k_lo = s_plan->k_lo, k_hi = s_plan->k_hi;
+    // plan values are uniform: keep them in scalar registers (the slice holds
+    // 4*E4 vector registers)
+    const float zmax = sgpr_f(s_plan->zmax);
+    const float invT32 = sgpr_f((float)(1.0 / (double)rp.temperature));
+    const uint32_t k0 = (uint32_t)rp.seed, k1 = (uint32_t)(rp.seed >> 32);
+    const uint32_t off_lo = (uint32_t)rp.offset, off_hi = (uint32_t)(rp.offset >> 32);
+    const float zc1 = sgpr_f(s_plan->zcut1);
+    const float zs = fmaxf(fmaxf(sgpr_f(s_plan->z_sure), zc1), -FLT_MAX);
+    const float a_lo = sgpr_f(s_plan->a_lo), a_hi = sgpr_f(s_plan->a_hi);
+    const float k_lo = sgpr_f(s_plan->k_lo), k_hi = sgpr_f(s_plan->k_hi);
     const bool has_u = a_lo < a_hi || k_lo < k_hi;
-    const int lane = tid & 63;
     Top2 b = top2_init();
-    uint32_t nonfin = 0;
-    // groups of G chunks, the next group's loads in flight while one is
-    // raced (the slice was just streamed by the scan task, so it comes from
-    // the caches); boundary tokens are staged in LDS, one reservation per wave
-    constexpr int G = E4 < 4 ? E4 : 4;
-    if (tid == 0) s_word[1] = 0u;
-    __syncthreads();
-    float x[G][4], xn[G][4];
-    load_chunks<NT, G, BF16, VEC>(rv, lo, hi, 0, x, nonfin);
-#pragma unroll 1
-    for (int g0 = 0; g0 < E4; g0 += G) {
-      if (g0 + G < E4) load_chunks<NT, G, BF16, VEC>(rv, lo, hi, g0 + G, xn, nonfin);
-      int32_t ucnt = 0;
+    // the race over the sure tokens
 #pragma unroll
-      for (int i = 0; i < G; ++i) {
-        const int64_t t0 = lo + 4 * ((int64_t)(g0 + i) * NT + tid);
-        bool need = false;
+    for (int i = 0; i < E4; ++i) {
+      int32_t tb = tbase;
+      asm volatile("" : "+v"(tb));
+      const int32_t t0 = tb + 4 * NT * i;
+      bool need = false;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        need |= x[i][q] >= zs && race32_hopeful(b, x[i][q], zmax, invT32);
+      if (need) {
+        const uint4 blk =
+            philox4x32_10(make_uint4((uint32_t)t0 >> 2, off_lo, off_hi, 0u), k0, k1);
+        const uint32_t xs[4] = {blk.x, blk.y, blk.z, blk.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          need |= x[i][q] >= zs && race32_hopeful(b, x[i][q], c.zmax, c.invT32);
-        if (need) {
-          const uint4 blk = race_block(c, t0);
-          const uint32_t xs[4] = {blk.x, blk.y, blk.z, blk.w};
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            if (x[i][q] >= zs) race32(b, x[i][q], (int32_t)(t0 + q), xs[q], c.zmax, c.invT32);
-        }
-        if (has_u) {
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-            ucnt += is_boundary(x[i][q], zs, zc1, a_lo, a_hi, k_lo, k_hi) ? 1 : 0;
-        }
+          if (x[i][q] >= zs) race32(b, x[i][q], t0 + q, xs[q], zmax, invT32);
       }
-      if (has_u && __any(ucnt)) {
-        int32_t incl = ucnt;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-          const int32_t y = __shfl_up(incl, o, 64);
-          if (lane >= o) incl += y;
-        }
-        uint32_t base = 0;
-        if (lane == 63) base = atomicAdd(&s_word[1], (uint32_t)incl);
-        base = __shfl(base, 63, 64);
-        uint32_t pos = base + (uint32_t)(incl - ucnt);
-        if (ucnt) {
-#pragma unroll
-          for (int i = 0; i < G; ++i)
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              const float v = x[i][q];
-              if (is_boundary(v, zs, zc1, a_lo, a_hi, k_lo, k_hi)) {
-                if (pos < (uint32_t)SCAP)
-                  sh.stage[pos] = ((uint64_t)okey(v + 0.0f) << 32) |
-                                  (uint64_t)(0xFFFFFFFFu -
-                                             (uint32_t)(lo + 4 * ((int64_t)(g0 + i) * NT + tid) + q));
-                ++pos;
-              }
-            }
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < G; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) x[i][q] = xn[i][q];
     }
+    // the boundary-bin tokens, listed
+    if (has_u)
+      stage_tokens<NT, E4>(x, tbase, sh.stage, &s_word[1], [&](float v) {
+        return is_boundary(v, zs, zc1, a_lo, a_hi, k_lo, k_hi);
+      });
     __syncthreads();
     const uint32_t nst = s_word[1];
     if (nst && nst <= (uint32_t)SCAP) {
@@ -1154,12 +1408,15 @@ __device__ __forceinline__ void race_task(const SampleArgs& a, int r, int sl, Fu
     }
   }
 
-  // the last race task of the row finishes it
+  // the last slice of the row to finish its race resolves the row
   vm_drain();
   __syncthreads();
   if (tid == 0) s_word[0] = gen_add(&sy->done, a.gen, 1u);
   __syncthreads();
-  if (s_word[0] != (uint32_t)(P - 1)) return;
+  if (s_word[0] != (uint32_t)(P - 1)) {
+    CDS_TRACE(7);
+    return;
+  }
   if (tid == 0) s_word[0] = ld_u32(&sy->failed) == a.gen;
   __syncthreads();
   const bool failed = s_word[0] != 0u;
@@ -1171,30 +1428,28 @@ __device__ __forceinline__ void race_task(const SampleArgs& a, int r, int sl, Fu
     row_exact<NT, BF16, VEC>(a, r, sh.fin.ex);
     if (tid == 0) a.plans[r].path = PATH_EXACT;
   }
+  CDS_TRACE(7);
 }
 
-// Four waves per SIMD (<= 128 VGPRs): 4 workgroups of 256 threads per CU.
+#ifndef CDS_WAVES_PER_EU
+#define CDS_WAVES_PER_EU 4
+#endif
+// CDS_WAVES_PER_EU waves per SIMD (the slice takes 4*E4 vector registers).
 template <int NT, int E4, bool BF16, bool VEC>
-__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(4))) void sample_kernel(
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CDS_WAVES_PER_EU))) void sample_kernel(
     const SampleArgs a) {
   __shared__ RedScratch<NT> red;
   __shared__ FusedLds<NT> sh;
   __shared__ Plan s_plan;
   __shared__ uint32_t s_word[2];
-  // Blocks [0, B*P): scan tasks (row block/P); then race tasks for the rows
-  // that are not greedy (the i-th of them for block/P - B = i); slice =
-  // block % P.  Every race task follows its row's scan tasks.
+  // block -> (the grp-th row of the packed row order, slice)
   const int grp = (int)(blockIdx.x / (unsigned)a.P);
   const int sl = (int)(blockIdx.x - (unsigned)grp * (unsigned)a.P);
-  if (grp < a.B) {
-    if (a.rows[grp].flags & ROW_GREEDY)
-      scan_task<NT, E4, BF16, VEC, true>(a, grp, sl, sh, red, &s_plan, s_word);
-    else
-      scan_task<NT, E4, BF16, VEC, false>(a, grp, sl, sh, red, &s_plan, s_word);
-  }
-  else {
-    race_task<NT, E4, BF16, VEC>(a, a.sampled[grp - a.B], sl, sh, red, &s_plan, s_word);
-  }
+  const int r = a.order[grp];
+  if (a.rows[r].flags & ROW_GREEDY)
+    slice_task<NT, E4, BF16, VEC, true>(a, r, sl, sh, red, &s_plan, s_word);
+  else
+    slice_task<NT, E4, BF16, VEC, false>(a, r, sl, sh, red, &s_plan, s_word);
 }
 
 // ============================================================================
@@ -1239,27 +1494,14 @@ static inline void rec(const KernelEvents* ev, bool start, hipStream_t s) {
   if (e) (void)hipEventRecord(e, s);
 }
 
-template <int E4, bool BF16, bool VEC>
+template <bool BF16, bool VEC>
 static hipError_t launch_fused(const SampleArgs& a, const KernelEvents* ev, hipStream_t s) {
+  if (a.S > kSliceMax) return hipErrorInvalidValue;
   rec(ev, true, s);
-  hipLaunchKernelGGL((sample_kernel<kScanThreads, E4, BF16, VEC>),
-                     dim3((unsigned)(a.B + a.n_sampled) * (unsigned)a.P), dim3(kScanThreads), 0, s,
-                     a);
+  hipLaunchKernelGGL((sample_kernel<kScanThreads, kMaxChunks, BF16, VEC>),
+                     dim3((unsigned)a.B * (unsigned)a.P), dim3(kScanThreads), 0, s, a);
   rec(ev, false, s);
   return hipGetLastError();
-}
-
-template <bool BF16, bool VEC>
-static hipError_t launch_fused_e4(const SampleArgs& a, const KernelEvents* ev, hipStream_t s) {
-  const int64_t e4 = (a.S + 4 * kScanThreads - 1) / (4 * kScanThreads);
-  if (e4 <= 1) return launch_fused<1, BF16, VEC>(a, ev, s);
-  if (e4 <= 2) return launch_fused<2, BF16, VEC>(a, ev, s);
-  if (e4 <= 4) return launch_fused<4, BF16, VEC>(a, ev, s);
-  if (e4 <= 8) return launch_fused<8, BF16, VEC>(a, ev, s);
-  if (e4 <= 12) return launch_fused<12, BF16, VEC>(a, ev, s);
-  if (e4 <= 16) return launch_fused<16, BF16, VEC>(a, ev, s);
-  if (e4 <= 20) return launch_fused<20, BF16, VEC>(a, ev, s);
-  return hipErrorInvalidValue;
 }
 
 template <bool BF16, bool VEC>
@@ -1272,7 +1514,7 @@ static hipError_t launch_any(const SampleArgs& a, int algo, const KernelEvents* 
     rec(ev, false, s);
     return hipGetLastError();
   }
-  return launch_fused_e4<BF16, VEC>(a, ev, s);
+  return launch_fused<BF16, VEC>(a, ev, s);
 }
 
 hipError_t launch_sample(const SampleArgs& a, bool bf16, bool vec, int algo,

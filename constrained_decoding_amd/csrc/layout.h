@@ -54,14 +54,40 @@ struct BiasEntry {
 // the race (the exponential-race key is bounded, see device_common.h) nor carry
 // mass that matters at the 1e-10 level.
 constexpr int NBINS = 560;
-constexpr int kScanThreads = 256;
-constexpr int kMaxChunks = 20;
-constexpr int64_t kSliceMax = (int64_t)kScanThreads * 4 * kMaxChunks;  // 20480 tokens
+#ifndef CDS_SCAN_THREADS
+#define CDS_SCAN_THREADS 512
+#endif
+#ifndef CDS_MAX_CHUNKS
+#define CDS_MAX_CHUNKS 15
+#endif
+constexpr int kScanThreads = CDS_SCAN_THREADS;
+constexpr int kMaxChunks = CDS_MAX_CHUNKS;
+constexpr int64_t kSliceMax = (int64_t)kScanThreads * 4 * kMaxChunks;  // 30720 tokens
 constexpr int kCountShift = 48;   // histogram word: count << 48 | fixed-point mass
-constexpr int UCAP = 4096;        // boundary tokens of a row the finisher holds on chip
-constexpr int SCAP = 2048;        // boundary tokens one slice can hand over
+constexpr int UCAP = 8192;        // listed tokens of a row the finisher holds on chip
+constexpr int SCAP = 2048;        // listed tokens one slice can hand over
 constexpr int kMaxSlices = 64;
 constexpr int kMaxRows = 65535;
+
+// How a row's slices work in the sampling kernel.  The host dispatches the rows
+// in the order HOLD, then RACE / LIST, then GREEDY.
+enum RowClass : uint32_t {
+  CLS_GREEDY = 0,  // argmax: the planner answers from the slice summaries
+  CLS_RACE = 1,    // no cut: each slice races all its tokens
+  CLS_LIST = 2,    // top-k (k <= SCAP) or min-p: each slice lists a superset of
+                   // its candidates; the planner resolves the row from the lists
+  CLS_HOLD = 3,    // top-p as the only cut, or top-k beyond SCAP: the slices
+                   // wait for the row's plan (histogram cuts)
+};
+
+// (constexpr: callable from host and device code alike)
+constexpr RowClass row_class_of(uint32_t flags, int32_t top_k) {
+  if (flags & ROW_GREEDY) return CLS_GREEDY;
+  if (flags & ROW_TOPK) return top_k <= SCAP ? CLS_LIST : CLS_HOLD;
+  if (flags & ROW_MINP) return CLS_LIST;
+  if (flags & ROW_TOPP) return CLS_HOLD;
+  return CLS_RACE;
+}
 
 // ---- workspace ------------------------------------------------------------
 // Per-row meeting point of the row's workgroups.  Counters hold the call's
@@ -91,13 +117,14 @@ struct SliceHead {
 };
 static_assert(sizeof(SliceHead) == 32, "SliceHead layout");
 
-struct SliceBest {  // fp32 race keys: the slice's best two, and its boundary tokens
+struct SliceBest {  // fp32 race keys: the slice's best two, and its listed tokens
   float k1;         // best key (-inf if the slice had no candidate)
   int32_t t1;       // its token
   float z1;         // its logit
   float k2;         // second-best key
-  uint32_t ucnt;    // boundary tokens in the slice's list (> SCAP: overflowed)
-  uint32_t pad[3];
+  uint32_t ucnt;    // tokens in the slice's list (> SCAP: overflowed)
+  uint32_t pad[3];  // pad[0] = 1: keys are relative to the slice maximum,
+                    // whose fp32 bits are pad[1]
 };
 static_assert(sizeof(SliceBest) == 32, "SliceBest layout");
 
@@ -119,8 +146,8 @@ struct alignas(16) Plan {
   double m_sure;     // mass (relative to exp(m)) of tokens >= z_sure
   double m_mid;      // mass of tokens below a_lo and at or above k_hi
   double p;          // top_p
-  int32_t path;      // how the finish kernel resolved the row (FinishPath)
-  int32_t pad;
+  int32_t path;      // how the row's finisher resolved the row (FinishPath)
+  int32_t list_mode; // 1: the slices' lists hold every candidate (no sure region)
 };
 static_assert(sizeof(Plan) == 96, "Plan layout");
 

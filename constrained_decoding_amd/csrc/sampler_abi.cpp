@@ -22,6 +22,7 @@ constexpr int32_t kMaxV = 1 << 24;
 constexpr int32_t kMaxB = kMaxRows;
 
 std::atomic<int> g_algo{0};
+std::atomic<unsigned long long> g_trace{0ull};  // SAMPLER_OPT_TRACE buffer
 // one-shot kernel timing hook (see sampler_time_next)
 std::atomic<uint32_t> g_gen{0u};  // call generations (see sampler_sample)
 std::atomic<void*> g_ev_start{nullptr};
@@ -29,8 +30,8 @@ std::atomic<void*> g_ev_stop{nullptr};
 
 inline bool finite_f(float x) { return std::isfinite(x); }
 
-// Device parameter block: RowParams[B] | int32 sampled-row list, room for B
-// (padded to 16 bytes) | PenEntry[n_pen] | BiasEntry[n_bias].
+// Device parameter block: RowParams[B] | int32 row order [B] (the dispatch order
+// of sampler_sample; padded to 16 bytes) | PenEntry[n_pen] | BiasEntry[n_bias].
 size_t list_bytes(int32_t B) { return ((size_t)B * sizeof(int32_t) + 15) / 16 * 16; }
 
 size_t params_bytes_exact(int32_t B, int64_t n_pen, int64_t n_bias) {
@@ -71,7 +72,7 @@ int pack_into(const sampler_host_params* h, std::vector<unsigned char>& out_buf,
   }
 
   std::vector<RowParams> rows((size_t)B);
-  std::vector<int32_t> sampled;
+  std::vector<int32_t> sampled, greedy_rows;
   std::vector<PenEntry> pen;
   std::vector<BiasEntry> bias;
   uint32_t flags = SAMPLER_FLAG_ALL_GREEDY;
@@ -106,6 +107,7 @@ int pack_into(const sampler_host_params* h, std::vector<unsigned char>& out_buf,
     rp.offset = h->offset ? h->offset[r] : (uint64_t)r;
     const bool greedy = (T < 1e-5f) || (k == 1);
     if (greedy) {
+      greedy_rows.push_back(r);
       rp.flags |= ROW_GREEDY;
       flags |= SAMPLER_FLAG_ANY_GREEDY;
     } else {
@@ -176,7 +178,19 @@ int pack_into(const sampler_host_params* h, std::vector<unsigned char>& out_buf,
   const size_t off_list = sizeof(RowParams) * (size_t)B;
   const size_t off_pen = off_list + list_bytes(B);
   std::memcpy(p, rows.data(), sizeof(RowParams) * rows.size());
-  std::memcpy(p + off_list, sampled.data(), sizeof(int32_t) * sampled.size());
+  // dispatch order: rows whose slices wait for the row's plan first, then the
+  // other sampled rows, then the greedy rows
+  std::vector<int32_t> order;
+  order.reserve((size_t)B);
+  auto holds = [&](int32_t r) {
+    return row_class_of(rows[(size_t)r].flags, rows[(size_t)r].top_k) == CLS_HOLD;
+  };
+  for (int32_t r : sampled)
+    if (holds(r)) order.push_back(r);
+  for (int32_t r : sampled)
+    if (!holds(r)) order.push_back(r);
+  order.insert(order.end(), greedy_rows.begin(), greedy_rows.end());
+  std::memcpy(p + off_list, order.data(), sizeof(int32_t) * order.size());
   std::memcpy(p + off_pen, pen.data(), sizeof(PenEntry) * pen.size());
   std::memcpy(p + off_pen + sizeof(PenEntry) * pen.size(), bias.data(),
               sizeof(BiasEntry) * bias.size());
@@ -315,11 +329,9 @@ int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_
 
   unsigned char* ws = static_cast<unsigned char*>(workspace);
   SampleArgs a;
-  if (b->n_sampled < 0 || b->n_sampled > B || (b->n_sampled > 0 && !b->d_sampled))
-    return SAMPLER_EINVAL;
+  if (b->n_sampled < 0 || b->n_sampled > B || !b->d_sampled) return SAMPLER_EINVAL;
   a.rows = static_cast<const RowParams*>(b->d_rows);
-  a.sampled = static_cast<const int32_t*>(b->d_sampled);
-  a.n_sampled = b->n_sampled;
+  a.order = static_cast<const int32_t*>(b->d_sampled);
   a.logits = logits;
   a.ld = ld;
   a.B = B;
@@ -358,6 +370,7 @@ int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_
   uint32_t gen = g_gen.fetch_add(1u) + 1u;
   if (gen == 0u) gen = g_gen.fetch_add(1u) + 1u;
   a.gen = gen;
+  a.trace = reinterpret_cast<unsigned long long*>(g_trace.load());
 
   KernelEvents ev;
   ev.start = static_cast<hipEvent_t>(g_ev_start.exchange(nullptr));
@@ -372,6 +385,11 @@ int sampler_set_option(int option, int64_t value) {
   if (option == SAMPLER_OPT_ALGO) {
     if (value != 0 && value != 1) return SAMPLER_EINVAL;
     g_algo.store((int)value);
+    return SAMPLER_OK;
+  }
+  if (option == SAMPLER_OPT_TRACE) {
+    if (value < 0) return SAMPLER_EINVAL;
+    g_trace.store((unsigned long long)value);
     return SAMPLER_OK;
   }
   return SAMPLER_EINVAL;

@@ -140,8 +140,12 @@ typedef struct sampler_batch {
   size_t bytes;         /* bytes of d_buf in use                             */
   int32_t n_sampled;    /* rows that are not greedy                          */
   int32_t reserved;
-  const void *d_sampled; /* dev: int32 indices of those rows, ascending,
-                            inside d_buf                                     */
+  const void *d_sampled; /* dev: int32 row order [B] inside d_buf, the order
+                            in which sampler_sample dispatches the rows: the
+                            n_sampled rows that are not greedy (first those
+                            whose cut needs the whole row's histogram: top-p
+                            as the only cut, or top_k > 2048), then the
+                            greedy rows; ascending within each group       */
 } sampler_batch;
 
 /* Message for a SAMPLER_* return code (static storage). */
@@ -247,11 +251,22 @@ int sampler_sample(const sampler_batch *b, const void *logits, int dtype,
  * passes; used to test the fast path and the fallback it takes for rows whose
  * boundary sets do not fit on chip).  Process-wide; not for concurrent use.
  *
+ * sampler_set_option(SAMPLER_OPT_TRACE, ptr): diagnostic phase timestamps.
+ * ptr = 0 turns it off (default); otherwise ptr is the device address of a
+ * caller-owned uint64 buffer of 8 words per workgroup of the sampling kernel
+ * (B * P workgroups, P = slices per row, at most 64), which every later
+ * sampler_sample call overwrites: word 0 = row | slice << 20 | class << 28 |
+ * planner << 31, words 1..7 = the 100 MHz device wall clock at the start, after
+ * the slice maximum, after the summary pass, after the class work, after the
+ * arrival ticket, after the plan (or the wait for it), and at the end.
+ * Process-wide; not for concurrent use.
+ *
  * sampler_time_next(0, start, stop): on the next sampler_sample call, record
  * hipEvent_t `start` / `stop` (passed as void*) on the call's stream right
  * before and after its sampling kernel.  One-shot; used by the benchmark to
  * time the kernel.  Any other first argument -> EINVAL. */
 #define SAMPLER_OPT_ALGO 1
+#define SAMPLER_OPT_TRACE 2
 int sampler_set_option(int option, int64_t value);
 int sampler_time_next(int kernel, void *start_event, void *stop_event);
 

@@ -153,12 +153,14 @@ def test_workspace_size_closed_form(cds):
 
 
 def test_sampled_row_list(cds):
-    """The packed block lists the rows that are not greedy (T >= 1e-5 and
-    top_k != 1), ascending; greedy rows get no race work."""
-    T = np.array([0.0, 0.7, 1e-6, 1.0, 0.9], np.float32)
-    k = np.array([0, 0, 0, 1, 50], np.int32)
-    buf, b = cds.pack_host(5, 1000, T, top_k=k)
-    assert b.n_sampled == 2
-    assert np.frombuffer(buf[64 * 5:64 * 5 + 8].tobytes(), "<i4").tolist() == [1, 4]
+    """The packed block holds the dispatch order of the rows: the rows that are
+    not greedy (T >= 1e-5 and top_k != 1) -- those whose only cut is top-p
+    first -- then the greedy rows, ascending within each group."""
+    T = np.array([0.0, 0.7, 1e-6, 1.0, 0.9, 0.8], np.float32)
+    k = np.array([0, 0, 0, 1, 50, 0], np.int32)
+    p = np.array([1, 1, 1, 1, 1, 0.9], np.float32)
+    buf, b = cds.pack_host(6, 1000, T, top_k=k, top_p=p)
+    assert b.n_sampled == 3
+    assert np.frombuffer(buf[64 * 6:64 * 6 + 24].tobytes(), "<i4").tolist() == [5, 1, 4, 0, 2, 3]
     buf, b = cds.pack_host(2, 1000, np.zeros(2, np.float32))
     assert b.n_sampled == 0 and b.flags & cds.FLAG_ALL_GREEDY
