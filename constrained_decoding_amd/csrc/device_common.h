@@ -38,9 +38,11 @@ __device__ __forceinline__ uint4 philox4x32_10(uint4 c, uint32_t k0, uint32_t k1
       k0 += 0x9E3779B9u;
       k1 += 0xBB67AE85u;
     }
-    const uint32_t lo0 = 0xD2511F53u * c.x, hi0 = __umulhi(0xD2511F53u, c.x);
-    const uint32_t lo1 = 0xCD9E8D57u * c.z, hi1 = __umulhi(0xCD9E8D57u, c.z);
-    c = make_uint4(hi1 ^ c.y ^ k0, lo1, hi0 ^ c.w ^ k1, lo0);
+    // full 64-bit products: one v_mad_u64_u32 each instead of a lo / hi pair
+    const uint64_t p0 = (uint64_t)0xD2511F53u * c.x;
+    const uint64_t p1 = (uint64_t)0xCD9E8D57u * c.z;
+    c = make_uint4((uint32_t)(p1 >> 32) ^ c.y ^ k0, (uint32_t)p1, (uint32_t)(p0 >> 32) ^ c.w ^ k1,
+                   (uint32_t)p0);
   }
   return c;
 }
@@ -248,8 +250,8 @@ __device__ __forceinline__ uint32_t wave_first_true(uint32_t lo, uint32_t hi, Pr
     const bool ok = (lane == 63) || (probe > lo && pred(probe));
     const unsigned long long msk = __ballot(ok);
     const int first = __ffsll((long long)msk) - 1;
-    const uint32_t nhi = __shfl(probe, first, 64);
-    const uint32_t nlo = first > 0 ? __shfl(probe, first - 1, 64) : lo;
+    const uint32_t nhi = (uint32_t)__builtin_amdgcn_readlane((int)probe, first);
+    const uint32_t nlo = first > 0 ? (uint32_t)__builtin_amdgcn_readlane((int)probe, first - 1) : lo;
     hi = nhi;
     lo = (nlo < nhi) ? nlo : lo;
   }
@@ -315,7 +317,9 @@ __device__ __forceinline__ void load4(const RowView& rv, int64_t t0, int64_t hi,
 // hi is whole): every load -- logits, then mask words -- is issued before any
 // value is used, with no branch between them; chunks at or beyond hi load
 // chunk `lo` (in bounds) and are discarded.  Otherwise guarded scalar loads.
-template <int NT, int N, bool BF16, bool VEC, bool STREAM = false>
+// CHECK_NF = false (vector path only): no per-token non-finite test; the
+// caller detects NaN / +inf from its own reductions instead.
+template <int NT, int N, bool BF16, bool VEC, bool STREAM = false, bool CHECK_NF = true>
 __device__ __forceinline__ void load_chunks(const RowView& rv, int64_t lo, int64_t hi, int first,
                                             float x[N][4], uint32_t& nonfin) {
   if (!VEC) {
@@ -393,8 +397,10 @@ __device__ __forceinline__ void load_chunks(const RowView& rv, int64_t lo, int64
       for (int q = 0; q < 4; ++q)
         if (!((bits >> q) & 1u)) x[i][q] = CDS_NEG_INF;
     }
+    if (CHECK_NF) {
 #pragma unroll
-    for (int q = 0; q < 4; ++q) nf |= __builtin_amdgcn_class(x[i][q], 0x203) ? 1u : 0u;
+      for (int q = 0; q < 4; ++q) nf |= __builtin_amdgcn_class(x[i][q], 0x203) ? 1u : 0u;
+    }
   }
   nonfin |= nf;
 }
@@ -520,6 +526,113 @@ __device__ __forceinline__ int wave0_first_ge(const T* v, int n, T x) {
   return i;
 }
 
+// ---- wave all-reduce by DPP row rotations ----------------------------------------
+// Each 16-lane row is reduced by rotations (row_ror 8, 4, 2, 1), then the four
+// row results are read from lanes 0, 16, 32, 48 into scalar registers and
+// combined.  No lane-address registers, no LDS; a fixed combination order, so
+// the result is deterministic, and it is the same (uniform) value in every
+// lane.  All 64 lanes must be active; op must be commutative and associative
+// up to rounding.
+template <int CTRL, typename T>
+__device__ __forceinline__ T dpp_obj(const T& v) {
+  static_assert(sizeof(T) % 4 == 0, "32-bit words");
+  uint32_t w[sizeof(T) / 4];
+  __builtin_memcpy(w, &v, sizeof(T));
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(T) / 4); ++k)
+    w[k] = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)w[k], CTRL, 0xf, 0xf, false);
+  T r;
+  __builtin_memcpy(&r, w, sizeof(T));
+  return r;
+}
+template <typename T>
+__device__ __forceinline__ T readlane_obj(const T& v, int lane) {
+  uint32_t w[sizeof(T) / 4];
+  __builtin_memcpy(w, &v, sizeof(T));
+#pragma unroll
+  for (int k = 0; k < (int)(sizeof(T) / 4); ++k)
+    w[k] = (uint32_t)__builtin_amdgcn_readlane((int)w[k], lane);
+  T r;
+  __builtin_memcpy(&r, w, sizeof(T));
+  return r;
+}
+template <typename T, typename Op>
+__device__ __forceinline__ T wave_allreduce(T v, Op op) {
+  v = op(v, dpp_obj<0x128>(v));  // row_ror:8
+  v = op(v, dpp_obj<0x124>(v));  // row_ror:4
+  v = op(v, dpp_obj<0x122>(v));  // row_ror:2
+  v = op(v, dpp_obj<0x121>(v));  // row_ror:1
+  const T r0 = readlane_obj(v, 0), r1 = readlane_obj(v, 16);
+  const T r2 = readlane_obj(v, 32), r3 = readlane_obj(v, 48);
+  return op(op(r0, r1), op(r2, r3));
+}
+
+// ---- one-pass slice summary ----------------------------------------------------
+// The per-thread summary of a thread's values, and its merge: max, the lowest
+// index holding it, sum exp2((x - max) * c) relative to that max, the
+// non-finite flag, and the minimum of a per-thread lower bound (top-k filter).
+struct SliceStat {
+  float m;      // max (-inf if none)
+  int32_t a;    // lowest index holding it (INT_MAX if none)
+  double s;     // sum exp2((x - m) * c)
+  uint32_t nf;  // a non-finite value seen
+  float lb;     // min of the per-thread bounds
+};
+
+__device__ __forceinline__ SliceStat stat_merge(const SliceStat& x, const SliceStat& y, float c) {
+  SliceStat r;
+  r.m = fmaxf(x.m, y.m);
+  r.a = x.m > y.m ? x.a : (y.m > x.m ? y.a : min(x.a, y.a));
+  const double sx = x.m == CDS_NEG_INF ? 0.0 : x.s * (double)__builtin_amdgcn_exp2f((x.m - r.m) * c);
+  const double sy = y.m == CDS_NEG_INF ? 0.0 : y.s * (double)__builtin_amdgcn_exp2f((y.m - r.m) * c);
+  r.s = sx + sy;
+  r.nf = x.nf | y.nf;
+  r.lb = fminf(x.lb, y.lb);
+  return r;
+}
+
+template <int NT>
+struct StatScratch {
+  float m[NT / 64];
+  int32_t a[NT / 64];
+  double s[NT / 64];
+  uint32_t nf[NT / 64];
+  float lb[NT / 64];
+};
+
+// Workgroup merge of the threads' summaries (a fixed tree: deterministic);
+// every thread gets the result.  One barrier.
+template <int NT>
+__device__ __forceinline__ SliceStat block_stat(SliceStat v, float c, StatScratch<NT>& sc) {
+  v = wave_allreduce(v, [c](const SliceStat& x, const SliceStat& y) { return stat_merge(x, y, c); });
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sc.m[w] = v.m;
+    sc.a[w] = v.a;
+    sc.s[w] = v.s;
+    sc.nf[w] = v.nf;
+    sc.lb[w] = v.lb;
+  }
+  __syncthreads();
+  SliceStat r;
+  r.m = sc.m[0];
+  r.a = sc.a[0];
+  r.s = sc.s[0];
+  r.nf = sc.nf[0];
+  r.lb = sc.lb[0];
+#pragma unroll
+  for (int k = 1; k < NT / 64; ++k) {
+    SliceStat y;
+    y.m = sc.m[k];
+    y.a = sc.a[k];
+    y.s = sc.s[k];
+    y.nf = sc.nf[k];
+    y.lb = sc.lb[k];
+    r = stat_merge(r, y, c);
+  }
+  return r;
+}
+
 // ---- workgroup reductions (fixed trees: deterministic) -------------------------
 template <int NT>
 struct RedScratch {
@@ -531,8 +644,7 @@ struct RedScratch {
 
 template <int NT>
 __device__ __forceinline__ double block_sum_f64(double v, RedScratch<NT>& s) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = wave_allreduce(v, [](double x, double y) { return x + y; });
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) s.d[w] = v;
@@ -545,8 +657,7 @@ __device__ __forceinline__ double block_sum_f64(double v, RedScratch<NT>& s) {
 
 template <int NT>
 __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, RedScratch<NT>& s) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = wave_allreduce(v, [](uint64_t x, uint64_t y) { return x + y; });
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) s.u[w] = v;
@@ -559,8 +670,7 @@ __device__ __forceinline__ uint64_t block_sum_u64(uint64_t v, RedScratch<NT>& s)
 
 template <int NT>
 __device__ __forceinline__ int32_t block_sum_i32(int32_t v, RedScratch<NT>& s) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  v = wave_allreduce(v, [](int32_t x, int32_t y) { return x + y; });
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) s.i[w] = v;
@@ -573,8 +683,7 @@ __device__ __forceinline__ int32_t block_sum_i32(int32_t v, RedScratch<NT>& s) {
 
 template <int NT>
 __device__ __forceinline__ uint32_t block_or_u32(uint32_t v, RedScratch<NT>& s) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, 64);
+  v = wave_allreduce(v, [](uint32_t x, uint32_t y) { return x | y; });
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) s.i[w] = (int32_t)v;
@@ -587,8 +696,7 @@ __device__ __forceinline__ uint32_t block_or_u32(uint32_t v, RedScratch<NT>& s) 
 
 template <int NT>
 __device__ __forceinline__ float block_max_f32(float v, RedScratch<NT>& s) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  v = wave_allreduce(v, [](float x, float y) { return fmaxf(x, y); });
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) s.f[w] = v;
@@ -601,8 +709,7 @@ __device__ __forceinline__ float block_max_f32(float v, RedScratch<NT>& s) {
 
 template <int NT>
 __device__ __forceinline__ int32_t block_min_i32(int32_t v, RedScratch<NT>& s) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, 64));
+  v = wave_allreduce(v, [](int32_t x, int32_t y) { return min(x, y); });
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) s.i[w] = v;
@@ -615,15 +722,10 @@ __device__ __forceinline__ int32_t block_min_i32(int32_t v, RedScratch<NT>& s) {
 
 template <int NT>
 __device__ __forceinline__ void block_top2(Top2& b, RedScratch<NT>& s) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    Top2 p;
-    p.k1 = __shfl_xor(b.k1, o, 64);
-    p.t1 = __shfl_xor(b.t1, o, 64);
-    p.z1 = __shfl_xor(b.z1, o, 64);
-    p.k2 = __shfl_xor(b.k2, o, 64);
-    top2_merge(b, p);
-  }
+  b = wave_allreduce(b, [](Top2 x, const Top2& y) {
+    top2_merge(x, y);
+    return x;
+  });
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) {
@@ -649,15 +751,15 @@ __device__ __forceinline__ void block_top2(Top2& b, RedScratch<NT>& s) {
 // max value, lowest index among equal maxima
 template <int NT>
 __device__ __forceinline__ void block_argmax(float& z, int32_t& t, RedScratch<NT>& s) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float z2 = __shfl_xor(z, o, 64);
-    const int32_t t2 = __shfl_xor(t, o, 64);
-    if (z2 > z || (z2 == z && t2 < t)) {
-      z = z2;
-      t = t2;
-    }
-  }
+  struct ZT {
+    float z;
+    int32_t t;
+  };
+  const ZT zt = wave_allreduce(ZT{z, t}, [](const ZT& p, const ZT& q) {
+    return (q.z > p.z || (q.z == p.z && q.t < p.t)) ? q : p;
+  });
+  z = zt.z;
+  t = zt.t;
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) {
@@ -677,17 +779,7 @@ __device__ __forceinline__ void block_argmax(float& z, int32_t& t, RedScratch<NT
 
 template <int NT>
 __device__ __forceinline__ void block_best(Best& b, RedScratch<NT>& s) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const double k2 = __shfl_xor(b.key, o, 64);
-    const int32_t t2 = __shfl_xor(b.t, o, 64);
-    const float z2 = __shfl_xor(b.z, o, 64);
-    if (better(k2, t2, b.key, b.t)) {
-      b.key = k2;
-      b.t = t2;
-      b.z = z2;
-    }
-  }
+  b = wave_allreduce(b, [](const Best& p, const Best& q) { return better(q.key, q.t, p.key, p.t) ? q : p; });
   const int w = threadIdx.x >> 6;
   __syncthreads();
   if ((threadIdx.x & 63) == 0) {
@@ -707,39 +799,6 @@ __device__ __forceinline__ void block_best(Best& b, RedScratch<NT>& s) {
       b.z = s.f[k];
     }
   b.key32 = (float)b.key;
-}
-
-// Inclusive scan over n values held in LDS array `v` (in place): serial
-// within contiguous per-thread chunks, then wave shuffles and per-wave totals
-// -- a fixed combination order, so results are bit-reproducible.
-// `wtot` is LDS scratch of NT/64 elements.  All NT threads must call it.
-template <int NT, typename T, typename Op>
-__device__ __forceinline__ void block_scan_inplace(T* v, int n, T ident, Op op, T* wtot) {
-  const int chunk = (n + NT - 1) / NT;
-  const int lo = min((int)threadIdx.x * chunk, n);
-  const int hi = min(lo + chunk, n);
-  T acc = ident;
-  for (int i = lo; i < hi; ++i) acc = op(acc, v[i]);
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  T s = acc;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const T y = __shfl_up(s, o, 64);
-    if (lane >= o) s = op(y, s);
-  }
-  T ex = __shfl_up(s, 1, 64);
-  if (lane == 0) ex = ident;
-  __syncthreads();
-  if (lane == 63) wtot[w] = s;
-  __syncthreads();
-  T run = ident;
-  for (int k = 0; k < w; ++k) run = op(run, wtot[k]);
-  run = op(run, ex);
-  for (int i = lo; i < hi; ++i) {
-    run = op(run, v[i]);
-    v[i] = run;
-  }
-  __syncthreads();
 }
 
 }  // namespace cds

@@ -438,23 +438,11 @@ __device__ __forceinline__ void vm_drain() {
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
 }
 
-// Add `n` to the generation-tagged counter *w (high half: generation, low
-// half: count; another generation's count reads as zero); returns the count
-// before the addition.
-__device__ __forceinline__ uint32_t gen_add(unsigned long long* w, uint32_t gen, uint32_t n) {
-  unsigned long long old = ld_u64(w);
-  while (true) {
-    const uint32_t cnt = (uint32_t)(old >> 32) == gen ? (uint32_t)old : 0u;
-    const unsigned long long nw = ((unsigned long long)gen << 32) | (unsigned long long)(cnt + n);
-    if (__hip_atomic_compare_exchange_weak(w, &old, nw, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                           __HIP_MEMORY_SCOPE_AGENT))
-      return cnt;
-  }
-}
-
-__device__ __forceinline__ uint32_t gen_count(const unsigned long long* w, uint32_t gen) {
-  const unsigned long long v = ld_u64(w);
-  return (uint32_t)(v >> 32) == gen ? (uint32_t)v : 0u;
+// Row ticket: every slice of the row adds 1 once per call and gets the count
+// before its addition; the slice that gets P-1 is the last and resets the
+// counter to zero for the next call (no slice of this call touches it again).
+__device__ __forceinline__ uint32_t take_ticket(unsigned long long* w) {
+  return (uint32_t)__hip_atomic_fetch_add(w, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // Spin until *p == gen, at most `limit` ticks of the constant-rate wall
@@ -479,8 +467,6 @@ struct PlanShared {
   SliceHead head[kMaxSlices];
   double md[NBINS];                 // per-bin mass relative to exp(m), then scanned
   uint32_t cumc[NBINS];             // per-bin count, then scanned
-  unsigned long long accm[NBINS];   // merge accumulators
-  uint32_t accc[NBINS];
   double wtot_d[NT / 64];
   uint32_t wtot_u[NT / 64];
   int mode, inK, k_rank, rb12;
@@ -515,20 +501,22 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
       hs = h.sumexp;
     }
     const float hz = zm;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float z2 = __shfl_xor(zm, o, 64);
-      const int32_t a2 = __shfl_xor(am, o, 64);
-      if (z2 > zm || (z2 == zm && a2 < am)) {
-        zm = z2;
-        am = a2;
-      }
-      fl |= __shfl_xor(fl, o, 64);
-    }
+    struct ZAF {
+      float z;
+      int32_t a;
+      uint32_t f;
+    };
+    const ZAF hm = wave_allreduce(ZAF{zm, am, fl}, [](const ZAF& p, const ZAF& q) {
+      ZAF o = (q.z > p.z || (q.z == p.z && q.a < p.a)) ? q : p;
+      o.f = p.f | q.f;
+      return o;
+    });
+    zm = hm.z;
+    am = hm.a;
+    fl = hm.f;
     const double invTe = greedy ? 1.0 : 1.0 / Td;
     double Z = (!hist && hz != CDS_NEG_INF) ? hs * exp(((double)hz - (double)zm) * invTe) : 0.0;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) Z += __shfl_xor(Z, o, 64);
+    Z = wave_allreduce(Z, [](double x, double y) { return x + y; });
     if (tid == 0) {
       int mode = PLAN_FAST;
       if (zm == CDS_NEG_INF) {
@@ -588,43 +576,51 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
   // merge the slices' histograms: row bin = slice bin + (row kmax - slice kmax)
   const BinGeom g = bin_geom(rp.temperature);
   const float kmax = floorf(ps.zmax * g.inv_delta);
-  for (int b = tid; b < NBINS; b += NT) {
-    ps.accm[b] = 0ull;
-    ps.accc[b] = 0u;
-  }
-  __syncthreads();
+  // thread tid owns row bins tid, tid + NT, ...; slice j's bin sb lands in row
+  // bin sb + (kmax - kmax_j).  Every load is issued before any is used.
   {
-    // up to 18 loads in flight per thread (all of them for P <= 8)
-    constexpr int U = 18;
-    const int total = P * NBINS;
+    constexpr int BPT = (NBINS + NT - 1) / NT;  // row bins per thread
     const unsigned long long* gh = a.hist + (int64_t)r * P * NBINS;
-    for (int e0 = tid; e0 < total; e0 += U * NT) {
-      unsigned long long v[U];
+    uint32_t cnt[BPT];
+    unsigned long long mas[BPT];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int e = e0 + u * NT;
-        v[u] = e < total ? ld_u64(gh + e) : 0ull;
+    for (int k = 0; k < BPT; ++k) {
+      cnt[k] = 0u;
+      mas[k] = 0ull;
+    }
+#pragma unroll 1
+    for (int j0 = 0; j0 < P; j0 += 8) {
+      unsigned long long v[8][BPT];
+#pragma unroll
+      for (int jj = 0; jj < 8; ++jj) {
+        const int j = j0 + jj;
+        const bool live = j < P && ps.head[j < P ? j : 0].zmax != CDS_NEG_INF;
+        const int shift = live ? (int)(kmax - ps.head[j].kmax) : NBINS;
+#pragma unroll
+        for (int k = 0; k < BPT; ++k) {
+          const int sb = tid + k * NT - shift;
+          v[jj][k] = (live && sb >= 0 && sb < NBINS) ? ld_u64(gh + (int64_t)j * NBINS + sb) : 0ull;
+        }
       }
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int e = e0 + u * NT;
-        if (e >= total || v[u] == 0ull) continue;
-        const int j = e / NBINS, sb = e - j * NBINS;
-        if (ps.head[j].zmax == CDS_NEG_INF) continue;
-        const float rowbin = (kmax - ps.head[j].kmax) + (float)sb;
-        if (!(rowbin >= 0.0f && rowbin < (float)NBINS)) continue;
-        atomicAdd(&ps.accc[(int)rowbin], (uint32_t)(v[u] >> kCountShift));
-        atomicAdd(&ps.accm[(int)rowbin], v[u] & ((1ull << kCountShift) - 1ull));
+      for (int jj = 0; jj < 8; ++jj)
+#pragma unroll
+        for (int k = 0; k < BPT; ++k) {
+          cnt[k] += (uint32_t)(v[jj][k] >> kCountShift);
+          mas[k] += v[jj][k] & ((1ull << kCountShift) - 1ull);
+        }
+    }
+    const double m = ps.m;
+#pragma unroll
+    for (int k = 0; k < BPT; ++k) {
+      const int b = tid + k * NT;
+      if (b < NBINS) {
+        ps.cumc[b] = cnt[k];
+        // bin b spans [(kmax-b)*delta, (kmax-b+1)*delta); masses are relative to its top
+        const double top = ((double)kmax + 1.0 - (double)b) * (double)g.delta;
+        ps.md[b] = (double)mas[k] * 0x1p-31 * exp(top / Td - m);
       }
     }
-  }
-  __syncthreads();
-  const double m = ps.m;
-  for (int b = tid; b < NBINS; b += NT) {
-    ps.cumc[b] = ps.accc[b];
-    // bin b spans [(kmax-b)*delta, (kmax-b+1)*delta); masses are relative to its top
-    const double top = ((double)kmax + 1.0 - (double)b) * (double)g.delta;
-    ps.md[b] = (double)ps.accm[b] * 0x1p-31 * exp(top / Td - m);
   }
   __syncthreads();
   // cumulative counts and masses from the top, both by wave 0
@@ -695,6 +691,19 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
     st_obj(&a.plans[r], pl);
     *out = pl;
   }
+}
+
+// Radix selects over order keys of values in [lo, hi] start below the leading
+// bytes those keys all share: returns the first digit shift (24, 16, 8, 0, or
+// -8 when all four bytes are shared) and sets prefix / pmask to the shared bytes.
+__device__ __forceinline__ int radix_start(float lo, float hi, uint32_t& prefix, uint32_t& pmask) {
+  const uint32_t kl = okey(lo + 0.0f), kh = okey(hi + 0.0f);
+  const uint32_t diff = kl ^ kh;
+  const int nb = diff ? (int)(__clz(diff) >> 3) : 4;  // shared leading bytes
+  pmask = nb ? (0xFFFFFFFFu << (32 - 8 * nb)) : 0u;
+  if (nb == 4) pmask = 0xFFFFFFFFu;
+  prefix = kl & pmask;
+  return 24 - 8 * nb;
 }
 
 // ---- phase 4: the boundary list --------------------------------------------------
@@ -768,12 +777,7 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Pla
       }
       cnt = sb.ucnt > (uint32_t)SCAP ? (uint32_t)UCAP + 1u : sb.ucnt;
     }
-    uint32_t incl = cnt;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      const uint32_t y = __shfl_up(incl, o, 64);
-      if (tid >= o) incl += y;
-    }
+    const uint32_t incl = wave_incl_sum(cnt);
     off[tid + 1] = (int32_t)min(incl, (uint32_t)UCAP + 1u);
     if (tid == 0) off[0] = 0;
   }
@@ -812,10 +816,11 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Pla
     // k tokens; top-k then cuts nothing.
     if (cnt < pl.k_rank && !pl.list_mode) return false;
     if (cnt >= pl.k_rank) {
-      uint32_t prefix = 0, pmask = 0;
+      uint32_t prefix, pmask;
+      const int shift0 = radix_start(k_lo, k_hi, prefix, pmask);
       unsigned long long krem = (unsigned long long)pl.k_rank;
 #pragma unroll 1
-      for (int shift = 24; shift >= 0; shift -= 8) {
+      for (int shift = shift0; shift >= 0; shift -= 8) {
         if (tid < 256) sh.hist[tid] = 0ull;
         __syncthreads();
 #pragma unroll 1
@@ -864,10 +869,11 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Pla
     const double need = (pl.p * M2 - pl.m_sure) / F * kFix;
     if (!(need > 0.0)) return false;         // the cut lies above the range
     if ((double)m_in < need) return false;   // ... or below it
-    uint32_t prefix = 0, pmask = 0;
+    uint32_t prefix, pmask;
+    const int shift0 = radix_start(a_lo, zref, prefix, pmask);
     unsigned long long base = 0;
 #pragma unroll 1
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int shift = shift0; shift >= 0; shift -= 8) {
       if (tid < 256) sh.hist[tid] = 0ull;
       __syncthreads();
 #pragma unroll 1
@@ -941,15 +947,15 @@ union FusedLds {
     int32_t off[kMaxSlices + 1];
   } fin;
   struct {
-    ExactShared<NT> ex;
-    uint32_t gm[kMaxChunks * NT];  // group maxima (order keys)
+    uint32_t cnt[256];  // top-k filter histogram
+    uint32_t bstar;     // its cut bin
   } sel;
   uint64_t stage[SCAP];
 };
 
 
-__device__ __forceinline__ int row_class(const RowParams& rp) {
-  return (int)row_class_of(rp.flags, rp.top_k);
+__device__ __forceinline__ int row_class(const RowParams& rp, int P) {
+  return (int)row_class_of(rp.flags, rp.top_k, P);
 }
 
 // Appends the slice's tokens whose value passes keep() to the LDS stage as
@@ -1027,10 +1033,11 @@ __device__ __forceinline__ float minp_cut_wave(float zmax, double Td, float min_
 
 template <int NT, int E4, bool BF16, bool VEC, bool STREAM>
 __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, FusedLds<NT>& sh,
-                                           RedScratch<NT>& red, Plan* s_plan, uint32_t* s_word) {
+                                           RedScratch<NT>& red, StatScratch<NT>& sst,
+                                           Plan* s_plan, uint32_t* s_word) {
   const int tid = threadIdx.x, P = a.P;
   const RowParams rp = a.rows[r];
-  const int cls = row_class(rp);
+  const int cls = row_class(rp, a.P);
   const bool greedy = cls == CLS_GREEDY;
   const int64_t lo = (int64_t)sl * a.S;
   const int64_t hi = min(lo + a.S, (int64_t)a.V);
@@ -1041,44 +1048,73 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
 
   float x[E4][4];
   uint32_t nonfin = 0;
-  load_chunks<NT, E4, BF16, VEC, STREAM>(rv, lo, hi, 0, x, nonfin);
+  load_chunks<NT, E4, BF16, VEC, STREAM, false>(rv, lo, hi, 0, x, nonfin);
 
-  // max, then the lowest index holding it (searched only by threads that hold it)
-  float lm = CDS_NEG_INF;
+  // ---- the slice summary: one pass over the registers, one merge ----
+  // max, non-finite flag, sum exp((z - max)/T_eff) (rows that are not HOLD),
+  // and for top-k rows the minimum of the thread maxima; then the lowest index
+  // holding the max
+  const bool topk_list = cls == CLS_LIST && (rp.flags & ROW_TOPK);
+  const int kq = topk_list ? rp.top_k : 0;  // <= NT for LIST rows
+  const float cexp =
+      cls == CLS_HOLD ? 0.0f : (greedy ? 1.0f : (float)(1.0 / (double)rp.temperature)) * kLog2e;
+  SliceStat st;
+  st.m = CDS_NEG_INF;
+  st.a = INT_MAX;
+  st.s = 0.0;
+  st.nf = nonfin;
+  st.lb = CDS_POS_INF;
+  {
 #pragma unroll
-  for (int i = 0; i < E4; ++i)
+    for (int i = 0; i < E4; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) lm = fmaxf(lm, x[i][q]);
-  const float zm = block_max_f32<NT>(lm, red);
+      for (int q = 0; q < 4; ++q) st.m = fmaxf(st.m, x[i][q]);
+    // top-k rows (k <= NT): the thread maximum; the minimum over threads has
+    // at least NT >= k tokens at or above it
+    if (topk_list) st.lb = st.m;
+    if (cexp != 0.0f && st.m != CDS_NEG_INF) {
+      // exp2(x*c - max*c): one FMA per token; a NaN or +inf token makes the
+      // sum NaN (or the max +inf), which flags the slice
+      const float mc = st.m * cexp;
+#pragma unroll
+      for (int i = 0; i < E4; ++i) {
+        float part = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) part += __builtin_amdgcn_exp2f(fmaf(x[i][q], cexp, -mc));
+        st.s += (double)part;
+      }
+    }
+    if (cls == CLS_HOLD) {
+      // NaN / +inf check for rows without the sum: a plain sum propagates them
+      float sx = 0.0f;
+#pragma unroll
+      for (int i = 0; i < E4; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sx += x[i][q];
+      if (sx != sx || sx == CDS_POS_INF) st.nf = 1u;
+    }
+  }
+  const float lmax = st.m;
+  st = block_stat<NT>(st, cexp, sst);
+  const float zm = st.m == CDS_POS_INF ? CDS_NEG_INF : st.m;
+  if (st.m == CDS_POS_INF || st.s != st.s) st.nf = 1u;
+  // the lowest index holding the maximum (searched only by threads holding it)
   int32_t am = INT_MAX;
-  if (zm != CDS_NEG_INF && lm == zm) {
+  if (zm != CDS_NEG_INF && lmax == zm) {
 #pragma unroll
     for (int i = E4 - 1; i >= 0; --i)
 #pragma unroll
       for (int q = 3; q >= 0; --q)
         if (x[i][q] == zm) am = tbase + 4 * NT * i + q;
   }
+  if (zm != CDS_NEG_INF) am = block_min_i32<NT>(am, red);
+  nonfin = st.nf;
   CDS_TRACE(2);
-  am = block_min_i32<NT>(am, red);
-  nonfin = block_or_u32<NT>(nonfin, red);
 
   uint32_t flags = nonfin ? SLICE_NONFINITE : 0u;
-  double se = 0.0;
+  const double se = st.s;
   float kmax = 0.0f;
-  if (cls != CLS_HOLD) {
-    // sum exp((z - zmax) / T_eff): the row's log-partition for the logprob
-    const float cexp = (greedy ? 1.0f : (float)(1.0 / (double)rp.temperature)) * kLog2e;
-    if (zm != CDS_NEG_INF) {
-#pragma unroll
-      for (int i = 0; i < E4; ++i) {
-        float part = 0.0f;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) part += __builtin_amdgcn_exp2f((x[i][q] - zm) * cexp);
-        se += (double)part;
-      }
-    }
-    se = block_sum_f64<NT>(se, red);
-  } else if (zm != CDS_NEG_INF) {
+  if (cls == CLS_HOLD && zm != CDS_NEG_INF) {
     // histogram of the values below the slice maximum, bins aligned to delta
     const BinGeom g = bin_geom(rp.temperature);
     kmax = floorf(zm * g.inv_delta);
@@ -1115,8 +1151,9 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
       }
     }
   }
-
+#ifndef CDS_TRACE_DETAIL
   CDS_TRACE(3);
+#endif
   if (cls == CLS_RACE && zm != CDS_NEG_INF && !nonfin) {
     // the race over every allowed token, keys relative to the slice maximum
     const float invT32 = sgpr_f((float)(1.0 / (double)rp.temperature));
@@ -1154,88 +1191,61 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
       st_obj(&a.bests[slot], sb);
     }
   } else if (cls == CLS_LIST && zm != CDS_NEG_INF && !nonfin) {
-    // a superset of the slice's candidates, listed
+    // a superset of the slice's candidates, listed: every token at or above a
+    // cut that is at most the slice's top_k-th largest value (top-k rows) and
+    // at most the min-p bound relative to the slice maximum (min-p rows; the
+    // row's bound, relative to the row maximum, is at least as high)
     float cut = CDS_NEG_INF;
-    if (rp.flags & ROW_TOPK) {
-      // L = the q-th largest of NT*h group maxima (group g of thread tid =
-      // chunks [g*E4/h, (g+1)*E4/h)): at least q tokens lie at or above it, so
-      // it is at most the slice's own q-th largest value.  With about 4q
-      // groups few tokens beyond the q largest pass it.
-      const int q = min(rp.top_k, SCAP);
-      const int h = min(E4, (4 * q + NT - 1) / NT);
-      const int n = h * NT;
-#pragma unroll
-      for (int g = 0; g < E4; ++g) {
-        if (g < h) {
-          float gmx = CDS_NEG_INF;
-#pragma unroll
-          for (int i = 0; i < E4; ++i)
-            if ((i * h) / E4 == g)
-              gmx = fmaxf(gmx, fmaxf(fmaxf(x[i][0], x[i][1]), fmaxf(x[i][2], x[i][3])));
-          sh.sel.gm[g * NT + tid] = okey(gmx + 0.0f);
-        }
-      }
+    uint32_t bstar = 0u;
+    float inv_w = 0.0f;
+    const float L0 = st.lb;
+    if (topk_list && L0 != CDS_NEG_INF) {
+      // 256 bins over [L0, zm]; the cut bin holds the kq-th largest token
+      // (bins are monotone in the value: every token above a listed one is
+      // listed too)
+      inv_w = zm > L0 ? 255.0f / (zm - L0) : 0.0f;
+      uint32_t* cnt = sh.sel.cnt;
+      if (tid < 256) cnt[tid] = 0u;
       __syncthreads();
-      uint32_t prefix = 0, pmask = 0;
-      unsigned long long krem = (unsigned long long)q;
-#pragma unroll 1
-      for (int shift = 24; shift >= 0; shift -= 8) {
-        if (tid < 256) sh.sel.ex.hist[tid] = 0ull;
-        __syncthreads();
-        for (int i = tid; i < n; i += NT) {
-          const uint32_t u = sh.sel.gm[i];
-          if ((u & pmask) == prefix) atomicAdd(&sh.sel.ex.hist[(u >> shift) & 255u], 1ull);
-        }
-        __syncthreads();
-        unsigned long long above;
-        const int d = pick_digit<NT>(sh.sel.ex, (double)krem, 0ull, &above);
-        krem -= above;
-        prefix |= (uint32_t)d << shift;
-        pmask |= 255u << shift;
-      }
-      cut = from_okey(prefix);
-      // more than SCAP tokens at or above L: cut at the exact q-th largest
-      // value instead (a radix select over the tokens >= L, in registers)
-      const float lcut = sgpr_f(cut);
-      int c = 0;
 #pragma unroll
       for (int i = 0; i < E4; ++i)
 #pragma unroll
-        for (int qq = 0; qq < 4; ++qq) c += (x[i][qq] >= lcut && x[i][qq] != CDS_NEG_INF) ? 1 : 0;
-      c = block_sum_i32<NT>(c, red);
-      if (c > SCAP) {
-        uint32_t pfx = 0, pm = 0;
-        unsigned long long kr = (unsigned long long)q;
-#pragma unroll 1
-        for (int shift = 24; shift >= 0; shift -= 8) {
-          if (tid < 256) sh.sel.ex.hist[tid] = 0ull;
-          __syncthreads();
-#pragma unroll
-          for (int i = 0; i < E4; ++i)
-#pragma unroll
-            for (int qq = 0; qq < 4; ++qq) {
-              const float v = x[i][qq];
-              const uint32_t u = okey(v + 0.0f);
-              if (v >= lcut && v != CDS_NEG_INF && (u & pm) == pfx)
-                atomicAdd(&sh.sel.ex.hist[(u >> shift) & 255u], 1ull);
-            }
-          __syncthreads();
-          unsigned long long above;
-          const int d = pick_digit<NT>(sh.sel.ex, (double)kr, 0ull, &above);
-          kr -= above;
-          pfx |= (uint32_t)d << shift;
-          pm |= 255u << shift;
+        for (int q = 0; q < 4; ++q) {
+          const float v = x[i][q];
+          if (v >= L0) atomicAdd(&cnt[min(255, (int)((v - L0) * inv_w))], 1u);
         }
-        cut = from_okey(pfx);
-      }
-    }
-    if (rp.flags & ROW_MINP) {
+      __syncthreads();
       if (tid < 64) {
-        const float c = minp_cut_wave(zm, (double)rp.temperature, rp.min_p);
-        if (tid == 0) sh.sel.ex.fshare = c;
+        // lane l owns bins 255-4l .. 252-4l (descending values)
+        const int l = tid;
+        const uint32_t c1 = cnt[255 - 4 * l], c2 = c1 + cnt[254 - 4 * l];
+        const uint32_t c3 = c2 + cnt[253 - 4 * l], c4 = c3 + cnt[252 - 4 * l];
+        const uint32_t incl = wave_incl_sum(c4);
+        const uint32_t ex = incl - c4;
+        const unsigned long long hit = __ballot(incl >= (uint32_t)kq);
+        const int first = hit ? __ffsll((long long)hit) - 1 : 63;
+        if (l == first) {
+          int j;
+          if (!hit || ex + c1 >= (uint32_t)kq) j = 0;
+          else if (ex + c2 >= (uint32_t)kq) j = 1;
+          else if (ex + c3 >= (uint32_t)kq) j = 2;
+          else j = 3;
+          sh.sel.bstar = hit ? (uint32_t)(255 - 4 * l - j) : 0u;
+        }
       }
       __syncthreads();
-      cut = fmaxf(cut, sh.sel.ex.fshare);
+      bstar = sh.sel.bstar;
+      // every token with bin >= bstar is >= L0 + bstar / inv_w up to rounding;
+      // half a bin lower keeps a superset with one compare per token
+      cut = (bstar == 0u || inv_w == 0.0f) ? L0 : fmaxf(L0, L0 + ((float)bstar - 0.5f) / inv_w);
+#ifdef CDS_TRACE_DETAIL
+      CDS_TRACE(3);
+#endif
+    }
+    if (rp.flags & ROW_MINP) {
+      const double b = (double)zm + (double)rp.temperature * log((double)rp.min_p);
+      const float bm = (float)(b - 1e-5 * (1.0 + fabs(b) + fabs((double)zm)));
+      cut = fmaxf(cut, bm);
     }
     if (tid == 0) s_word[1] = 0u;
     __syncthreads();
@@ -1284,7 +1294,11 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
   vm_drain();
   __syncthreads();
   RowSync* sy = &a.sync[r];
-  if (tid == 0) s_word[0] = gen_add(&sy->arrive, a.gen, 1u);
+  if (tid == 0) {
+    const uint32_t t = take_ticket(&sy->arrive);
+    if (t == (uint32_t)(P - 1)) st_u64(&sy->arrive, 0ull);
+    s_word[0] = t;
+  }
   __syncthreads();
   const bool planner = s_word[0] == (uint32_t)(P - 1);
   if (a.trace && tid == 0)
@@ -1411,7 +1425,11 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
   // the last slice of the row to finish its race resolves the row
   vm_drain();
   __syncthreads();
-  if (tid == 0) s_word[0] = gen_add(&sy->done, a.gen, 1u);
+  if (tid == 0) {
+    const uint32_t t = take_ticket(&sy->done);
+    if (t == (uint32_t)(P - 1)) st_u64(&sy->done, 0ull);
+    s_word[0] = t;
+  }
   __syncthreads();
   if (s_word[0] != (uint32_t)(P - 1)) {
     CDS_TRACE(7);
@@ -1432,13 +1450,14 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
 }
 
 #ifndef CDS_WAVES_PER_EU
-#define CDS_WAVES_PER_EU 4
+#define CDS_WAVES_PER_EU 3
 #endif
 // CDS_WAVES_PER_EU waves per SIMD (the slice takes 4*E4 vector registers).
 template <int NT, int E4, bool BF16, bool VEC>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CDS_WAVES_PER_EU))) void sample_kernel(
     const SampleArgs a) {
   __shared__ RedScratch<NT> red;
+  __shared__ StatScratch<NT> sst;
   __shared__ FusedLds<NT> sh;
   __shared__ Plan s_plan;
   __shared__ uint32_t s_word[2];
@@ -1447,9 +1466,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CDS_WAVES_PE
   const int sl = (int)(blockIdx.x - (unsigned)grp * (unsigned)a.P);
   const int r = a.order[grp];
   if (a.rows[r].flags & ROW_GREEDY)
-    slice_task<NT, E4, BF16, VEC, true>(a, r, sl, sh, red, &s_plan, s_word);
+    slice_task<NT, E4, BF16, VEC, true>(a, r, sl, sh, red, sst, &s_plan, s_word);
   else
-    slice_task<NT, E4, BF16, VEC, false>(a, r, sl, sh, red, &s_plan, s_word);
+    slice_task<NT, E4, BF16, VEC, false>(a, r, sl, sh, red, sst, &s_plan, s_word);
 }
 
 // ============================================================================

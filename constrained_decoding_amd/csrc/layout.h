@@ -55,7 +55,7 @@ struct BiasEntry {
 // mass that matters at the 1e-10 level.
 constexpr int NBINS = 560;
 #ifndef CDS_SCAN_THREADS
-#define CDS_SCAN_THREADS 512
+#define CDS_SCAN_THREADS 256
 #endif
 #ifndef CDS_MAX_CHUNKS
 #define CDS_MAX_CHUNKS 15
@@ -64,7 +64,7 @@ constexpr int kScanThreads = CDS_SCAN_THREADS;
 constexpr int kMaxChunks = CDS_MAX_CHUNKS;
 constexpr int64_t kSliceMax = (int64_t)kScanThreads * 4 * kMaxChunks;  // 30720 tokens
 constexpr int kCountShift = 48;   // histogram word: count << 48 | fixed-point mass
-constexpr int UCAP = 8192;        // listed tokens of a row the finisher holds on chip
+constexpr int UCAP = 4096;        // listed tokens of a row the finisher holds on chip
 constexpr int SCAP = 2048;        // listed tokens one slice can hand over
 constexpr int kMaxSlices = 64;
 constexpr int kMaxRows = 65535;
@@ -74,28 +74,32 @@ constexpr int kMaxRows = 65535;
 enum RowClass : uint32_t {
   CLS_GREEDY = 0,  // argmax: the planner answers from the slice summaries
   CLS_RACE = 1,    // no cut: each slice races all its tokens
-  CLS_LIST = 2,    // top-k (k <= SCAP) or min-p: each slice lists a superset of
-                   // its candidates; the planner resolves the row from the lists
-  CLS_HOLD = 3,    // top-p as the only cut, or top-k beyond SCAP: the slices
-                   // wait for the row's plan (histogram cuts)
+  CLS_LIST = 2,    // top-k with k*P <= UCAP/2 and k <= kScanThreads, or min-p
+                   // without top-k: each
+                   // slice lists a superset of its candidates; the planner
+                   // resolves the row from the lists
+  CLS_HOLD = 3,    // top-p as the only cut, or a larger top-k: the slices wait
+                   // for the row's plan (histogram cuts)
 };
 
 // (constexpr: callable from host and device code alike)
-constexpr RowClass row_class_of(uint32_t flags, int32_t top_k) {
-  if (flags & ROW_GREEDY) return CLS_GREEDY;
-  if (flags & ROW_TOPK) return top_k <= SCAP ? CLS_LIST : CLS_HOLD;
-  if (flags & ROW_MINP) return CLS_LIST;
-  if (flags & ROW_TOPP) return CLS_HOLD;
-  return CLS_RACE;
+constexpr RowClass row_class_of(uint32_t flags, int32_t top_k, int32_t P) {
+  return (flags & ROW_GREEDY)  ? CLS_GREEDY
+         : (flags & ROW_TOPK)  ? ((int64_t)top_k * P <= UCAP / 2 && top_k <= kScanThreads
+                                      ? CLS_LIST : CLS_HOLD)
+         : (flags & ROW_MINP)  ? CLS_LIST
+         : (flags & ROW_TOPP)  ? CLS_HOLD
+                               : CLS_RACE;
 }
 
 // ---- workspace ------------------------------------------------------------
-// Per-row meeting point of the row's workgroups.  Counters hold the call's
-// generation in the high half and a count in the low half (a counter of
-// another generation counts as zero); flags hold the generation that set them.
+// Per-row meeting point of the row's workgroups.  Counters count the slices
+// of the current call that passed them; the last one resets the counter to
+// zero (so they are zero between calls).  Flags hold the call generation that
+// set them.
 struct RowSync {
-  unsigned long long arrive;  // scan tasks done
-  unsigned long long done;    // race tasks done
+  unsigned long long arrive;  // slices that published their summary
+  unsigned long long done;    // HOLD slices that finished their race
   uint32_t ready;             // generation whose plan is published
   uint32_t failed;            // generation in which a race task gave up waiting
   uint32_t pad[2];

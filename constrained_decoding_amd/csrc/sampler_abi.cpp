@@ -182,14 +182,23 @@ int pack_into(const sampler_host_params* h, std::vector<unsigned char>& out_buf,
   // other sampled rows, then the greedy rows
   std::vector<int32_t> order;
   order.reserve((size_t)B);
+  const int P = choose_slices(V);
   auto holds = [&](int32_t r) {
-    return row_class_of(rows[(size_t)r].flags, rows[(size_t)r].top_k) == CLS_HOLD;
+    return row_class_of(rows[(size_t)r].flags, rows[(size_t)r].top_k, P) == CLS_HOLD;
   };
+#ifdef CDS_HOLD_LAST
+  for (int32_t r : sampled)
+    if (!holds(r)) order.push_back(r);
+  order.insert(order.end(), greedy_rows.begin(), greedy_rows.end());
+  for (int32_t r : sampled)
+    if (holds(r)) order.push_back(r);
+#else
   for (int32_t r : sampled)
     if (holds(r)) order.push_back(r);
   for (int32_t r : sampled)
     if (!holds(r)) order.push_back(r);
   order.insert(order.end(), greedy_rows.begin(), greedy_rows.end());
+#endif
   std::memcpy(p + off_list, order.data(), sizeof(int32_t) * order.size());
   std::memcpy(p + off_pen, pen.data(), sizeof(PenEntry) * pen.size());
   std::memcpy(p + off_pen + sizeof(PenEntry) * pen.size(), bias.data(),

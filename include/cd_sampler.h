@@ -144,8 +144,9 @@ typedef struct sampler_batch {
                             in which sampler_sample dispatches the rows: the
                             n_sampled rows that are not greedy (first those
                             whose cut needs the whole row's histogram: top-p
-                            as the only cut, or top_k > 2048), then the
-                            greedy rows; ascending within each group       */
+                            as the only cut, or a top_k above a bound that
+                            depends on V), then the greedy rows; ascending
+                            within each group                              */
 } sampler_batch;
 
 /* Message for a SAMPLER_* return code (static storage). */
