@@ -567,6 +567,29 @@ __device__ __forceinline__ T wave_allreduce(T v, Op op) {
   return op(op(r0, r1), op(r2, r3));
 }
 
+// q-th largest (1 <= q <= 64) of one value per lane, by a walk over the order
+// key bits with ballots (scalar work, no LDS); every lane gets the result.  All
+// 64 lanes must be active.
+__device__ __forceinline__ float wave_kth_largest(float v, int q) {
+  const uint32_t key = okey(v + 0.0f);
+  unsigned long long cand = ~0ull;
+  uint32_t prefix = 0u;
+  int need = q;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    const unsigned long long ones = __ballot((key >> bit) & 1u) & cand;
+    const int n1 = __popcll(ones);
+    if (n1 >= need) {
+      cand = ones;
+      prefix |= 1u << bit;
+    } else {
+      need -= n1;
+      cand &= ~ones;
+    }
+  }
+  return from_okey(prefix);
+}
+
 // ---- one-pass slice summary ----------------------------------------------------
 // The per-thread summary of a thread's values, and its merge: max, the lowest
 // index holding it, sum exp2((x - max) * c) relative to that max, the

@@ -947,10 +947,8 @@ union FusedLds {
     int32_t off[kMaxSlices + 1];
   } fin;
   struct {
-    uint32_t cnt[256];  // top-k filter histogram
-    uint32_t bstar;     // its cut bin
+    uint32_t wt[NT / 64];  // per-wave token counts (list_tokens)
   } sel;
-  uint64_t stage[SCAP];
 };
 
 
@@ -958,38 +956,45 @@ __device__ __forceinline__ int row_class(const RowParams& rp, int P) {
   return (int)row_class_of(rp.flags, rp.top_k, P);
 }
 
-// Appends the slice's tokens whose value passes keep() to the LDS stage as
-// okey(v) << 32 | ~t: one LDS reservation per wave and chunk, only where some
-// lane holds such a token.  *cnt (LDS) counts them all (stage holds SCAP).
+// Lists the slice's tokens whose value passes keep() in the slice's global
+// list (up to SCAP entries, okey(v) << 32 | ~t, in thread-major order): each
+// thread counts its tokens, a wave prefix sum and one workgroup barrier give
+// every thread its position, then the tokens are stored directly.  Returns the
+// number of tokens that passed (> SCAP: the list overflowed).  wt is LDS
+// scratch of NT/64 words; all NT threads must call it.
 template <int NT, int E4, typename Keep>
-__device__ __forceinline__ void stage_tokens(const float (&x)[E4][4], int32_t tbase,
-                                             uint64_t* stage, uint32_t* cnt, Keep keep) {
-  const int lane = threadIdx.x & 63;
+__device__ __forceinline__ uint32_t list_tokens(const float (&x)[E4][4], int32_t tbase,
+                                                uint64_t* list, uint32_t* wt, Keep keep) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t c = 0u;
 #pragma unroll
-  for (int i = 0; i < E4; ++i) {
-    uint32_t um = 0u;
+  for (int i = 0; i < E4; ++i)
 #pragma unroll
-    for (int q = 0; q < 4; ++q) um |= keep(x[i][q]) ? (1u << q) : 0u;
-    if (__any(um)) {
-      int32_t tb = tbase;
-      asm volatile("" : "+v"(tb));
-      const int32_t t0 = tb + 4 * NT * i;
-      const uint32_t c = (uint32_t)__popc(um);
-      const uint32_t incl = wave_incl_sum(c);
-      uint32_t base = 0;
-      if (lane == 63) base = atomicAdd(cnt, incl);
-      base = (uint32_t)__builtin_amdgcn_readlane((int)base, 63);
-      uint32_t pos = base + incl - c;
+    for (int q = 0; q < 4; ++q) c += keep(x[i][q]) ? 1u : 0u;
+  const uint32_t incl = wave_incl_sum(c);
+  if (lane == 63) wt[w] = incl;
+  __syncthreads();
+  uint32_t base = 0u, total = 0u;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) {
+    const uint32_t tk = wt[k];
+    base += k < w ? tk : 0u;
+    total += tk;
+  }
+  if (c) {
+    uint32_t pos = base + incl - c;
+#pragma unroll
+    for (int i = 0; i < E4; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        if ((um >> q) & 1u) {
+        if (keep(x[i][q])) {
           if (pos < (uint32_t)SCAP)
-            stage[pos] = ((uint64_t)okey(x[i][q] + 0.0f) << 32) |
-                         (uint64_t)(0xFFFFFFFFu - (uint32_t)(t0 + q));
+            st_u64(list + pos, ((uint64_t)okey(x[i][q] + 0.0f) << 32) |
+                                   (uint64_t)(0xFFFFFFFFu - (uint32_t)(tbase + 4 * NT * i + q)));
           ++pos;
         }
-    }
   }
+  return total;
 }
 
 // Smallest fp32 value v with exp(v/T - zmax/T) >= min_p (the min-p set
@@ -1069,9 +1074,10 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
     for (int i = 0; i < E4; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) st.m = fmaxf(st.m, x[i][q]);
-    // top-k rows (k <= NT): the thread maximum; the minimum over threads has
-    // at least NT >= k tokens at or above it
-    if (topk_list) st.lb = st.m;
+    // top-k rows (k <= NT): each wave's ceil(k/W)-th largest lane maximum
+    // (W waves); every wave has that many tokens at or above its own value, so
+    // at least k tokens of the slice lie at or above the minimum over waves
+    if (topk_list) st.lb = wave_kth_largest(st.m, (kq + NT / 64 - 1) / (NT / 64));
     if (cexp != 0.0f && st.m != CDS_NEG_INF) {
       // exp2(x*c - max*c): one FMA per token; a NaN or +inf token makes the
       // sum NaN (or the max +inf), which flags the slice
@@ -1151,9 +1157,7 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
       }
     }
   }
-#ifndef CDS_TRACE_DETAIL
   CDS_TRACE(3);
-#endif
   if (cls == CLS_RACE && zm != CDS_NEG_INF && !nonfin) {
     // the race over every allowed token, keys relative to the slice maximum
     const float invT32 = sgpr_f((float)(1.0 / (double)rp.temperature));
@@ -1195,69 +1199,15 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
     // cut that is at most the slice's top_k-th largest value (top-k rows) and
     // at most the min-p bound relative to the slice maximum (min-p rows; the
     // row's bound, relative to the row maximum, is at least as high)
-    float cut = CDS_NEG_INF;
-    uint32_t bstar = 0u;
-    float inv_w = 0.0f;
-    const float L0 = st.lb;
-    if (topk_list && L0 != CDS_NEG_INF) {
-      // 256 bins over [L0, zm]; the cut bin holds the kq-th largest token
-      // (bins are monotone in the value: every token above a listed one is
-      // listed too)
-      inv_w = zm > L0 ? 255.0f / (zm - L0) : 0.0f;
-      uint32_t* cnt = sh.sel.cnt;
-      if (tid < 256) cnt[tid] = 0u;
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < E4; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const float v = x[i][q];
-          if (v >= L0) atomicAdd(&cnt[min(255, (int)((v - L0) * inv_w))], 1u);
-        }
-      __syncthreads();
-      if (tid < 64) {
-        // lane l owns bins 255-4l .. 252-4l (descending values)
-        const int l = tid;
-        const uint32_t c1 = cnt[255 - 4 * l], c2 = c1 + cnt[254 - 4 * l];
-        const uint32_t c3 = c2 + cnt[253 - 4 * l], c4 = c3 + cnt[252 - 4 * l];
-        const uint32_t incl = wave_incl_sum(c4);
-        const uint32_t ex = incl - c4;
-        const unsigned long long hit = __ballot(incl >= (uint32_t)kq);
-        const int first = hit ? __ffsll((long long)hit) - 1 : 63;
-        if (l == first) {
-          int j;
-          if (!hit || ex + c1 >= (uint32_t)kq) j = 0;
-          else if (ex + c2 >= (uint32_t)kq) j = 1;
-          else if (ex + c3 >= (uint32_t)kq) j = 2;
-          else j = 3;
-          sh.sel.bstar = hit ? (uint32_t)(255 - 4 * l - j) : 0u;
-        }
-      }
-      __syncthreads();
-      bstar = sh.sel.bstar;
-      // every token with bin >= bstar is >= L0 + bstar / inv_w up to rounding;
-      // half a bin lower keeps a superset with one compare per token
-      cut = (bstar == 0u || inv_w == 0.0f) ? L0 : fmaxf(L0, L0 + ((float)bstar - 0.5f) / inv_w);
-#ifdef CDS_TRACE_DETAIL
-      CDS_TRACE(3);
-#endif
-    }
+    float cut = (topk_list && st.lb != CDS_POS_INF) ? st.lb : CDS_NEG_INF;
     if (rp.flags & ROW_MINP) {
       const double b = (double)zm + (double)rp.temperature * log((double)rp.min_p);
       const float bm = (float)(b - 1e-5 * (1.0 + fabs(b) + fabs((double)zm)));
       cut = fmaxf(cut, bm);
     }
-    if (tid == 0) s_word[1] = 0u;
-    __syncthreads();
     const float cutv = sgpr_f(cut);
-    stage_tokens<NT, E4>(x, tbase, sh.stage, &s_word[1],
-                         [&](float v) { return v >= cutv && v != CDS_NEG_INF; });
-    __syncthreads();
-    const uint32_t nst = s_word[1];
-    if (nst <= (uint32_t)SCAP) {
-      uint64_t* ul = a.ulist + slot * SCAP;
-      for (uint32_t i = tid; i < nst; i += NT) st_u64(ul + i, sh.stage[i]);
-    }
+    const uint32_t nst = list_tokens<NT, E4>(x, tbase, a.ulist + slot * SCAP, sh.sel.wt,
+                                             [&](float v) { return v >= cutv && v != CDS_NEG_INF; });
     if (tid == 0) {
       SliceBest sb;
       sb.k1 = CDS_NEG_INF;
@@ -1362,7 +1312,6 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
       st_u32(&sy->failed, a.gen);
     }
   }
-  if (tid == 0) s_word[1] = 0u;
   __syncthreads();
   CDS_TRACE(6);
 
@@ -1399,16 +1348,11 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
       }
     }
     // the boundary-bin tokens, listed
+    uint32_t nst = 0u;
     if (has_u)
-      stage_tokens<NT, E4>(x, tbase, sh.stage, &s_word[1], [&](float v) {
+      nst = list_tokens<NT, E4>(x, tbase, a.ulist + slot * SCAP, sh.sel.wt, [&](float v) {
         return is_boundary(v, zs, zc1, a_lo, a_hi, k_lo, k_hi);
       });
-    __syncthreads();
-    const uint32_t nst = s_word[1];
-    if (nst && nst <= (uint32_t)SCAP) {
-      uint64_t* ul = a.ulist + slot * SCAP;
-      for (uint32_t i = tid; i < nst; i += NT) st_u64(ul + i, sh.stage[i]);
-    }
     block_top2<NT>(b, red);
     if (tid == 0) {
       SliceBest sb;
@@ -1461,9 +1405,16 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CDS_WAVES_PE
   __shared__ FusedLds<NT> sh;
   __shared__ Plan s_plan;
   __shared__ uint32_t s_word[2];
-  // block -> (the grp-th row of the packed row order, slice)
-  const int grp = (int)(blockIdx.x / (unsigned)a.P);
-  const int sl = (int)(blockIdx.x - (unsigned)grp * (unsigned)a.P);
+  // Workgroups are dispatched round-robin over the kXcds XCDs.  Block b runs on
+  // XCD x = b % kXcds as that XCD's j-th block (j = b / kXcds); it takes slice
+  // j % P of the XCD's (j / P)-th row, the ordered row g = (j / P) * kXcds + x.
+  // All slices of a row then run on one XCD, next to each other in its
+  // dispatch order, and every XCD gets every kXcds-th row of the packed order.
+  const unsigned x = blockIdx.x % (unsigned)kXcds, j = blockIdx.x / (unsigned)kXcds;
+  const int lr = (int)(j / (unsigned)a.P);
+  const int sl = (int)(j - (unsigned)lr * (unsigned)a.P);
+  const int grp = lr * kXcds + (int)x;
+  if (grp >= a.B) return;
   const int r = a.order[grp];
   if (a.rows[r].flags & ROW_GREEDY)
     slice_task<NT, E4, BF16, VEC, true>(a, r, sl, sh, red, sst, &s_plan, s_word);
@@ -1518,7 +1469,8 @@ static hipError_t launch_fused(const SampleArgs& a, const KernelEvents* ev, hipS
   if (a.S > kSliceMax) return hipErrorInvalidValue;
   rec(ev, true, s);
   hipLaunchKernelGGL((sample_kernel<kScanThreads, kMaxChunks, BF16, VEC>),
-                     dim3((unsigned)a.B * (unsigned)a.P), dim3(kScanThreads), 0, s, a);
+                     dim3((unsigned)((a.B + kXcds - 1) / kXcds * kXcds) * (unsigned)a.P),
+                     dim3(kScanThreads), 0, s, a);
   rec(ev, false, s);
   return hipGetLastError();
 }

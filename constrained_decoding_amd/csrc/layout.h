@@ -67,6 +67,7 @@ constexpr int kCountShift = 48;   // histogram word: count << 48 | fixed-point m
 constexpr int UCAP = 4096;        // listed tokens of a row the finisher holds on chip
 constexpr int SCAP = 2048;        // listed tokens one slice can hand over
 constexpr int kMaxSlices = 64;
+constexpr int kXcds = 8;          // XCDs of an MI355X (workgroups go round-robin over them)
 constexpr int kMaxRows = 65535;
 
 // How a row's slices work in the sampling kernel.  The host dispatches the rows

@@ -255,7 +255,7 @@ int sampler_sample(const sampler_batch *b, const void *logits, int dtype,
  * sampler_set_option(SAMPLER_OPT_TRACE, ptr): diagnostic phase timestamps.
  * ptr = 0 turns it off (default); otherwise ptr is the device address of a
  * caller-owned uint64 buffer of 8 words per workgroup of the sampling kernel
- * (B * P workgroups, P = slices per row, at most 64), which every later
+ * (8 * ceil(B/8) * P workgroups, P = slices per row, at most 64), which every later
  * sampler_sample call overwrites: word 0 = row | slice << 20 | class << 28 |
  * planner << 31, words 1..7 = the 100 MHz device wall clock at the start, after
  * the slice maximum, after the summary pass, after the class work, after the
