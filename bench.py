@@ -70,7 +70,7 @@ def kernel_sources_digest():
 
 
 def measured_traffic(config):
-    """HBM bytes per scan_kernel launch from the committed FETCH_SIZE /
+    """HBM bytes per sample_kernel launch from the committed FETCH_SIZE /
     WRITE_SIZE summary of this workload, or None when that summary is missing
     or was taken on different kernel sources."""
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{WORKLOAD_FILES[config]}.md")
@@ -79,7 +79,7 @@ def measured_traffic(config):
     fields = {}
     with open(path) as fh:
         for ln in fh:
-            if ln.startswith("scan_kernel ") and ":" in ln:
+            if ln.startswith("sample_kernel ") and ":" in ln:
                 k, v = ln.split(":", 1)
                 fields[k.split()[1]] = v.strip()
     if fields.get("traffic_sources_sha256") != kernel_sources_digest():
@@ -245,7 +245,7 @@ def main():
         "config": {"workload": names[args.config], "B": B, "V": V, "input_sets": len(sets),
                    "algo": "fast" if args.algo == 0 else "row-exact"},
         "pipeline_gbs": round(alg / (ms_per_step * 1e-3) / 1e9, 1),
-        "roofline": {"bound": "hbm", "kernel": "scan_kernel", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "sample_kernel", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(args.config),

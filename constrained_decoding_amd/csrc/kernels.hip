@@ -1,32 +1,19 @@
 // kernels.hip -- HIP kernels of libcd_sampler.so for gfx950 (MI355X).
 //
-// The sampling step for rows that are not greedy runs as three kernels:
-//
-//   scan    grid (P, B): one workgroup per slice of S tokens.  Streams the
-//           slice from HBM once into registers (bf16 upcast and the grammar
-//           bitmask fused into the load), reduces max / argmax / finite count /
-//           sum exp, and for rows with a top-k or top-p cut builds a histogram
-//           of s = z/T over bins of width 1/16 aligned to an absolute grid
-//           (counts, and fixed-point masses relative to each bin's upper edge,
-//           so slices merge by integer addition).  The last slice of a row to
-//           finish (atomic ticket) merges the slices, writes greedy / invalid
-//           rows' outputs, and for the rest writes a plan: the exact min-p cut,
-//           the value range of "sure" tokens (certainly inside the final
-//           candidate set), and the value ranges of the bins that hold the top-k
-//           and top-p boundaries.
-//   race    grid (P, B): re-reads the slice; runs the exponential race over the
-//           sure tokens and appends the boundary-bin tokens to a per-row list.
-//   finish  grid (B): sorts the boundary list in LDS, finds the exact top-k
-//           value, the exact top-p cut (fp64 cumulative mass in sorted order),
-//           races the boundary tokens that survive, merges with the slices'
-//           winners and writes the output.  Rows whose boundary list would not
-//           fit in LDS, and rows whose plan the exact pass contradicts, run the
-//           row-serial exact path instead.
+// The sampling step is one kernel, sample_kernel: one workgroup per slice of a
+// row (P slices of at most kMaxChunks * 4 * kScanThreads tokens).  Each slice
+// streams its tokens from HBM once into registers (bf16 upcast and the grammar
+// bitmask fused into the load), summarises them, does the work its row's
+// class asks for (see slice_task), and publishes the result; the last slice of
+// a row to arrive resolves the row.  Only rows whose cut needs the whole row's
+// histogram (top-p as the only cut, large top-k) make their slices wait for a
+// row plan, with their tokens still in registers.
 //
 // The row-serial exact path (row_exact) does everything with one workgroup
 // and several passes over the row: radix select for the k-th largest value,
 // a mass-weighted radix select for the top-p cut (fixed-point masses), then
-// the race.  It is also selectable for all rows (SAMPLER_OPT_ALGO = 1).
+// the race.  It is the fallback of rows the fast path cannot hold on chip, and
+// selectable for all rows (SAMPLER_OPT_ALGO = 1).
 //
 // Definitions followed (sources cited by page title and section):
 //  - transforms: "SGLang 源码完全拆解(十)", section 惩罚项的顺序语义 (additive
@@ -360,36 +347,8 @@ __global__ __launch_bounds__(NT) void exact_kernel(const SampleArgs a) {
 }
 
 // ============================================================================
-// fast path: one kernel, (B + sampled rows)*P workgroups, two kinds of task
+// fast path: one kernel, one workgroup per slice (see slice_task)
 // ============================================================================
-//
-// Scan task for slice s of row r.  Streams
-//   the slice into registers; reduces max, argmax and the non-finite flag;
-//   builds either the histogram (rows with a top-k or top-p cut) or sum exp;
-//   writes the slice summary and takes the row's arrival ticket.  The last
-//   slice of a row to arrive merges the summaries into the row's plan (greedy,
-//   invalid and overflow rows get their output here) and raises the row's
-//   ready flag.
-// Race task for slice s of row r
-//   (sampled rows only).  Waits for the row's plan, re-reads the slice (just
-//   read by the scan task, so it comes from the caches), races the tokens
-//   that are surely in the final set, stages the boundary-bin tokens in LDS
-//   and copies them to the slice's own list; then takes the row's done
-//   ticket.  The last race task of a row resolves the boundary list
-//   (exact top-k value and top-p cut by radix selects), races the surviving
-//   boundary tokens, merges the slices' top two and writes the output; rows
-//   the plan could not handle take the row-serial exact path there.
-//
-// Race tasks follow every scan task in dispatch order, so while early rows
-// race, later rows still stream from HBM, and a race task's wait ends once
-// the scans of its row, dispatched before it, complete.  Greedy rows get no
-// race tasks.  The wait is still
-// bounded by wall-clock time: a task that gives up marks the row and the
-// finisher then runs the exact path, so results never depend on timing.
-//
-// The row's counters carry the call's generation number in their high half:
-// a counter left by another call reads as zero, so nothing needs resetting
-// between calls (and a task that gave up cannot disturb a later call).
 
 // ---- cross-workgroup data and counters ----------------------------------------
 // Everything one workgroup hands to another goes through agent-coherent
