@@ -78,22 +78,57 @@ __device__ __forceinline__ float minp_cut(float zmax, double Td, double m, float
 // ============================================================================
 // transforms and bitmask (in place)
 // ============================================================================
+// One workgroup per row.  Raw history rows (ROW_PEN_RAW, at most kHistDevice
+// tokens) are first merged into (token, count) pairs in an LDS hash table with
+// at least twice as many slots as tokens (linear probing, atomicCAS on the
+// key), so every penalised token is updated exactly once with its full count.
+__device__ __forceinline__ void apply_penalty(float* z, int32_t id, int32_t count,
+                                              const RowParams& rp) {
+  float v = z[id];
+  const float p = __fadd_rn(__fmul_rn(rp.freq, (float)count), rp.pres);
+  v = __fsub_rn(v, p);
+  if (rp.rep != 1.0f) v = (v > 0.0f) ? __fdiv_rn(v, rp.rep) : __fmul_rn(v, rp.rep);
+  z[id] = v;
+}
+
 __global__ __launch_bounds__(256) void transforms_kernel(const RowParams* rows,
                                                          const PenEntry* pen,
                                                          const BiasEntry* bias, float* logits,
                                                          int64_t ld) {
+  constexpr uint32_t kEmpty = 0xFFFFFFFFu;
+  __shared__ uint32_t keys[2 * kHistDevice];
+  __shared__ int32_t cnts[2 * kHistDevice];
   const int r = blockIdx.x;
   const RowParams rp = rows[r];
   float* z = logits + (int64_t)r * ld;
-  if (rp.flags & ROW_PEN) {
+  if ((rp.flags & ROW_PEN) && (rp.flags & ROW_PEN_RAW)) {
+    const int n = rp.pen_hi - rp.pen_lo;
+    int lg = 6;
+    while ((1 << lg) < 2 * n) ++lg;  // <= log2(2 * kHistDevice)
+    const uint32_t ht = 1u << lg;
+    for (uint32_t k = threadIdx.x; k < ht; k += blockDim.x) {
+      keys[k] = kEmpty;
+      cnts[k] = 0;
+    }
+    __syncthreads();
     for (int i = rp.pen_lo + (int)threadIdx.x; i < rp.pen_hi; i += blockDim.x) {
       const PenEntry e = pen[i];
-      float v = z[e.id];
-      const float p = __fadd_rn(__fmul_rn(rp.freq, (float)e.count), rp.pres);
-      v = __fsub_rn(v, p);
-      if (rp.rep != 1.0f) v = (v > 0.0f) ? __fdiv_rn(v, rp.rep) : __fmul_rn(v, rp.rep);
-      z[e.id] = v;
+      uint32_t h = ((uint32_t)e.id * 0x9E3779B1u) >> (32 - lg);
+      while (true) {
+        const uint32_t old = atomicCAS(&keys[h], kEmpty, (uint32_t)e.id);
+        if (old == kEmpty || old == (uint32_t)e.id) {
+          atomicAdd(&cnts[h], e.count);
+          break;
+        }
+        h = (h + 1u) & (ht - 1u);
+      }
     }
+    __syncthreads();
+    for (uint32_t k = threadIdx.x; k < ht; k += blockDim.x)
+      if (keys[k] != kEmpty) apply_penalty(z, (int32_t)keys[k], cnts[k], rp);
+  } else if (rp.flags & ROW_PEN) {
+    for (int i = rp.pen_lo + (int)threadIdx.x; i < rp.pen_hi; i += blockDim.x)
+      apply_penalty(z, pen[i].id, pen[i].count, rp);
   }
   __syncthreads();  // a token may carry both a penalty and a bias
   if (rp.flags & ROW_BIAS) {

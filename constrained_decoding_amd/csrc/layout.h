@@ -14,6 +14,8 @@ enum RowFlag : uint32_t {
   ROW_TOPP = 1u << 2,    // top_p < 1 on a non-greedy row
   ROW_MINP = 1u << 3,    // min_p > 0 on a non-greedy row
   ROW_PEN = 1u << 4,     // has penalty entries
+  ROW_PEN_RAW = 1u << 6, // its penalty entries are raw history tokens (count 1,
+                         // repeats not merged): the transforms kernel counts them
   ROW_BIAS = 1u << 5,    // has bias entries
 };
 
@@ -66,6 +68,7 @@ constexpr int64_t kSliceMax = (int64_t)kScanThreads * 4 * kMaxChunks;  // 30720 
 constexpr int kCountShift = 48;   // histogram word: count << 48 | fixed-point mass
 constexpr int UCAP = 4096;        // listed tokens of a row the finisher holds on chip
 constexpr int SCAP = 2048;        // listed tokens one slice can hand over
+constexpr int kHistDevice = 4096;  // history tokens per row counted on the device
 constexpr int kMaxSlices = 64;
 constexpr int kXcds = 8;          // XCDs of an MI355X (workgroups go round-robin over them)
 constexpr int kMaxRows = 65535;

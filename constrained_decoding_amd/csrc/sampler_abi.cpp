@@ -137,13 +137,19 @@ int pack_into(const sampler_host_params* h, std::vector<unsigned char>& out_buf,
     if (h->hist_indptr && pen_active) {
       const int64_t lo = h->hist_indptr[r], hi = h->hist_indptr[r + 1];
       if (hi > lo) {
-        scratch_ids.assign(h->hist_ids + lo, h->hist_ids + hi);
-        std::sort(scratch_ids.begin(), scratch_ids.end());
-        for (size_t i = 0; i < scratch_ids.size();) {
-          size_t j = i;
-          while (j < scratch_ids.size() && scratch_ids[j] == scratch_ids[i]) ++j;
-          pen.push_back(PenEntry{scratch_ids[i], (int32_t)(j - i)});
-          i = j;
+        if (hi - lo <= kHistDevice) {
+          // as they come: the transforms kernel merges repeats
+          for (int64_t i = lo; i < hi; ++i) pen.push_back(PenEntry{h->hist_ids[i], 1});
+          rp.flags |= ROW_PEN_RAW;
+        } else {
+          scratch_ids.assign(h->hist_ids + lo, h->hist_ids + hi);
+          std::sort(scratch_ids.begin(), scratch_ids.end());
+          for (size_t i = 0; i < scratch_ids.size();) {
+            size_t j = i;
+            while (j < scratch_ids.size() && scratch_ids[j] == scratch_ids[i]) ++j;
+            pen.push_back(PenEntry{scratch_ids[i], (int32_t)(j - i)});
+            i = j;
+          }
         }
         rp.pen_hi = (int32_t)pen.size();
         rp.flags |= ROW_PEN;

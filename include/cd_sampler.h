@@ -159,8 +159,10 @@ const char *sampler_version(void);
  * n_hist history ids and n_bias bias entries in total. */
 size_t sampler_params_bytes(int32_t B, int64_t n_hist, int64_t n_bias);
 
-/* Validate `h`, compute the batch flags and max_top_k, count each row's
- * history into (token, count) entries, deduplicate the bias, and copy the
+/* Validate `h`, compute the batch flags and max_top_k, pack each row's
+ * history as (token, count) entries (rows of up to 4096 history tokens as
+ * they come, count 1 each, counted on the device by sampler_apply_transforms;
+ * longer rows counted here), deduplicate the bias, and copy the
  * packed block to d_buf (dev, >= sampler_params_bytes(...) bytes) on
  * `stream`.  h_staging: pinned host memory of >= the same size used as the
  * copy source (it must stay untouched until the copy has run), or NULL:
@@ -188,6 +190,8 @@ int sampler_pack_host(const sampler_host_params *h, void *host_buf,
  * ([SGL] "惩罚项的顺序语义": additive before scaling), then z += bias for
  * each deduplicated bias entry ([SGL] same section: bias after the mask;
  * applying it before a later mask is identical because -inf + b = -inf).
+ * Repeated history tokens are merged into one count per token on the device
+ * (an LDS hash table per row), so each token is updated once.
  * Tokens outside history and bias are not touched.  Skipped (no launch) when
  * the batch has neither NEED_PENALTY nor HAS_BIAS.  bf16 logits would round
  * the transformed values, so only fp32 is accepted here. */

@@ -90,8 +90,11 @@ def test_penalty_counts_and_bias_dedup(cds):
     assert np.frombuffer(buf[64 * 3:64 * 3 + 12].tobytes(), "<i4").tolist() == [0, 1, 2]
     pen_off = 64 * 3 + 16        # the sampled-row list: room for B int32, 16-byte padded
     pen = np.frombuffer(buf[pen_off:pen_off + 8 * b.n_pen].tobytes(), "<i4").reshape(-1, 2)
-    np.testing.assert_array_equal(pen, [[3, 3], [7, 1]])      # row 2 has no active penalty
-    assert (rows["pen_lo"][0], rows["pen_hi"][0]) == (0, 2)
+    # rows of up to 4096 history tokens are packed as they come (count 1 each;
+    # the transforms kernel merges repeats); row 2 has no active penalty
+    np.testing.assert_array_equal(pen, [[3, 1], [3, 1], [7, 1], [3, 1]])
+    assert (rows["pen_lo"][0], rows["pen_hi"][0]) == (0, 4)
+    assert rows["flags"][0] & (1 << 6)                      # ROW_PEN_RAW
     assert b.flags & cds.FLAG_NEED_PENALTY and b.flags & cds.FLAG_HAS_BIAS
     off = pen_off + 8 * b.n_pen
     bias = np.frombuffer(buf[off:off + 8 * b.n_bias].tobytes(),

@@ -100,6 +100,32 @@ def test_transformed_logits_bit_exact():
         np.testing.assert_array_equal(got[r].view(np.uint32), ref.view(np.uint32))
 
 
+def test_transforms_history_counting_paths():
+    """Histories of up to 4096 tokens are counted on the device (LDS hash
+    table), longer ones on the host: one row of 5000 tokens, one of a single
+    token repeated 600 times, one of 4096 distinct tokens; bit-exact."""
+    import torch
+    import constrained_decoding_amd as cds
+    b = workloads.c3_penalties(B=6, V=30000, salt=13)
+    rng = np.random.default_rng(14)
+    hist = [b.hist(r) for r in range(b.B)]
+    hist[0] = rng.integers(0, b.V, 5000).astype(np.int32)
+    hist[1] = np.full(600, 17, np.int32)
+    hist[2] = rng.permutation(b.V)[:4096].astype(np.int32)
+    hist[3] = np.zeros(0, np.int32)
+    b.hist_indptr, b.hist_ids = cds.csr(hist)
+    x = to_device(b)
+    cds.apply_transforms(pack(b), x)
+    torch.cuda.synchronize()
+    got = x.cpu().numpy()
+    for r in range(b.B):
+        ref = oracle.transform_row(b.logits[r], hist_ids=b.hist(r), rep=float(b.rep[r]),
+                                   freq=float(b.freq[r]), pres=float(b.pres[r]),
+                                   bias_ids=b.bias_ids[b.bias_indptr[r]:b.bias_indptr[r + 1]],
+                                   bias_vals=b.bias_vals[b.bias_indptr[r]:b.bias_indptr[r + 1]])
+        np.testing.assert_array_equal(got[r].view(np.uint32), ref.view(np.uint32))
+
+
 def test_bitmask_inplace_matches_oracle_fp32_and_bf16():
     import torch
     import constrained_decoding_amd as cds
