@@ -39,9 +39,11 @@ size_t params_bytes_exact(int32_t B, int64_t n_pen, int64_t n_bias) {
          sizeof(BiasEntry) * (size_t)n_bias;
 }
 
-// Validate and pack into `out_buf` (host memory).  Returns a SAMPLER_* code.
-int pack_into(const sampler_host_params* h, std::vector<unsigned char>& out_buf,
-              sampler_batch* out) {
+// Validate and pack into host memory: `dst` (cap bytes), or when dst is null
+// into `tmp`.  Everything is validated and sized first, then written once into
+// the destination.  Returns a SAMPLER_* code (ENOSPC: cap too small).
+int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
+              std::vector<unsigned char>* tmp, sampler_batch* out) {
   if (!h || !out) return SAMPLER_EINVAL;
   const int32_t B = h->B, V = h->V;
   if (B <= 0 || V <= 0) return SAMPLER_EINVAL;
@@ -73,8 +75,13 @@ int pack_into(const sampler_host_params* h, std::vector<unsigned char>& out_buf,
 
   std::vector<RowParams> rows((size_t)B);
   std::vector<int32_t> sampled, greedy_rows;
+  // Penalty entries: rows of up to kHistDevice history tokens are written
+  // later straight from hist_ids (count 1 each); only longer rows are counted
+  // here, into `pen`.  n_pen counts both.
   std::vector<PenEntry> pen;
+  int64_t n_pen = 0;
   std::vector<BiasEntry> bias;
+  if (h->bias_indptr) bias.reserve((size_t)h->bias_indptr[B]);
   uint32_t flags = SAMPLER_FLAG_ALL_GREEDY;
   bool all_nongreedy_have_k = true;
   int32_t max_k = 0;
@@ -132,14 +139,15 @@ int pack_into(const sampler_host_params* h, std::vector<unsigned char>& out_buf,
     }
 
     // penalties: (token, count) from the row's history
-    rp.pen_lo = rp.pen_hi = (int32_t)pen.size();
+    if (n_pen > (int64_t)INT32_MAX) return SAMPLER_ERANGE;
+    rp.pen_lo = rp.pen_hi = (int32_t)n_pen;
     const bool pen_active = (rep != 1.0f) || (fr != 0.0f) || (pr != 0.0f);
     if (h->hist_indptr && pen_active) {
       const int64_t lo = h->hist_indptr[r], hi = h->hist_indptr[r + 1];
       if (hi > lo) {
         if (hi - lo <= kHistDevice) {
           // as they come: the transforms kernel merges repeats
-          for (int64_t i = lo; i < hi; ++i) pen.push_back(PenEntry{h->hist_ids[i], 1});
+          n_pen += hi - lo;
           rp.flags |= ROW_PEN_RAW;
         } else {
           scratch_ids.assign(h->hist_ids + lo, h->hist_ids + hi);
@@ -148,10 +156,12 @@ int pack_into(const sampler_host_params* h, std::vector<unsigned char>& out_buf,
             size_t j = i;
             while (j < scratch_ids.size() && scratch_ids[j] == scratch_ids[i]) ++j;
             pen.push_back(PenEntry{scratch_ids[i], (int32_t)(j - i)});
+            ++n_pen;
             i = j;
           }
         }
-        rp.pen_hi = (int32_t)pen.size();
+        if (n_pen > (int64_t)INT32_MAX) return SAMPLER_ERANGE;
+        rp.pen_hi = (int32_t)n_pen;
         rp.flags |= ROW_PEN;
         flags |= SAMPLER_FLAG_NEED_PENALTY;
       }
@@ -176,11 +186,16 @@ int pack_into(const sampler_host_params* h, std::vector<unsigned char>& out_buf,
     }
     rows[(size_t)r] = rp;
   }
-  if (pen.size() > (size_t)INT32_MAX || bias.size() > (size_t)INT32_MAX) return SAMPLER_ERANGE;
+  if (bias.size() > (size_t)INT32_MAX) return SAMPLER_ERANGE;
 
-  const size_t bytes = params_bytes_exact(B, (int64_t)pen.size(), (int64_t)bias.size());
-  out_buf.assign(bytes, 0);
-  unsigned char* p = out_buf.data();
+  const size_t bytes = params_bytes_exact(B, n_pen, (int64_t)bias.size());
+  unsigned char* p = dst;
+  if (!p) {
+    tmp->resize(bytes);
+    p = tmp->data();
+  } else if (cap < bytes) {
+    return SAMPLER_ENOSPC;
+  }
   const size_t off_list = sizeof(RowParams) * (size_t)B;
   const size_t off_pen = off_list + list_bytes(B);
   std::memcpy(p, rows.data(), sizeof(RowParams) * rows.size());
@@ -206,8 +221,25 @@ int pack_into(const sampler_host_params* h, std::vector<unsigned char>& out_buf,
   order.insert(order.end(), greedy_rows.begin(), greedy_rows.end());
 #endif
   std::memcpy(p + off_list, order.data(), sizeof(int32_t) * order.size());
-  std::memcpy(p + off_pen, pen.data(), sizeof(PenEntry) * pen.size());
-  std::memcpy(p + off_pen + sizeof(PenEntry) * pen.size(), bias.data(),
+  std::memset(p + off_list + sizeof(int32_t) * order.size(), 0,
+              list_bytes(B) - sizeof(int32_t) * order.size());
+  // penalty entries in row order: raw rows straight from hist_ids, counted
+  // rows from `pen`
+  PenEntry* pe = reinterpret_cast<PenEntry*>(p + off_pen);
+  size_t counted = 0;
+  for (int32_t r = 0; r < B; ++r) {
+    const RowParams& rp = rows[(size_t)r];
+    if (!(rp.flags & ROW_PEN)) continue;
+    if (rp.flags & ROW_PEN_RAW) {
+      const int32_t* ids = h->hist_ids + h->hist_indptr[r];
+      for (int32_t i = 0; i < rp.pen_hi - rp.pen_lo; ++i) pe[rp.pen_lo + i] = PenEntry{ids[i], 1};
+    } else {
+      std::memcpy(pe + rp.pen_lo, pen.data() + counted,
+                  sizeof(PenEntry) * (size_t)(rp.pen_hi - rp.pen_lo));
+      counted += (size_t)(rp.pen_hi - rp.pen_lo);
+    }
+  }
+  std::memcpy(p + off_pen + sizeof(PenEntry) * (size_t)n_pen, bias.data(),
               sizeof(BiasEntry) * bias.size());
 
   std::memset(out, 0, sizeof *out);
@@ -215,7 +247,7 @@ int pack_into(const sampler_host_params* h, std::vector<unsigned char>& out_buf,
   out->V = V;
   out->flags = flags;
   out->max_top_k = ((flags & SAMPLER_FLAG_ALL_GREEDY) || !all_nongreedy_have_k) ? 0 : max_k;
-  out->n_pen = (int64_t)pen.size();
+  out->n_pen = n_pen;
   out->n_bias = (int64_t)bias.size();
   out->bytes = bytes;
   out->n_sampled = (int32_t)sampled.size();
@@ -259,12 +291,10 @@ size_t sampler_params_bytes(int32_t B, int64_t n_hist, int64_t n_bias) {
 
 int sampler_pack_host(const sampler_host_params* h, void* host_buf, size_t bytes,
                       sampler_batch* out) {
-  std::vector<unsigned char> buf;
+  if (!host_buf) return SAMPLER_ENOSPC;
   sampler_batch tmp;
-  const int rc = pack_into(h, buf, &tmp);
+  const int rc = pack_into(h, static_cast<unsigned char*>(host_buf), bytes, nullptr, &tmp);
   if (rc != SAMPLER_OK) return rc;
-  if (!host_buf || bytes < buf.size()) return SAMPLER_ENOSPC;
-  std::memcpy(host_buf, buf.data(), buf.size());
   set_pointers(&tmp, host_buf);
   *out = tmp;
   return SAMPLER_OK;
@@ -272,15 +302,16 @@ int sampler_pack_host(const sampler_host_params* h, void* host_buf, size_t bytes
 
 int sampler_pack_params(const sampler_host_params* h, void* d_buf, size_t d_bytes,
                         void* h_staging, void* stream, sampler_batch* out) {
+  if (!d_buf) return SAMPLER_ENOSPC;
   std::vector<unsigned char> buf;
   sampler_batch tmp;
-  const int rc = pack_into(h, buf, &tmp);
+  // with a staging buffer (>= d_bytes) the block is packed straight into it
+  const int rc = pack_into(h, static_cast<unsigned char*>(h_staging), d_bytes, &buf, &tmp);
   if (rc != SAMPLER_OK) return rc;
-  if (!d_buf || d_bytes < buf.size()) return SAMPLER_ENOSPC;
+  if (d_bytes < tmp.bytes) return SAMPLER_ENOSPC;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (h_staging) {
-    std::memcpy(h_staging, buf.data(), buf.size());
-    if (hipMemcpyAsync(d_buf, h_staging, buf.size(), hipMemcpyHostToDevice, s) != hipSuccess)
+    if (hipMemcpyAsync(d_buf, h_staging, tmp.bytes, hipMemcpyHostToDevice, s) != hipSuccess)
       return SAMPLER_EHIP;
   } else {
     if (hipMemcpyAsync(d_buf, buf.data(), buf.size(), hipMemcpyHostToDevice, s) != hipSuccess)
