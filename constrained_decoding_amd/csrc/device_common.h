@@ -154,19 +154,18 @@ __device__ __forceinline__ void race_consider(Best& b, float z, int32_t t, uint3
 // re-raced in fp64 by the row's finisher.
 constexpr float kRaceEps = 2e-5f;
 
-// -ln(-ln U) in fp32: -ln U by a degree-5 series in d = 1-U when d < 1/16
-// (relative error < 2e-7; U near 1 would lose -ln U to cancellation in a
-// log), by the hardware log otherwise.
+// -ln(-ln U) in fp32, branch-free: E2 = -log2 U by a degree-5 series in
+// d = 1-U when d < 1/16 (relative error < 2e-7; U near 1 would lose -log2 U to
+// cancellation in a log), by the hardware log2 otherwise; then
+// -ln(-ln U) = -ln(E2 ln 2) = -ln 2 log2(E2) - ln ln 2.  Both logs take normal
+// arguments (U >= 2^-24, E2 > 8e-8), where the hardware log2 is within 1 ulp.
 __device__ __forceinline__ float gumbel_fast(uint32_t x) {
-  const uint32_t n = 2u * (x >> 9) + 1u;                  // U = n * 2^-24
-  const float d = (float)((1u << 24) - n) * 0x1p-24f;     // 1 - U, exact
-  float e;
-  if (d < 0.0625f) {
-    e = d * (1.0f + d * (0.5f + d * (0.33333334f + d * (0.25f + d * 0.2f))));
-  } else {
-    e = -__logf((float)n * 0x1p-24f);
-  }
-  return -__logf(e);
+  const float u = fmaf((float)(x >> 9), 0x1p-23f, 0x1p-24f);  // (2 (x>>9) + 1) 2^-24, exact
+  const float d = 1.0f - u;                                   // exact
+  constexpr float L = 1.4426950408889634f;                    // 1 / ln 2
+  const float ser = d * fmaf(d, fmaf(d, fmaf(d, fmaf(d, L / 5, L / 4), L / 3), L / 2), L);
+  const float e2 = d < 0.0625f ? ser : -__builtin_amdgcn_logf(u);
+  return fmaf(-0.6931471805599453f, __builtin_amdgcn_logf(e2), 0.36651292058166435f);
 }
 
 struct Top2 {
@@ -185,15 +184,13 @@ __device__ __forceinline__ Top2 top2_init() {
   return b;
 }
 
+// (branch-free: selects instead of divergent paths)
 __device__ __forceinline__ void top2_add(Top2& b, float k, int32_t t, float z) {
-  if (k > b.k1 || (k == b.k1 && t < b.t1)) {
-    b.k2 = b.k1;
-    b.k1 = k;
-    b.t1 = t;
-    b.z1 = z;
-  } else if (k > b.k2) {
-    b.k2 = k;
-  }
+  const bool gt = (k > b.k1) | ((k == b.k1) & (t < b.t1));  // no short circuit: no branches
+  b.k2 = fmaxf(b.k2, gt ? b.k1 : k);
+  b.k1 = gt ? k : b.k1;
+  b.t1 = gt ? t : b.t1;
+  b.z1 = gt ? z : b.z1;
 }
 
 __device__ __forceinline__ void top2_merge(Top2& a, const Top2& o) {
@@ -213,11 +210,23 @@ __device__ __forceinline__ bool race32_hopeful(const Top2& b, float z, float zma
   return sd >= -19.5f && sd + 16.7f >= b.k2;
 }
 
+// Token t (value z, draw x) enters the race if ok; branch-free.  A token with
+// s_t - m < -19.5 (including z = -inf) never wins and is left out.
+__device__ __forceinline__ void race32_if(Top2& b, bool ok, float z, int32_t t, uint32_t x,
+                                          float zmax, float invT32) {
+  const float sd = (z - zmax) * invT32;
+  const float k = sd + gumbel_fast(x);
+  const bool in2 = ok & (sd >= -19.5f);  // bitwise: no short circuit, no branches
+  const bool gt = in2 & ((k > b.k1) | ((k == b.k1) & (t < b.t1)));
+  b.k2 = fmaxf(b.k2, gt ? b.k1 : (in2 ? k : CDS_NEG_INF));
+  b.k1 = gt ? k : b.k1;
+  b.t1 = gt ? t : b.t1;
+  b.z1 = gt ? z : b.z1;
+}
+
 __device__ __forceinline__ void race32(Top2& b, float z, int32_t t, uint32_t x, float zmax,
                                        float invT32) {
-  const float sd = (z - zmax) * invT32;
-  if (sd < -19.5f || sd + 16.7f < b.k2) return;
-  top2_add(b, sd + gumbel_fast(x), t, z);
+  race32_if(b, true, z, t, x, zmax, invT32);
 }
 
 // ---- histogram bins ------------------------------------------------------------
@@ -585,6 +594,41 @@ __device__ __forceinline__ float wave_kth_largest(float v, int q) {
     } else {
       need -= n1;
       cand &= ~ones;
+    }
+  }
+  return from_okey(prefix);
+}
+
+// q-th largest (1 <= q <= 64 N) of N values per lane, the same walk with one
+// candidate mask per value.
+template <int N>
+__device__ __forceinline__ float wave_kth_largest_n(const float (&v)[N], int q) {
+  uint32_t k[N];
+  unsigned long long c[N];
+#pragma unroll
+  for (int j = 0; j < N; ++j) {
+    k[j] = okey(v[j] + 0.0f);
+    c[j] = ~0ull;
+  }
+  uint32_t prefix = 0u;
+  int need = q;
+#pragma unroll
+  for (int bit = 31; bit >= 0; --bit) {
+    unsigned long long o[N];
+    int n1 = 0;
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      o[j] = __ballot((k[j] >> bit) & 1u) & c[j];
+      n1 += __popcll(o[j]);
+    }
+    if (n1 >= need) {
+#pragma unroll
+      for (int j = 0; j < N; ++j) c[j] = o[j];
+      prefix |= 1u << bit;
+    } else {
+      need -= n1;
+#pragma unroll
+      for (int j = 0; j < N; ++j) c[j] &= ~o[j];
     }
   }
   return from_okey(prefix);

@@ -687,23 +687,202 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
   }
 }
 
-// Radix selects over order keys of values in [lo, hi] start below the leading
-// bytes those keys all share: returns the first digit shift (24, 16, 8, 0, or
-// -8 when all four bytes are shared) and sets prefix / pmask to the shared bytes.
-__device__ __forceinline__ int radix_start(float lo, float hi, uint32_t& prefix, uint32_t& pmask) {
-  const uint32_t kl = okey(lo + 0.0f), kh = okey(hi + 0.0f);
-  const uint32_t diff = kl ^ kh;
-  const int nb = diff ? (int)(__clz(diff) >> 3) : 4;  // shared leading bytes
-  pmask = nb ? (0xFFFFFFFFu << (32 - 8 * nb)) : 0u;
-  if (nb == 4) pmask = 0xFFFFFFFFu;
-  prefix = kl & pmask;
-  return 24 - 8 * nb;
+// Two u64 sums and the range [lo, hi] of a u32 over the block in one exchange
+// (all NT threads; every thread gets the results).  Nothing: lo > hi.
+template <int NT>
+__device__ __forceinline__ void block_sums_range(unsigned long long& s0, unsigned long long& s1,
+                                                 uint32_t& lo, uint32_t& hi, RedScratch<NT>& red) {
+  // (~min, max) as two 32-bit maxima
+  auto mm = [](unsigned long long a, unsigned long long b) {
+    const uint32_t ah = (uint32_t)(a >> 32), bh = (uint32_t)(b >> 32);
+    const uint32_t al = (uint32_t)a, bl = (uint32_t)b;
+    return ((unsigned long long)(ah > bh ? ah : bh) << 32) | (unsigned long long)(al > bl ? al : bl);
+  };
+  auto add = [](unsigned long long a, unsigned long long b) { return a + b; };
+  const unsigned long long pr = wave_allreduce(((unsigned long long)(~lo) << 32) | hi, mm);
+  const unsigned long long t0 = wave_allreduce(s0, add), t1 = wave_allreduce(s1, add);
+  const int w = threadIdx.x >> 6;
+  __syncthreads();
+  if ((threadIdx.x & 63) == 0) {
+    red.u[w] = t0;
+    red.d[w] = __longlong_as_double((long long)t1);
+    red.i[w] = (int32_t)(uint32_t)(pr >> 32);
+    red.f[w] = __uint_as_float((uint32_t)pr);
+  }
+  __syncthreads();
+  unsigned long long r = 0ull;
+  s0 = s1 = 0ull;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) {
+    s0 += red.u[k];
+    s1 += (unsigned long long)__double_as_longlong(red.d[k]);
+    r = mm(r, ((unsigned long long)(uint32_t)red.i[k] << 32) | __float_as_uint(red.f[k]));
+  }
+  lo = ~(uint32_t)(r >> 32);
+  hi = (uint32_t)r;
+}
+
+// LDS of the finisher's selections.
+struct alignas(16) SelShared {
+  unsigned long long hist[2048];  // one radix round: weight per digit
+  unsigned long long cw[64];      // the bin holding the answer, compacted
+  uint32_t ck[64];
+  unsigned long long above;       // weight above the picked digit
+  int32_t pick;
+  int32_t cnt;
+  uint32_t result;
+  uint32_t wt[16];                // block prefix sums (NT <= 1024)
+};
+
+// Weighted selection over the finisher's list ul[0, n): the largest order key
+// v such that base + (sum of wt(e) over entries e with sel(e), wt(e) > 0 and
+// key(e) >= v) reaches `need`.  The caller guarantees that the selected keys
+// lie in [lo, hi] and that their whole weight reaches need - base > 0.  The
+// bits in which lo and hi differ are resolved top-down in radix rounds of up
+// to 11 bits; as soon as the bin holding v has at most 64 entries, they are
+// compacted and wave 0 finishes the select from one entry per lane.  Weights
+// are integers (counts, or fixed-point masses), so sums are exact in any
+// order.  All NT threads call it; all get v.
+template <int NT, typename Sel, typename Wt>
+__device__ __forceinline__ uint32_t list_select(const uint64_t* ul, int n, Sel sel, Wt wt,
+                                                double need, unsigned long long base,
+                                                uint32_t lo, uint32_t hi, SelShared& s) {
+  const int tid = threadIdx.x;
+  if (lo == hi) return lo;
+  int h = 31 - (int)__clz(lo ^ hi);  // the highest differing bit
+  uint32_t pmask = h == 31 ? 0u : ~0u << (h + 1);
+  uint32_t prefix = lo & pmask;
+  while (true) {
+    const int shift = h > 10 ? h - 10 : 0;
+    const uint32_t dmask = (2u << (h - shift)) - 1u;
+    {
+      ulonglong2* h2 = reinterpret_cast<ulonglong2*>(s.hist);
+      for (int i = tid; i < 1024; i += NT) h2[i] = make_ulonglong2(0ull, 0ull);
+    }
+    __syncthreads();
+#pragma unroll 1
+    for (int i = tid; i < n; i += NT) {
+      const unsigned long long e = ul[i];
+      const uint32_t u = (uint32_t)(e >> 32);
+      if ((u & pmask) == prefix && sel(e)) {
+        const unsigned long long w = wt(e);
+        if (w) atomicAdd(&s.hist[(u >> shift) & dmask], w);
+      }
+    }
+    __syncthreads();
+    // wave 0 picks the digit: lane l sums bins 2047-32l down to 2016-32l, the
+    // first lane whose running total reaches need holds the digit's bin
+    if (tid < 64) {
+      const int l = tid;
+      const ulonglong2* hp = reinterpret_cast<const ulonglong2*>(s.hist + 2016 - 32 * l);
+      unsigned long long sum = 0ull;
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const ulonglong2 v = hp[q];
+        sum += v.x + v.y;
+      }
+      const unsigned long long incl = wave_incl_sum(sum);
+      const unsigned long long hit = __ballot((double)(base + incl) >= need);
+      const int f = hit ? __ffsll((long long)hit) - 1 : 63;
+      const unsigned long long ex = readlane_obj(incl - sum, f);
+      const unsigned long long hb = l < 32 ? s.hist[2047 - 32 * f - l] : 0ull;
+      const unsigned long long incl2 = wave_incl_sum(hb);
+      const unsigned long long hit2 = __ballot(l < 32 && (double)(base + ex + incl2) >= need);
+      const int g = hit2 ? __ffsll((long long)hit2) - 1 : 31;
+      if (l == g) {
+        s.pick = 2047 - 32 * f - g;
+        s.above = base + ex + incl2 - hb;
+        s.cnt = 0;
+      }
+    }
+    __syncthreads();
+    prefix |= (uint32_t)s.pick << shift;
+    pmask |= dmask << shift;
+    base = s.above;
+    if (shift == 0) return prefix;  // every bit resolved
+    h = shift - 1;
+    // compact the bin's entries (the count goes on past 64: then another round)
+#pragma unroll 1
+    for (int i = tid; i < n; i += NT) {
+      const unsigned long long e = ul[i];
+      const uint32_t u = (uint32_t)(e >> 32);
+      if ((u & pmask) == prefix && sel(e)) {
+        const unsigned long long w = wt(e);
+        if (w) {
+          const int j = atomicAdd(&s.cnt, 1);
+          if (j < 64) {
+            s.ck[j] = u;
+            s.cw[j] = w;
+          }
+        }
+      }
+    }
+    __syncthreads();
+    const int cnt = s.cnt;
+    if (cnt <= 64) {
+      if (tid < 64) {
+        const bool valid = tid < cnt;
+        const uint32_t uj = valid ? s.ck[tid] : 0u;
+        const unsigned long long wj = valid ? s.cw[tid] : 0ull;
+        unsigned long long cum = base;  // weight at keys >= uj
+#pragma unroll 1
+        for (int i = 0; i < cnt; ++i) {
+          const uint32_t ui = (uint32_t)__builtin_amdgcn_readlane((int)uj, i);
+          const unsigned long long wi = readlane_obj(wj, i);
+          cum += ui >= uj ? wi : 0ull;
+        }
+        uint32_t v = valid && (double)cum >= need ? uj : 0u;
+        v = wave_allreduce(v, [](uint32_t x, uint32_t y) { return x > y ? x : y; });
+        if (tid == 0) s.result = v;
+      }
+      __syncthreads();
+      return s.result;
+    }
+  }
 }
 
 // ---- phase 4: the boundary list --------------------------------------------------
 __device__ __forceinline__ float ukey_z(unsigned long long k) { return from_okey((uint32_t)(k >> 32)); }
 __device__ __forceinline__ int32_t ukey_t(unsigned long long k) {
   return (int32_t)(0xFFFFFFFFu - (uint32_t)k);
+}
+
+// The race over list entries l[0, n) (okey << 32 | ~t), thread tid taking
+// entries tid, tid + NT, ...: a draw only for tokens that can still enter the
+// thread's top two.  draw(t0) gives the four 32-bit draws of tokens t0..t0+3.
+template <int NT, typename Draw>
+__device__ __forceinline__ void race_list(Top2& b, const uint64_t* l, int n, float zmax,
+                                          float invT32, Draw draw) {
+#pragma unroll 1
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const uint64_t e = l[i];
+    const float z = ukey_z(e);
+    if (!race32_hopeful(b, z, zmax, invT32)) continue;
+    const int32_t t = ukey_t(e);
+    const uint4 blk = draw(t & ~3);
+    const int w = t & 3;
+    const uint32_t xw = w == 0 ? blk.x : (w == 1 ? blk.y : (w == 2 ? blk.z : blk.w));
+    race32(b, z, t, xw, zmax, invT32);
+  }
+}
+
+// Exclusive prefix sum of c over the block (thread order) and its total, with
+// one barrier; wt is LDS scratch of NT/64 words.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl(uint32_t c, uint32_t* wt, uint32_t& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_sum(c);
+  if (lane == 63) wt[w] = incl;
+  __syncthreads();
+  uint32_t base = 0u;
+  total = 0u;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) {
+    const uint32_t tk = wt[k];
+    base += k < w ? tk : 0u;
+    total += tk;
+  }
+  return base + incl - c;
 }
 
 // fp64 race over {z >= zfinal} for tokens whose fp32 key reaches k_floor: the
@@ -746,10 +925,20 @@ __device__ __forceinline__ Best exact_rerace(const SampleArgs& a, int r, const P
 // Resolve the boundary list of row r and write its output (all NT threads of
 // the finisher).  The row's list is gathered from the slices' lists into LDS.
 // Returns false when the row must take the exact path.
+#ifdef CDS_TRACE_DETAIL
+#define CDS_TRACE_ROW(k)                                                                        \
+  do {                                                                                          \
+    if (a.trace && threadIdx.x == 0)                                                            \
+      a.trace[(size_t)gridDim.x * 8 + (size_t)r * 8 + (k)] = wall_clock64();                   \
+  } while (0)
+#else
+#define CDS_TRACE_ROW(k) do {} while (0)
+#endif
+
 template <int NT, bool BF16, bool VEC>
 __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Plan& pl,
                                            ExactShared<NT>& sh, uint64_t* ul, int32_t* off,
-                                           RedScratch<NT>& red) {
+                                           SelShared& sel, RedScratch<NT>& red) {
   const int tid = threadIdx.x, P = a.P;
   const RowParams rp = a.rows[r];
   const double Td = (double)rp.temperature;
@@ -757,6 +946,7 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Pla
   Top2 b = top2_init();
   if (tid < 64) {  // P <= 64: one wave
     uint32_t cnt = 0;
+    float lcut = CDS_NEG_INF;  // list mode: the highest slice list cut
     if (tid < P) {
       const SliceBest sb = ld_obj(&a.bests[(int64_t)r * P + tid]);
       b.k1 = sb.k1;
@@ -770,29 +960,38 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Pla
         b.k2 += sh_k;
       }
       cnt = sb.ucnt > (uint32_t)SCAP ? (uint32_t)UCAP + 1u : sb.ucnt;
+      if (pl.list_mode) lcut = __uint_as_float(sb.pad[2]);
     }
+    lcut = wave_allreduce(lcut, [](float u, float v) { return fmaxf(u, v); });
+    if (tid == 0) sh.fshare = lcut;
     const uint32_t incl = wave_incl_sum(cnt);
     off[tid + 1] = (int32_t)min(incl, (uint32_t)UCAP + 1u);
     if (tid == 0) off[0] = 0;
   }
   __syncthreads();
+  CDS_TRACE_ROW(0);
   const int n = off[P];
   if (n > UCAP) return false;
-  // gather the slices' lists into LDS, every load in flight at once
+  // gather the slices' lists into LDS: every load is issued before any result
+  // is stored; element i = tid + k*NT increases with k, so its slice j (with
+  // off[j] <= i < off[j+1]) is found by a forward scan
+  {
+    constexpr int KG = UCAP / NT;
+    unsigned long long v[KG];
+    int j = 0;
 #pragma unroll
-  for (int k = 0; k < UCAP / NT; ++k) {
-    const int i = tid + k * NT;
-    if (i < n) {
-      int lo = 0, hi = P;  // the slice j with off[j] <= i < off[j+1]
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (off[mid] <= i) lo = mid; else hi = mid;
-      }
-      ul[i] = ld_u64(a.ulist + ((int64_t)r * P + lo) * SCAP + (i - off[lo]));
+    for (int k = 0; k < KG; ++k) {
+      const int i = tid + k * NT;
+      while (j + 1 < P && off[j + 1] <= i) ++j;
+      v[k] = i < n ? ld_u64(a.ulist + ((int64_t)r * P + j) * SCAP + (i - off[j])) : 0ull;
     }
+#pragma unroll
+    for (int k = 0; k < KG; ++k)
+      if (tid + k * NT < n) ul[tid + k * NT] = v[k];
   }
   __syncthreads();
 
+  CDS_TRACE_ROW(1);
   // exact top-k value: the k_rank-th largest list value inside [k_lo, k_hi)
   float zc12 = pl.zcut1;
   if (pl.k_rank > 0) {
@@ -801,38 +1000,35 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Pla
       const float z = ukey_z(e);
       return z >= k_lo && z < k_hi;
     };
-    int cnt = 0;
+    unsigned long long cnt = 0ull, none = 0ull;
+    uint32_t klo = 0xFFFFFFFFu, khi = 0u;
 #pragma unroll 1
-    for (int i = tid; i < n; i += NT) cnt += inK(ul[i]) ? 1 : 0;
-    cnt = block_sum_i32<NT>(cnt, red);
+    for (int i = tid; i < n; i += NT) {
+      const unsigned long long e = ul[i];
+      if (inK(e)) {
+        const uint32_t u = (uint32_t)(e >> 32);
+        ++cnt;
+        klo = min(klo, u);
+        khi = max(khi, u);
+      }
+    }
+    block_sums_range<NT>(cnt, none, klo, khi, red);
     // A boundary list short of k_rank contradicts the plan.  A candidate list
     // (list_mode) holds every token of the min-p set when that set has at most
     // k tokens; top-k then cuts nothing.
-    if (cnt < pl.k_rank && !pl.list_mode) return false;
-    if (cnt >= pl.k_rank) {
-      uint32_t prefix, pmask;
-      const int shift0 = radix_start(k_lo, k_hi, prefix, pmask);
-      unsigned long long krem = (unsigned long long)pl.k_rank;
-#pragma unroll 1
-      for (int shift = shift0; shift >= 0; shift -= 8) {
-        if (tid < 256) sh.hist[tid] = 0ull;
-        __syncthreads();
-#pragma unroll 1
-        for (int i = tid; i < n; i += NT) {
-          const unsigned long long e = ul[i];
-          const uint32_t u = (uint32_t)(e >> 32);
-          if (inK(e) && (u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & 255u], 1ull);
-        }
-        __syncthreads();
-        unsigned long long above;
-        const int d = pick_digit<NT>(sh, (double)krem, 0ull, &above);
-        krem -= above;
-        prefix |= (uint32_t)d << shift;
-        pmask |= 255u << shift;
-      }
-      zc12 = fmaxf(zc12, from_okey(prefix));
+    if (cnt < (unsigned long long)pl.k_rank && !pl.list_mode) return false;
+    if (cnt >= (unsigned long long)pl.k_rank) {
+      const uint32_t v = list_select<NT>(
+          ul, n, inK, [](unsigned long long) { return 1ull; }, (double)pl.k_rank, 0ull, klo, khi,
+          sel);
+      zc12 = fmaxf(zc12, from_okey(v));
     }
   }
+  // list mode: the lists hold every token >= their slice's cut, so the set
+  // {z >= zc12} is complete only if zc12 is at or above every cut (always so
+  // when the slices listed their full top-k; truncated lists may miss it)
+  if (pl.list_mode && zc12 < sh.fshare) return false;
+  CDS_TRACE_ROW(2);
   float zfin = zc12;
 
   // exact top-p cut: the largest value v in [a_lo, a_hi) whose cumulative mass
@@ -848,63 +1044,71 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Pla
       return z >= zc ? (unsigned long long)((double)__builtin_amdgcn_exp2f((z - zref) * c32) * kFix)
                      : 0ull;
     };
-    unsigned long long mu = 0, m_in = 0;
+    unsigned long long mu = 0ull, m_in = 0ull;
+    uint32_t plo = 0xFFFFFFFFu, phi = 0u;
 #pragma unroll 1
     for (int i = tid; i < n; i += NT) {
-      const float z = ukey_z(ul[i]);
+      const unsigned long long e = ul[i];
+      const float z = ukey_z(e);
       const unsigned long long w = wfix(z);
       mu += w;
-      if (z >= a_lo) m_in += w;
+      if (z >= a_lo && w) {
+        const uint32_t u = (uint32_t)(e >> 32);
+        m_in += w;
+        plo = min(plo, u);
+        phi = max(phi, u);
+      }
     }
-    mu = block_sum_u64<NT>(mu, red);
-    m_in = block_sum_u64<NT>(m_in, red);
+    block_sums_range<NT>(mu, m_in, plo, phi, red);
     const double M2 = pl.m_sure + pl.m_mid + F * ((double)mu / kFix);
     // the list mass (in fixed units) the cut must reach above the sure region
     const double need = (pl.p * M2 - pl.m_sure) / F * kFix;
     if (!(need > 0.0)) return false;         // the cut lies above the range
     if ((double)m_in < need) return false;   // ... or below it
-    uint32_t prefix, pmask;
-    const int shift0 = radix_start(a_lo, zref, prefix, pmask);
-    unsigned long long base = 0;
+    const uint32_t v = list_select<NT>(
+        ul, n, [=](unsigned long long e) { return ukey_z(e) >= a_lo; },
+        [=](unsigned long long e) { return wfix(ukey_z(e)); }, need, 0ull, plo, phi, sel);
+    zfin = fmaxf(zfin, from_okey(v));
+  }
+
+  CDS_TRACE_ROW(3);
+  // race the list tokens that survive, merge with the slices' top two; the
+  // survivors are first compacted (when they fit), so that a wave draws only
+  // for tokens that race
+  const RaceCtx c = make_race_ctx(rp, pl.zmax);
+  auto draw = [&](int32_t t0) { return race_block(c, (int64_t)t0); };
+  {
+    uint32_t cs = 0u;
 #pragma unroll 1
-    for (int shift = shift0; shift >= 0; shift -= 8) {
-      if (tid < 256) sh.hist[tid] = 0ull;
-      __syncthreads();
+    for (int i = tid; i < n; i += NT) cs += ukey_z(ul[i]) >= zfin ? 1u : 0u;
+    uint32_t ns;
+    uint32_t pos = block_excl<NT>(cs, sel.wt, ns);
+    if (ns <= 2048u) {
+      uint64_t* dense = reinterpret_cast<uint64_t*>(sel.hist);
 #pragma unroll 1
       for (int i = tid; i < n; i += NT) {
         const unsigned long long e = ul[i];
-        const uint32_t u = (uint32_t)(e >> 32);
-        const float z = ukey_z(e);
-        if (z >= a_lo && (u & pmask) == prefix) {
-          const unsigned long long w = wfix(z);
-          if (w) atomicAdd(&sh.hist[(u >> shift) & 255u], w);
-        }
+        if (ukey_z(e) >= zfin) dense[pos++] = e;
       }
       __syncthreads();
-      unsigned long long above;
-      const int d = pick_digit<NT>(sh, need, base, &above);
-      base = above;
-      prefix |= (uint32_t)d << shift;
-      pmask |= 255u << shift;
-    }
-    zfin = fmaxf(zfin, from_okey(prefix));
-  }
-
-  // race the list tokens that survive, merge with the slices' top two
-  const RaceCtx c = make_race_ctx(rp, pl.zmax);
+      race_list<NT>(b, dense, (int)ns, c.zmax, c.invT32, draw);
+    } else {
 #pragma unroll 1
-  for (int i = tid; i < n; i += NT) {
-    const unsigned long long e = ul[i];
-    const float z = ukey_z(e);
-    if (!(z >= zfin)) continue;
-    const int32_t t = ukey_t(e);
-    if (!race32_hopeful(b, z, c.zmax, c.invT32)) continue;
-    const uint4 blk = race_block(c, (int64_t)(t & ~3));
-    const int w = t & 3;
-    const uint32_t xw = w == 0 ? blk.x : (w == 1 ? blk.y : (w == 2 ? blk.z : blk.w));
-    race32(b, z, t, xw, c.zmax, c.invT32);
+      for (int i = tid; i < n; i += NT) {
+        const unsigned long long e = ul[i];
+        const float z = ukey_z(e);
+        if (!(z >= zfin)) continue;
+        const int32_t t = ukey_t(e);
+        if (!race32_hopeful(b, z, c.zmax, c.invT32)) continue;
+        const uint4 blk = draw(t & ~3);
+        const int w = t & 3;
+        const uint32_t xw = w == 0 ? blk.x : (w == 1 ? blk.y : (w == 2 ? blk.z : blk.w));
+        race32(b, z, t, xw, c.zmax, c.invT32);
+      }
+    }
   }
   block_top2<NT>(b, red);
+  CDS_TRACE_ROW(4);
   if (b.t1 == INT_MAX) return false;
   if (b.k1 - b.k2 > 2.0f * kRaceEps) {
     if (tid == 0) {
@@ -939,6 +1143,7 @@ union FusedLds {
     ExactShared<NT> ex;
     uint64_t list[UCAP];
     int32_t off[kMaxSlices + 1];
+    SelShared select;
   } fin;
   struct {
     uint32_t wt[NT / 64];  // per-wave token counts (list_tokens)
@@ -950,15 +1155,17 @@ __device__ __forceinline__ int row_class(const RowParams& rp, int P) {
   return (int)row_class_of(rp.flags, rp.top_k, P);
 }
 
-// Lists the slice's tokens whose value passes keep() in the slice's global
-// list (up to SCAP entries, okey(v) << 32 | ~t, in thread-major order): each
-// thread counts its tokens, a wave prefix sum and one workgroup barrier give
-// every thread its position, then the tokens are stored directly.  Returns the
-// number of tokens that passed (> SCAP: the list overflowed).  wt is LDS
-// scratch of NT/64 words; all NT threads must call it.
-template <int NT, int E4, typename Keep>
+// Lists the slice's tokens whose value passes keep() (okey(v) << 32 | ~t, in
+// thread-major order, up to cap entries): each thread counts its tokens, a
+// wave prefix sum and one workgroup barrier give every thread its position,
+// then the tokens are stored directly -- to the slice's global list, or, with
+// LDS, to workgroup memory.  Returns the number of tokens that passed (> cap:
+// the list overflowed).  wt is LDS scratch of NT/64 words; all NT threads must
+// call it.
+template <int NT, int E4, bool LDS = false, typename Keep>
 __device__ __forceinline__ uint32_t list_tokens(const float (&x)[E4][4], int32_t tbase,
-                                                uint64_t* list, uint32_t* wt, Keep keep) {
+                                                uint64_t* list, uint32_t cap, uint32_t* wt,
+                                                Keep keep) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint32_t c = 0u;
 #pragma unroll
@@ -982,9 +1189,12 @@ __device__ __forceinline__ uint32_t list_tokens(const float (&x)[E4][4], int32_t
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (keep(x[i][q])) {
-          if (pos < (uint32_t)SCAP)
-            st_u64(list + pos, ((uint64_t)okey(x[i][q] + 0.0f) << 32) |
-                                   (uint64_t)(0xFFFFFFFFu - (uint32_t)(tbase + 4 * NT * i + q)));
+          const uint64_t e = ((uint64_t)okey(x[i][q] + 0.0f) << 32) |
+                             (uint64_t)(0xFFFFFFFFu - (uint32_t)(tbase + 4 * NT * i + q));
+          if (pos < cap) {
+            if (LDS) list[pos] = e;
+            else st_u64(list + pos, e);
+          }
           ++pos;
         }
   }
@@ -1054,7 +1264,7 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
   // and for top-k rows the minimum of the thread maxima; then the lowest index
   // holding the max
   const bool topk_list = cls == CLS_LIST && (rp.flags & ROW_TOPK);
-  const int kq = topk_list ? rp.top_k : 0;  // <= NT for LIST rows
+  const int kq = topk_list ? list_q(rp.top_k, P) : 0;  // <= 4 * NT for LIST rows
   const float cexp =
       cls == CLS_HOLD ? 0.0f : (greedy ? 1.0f : (float)(1.0 / (double)rp.temperature)) * kLog2e;
   SliceStat st;
@@ -1068,10 +1278,25 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
     for (int i = 0; i < E4; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) st.m = fmaxf(st.m, x[i][q]);
-    // top-k rows (k <= NT): each wave's ceil(k/W)-th largest lane maximum
-    // (W waves); every wave has that many tokens at or above its own value, so
-    // at least k tokens of the slice lie at or above the minimum over waves
-    if (topk_list) st.lb = wave_kth_largest(st.m, (kq + NT / 64 - 1) / (NT / 64));
+    // top-k rows (q = list_q <= 4 NT): each wave's ceil(q/W)-th largest of the
+    // lanes' maxima (of the whole lane, or of four groups of its chunks when
+    // one value per lane is not enough; W waves).  Every wave has that many tokens
+    // at or above its own value, so at least q tokens of the slice lie at or
+    // above the minimum over waves.
+    if (topk_list) {
+      const int qw = (kq + NT / 64 - 1) / (NT / 64);
+      if (qw <= 64) {
+        st.lb = wave_kth_largest(st.m, qw);
+      } else {
+        // the maxima of four groups of the lane's chunks: four distinct tokens
+        float gm[4] = {CDS_NEG_INF, CDS_NEG_INF, CDS_NEG_INF, CDS_NEG_INF};
+#pragma unroll
+        for (int i = 0; i < E4; ++i)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) gm[(i * 4) / E4] = fmaxf(gm[(i * 4) / E4], x[i][q]);
+        st.lb = wave_kth_largest_n<4>(gm, qw);
+      }
+    }
     if (cexp != 0.0f && st.m != CDS_NEG_INF) {
       // exp2(x*c - max*c): one FMA per token; a NaN or +inf token makes the
       // sum NaN (or the max +inf), which flags the slice
@@ -1172,7 +1397,7 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
         const uint32_t xs[4] = {blk.x, blk.y, blk.z, blk.w};
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (x[i][q] != CDS_NEG_INF) race32(b, x[i][q], t0 + q, xs[q], zm, invT32);
+          race32_if(b, x[i][q] != CDS_NEG_INF, x[i][q], t0 + q, xs[q], zm, invT32);
       }
     }
     block_top2<NT>(b, red);
@@ -1185,7 +1410,7 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
       sb.ucnt = 0u;
       sb.pad[0] = 1u;
       sb.pad[1] = __float_as_uint(zm);
-      sb.pad[2] = 0u;
+      sb.pad[2] = __float_as_uint(CDS_NEG_INF);  // no list
       st_obj(&a.bests[slot], sb);
     }
   } else if (cls == CLS_LIST && zm != CDS_NEG_INF && !nonfin) {
@@ -1200,7 +1425,7 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
       cut = fmaxf(cut, bm);
     }
     const float cutv = sgpr_f(cut);
-    const uint32_t nst = list_tokens<NT, E4>(x, tbase, a.ulist + slot * SCAP, sh.sel.wt,
+    const uint32_t nst = list_tokens<NT, E4>(x, tbase, a.ulist + slot * SCAP, (uint32_t)SCAP, sh.sel.wt,
                                              [&](float v) { return v >= cutv && v != CDS_NEG_INF; });
     if (tid == 0) {
       SliceBest sb;
@@ -1209,7 +1434,8 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
       sb.z1 = CDS_NEG_INF;
       sb.k2 = CDS_NEG_INF;
       sb.ucnt = nst;
-      sb.pad[0] = sb.pad[1] = sb.pad[2] = 0u;
+      sb.pad[0] = sb.pad[1] = 0u;
+      sb.pad[2] = __float_as_uint(cutv);  // the list holds every token >= this
       st_obj(&a.bests[slot], sb);
     }
   } else if ((cls == CLS_RACE || cls == CLS_LIST) && tid == 0) {
@@ -1220,7 +1446,8 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
     sb.z1 = CDS_NEG_INF;
     sb.k2 = CDS_NEG_INF;
     sb.ucnt = 0u;
-    sb.pad[0] = sb.pad[1] = sb.pad[2] = 0u;
+    sb.pad[0] = sb.pad[1] = 0u;
+    sb.pad[2] = __float_as_uint(CDS_NEG_INF);  // lists nothing, holds nothing
     st_obj(&a.bests[slot], sb);
   }
 
@@ -1282,7 +1509,7 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
       pl.a_lo = -FLT_MAX;
       pl.a_hi = pl.zmax;   // masses exp((z - zmax)/T) <= 1
     }
-    if (!finish_row<NT, BF16, VEC>(a, r, pl, sh.fin.ex, sh.fin.list, sh.fin.off, red)) {
+    if (!finish_row<NT, BF16, VEC>(a, r, pl, sh.fin.ex, sh.fin.list, sh.fin.off, sh.fin.select, red)) {
       __syncthreads();
       row_exact<NT, BF16, VEC>(a, r, sh.fin.ex);
       if (tid == 0) a.plans[r].path = PATH_EXACT;
@@ -1322,29 +1549,41 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
     const float k_lo = sgpr_f(s_plan->k_lo), k_hi = sgpr_f(s_plan->k_hi);
     const bool has_u = a_lo < a_hi || k_lo < k_hi;
     Top2 b = top2_init();
-    // the race over the sure tokens
+    // the race over the sure tokens: staged densely in LDS when they fit, so
+    // that a wave draws only for tokens that race (not for every block in
+    // which one of its lanes has one); else straight from registers
+    uint64_t* stage = sh.fin.list;
+    const uint32_t nsure = list_tokens<NT, E4, true>(x, tbase, stage, (uint32_t)UCAP, sh.sel.wt,
+                                                     [&](float v) { return v >= zs; });
+    __syncthreads();
+    if (nsure <= (uint32_t)UCAP) {
+      race_list<NT>(b, stage, (int)nsure, zmax, invT32, [&](int32_t t0) {
+        return philox4x32_10(make_uint4((uint32_t)t0 >> 2, off_lo, off_hi, 0u), k0, k1);
+      });
+    } else {
 #pragma unroll
-    for (int i = 0; i < E4; ++i) {
-      int32_t tb = tbase;
-      asm volatile("" : "+v"(tb));
-      const int32_t t0 = tb + 4 * NT * i;
-      bool need = false;
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        need |= x[i][q] >= zs && race32_hopeful(b, x[i][q], zmax, invT32);
-      if (need) {
-        const uint4 blk =
-            philox4x32_10(make_uint4((uint32_t)t0 >> 2, off_lo, off_hi, 0u), k0, k1);
-        const uint32_t xs[4] = {blk.x, blk.y, blk.z, blk.w};
+      for (int i = 0; i < E4; ++i) {
+        int32_t tb = tbase;
+        asm volatile("" : "+v"(tb));
+        const int32_t t0 = tb + 4 * NT * i;
+        bool need = false;
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          if (x[i][q] >= zs) race32(b, x[i][q], t0 + q, xs[q], zmax, invT32);
+          need |= x[i][q] >= zs && race32_hopeful(b, x[i][q], zmax, invT32);
+        if (need) {
+          const uint4 blk =
+              philox4x32_10(make_uint4((uint32_t)t0 >> 2, off_lo, off_hi, 0u), k0, k1);
+          const uint32_t xs[4] = {blk.x, blk.y, blk.z, blk.w};
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            race32_if(b, x[i][q] >= zs, x[i][q], t0 + q, xs[q], zmax, invT32);
+        }
       }
     }
     // the boundary-bin tokens, listed
     uint32_t nst = 0u;
     if (has_u)
-      nst = list_tokens<NT, E4>(x, tbase, a.ulist + slot * SCAP, sh.sel.wt, [&](float v) {
+      nst = list_tokens<NT, E4>(x, tbase, a.ulist + slot * SCAP, (uint32_t)SCAP, sh.sel.wt, [&](float v) {
         return is_boundary(v, zs, zc1, a_lo, a_hi, k_lo, k_hi);
       });
     block_top2<NT>(b, red);
@@ -1379,7 +1618,7 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
   const Plan pl = *s_plan;
   if (failed || pl.mode == PLAN_SLOW ||
       (pl.mode == PLAN_FAST &&
-       !finish_row<NT, BF16, VEC>(a, r, pl, sh.fin.ex, sh.fin.list, sh.fin.off, red))) {
+       !finish_row<NT, BF16, VEC>(a, r, pl, sh.fin.ex, sh.fin.list, sh.fin.off, sh.fin.select, red))) {
     __syncthreads();
     row_exact<NT, BF16, VEC>(a, r, sh.fin.ex);
     if (tid == 0) a.plans[r].path = PATH_EXACT;

@@ -78,18 +78,25 @@ constexpr int kMaxRows = 65535;
 enum RowClass : uint32_t {
   CLS_GREEDY = 0,  // argmax: the planner answers from the slice summaries
   CLS_RACE = 1,    // no cut: each slice races all its tokens
-  CLS_LIST = 2,    // top-k with k*P <= UCAP/2 and k <= kScanThreads, or min-p
-                   // without top-k: each
+  CLS_LIST = 2,    // top-k whose lists fit (list_q), or min-p without top-k:
+                   // each
                    // slice lists a superset of its candidates; the planner
                    // resolves the row from the lists
   CLS_HOLD = 3,    // top-p as the only cut, or a larger top-k: the slices wait
                    // for the row's plan (histogram cuts)
 };
 
+// Tokens a slice of a top-k row lists: its own top-q, q = min(k, ceil(2 k/P)
+// + 64), enough for its share of the row's top-k unless that share is far
+// above the average k/P (the row's finisher checks, and falls back).
 // (constexpr: callable from host and device code alike)
+constexpr int32_t list_q(int32_t top_k, int32_t P) {
+  return top_k < (2 * top_k + P - 1) / P + 64 ? top_k : (2 * top_k + P - 1) / P + 64;
+}
 constexpr RowClass row_class_of(uint32_t flags, int32_t top_k, int32_t P) {
   return (flags & ROW_GREEDY)  ? CLS_GREEDY
-         : (flags & ROW_TOPK)  ? ((int64_t)top_k * P <= UCAP / 2 && top_k <= kScanThreads
+         : (flags & ROW_TOPK)  ? ((int64_t)list_q(top_k, P) * P <= UCAP &&
+                                          list_q(top_k, P) <= 4 * kScanThreads
                                       ? CLS_LIST : CLS_HOLD)
          : (flags & ROW_MINP)  ? CLS_LIST
          : (flags & ROW_TOPP)  ? CLS_HOLD

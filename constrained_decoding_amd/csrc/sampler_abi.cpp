@@ -30,6 +30,13 @@ std::atomic<void*> g_ev_stop{nullptr};
 
 inline bool finite_f(float x) { return std::isfinite(x); }
 
+#ifndef CDS_RANK_HOLD
+#define CDS_RANK_HOLD 0
+#endif
+#ifndef CDS_RANK_LONG
+#define CDS_RANK_LONG 1
+#endif
+
 // Device parameter block: RowParams[B] | int32 row order [B] (the dispatch order
 // of sampler_sample; padded to 16 bytes) | PenEntry[n_pen] | BiasEntry[n_bias].
 size_t list_bytes(int32_t B) { return ((size_t)B * sizeof(int32_t) + 15) / 16 * 16; }
@@ -199,27 +206,25 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   const size_t off_list = sizeof(RowParams) * (size_t)B;
   const size_t off_pen = off_list + list_bytes(B);
   std::memcpy(p, rows.data(), sizeof(RowParams) * rows.size());
-  // dispatch order: rows whose slices wait for the row's plan first, then the
-  // other sampled rows, then the greedy rows
+  // dispatch order: the rows whose last slice has the longest way to go
+  // first -- rows whose slices wait for the row's plan, then top-k rows with
+  // long candidate lists -- then the other sampled rows, then the greedy rows
   std::vector<int32_t> order;
   order.reserve((size_t)B);
   const int P = choose_slices(V);
-  auto holds = [&](int32_t r) {
-    return row_class_of(rows[(size_t)r].flags, rows[(size_t)r].top_k, P) == CLS_HOLD;
+  auto rank = [&](int32_t r) {
+    const RowParams& q = rows[(size_t)r];
+    const RowClass c = row_class_of(q.flags, q.top_k, P);
+    if (c == CLS_HOLD) return CDS_RANK_HOLD;
+    if (c == CLS_LIST && (q.flags & ROW_TOPK) && !(q.flags & ROW_MINP) &&
+        (int64_t)list_q(q.top_k, P) * P > 1024)
+      return CDS_RANK_LONG;
+    return 2;
   };
-#ifdef CDS_HOLD_LAST
-  for (int32_t r : sampled)
-    if (!holds(r)) order.push_back(r);
+  for (int k = 0; k < 3; ++k)
+    for (int32_t r : sampled)
+      if (rank(r) == k) order.push_back(r);
   order.insert(order.end(), greedy_rows.begin(), greedy_rows.end());
-  for (int32_t r : sampled)
-    if (holds(r)) order.push_back(r);
-#else
-  for (int32_t r : sampled)
-    if (holds(r)) order.push_back(r);
-  for (int32_t r : sampled)
-    if (!holds(r)) order.push_back(r);
-  order.insert(order.end(), greedy_rows.begin(), greedy_rows.end());
-#endif
   std::memcpy(p + off_list, order.data(), sizeof(int32_t) * order.size());
   std::memset(p + off_list + sizeof(int32_t) * order.size(), 0,
               list_bytes(B) - sizeof(int32_t) * order.size());
