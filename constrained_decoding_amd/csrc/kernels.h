@@ -12,6 +12,7 @@ namespace cds {
 struct SampleArgs {
   const RowParams* rows;
   const int32_t* order;  // dispatch order of the B rows (sampler_batch.d_sampled)
+  const RowParams* rows_ord;  // rows[order[g]] at g: the parameters in dispatch order
   const void* logits;
   int64_t ld;
   int32_t B, V;

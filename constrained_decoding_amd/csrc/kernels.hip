@@ -469,6 +469,28 @@ struct PlanShared {
   double m, log_z, tlo, thi;
 };
 
+// Per-row phase marks (wall clock) in a.trace after the workgroup words.
+#ifdef CDS_TRACE_DETAIL
+#define CDS_TRACE_ROW(k)                                                                        \
+  do {                                                                                          \
+    if (a.trace && threadIdx.x == 0)                                                            \
+      a.trace[(size_t)gridDim.x * 8 + (size_t)r * 8 + (k)] = wall_clock64();                   \
+  } while (0)
+#else
+#define CDS_TRACE_ROW(k) do {} while (0)
+#endif
+// Per-workgroup sub-phase marks after the per-row marks (detail traces only).
+#ifdef CDS_TRACE_DETAIL
+#define CDS_TRACE_SUB(k)                                                                        \
+  do {                                                                                          \
+    if (a.trace && threadIdx.x == 0)                                                            \
+      a.trace[(size_t)gridDim.x * 8 + (size_t)a.B * 8 + (size_t)blockIdx.x * 8 + (k)] =         \
+          wall_clock64();                                                                       \
+  } while (0)
+#else
+#define CDS_TRACE_SUB(k) do {} while (0)
+#endif
+
 // Merge the slice summaries of row r into its plan (all NT threads).  Writes
 // the output of rows that end here (greedy, no finite token, non-finite
 // token) and the plan to a.plans[r] and to *out (LDS).
@@ -480,6 +502,28 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
   const bool greedy = (rp.flags & ROW_GREEDY) != 0;
   const bool topk = (rp.flags & ROW_TOPK) != 0, topp = (rp.flags & ROW_TOPP) != 0;
   const double Td = (double)rp.temperature;
+  // HOLD rows: the first slices' histograms are loaded in the slices' own bin
+  // frames right away, alongside the heads (the row frame needs the heads)
+  constexpr int BPT = (NBINS + NT - 1) / NT;  // bins per thread and slice
+  constexpr int JC = 5;                        // slices per round of loads
+  const unsigned long long* gh = a.hist + (int64_t)r * P * NBINS;
+  unsigned long long hv[JC][BPT];
+  auto load_hist = [&](int j0) {
+#pragma unroll
+    for (int jj = 0; jj < JC; ++jj)
+#pragma unroll
+      for (int k = 0; k < BPT; ++k) {
+        const int sb = tid + k * NT;
+        hv[jj][k] = (j0 + jj < P && sb < NBINS) ? ld_u64(gh + (int64_t)(j0 + jj) * NBINS + sb) : 0ull;
+      }
+  };
+  if (hist) {
+    load_hist(0);
+    for (int b = tid; b < NBINS; b += NT) {
+      ps.cumc[b] = 0u;
+      ps.md[b] = 0.0;  // as u64 mass sums first
+    }
+  }
   // merge the slice heads: wave 0, lane j holds slice j (P <= 64)
   if (tid < 64) {
     float zm = CDS_NEG_INF;
@@ -567,56 +611,42 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
     return;
   }
 
-  // merge the slices' histograms: row bin = slice bin + (row kmax - slice kmax)
+  CDS_TRACE_ROW(5);
+  // merge the slices' histograms: slice j's bin sb is row bin
+  // sb + (row kmax - kmax_j); counts and fixed-point masses are summed into LDS
+  // (integer atomics: exact in any order)
   const BinGeom g = bin_geom(rp.temperature);
   const float kmax = floorf(ps.zmax * g.inv_delta);
-  // thread tid owns row bins tid, tid + NT, ...; slice j's bin sb lands in row
-  // bin sb + (kmax - kmax_j).  Every load is issued before any is used.
-  {
-    constexpr int BPT = (NBINS + NT - 1) / NT;  // row bins per thread
-    const unsigned long long* gh = a.hist + (int64_t)r * P * NBINS;
-    uint32_t cnt[BPT];
-    unsigned long long mas[BPT];
+  unsigned long long* mas = reinterpret_cast<unsigned long long*>(ps.md);
+  for (int j0 = 0; j0 < P; j0 += JC) {
+    if (j0) load_hist(j0);
 #pragma unroll
-    for (int k = 0; k < BPT; ++k) {
-      cnt[k] = 0u;
-      mas[k] = 0ull;
-    }
-#pragma unroll 1
-    for (int j0 = 0; j0 < P; j0 += 8) {
-      unsigned long long v[8][BPT];
+    for (int jj = 0; jj < JC; ++jj) {
+      const int j = j0 + jj;
+      if (j >= P || ps.head[j].zmax == CDS_NEG_INF) continue;
+      const int shift = (int)(kmax - ps.head[j].kmax);
 #pragma unroll
-      for (int jj = 0; jj < 8; ++jj) {
-        const int j = j0 + jj;
-        const bool live = j < P && ps.head[j < P ? j : 0].zmax != CDS_NEG_INF;
-        const int shift = live ? (int)(kmax - ps.head[j].kmax) : NBINS;
-#pragma unroll
-        for (int k = 0; k < BPT; ++k) {
-          const int sb = tid + k * NT - shift;
-          v[jj][k] = (live && sb >= 0 && sb < NBINS) ? ld_u64(gh + (int64_t)j * NBINS + sb) : 0ull;
+      for (int k = 0; k < BPT; ++k) {
+        const unsigned long long v = hv[jj][k];
+        const int rb = tid + k * NT + shift;
+        if (v && rb < NBINS) {
+          atomicAdd(&ps.cumc[rb], (uint32_t)(v >> kCountShift));
+          atomicAdd(&mas[rb], v & ((1ull << kCountShift) - 1ull));
         }
-      }
-#pragma unroll
-      for (int jj = 0; jj < 8; ++jj)
-#pragma unroll
-        for (int k = 0; k < BPT; ++k) {
-          cnt[k] += (uint32_t)(v[jj][k] >> kCountShift);
-          mas[k] += v[jj][k] & ((1ull << kCountShift) - 1ull);
-        }
-    }
-    const double m = ps.m;
-#pragma unroll
-    for (int k = 0; k < BPT; ++k) {
-      const int b = tid + k * NT;
-      if (b < NBINS) {
-        ps.cumc[b] = cnt[k];
-        // bin b spans [(kmax-b)*delta, (kmax-b+1)*delta); masses are relative to its top
-        const double top = ((double)kmax + 1.0 - (double)b) * (double)g.delta;
-        ps.md[b] = (double)mas[k] * 0x1p-31 * exp(top / Td - m);
       }
     }
   }
   __syncthreads();
+  {
+    const double m = ps.m;
+    for (int b = tid; b < NBINS; b += NT) {
+      // bin b spans [(kmax-b)*delta, (kmax-b+1)*delta); masses are relative to its top
+      const double top = ((double)kmax + 1.0 - (double)b) * (double)g.delta;
+      ps.md[b] = (double)mas[b] * 0x1p-31 * exp(top / Td - m);
+    }
+  }
+  __syncthreads();
+  CDS_TRACE_ROW(6);
   // cumulative counts and masses from the top, both by wave 0
   constexpr int KB = (NBINS + 63) / 64;
   wave0_scan_inplace<KB>(ps.cumc, NBINS);
@@ -682,6 +712,7 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
     const int end = inK >= 0 ? inK - 1 : NBINS - 1;
     pl.m_mid = (topp && end > rb3_hi) ? ps.md[end] - ps.md[rb3_hi] : 0.0;
     pl.log_z = ps.log_z;
+    CDS_TRACE_ROW(7);
     st_obj(&a.plans[r], pl);
     *out = pl;
   }
@@ -847,18 +878,19 @@ __device__ __forceinline__ int32_t ukey_t(unsigned long long k) {
   return (int32_t)(0xFFFFFFFFu - (uint32_t)k);
 }
 
-// The race over list entries l[0, n) (okey << 32 | ~t), thread tid taking
-// entries tid, tid + NT, ...: a draw only for tokens that can still enter the
-// thread's top two.  draw(t0) gives the four 32-bit draws of tokens t0..t0+3.
-template <int NT, typename Draw>
-__device__ __forceinline__ void race_list(Top2& b, const uint64_t* l, int n, float zmax,
-                                          float invT32, Draw draw) {
+// The race over n listed tokens (get(i, z, t) reads entry i), thread tid
+// taking entries tid, tid + NT, ...: a draw only for tokens that can still
+// enter the thread's top two.  draw(t0) gives the four 32-bit draws of tokens
+// t0..t0+3.
+template <int NT, typename Get, typename Draw>
+__device__ __forceinline__ void race_list(Top2& b, int n, float zmax, float invT32, Get get,
+                                          Draw draw) {
 #pragma unroll 1
   for (int i = threadIdx.x; i < n; i += NT) {
-    const uint64_t e = l[i];
-    const float z = ukey_z(e);
+    float z;
+    int32_t t;
+    get(i, z, t);
     if (!race32_hopeful(b, z, zmax, invT32)) continue;
-    const int32_t t = ukey_t(e);
     const uint4 blk = draw(t & ~3);
     const int w = t & 3;
     const uint32_t xw = w == 0 ? blk.x : (w == 1 ? blk.y : (w == 2 ? blk.z : blk.w));
@@ -925,15 +957,6 @@ __device__ __forceinline__ Best exact_rerace(const SampleArgs& a, int r, const P
 // Resolve the boundary list of row r and write its output (all NT threads of
 // the finisher).  The row's list is gathered from the slices' lists into LDS.
 // Returns false when the row must take the exact path.
-#ifdef CDS_TRACE_DETAIL
-#define CDS_TRACE_ROW(k)                                                                        \
-  do {                                                                                          \
-    if (a.trace && threadIdx.x == 0)                                                            \
-      a.trace[(size_t)gridDim.x * 8 + (size_t)r * 8 + (k)] = wall_clock64();                   \
-  } while (0)
-#else
-#define CDS_TRACE_ROW(k) do {} while (0)
-#endif
 
 template <int NT, bool BF16, bool VEC>
 __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Plan& pl,
@@ -1091,7 +1114,14 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Pla
         if (ukey_z(e) >= zfin) dense[pos++] = e;
       }
       __syncthreads();
-      race_list<NT>(b, dense, (int)ns, c.zmax, c.invT32, draw);
+      race_list<NT>(
+          b, (int)ns, c.zmax, c.invT32,
+          [&](int i, float& z, int32_t& t) {
+            const uint64_t e = dense[i];
+            z = ukey_z(e);
+            t = ukey_t(e);
+          },
+          draw);
     } else {
 #pragma unroll 1
       for (int i = tid; i < n; i += NT) {
@@ -1155,17 +1185,17 @@ __device__ __forceinline__ int row_class(const RowParams& rp, int P) {
   return (int)row_class_of(rp.flags, rp.top_k, P);
 }
 
-// Lists the slice's tokens whose value passes keep() (okey(v) << 32 | ~t, in
-// thread-major order, up to cap entries): each thread counts its tokens, a
-// wave prefix sum and one workgroup barrier give every thread its position,
-// then the tokens are stored directly -- to the slice's global list, or, with
-// LDS, to workgroup memory.  Returns the number of tokens that passed (> cap:
-// the list overflowed).  wt is LDS scratch of NT/64 words; all NT threads must
+// Lists the slice's tokens whose value passes keep(), in thread-major order:
+// each thread counts its tokens, a wave prefix sum and one workgroup barrier
+// give every thread its position, then emit(pos, v, t) stores token t (value
+// v) at list position pos.  Returns the number of tokens that passed; when it
+// exceeds cap the list is not written at all (every consumer then takes
+// another path).  Blocks of four tokens that no lane of a wave keeps are
+// skipped as a whole.  wt is LDS scratch of NT/64 words; all NT threads must
 // call it.
-template <int NT, int E4, bool LDS = false, typename Keep>
+template <int NT, int E4, typename Keep, typename Emit>
 __device__ __forceinline__ uint32_t list_tokens(const float (&x)[E4][4], int32_t tbase,
-                                                uint64_t* list, uint32_t cap, uint32_t* wt,
-                                                Keep keep) {
+                                                uint32_t cap, uint32_t* wt, Keep keep, Emit emit) {
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   uint32_t c = 0u;
 #pragma unroll
@@ -1182,23 +1212,37 @@ __device__ __forceinline__ uint32_t list_tokens(const float (&x)[E4][4], int32_t
     base += k < w ? tk : 0u;
     total += tk;
   }
-  if (c) {
+  if (total <= cap && c) {
     uint32_t pos = base + incl - c;
 #pragma unroll
-    for (int i = 0; i < E4; ++i)
+    for (int i = 0; i < E4; ++i) {
+      // the predicates are evaluated again here (opaque copies): keeping the
+      // counting pass's E4*4 masks alive across the barrier costs registers
+      float v[4];
+      bool kq[4];
+      bool any = false;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (keep(x[i][q])) {
-          const uint64_t e = ((uint64_t)okey(x[i][q] + 0.0f) << 32) |
-                             (uint64_t)(0xFFFFFFFFu - (uint32_t)(tbase + 4 * NT * i + q));
-          if (pos < cap) {
-            if (LDS) list[pos] = e;
-            else st_u64(list + pos, e);
-          }
-          ++pos;
-        }
+      for (int q = 0; q < 4; ++q) {
+        v[q] = x[i][q];
+        asm volatile("" : "+v"(v[q]));
+        kq[q] = keep(v[q]);
+        any |= kq[q];
+      }
+      if (any) {
+        const int32_t t0 = tbase + 4 * NT * i;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (kq[q]) emit(pos++, v[q], t0 + q);
+      }
+    }
   }
   return total;
+}
+
+// List entry of the row's boundary and candidate lists: okey(v) << 32 | ~t
+// (larger values first, then lower token ids, in unsigned order).
+__device__ __forceinline__ uint64_t ulist_entry(float v, int32_t t) {
+  return ((uint64_t)okey(v + 0.0f) << 32) | (uint64_t)(0xFFFFFFFFu - (uint32_t)t);
 }
 
 // Smallest fp32 value v with exp(v/T - zmax/T) >= min_p (the min-p set
@@ -1241,11 +1285,10 @@ __device__ __forceinline__ float minp_cut_wave(float zmax, double Td, float min_
   } while (0)
 
 template <int NT, int E4, bool BF16, bool VEC, bool STREAM>
-__device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, FusedLds<NT>& sh,
-                                           RedScratch<NT>& red, StatScratch<NT>& sst,
-                                           Plan* s_plan, uint32_t* s_word) {
+__device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const RowParams& rp, int sl,
+                                           FusedLds<NT>& sh, RedScratch<NT>& red,
+                                           StatScratch<NT>& sst, Plan* s_plan, uint32_t* s_word) {
   const int tid = threadIdx.x, P = a.P;
-  const RowParams rp = a.rows[r];
   const int cls = row_class(rp, a.P);
   const bool greedy = cls == CLS_GREEDY;
   const int64_t lo = (int64_t)sl * a.S;
@@ -1425,8 +1468,11 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
       cut = fmaxf(cut, bm);
     }
     const float cutv = sgpr_f(cut);
-    const uint32_t nst = list_tokens<NT, E4>(x, tbase, a.ulist + slot * SCAP, (uint32_t)SCAP, sh.sel.wt,
-                                             [&](float v) { return v >= cutv && v != CDS_NEG_INF; });
+    uint64_t* gl = a.ulist + slot * SCAP;
+    const uint32_t nst = list_tokens<NT, E4>(
+        x, tbase, (uint32_t)SCAP, sh.sel.wt,
+        [&](float v) { return v >= cutv && v != CDS_NEG_INF; },
+        [&](uint32_t pos, float v, int32_t t) { st_u64(gl + pos, ulist_entry(v, t)); });
     if (tid == 0) {
       SliceBest sb;
       sb.k1 = CDS_NEG_INF;
@@ -1552,14 +1598,23 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
     // the race over the sure tokens: staged densely in LDS when they fit, so
     // that a wave draws only for tokens that race (not for every block in
     // which one of its lanes has one); else straight from registers
-    uint64_t* stage = sh.fin.list;
-    const uint32_t nsure = list_tokens<NT, E4, true>(x, tbase, stage, (uint32_t)UCAP, sh.sel.wt,
-                                                     [&](float v) { return v >= zs; });
+    uint2* stage = reinterpret_cast<uint2*>(sh.fin.list);  // (token, value bits)
+    const uint32_t nsure = list_tokens<NT, E4>(
+        x, tbase, (uint32_t)UCAP, sh.sel.wt, [&](float v) { return v >= zs; },
+        [&](uint32_t pos, float v, int32_t t) { stage[pos] = make_uint2((uint32_t)t, __float_as_uint(v)); });
     __syncthreads();
+    CDS_TRACE_SUB(0);
     if (nsure <= (uint32_t)UCAP) {
-      race_list<NT>(b, stage, (int)nsure, zmax, invT32, [&](int32_t t0) {
-        return philox4x32_10(make_uint4((uint32_t)t0 >> 2, off_lo, off_hi, 0u), k0, k1);
-      });
+      race_list<NT>(
+          b, (int)nsure, zmax, invT32,
+          [&](int i, float& z, int32_t& t) {
+            const uint2 e = stage[i];
+            t = (int32_t)e.x;
+            z = __uint_as_float(e.y);
+          },
+          [&](int32_t t0) {
+            return philox4x32_10(make_uint4((uint32_t)t0 >> 2, off_lo, off_hi, 0u), k0, k1);
+          });
     } else {
 #pragma unroll
       for (int i = 0; i < E4; ++i) {
@@ -1580,12 +1635,17 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
         }
       }
     }
+    CDS_TRACE_SUB(1);
     // the boundary-bin tokens, listed
     uint32_t nst = 0u;
-    if (has_u)
-      nst = list_tokens<NT, E4>(x, tbase, a.ulist + slot * SCAP, (uint32_t)SCAP, sh.sel.wt, [&](float v) {
-        return is_boundary(v, zs, zc1, a_lo, a_hi, k_lo, k_hi);
-      });
+    if (has_u) {
+      uint64_t* gl = a.ulist + slot * SCAP;
+      nst = list_tokens<NT, E4>(
+          x, tbase, (uint32_t)SCAP, sh.sel.wt,
+          [&](float v) { return is_boundary(v, zs, zc1, a_lo, a_hi, k_lo, k_hi); },
+          [&](uint32_t pos, float v, int32_t t) { st_u64(gl + pos, ulist_entry(v, t)); });
+    }
+    CDS_TRACE_SUB(2);
     block_top2<NT>(b, red);
     if (tid == 0) {
       SliceBest sb;
@@ -1599,15 +1659,18 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, int sl, F
     }
   }
 
+  CDS_TRACE_SUB(3);
   // the last slice of the row to finish its race resolves the row
   vm_drain();
   __syncthreads();
+  CDS_TRACE_SUB(4);
   if (tid == 0) {
     const uint32_t t = take_ticket(&sy->done);
     if (t == (uint32_t)(P - 1)) st_u64(&sy->done, 0ull);
     s_word[0] = t;
   }
   __syncthreads();
+  CDS_TRACE_SUB(5);
   if (s_word[0] != (uint32_t)(P - 1)) {
     CDS_TRACE(7);
     return;
@@ -1643,16 +1706,19 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CDS_WAVES_PE
   // j % P of the XCD's (j / P)-th row, the ordered row g = (j / P) * kXcds + x.
   // All slices of a row then run on one XCD, next to each other in its
   // dispatch order, and every XCD gets every kXcds-th row of the packed order.
+  CDS_TRACE_SUB(6);
   const unsigned x = blockIdx.x % (unsigned)kXcds, j = blockIdx.x / (unsigned)kXcds;
   const int lr = (int)(j / (unsigned)a.P);
   const int sl = (int)(j - (unsigned)lr * (unsigned)a.P);
   const int grp = lr * kXcds + (int)x;
   if (grp >= a.B) return;
+  // the row index and its parameters: two independent loads
   const int r = a.order[grp];
-  if (a.rows[r].flags & ROW_GREEDY)
-    slice_task<NT, E4, BF16, VEC, true>(a, r, sl, sh, red, sst, &s_plan, s_word);
+  const RowParams rp = a.rows_ord[grp];
+  if (rp.flags & ROW_GREEDY)
+    slice_task<NT, E4, BF16, VEC, true>(a, r, rp, sl, sh, red, sst, &s_plan, s_word);
   else
-    slice_task<NT, E4, BF16, VEC, false>(a, r, sl, sh, red, sst, &s_plan, s_word);
+    slice_task<NT, E4, BF16, VEC, false>(a, r, rp, sl, sh, red, sst, &s_plan, s_word);
 }
 
 // ============================================================================

@@ -30,19 +30,14 @@ std::atomic<void*> g_ev_stop{nullptr};
 
 inline bool finite_f(float x) { return std::isfinite(x); }
 
-#ifndef CDS_RANK_HOLD
-#define CDS_RANK_HOLD 0
-#endif
-#ifndef CDS_RANK_LONG
-#define CDS_RANK_LONG 1
-#endif
-
 // Device parameter block: RowParams[B] | int32 row order [B] (the dispatch order
-// of sampler_sample; padded to 16 bytes) | PenEntry[n_pen] | BiasEntry[n_bias].
+// of sampler_sample; padded to 16 bytes) | RowParams[B] again, in that order
+// (the sampling kernel reads a row's parameters and its index side by side,
+// without a dependent load) | PenEntry[n_pen] | BiasEntry[n_bias].
 size_t list_bytes(int32_t B) { return ((size_t)B * sizeof(int32_t) + 15) / 16 * 16; }
 
 size_t params_bytes_exact(int32_t B, int64_t n_pen, int64_t n_bias) {
-  return sizeof(RowParams) * (size_t)B + list_bytes(B) + sizeof(PenEntry) * (size_t)n_pen +
+  return 2 * sizeof(RowParams) * (size_t)B + list_bytes(B) + sizeof(PenEntry) * (size_t)n_pen +
          sizeof(BiasEntry) * (size_t)n_bias;
 }
 
@@ -204,7 +199,8 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
     return SAMPLER_ENOSPC;
   }
   const size_t off_list = sizeof(RowParams) * (size_t)B;
-  const size_t off_pen = off_list + list_bytes(B);
+  const size_t off_ord = off_list + list_bytes(B);
+  const size_t off_pen = off_ord + sizeof(RowParams) * (size_t)B;
   std::memcpy(p, rows.data(), sizeof(RowParams) * rows.size());
   // dispatch order: the rows whose last slice has the longest way to go
   // first -- rows whose slices wait for the row's plan, then top-k rows with
@@ -215,10 +211,10 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   auto rank = [&](int32_t r) {
     const RowParams& q = rows[(size_t)r];
     const RowClass c = row_class_of(q.flags, q.top_k, P);
-    if (c == CLS_HOLD) return CDS_RANK_HOLD;
+    if (c == CLS_HOLD) return 0;
     if (c == CLS_LIST && (q.flags & ROW_TOPK) && !(q.flags & ROW_MINP) &&
         (int64_t)list_q(q.top_k, P) * P > 1024)
-      return CDS_RANK_LONG;
+      return 1;
     return 2;
   };
   for (int k = 0; k < 3; ++k)
@@ -228,6 +224,8 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   std::memcpy(p + off_list, order.data(), sizeof(int32_t) * order.size());
   std::memset(p + off_list + sizeof(int32_t) * order.size(), 0,
               list_bytes(B) - sizeof(int32_t) * order.size());
+  for (size_t g = 0; g < order.size(); ++g)
+    std::memcpy(p + off_ord + sizeof(RowParams) * g, &rows[(size_t)order[g]], sizeof(RowParams));
   // penalty entries in row order: raw rows straight from hist_ids, counted
   // rows from `pen`
   PenEntry* pe = reinterpret_cast<PenEntry*>(p + off_pen);
@@ -262,7 +260,7 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
 void set_pointers(sampler_batch* out, const void* base) {
   const unsigned char* b = static_cast<const unsigned char*>(base);
   const size_t off_list = sizeof(RowParams) * (size_t)out->B;
-  const size_t off_pen = off_list + list_bytes(out->B);
+  const size_t off_pen = off_list + list_bytes(out->B) + sizeof(RowParams) * (size_t)out->B;
   out->d_rows = b;
   out->d_sampled = b + off_list;
   out->d_pen = b + off_pen;
@@ -383,6 +381,8 @@ int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_
   if (b->n_sampled < 0 || b->n_sampled > B || !b->d_sampled) return SAMPLER_EINVAL;
   a.rows = static_cast<const RowParams*>(b->d_rows);
   a.order = static_cast<const int32_t*>(b->d_sampled);
+  a.rows_ord = reinterpret_cast<const RowParams*>(static_cast<const unsigned char*>(b->d_sampled) +
+                                                  list_bytes(B));
   a.logits = logits;
   a.ld = ld;
   a.B = B;

@@ -145,8 +145,11 @@ typedef struct sampler_batch {
                             n_sampled rows that are not greedy (first those
                             whose cut needs the whole row's histogram: top-p
                             as the only cut, or a top_k above a bound that
-                            depends on V), then the greedy rows; ascending
-                            within each group                              */
+                            depends on V; then top-k rows without min-p whose
+                            candidate lists are long), then the greedy rows;
+                            ascending within each group.  The per-row records
+                            follow it again in this order (after the order
+                            padded to 16 bytes)                             */
 } sampler_batch;
 
 /* Message for a SAMPLER_* return code (static storage). */

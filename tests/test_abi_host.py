@@ -88,7 +88,10 @@ def test_penalty_counts_and_bias_dedup(cds):
     rows = _rowparams(buf, 3)
     assert b.n_sampled == 3
     assert np.frombuffer(buf[64 * 3:64 * 3 + 12].tobytes(), "<i4").tolist() == [0, 1, 2]
-    pen_off = 64 * 3 + 16        # the sampled-row list: room for B int32, 16-byte padded
+    # the row order (room for B int32, 16-byte padded), then the rows again in that order
+    pen_off = 64 * 3 + 16 + 64 * 3
+    np.testing.assert_array_equal(np.frombuffer(buf[64 * 3 + 16:pen_off].tobytes(), np.uint8),
+                                  np.frombuffer(buf[:64 * 3].tobytes(), np.uint8))
     pen = np.frombuffer(buf[pen_off:pen_off + 8 * b.n_pen].tobytes(), "<i4").reshape(-1, 2)
     # rows of up to 4096 history tokens are packed as they come (count 1 each;
     # the transforms kernel merges repeats); row 2 has no active penalty
@@ -164,6 +167,10 @@ def test_sampled_row_list(cds):
     p = np.array([1, 1, 1, 1, 1, 0.9], np.float32)
     buf, b = cds.pack_host(6, 1000, T, top_k=k, top_p=p)
     assert b.n_sampled == 3
-    assert np.frombuffer(buf[64 * 6:64 * 6 + 24].tobytes(), "<i4").tolist() == [5, 1, 4, 0, 2, 3]
+    order = [5, 1, 4, 0, 2, 3]
+    assert np.frombuffer(buf[64 * 6:64 * 6 + 24].tobytes(), "<i4").tolist() == order
+    rows = _rowparams(buf, 6)
+    ordered = np.frombuffer(buf[64 * 6 + 32:64 * 6 + 32 + 64 * 6].tobytes(), rows.dtype)
+    np.testing.assert_array_equal(ordered, rows[order])
     buf, b = cds.pack_host(2, 1000, np.zeros(2, np.float32))
     assert b.n_sampled == 0 and b.flags & cds.FLAG_ALL_GREEDY
