@@ -48,7 +48,7 @@ class Batch(ct.Structure):
         ("B", ct.c_int32), ("V", ct.c_int32), ("flags", ct.c_uint32),
         ("max_top_k", ct.c_int32), ("n_pen", ct.c_int64), ("n_bias", ct.c_int64),
         ("d_rows", ct.c_void_p), ("d_pen", ct.c_void_p), ("d_bias", ct.c_void_p),
-        ("bytes", ct.c_size_t), ("n_sampled", ct.c_int32), ("reserved", ct.c_int32),
+        ("bytes", ct.c_size_t), ("n_sampled", ct.c_int32), ("n_hold", ct.c_int32),
         ("d_sampled", ct.c_void_p),
     ]
 

@@ -505,7 +505,7 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
   // HOLD rows: the first slices' histograms are loaded in the slices' own bin
   // frames right away, alongside the heads (the row frame needs the heads)
   constexpr int BPT = (NBINS + NT - 1) / NT;  // bins per thread and slice
-  constexpr int JC = 5;                        // slices per round of loads
+  constexpr int JC = 10;                       // slices per round of loads
   const unsigned long long* gh = a.hist + (int64_t)r * P * NBINS;
   unsigned long long hv[JC][BPT];
   auto load_hist = [&](int j0) {
@@ -755,7 +755,7 @@ __device__ __forceinline__ void block_sums_range(unsigned long long& s0, unsigne
 
 // LDS of the finisher's selections.
 struct alignas(16) SelShared {
-  unsigned long long hist[2048];  // one radix round: weight per digit
+  unsigned long long hist[512];   // one radix round: weight per digit
   unsigned long long cw[64];      // the bin holding the answer, compacted
   uint32_t ck[64];
   unsigned long long above;       // weight above the picked digit
@@ -770,7 +770,7 @@ struct alignas(16) SelShared {
 // key(e) >= v) reaches `need`.  The caller guarantees that the selected keys
 // lie in [lo, hi] and that their whole weight reaches need - base > 0.  The
 // bits in which lo and hi differ are resolved top-down in radix rounds of up
-// to 11 bits; as soon as the bin holding v has at most 64 entries, they are
+// to 9 bits; as soon as the bin holding v has at most 64 entries, they are
 // compacted and wave 0 finishes the select from one entry per lane.  Weights
 // are integers (counts, or fixed-point masses), so sums are exact in any
 // order.  All NT threads call it; all get v.
@@ -784,11 +784,11 @@ __device__ __forceinline__ uint32_t list_select(const uint64_t* ul, int n, Sel s
   uint32_t pmask = h == 31 ? 0u : ~0u << (h + 1);
   uint32_t prefix = lo & pmask;
   while (true) {
-    const int shift = h > 10 ? h - 10 : 0;
+    const int shift = h > 8 ? h - 8 : 0;
     const uint32_t dmask = (2u << (h - shift)) - 1u;
     {
       ulonglong2* h2 = reinterpret_cast<ulonglong2*>(s.hist);
-      for (int i = tid; i < 1024; i += NT) h2[i] = make_ulonglong2(0ull, 0ull);
+      for (int i = tid; i < 256; i += NT) h2[i] = make_ulonglong2(0ull, 0ull);
     }
     __syncthreads();
 #pragma unroll 1
@@ -801,14 +801,14 @@ __device__ __forceinline__ uint32_t list_select(const uint64_t* ul, int n, Sel s
       }
     }
     __syncthreads();
-    // wave 0 picks the digit: lane l sums bins 2047-32l down to 2016-32l, the
+    // wave 0 picks the digit: lane l sums bins 511-8l down to 504-8l, the
     // first lane whose running total reaches need holds the digit's bin
     if (tid < 64) {
       const int l = tid;
-      const ulonglong2* hp = reinterpret_cast<const ulonglong2*>(s.hist + 2016 - 32 * l);
+      const ulonglong2* hp = reinterpret_cast<const ulonglong2*>(s.hist + 504 - 8 * l);
       unsigned long long sum = 0ull;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
+      for (int q = 0; q < 4; ++q) {
         const ulonglong2 v = hp[q];
         sum += v.x + v.y;
       }
@@ -816,12 +816,12 @@ __device__ __forceinline__ uint32_t list_select(const uint64_t* ul, int n, Sel s
       const unsigned long long hit = __ballot((double)(base + incl) >= need);
       const int f = hit ? __ffsll((long long)hit) - 1 : 63;
       const unsigned long long ex = readlane_obj(incl - sum, f);
-      const unsigned long long hb = l < 32 ? s.hist[2047 - 32 * f - l] : 0ull;
+      const unsigned long long hb = l < 8 ? s.hist[511 - 8 * f - l] : 0ull;
       const unsigned long long incl2 = wave_incl_sum(hb);
-      const unsigned long long hit2 = __ballot(l < 32 && (double)(base + ex + incl2) >= need);
-      const int g = hit2 ? __ffsll((long long)hit2) - 1 : 31;
+      const unsigned long long hit2 = __ballot(l < 8 && (double)(base + ex + incl2) >= need);
+      const int g = hit2 ? __ffsll((long long)hit2) - 1 : 7;
       if (l == g) {
-        s.pick = 2047 - 32 * f - g;
+        s.pick = 511 - 8 * f - g;
         s.above = base + ex + incl2 - hb;
         s.cnt = 0;
       }
@@ -1101,41 +1101,31 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Pla
   const RaceCtx c = make_race_ctx(rp, pl.zmax);
   auto draw = [&](int32_t t0) { return race_block(c, (int64_t)t0); };
   {
+    // the survivors move to the front of the list, in place: every entry is
+    // read into registers before the barrier inside block_excl
+    constexpr int KG = UCAP / NT;
+    unsigned long long e[KG];
     uint32_t cs = 0u;
-#pragma unroll 1
-    for (int i = tid; i < n; i += NT) cs += ukey_z(ul[i]) >= zfin ? 1u : 0u;
+#pragma unroll
+    for (int k = 0; k < KG; ++k) {
+      const int i = tid + k * NT;
+      e[k] = i < n ? ul[i] : 0ull;
+      cs += (i < n && ukey_z(e[k]) >= zfin) ? 1u : 0u;
+    }
     uint32_t ns;
     uint32_t pos = block_excl<NT>(cs, sel.wt, ns);
-    if (ns <= 2048u) {
-      uint64_t* dense = reinterpret_cast<uint64_t*>(sel.hist);
-#pragma unroll 1
-      for (int i = tid; i < n; i += NT) {
-        const unsigned long long e = ul[i];
-        if (ukey_z(e) >= zfin) dense[pos++] = e;
-      }
-      __syncthreads();
-      race_list<NT>(
-          b, (int)ns, c.zmax, c.invT32,
-          [&](int i, float& z, int32_t& t) {
-            const uint64_t e = dense[i];
-            z = ukey_z(e);
-            t = ukey_t(e);
-          },
-          draw);
-    } else {
-#pragma unroll 1
-      for (int i = tid; i < n; i += NT) {
-        const unsigned long long e = ul[i];
-        const float z = ukey_z(e);
-        if (!(z >= zfin)) continue;
-        const int32_t t = ukey_t(e);
-        if (!race32_hopeful(b, z, c.zmax, c.invT32)) continue;
-        const uint4 blk = draw(t & ~3);
-        const int w = t & 3;
-        const uint32_t xw = w == 0 ? blk.x : (w == 1 ? blk.y : (w == 2 ? blk.z : blk.w));
-        race32(b, z, t, xw, c.zmax, c.invT32);
-      }
-    }
+#pragma unroll
+    for (int k = 0; k < KG; ++k)
+      if (tid + k * NT < n && ukey_z(e[k]) >= zfin) ul[pos++] = e[k];
+    __syncthreads();
+    race_list<NT>(
+        b, (int)ns, c.zmax, c.invT32,
+        [&](int i, float& z, int32_t& t) {
+          const uint64_t v = ul[i];
+          z = ukey_z(v);
+          t = ukey_t(v);
+        },
+        draw);
   }
   block_top2<NT>(b, red);
   CDS_TRACE_ROW(4);
@@ -1158,11 +1148,6 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Pla
   return true;
 }
 
-__device__ __forceinline__ bool is_boundary(float v, float zs, float zc1, float a_lo, float a_hi,
-                                            float k_lo, float k_hi) {
-  return v < zs && v >= zc1 && ((v >= a_lo && v < a_hi) || (v >= k_lo && v < k_hi));
-}
-
 constexpr int kHistCopies = 4;
 
 template <int NT>
@@ -1176,7 +1161,7 @@ union FusedLds {
     SelShared select;
   } fin;
   struct {
-    uint32_t wt[NT / 64];  // per-wave token counts (list_tokens)
+    uint32_t wt[2 * NT / 64];  // per-wave token counts (list_tokens, list_tokens2)
   } sel;
 };
 
@@ -1237,6 +1222,66 @@ __device__ __forceinline__ uint32_t list_tokens(const float (&x)[E4][4], int32_t
     }
   }
   return total;
+}
+
+// list_tokens for two disjoint predicates at once: one counting pass, one
+// barrier, one writing pass; returns (number kept by keep1, by keep2).  wt is
+// LDS scratch of 2*NT/64 words.
+template <int NT, int E4, typename K1, typename E1, typename K2, typename E2>
+__device__ __forceinline__ uint2 list_tokens2(const float (&x)[E4][4], int32_t tbase,
+                                              uint32_t cap1, uint32_t cap2, uint32_t* wt,
+                                              K1 keep1, E1 emit1, K2 keep2, E2 emit2) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint32_t c1 = 0u, c2 = 0u;
+#pragma unroll
+  for (int i = 0; i < E4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      c1 += keep1(x[i][q]) ? 1u : 0u;
+      c2 += keep2(x[i][q]) ? 1u : 0u;
+    }
+  const uint32_t incl1 = wave_incl_sum(c1), incl2 = wave_incl_sum(c2);
+  if (lane == 63) {
+    wt[w] = incl1;
+    wt[NT / 64 + w] = incl2;
+  }
+  __syncthreads();
+  uint32_t base1 = 0u, base2 = 0u, n1 = 0u, n2 = 0u;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) {
+    const uint32_t t1 = wt[k], t2 = wt[NT / 64 + k];
+    base1 += k < w ? t1 : 0u;
+    base2 += k < w ? t2 : 0u;
+    n1 += t1;
+    n2 += t2;
+  }
+  const bool w1 = n1 <= cap1 && c1, w2 = n2 <= cap2 && c2;
+  if (w1 || w2) {
+    uint32_t pos1 = base1 + incl1 - c1, pos2 = base2 + incl2 - c2;
+#pragma unroll
+    for (int i = 0; i < E4; ++i) {
+      float v[4];
+      bool k1[4], k2[4];
+      bool any = false;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] = x[i][q];
+        asm volatile("" : "+v"(v[q]));  // evaluated again, see list_tokens
+        k1[q] = w1 && keep1(v[q]);
+        k2[q] = w2 && keep2(v[q]);
+        any |= k1[q] | k2[q];
+      }
+      if (any) {
+        const int32_t t0 = tbase + 4 * NT * i;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (k1[q]) emit1(pos1++, v[q], t0 + q);
+          if (k2[q]) emit2(pos2++, v[q], t0 + q);
+        }
+      }
+    }
+  }
+  return make_uint2(n1, n2);
 }
 
 // List entry of the row's boundary and candidate lists: okey(v) << 32 | ~t
@@ -1564,14 +1609,40 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
     return;
   }
 
-  // ---- HOLD rows: the plan, then the race from registers ----
+  // ---- HOLD rows: the last slice plans the row; the race is a pass-2 task ----
   if (planner) {
     plan_row<NT>(a, r, true, sh.plan, s_plan);
     if (tid == 0) {
       vm_drain();  // the plan (written by this thread) before its flag
       st_u32(&sy->ready, a.gen);
     }
-  } else if (tid == 0) {
+    CDS_TRACE(6);
+  }
+  CDS_TRACE(7);
+}
+
+// Pass 2 of a HOLD row (slice sl): the slice is loaded again (the loads are
+// issued before the wait), the row's plan awaited, then the sure tokens race,
+// the boundary tokens are listed, and the last slice resolves the row.
+template <int NT, int E4, bool BF16, bool VEC>
+__device__ __forceinline__ void hold_race_task(const SampleArgs& a, int r, const RowParams& rp,
+                                               int sl, FusedLds<NT>& sh, RedScratch<NT>& red,
+                                               Plan* s_plan, uint32_t* s_word) {
+  const int tid = threadIdx.x, P = a.P;
+  const int64_t lo = (int64_t)sl * a.S;
+  const int64_t hi = min(lo + a.S, (int64_t)a.V);
+  const int32_t tbase = (int32_t)lo + 4 * tid;  // token of chunk i: tbase + 4*NT*i
+  const RowView rv = row_view<BF16>(a, r);
+  const int64_t slot = (int64_t)r * P + sl;
+  RowSync* sy = &a.sync[r];
+  if (a.trace && tid == 0)
+    a.trace[(size_t)blockIdx.x * 8] = (unsigned long long)r | ((unsigned long long)sl << 20) |
+                                      (4ull << 28);
+  CDS_TRACE(1);
+  float x[E4][4];
+  uint32_t nonfin = 0;
+  load_chunks<NT, E4, BF16, VEC, true, false>(rv, lo, hi, 0, x, nonfin);
+  if (tid == 0) {
     if (gen_wait(&sy->ready, a.gen, a.spin_limit)) {
       *s_plan = ld_obj(&a.plans[r]);
     } else {
@@ -1598,10 +1669,21 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
     // the race over the sure tokens: staged densely in LDS when they fit, so
     // that a wave draws only for tokens that race (not for every block in
     // which one of its lanes has one); else straight from registers
-    uint2* stage = reinterpret_cast<uint2*>(sh.fin.list);  // (token, value bits)
-    const uint32_t nsure = list_tokens<NT, E4>(
-        x, tbase, (uint32_t)UCAP, sh.sel.wt, [&](float v) { return v >= zs; },
-        [&](uint32_t pos, float v, int32_t t) { stage[pos] = make_uint2((uint32_t)t, __float_as_uint(v)); });
+    // One listing pass for both lists: the sure tokens staged in LDS as (token,
+    // value bits), and the boundary-bin tokens to the slice's global list.
+    // Boundary: below zs, at or above zc1, inside [a_lo, a_hi) or [k_lo, k_hi).
+    uint2* stage = reinterpret_cast<uint2*>(sh.fin.list);
+    uint64_t* gl = a.ulist + slot * SCAP;
+    const float lo1 = fmaxf(a_lo, zc1), hi1 = fminf(a_hi, zs);
+    const float lo2 = fmaxf(k_lo, zc1), hi2 = fminf(k_hi, zs);
+    const uint2 nn = list_tokens2<NT, E4>(
+        x, tbase, (uint32_t)UCAP, (uint32_t)SCAP, sh.sel.wt, [&](float v) { return v >= zs; },
+        [&](uint32_t pos, float v, int32_t t) {
+          stage[pos] = make_uint2((uint32_t)t, __float_as_uint(v));
+        },
+        [&](float v) { return ((v >= lo1) & (v < hi1)) | ((v >= lo2) & (v < hi2)); },
+        [&](uint32_t pos, float v, int32_t t) { st_u64(gl + pos, ulist_entry(v, t)); });
+    const uint32_t nsure = nn.x, nst = has_u ? nn.y : 0u;
     __syncthreads();
     CDS_TRACE_SUB(0);
     if (nsure <= (uint32_t)UCAP) {
@@ -1636,16 +1718,6 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
       }
     }
     CDS_TRACE_SUB(1);
-    // the boundary-bin tokens, listed
-    uint32_t nst = 0u;
-    if (has_u) {
-      uint64_t* gl = a.ulist + slot * SCAP;
-      nst = list_tokens<NT, E4>(
-          x, tbase, (uint32_t)SCAP, sh.sel.wt,
-          [&](float v) { return is_boundary(v, zs, zc1, a_lo, a_hi, k_lo, k_hi); },
-          [&](uint32_t pos, float v, int32_t t) { st_u64(gl + pos, ulist_entry(v, t)); });
-    }
-    CDS_TRACE_SUB(2);
     block_top2<NT>(b, red);
     if (tid == 0) {
       SliceBest sb;
@@ -1690,7 +1762,7 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
 }
 
 #ifndef CDS_WAVES_PER_EU
-#define CDS_WAVES_PER_EU 3
+#define CDS_WAVES_PER_EU 4
 #endif
 // CDS_WAVES_PER_EU waves per SIMD (the slice takes 4*E4 vector registers).
 template <int NT, int E4, bool BF16, bool VEC>
@@ -1703,19 +1775,24 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CDS_WAVES_PE
   __shared__ uint32_t s_word[2];
   // Workgroups are dispatched round-robin over the kXcds XCDs.  Block b runs on
   // XCD x = b % kXcds as that XCD's j-th block (j = b / kXcds); it takes slice
-  // j % P of the XCD's (j / P)-th row, the ordered row g = (j / P) * kXcds + x.
-  // All slices of a row then run on one XCD, next to each other in its
-  // dispatch order, and every XCD gets every kXcds-th row of the packed order.
+  // j % P of the XCD's (j / P)-th task, task k = (j / P) * kXcds + x of the
+  // packed task table.  All slices of a task then run on one XCD, next to each
+  // other in its dispatch order; a pass-2 task comes after its row's pass-1
+  // task in every XCD's order, so the pass-1 slices it waits for are running
+  // or done.
   CDS_TRACE_SUB(6);
   const unsigned x = blockIdx.x % (unsigned)kXcds, j = blockIdx.x / (unsigned)kXcds;
   const int lr = (int)(j / (unsigned)a.P);
   const int sl = (int)(j - (unsigned)lr * (unsigned)a.P);
-  const int grp = lr * kXcds + (int)x;
-  if (grp >= a.B) return;
-  // the row index and its parameters: two independent loads
-  const int r = a.order[grp];
-  const RowParams rp = a.rows_ord[grp];
-  if (rp.flags & ROW_GREEDY)
+  const int k = lr * kXcds + (int)x;
+  // the task's row and its parameters: two independent loads
+  const int32_t tr = a.task_row[k];
+  const RowParams rp = a.task_rows[k];
+  if (tr < 0) return;
+  const int r = tr & ~kPass2;
+  if (tr & kPass2)
+    hold_race_task<NT, E4, BF16, VEC>(a, r, rp, sl, sh, red, &s_plan, s_word);
+  else if (rp.flags & ROW_GREEDY)
     slice_task<NT, E4, BF16, VEC, true>(a, r, rp, sl, sh, red, sst, &s_plan, s_word);
   else
     slice_task<NT, E4, BF16, VEC, false>(a, r, rp, sl, sh, red, sst, &s_plan, s_word);
@@ -1768,7 +1845,7 @@ static hipError_t launch_fused(const SampleArgs& a, const KernelEvents* ev, hipS
   if (a.S > kSliceMax) return hipErrorInvalidValue;
   rec(ev, true, s);
   hipLaunchKernelGGL((sample_kernel<kScanThreads, kMaxChunks, BF16, VEC>),
-                     dim3((unsigned)((a.B + kXcds - 1) / kXcds * kXcds) * (unsigned)a.P),
+                     dim3((unsigned)(a.n_groups * kXcds) * (unsigned)a.P),
                      dim3(kScanThreads), 0, s, a);
   rec(ev, false, s);
   return hipGetLastError();

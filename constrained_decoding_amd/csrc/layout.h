@@ -33,6 +33,10 @@ struct alignas(16) RowParams {
 };
 static_assert(sizeof(RowParams) == 64, "RowParams layout");
 
+// Task rows of the sampling kernel: a pass-2 task (the race of a row whose
+// slices needed the row's plan first) carries this bit on its row index.
+constexpr int32_t kPass2 = 1 << 30;
+
 struct PenEntry {
   int32_t id;
   int32_t count;

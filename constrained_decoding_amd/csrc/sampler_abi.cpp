@@ -31,15 +31,34 @@ std::atomic<void*> g_ev_stop{nullptr};
 inline bool finite_f(float x) { return std::isfinite(x); }
 
 // Device parameter block: RowParams[B] | int32 row order [B] (the dispatch order
-// of sampler_sample; padded to 16 bytes) | RowParams[B] again, in that order
-// (the sampling kernel reads a row's parameters and its index side by side,
-// without a dependent load) | PenEntry[n_pen] | BiasEntry[n_bias].
+// of sampler_sample) | int32 task rows [tasks_max(B)] | RowParams
+// [tasks_max(B)] (the sampling kernel's tasks, see below) | PenEntry[n_pen] |
+// BiasEntry[n_bias]; the int32 arrays are padded to 16 bytes.
+//
+// Tasks: the sampling kernel runs groups of 8 tasks (one per XCD), each task
+// a row's P slices.  Task k is row task_row[k] & ~kPass2 (-1: none), with its
+// parameters at task_rows[k] (read side by side with the index, without a
+// dependent load).  Pass-1 task groups take the ordered rows 8 at a time;
+// rows whose cut needs the whole row's histogram (the first n_hold of the
+// order) also get a pass-2 group (bit kPass2), kPass2Lag groups after their
+// pass-1 group, whose slices race once the row's plan is out.
 size_t list_bytes(int32_t B) { return ((size_t)B * sizeof(int32_t) + 15) / 16 * 16; }
+int32_t tasks_max(int32_t B) { return 16 * ((B + 7) / 8); }
+size_t task_bytes(int32_t B) {
+  return list_bytes(tasks_max(B)) + sizeof(RowParams) * (size_t)tasks_max(B);
+}
 
 size_t params_bytes_exact(int32_t B, int64_t n_pen, int64_t n_bias) {
-  return 2 * sizeof(RowParams) * (size_t)B + list_bytes(B) + sizeof(PenEntry) * (size_t)n_pen +
-         sizeof(BiasEntry) * (size_t)n_bias;
+  return sizeof(RowParams) * (size_t)B + list_bytes(B) + task_bytes(B) +
+         sizeof(PenEntry) * (size_t)n_pen + sizeof(BiasEntry) * (size_t)n_bias;
 }
+
+// Pass-2 groups follow their pass-1 group after about one generation of
+// resident workgroups (4 per CU on 256 CUs), when the row's plan is likely out.
+#ifndef CDS_PASS2_LAG_SLOTS
+#define CDS_PASS2_LAG_SLOTS 1024
+#endif
+int pass2_lag(int P) { return std::max(1, (CDS_PASS2_LAG_SLOTS + 8 * P - 1) / (8 * P)); }
 
 // Validate and pack into host memory: `dst` (cap bytes), or when dst is null
 // into `tmp`.  Everything is validated and sized first, then written once into
@@ -199,8 +218,9 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
     return SAMPLER_ENOSPC;
   }
   const size_t off_list = sizeof(RowParams) * (size_t)B;
-  const size_t off_ord = off_list + list_bytes(B);
-  const size_t off_pen = off_ord + sizeof(RowParams) * (size_t)B;
+  const size_t off_task = off_list + list_bytes(B);
+  const size_t off_trows = off_task + list_bytes(tasks_max(B));
+  const size_t off_pen = off_list + list_bytes(B) + task_bytes(B);
   std::memcpy(p, rows.data(), sizeof(RowParams) * rows.size());
   // dispatch order: the rows whose last slice has the longest way to go
   // first -- rows whose slices wait for the row's plan, then top-k rows with
@@ -220,12 +240,32 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   for (int k = 0; k < 3; ++k)
     for (int32_t r : sampled)
       if (rank(r) == k) order.push_back(r);
+  int32_t n_hold = 0;
+  while (n_hold < (int32_t)order.size() && rank(order[(size_t)n_hold]) == 0) ++n_hold;
   order.insert(order.end(), greedy_rows.begin(), greedy_rows.end());
   std::memcpy(p + off_list, order.data(), sizeof(int32_t) * order.size());
   std::memset(p + off_list + sizeof(int32_t) * order.size(), 0,
               list_bytes(B) - sizeof(int32_t) * order.size());
-  for (size_t g = 0; g < order.size(); ++g)
-    std::memcpy(p + off_ord + sizeof(RowParams) * g, &rows[(size_t)order[g]], sizeof(RowParams));
+  // the task groups: pass-1 group g, and pass-2 group g - lag after it
+  const int32_t G1 = (B + 7) / 8, GH = (n_hold + 7) / 8, lag = pass2_lag(P);
+  std::vector<std::pair<int, int32_t>> seq;  // (pass, group)
+  for (int32_t g = 0; g < G1; ++g) {
+    seq.push_back({1, g});
+    if (g - lag >= 0 && g - lag < GH) seq.push_back({2, g - lag});
+  }
+  for (int32_t g = std::max(0, G1 - lag); g < GH; ++g) seq.push_back({2, g});
+  int32_t* trow = reinterpret_cast<int32_t*>(p + off_task);
+  RowParams* tpar = reinterpret_cast<RowParams*>(p + off_trows);
+  std::memset(p + off_task, 0, task_bytes(B));
+  for (int32_t k = 0; k < tasks_max(B); ++k) trow[k] = -1;
+  for (size_t q = 0; q < seq.size(); ++q)
+    for (int32_t x = 0; x < 8; ++x) {
+      const int32_t o = seq[q].second * 8 + x;
+      if (o >= (seq[q].first == 1 ? B : n_hold)) continue;
+      const int32_t r = order[(size_t)o];
+      trow[q * 8 + (size_t)x] = r | (seq[q].first == 2 ? kPass2 : 0);
+      tpar[q * 8 + (size_t)x] = rows[(size_t)r];
+    }
   // penalty entries in row order: raw rows straight from hist_ids, counted
   // rows from `pen`
   PenEntry* pe = reinterpret_cast<PenEntry*>(p + off_pen);
@@ -254,13 +294,14 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   out->n_bias = (int64_t)bias.size();
   out->bytes = bytes;
   out->n_sampled = (int32_t)sampled.size();
+  out->n_hold = n_hold;
   return SAMPLER_OK;
 }
 
 void set_pointers(sampler_batch* out, const void* base) {
   const unsigned char* b = static_cast<const unsigned char*>(base);
   const size_t off_list = sizeof(RowParams) * (size_t)out->B;
-  const size_t off_pen = off_list + list_bytes(out->B) + sizeof(RowParams) * (size_t)out->B;
+  const size_t off_pen = off_list + list_bytes(out->B) + task_bytes(out->B);
   out->d_rows = b;
   out->d_sampled = b + off_list;
   out->d_pen = b + off_pen;
@@ -380,9 +421,13 @@ int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_
   SampleArgs a;
   if (b->n_sampled < 0 || b->n_sampled > B || !b->d_sampled) return SAMPLER_EINVAL;
   a.rows = static_cast<const RowParams*>(b->d_rows);
-  a.order = static_cast<const int32_t*>(b->d_sampled);
-  a.rows_ord = reinterpret_cast<const RowParams*>(static_cast<const unsigned char*>(b->d_sampled) +
-                                                  list_bytes(B));
+  if (b->n_hold < 0 || b->n_hold > b->n_sampled) return SAMPLER_EINVAL;
+  {
+    const unsigned char* t = static_cast<const unsigned char*>(b->d_sampled) + list_bytes(B);
+    a.task_row = reinterpret_cast<const int32_t*>(t);
+    a.task_rows = reinterpret_cast<const RowParams*>(t + list_bytes(tasks_max(B)));
+    a.n_groups = (B + 7) / 8 + (b->n_hold + 7) / 8;
+  }
   a.logits = logits;
   a.ld = ld;
   a.B = B;

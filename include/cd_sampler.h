@@ -139,7 +139,9 @@ typedef struct sampler_batch {
   const void *d_bias;   /* dev: bias entries inside d_buf                    */
   size_t bytes;         /* bytes of d_buf in use                             */
   int32_t n_sampled;    /* rows that are not greedy                          */
-  int32_t reserved;
+  int32_t n_hold;       /* of these, rows whose cut needs the whole row's
+                           histogram (the first n_hold of d_sampled): their
+                           slices race in a second pass, after the plan     */
   const void *d_sampled; /* dev: int32 row order [B] inside d_buf, the order
                             in which sampler_sample dispatches the rows: the
                             n_sampled rows that are not greedy (first those
@@ -147,8 +149,8 @@ typedef struct sampler_batch {
                             as the only cut, or a top_k above a bound that
                             depends on V; then top-k rows without min-p whose
                             candidate lists are long), then the greedy rows;
-                            ascending within each group.  The per-row records
-                            follow it again in this order (after the order
+                            ascending within each group.  The sampling
+                            kernel's task table follows it (after the order
                             padded to 16 bytes)                             */
 } sampler_batch;
 
@@ -262,9 +264,10 @@ int sampler_sample(const sampler_batch *b, const void *logits, int dtype,
  * sampler_set_option(SAMPLER_OPT_TRACE, ptr): diagnostic phase timestamps.
  * ptr = 0 turns it off (default); otherwise ptr is the device address of a
  * caller-owned uint64 buffer of 8 words per workgroup of the sampling kernel
- * (8 * ceil(B/8) * P workgroups, P = slices per row, at most 64), which every later
- * sampler_sample call overwrites: word 0 = row | slice << 20 | class << 28 |
- * planner << 31, words 1..7 = the 100 MHz device wall clock at the start, after
+ * (8 * (ceil(B/8) + ceil(n_hold/8)) * P workgroups, P = slices per row, at most
+ * 64; never more than 16 * ceil(B/8) * P), which every later sampler_sample
+ * call overwrites: word 0 = row | slice << 20 | class << 28 | planner << 31
+ * (class 4: a pass-2 task), words 1..7 = the 100 MHz device wall clock at the start, after
  * the slice maximum, after the summary pass, after the class work, after the
  * arrival ticket, after the plan (or the wait for it), and at the end.
  * Process-wide; not for concurrent use.
