@@ -12,7 +12,6 @@ namespace cds {
 struct SampleArgs {
   const RowParams* rows;
   const int32_t* task_row;     // task k: row index | kPass2 (pass-2 task), -1: none
-  const RowParams* task_rows;  // task k: the row's parameters
   int32_t n_groups;            // task groups of kXcds tasks (grid: n_groups * kXcds * P)
   const void* logits;
   int64_t ld;

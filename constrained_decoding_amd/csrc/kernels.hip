@@ -1785,11 +1785,10 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CDS_WAVES_PE
   const int lr = (int)(j / (unsigned)a.P);
   const int sl = (int)(j - (unsigned)lr * (unsigned)a.P);
   const int k = lr * kXcds + (int)x;
-  // the task's row and its parameters: two independent loads
   const int32_t tr = a.task_row[k];
-  const RowParams rp = a.task_rows[k];
   if (tr < 0) return;
   const int r = tr & ~kPass2;
+  const RowParams rp = a.rows[r];
   if (tr & kPass2)
     hold_race_task<NT, E4, BF16, VEC>(a, r, rp, sl, sh, red, &s_plan, s_word);
   else if (rp.flags & ROW_GREEDY)

@@ -31,22 +31,19 @@ std::atomic<void*> g_ev_stop{nullptr};
 inline bool finite_f(float x) { return std::isfinite(x); }
 
 // Device parameter block: RowParams[B] | int32 row order [B] (the dispatch order
-// of sampler_sample) | int32 task rows [tasks_max(B)] | RowParams
-// [tasks_max(B)] (the sampling kernel's tasks, see below) | PenEntry[n_pen] |
-// BiasEntry[n_bias]; the int32 arrays are padded to 16 bytes.
+// of sampler_sample) | int32 task rows [tasks_max(B)] (the sampling kernel's
+// tasks, see below) | PenEntry[n_pen] | BiasEntry[n_bias]; the int32 arrays
+// are padded to 16 bytes.  (The block stays small: it is copied every step.)
 //
 // Tasks: the sampling kernel runs groups of 8 tasks (one per XCD), each task
-// a row's P slices.  Task k is row task_row[k] & ~kPass2 (-1: none), with its
-// parameters at task_rows[k] (read side by side with the index, without a
-// dependent load).  Pass-1 task groups take the ordered rows 8 at a time;
+// a row's P slices.  Task k is row task_row[k] & ~kPass2 (-1: none).  Pass-1
+// task groups take the ordered rows 8 at a time;
 // rows whose cut needs the whole row's histogram (the first n_hold of the
 // order) also get a pass-2 group (bit kPass2), kPass2Lag groups after their
 // pass-1 group, whose slices race once the row's plan is out.
 size_t list_bytes(int32_t B) { return ((size_t)B * sizeof(int32_t) + 15) / 16 * 16; }
 int32_t tasks_max(int32_t B) { return 16 * ((B + 7) / 8); }
-size_t task_bytes(int32_t B) {
-  return list_bytes(tasks_max(B)) + sizeof(RowParams) * (size_t)tasks_max(B);
-}
+size_t task_bytes(int32_t B) { return list_bytes(tasks_max(B)); }
 
 size_t params_bytes_exact(int32_t B, int64_t n_pen, int64_t n_bias) {
   return sizeof(RowParams) * (size_t)B + list_bytes(B) + task_bytes(B) +
@@ -219,7 +216,6 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   }
   const size_t off_list = sizeof(RowParams) * (size_t)B;
   const size_t off_task = off_list + list_bytes(B);
-  const size_t off_trows = off_task + list_bytes(tasks_max(B));
   const size_t off_pen = off_list + list_bytes(B) + task_bytes(B);
   std::memcpy(p, rows.data(), sizeof(RowParams) * rows.size());
   // dispatch order: the rows whose last slice has the longest way to go
@@ -255,7 +251,6 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   }
   for (int32_t g = std::max(0, G1 - lag); g < GH; ++g) seq.push_back({2, g});
   int32_t* trow = reinterpret_cast<int32_t*>(p + off_task);
-  RowParams* tpar = reinterpret_cast<RowParams*>(p + off_trows);
   std::memset(p + off_task, 0, task_bytes(B));
   for (int32_t k = 0; k < tasks_max(B); ++k) trow[k] = -1;
   for (size_t q = 0; q < seq.size(); ++q)
@@ -264,7 +259,6 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
       if (o >= (seq[q].first == 1 ? B : n_hold)) continue;
       const int32_t r = order[(size_t)o];
       trow[q * 8 + (size_t)x] = r | (seq[q].first == 2 ? kPass2 : 0);
-      tpar[q * 8 + (size_t)x] = rows[(size_t)r];
     }
   // penalty entries in row order: raw rows straight from hist_ids, counted
   // rows from `pen`
@@ -425,7 +419,6 @@ int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_
   {
     const unsigned char* t = static_cast<const unsigned char*>(b->d_sampled) + list_bytes(B);
     a.task_row = reinterpret_cast<const int32_t*>(t);
-    a.task_rows = reinterpret_cast<const RowParams*>(t + list_bytes(tasks_max(B)));
     a.n_groups = (B + 7) / 8 + (b->n_hold + 7) / 8;
   }
   a.logits = logits;
