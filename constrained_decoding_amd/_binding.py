@@ -19,7 +19,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 STATUS_OK, STATUS_OVERFLOW, STATUS_INVALID = 0, 1, 2
 FLAG_ALL_GREEDY, FLAG_ANY_GREEDY = 1 << 0, 1 << 1
 FLAG_NEED_TOP_K, FLAG_NEED_TOP_P, FLAG_NEED_MIN_P = 1 << 2, 1 << 3, 1 << 4
-FLAG_NEED_PENALTY, FLAG_HAS_BIAS = 1 << 5, 1 << 6
+FLAG_NEED_PENALTY, FLAG_HAS_BIAS, FLAG_SPLIT_PASS2 = 1 << 5, 1 << 6, 1 << 7
 OPT_ALGO = 1
 OPT_TRACE = 2
 

@@ -959,19 +959,21 @@ __device__ __forceinline__ Best exact_rerace(const SampleArgs& a, int r, const P
 // Returns false when the row must take the exact path.
 
 template <int NT, bool BF16, bool VEC>
-__device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Plan& pl,
+__device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, const Plan& pl,
                                            ExactShared<NT>& sh, uint64_t* ul, int32_t* off,
                                            SelShared& sel, RedScratch<NT>& red) {
-  const int tid = threadIdx.x, P = a.P;
+  // the row's nl <= 64 lists: list j is number r * 2P + j
+  const int tid = threadIdx.x;
+  const int64_t l0 = (int64_t)r * 2 * a.P;
   const RowParams rp = a.rows[r];
   const double Td = (double)rp.temperature;
   // the slices' top two and list lengths; list offsets by a prefix sum
   Top2 b = top2_init();
-  if (tid < 64) {  // P <= 64: one wave
+  if (tid < 64) {  // nl <= 64: one wave
     uint32_t cnt = 0;
     float lcut = CDS_NEG_INF;  // list mode: the highest slice list cut
-    if (tid < P) {
-      const SliceBest sb = ld_obj(&a.bests[(int64_t)r * P + tid]);
+    if (tid < nl) {
+      const SliceBest sb = ld_obj(&a.bests[l0 + tid]);
       b.k1 = sb.k1;
       b.t1 = sb.t1;
       b.z1 = sb.z1;
@@ -993,7 +995,7 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Pla
   }
   __syncthreads();
   CDS_TRACE_ROW(0);
-  const int n = off[P];
+  const int n = off[nl];
   if (n > UCAP) return false;
   // gather the slices' lists into LDS: every load is issued before any result
   // is stored; element i = tid + k*NT increases with k, so its slice j (with
@@ -1005,8 +1007,8 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, const Pla
 #pragma unroll
     for (int k = 0; k < KG; ++k) {
       const int i = tid + k * NT;
-      while (j + 1 < P && off[j + 1] <= i) ++j;
-      v[k] = i < n ? ld_u64(a.ulist + ((int64_t)r * P + j) * SCAP + (i - off[j])) : 0ull;
+      while (j + 1 < nl && off[j + 1] <= i) ++j;
+      v[k] = i < n ? ld_u64(a.ulist + (l0 + j) * SCAP + (i - off[j])) : 0ull;
     }
 #pragma unroll
     for (int k = 0; k < KG; ++k)
@@ -1340,7 +1342,8 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
   const int64_t hi = min(lo + a.S, (int64_t)a.V);
   const int32_t tbase = (int32_t)lo + 4 * tid;  // token of chunk i: tbase + 4*NT*i
   const RowView rv = row_view<BF16>(a, r);
-  const int64_t slot = (int64_t)r * P + sl;
+  const int64_t slot = (int64_t)r * P + sl;       // heads and histograms
+  const int64_t lslot = (int64_t)r * 2 * P + sl;  // list and record: list sl of the row
   CDS_TRACE(1);
 
   float x[E4][4];
@@ -1499,7 +1502,7 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
       sb.pad[0] = 1u;
       sb.pad[1] = __float_as_uint(zm);
       sb.pad[2] = __float_as_uint(CDS_NEG_INF);  // no list
-      st_obj(&a.bests[slot], sb);
+      st_obj(&a.bests[lslot], sb);
     }
   } else if (cls == CLS_LIST && zm != CDS_NEG_INF && !nonfin) {
     // a superset of the slice's candidates, listed: every token at or above a
@@ -1513,7 +1516,7 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
       cut = fmaxf(cut, bm);
     }
     const float cutv = sgpr_f(cut);
-    uint64_t* gl = a.ulist + slot * SCAP;
+    uint64_t* gl = a.ulist + lslot * SCAP;
     const uint32_t nst = list_tokens<NT, E4>(
         x, tbase, (uint32_t)SCAP, sh.sel.wt,
         [&](float v) { return v >= cutv && v != CDS_NEG_INF; },
@@ -1527,7 +1530,7 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
       sb.ucnt = nst;
       sb.pad[0] = sb.pad[1] = 0u;
       sb.pad[2] = __float_as_uint(cutv);  // the list holds every token >= this
-      st_obj(&a.bests[slot], sb);
+      st_obj(&a.bests[lslot], sb);
     }
   } else if ((cls == CLS_RACE || cls == CLS_LIST) && tid == 0) {
     // nothing allowed or a non-finite value: the planner answers the row
@@ -1539,7 +1542,7 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
     sb.ucnt = 0u;
     sb.pad[0] = sb.pad[1] = 0u;
     sb.pad[2] = __float_as_uint(CDS_NEG_INF);  // lists nothing, holds nothing
-    st_obj(&a.bests[slot], sb);
+    st_obj(&a.bests[lslot], sb);
   }
 
   CDS_TRACE(4);
@@ -1600,7 +1603,8 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
       pl.a_lo = -FLT_MAX;
       pl.a_hi = pl.zmax;   // masses exp((z - zmax)/T) <= 1
     }
-    if (!finish_row<NT, BF16, VEC>(a, r, pl, sh.fin.ex, sh.fin.list, sh.fin.off, sh.fin.select, red)) {
+    if (!finish_row<NT, BF16, VEC>(a, r, P, pl, sh.fin.ex, sh.fin.list, sh.fin.off, sh.fin.select,
+                                   red)) {
       __syncthreads();
       row_exact<NT, BF16, VEC>(a, r, sh.fin.ex);
       if (tid == 0) a.plans[r].path = PATH_EXACT;
@@ -1626,14 +1630,20 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
 // the boundary tokens are listed, and the last slice resolves the row.
 template <int NT, int E4, bool BF16, bool VEC>
 __device__ __forceinline__ void hold_race_task(const SampleArgs& a, int r, const RowParams& rp,
-                                               int sl, FusedLds<NT>& sh, RedScratch<NT>& red,
+                                               int sl, int halves, int half,
+                                               FusedLds<NT>& sh, RedScratch<NT>& red,
                                                Plan* s_plan, uint32_t* s_word) {
   const int tid = threadIdx.x, P = a.P;
-  const int64_t lo = (int64_t)sl * a.S;
-  const int64_t hi = min(lo + a.S, (int64_t)a.V);
+  // the task's part of slice sl: all of it, or one of two halves (the first
+  // holds chunks 0 .. ceil(E4/2)-1 of the slice)
+  const int64_t s0 = (int64_t)sl * a.S, s1 = min(s0 + a.S, (int64_t)a.V);
+  constexpr int64_t kHalfLen = (int64_t)((E4 + 1) / 2) * 4 * NT;
+  const int64_t lo = halves == 1 ? s0 : min(s0 + half * kHalfLen, s1);
+  const int64_t hi = halves == 1 ? s1 : (half ? s1 : min(s0 + kHalfLen, s1));
   const int32_t tbase = (int32_t)lo + 4 * tid;  // token of chunk i: tbase + 4*NT*i
   const RowView rv = row_view<BF16>(a, r);
-  const int64_t slot = (int64_t)r * P + sl;
+  const int nl = halves * P;                                     // the row's lists
+  const int64_t slot = (int64_t)r * 2 * P + sl * halves + half;  // this task's list
   RowSync* sy = &a.sync[r];
   if (a.trace && tid == 0)
     a.trace[(size_t)blockIdx.x * 8] = (unsigned long long)r | ((unsigned long long)sl << 20) |
@@ -1738,12 +1748,12 @@ __device__ __forceinline__ void hold_race_task(const SampleArgs& a, int r, const
   CDS_TRACE_SUB(4);
   if (tid == 0) {
     const uint32_t t = take_ticket(&sy->done);
-    if (t == (uint32_t)(P - 1)) st_u64(&sy->done, 0ull);
+    if (t == (uint32_t)(nl - 1)) st_u64(&sy->done, 0ull);
     s_word[0] = t;
   }
   __syncthreads();
   CDS_TRACE_SUB(5);
-  if (s_word[0] != (uint32_t)(P - 1)) {
+  if (s_word[0] != (uint32_t)(nl - 1)) {
     CDS_TRACE(7);
     return;
   }
@@ -1753,7 +1763,8 @@ __device__ __forceinline__ void hold_race_task(const SampleArgs& a, int r, const
   const Plan pl = *s_plan;
   if (failed || pl.mode == PLAN_SLOW ||
       (pl.mode == PLAN_FAST &&
-       !finish_row<NT, BF16, VEC>(a, r, pl, sh.fin.ex, sh.fin.list, sh.fin.off, sh.fin.select, red))) {
+       !finish_row<NT, BF16, VEC>(a, r, nl, pl, sh.fin.ex, sh.fin.list, sh.fin.off, sh.fin.select,
+                                  red))) {
     __syncthreads();
     row_exact<NT, BF16, VEC>(a, r, sh.fin.ex);
     if (tid == 0) a.plans[r].path = PATH_EXACT;
@@ -1787,10 +1798,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CDS_WAVES_PE
   const int k = lr * kXcds + (int)x;
   const int32_t tr = a.task_row[k];
   if (tr < 0) return;
-  const int r = tr & ~kPass2;
+  const int r = tr & kTaskRow;
   const RowParams rp = a.rows[r];
   if (tr & kPass2)
-    hold_race_task<NT, E4, BF16, VEC>(a, r, rp, sl, sh, red, &s_plan, s_word);
+    hold_race_task<NT, E4, BF16, VEC>(a, r, rp, sl, (tr & kSplit) ? 2 : 1, (tr & kHalf) ? 1 : 0,
+                                      sh, red, &s_plan, s_word);
   else if (rp.flags & ROW_GREEDY)
     slice_task<NT, E4, BF16, VEC, true>(a, r, rp, sl, sh, red, sst, &s_plan, s_word);
   else

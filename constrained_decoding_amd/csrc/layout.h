@@ -34,8 +34,13 @@ struct alignas(16) RowParams {
 static_assert(sizeof(RowParams) == 64, "RowParams layout");
 
 // Task rows of the sampling kernel: a pass-2 task (the race of a row whose
-// slices needed the row's plan first) carries this bit on its row index.
+// slices needed the row's plan first) carries kPass2 on its row index.  In a
+// split batch (kSplit) a pass-2 task covers one half of its slice (kHalf: the
+// second half), so that twice as many workgroups share a row's race.
 constexpr int32_t kPass2 = 1 << 30;
+constexpr int32_t kHalf = 1 << 29;
+constexpr int32_t kSplit = 1 << 28;
+constexpr int32_t kTaskRow = kSplit - 1;  // the row index bits
 
 struct PenEntry {
   int32_t id;
@@ -194,6 +199,14 @@ inline int choose_slices(int32_t V) {
   return (int)p;
 }
 
+// Pass-2 tasks per row slice: two halves when the pass-2 rows are few (at
+// most a quarter of the batch: their latency then matters more than the
+// workgroups' count) and the row's 2P lists fit one wave of the finisher
+// (P <= 32); else one.
+constexpr int pass2_halves(int P, int32_t n_hold, int32_t B) {
+  return (2 * P <= 64 && 4 * n_hold <= B) ? 2 : 1;
+}
+
 inline WorkspaceLayout workspace_layout(int32_t B, int32_t V) {
   WorkspaceLayout L;
   L.P = choose_slices(V);
@@ -212,8 +225,10 @@ inline WorkspaceLayout workspace_layout(int32_t B, int32_t V) {
   L.plan_off = take(sizeof(Plan) * (size_t)B);
   L.head_off = take(sizeof(SliceHead) * (size_t)B * L.P);
   L.hist_off = take(sizeof(uint64_t) * NBINS * (size_t)B * L.P);
-  L.best_off = take(sizeof(SliceBest) * (size_t)B * L.P);
-  L.ulist_off = take(sizeof(uint64_t) * SCAP * (size_t)B * L.P);
+  // lists and their records: up to 2P per row (a slice each, or a half slice
+  // each for pass-2 rows); list j of row r is number r * 2P + j
+  L.best_off = take(sizeof(SliceBest) * (size_t)B * 2 * L.P);
+  L.ulist_off = take(sizeof(uint64_t) * SCAP * (size_t)B * 2 * L.P);
   L.total = off;
   return L;
 }

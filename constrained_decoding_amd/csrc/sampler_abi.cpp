@@ -36,13 +36,14 @@ inline bool finite_f(float x) { return std::isfinite(x); }
 // are padded to 16 bytes.  (The block stays small: it is copied every step.)
 //
 // Tasks: the sampling kernel runs groups of 8 tasks (one per XCD), each task
-// a row's P slices.  Task k is row task_row[k] & ~kPass2 (-1: none).  Pass-1
-// task groups take the ordered rows 8 at a time;
+// a row's P slices.  Task k is row task_row[k] & ~(kPass2 | kHalf) (-1:
+// none).  Pass-1 task groups take the ordered rows 8 at a time;
 // rows whose cut needs the whole row's histogram (the first n_hold of the
-// order) also get a pass-2 group (bit kPass2), kPass2Lag groups after their
-// pass-1 group, whose slices race once the row's plan is out.
+// order) also get pass-2 groups (bit kPass2; one per slice half, the second
+// with kHalf), a lag of groups after their pass-1 group, whose workgroups race
+// once the row's plan is out.
 size_t list_bytes(int32_t B) { return ((size_t)B * sizeof(int32_t) + 15) / 16 * 16; }
-int32_t tasks_max(int32_t B) { return 16 * ((B + 7) / 8); }
+int32_t tasks_max(int32_t B) { return 24 * ((B + 7) / 8); }  // pass 1 + two pass-2 halves
 size_t task_bytes(int32_t B) { return list_bytes(tasks_max(B)); }
 
 size_t params_bytes_exact(int32_t B, int64_t n_pen, int64_t n_bias) {
@@ -244,12 +245,17 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
               list_bytes(B) - sizeof(int32_t) * order.size());
   // the task groups: pass-1 group g, and pass-2 group g - lag after it
   const int32_t G1 = (B + 7) / 8, GH = (n_hold + 7) / 8, lag = pass2_lag(P);
-  std::vector<std::pair<int, int32_t>> seq;  // (pass, group)
+  const int halves = pass2_halves(P, n_hold, B);
+  if (halves == 2) flags |= SAMPLER_FLAG_SPLIT_PASS2;
+  std::vector<std::pair<int, int32_t>> seq;  // (pass: 1, or 2 + half, group)
+  auto pass2 = [&](int32_t g) {
+    for (int h = 0; h < halves; ++h) seq.push_back({2 + h, g});
+  };
   for (int32_t g = 0; g < G1; ++g) {
     seq.push_back({1, g});
-    if (g - lag >= 0 && g - lag < GH) seq.push_back({2, g - lag});
+    if (g - lag >= 0 && g - lag < GH) pass2(g - lag);
   }
-  for (int32_t g = std::max(0, G1 - lag); g < GH; ++g) seq.push_back({2, g});
+  for (int32_t g = std::max(0, G1 - lag); g < GH; ++g) pass2(g);
   int32_t* trow = reinterpret_cast<int32_t*>(p + off_task);
   std::memset(p + off_task, 0, task_bytes(B));
   for (int32_t k = 0; k < tasks_max(B); ++k) trow[k] = -1;
@@ -258,7 +264,9 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
       const int32_t o = seq[q].second * 8 + x;
       if (o >= (seq[q].first == 1 ? B : n_hold)) continue;
       const int32_t r = order[(size_t)o];
-      trow[q * 8 + (size_t)x] = r | (seq[q].first == 2 ? kPass2 : 0);
+      trow[q * 8 + (size_t)x] = r | (seq[q].first >= 2 ? kPass2 : 0) |
+                                (seq[q].first >= 2 && halves == 2 ? kSplit : 0) |
+                                (seq[q].first == 3 ? kHalf : 0);
     }
   // penalty entries in row order: raw rows straight from hist_ids, counted
   // rows from `pen`
@@ -419,7 +427,7 @@ int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_
   {
     const unsigned char* t = static_cast<const unsigned char*>(b->d_sampled) + list_bytes(B);
     a.task_row = reinterpret_cast<const int32_t*>(t);
-    a.n_groups = (B + 7) / 8 + (b->n_hold + 7) / 8;
+    a.n_groups = (B + 7) / 8 + ((b->flags & SAMPLER_FLAG_SPLIT_PASS2) ? 2 : 1) * ((b->n_hold + 7) / 8);
   }
   a.logits = logits;
   a.ld = ld;

@@ -80,6 +80,10 @@ extern "C" {
 #define SAMPLER_FLAG_NEED_MIN_P (1u << 4)
 #define SAMPLER_FLAG_NEED_PENALTY (1u << 5)
 #define SAMPLER_FLAG_HAS_BIAS (1u << 6)
+/* Layout, not semantics: the n_hold rows' second-pass tasks each take half a
+ * slice (set when n_hold is small against B, so that those rows' latency is
+ * spread over twice the workgroups).                                      */
+#define SAMPLER_FLAG_SPLIT_PASS2 (1u << 7)
 
 /* ---- host-side per-request parameters ------------------------------------
  * All arrays are host memory, [B] unless noted; NULL selects the default.
@@ -264,8 +268,8 @@ int sampler_sample(const sampler_batch *b, const void *logits, int dtype,
  * sampler_set_option(SAMPLER_OPT_TRACE, ptr): diagnostic phase timestamps.
  * ptr = 0 turns it off (default); otherwise ptr is the device address of a
  * caller-owned uint64 buffer of 8 words per workgroup of the sampling kernel
- * (8 * (ceil(B/8) + ceil(n_hold/8)) * P workgroups, P = slices per row, at most
- * 64; never more than 16 * ceil(B/8) * P), which every later sampler_sample
+ * (8 * (ceil(B/8) + 2 * ceil(n_hold/8)) * P workgroups, P = slices per row, at
+ * most 64; never more than 24 * ceil(B/8) * P), which every later sampler_sample
  * call overwrites: word 0 = row | slice << 20 | class << 28 | planner << 31
  * (class 4: a pass-2 task), words 1..7 = the 100 MHz device wall clock at the start, after
  * the slice maximum, after the summary pass, after the class work, after the

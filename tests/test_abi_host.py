@@ -88,9 +88,9 @@ def test_penalty_counts_and_bias_dedup(cds):
     rows = _rowparams(buf, 3)
     assert b.n_sampled == 3
     assert np.frombuffer(buf[64 * 3:64 * 3 + 12].tobytes(), "<i4").tolist() == [0, 1, 2]
-    # the row order (room for B int32, 16-byte padded), then the task table: 16
+    # the row order (room for B int32, 16-byte padded), then the task table: 24
     # task rows (int32)
-    pen_off = 64 * 3 + 16 + 64
+    pen_off = 64 * 3 + 16 + 96
     pen = np.frombuffer(buf[pen_off:pen_off + 8 * b.n_pen].tobytes(), "<i4").reshape(-1, 2)
     # rows of up to 4096 history tokens are packed as they come (count 1 each;
     # the transforms kernel merges repeats); row 2 has no active penalty
@@ -168,13 +168,21 @@ def test_sampled_row_list(cds):
     assert b.n_sampled == 3
     order = [5, 1, 4, 0, 2, 3]
     assert np.frombuffer(buf[64 * 6:64 * 6 + 24].tobytes(), "<i4").tolist() == order
-    # the kernel's task table: 16 task slots (two groups of 8 for B = 6); pass 1
-    # takes the ordered rows, the one top-p-only row (5) gets a pass-2 task
-    assert b.n_hold == 1
+    # the kernel's task table: 24 task slots (three groups of 8 for B = 6); pass
+    # 1 takes the ordered rows, the one top-p-only row (5) gets two pass-2
+    # tasks (bit 30), one per slice half (bit 28: split; bit 29: second half),
+    # as one such row in six is few
+    assert b.n_hold == 1 and b.flags & cds.FLAG_SPLIT_PASS2
     t0 = 64 * 6 + 32
-    tasks = np.frombuffer(buf[t0:t0 + 64].tobytes(), "<i4")
+    tasks = np.frombuffer(buf[t0:t0 + 96].tobytes(), "<i4")
     assert tasks[:8].tolist() == order + [-1, -1]
-    assert tasks[8] == 5 | (1 << 30) and (tasks[9:] == -1).all()
+    assert tasks[8] == 5 | (1 << 30) | (1 << 28) and (tasks[9:16] == -1).all()
+    assert tasks[16] == 5 | (1 << 30) | (1 << 29) | (1 << 28) and (tasks[17:] == -1).all()
+    # when most rows need the second pass, its tasks take whole slices
+    buf, b = cds.pack_host(4, 1000, np.ones(4, np.float32), top_p=np.full(4, 0.9, np.float32))
+    assert b.n_hold == 4 and not b.flags & cds.FLAG_SPLIT_PASS2
+    tasks = np.frombuffer(buf[64 * 4 + 16:64 * 4 + 16 + 96].tobytes(), "<i4")
+    assert tasks[8:12].tolist() == [(1 << 30) | r for r in range(4)] and (tasks[16:] == -1).all()
 
     buf, b = cds.pack_host(2, 1000, np.zeros(2, np.float32))
     assert b.n_sampled == 0 and b.flags & cds.FLAG_ALL_GREEDY
