@@ -210,18 +210,25 @@ __device__ __forceinline__ bool race32_hopeful(const Top2& b, float z, float zma
   return sd >= -19.5f && sd + 16.7f >= b.k2;
 }
 
-// Token t (value z, draw x) enters the race if ok; branch-free.  A token with
-// s_t - m < -19.5 (including z = -inf) never wins and is left out.
-__device__ __forceinline__ void race32_if(Top2& b, bool ok, float z, int32_t t, uint32_t x,
-                                          float zmax, float invT32) {
+// Token t (value z, Gumbel term g = gumbel_fast of its draw) enters the race
+// if ok; branch-free.  A token with s_t - m < -19.5 (including z = -inf) never
+// wins and is left out.
+__device__ __forceinline__ void race32_g_if(Top2& b, bool ok, float z, int32_t t, float g,
+                                            float zmax, float invT32) {
   const float sd = (z - zmax) * invT32;
-  const float k = sd + gumbel_fast(x);
+  const float k = sd + g;
   const bool in2 = ok & (sd >= -19.5f);  // bitwise: no short circuit, no branches
   const bool gt = in2 & ((k > b.k1) | ((k == b.k1) & (t < b.t1)));
   b.k2 = fmaxf(b.k2, gt ? b.k1 : (in2 ? k : CDS_NEG_INF));
   b.k1 = gt ? k : b.k1;
   b.t1 = gt ? t : b.t1;
   b.z1 = gt ? z : b.z1;
+}
+
+// As race32_g_if, from the token's 32-bit draw x.
+__device__ __forceinline__ void race32_if(Top2& b, bool ok, float z, int32_t t, uint32_t x,
+                                          float zmax, float invT32) {
+  race32_g_if(b, ok, z, t, gumbel_fast(x), zmax, invT32);
 }
 
 __device__ __forceinline__ void race32(Top2& b, float z, int32_t t, uint32_t x, float zmax,
@@ -495,12 +502,13 @@ __device__ __forceinline__ double wave_shift_up(double v) {
 }
 
 // Inclusive prefix sum, in place, over n <= 64*K values of an LDS array, by
-// wave 0 alone: lane l owns elements [K*l, K*l + K).  The caller
-// synchronises the workgroup before (values written) and after (results read).
+// one wave (`wave`, default 0) alone: lane l owns elements [K*l, K*l + K).
+// The caller synchronises the workgroup before (values written) and after
+// (results read).
 template <int K, typename T>
-__device__ __forceinline__ void wave0_scan_inplace(T* v, int n) {
-  if (threadIdx.x >= 64) return;
-  const int l = threadIdx.x;
+__device__ __forceinline__ void wave_scan_inplace(T* v, int n, int wave = 0) {
+  if ((int)(threadIdx.x >> 6) != wave) return;
+  const int l = threadIdx.x & 63;
   T loc[K];
   T run = T(0);
 #pragma unroll

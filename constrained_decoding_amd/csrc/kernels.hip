@@ -647,10 +647,10 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
   }
   __syncthreads();
   CDS_TRACE_ROW(6);
-  // cumulative counts and masses from the top, both by wave 0
+  // cumulative counts and masses from the top: waves 0 and 1
   constexpr int KB = (NBINS + 63) / 64;
-  wave0_scan_inplace<KB>(ps.cumc, NBINS);
-  wave0_scan_inplace<KB>(ps.md, NBINS);
+  wave_scan_inplace<KB>(ps.cumc, NBINS, 0);  // two waves, side by side
+  wave_scan_inplace<KB>(ps.md, NBINS, 1);
   __syncthreads();
   // the rest is searches over the monotone cumulative arrays: wave 0 only
   if (tid >= 64) return;
@@ -1628,11 +1628,15 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
 // Pass 2 of a HOLD row (slice sl): the slice is loaded again (the loads are
 // issued before the wait), the row's plan awaited, then the sure tokens race,
 // the boundary tokens are listed, and the last slice resolves the row.
-template <int NT, int E4, bool BF16, bool VEC>
+// SPLIT: the task takes one half of the slice (EC = ceil(E4/2) chunks), and
+// draws every token's Gumbel term while the plan is being made.
+template <int NT, int E4, bool SPLIT, bool BF16, bool VEC>
 __device__ __forceinline__ void hold_race_task(const SampleArgs& a, int r, const RowParams& rp,
-                                               int sl, int halves, int half,
-                                               FusedLds<NT>& sh, RedScratch<NT>& red,
-                                               Plan* s_plan, uint32_t* s_word) {
+                                               int sl, int half, FusedLds<NT>& sh,
+                                               RedScratch<NT>& red, Plan* s_plan,
+                                               uint32_t* s_word) {
+  constexpr int EC = SPLIT ? (E4 + 1) / 2 : E4;  // chunks held
+  constexpr int halves = SPLIT ? 2 : 1;
   const int tid = threadIdx.x, P = a.P;
   // the task's part of slice sl: all of it, or one of two halves (the first
   // holds chunks 0 .. ceil(E4/2)-1 of the slice)
@@ -1649,9 +1653,27 @@ __device__ __forceinline__ void hold_race_task(const SampleArgs& a, int r, const
     a.trace[(size_t)blockIdx.x * 8] = (unsigned long long)r | ((unsigned long long)sl << 20) |
                                       (4ull << 28);
   CDS_TRACE(1);
-  float x[E4][4];
+  float x[EC][4];
   uint32_t nonfin = 0;
-  load_chunks<NT, E4, BF16, VEC, true, false>(rv, lo, hi, 0, x, nonfin);
+  load_chunks<NT, EC, BF16, VEC, true, false>(rv, lo, hi, 0, x, nonfin);
+  // SPLIT: the draws do not depend on the plan: every token's Gumbel term is
+  // computed now, while the row's plan is being made
+  float g[SPLIT ? EC : 1][4];
+  if (SPLIT) {
+    const uint32_t k0 = (uint32_t)rp.seed, k1 = (uint32_t)(rp.seed >> 32);
+    const uint32_t off_lo = (uint32_t)rp.offset, off_hi = (uint32_t)(rp.offset >> 32);
+#pragma unroll
+    for (int i = 0; i < (SPLIT ? EC : 0); ++i) {
+      int32_t tb = tbase;
+      asm volatile("" : "+v"(tb));
+      const uint4 blk =
+          philox4x32_10(make_uint4((uint32_t)(tb + 4 * NT * i) >> 2, off_lo, off_hi, 0u), k0, k1);
+      g[i][0] = gumbel_fast(blk.x);
+      g[i][1] = gumbel_fast(blk.y);
+      g[i][2] = gumbel_fast(blk.z);
+      g[i][3] = gumbel_fast(blk.w);
+    }
+  }
   if (tid == 0) {
     if (gen_wait(&sy->ready, a.gen, a.spin_limit)) {
       *s_plan = ld_obj(&a.plans[r]);
@@ -1686,8 +1708,9 @@ __device__ __forceinline__ void hold_race_task(const SampleArgs& a, int r, const
     uint64_t* gl = a.ulist + slot * SCAP;
     const float lo1 = fmaxf(a_lo, zc1), hi1 = fminf(a_hi, zs);
     const float lo2 = fmaxf(k_lo, zc1), hi2 = fminf(k_hi, zs);
-    const uint2 nn = list_tokens2<NT, E4>(
-        x, tbase, (uint32_t)UCAP, (uint32_t)SCAP, sh.sel.wt, [&](float v) { return v >= zs; },
+    const uint2 nn = list_tokens2<NT, EC>(
+        x, tbase, (uint32_t)UCAP, (uint32_t)SCAP, sh.sel.wt,
+        [&](float v) { return !SPLIT && v >= zs; },
         [&](uint32_t pos, float v, int32_t t) {
           stage[pos] = make_uint2((uint32_t)t, __float_as_uint(v));
         },
@@ -1696,7 +1719,15 @@ __device__ __forceinline__ void hold_race_task(const SampleArgs& a, int r, const
     const uint32_t nsure = nn.x, nst = has_u ? nn.y : 0u;
     __syncthreads();
     CDS_TRACE_SUB(0);
-    if (nsure <= (uint32_t)UCAP) {
+    if (SPLIT) {
+      // the sure tokens race with the Gumbel terms drawn before the plan
+#pragma unroll
+      for (int i = 0; i < EC; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          race32_g_if(b, x[i][q] >= zs, x[i][q], tbase + 4 * NT * i + q, g[SPLIT ? i : 0][q],
+                      zmax, invT32);
+    } else if (nsure <= (uint32_t)UCAP) {
       race_list<NT>(
           b, (int)nsure, zmax, invT32,
           [&](int i, float& z, int32_t& t) {
@@ -1709,7 +1740,7 @@ __device__ __forceinline__ void hold_race_task(const SampleArgs& a, int r, const
           });
     } else {
 #pragma unroll
-      for (int i = 0; i < E4; ++i) {
+      for (int i = 0; i < EC; ++i) {
         int32_t tb = tbase;
         asm volatile("" : "+v"(tb));
         const int32_t t0 = tb + 4 * NT * i;
@@ -1800,9 +1831,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CDS_WAVES_PE
   if (tr < 0) return;
   const int r = tr & kTaskRow;
   const RowParams rp = a.rows[r];
-  if (tr & kPass2)
-    hold_race_task<NT, E4, BF16, VEC>(a, r, rp, sl, (tr & kSplit) ? 2 : 1, (tr & kHalf) ? 1 : 0,
-                                      sh, red, &s_plan, s_word);
+  if ((tr & kPass2) && (tr & kSplit))
+    hold_race_task<NT, E4, true, BF16, VEC>(a, r, rp, sl, (tr & kHalf) ? 1 : 0, sh, red,
+                                            &s_plan, s_word);
+  else if (tr & kPass2)
+    hold_race_task<NT, E4, false, BF16, VEC>(a, r, rp, sl, 0, sh, red, &s_plan, s_word);
   else if (rp.flags & ROW_GREEDY)
     slice_task<NT, E4, BF16, VEC, true>(a, r, rp, sl, sh, red, sst, &s_plan, s_word);
   else
