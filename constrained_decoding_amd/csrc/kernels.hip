@@ -898,6 +898,44 @@ __device__ __forceinline__ void race_list(Top2& b, int n, float zmax, float invT
   }
 }
 
+// One-wave selections over up to 64*KW list entries held KW per lane (lane l
+// holds entries l + 64k): the largest order key v with (number, or summed
+// integer weight, of the selected entries with key >= v) reaching need.  The
+// selected keys lie in [lo, hi]; the bits below their common prefix are set
+// greedily from the top.  Same definition as list_select, no barrier.
+template <int KW>
+__device__ __forceinline__ uint32_t wave_select_count(const uint32_t (&u)[KW], const bool (&sel)[KW],
+                                                      uint32_t need, uint32_t lo, uint32_t hi) {
+  if (lo == hi) return lo;
+  const int h = 31 - (int)__clz(lo ^ hi);
+  uint32_t prefix = h == 31 ? 0u : lo & ~((2u << h) - 1u);
+  for (int bit = h; bit >= 0; --bit) {
+    const uint32_t t = prefix | (1u << bit);
+    uint32_t c = 0u;
+#pragma unroll
+    for (int k = 0; k < KW; ++k) c += (uint32_t)__popcll(__ballot(sel[k] && u[k] >= t));
+    if (c >= need) prefix = t;
+  }
+  return prefix;
+}
+template <int KW>
+__device__ __forceinline__ uint32_t wave_select_mass(const uint32_t (&u)[KW],
+                                                     const unsigned long long (&w)[KW],
+                                                     double need, uint32_t lo, uint32_t hi) {
+  if (lo == hi) return lo;
+  const int h = 31 - (int)__clz(lo ^ hi);
+  uint32_t prefix = h == 31 ? 0u : lo & ~((2u << h) - 1u);
+  auto add = [](unsigned long long a, unsigned long long b) { return a + b; };
+  for (int bit = h; bit >= 0; --bit) {
+    const uint32_t t = prefix | (1u << bit);
+    unsigned long long m = 0ull;
+#pragma unroll
+    for (int k = 0; k < KW; ++k) m += u[k] >= t ? w[k] : 0ull;
+    if ((double)wave_allreduce(m, add) >= need) prefix = t;
+  }
+  return prefix;
+}
+
 // Exclusive prefix sum of c over the block (thread order) and its total, with
 // one barrier; wt is LDS scratch of NT/64 words.
 template <int NT>
@@ -958,6 +996,9 @@ __device__ __forceinline__ Best exact_rerace(const SampleArgs& a, int r, const P
 // the finisher).  The row's list is gathered from the slices' lists into LDS.
 // Returns false when the row must take the exact path.
 
+// Lists of at most this many tokens are resolved by one wave.
+constexpr int kShortList = 256;
+
 template <int NT, bool BF16, bool VEC>
 __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, const Plan& pl,
                                            ExactShared<NT>& sh, uint64_t* ul, int32_t* off,
@@ -1017,6 +1058,112 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
   __syncthreads();
 
   CDS_TRACE_ROW(1);
+  float zfin;
+  if (n <= kShortList) {
+    // short lists: wave 0 alone resolves the row (no workgroup barrier until
+    // the result is shared): the same cuts and race as below
+    if (tid < 64) {
+      constexpr int KW = kShortList / 64;
+      uint32_t u[KW], tl[KW];  // entry halves: order key, ~token
+      float z[KW];
+      bool v[KW];
+#pragma unroll
+      for (int k = 0; k < KW; ++k) {
+        const int i = tid + 64 * k;
+        v[k] = i < n;
+        const unsigned long long e = v[k] ? ul[i] : 0ull;
+        u[k] = (uint32_t)(e >> 32);
+        tl[k] = (uint32_t)e;
+        z[k] = v[k] ? ukey_z(e) : CDS_NEG_INF;
+      }
+      auto mn = [](uint32_t x, uint32_t y) { return x < y ? x : y; };
+      auto mx = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
+      int status = 0;  // 1: the row takes the exact path
+      float zc12 = pl.zcut1;
+      if (pl.k_rank > 0) {
+        bool inK[KW];
+        uint32_t c = 0u, lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+        for (int k = 0; k < KW; ++k) {
+          inK[k] = v[k] && z[k] >= pl.k_lo && z[k] < pl.k_hi;
+          c += (uint32_t)__popcll(__ballot(inK[k]));
+          if (inK[k]) {
+            lo = mn(lo, u[k]);
+            hi = mx(hi, u[k]);
+          }
+        }
+        lo = wave_allreduce(lo, mn);
+        hi = wave_allreduce(hi, mx);
+        if (c < (uint32_t)pl.k_rank && !pl.list_mode) status = 1;
+        else if (c >= (uint32_t)pl.k_rank)
+          zc12 = fmaxf(zc12, from_okey(wave_select_count<KW>(u, inK, (uint32_t)pl.k_rank, lo, hi)));
+      }
+      if (pl.list_mode && zc12 < sh.fshare) status = 1;
+      float zf = zc12;
+      if (status == 0 && pl.topp) {
+        const float zref = pl.a_hi, a_lo = pl.a_lo, zc = zc12;
+        const float c32 = (float)(1.4426950408889634 / Td);
+        const double F = exp((double)zref / Td - pl.m);
+        constexpr double kFix = 0x1p46;
+        unsigned long long w[KW], wi[KW], mu = 0ull, m_in = 0ull;
+        uint32_t lo = 0xFFFFFFFFu, hi = 0u;
+#pragma unroll
+        for (int k = 0; k < KW; ++k) {
+          w[k] = z[k] >= zc ? (unsigned long long)((double)__builtin_amdgcn_exp2f((z[k] - zref) * c32) *
+                                                  kFix)
+                            : 0ull;
+          mu += w[k];
+          wi[k] = (z[k] >= a_lo) ? w[k] : 0ull;
+          m_in += wi[k];
+          if (wi[k]) {
+            lo = mn(lo, u[k]);
+            hi = mx(hi, u[k]);
+          }
+        }
+        auto add = [](unsigned long long a, unsigned long long b) { return a + b; };
+        mu = wave_allreduce(mu, add);
+        m_in = wave_allreduce(m_in, add);
+        lo = wave_allreduce(lo, mn);
+        hi = wave_allreduce(hi, mx);
+        const double M2 = pl.m_sure + pl.m_mid + F * ((double)mu / kFix);
+        const double need = (pl.p * M2 - pl.m_sure) / F * kFix;
+        if (!(need > 0.0) || (double)m_in < need) status = 1;
+        else zf = fmaxf(zf, from_okey(wave_select_mass<KW>(u, wi, need, lo, hi)));
+      }
+      if (status == 0) {
+        // the race over the survivors, merged with the slices' top two (lanes
+        // below the list count hold those in b)
+        const RaceCtx c = make_race_ctx(rp, pl.zmax);
+#pragma unroll
+        for (int k = 0; k < KW; ++k) {
+          const bool in = v[k] && z[k] >= zf;
+          if (in && race32_hopeful(b, z[k], c.zmax, c.invT32)) {
+            const int32_t t = (int32_t)(0xFFFFFFFFu - tl[k]);
+            const uint4 blk = race_block(c, (int64_t)(t & ~3));
+            const int q = t & 3;
+            const uint32_t xw = q == 0 ? blk.x : (q == 1 ? blk.y : (q == 2 ? blk.z : blk.w));
+            race32(b, z[k], t, xw, c.zmax, c.invT32);
+          }
+        }
+        b = wave_allreduce(b, [](Top2 x, const Top2& y) {
+          top2_merge(x, y);
+          return x;
+        });
+      }
+      if (tid == 0) {
+        sel.cw[0] = ((unsigned long long)__float_as_uint(b.k1) << 32) | (uint32_t)b.t1;
+        sel.cw[1] = ((unsigned long long)__float_as_uint(b.z1) << 32) | __float_as_uint(b.k2);
+        sel.cw[2] = ((unsigned long long)__float_as_uint(zf) << 32) | (uint32_t)status;
+      }
+    }
+    __syncthreads();
+    if ((uint32_t)sel.cw[2] != 0u) return false;
+    b.k1 = __uint_as_float((uint32_t)(sel.cw[0] >> 32));
+    b.t1 = (int32_t)(uint32_t)sel.cw[0];
+    b.z1 = __uint_as_float((uint32_t)(sel.cw[1] >> 32));
+    b.k2 = __uint_as_float((uint32_t)sel.cw[1]);
+    zfin = __uint_as_float((uint32_t)(sel.cw[2] >> 32));
+  } else {
   // exact top-k value: the k_rank-th largest list value inside [k_lo, k_hi)
   float zc12 = pl.zcut1;
   if (pl.k_rank > 0) {
@@ -1054,7 +1201,7 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
   // when the slices listed their full top-k; truncated lists may miss it)
   if (pl.list_mode && zc12 < sh.fshare) return false;
   CDS_TRACE_ROW(2);
-  float zfin = zc12;
+  zfin = zc12;
 
   // exact top-p cut: the largest value v in [a_lo, a_hi) whose cumulative mass
   // (the sure region, plus every list token >= v that survived top-k) reaches
@@ -1130,6 +1277,7 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
         draw);
   }
   block_top2<NT>(b, red);
+  }
   CDS_TRACE_ROW(4);
   if (b.t1 == INT_MAX) return false;
   if (b.k1 - b.k2 > 2.0f * kRaceEps) {
