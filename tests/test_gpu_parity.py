@@ -240,3 +240,29 @@ def test_workspace_reuse_across_calls_and_shapes():
         np.testing.assert_array_equal(x, y)
     ref, _ = run_oracle(small)
     compare(small, r2, ref, label="ws-reuse")
+
+
+def test_second_pass_layouts_agree():
+    """Rows whose cut needs the whole row's histogram race in a second pass:
+    whole-slice tasks when most of the batch is such rows, half-slice tasks
+    (Gumbel terms drawn before the plan) when few are.  The same requests give
+    the same results either way, and match the oracle."""
+    import constrained_decoding_amd as cds
+    b = workloads.c2_decode(B=16, V=40001, salt=21)
+    b.top_k[:] = 0
+    b.min_p[:] = 0
+    b.top_p[:] = np.linspace(0.8, 0.99, 16).astype(np.float32)
+    b.temperature[:] = np.linspace(0.5, 1.3, 16).astype(np.float32)
+    whole = run_gpu(b)                                  # 16 of 16 rows: whole slices
+    assert not pack(b).batch.flags & cds.FLAG_SPLIT_PASS2
+    mixed = workloads.c2_decode(B=16, V=40001, salt=21)
+    mixed.logits[:] = b.logits
+    for f in ("temperature", "top_k", "top_p", "min_p", "seed", "offset"):
+        getattr(mixed, f)[:] = getattr(b, f)
+    mixed.temperature[4:] = 0.0                         # 4 of 16 rows: half slices
+    assert pack(mixed).batch.flags & cds.FLAG_SPLIT_PASS2
+    split = run_gpu(mixed)
+    for x, y in zip(whole, split):
+        np.testing.assert_array_equal(x[:4], y[:4])
+    ref, _ = run_oracle(b, rows=np.arange(16))
+    _report("second-pass layouts", compare(b, whole, ref, rows=np.arange(16), label="layouts"))
