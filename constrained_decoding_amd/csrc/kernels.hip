@@ -1524,7 +1524,11 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
     // above the minimum over waves.
     if (topk_list) {
       const int qw = (kq + NT / 64 - 1) / (NT / 64);
-      if (qw <= 64) {
+      // one maximum per lane keeps the cut tight only while qw is a small
+      // share of the 64 lanes (a low rank among lane maxima lets several
+      // tokens of each lane through, and the row's lists overflow); past 16,
+      // four group maxima per lane
+      if (qw <= 16) {
         st.lb = wave_kth_largest(st.m, qw);
       } else {
         // the maxima of four groups of the lane's chunks: four distinct tokens

@@ -73,7 +73,7 @@ constexpr int NBINS = 560;
 #endif
 constexpr int kScanThreads = CDS_SCAN_THREADS;
 constexpr int kMaxChunks = CDS_MAX_CHUNKS;
-constexpr int64_t kSliceMax = (int64_t)kScanThreads * 4 * kMaxChunks;  // 30720 tokens
+constexpr int64_t kSliceMax = (int64_t)kScanThreads * 4 * kMaxChunks;  // 15360 tokens
 constexpr int kCountShift = 48;   // histogram word: count << 48 | fixed-point mass
 constexpr int UCAP = 4096;        // listed tokens of a row the finisher holds on chip
 constexpr int SCAP = 2048;        // listed tokens one slice can hand over
