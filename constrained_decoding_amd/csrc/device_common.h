@@ -238,14 +238,14 @@ __device__ __forceinline__ void race32(Top2& b, float z, int32_t t, uint32_t x, 
 
 // ---- histogram bins ------------------------------------------------------------
 struct BinGeom {
-  float delta;      // 2^floor(log2(T/8))
+  float delta;      // 2^floor(log2(T/16))
   float inv_delta;  // 1 / delta (exact)
   float c_bin;      // delta * log2(e) / T: exp2((off - 1) * c_bin) = mass vs bin top
 };
 
 __device__ __forceinline__ BinGeom bin_geom(float T) {
   int e;
-  (void)frexpf(T * 0.125f, &e);  // T/8 = f * 2^e, f in [0.5, 1)
+  (void)frexpf(T * 0.0625f, &e);  // T/16 = f * 2^e, f in [0.5, 1)
   BinGeom g;
   g.delta = ldexpf(1.0f, e - 1);
   g.inv_delta = ldexpf(1.0f, 1 - e);

@@ -505,7 +505,7 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
   // HOLD rows: the first slices' histograms are loaded in the slices' own bin
   // frames right away, alongside the heads (the row frame needs the heads)
   constexpr int BPT = (NBINS + NT - 1) / NT;  // bins per thread and slice
-  constexpr int JC = 10;                       // slices per round of loads
+  constexpr int JC = 4;                        // slices per round of loads
   const unsigned long long* gh = a.hist + (int64_t)r * P * NBINS;
   unsigned long long hv[JC][BPT];
   auto load_hist = [&](int j0) {
@@ -1025,24 +1025,29 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
         b.k1 += sh_k;
         b.k2 += sh_k;
       }
-      cnt = sb.ucnt > (uint32_t)SCAP ? (uint32_t)UCAP + 1u : sb.ucnt;
+      // a list past SCAP was not written: the row takes the exact path
+      cnt = sb.ucnt > (uint32_t)SCAP ? (uint32_t)(SCAP * 64 + 1) : sb.ucnt;
       if (pl.list_mode) lcut = __uint_as_float(sb.pad[2]);
     }
     lcut = wave_allreduce(lcut, [](float u, float v) { return fmaxf(u, v); });
     if (tid == 0) sh.fshare = lcut;
     const uint32_t incl = wave_incl_sum(cnt);
-    off[tid + 1] = (int32_t)min(incl, (uint32_t)UCAP + 1u);
+    off[tid + 1] = (int32_t)incl;
     if (tid == 0) off[0] = 0;
   }
   __syncthreads();
   CDS_TRACE_ROW(0);
-  const int n = off[nl];
-  if (n > UCAP) return false;
-  // gather the slices' lists into LDS: every load is issued before any result
-  // is stored; element i = tid + k*NT increases with k, so its slice j (with
-  // off[j] <= i < off[j+1]) is found by a forward scan
-  {
-    constexpr int KG = UCAP / NT;
+  const int n_all = off[nl];
+  if (n_all > SCAP * nl) return false;
+  // gather the slices' lists into LDS: every load of a round is issued before
+  // any result is stored; element i = tid + k*NT of a round increases with k
+  // (and over rounds), so its slice j (with off[j] <= i < off[j+1]) is found
+  // by a forward scan.  Lists longer than the finisher holds are gathered in
+  // rounds keeping only the tokens at or above the row's min-p cut (none below
+  // it can be drawn); the row takes the exact path if even those overflow.
+  int n = n_all;
+  constexpr int KG = UCAP / NT;
+  if (__builtin_expect(n_all <= UCAP, 1)) {
     unsigned long long v[KG];
     int j = 0;
 #pragma unroll
@@ -1054,6 +1059,32 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
 #pragma unroll
     for (int k = 0; k < KG; ++k)
       if (tid + k * NT < n) ul[tid + k * NT] = v[k];
+  } else {
+    if (!(pl.zcut1 > CDS_NEG_INF)) return false;  // nothing to filter by
+    const float zf = pl.zcut1;
+    int j = 0, kept = 0;
+#pragma unroll 1
+    for (int base = 0; base < n_all; base += UCAP) {
+      unsigned long long v[KG];
+#pragma unroll
+      for (int k = 0; k < KG; ++k) {
+        const int i = base + tid + k * NT;
+        while (j + 1 < nl && off[j + 1] <= i) ++j;
+        v[k] = i < n_all ? ld_u64(a.ulist + (l0 + j) * SCAP + (i - off[j])) : 0ull;
+      }
+      uint32_t c = 0u;
+#pragma unroll
+      for (int k = 0; k < KG; ++k) c += (base + tid + k * NT < n_all && ukey_z(v[k]) >= zf) ? 1u : 0u;
+      uint32_t tot;
+      uint32_t pos = block_excl<NT>(c, sel.wt, tot);
+      if (kept + (int)tot > UCAP) return false;  // (uniform)
+#pragma unroll
+      for (int k = 0; k < KG; ++k)
+        if (base + tid + k * NT < n_all && ukey_z(v[k]) >= zf) ul[kept + (int)pos++] = v[k];
+      kept += (int)tot;
+      __syncthreads();  // sel.wt is read again by the next round
+    }
+    n = kept;
   }
   __syncthreads();
 
@@ -1517,7 +1548,7 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
     for (int i = 0; i < E4; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) st.m = fmaxf(st.m, x[i][q]);
-    // top-k rows (q = list_q <= 4 NT): each wave's ceil(q/W)-th largest of the
+    // top-k rows (q = list_q <= 3 NT / 2): each wave's ceil(q/W)-th largest of the
     // lanes' maxima (of the whole lane, or of four groups of its chunks when
     // one value per lane is not enough; W waves).  Every wave has that many tokens
     // at or above its own value, so at least q tokens of the slice lie at or

@@ -57,14 +57,14 @@ struct BiasEntry {
 // chunks of four tokens in registers.
 //
 // Histogram bins are aligned to a power-of-two grid in z: width
-// delta = 2^floor(log2(T/8)), i.e. between 1/16 and 1/8 in s = z/T.  Bin
+// delta = 2^floor(log2(T/16)), i.e. between 1/32 and 1/16 in s = z/T.  Bin
 // index floor(z/delta) and the offset inside the bin are exact fp32
 // operations, bins of different slices line up, and the value range of a bin
 // is exactly [k*delta, (k+1)*delta).  The window holds the NBINS bins below the
 // row maximum (at least 35 units of s); tokens further down can neither win
 // the race (the exponential-race key is bounded, see device_common.h) nor carry
 // mass that matters at the 1e-10 level.
-constexpr int NBINS = 560;
+constexpr int NBINS = 1120;
 #ifndef CDS_SCAN_THREADS
 #define CDS_SCAN_THREADS 256
 #endif
@@ -88,24 +88,29 @@ enum RowClass : uint32_t {
   CLS_GREEDY = 0,  // argmax: the planner answers from the slice summaries
   CLS_RACE = 1,    // no cut: each slice races all its tokens
   CLS_LIST = 2,    // top-k whose lists fit (list_q), or min-p without top-k:
-                   // each
-                   // slice lists a superset of its candidates; the planner
-                   // resolves the row from the lists
-  CLS_HOLD = 3,    // top-p as the only cut, or a larger top-k: the slices wait
-                   // for the row's plan (histogram cuts)
+                   // each slice lists a superset of its candidates; the
+                   // planner resolves the row from the lists
+  CLS_HOLD = 3,    // top-p as the only cut, or a larger top-k: the row's plan
+                   // (histogram cuts) comes first, then a second pass races
 };
 
 // Tokens a slice of a top-k row lists: its own top-q, q = min(k, ceil(2 k/P)
 // + 64), enough for its share of the row's top-k unless that share is far
 // above the average k/P (the row's finisher checks, and falls back).
 // (constexpr: callable from host and device code alike)
+// A slice finds its list cut from its waves' ceil(q/W)-th largest of four
+// group maxima per lane (W waves); past q = 3/8 of the 4*kScanThreads group
+// maxima that cut lets too many tokens through, and the row takes HOLD.  The
+// cut passes up to ~1.5 q tokens of a slice, so a LIST row also needs
+// 1.5 q P <= UCAP (the finisher's capacity).
+constexpr int32_t kListQMax = 3 * kScanThreads / 2;
 constexpr int32_t list_q(int32_t top_k, int32_t P) {
   return top_k < (2 * top_k + P - 1) / P + 64 ? top_k : (2 * top_k + P - 1) / P + 64;
 }
 constexpr RowClass row_class_of(uint32_t flags, int32_t top_k, int32_t P) {
   return (flags & ROW_GREEDY)  ? CLS_GREEDY
-         : (flags & ROW_TOPK)  ? ((int64_t)list_q(top_k, P) * P <= UCAP &&
-                                          list_q(top_k, P) <= 4 * kScanThreads
+         : (flags & ROW_TOPK)  ? (3 * (int64_t)list_q(top_k, P) * P <= 2 * UCAP &&
+                                          list_q(top_k, P) <= kListQMax
                                       ? CLS_LIST : CLS_HOLD)
          : (flags & ROW_MINP)  ? CLS_LIST
          : (flags & ROW_TOPP)  ? CLS_HOLD

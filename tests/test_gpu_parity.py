@@ -266,3 +266,18 @@ def test_second_pass_layouts_agree():
         np.testing.assert_array_equal(x[:4], y[:4])
     ref, _ = run_oracle(b, rows=np.arange(16))
     _report("second-pass layouts", compare(b, whole, ref, rows=np.arange(16), label="layouts"))
+
+
+def test_min_p_lists_longer_than_the_finisher_holds():
+    """At V=200000 (14 slices) a min-p row at high temperature lists more
+    tokens (each slice cuts relative to its own maximum) than the row's
+    finisher holds; the finisher then gathers in rounds, keeping the tokens at
+    or above the row's min-p cut.  Results match the oracle."""
+    b = workloads.c2_decode(B=12, V=200000, salt=23)
+    b.temperature[:] = np.linspace(1.1, 1.3, 12).astype(np.float32)
+    b.top_k[:] = 0
+    b.min_p[:] = 0.05
+    b.top_p[:] = np.array([0.8, 0.95, 1.0] * 4, np.float32)
+    gpu = run_gpu(b)
+    ref, _ = run_oracle(b)
+    _report("long min-p lists", compare(b, gpu, ref, label="long-minp"))
