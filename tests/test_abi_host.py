@@ -186,3 +186,20 @@ def test_sampled_row_list(cds):
 
     buf, b = cds.pack_host(2, 1000, np.zeros(2, np.float32))
     assert b.n_sampled == 0 and b.flags & cds.FLAG_ALL_GREEDY
+
+
+def test_row_classes_follow_list_capacity(cds):
+    """Top-k rows list candidates only while the lists fit the finisher:
+    q = min(k, ceil(2k/P) + 64) <= 384 and 1.5 q P <= 4096 (P = ceil(V/15360)
+    slices); other top-k rows need the row's histogram first (n_hold, listed
+    first in the order).  Top-p as the only cut always needs it."""
+    def holds(V, k, p=1.0):
+        buf, b = cds.pack_host(2, V, np.ones(2, np.float32), top_k=np.full(2, k, np.int32),
+                               top_p=np.full(2, p, np.float32))
+        return b.n_hold
+    assert holds(151936, 1000) == 0     # P=10: q=264, 1.5*264*10 = 3960
+    assert holds(151936, 50) == 0
+    assert holds(32000, 1000) == 2      # P=3: q=731 > 384
+    assert holds(200000, 1000) == 2     # P=14: 1.5*207*14 = 4347 > 4096
+    assert holds(200000, 100) == 0
+    assert holds(151936, 0, 0.9) == 2   # top-p only
