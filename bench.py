@@ -8,8 +8,10 @@ top-p / min-p mixes on the rest), seeded synthetic logits.  Three distinct
 input sets rotate so the 117 MB working set of a step does not stay in the
 256 MB Infinity Cache between steps.
 
-Prints one JSON line (see the design doc for the fields, the roofline definition
-and the cpu_baseline sample).
+Prints one JSON line: metric and value, a roofline object for
+sample_kernel (algorithmic HBM bytes per launch over its HIP-event launch
+time, against 8 TB/s) and a cpu_baseline object (the CPU oracle timed on a
+bounded sample of the same workload).
 """
 import argparse
 import json
@@ -112,8 +114,8 @@ def algorithmic_bytes(batch):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py: this build measures one GPU; --gpus {args.gpus} is not supported "
-              "(the path shards by rows or by vocabulary, see DESIGN.md)", file=sys.stderr)
+        print(f"bench.py: measures one GPU; --gpus {args.gpus} is not supported "
+              "(the path shards by rows or by vocabulary)", file=sys.stderr)
         sys.exit(2)
 
     import torch

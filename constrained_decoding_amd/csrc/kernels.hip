@@ -996,9 +996,7 @@ __device__ __forceinline__ Best exact_rerace(const SampleArgs& a, int r, const P
 // the finisher).  The row's list is gathered from the slices' lists into LDS.
 // Returns false when the row must take the exact path.
 
-// Lists of at most this many tokens are resolved by one wave.
-constexpr int kShortList = 256;
-
+// Lists of at most kShortList tokens are resolved by one wave.
 template <int NT, bool BF16, bool VEC>
 __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, const Plan& pl,
                                            ExactShared<NT>& sh, uint64_t* ul, int32_t* off,

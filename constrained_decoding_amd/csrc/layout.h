@@ -79,11 +79,13 @@ constexpr int UCAP = 4096;        // listed tokens of a row the finisher holds o
 constexpr int SCAP = 2048;        // listed tokens one slice can hand over
 constexpr int kHistDevice = 4096;  // history tokens per row counted on the device
 constexpr int kMaxSlices = 64;
+constexpr int kShortList = 256;   // a row's listed tokens one wave of the finisher resolves
 constexpr int kXcds = 8;          // XCDs of an MI355X (workgroups go round-robin over them)
 constexpr int kMaxRows = 65535;
 
 // How a row's slices work in the sampling kernel.  The host dispatches the rows
-// in the order HOLD, then RACE / LIST, then GREEDY.
+// in the order HOLD, then top-k LIST rows by the length of their lists, then
+// the other RACE and LIST rows, then GREEDY.
 enum RowClass : uint32_t {
   CLS_GREEDY = 0,  // argmax: the planner answers from the slice summaries
   CLS_RACE = 1,    // no cut: each slice races all its tokens
@@ -180,7 +182,8 @@ struct alignas(16) Plan {
 };
 static_assert(sizeof(Plan) == 96, "Plan layout");
 
-// Written back into Plan::path by the finish kernel (diagnostics and tests).
+// Written back into Plan::path by the workgroup that resolved the row
+// (diagnostics and tests).
 enum FinishPath : int32_t {
   PATH_NONE = 0,
   PATH_FAST = 1,       // fp32 race margin decided the winner

@@ -221,7 +221,9 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   std::memcpy(p, rows.data(), sizeof(RowParams) * rows.size());
   // dispatch order: the rows whose last slice has the longest way to go
   // first -- rows whose slices wait for the row's plan, then top-k rows with
-  // long candidate lists -- then the other sampled rows, then the greedy rows
+  // long candidate lists, then top-k rows whose lists are too long for the
+  // finisher's one-wave path -- then the other sampled rows, then the greedy
+  // rows
   std::vector<int32_t> order;
   order.reserve((size_t)B);
   const int P = choose_slices(V);
@@ -229,12 +231,14 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
     const RowParams& q = rows[(size_t)r];
     const RowClass c = row_class_of(q.flags, q.top_k, P);
     if (c == CLS_HOLD) return 0;
-    if (c == CLS_LIST && (q.flags & ROW_TOPK) && !(q.flags & ROW_MINP) &&
-        (int64_t)list_q(q.top_k, P) * P > 1024)
-      return 1;
-    return 2;
+    if (c == CLS_LIST && (q.flags & ROW_TOPK)) {
+      const int64_t n = (int64_t)list_q(q.top_k, P) * P;  // the lists' nominal length
+      if (!(q.flags & ROW_MINP) && n > 1024) return 1;
+      if (n > kShortList) return 2;
+    }
+    return 3;
   };
-  for (int k = 0; k < 3; ++k)
+  for (int k = 0; k < 4; ++k)
     for (int32_t r : sampled)
       if (rank(r) == k) order.push_back(r);
   int32_t n_hold = 0;

@@ -5,7 +5,7 @@
  * cpu_baseline leg of bench.py load this library.  It shares no code, header,
  * table or helper with the HIP path under constrained_decoding_amd/.
  *
- * Sources, cited by page title and section (see the design doc for the handles):
+ * Sources, cited by page title and section:
  *   [SGL] "SGLang 源码完全拆解(十): Sampling、Grammar 与结构化输出"
  *   [VLP] vLLM design document "Logits Processors" (Chinese translation)
  *   [SO]  "04 · 结构化输出: 在采样器上强制合法"

@@ -203,3 +203,19 @@ def test_row_classes_follow_list_capacity(cds):
     assert holds(200000, 1000) == 2     # P=14: 1.5*207*14 = 4347 > 4096
     assert holds(200000, 100) == 0
     assert holds(151936, 0, 0.9) == 2   # top-p only
+
+
+def test_dispatch_order_by_list_length(cds):
+    """Sampled rows go out in the order: rows that need the row's histogram
+    first; top-k rows with long lists (q P > 1024, no min-p); other top-k rows
+    whose lists pass the finisher's one-wave limit (q P > 256); the rest; then
+    the greedy rows -- ascending row index within each group.  V = 151936
+    gives P = 10 slices, so k = 20, 50, 1000 list q P = 200, 500, 2640."""
+    T = np.array([0.8, 0.8, 0.8, 0.8, 0.8, 0.8, 0.0], np.float32)
+    k = np.array([20, 50, 1000, 1000, 0, 0, 0], np.int32)
+    p = np.array([1, 1, 1, 1, 1, 0.9, 1], np.float32)
+    mp = np.array([0, 0, 0, 0.05, 0.05, 0, 0], np.float32)
+    buf, b = cds.pack_host(7, 151936, T, top_k=k, top_p=p, min_p=mp)
+    assert b.n_sampled == 6 and b.n_hold == 1
+    order = np.frombuffer(buf[64 * 7:64 * 7 + 28].tobytes(), "<i4").tolist()
+    assert order == [5, 2, 1, 3, 0, 4, 6]
