@@ -225,7 +225,6 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   // finisher's one-wave path -- then the other sampled rows, then the greedy
   // rows
   std::vector<int32_t> order;
-  order.reserve((size_t)B);
   const int P = choose_slices(V);
   auto rank = [&](int32_t r) {
     const RowParams& q = rows[(size_t)r];
@@ -238,9 +237,14 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
     }
     return 3;
   };
-  for (int k = 0; k < 4; ++k)
-    for (int32_t r : sampled)
-      if (rank(r) == k) order.push_back(r);
+  // within a group, hotter rows first: a flatter distribution lists and races
+  // more tokens at the end
+  order = sampled;
+  std::stable_sort(order.begin(), order.end(), [&](int32_t x, int32_t y) {
+    const int rx = rank(x), ry = rank(y);
+    if (rx != ry) return rx < ry;
+    return rows[(size_t)x].temperature > rows[(size_t)y].temperature;
+  });
   int32_t n_hold = 0;
   while (n_hold < (int32_t)order.size() && rank(order[(size_t)n_hold]) == 0) ++n_hold;
   order.insert(order.end(), greedy_rows.begin(), greedy_rows.end());

@@ -160,13 +160,14 @@ def test_workspace_size_closed_form(cds):
 def test_sampled_row_list(cds):
     """The packed block holds the dispatch order of the rows: the rows that are
     not greedy (T >= 1e-5 and top_k != 1) -- those whose only cut is top-p
-    first -- then the greedy rows, ascending within each group."""
+    first, hotter rows first within a group -- then the greedy rows,
+    ascending."""
     T = np.array([0.0, 0.7, 1e-6, 1.0, 0.9, 0.8], np.float32)
     k = np.array([0, 0, 0, 1, 50, 0], np.int32)
     p = np.array([1, 1, 1, 1, 1, 0.9], np.float32)
     buf, b = cds.pack_host(6, 1000, T, top_k=k, top_p=p)
     assert b.n_sampled == 3
-    order = [5, 1, 4, 0, 2, 3]
+    order = [5, 4, 1, 0, 2, 3]
     assert np.frombuffer(buf[64 * 6:64 * 6 + 24].tobytes(), "<i4").tolist() == order
     # the kernel's task table: 24 task slots (three groups of 8 for B = 6); pass
     # 1 takes the ordered rows, the one top-p-only row (5) gets two pass-2
@@ -209,8 +210,9 @@ def test_dispatch_order_by_list_length(cds):
     """Sampled rows go out in the order: rows that need the row's histogram
     first; top-k rows with long lists (q P > 1024, no min-p); other top-k rows
     whose lists pass the finisher's one-wave limit (q P > 256); the rest; then
-    the greedy rows -- ascending row index within each group.  V = 151936
-    gives P = 10 slices, so k = 20, 50, 1000 list q P = 200, 500, 2640."""
+    the greedy rows; within a group by falling temperature, then by row
+    index.  V = 151936 gives P = 10 slices, so k = 20, 50, 1000 list
+    q P = 200, 500, 2640."""
     T = np.array([0.8, 0.8, 0.8, 0.8, 0.8, 0.8, 0.0], np.float32)
     k = np.array([20, 50, 1000, 1000, 0, 0, 0], np.int32)
     p = np.array([1, 1, 1, 1, 1, 0.9, 1], np.float32)
@@ -219,3 +221,7 @@ def test_dispatch_order_by_list_length(cds):
     assert b.n_sampled == 6 and b.n_hold == 1
     order = np.frombuffer(buf[64 * 7:64 * 7 + 28].tobytes(), "<i4").tolist()
     assert order == [5, 2, 1, 3, 0, 4, 6]
+    # within a group, hotter rows first (ties keep the row order)
+    T2 = np.array([0.5, 1.2, 0.5, 0.9], np.float32)
+    buf, b = cds.pack_host(4, 151936, T2, top_k=np.full(4, 50, np.int32))
+    assert np.frombuffer(buf[64 * 4:64 * 4 + 16].tobytes(), "<i4").tolist() == [1, 3, 0, 2]
