@@ -1156,8 +1156,48 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
         hi = wave_allreduce(hi, mx);
         const double M2 = pl.m_sure + pl.m_mid + F * ((double)mu / kFix);
         const double need = (pl.p * M2 - pl.m_sure) / F * kFix;
-        if (!(need > 0.0) || (double)m_in < need) status = 1;
-        else zf = fmaxf(zf, from_okey(wave_select_mass<KW>(u, wi, need, lo, hi)));
+        if (!(need > 0.0) || (double)m_in < need) {
+          status = 1;
+        } else {
+          // the cut is the key of a boundary entry (wi > 0): with at most 64
+          // such entries, one per lane, each lane sums the weight at or above
+          // its own key and the largest key whose sum reaches need wins (the
+          // same value as the bitwise select, without a cross-lane sum per bit)
+          uint32_t nb = 0u;
+#pragma unroll
+          for (int k = 0; k < KW; ++k) nb += (uint32_t)__popcll(__ballot(wi[k] != 0ull));
+          uint32_t v;
+          if (nb <= 64u) {
+            uint32_t slot0 = 0u;
+#pragma unroll
+            for (int k = 0; k < KW; ++k) {
+              const unsigned long long bm = __ballot(wi[k] != 0ull);
+              if (wi[k]) {
+                const uint32_t s = slot0 + (uint32_t)__popcll(bm & ((1ull << tid) - 1ull));
+                sel.ck[s] = u[k];
+                sel.cw[s] = wi[k];
+              }
+              slot0 += (uint32_t)__popcll(bm);
+            }
+            __builtin_amdgcn_wave_barrier();
+            const bool valid = (uint32_t)tid < nb;
+            const uint32_t uj = valid ? sel.ck[tid] : 0u;
+            const unsigned long long wj = valid ? sel.cw[tid] : 0ull;
+            unsigned long long cum = 0ull;
+#pragma unroll 1
+            for (uint32_t i = 0; i < nb; ++i) {
+              const uint32_t ui = (uint32_t)__builtin_amdgcn_readlane((int)uj, (int)i);
+              const unsigned long long wq = readlane_obj(wj, (int)i);
+              cum += ui >= uj ? wq : 0ull;
+            }
+            v = valid && (double)cum >= need ? uj : 0u;
+            v = wave_allreduce(v, mx);
+            __builtin_amdgcn_wave_barrier();
+          } else {
+            v = wave_select_mass<KW>(u, wi, need, lo, hi);
+          }
+          zf = fmaxf(zf, from_okey(v));
+        }
       }
       if (status == 0) {
         // the race over the survivors, merged with the slices' top two (lanes
