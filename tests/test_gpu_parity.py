@@ -281,3 +281,27 @@ def test_min_p_lists_longer_than_the_finisher_holds():
     gpu = run_gpu(b)
     ref, _ = run_oracle(b)
     _report("long min-p lists", compare(b, gpu, ref, label="long-minp"))
+
+
+def test_one_wave_top_p_select_both_boundary_sizes():
+    """Min-p rows whose lists are a plateau of 40 or 200 tokens well above the
+    rest (so the row's list fits one wave of the finisher), with top-p on top:
+    the top-p cut over at most 64 boundary tokens is taken one token per lane,
+    over more by the bitwise select.  Some plateau values repeat exactly (ties
+    of the cut).  Results match the oracle."""
+    b = workloads.c2_decode(B=8, V=151936, salt=31)
+    rng = np.random.default_rng(31)
+    for r in range(b.B):
+        m = 40 if r % 2 == 0 else 200
+        idx = rng.choice(b.V, size=m, replace=False)
+        top = float(b.logits[r].max()) + 3.0
+        vals = top + rng.uniform(0.0, 0.5, size=m).astype(np.float32)
+        vals[m // 2:m // 2 + 4] = vals[0]  # exact repeats
+        b.logits[r, idx] = vals.astype(np.float32)
+    b.temperature[:] = 1.0
+    b.top_k[:] = 0
+    b.min_p[:] = 0.3
+    b.top_p[:] = np.array([0.5, 0.5, 0.9, 0.9, 0.3, 0.3, 0.99, 0.99], np.float32)
+    gpu = run_gpu(b)
+    ref, _ = run_oracle(b)
+    _report("one-wave top-p select", compare(b, gpu, ref, label="wave-topp"))
