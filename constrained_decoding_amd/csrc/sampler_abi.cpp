@@ -52,11 +52,19 @@ size_t params_bytes_exact(int32_t B, int64_t n_pen, int64_t n_bias) {
 }
 
 // Pass-2 groups follow their pass-1 group after about one generation of
-// resident workgroups (4 per CU on 256 CUs), when the row's plan is likely out.
+// resident workgroups (4 per CU on 256 CUs), when the row's plan is likely out;
+// a quarter generation later when the pass-2 tasks take whole slices (many
+// such rows: their plans come out later, as their slices load together).
 #ifndef CDS_PASS2_LAG_SLOTS
 #define CDS_PASS2_LAG_SLOTS 1024
 #endif
-int pass2_lag(int P) { return std::max(1, (CDS_PASS2_LAG_SLOTS + 8 * P - 1) / (8 * P)); }
+#ifndef CDS_PASS2_LAG_SLOTS_WHOLE
+#define CDS_PASS2_LAG_SLOTS_WHOLE 1280
+#endif
+int pass2_lag(int P, int halves) {
+  const int slots = halves == 2 ? CDS_PASS2_LAG_SLOTS : CDS_PASS2_LAG_SLOTS_WHOLE;
+  return std::max(1, (slots + 8 * P - 1) / (8 * P));
+}
 
 // Validate and pack into host memory: `dst` (cap bytes), or when dst is null
 // into `tmp`.  Everything is validated and sized first, then written once into
@@ -252,8 +260,8 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   std::memset(p + off_list + sizeof(int32_t) * order.size(), 0,
               list_bytes(B) - sizeof(int32_t) * order.size());
   // the task groups: pass-1 group g, and pass-2 group g - lag after it
-  const int32_t G1 = (B + 7) / 8, GH = (n_hold + 7) / 8, lag = pass2_lag(P);
   const int halves = pass2_halves(P, n_hold, B);
+  const int32_t G1 = (B + 7) / 8, GH = (n_hold + 7) / 8, lag = pass2_lag(P, halves);
   if (halves == 2) flags |= SAMPLER_FLAG_SPLIT_PASS2;
   std::vector<std::pair<int, int32_t>> seq;  // (pass: 1, or 2 + half, group)
   auto pass2 = [&](int32_t g) {
