@@ -1,19 +1,25 @@
 """Benchmark of the sampling step on one MI355X.
 
 One step = the whole hot path on one batch: sampler_pack_params (host
-validation + flags + async H2D of the packed parameters), the transforms and
-bitmask when the workload has them, and sampler_sample.  Default workload:
-B=192, V=151936 fp32 decode batch (greedy on a quarter of the rows, top-k /
-top-p / min-p mixes on the rest), seeded synthetic logits.  Three distinct
-input sets rotate so the 117 MB working set of a step does not stay in the
-256 MB Infinity Cache between steps.
+validation + flags + packing + async H2D of the parameter block, on a copy
+stream so that it overlaps the previous step's kernels), the transforms
+kernel when the workload has penalties or bias, and sampler_sample (the
+fused sampling kernel, with the grammar bitmask fused into its loads when the
+workload has one).  Default workload: B=192, V=151936 fp32 decode batch
+(greedy on a quarter of the rows, top-k / top-p / min-p mixes on the rest),
+seeded synthetic logits.  Three distinct input sets rotate so that the 117 MB
+working set of a step does not stay in the 256 MB Infinity Cache between
+steps.
 
-Prints one JSON line: metric and value, a roofline object for
-sample_kernel (algorithmic HBM bytes per launch over its HIP-event launch
-time, against 8 TB/s) and a cpu_baseline object (the CPU oracle timed on a
-bounded sample of the same workload).
+Prints one JSON line: metric and value (rows/s over the whole timed region),
+a roofline object for sample_kernel (algorithmic HBM bytes per launch over
+its HIP-event launch time, against 8 TB/s; median, p10 and p90 of the
+per-launch times; a warm figure from steps that reuse one input set) and a
+cpu_baseline object (the CPU oracle timed on a bounded sample of the same
+workload on all host cores, with the single-thread figure beside it).
 """
 import argparse
+import ctypes as ct
 import json
 import os
 import sys
@@ -26,8 +32,9 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sampled rows/sec and achieved HBM GB/s at B=192, V=151936 fp32 (1 GPU)"
 PEAK_HBM_GBS = 8000.0
-ROW_PARAM_BYTES = 64   # packed per-row record read by the scan kernel
+ROW_PARAM_BYTES = 64   # packed per-row record read by the sampling kernel
 ROW_OUT_BYTES = 12     # id + logprob + status written per row
+MAX_CPU_WORKERS = 16   # the machine's CPU share for one GPU
 
 
 def parse():
@@ -37,6 +44,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--config", default="c2", choices=["c2", "c3", "c4", "c5a", "c5b"])
     ap.add_argument("--sets", type=int, default=3, help="rotating input sets")
+    ap.add_argument("--warm-steps", type=int, default=50,
+                    help="extra steps on one input set (warm Infinity Cache figure)")
     ap.add_argument("--cpu-rows", type=int, default=2304,
                     help="rows of the workload the oracle is timed on (cpu_baseline)")
     ap.add_argument("--no-cpu", action="store_true")
@@ -111,6 +120,65 @@ def algorithmic_bytes(batch):
     return n
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(sets, n_rows):
+    """The oracle as it stands on a bounded sample of the workload: rows taken
+    in order from the rotating input sets, once on one thread and once spread
+    over the host cores (threads: the oracle's C calls release the GIL)."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    B = sets[0].B
+    work = []
+    done = k = 0
+    while done < n_rows:
+        take = min(B, n_rows - done)
+        work.append((k % len(sets), np.arange(take)))
+        done += take
+        k += 1
+    params = [b.oracle_params() for b in sets]
+
+    def run(j, rows):
+        b = sets[j]
+        oracle.pipeline(b.logits, params[j], bf16=b.bf16, masks=b.masks,
+                        row_has_mask=b.row_has_mask, rows=rows)
+
+    oracle.sample_row(np.zeros(4, np.float32), T=1.0)   # load the library first
+    one_rows = max(1, n_rows // 4)                        # single thread: a quarter
+    t0 = time.perf_counter()
+    left = one_rows
+    for j, rows in work:
+        if left <= 0:
+            break
+        run(j, rows[:left])
+        left -= len(rows)
+    t1 = time.perf_counter() - t0
+    workers = max(1, min(MAX_CPU_WORKERS, len(os.sched_getaffinity(0))))
+    chunks = [(j, c) for j, rows in work for c in np.array_split(rows, workers) if len(c)]
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(lambda jc: run(*jc), chunks))
+    tn = time.perf_counter() - t0
+    return {"value": round(done / tn, 3), "unit": "rows/s", "cores": workers, "kind": "oracle",
+            "cpu_model": cpu_model(),
+            "sample": f"{done} rows ({k} steps' worth, rotating the {len(sets)} input sets) "
+                      f"of the same workload, row-parallel over {workers} threads, "
+                      f"{tn:.1f} s",
+            "single_thread": {"value": round(one_rows / t1, 3), "unit": "rows/s", "cores": 1,
+                              "sample": f"the first {one_rows} of those rows, {t1:.1f} s"}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -126,18 +194,10 @@ def main():
         return
 
     import constrained_decoding_amd as cds
+    from constrained_decoding_amd import _binding as bd
     import workloads
 
-    make = workloads.CONFIGS[args.config]
-    sets = []
-    for s in range(args.sets):
-        if args.config in ("c5a", "c5b"):
-            b = make()
-            if s:
-                b.seed = b.seed + np.uint64(s)
-        else:
-            b = make(salt=s)
-        sets.append(b)
+    sets = [workloads.input_set(args.config, s) for s in range(args.sets)]
     b0 = sets[0]
     B, V = b0.B, b0.V
 
@@ -156,9 +216,11 @@ def main():
     outs = (torch.empty(B, dtype=torch.int32, device="cuda"),
             torch.empty(B, dtype=torch.float32, device="cuda"),
             torch.empty(B, dtype=torch.int32, device="cuda"))
-    cds.set_algo(args.algo)
 
-    host_kw = []
+    # Everything a step needs from the host, prepared once per input set: the
+    # host parameter arrays (what a serving loop would hand over each step),
+    # a device parameter block and a pinned staging buffer.
+    host = []
     for b in sets:
         kw = dict(top_k=b.top_k, top_p=b.top_p, min_p=b.min_p, seed=b.seed, offset=b.offset)
         if b.rep is not None:
@@ -166,18 +228,60 @@ def main():
                       presence_penalty=b.pres, hist_indptr=b.hist_indptr, hist_ids=b.hist_ids)
         if b.bias_indptr is not None:
             kw.update(bias_indptr=b.bias_indptr, bias_ids=b.bias_ids, bias_vals=b.bias_vals)
-        host_kw.append(kw)
+        h = bd._HostArrays(B, V, b.temperature, **kw)
+        nbytes = h.bytes_bound()
+        host.append(dict(h=h, nbytes=nbytes,
+                         d_buf=torch.empty(nbytes, dtype=torch.uint8, device="cuda"),
+                         staging=torch.empty(nbytes, dtype=torch.uint8, pin_memory=True),
+                         batch=bd.Batch(), copied=None, used=None))
+    compute = torch.cuda.current_stream()
+    copy_s = torch.cuda.Stream()
+    lib = bd.lib
+    mask_args = [(None, 0, None) if masks[j] is None else
+                 (masks[j].data_ptr(), masks[j].stride(0),
+                  None if rhm[j] is None else rhm[j].data_ptr()) for j in range(len(sets))]
+    dtype = cds.DTYPE_BF16 if b0.bf16 else cds.DTYPE_F32
+    out_ptrs = tuple(t.data_ptr() for t in outs)
+    pack_s = []
 
-    def step(i, ev=None):
-        j = i % len(sets)
-        b = sets[j]
-        pk = cds.PackedBatch(B, V, b.temperature, **host_kw[j])
+    def step(i, ev=None, j=None):
+        j = i % len(sets) if j is None else j
+        hs = host[j]
+        # the staging buffer and the device block are reused: the previous copy
+        # out of the staging buffer must have run, and the previous kernels that
+        # read the device block must be done before the copy overwrites it
+        if hs["copied"] is not None:
+            hs["copied"].synchronize()
+        if hs["used"] is not None:
+            copy_s.wait_event(hs["used"])
+        t0 = time.perf_counter()
+        rc = lib.sampler_pack_params(ct.byref(hs["h"].hp), hs["d_buf"].data_ptr(), hs["nbytes"],
+                                     hs["staging"].data_ptr(), copy_s.cuda_stream,
+                                     ct.byref(hs["batch"]))
+        pack_s.append(time.perf_counter() - t0)
+        if rc != 0:
+            raise cds.SamplerError(rc, "sampler_pack_params")
+        copied = torch.cuda.Event()
+        copied.record(copy_s)
+        hs["copied"] = copied
+        compute.wait_event(copied)
         if transforms:
-            cds.apply_transforms(pk, work[j])
+            rc = lib.sampler_apply_transforms(ct.byref(hs["batch"]), work[j].data_ptr(),
+                                              work[j].stride(0), compute.cuda_stream)
+            if rc != 0:
+                raise cds.SamplerError(rc, "sampler_apply_transforms")
+        mp, mld, rp = mask_args[j]
+        o = bd.Options(size=ct.sizeof(bd.Options), algo=args.algo)
         if ev is not None:
-            cds.time_next(0, ev[0], ev[1])
-        cds.sample(pk, work[j], bitmask=masks[j], row_has_mask=rhm[j], workspace=ws, out=outs)
-        return pk
+            o.start_event, o.stop_event = bd._event_ptr(ev[0]), bd._event_ptr(ev[1])
+        rc = lib.sampler_sample_ex(ct.byref(hs["batch"]), work[j].data_ptr(), dtype,
+                                   work[j].stride(0), mp, mld, rp, *out_ptrs, ws.ptr, ws.nbytes,
+                                   compute.cuda_stream, ct.byref(o))
+        if rc != 0:
+            raise cds.SamplerError(rc, "sampler_sample_ex")
+        used = torch.cuda.Event()
+        used.record(compute)
+        hs["used"] = used
 
     # The transforms write their (few hundred per row) tokens in place, so a
     # step re-applies them to the previous step's output: the same work, on
@@ -185,10 +289,14 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    pack_s.clear()
 
     # timed region: K whole steps, inputs resident in HBM
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
            for _ in range(args.steps)]
+    for e in evs:                      # create the HIP events outside the timed region
+        e[0].record()
+        e[1].record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
@@ -197,34 +305,30 @@ def main():
     t1 = time.perf_counter()
     elapsed = t1 - t0
     ms_per_step = elapsed * 1e3 / args.steps
-    kern_ms = float(np.mean([a.elapsed_time(z) for a, z in evs]))
+    kern = np.array([a.elapsed_time(z) for a, z in evs]) * 1e3   # us
+    host_pack_us = float(np.mean(pack_s)) * 1e6
+
+    # warm figure: the same input set every step (its 117 MB can stay in the
+    # Infinity Cache); reported beside, never as the value
+    warm = None
+    if args.warm_steps > 0:
+        wevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.warm_steps)]
+        for i in range(args.warm_steps):
+            step(i, wevs[i], j=0)
+        torch.cuda.synchronize()
+        warm = float(np.median([a.elapsed_time(z) for a, z in wevs])) * 1e3
 
     alg = algorithmic_bytes(b0)
     scan_bytes = B * V * (2 if b0.bf16 else 4) + B * ROW_PARAM_BYTES
     if b0.masks is not None:
         rows = B if b0.row_has_mask is None else int(b0.row_has_mask.sum())
         scan_bytes += rows * ((V + 31) // 32) * 4
-    achieved = scan_bytes / (kern_ms * 1e-3) / 1e9
+    kern_mean = float(np.mean(kern))
+    achieved = scan_bytes / (kern_mean * 1e-6) / 1e9
     rows_per_s = B * args.steps / elapsed
 
-    cpu = None
-    if not args.no_cpu:
-        import oracle
-        n_rows = args.cpu_rows
-        done = 0
-        t0 = time.perf_counter()
-        k = 0
-        while done < n_rows:
-            b = sets[k % len(sets)]
-            take = min(B, n_rows - done)
-            oracle.pipeline(b.logits, b.oracle_params(), bf16=b.bf16, masks=b.masks,
-                            row_has_mask=b.row_has_mask, rows=range(take))
-            done += take
-            k += 1
-        cpu_s = time.perf_counter() - t0
-        cpu = {"value": round(done / cpu_s, 3), "unit": "rows/s", "cores": 1, "kind": "oracle",
-               "sample": f"{done} rows ({k} steps' worth, rotating the {len(sets)} input sets) "
-                         f"of the same workload, single-threaded, {cpu_s:.1f} s"}
+    cpu = None if args.no_cpu else cpu_baseline(sets, args.cpu_rows)
 
     names = {"c2": "decode B=192 V=151936 fp32, mixed greedy/top-k/top-p/min-p",
              "c3": "penalties+bias B=192 V=151936 fp32, T=0.8 top_p=0.95",
@@ -247,11 +351,16 @@ def main():
         "config": {"workload": names[args.config], "B": B, "V": V, "input_sets": len(sets),
                    "algo": "fast" if args.algo == 0 else "row-exact"},
         "pipeline_gbs": round(alg / (ms_per_step * 1e-3) / 1e9, 1),
+        "host_pack_us": round(host_pack_us, 2),
         "roofline": {"bound": "hbm", "kernel": "sample_kernel", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(args.config),
-                     "kernel_us": round(kern_ms * 1e3, 2), "bytes_per_launch": scan_bytes},
+                     "kernel_us": round(kern_mean, 2),
+                     "kernel_us_p10_p50_p90": [round(float(np.percentile(kern, q)), 2)
+                                               for q in (10, 50, 90)],
+                     "kernel_us_warm_p50": None if warm is None else round(warm, 2),
+                     "bytes_per_launch": scan_bytes},
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)

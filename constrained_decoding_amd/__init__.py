@@ -6,9 +6,9 @@ in hand-written HIP kernels behind the C ABI of libcd_sampler.so
 (include/cd_sampler.h).  This package is the thin Python binding.
 """
 from ._binding import (  # noqa: F401
-    DTYPE_BF16, DTYPE_F32, EXPORTS, FLAG_ALL_GREEDY, FLAG_ANY_GREEDY, FLAG_HAS_BIAS,
+    ALGO_EXACT, ALGO_FAST, DTYPE_BF16, DTYPE_F32, EXPORTS, FLAG_ALL_GREEDY, FLAG_ANY_GREEDY, FLAG_HAS_BIAS,
     FLAG_NEED_MIN_P, FLAG_NEED_PENALTY, FLAG_NEED_TOP_K, FLAG_NEED_TOP_P, FLAG_SPLIT_PASS2, LIB_PATH,
-    STATUS_INVALID, STATUS_OK, STATUS_OVERFLOW, Batch, HostParams, PackedBatch, SamplerError,
-    Workspace, apply_bitmask, apply_transforms, bias_from_dict, csr, lib, pack_host, sample,
-    set_algo, set_trace, strerror, time_next, version,
+    STATUS_INVALID, STATUS_OK, STATUS_OVERFLOW, WAIT_NONE, Batch, HostParams, Options,
+    PackedBatch, SamplerError, Workspace, apply_bitmask, apply_transforms, bias_from_dict, csr,
+    lib, pack_host, sample, strerror, version,
 )

@@ -20,14 +20,14 @@ STATUS_OK, STATUS_OVERFLOW, STATUS_INVALID = 0, 1, 2
 FLAG_ALL_GREEDY, FLAG_ANY_GREEDY = 1 << 0, 1 << 1
 FLAG_NEED_TOP_K, FLAG_NEED_TOP_P, FLAG_NEED_MIN_P = 1 << 2, 1 << 3, 1 << 4
 FLAG_NEED_PENALTY, FLAG_HAS_BIAS, FLAG_SPLIT_PASS2 = 1 << 5, 1 << 6, 1 << 7
-OPT_ALGO = 1
-OPT_TRACE = 2
+ALGO_FAST, ALGO_EXACT = 0, 1
+WAIT_NONE = -1
 
 EXPORTS = [
     "sampler_strerror", "sampler_version", "sampler_params_bytes", "sampler_pack_params",
     "sampler_pack_host", "sampler_apply_transforms", "sampler_apply_bitmask",
     "sampler_workspace_bytes", "sampler_workspace_init", "sampler_sample",
-    "sampler_set_option", "sampler_time_next",
+    "sampler_sample_ex",
 ]
 
 
@@ -49,7 +49,14 @@ class Batch(ct.Structure):
         ("max_top_k", ct.c_int32), ("n_pen", ct.c_int64), ("n_bias", ct.c_int64),
         ("d_rows", ct.c_void_p), ("d_pen", ct.c_void_p), ("d_bias", ct.c_void_p),
         ("bytes", ct.c_size_t), ("n_sampled", ct.c_int32), ("n_hold", ct.c_int32),
-        ("d_sampled", ct.c_void_p),
+        ("d_sampled", ct.c_void_p), ("n_hist_raw", ct.c_int64), ("d_hist_raw", ct.c_void_p),
+    ]
+
+
+class Options(ct.Structure):
+    _fields_ = [
+        ("size", ct.c_uint32), ("algo", ct.c_int32), ("wait_ns", ct.c_int64),
+        ("trace", ct.c_void_p), ("start_event", ct.c_void_p), ("stop_event", ct.c_void_p),
     ]
 
 
@@ -76,8 +83,7 @@ def _load():
         "sampler_workspace_bytes": ([I32, I32], SZ),
         "sampler_workspace_init": ([P, SZ, P], ct.c_int),
         "sampler_sample": ([P, P, ct.c_int, I64, P, I64, P, P, P, P, P, SZ, P], ct.c_int),
-        "sampler_set_option": ([ct.c_int, I64], ct.c_int),
-        "sampler_time_next": ([ct.c_int, P, P], ct.c_int),
+        "sampler_sample_ex": ([P, P, ct.c_int, I64, P, I64, P, P, P, P, P, SZ, P, P], ct.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -280,10 +286,23 @@ def apply_bitmask(logits, bitmask, row_has_mask=None, stream=None):
         _stream_ptr(stream)), "sampler_apply_bitmask")
 
 
+def _event_ptr(e):
+    if e is None:
+        return None
+    if not e.cuda_event:   # torch creates the HIP event on first record
+        e.record()
+    return e.cuda_event
+
+
 def sample(packed: PackedBatch, logits, *, bitmask=None, row_has_mask=None, workspace=None,
-           out=None, stream=None):
+           out=None, stream=None, algo=ALGO_FAST, wait_ns=0, trace=None, events=None):
     """The sampling step.  Returns (ids int32 [B], logprobs float32 [B],
-    status int32 [B]) as device tensors (``out`` may supply them)."""
+    status int32 [B]) as device tensors (``out`` may supply them).
+
+    Per-call options (sampler_sample_ex): ``algo`` ALGO_FAST or ALGO_EXACT;
+    ``wait_ns`` 0 (default wait), WAIT_NONE or nanoseconds; ``trace`` a
+    device int64 tensor for phase timestamps; ``events`` a pair of
+    torch.cuda.Event recorded right around the sampling kernel."""
     import torch
     B, V = logits.shape
     if (B, V) != (packed.B, packed.V):
@@ -298,33 +317,19 @@ def sample(packed: PackedBatch, logits, *, bitmask=None, row_has_mask=None, work
         st = torch.empty(B, dtype=torch.int32, device=logits.device)
     else:
         ids, lp, st = out
-    _check(lib.sampler_sample(
-        ct.byref(packed.batch), logits.data_ptr(), _dtype_code(logits), logits.stride(0),
-        None if bitmask is None else bitmask.data_ptr(),
-        0 if bitmask is None else bitmask.stride(0),
-        None if row_has_mask is None else row_has_mask.data_ptr(),
-        ids.data_ptr(), None if lp is None else lp.data_ptr(),
-        None if st is None else st.data_ptr(), workspace.ptr, workspace.nbytes,
-        _stream_ptr(stream)), "sampler_sample")
+    args = (ct.byref(packed.batch), logits.data_ptr(), _dtype_code(logits), logits.stride(0),
+            None if bitmask is None else bitmask.data_ptr(),
+            0 if bitmask is None else bitmask.stride(0),
+            None if row_has_mask is None else row_has_mask.data_ptr(),
+            ids.data_ptr(), None if lp is None else lp.data_ptr(),
+            None if st is None else st.data_ptr(), workspace.ptr, workspace.nbytes,
+            _stream_ptr(stream))
+    if algo == ALGO_FAST and wait_ns == 0 and trace is None and events is None:
+        _check(lib.sampler_sample(*args), "sampler_sample")
+    else:
+        o = Options(size=ct.sizeof(Options), algo=int(algo), wait_ns=int(wait_ns),
+                    trace=None if trace is None else trace.data_ptr(),
+                    start_event=None if events is None else _event_ptr(events[0]),
+                    stop_event=None if events is None else _event_ptr(events[1]))
+        _check(lib.sampler_sample_ex(*args, ct.byref(o)), "sampler_sample_ex")
     return ids, lp, st
-
-
-def set_algo(algo: int):
-    """0: fast path (default); 1: row-serial exact path for every row."""
-    _check(lib.sampler_set_option(OPT_ALGO, int(algo)), "sampler_set_option")
-
-
-def set_trace(buf=None):
-    """Diagnostic phase timestamps: ``buf`` is a device int64 tensor of 8 words
-    per workgroup of the sampling kernel (see SAMPLER_OPT_TRACE), or None."""
-    _check(lib.sampler_set_option(OPT_TRACE, 0 if buf is None else int(buf.data_ptr())),
-           "sampler_set_option")
-
-
-def time_next(kernel: int, start_event, stop_event):
-    """Record torch.cuda.Event pair around kernel `kernel` of the next sample()."""
-    for e in (start_event, stop_event):
-        if not e.cuda_event:   # torch creates the HIP event on first record
-            e.record()
-    _check(lib.sampler_time_next(int(kernel), start_event.cuda_event, stop_event.cuda_event),
-           "sampler_time_next")

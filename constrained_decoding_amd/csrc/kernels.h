@@ -41,8 +41,9 @@ struct KernelEvents {
   hipEvent_t stop;
 };
 
-hipError_t launch_transforms(const RowParams* rows, const PenEntry* pen, const BiasEntry* bias,
-                             float* logits, int64_t ld, int32_t B, hipStream_t stream);
+hipError_t launch_transforms(const RowParams* rows, const int32_t* hist_raw, const PenEntry* pen,
+                             const BiasEntry* bias, float* logits, int64_t ld, int32_t B,
+                             hipStream_t stream);
 hipError_t launch_bitmask(void* logits, bool bf16, int64_t ld, int32_t B, int32_t V,
                           const int32_t* mask, int64_t mask_ld, const uint8_t* row_has_mask,
                           hipStream_t stream);

@@ -79,7 +79,7 @@ __device__ __forceinline__ float minp_cut(float zmax, double Td, double m, float
 // transforms and bitmask (in place)
 // ============================================================================
 // One workgroup per row.  Raw history rows (ROW_PEN_RAW, at most kHistDevice
-// tokens) are first merged into (token, count) pairs in an LDS hash table with
+// int32 ids) are first merged into (token, count) pairs in an LDS hash table with
 // at least twice as many slots as tokens (linear probing, atomicCAS on the
 // key), so every penalised token is updated exactly once with its full count.
 __device__ __forceinline__ void apply_penalty(float* z, int32_t id, int32_t count,
@@ -92,6 +92,7 @@ __device__ __forceinline__ void apply_penalty(float* z, int32_t id, int32_t coun
 }
 
 __global__ __launch_bounds__(256) void transforms_kernel(const RowParams* rows,
+                                                         const int32_t* hist_raw,
                                                          const PenEntry* pen,
                                                          const BiasEntry* bias, float* logits,
                                                          int64_t ld) {
@@ -112,12 +113,12 @@ __global__ __launch_bounds__(256) void transforms_kernel(const RowParams* rows,
     }
     __syncthreads();
     for (int i = rp.pen_lo + (int)threadIdx.x; i < rp.pen_hi; i += blockDim.x) {
-      const PenEntry e = pen[i];
-      uint32_t h = ((uint32_t)e.id * 0x9E3779B1u) >> (32 - lg);
+      const uint32_t id = (uint32_t)hist_raw[i];
+      uint32_t h = (id * 0x9E3779B1u) >> (32 - lg);
       while (true) {
-        const uint32_t old = atomicCAS(&keys[h], kEmpty, (uint32_t)e.id);
-        if (old == kEmpty || old == (uint32_t)e.id) {
-          atomicAdd(&cnts[h], e.count);
+        const uint32_t old = atomicCAS(&keys[h], kEmpty, id);
+        if (old == kEmpty || old == id) {
+          atomicAdd(&cnts[h], 1);
           break;
         }
         h = (h + 1u) & (ht - 1u);
@@ -440,8 +441,9 @@ __device__ __forceinline__ uint32_t take_ticket(unsigned long long* w) {
 }
 
 // Spin until *p == gen, at most `limit` ticks of the constant-rate wall
-// clock; false on timeout.
+// clock; false on timeout, and at once when limit is 0.
 __device__ __forceinline__ bool gen_wait(const uint32_t* p, uint32_t gen, uint64_t limit) {
+  if (limit == 0) return false;  // the caller asked for no wait at all
   const uint64_t t0 = wall_clock64();
   while (ld_u32(p) != gen) {
     if (wall_clock64() - t0 > limit) return false;
@@ -1610,19 +1612,23 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
       }
     }
     if (cexp != 0.0f && st.m != CDS_NEG_INF) {
-      // exp2(x*c - max*c): one FMA per token; a NaN or +inf token makes the
+      // exp2((x - max) * c): the difference first, so that the rounding of
+      // max * c does not scale every term of the sum alike (that offset would
+      // reach the logprob at low temperatures); a NaN or +inf token makes the
       // sum NaN (or the max +inf), which flags the slice
-      const float mc = st.m * cexp;
+      const float mt = st.m;
 #pragma unroll
       for (int i = 0; i < E4; ++i) {
         float part = 0.0f;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) part += __builtin_amdgcn_exp2f(fmaf(x[i][q], cexp, -mc));
+        for (int q = 0; q < 4; ++q) part += __builtin_amdgcn_exp2f((x[i][q] - mt) * cexp);
         st.s += (double)part;
       }
     }
-    if (cls == CLS_HOLD) {
-      // NaN / +inf check for rows without the sum: a plain sum propagates them
+    if (cls == CLS_HOLD || st.m == CDS_NEG_INF) {
+      // NaN / +inf check where the exp-sum does not run (HOLD rows, and threads
+      // whose values are all -inf: fmaxf passes over a NaN, so a NaN among
+      // masked tokens would otherwise go unseen): a plain sum propagates them
       float sx = 0.0f;
 #pragma unroll
       for (int i = 0; i < E4; ++i)
@@ -2066,10 +2072,11 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CDS_WAVES_PE
 // ============================================================================
 // launchers
 // ============================================================================
-hipError_t launch_transforms(const RowParams* rows, const PenEntry* pen, const BiasEntry* bias,
-                             float* logits, int64_t ld, int32_t B, hipStream_t stream) {
-  hipLaunchKernelGGL(transforms_kernel, dim3(B), dim3(256), 0, stream, rows, pen, bias, logits,
-                     ld);
+hipError_t launch_transforms(const RowParams* rows, const int32_t* hist_raw, const PenEntry* pen,
+                             const BiasEntry* bias, float* logits, int64_t ld, int32_t B,
+                             hipStream_t stream) {
+  hipLaunchKernelGGL(transforms_kernel, dim3(B), dim3(256), 0, stream, rows, hist_raw, pen, bias,
+                     logits, ld);
   return hipGetLastError();
 }
 

@@ -14,8 +14,8 @@ enum RowFlag : uint32_t {
   ROW_TOPP = 1u << 2,    // top_p < 1 on a non-greedy row
   ROW_MINP = 1u << 3,    // min_p > 0 on a non-greedy row
   ROW_PEN = 1u << 4,     // has penalty entries
-  ROW_PEN_RAW = 1u << 6, // its penalty entries are raw history tokens (count 1,
-                         // repeats not merged): the transforms kernel counts them
+  ROW_PEN_RAW = 1u << 6, // its history is raw int32 ids (repeats not merged):
+                         // the transforms kernel counts them
   ROW_BIAS = 1u << 5,    // has bias entries
 };
 
@@ -26,7 +26,8 @@ struct alignas(16) RowParams {
   int32_t top_k;  // effective: 0 when off
   float rep, freq, pres;
   uint32_t flags;  // RowFlag
-  int32_t pen_lo, pen_hi;    // [lo, hi) into the penalty entries
+  int32_t pen_lo, pen_hi;    // [lo, hi) into the raw history ids (ROW_PEN_RAW)
+                             // or into the counted penalty entries
   int32_t bias_lo, bias_hi;  // [lo, hi) into the bias entries
   uint64_t seed;
   uint64_t offset;

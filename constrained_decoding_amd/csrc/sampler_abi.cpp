@@ -21,19 +21,31 @@ namespace {
 constexpr int32_t kMaxV = 1 << 24;
 constexpr int32_t kMaxB = kMaxRows;
 
-std::atomic<int> g_algo{0};
-std::atomic<unsigned long long> g_trace{0ull};  // SAMPLER_OPT_TRACE buffer
-// one-shot kernel timing hook (see sampler_time_next)
-std::atomic<uint32_t> g_gen{0u};  // call generations (see sampler_sample)
-std::atomic<void*> g_ev_start{nullptr};
-std::atomic<void*> g_ev_stop{nullptr};
+std::atomic<uint32_t> g_gen{0u};  // call generations (see sampler_sample_ex)
+
+// Wall-clock rate (kHz) of each device, read once per device: a property of
+// the device, so concurrent first calls store the same value.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_rate_khz[kMaxDevices];
+
+int wall_clock_khz() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 100000;
+  int r = g_rate_khz[dev].load(std::memory_order_relaxed);
+  if (r > 0) return r;
+  if (hipDeviceGetAttribute(&r, hipDeviceAttributeWallClockRate, dev) != hipSuccess || r <= 0)
+    r = 100000;
+  g_rate_khz[dev].store(r, std::memory_order_relaxed);
+  return r;
+}
 
 inline bool finite_f(float x) { return std::isfinite(x); }
 
 // Device parameter block: RowParams[B] | int32 row order [B] (the dispatch order
 // of sampler_sample) | int32 task rows [tasks_max(B)] (the sampling kernel's
-// tasks, see below) | PenEntry[n_pen] | BiasEntry[n_bias]; the int32 arrays
-// are padded to 16 bytes.  (The block stays small: it is copied every step.)
+// tasks, see below) | PenEntry[n_pen] (counted histories) | BiasEntry[n_bias]
+// | int32 raw history ids [n_hist_raw]; the int32 arrays are padded to 16
+// bytes.  (The block stays small: it is copied every step.)
 //
 // Tasks: the sampling kernel runs groups of 8 tasks (one per XCD), each task
 // a row's P slices.  Task k is row task_row[k] & ~(kPass2 | kHalf) (-1:
@@ -46,9 +58,10 @@ size_t list_bytes(int32_t B) { return ((size_t)B * sizeof(int32_t) + 15) / 16 * 
 int32_t tasks_max(int32_t B) { return 24 * ((B + 7) / 8); }  // pass 1 + two pass-2 halves
 size_t task_bytes(int32_t B) { return list_bytes(tasks_max(B)); }
 
-size_t params_bytes_exact(int32_t B, int64_t n_pen, int64_t n_bias) {
+size_t params_bytes_exact(int32_t B, int64_t n_pen, int64_t n_bias, int64_t n_raw) {
   return sizeof(RowParams) * (size_t)B + list_bytes(B) + task_bytes(B) +
-         sizeof(PenEntry) * (size_t)n_pen + sizeof(BiasEntry) * (size_t)n_bias;
+         sizeof(PenEntry) * (size_t)n_pen + sizeof(BiasEntry) * (size_t)n_bias +
+         list_bytes((int32_t)n_raw);
 }
 
 // Pass-2 groups follow their pass-1 group after about one generation of
@@ -81,13 +94,13 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
       (h->bias_ids == nullptr) != (h->bias_vals == nullptr))
     return SAMPLER_EINVAL;
 
-  // CSR structure
+  // CSR structure (the ids themselves are range-checked where they are
+  // copied or counted below, before anything reaches the device)
   if (h->hist_indptr) {
     if (h->hist_indptr[0] != 0) return SAMPLER_EINVAL;
     for (int32_t r = 0; r < B; ++r)
       if (h->hist_indptr[r + 1] < h->hist_indptr[r]) return SAMPLER_EINVAL;
-    for (int64_t i = 0; i < h->hist_indptr[B]; ++i)
-      if (h->hist_ids[i] < 0 || h->hist_ids[i] >= V) return SAMPLER_EINVAL;
+    if (h->hist_indptr[B] > (int64_t)INT32_MAX) return SAMPLER_ERANGE;
   }
   if (h->bias_indptr) {
     if (h->bias_indptr[0] != 0) return SAMPLER_EINVAL;
@@ -102,11 +115,11 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
 
   std::vector<RowParams> rows((size_t)B);
   std::vector<int32_t> sampled, greedy_rows;
-  // Penalty entries: rows of up to kHistDevice history tokens are written
-  // later straight from hist_ids (count 1 each); only longer rows are counted
-  // here, into `pen`.  n_pen counts both.
+  // Penalties: rows of up to kHistDevice history tokens go to the device as
+  // raw ids (copied later straight from hist_ids, n_raw in all; the transforms
+  // kernel counts them); only longer rows are counted here, into `pen`.
   std::vector<PenEntry> pen;
-  int64_t n_pen = 0;
+  int64_t n_raw = 0;
   std::vector<BiasEntry> bias;
   if (h->bias_indptr) bias.reserve((size_t)h->bias_indptr[B]);
   uint32_t flags = SAMPLER_FLAG_ALL_GREEDY;
@@ -165,30 +178,42 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
       }
     }
 
-    // penalties: (token, count) from the row's history
-    if (n_pen > (int64_t)INT32_MAX) return SAMPLER_ERANGE;
-    rp.pen_lo = rp.pen_hi = (int32_t)n_pen;
+    // penalties: the row's history, raw (counted on the device) or as
+    // (token, count) entries; pen_lo / pen_hi index the raw ids or the entries
     const bool pen_active = (rep != 1.0f) || (fr != 0.0f) || (pr != 0.0f);
+    if (h->hist_indptr && !pen_active) {
+      // an unused history is still checked: any id outside [0, V) is rejected
+      const int64_t lo = h->hist_indptr[r], hi = h->hist_indptr[r + 1];
+      int32_t mn = 0, mx = 0;
+      for (int64_t i = lo; i < hi; ++i) {
+        mn = std::min(mn, h->hist_ids[i]);
+        mx = std::max(mx, h->hist_ids[i]);
+      }
+      if (mn < 0 || mx >= V) return SAMPLER_EINVAL;
+    }
     if (h->hist_indptr && pen_active) {
       const int64_t lo = h->hist_indptr[r], hi = h->hist_indptr[r + 1];
       if (hi > lo) {
         if (hi - lo <= kHistDevice) {
           // as they come: the transforms kernel merges repeats
-          n_pen += hi - lo;
+          rp.pen_lo = (int32_t)n_raw;
+          n_raw += hi - lo;
+          rp.pen_hi = (int32_t)n_raw;
           rp.flags |= ROW_PEN_RAW;
         } else {
+          rp.pen_lo = (int32_t)pen.size();
           scratch_ids.assign(h->hist_ids + lo, h->hist_ids + hi);
+          for (const int32_t id : scratch_ids)
+            if (id < 0 || id >= V) return SAMPLER_EINVAL;
           std::sort(scratch_ids.begin(), scratch_ids.end());
           for (size_t i = 0; i < scratch_ids.size();) {
             size_t j = i;
             while (j < scratch_ids.size() && scratch_ids[j] == scratch_ids[i]) ++j;
             pen.push_back(PenEntry{scratch_ids[i], (int32_t)(j - i)});
-            ++n_pen;
             i = j;
           }
+          rp.pen_hi = (int32_t)pen.size();
         }
-        if (n_pen > (int64_t)INT32_MAX) return SAMPLER_ERANGE;
-        rp.pen_hi = (int32_t)n_pen;
         rp.flags |= ROW_PEN;
         flags |= SAMPLER_FLAG_NEED_PENALTY;
       }
@@ -198,13 +223,24 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
     if (h->bias_indptr) {
       const int64_t lo = h->bias_indptr[r], hi = h->bias_indptr[r + 1];
       if (hi > lo) {
-        scratch_bias.clear();
-        for (int64_t i = lo; i < hi; ++i) scratch_bias.emplace_back(h->bias_ids[i], i);
-        std::sort(scratch_bias.begin(), scratch_bias.end());
-        for (size_t i = 0; i < scratch_bias.size(); ++i) {
-          if (i + 1 < scratch_bias.size() && scratch_bias[i + 1].first == scratch_bias[i].first)
-            continue;  // a later duplicate follows
-          bias.push_back(BiasEntry{scratch_bias[i].first, h->bias_vals[scratch_bias[i].second]});
+        if (hi - lo <= 32) {
+          // short rows (the usual case): an entry survives unless a later one
+          // names the same token; survivors keep their order
+          for (int64_t i = lo; i < hi; ++i) {
+            const int32_t id = h->bias_ids[i];
+            bool later = false;
+            for (int64_t j = i + 1; j < hi; ++j) later |= h->bias_ids[j] == id;
+            if (!later) bias.push_back(BiasEntry{id, h->bias_vals[i]});
+          }
+        } else {
+          scratch_bias.clear();
+          for (int64_t i = lo; i < hi; ++i) scratch_bias.emplace_back(h->bias_ids[i], i);
+          std::sort(scratch_bias.begin(), scratch_bias.end());
+          for (size_t i = 0; i < scratch_bias.size(); ++i) {
+            if (i + 1 < scratch_bias.size() && scratch_bias[i + 1].first == scratch_bias[i].first)
+              continue;  // a later duplicate follows
+            bias.push_back(BiasEntry{scratch_bias[i].first, h->bias_vals[scratch_bias[i].second]});
+          }
         }
         rp.bias_hi = (int32_t)bias.size();
         rp.flags |= ROW_BIAS;
@@ -215,7 +251,8 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   }
   if (bias.size() > (size_t)INT32_MAX) return SAMPLER_ERANGE;
 
-  const size_t bytes = params_bytes_exact(B, n_pen, (int64_t)bias.size());
+  const int64_t n_pen = (int64_t)pen.size();
+  const size_t bytes = params_bytes_exact(B, n_pen, (int64_t)bias.size(), n_raw);
   unsigned char* p = dst;
   if (!p) {
     tmp->resize(bytes);
@@ -284,24 +321,41 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
                                 (seq[q].first >= 2 && halves == 2 ? kSplit : 0) |
                                 (seq[q].first == 3 ? kHalf : 0);
     }
-  // penalty entries in row order: raw rows straight from hist_ids, counted
-  // rows from `pen`
-  PenEntry* pe = reinterpret_cast<PenEntry*>(p + off_pen);
-  size_t counted = 0;
-  for (int32_t r = 0; r < B; ++r) {
-    const RowParams& rp = rows[(size_t)r];
-    if (!(rp.flags & ROW_PEN)) continue;
-    if (rp.flags & ROW_PEN_RAW) {
-      const int32_t* ids = h->hist_ids + h->hist_indptr[r];
-      for (int32_t i = 0; i < rp.pen_hi - rp.pen_lo; ++i) pe[rp.pen_lo + i] = PenEntry{ids[i], 1};
-    } else {
-      std::memcpy(pe + rp.pen_lo, pen.data() + counted,
-                  sizeof(PenEntry) * (size_t)(rp.pen_hi - rp.pen_lo));
-      counted += (size_t)(rp.pen_hi - rp.pen_lo);
-    }
-  }
+  // counted penalty entries, the bias, then the raw history ids in row order
+  // (runs of consecutive raw rows are one copy each: their CSR ranges adjoin)
+  std::memcpy(p + off_pen, pen.data(), sizeof(PenEntry) * pen.size());
   std::memcpy(p + off_pen + sizeof(PenEntry) * (size_t)n_pen, bias.data(),
               sizeof(BiasEntry) * bias.size());
+  const size_t off_raw = off_pen + sizeof(PenEntry) * (size_t)n_pen +
+                         sizeof(BiasEntry) * bias.size();
+  int32_t* raw = reinterpret_cast<int32_t*>(p + off_raw);
+  for (int32_t r = 0; r < B;) {
+    if (!(rows[(size_t)r].flags & ROW_PEN_RAW)) {
+      ++r;
+      continue;
+    }
+    int32_t e = r + 1;
+    while (e < B && (rows[(size_t)e].flags & ROW_PEN_RAW) &&
+           rows[(size_t)e].pen_lo == rows[(size_t)(e - 1)].pen_hi &&
+           h->hist_indptr[e] == h->hist_indptr[e - 1] + (rows[(size_t)(e - 1)].pen_hi -
+                                                         rows[(size_t)(e - 1)].pen_lo))
+      ++e;
+    // copy and range-check in one pass (min / max, no branch per id)
+    const int32_t n = rows[(size_t)(e - 1)].pen_hi - rows[(size_t)r].pen_lo;
+    const int32_t* src = h->hist_ids + h->hist_indptr[r];
+    int32_t* dstp = raw + rows[(size_t)r].pen_lo;
+    int32_t mn = src[0], mx = src[0];
+    for (int32_t i = 0; i < n; ++i) {
+      const int32_t v = src[i];
+      dstp[i] = v;
+      mn = std::min(mn, v);
+      mx = std::max(mx, v);
+    }
+    if (mn < 0 || mx >= V) return SAMPLER_EINVAL;
+    r = e;
+  }
+  std::memset(reinterpret_cast<unsigned char*>(raw + n_raw), 0,
+              list_bytes((int32_t)n_raw) - sizeof(int32_t) * (size_t)n_raw);
 
   std::memset(out, 0, sizeof *out);
   out->B = B;
@@ -310,6 +364,7 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   out->max_top_k = ((flags & SAMPLER_FLAG_ALL_GREEDY) || !all_nongreedy_have_k) ? 0 : max_k;
   out->n_pen = n_pen;
   out->n_bias = (int64_t)bias.size();
+  out->n_hist_raw = n_raw;
   out->bytes = bytes;
   out->n_sampled = (int32_t)sampled.size();
   out->n_hold = n_hold;
@@ -324,6 +379,8 @@ void set_pointers(sampler_batch* out, const void* base) {
   out->d_sampled = b + off_list;
   out->d_pen = b + off_pen;
   out->d_bias = b + off_pen + sizeof(PenEntry) * (size_t)out->n_pen;
+  out->d_hist_raw = b + off_pen + sizeof(PenEntry) * (size_t)out->n_pen +
+                    sizeof(BiasEntry) * (size_t)out->n_bias;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -348,7 +405,8 @@ const char* sampler_version(void) { return "cd_sampler 0.1 (gfx950)"; }
 
 size_t sampler_params_bytes(int32_t B, int64_t n_hist, int64_t n_bias) {
   if (B < 0 || n_hist < 0 || n_bias < 0) return 0;
-  return params_bytes_exact(B, n_hist, n_bias);
+  // a history id takes 8 bytes at most (a counted entry) and 4 at least
+  return params_bytes_exact(B, n_hist, n_bias, 0) + 16;
 }
 
 int sampler_pack_host(const sampler_host_params* h, void* host_buf, size_t bytes,
@@ -390,7 +448,8 @@ int sampler_apply_transforms(const sampler_batch* b, float* logits, int64_t ld, 
   if (!aligned(logits, 4)) return SAMPLER_EINVAL;
   if (!(b->flags & (SAMPLER_FLAG_NEED_PENALTY | SAMPLER_FLAG_HAS_BIAS))) return SAMPLER_OK;
   const hipError_t e = launch_transforms(
-      static_cast<const RowParams*>(b->d_rows), static_cast<const PenEntry*>(b->d_pen),
+      static_cast<const RowParams*>(b->d_rows), static_cast<const int32_t*>(b->d_hist_raw),
+      static_cast<const PenEntry*>(b->d_pen),
       static_cast<const BiasEntry*>(b->d_bias), logits, ld, b->B,
       static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SAMPLER_OK : SAMPLER_EHIP;
@@ -419,10 +478,19 @@ int sampler_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
   return e == hipSuccess ? SAMPLER_OK : SAMPLER_EHIP;
 }
 
-int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_t ld,
-                   const int32_t* bitmask, int64_t mask_ld, const uint8_t* row_has_mask,
-                   int32_t* out_ids, float* out_logprobs, int32_t* out_status, void* workspace,
-                   size_t ws_bytes, void* stream) {
+int sampler_sample_ex(const sampler_batch* b, const void* logits, int dtype, int64_t ld,
+                      const int32_t* bitmask, int64_t mask_ld, const uint8_t* row_has_mask,
+                      int32_t* out_ids, float* out_logprobs, int32_t* out_status,
+                      void* workspace, size_t ws_bytes, void* stream,
+                      const sampler_options* opt) {
+  sampler_options o;
+  std::memset(&o, 0, sizeof o);
+  if (opt) {
+    if (opt->size != sizeof(sampler_options)) return SAMPLER_EINVAL;
+    o = *opt;
+  }
+  if (o.algo != SAMPLER_ALGO_FAST && o.algo != SAMPLER_ALGO_EXACT) return SAMPLER_EINVAL;
+  if (o.wait_ns < 0 && o.wait_ns != SAMPLER_WAIT_NONE) return SAMPLER_EINVAL;
   if (!b || !logits || !out_ids || !b->d_rows) return SAMPLER_EINVAL;
   const int32_t B = b->B, V = b->V;
   if (B <= 0 || V <= 0 || ld < V) return SAMPLER_EINVAL;
@@ -467,52 +535,40 @@ int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_
   // 16-byte vector loads need every row start (and the base) 16-byte aligned
   const size_t elem = bf16 ? 2 : 4;
   const bool vec = aligned(logits, 4 * elem) && (ld % 4 == 0) && (V % 4 == 0);
-  int algo = g_algo.load();
-  if (L.S > kSliceMax) algo = 1;  // slices beyond the register-resident size
+  int algo = o.algo;
+  if (L.S > kSliceMax) algo = SAMPLER_ALGO_EXACT;  // slices beyond the register-resident size
 
-  // A slice waits at most ~5 ms of wall clock for its row's plan (then the
-  // row takes the exact path); the wall clock's rate is a device attribute.
-  int dev = 0, rate_khz = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&rate_khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess ||
-      rate_khz <= 0)
-    rate_khz = 100000;
-  a.spin_limit = (uint64_t)rate_khz * 5u;
-  // Generation of this call: tags the workspace's row counters, so counters
-  // left by any earlier call read as zero.  Never 0 (a zeroed workspace).
+  // A slice waits at most wait_ns (default 5 ms) of wall clock for its row's
+  // plan, then the row takes the exact path; 0 ticks = no wait at all.
+  const int64_t wait_ns = o.wait_ns == 0 ? 5000000 : (o.wait_ns < 0 ? 0 : o.wait_ns);
+  a.spin_limit = wait_ns == 0 ? 0u
+                              : std::max<uint64_t>(1u, (uint64_t)wait_ns * (uint64_t)wall_clock_khz() /
+                                                           1000000u);
+  // Generation of this call: the plan-ready and wait-failed flags hold the
+  // generation that set them, so a flag left by an earlier call never reads
+  // as set.  Never 0 (a zeroed workspace).  (The arrival / done tickets are
+  // plain counters that the last slice of each row resets: a workspace must
+  // be zero before its first call, sampler_workspace_init.)
   uint32_t gen = g_gen.fetch_add(1u) + 1u;
   if (gen == 0u) gen = g_gen.fetch_add(1u) + 1u;
   a.gen = gen;
-  a.trace = reinterpret_cast<unsigned long long*>(g_trace.load());
+  a.trace = static_cast<unsigned long long*>(o.trace);
 
   KernelEvents ev;
-  ev.start = static_cast<hipEvent_t>(g_ev_start.exchange(nullptr));
-  ev.stop = static_cast<hipEvent_t>(g_ev_stop.exchange(nullptr));
+  ev.start = static_cast<hipEvent_t>(o.start_event);
+  ev.stop = static_cast<hipEvent_t>(o.stop_event);
   const bool have_ev = ev.start || ev.stop;
   const hipError_t e = launch_sample(a, bf16, vec, algo, have_ev ? &ev : nullptr,
                                      static_cast<hipStream_t>(stream));
   return e == hipSuccess ? SAMPLER_OK : SAMPLER_EHIP;
 }
 
-int sampler_set_option(int option, int64_t value) {
-  if (option == SAMPLER_OPT_ALGO) {
-    if (value != 0 && value != 1) return SAMPLER_EINVAL;
-    g_algo.store((int)value);
-    return SAMPLER_OK;
-  }
-  if (option == SAMPLER_OPT_TRACE) {
-    if (value < 0) return SAMPLER_EINVAL;
-    g_trace.store((unsigned long long)value);
-    return SAMPLER_OK;
-  }
-  return SAMPLER_EINVAL;
-}
-
-int sampler_time_next(int kernel, void* start_event, void* stop_event) {
-  if (kernel != 0) return SAMPLER_EINVAL;
-  g_ev_start.store(start_event);
-  g_ev_stop.store(stop_event);
-  return SAMPLER_OK;
+int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_t ld,
+                   const int32_t* bitmask, int64_t mask_ld, const uint8_t* row_has_mask,
+                   int32_t* out_ids, float* out_logprobs, int32_t* out_status, void* workspace,
+                   size_t ws_bytes, void* stream) {
+  return sampler_sample_ex(b, logits, dtype, ld, bitmask, mask_ld, row_has_mask, out_ids,
+                           out_logprobs, out_status, workspace, ws_bytes, stream, nullptr);
 }
 
 }  // extern "C"

@@ -24,14 +24,16 @@
  *     sampler_strerror() describes it.  Nothing throws across the ABI.
  *   - "dev" pointers are device memory, "host" pointers host memory.  All
  *     device memory is allocated and owned by the caller; the library keeps
- *     no device allocation and no mutable global state (except the optional
- *     one-shot timing hook below), so calls on different streams and
- *     workspaces may run concurrently.
+ *     no device allocation.  Its only process-wide state is an atomic call
+ *     counter and a per-device cache of the device wall-clock rate, so calls
+ *     on different streams and workspaces may run concurrently from any
+ *     threads.  Calls that share a workspace must not overlap.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     No call synchronises the stream, except sampler_pack_params without a
  *     staging buffer (documented there).  Device inputs must stay alive and
  *     unmodified until the stream reaches the call.
- *   - A call that returns an error has launched nothing and written nothing.
+ *   - A call that returns an error has launched nothing and written no
+ *     device memory (a caller's host staging buffer may hold partial data).
  *   - Data-dependent failures never return an error: they come back per row
  *     in out_status (OK=0 < OVERFLOW=1 < INVALID=2, ordered by severity as
  *     [SGL] "LogitsProcessorOutput" orders its mask statuses).
@@ -136,7 +138,8 @@ typedef struct sampler_batch {
   uint32_t flags;       /* SAMPLER_FLAG_*                                      */
   int32_t max_top_k;    /* max top_k over non-greedy rows if every one of them
                            has 1 < top_k < V, else 0 ([SGL] "max_top_k")      */
-  int64_t n_pen;        /* packed (token, count) penalty entries             */
+  int64_t n_pen;        /* packed (token, count) penalty entries (histories
+                           longer than 4096 tokens, counted on the host)    */
   int64_t n_bias;       /* packed (token, value) bias entries after dedup    */
   const void *d_rows;   /* dev: per-row records inside the caller's d_buf    */
   const void *d_pen;    /* dev: penalty entries inside d_buf                 */
@@ -156,6 +159,9 @@ typedef struct sampler_batch {
                             ascending within each group.  The sampling
                             kernel's task table follows it (after the order
                             padded to 16 bytes)                             */
+  int64_t n_hist_raw;   /* raw history ids (histories of up to 4096 tokens,
+                           counted on the device by the transforms kernel)  */
+  const void *d_hist_raw; /* dev: int32 raw history ids inside d_buf        */
 } sampler_batch;
 
 /* Message for a SAMPLER_* return code (static storage). */
@@ -169,10 +175,10 @@ const char *sampler_version(void);
 size_t sampler_params_bytes(int32_t B, int64_t n_hist, int64_t n_bias);
 
 /* Validate `h`, compute the batch flags and max_top_k, pack each row's
- * history as (token, count) entries (rows of up to 4096 history tokens as
- * they come, count 1 each, counted on the device by sampler_apply_transforms;
- * longer rows counted here), deduplicate the bias, and copy the
- * packed block to d_buf (dev, >= sampler_params_bytes(...) bytes) on
+ * history (rows of up to 4096 history tokens as raw int32 ids, counted on
+ * the device by sampler_apply_transforms; longer rows as (token, count)
+ * entries counted here), deduplicate the bias, and copy the packed block to
+ * d_buf (dev, >= sampler_params_bytes(...) bytes) on
  * `stream`.  h_staging: pinned host memory of >= the same size used as the
  * copy source (it must stay untouched until the copy has run), or NULL:
  * then the call copies from a temporary host buffer and synchronises
@@ -259,31 +265,51 @@ int sampler_sample(const sampler_batch *b, const void *logits, int dtype,
                    float *out_logprobs, int32_t *out_status, void *workspace,
                    size_t ws_bytes, void *stream);
 
-/* ---- options and instrumentation ------------------------------------------
- * sampler_set_option(SAMPLER_OPT_ALGO, v): 0 = fast path (default),
- * 1 = the row-serial exact path for every row (one workgroup per row, many
- * passes; used to test the fast path and the fallback it takes for rows whose
- * boundary sets do not fit on chip).  Process-wide; not for concurrent use.
- *
- * sampler_set_option(SAMPLER_OPT_TRACE, ptr): diagnostic phase timestamps.
- * ptr = 0 turns it off (default); otherwise ptr is the device address of a
- * caller-owned uint64 buffer of 8 words per workgroup of the sampling kernel
- * (8 * (ceil(B/8) + 2 * ceil(n_hold/8)) * P workgroups, P = slices per row, at
- * most 64; never more than 24 * ceil(B/8) * P), which every later sampler_sample
- * call overwrites: word 0 = row | slice << 20 | class << 28 | planner << 31
- * (class 4: a pass-2 task), words 1..7 = the 100 MHz device wall clock at the start, after
- * the slice maximum, after the summary pass, after the class work, after the
- * arrival ticket, after the plan (or the wait for it), and at the end.
- * Process-wide; not for concurrent use.
- *
- * sampler_time_next(0, start, stop): on the next sampler_sample call, record
- * hipEvent_t `start` / `stop` (passed as void*) on the call's stream right
- * before and after its sampling kernel.  One-shot; used by the benchmark to
- * time the kernel.  Any other first argument -> EINVAL. */
-#define SAMPLER_OPT_ALGO 1
-#define SAMPLER_OPT_TRACE 2
-int sampler_set_option(int option, int64_t value);
-int sampler_time_next(int kernel, void *start_event, void *stop_event);
+/* ---- per-call options -----------------------------------------------------
+ * sampler_sample_ex is sampler_sample with a per-call options record; every
+ * option belongs to that one call (nothing is kept between calls).
+ * opt == NULL, or all fields zero: the same call as sampler_sample.
+ *   size        sizeof(sampler_options) as the caller compiled it (a record of
+ *               another size -> SAMPLER_EINVAL).
+ *   algo        SAMPLER_ALGO_FAST (0): the fused kernel; SAMPLER_ALGO_EXACT
+ *               (1): the row-serial exact path for every row (one workgroup
+ *               per row, several passes; the fallback the fast path takes for
+ *               rows whose boundary sets do not fit on chip).  Same results.
+ *   wait_ns     how long a workgroup that needs its row's plan waits for it
+ *               before the row falls back to the exact path, in nanoseconds:
+ *               0 = the default (5 ms); SAMPLER_WAIT_NONE (-1) = no wait at
+ *               all (every such row takes the exact path; used to exercise
+ *               that path); other negative values -> SAMPLER_EINVAL.
+ *   trace       dev uint64 buffer or NULL: diagnostic phase timestamps, 8
+ *               words per workgroup of the sampling kernel (8 * (ceil(B/8) +
+ *               2 * ceil(n_hold/8)) * P workgroups, P = slices per row, at
+ *               most 64; never more than 24 * ceil(B/8) * P): word 0 = row |
+ *               slice << 20 | class << 28 | planner << 31 (class 4: a pass-2
+ *               task), words 1..7 = the 100 MHz device wall clock at the
+ *               start, after the slice maximum, after the summary pass, after
+ *               the class work, after the arrival ticket, after the plan (or
+ *               the wait for it), and at the end.
+ *   start_event, stop_event  hipEvent_t (as void*) or NULL: recorded on the
+ *               call's stream right before and after the sampling kernel.
+ * -------------------------------------------------------------------------- */
+#define SAMPLER_ALGO_FAST 0
+#define SAMPLER_ALGO_EXACT 1
+#define SAMPLER_WAIT_NONE (-1)
+typedef struct sampler_options {
+  uint32_t size;
+  int32_t algo;
+  int64_t wait_ns;
+  void *trace;
+  void *start_event;
+  void *stop_event;
+} sampler_options;
+
+int sampler_sample_ex(const sampler_batch *b, const void *logits, int dtype,
+                      int64_t ld, const int32_t *bitmask, int64_t mask_ld,
+                      const uint8_t *row_has_mask, int32_t *out_ids,
+                      float *out_logprobs, int32_t *out_status,
+                      void *workspace, size_t ws_bytes, void *stream,
+                      const sampler_options *opt);
 
 #ifdef __cplusplus
 }

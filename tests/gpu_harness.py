@@ -31,38 +31,70 @@ def pack(batch: workloads.Batch, stream=None):
 
 
 def run_gpu(batch: workloads.Batch, *, algo=0, fused_mask=True, logits=None, packed=None,
-            workspace=None, return_logits=False):
+            workspace=None, return_logits=False, wait_ns=0):
     """Full step on the GPU: pack -> transforms -> (mask) -> sample."""
     import torch
     import constrained_decoding_amd as cds
-    cds.set_algo(algo)
-    try:
-        x = to_device(batch) if logits is None else logits
-        pk = pack(batch) if packed is None else packed
-        if batch.rep is not None or batch.bias_indptr is not None:
-            cds.apply_transforms(pk, x)
-        mask = rhm = None
-        if batch.masks is not None:
-            mask = torch.from_numpy(batch.masks).cuda()
-            rhm = None if batch.row_has_mask is None else \
-                torch.from_numpy(batch.row_has_mask.astype(np.uint8)).cuda()
-            if not fused_mask:
-                cds.apply_bitmask(x, mask, rhm)
-                mask = rhm = None
-        ids, lp, st = cds.sample(pk, x, bitmask=mask, row_has_mask=rhm, workspace=workspace)
-        torch.cuda.synchronize()
-        out = (ids.cpu().numpy(), lp.cpu().numpy(), st.cpu().numpy())
-        if return_logits:
-            return out, x
-        return out
-    finally:
-        cds.set_algo(0)
+    x = to_device(batch) if logits is None else logits
+    pk = pack(batch) if packed is None else packed
+    if batch.rep is not None or batch.bias_indptr is not None:
+        cds.apply_transforms(pk, x)
+    mask = rhm = None
+    if batch.masks is not None:
+        mask = torch.from_numpy(batch.masks).cuda()
+        rhm = None if batch.row_has_mask is None else \
+            torch.from_numpy(batch.row_has_mask.astype(np.uint8)).cuda()
+        if not fused_mask:
+            cds.apply_bitmask(x, mask, rhm)
+            mask = rhm = None
+    ids, lp, st = cds.sample(pk, x, bitmask=mask, row_has_mask=rhm, workspace=workspace,
+                             algo=algo, wait_ns=wait_ns)
+    torch.cuda.synchronize()
+    out = (ids.cpu().numpy(), lp.cpu().numpy(), st.cpu().numpy())
+    if return_logits:
+        return out, x
+    return out
 
 
 def run_oracle(batch: workloads.Batch, rows=None):
     masks = batch.masks
     return oracle.pipeline(batch.logits, batch.oracle_params(), bf16=batch.bf16, masks=masks,
                            row_has_mask=batch.row_has_mask, rows=rows)
+
+
+def run_oracle_parallel(batch: workloads.Batch, rows=None, workers=None):
+    """run_oracle over row chunks in threads (the oracle's C calls release the
+    GIL and share no state); the same records, in row order."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+    rows = np.arange(batch.B) if rows is None else np.asarray(rows)
+    if workers is None:
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    chunks = [c for c in np.array_split(rows, workers * 4) if len(c)]
+    params = batch.oracle_params()
+    oracle.sample_row(np.zeros(4, np.float32), T=1.0)   # load the library once
+    def one(c):
+        return oracle.pipeline(batch.logits, params, bf16=batch.bf16, masks=batch.masks,
+                               row_has_mask=batch.row_has_mask, rows=c)[0]
+    with ThreadPoolExecutor(workers) as ex:
+        parts = list(ex.map(one, chunks))
+    return np.concatenate(parts)
+
+
+def record_parity(label, stats):
+    """Print the parity counts of a case and, when CDS_PARITY_RECORD names a
+    file, append them to it as one JSON line (the flagged fraction per case
+    is part of the parity report)."""
+    import json
+    import os
+    n, nf, nfm = stats
+    line = {"case": label, "rows": int(n), "flagged": int(nf),
+            "flagged_fraction": nf / max(n, 1), "flagged_mismatch": int(nfm)}
+    print("[parity] " + json.dumps(line), flush=True)
+    path = os.environ.get("CDS_PARITY_RECORD")
+    if path:
+        with open(path, "a") as f:
+            f.write(json.dumps(line) + "\n")
 
 
 def compare(batch, gpu, ref, rows=None, *, lp_tol=1e-5, label=""):

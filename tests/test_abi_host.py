@@ -91,14 +91,17 @@ def test_penalty_counts_and_bias_dedup(cds):
     # the row order (room for B int32, 16-byte padded), then the task table: 24
     # task rows (int32)
     pen_off = 64 * 3 + 16 + 96
-    pen = np.frombuffer(buf[pen_off:pen_off + 8 * b.n_pen].tobytes(), "<i4").reshape(-1, 2)
-    # rows of up to 4096 history tokens are packed as they come (count 1 each;
-    # the transforms kernel merges repeats); row 2 has no active penalty
-    np.testing.assert_array_equal(pen, [[3, 1], [3, 1], [7, 1], [3, 1]])
+    assert b.n_pen == 0 and b.n_hist_raw == 4
+    raw_off = pen_off + 8 * b.n_bias
+    pen = np.frombuffer(buf[raw_off:raw_off + 4 * b.n_hist_raw].tobytes(), "<i4")
+    # rows of up to 4096 history tokens are packed as they come, as raw int32
+    # ids after the bias entries (the transforms kernel merges repeats); row 2
+    # has no active penalty
+    np.testing.assert_array_equal(pen, [3, 3, 7, 3])
     assert (rows["pen_lo"][0], rows["pen_hi"][0]) == (0, 4)
     assert rows["flags"][0] & (1 << 6)                      # ROW_PEN_RAW
     assert b.flags & cds.FLAG_NEED_PENALTY and b.flags & cds.FLAG_HAS_BIAS
-    off = pen_off + 8 * b.n_pen
+    off = pen_off
     bias = np.frombuffer(buf[off:off + 8 * b.n_bias].tobytes(),
                          [("id", "<i4"), ("val", "<f4")])
     assert bias["id"].tolist() == [1, 7]

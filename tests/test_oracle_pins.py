@@ -503,3 +503,93 @@ def test_temperature_limits():
     zc = np.array([0.0, 0.02, 0.5, 0.49], np.float32)
     cold = oracle.sample_batch(zc, T=np.full(n, 1e-4, np.float32), **common)["id"]
     assert np.all(cold == 2)                                          # one-hot
+
+
+# ------------------------------------------------- near-tie flag thresholds --
+# Each flag is pinned from both sides of its 1e-6 threshold: a row built so
+# that the flagged quantity sits about 5e-7 from its boundary must carry the
+# flag, one built 5e-6 away must not.  The distances are computed here in
+# float64 straight from the definitions (Philox words through race_bits only),
+# not from the oracle's own key or mass code, so a wrong threshold, a dropped
+# term or a wrong comparison in the flag code fails one of the two cases.
+
+def _uniform_from_bits(x):
+    return (2.0 * float(x >> 9) + 1.0) * 2.0 ** -24
+
+
+def _gumbel(seed, offset, t):
+    return -math.log(-math.log(_uniform_from_bits(oracle.race_bits(seed, offset, t))))
+
+
+@pytest.mark.parametrize("gap,flagged", [(5e-7, True), (5e-6, False), (2e-6, False),
+                                         (0.0, True)])
+def test_race_flag_threshold_two_sided(gap, flagged):
+    """F_RACE: the best two race keys over S3 within 1e-6.  Tokens 3 and 5
+    are the only finite ones besides a far-down token 0; z[5] is set so that
+    key_3 - key_5 = gap (up to fp32 rounding of z[5], measured below)."""
+    seed, offset, T = 0x1234_5678_9ABC_DEF0, 77, 1.0
+    V = 8
+    g = [_gumbel(seed, offset, t) for t in range(V)]
+    z = np.full(V, -np.inf, np.float32)
+    z[0] = np.float32(-40.0)
+    z[3] = np.float32(0.0)
+    z[5] = np.float32(g[3] - g[5] - gap)
+    s = z.astype(np.float64) / T
+    m = float(np.max(s))
+    keys = sorted(((s[t] - m) + g[t] for t in (0, 3, 5)), reverse=True)
+    d = keys[0] - keys[1]
+    assert abs(d - gap) < 2e-7                 # the construction worked
+    r = oracle.sample_row(z, T=T, seed=seed, offset=offset)
+    assert r["n3"] == 3
+    assert bool(r["flags"] & oracle.F_RACE) == (abs(d) <= 1e-6), d
+    assert bool(r["flags"] & oracle.F_RACE) == flagged
+    # the winner is the larger key (lowest index on an exact tie)
+    k3, k5 = (s[3] - m) + g[3], (s[5] - m) + g[5]
+    assert r["id"] == (3 if k3 >= k5 else 5)
+
+
+@pytest.mark.parametrize("rel,flagged", [(5e-7, True), (-5e-7, True), (5e-6, False),
+                                         (-5e-6, False)])
+def test_min_p_flag_threshold_two_sided(rel, flagged):
+    """F_MINP: some weight w_t = exp(s_t - m) within 1e-6 * min_p of min_p."""
+    min_p = np.float32(0.25)
+    z = np.array([0.0, np.log(float(min_p) * (1.0 + rel)), -5.0], np.float32)
+    w = np.exp(z.astype(np.float64) - 0.0)
+    d = abs(w[1] - float(min_p)) / float(min_p)
+    assert abs(d - abs(rel)) < 1e-7
+    r = oracle.sample_row(z, T=1.0, min_p=min_p)
+    assert bool(r["flags"] & oracle.F_MINP) == flagged
+    assert r["n1"] == (2 if w[1] >= float(min_p) else 1)
+
+
+@pytest.mark.parametrize("rel,flagged", [(5e-7, True), (5e-6, False)])
+def test_top_k_flag_threshold_two_sided(rel, flagged):
+    """F_TOPK: the weight at rank k+1 is at least (1 - 1e-6) times the weight
+    at rank k (k = 2 here)."""
+    z = np.array([0.0, -1.0, -1.0 + np.log1p(-rel), -6.0], np.float32)
+    w = np.exp(z.astype(np.float64))
+    ratio = w[2] / w[1]
+    assert abs((1.0 - ratio) - rel) < 1e-7
+    r = oracle.sample_row(z, T=1.0, top_k=2)
+    assert bool(r["flags"] & oracle.F_TOPK) == flagged
+    assert r["n2"] == 2
+
+
+@pytest.mark.parametrize("dist,flagged", [(5e-7, True), (-5e-7, True), (5e-6, False),
+                                          (-5e-6, False)])
+def test_top_p_flag_threshold_two_sided(dist, flagged):
+    """F_TOPP: a normalised prefix mass above(t) / M2 within 1e-6 of top_p.
+    The prefix masses of z are 0, w0/M, (w0 + w1)/M, ...; top_p is placed
+    `dist` from the second one (fp32 rounding of top_p measured)."""
+    z = np.array([1.0, 0.3, -0.2, -2.0], np.float32)
+    w = np.exp(z.astype(np.float64) - 1.0)
+    M = w.sum()
+    f = w[0] / M
+    top_p = np.float32(f + dist)
+    d = float(top_p) - f
+    assert abs(d - dist) < 1e-7
+    r = oracle.sample_row(z, T=1.0, top_p=top_p)
+    assert bool(r["flags"] & oracle.F_TOPP) == flagged
+    # S3 is the smallest prefix whose mass reaches top_p: one token if
+    # top_p <= w0/M, else two
+    assert r["n3"] == (1 if float(top_p) <= f else 2)

@@ -262,3 +262,15 @@ CONFIGS = {
     "c1": c1_tiny, "c2": c2_decode, "c3": c3_penalties, "c4": c4_grammar,
     "c5a": lambda **kw: c5_spec("a", **kw), "c5b": lambda **kw: c5_spec("b", **kw),
 }
+
+
+def input_set(name: str, s: int) -> Batch:
+    """Input set s of a full-size workload, as the benchmark rotates them:
+    another salt of the same recipe (C5: the same logits with every request
+    seed shifted by s, as its recipe fixes the logits)."""
+    if name in ("c5a", "c5b"):
+        b = CONFIGS[name]()
+        if s:
+            b.seed = b.seed + np.uint64(s)
+        return b
+    return CONFIGS[name](salt=s)
