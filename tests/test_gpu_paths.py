@@ -50,7 +50,8 @@ def test_plan_wait_give_up_takes_exact_path():
     """A decode-shaped batch (B=192, V=151936) of top-p-only rows, whose slices
     need the row's plan before they race: with no wait allowed every such
     row gives up at once and is resolved by the exact path; results match
-    the oracle and the default path bit for bit."""
+    the oracle, and the default path's ids and statuses bit for bit (the two
+    paths sum the logprob's normaliser differently: within 1e-5)."""
     import constrained_decoding_amd as cds
     b = workloads.c2_decode(salt=41)
     b.top_k[:] = 0
@@ -60,8 +61,9 @@ def test_plan_wait_give_up_takes_exact_path():
     ref = run_oracle_parallel(b)
     record_parity("wait-give-up", compare(b, gave_up, ref, label="give-up"))
     normal = run_gpu(b)
-    for x, y in zip(gave_up, normal):
-        np.testing.assert_array_equal(x, y)
+    np.testing.assert_array_equal(gave_up[0], normal[0])
+    np.testing.assert_array_equal(gave_up[2], normal[2])
+    assert np.max(np.abs(gave_up[1] - normal[1])) <= 1e-5
 
 
 def test_bins_lost_rows_take_exact_path():
