@@ -538,9 +538,12 @@ __device__ __forceinline__ int wave0_first_ge(const T* v, int n, T x) {
   const unsigned long long m = __ballot(any);
   if (!m) return n;
   const int f = __ffsll((long long)m) - 1;
-  int i = K * f;
-  while (!(v[i] >= x)) ++i;  // stops inside lane f's range, whose last value is >= x
-  return i;
+  // inside lane f's range (whose last value is >= x): one element per lane,
+  // one LDS round instead of a walk
+  static_assert(K <= 64, "one ballot covers a lane's range");
+  const int i = K * f + l;
+  const unsigned long long m2 = __ballot(l < K && i < n && v[i] >= x);
+  return K * f + (__ffsll((long long)m2) - 1);
 }
 
 // ---- wave all-reduce by DPP row rotations ----------------------------------------

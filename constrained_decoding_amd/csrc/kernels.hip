@@ -461,8 +461,11 @@ __device__ __forceinline__ float sgpr_f(float v) {
 template <int NT>
 struct PlanShared {
   SliceHead head[kMaxSlices];
-  double md[NBINS];                 // per-bin mass relative to exp(m), then scanned
-  uint32_t cumc[NBINS];             // per-bin count, then scanned
+  int32_t shift[kMaxSlices];        // row bin of slice j's bin 0 (-1: nothing allowed)
+  double md[NBINS];                 // cumulative mass from the top, relative to exp(m)
+  uint32_t cumc[NBINS];             // cumulative count from the top
+  unsigned long long bm[NT];        // one block of NT merged row bins: fixed-point masses
+  uint32_t bc[NT];                  //   and counts
   double wtot_d[NT / 64];
   uint32_t wtot_u[NT / 64];
   int mode, inK, k_rank, rb12;
@@ -496,6 +499,15 @@ struct PlanShared {
 // Merge the slice summaries of row r into its plan (all NT threads).  Writes
 // the output of rows that end here (greedy, no finite token, non-finite
 // token) and the plan to a.plans[r] and to *out (LDS).
+//
+// HOLD rows (hist): the row's histogram is merged from the slices' in blocks
+// of NT bins from the top (row frame: bin b spans [(kmax-b)*delta,
+// (kmax-b+1)*delta), kmax the row maximum's bin), with integer LDS atomics
+// (exact in any order), and scanned; further blocks are merged only while
+// the cuts lie below the part scanned so far.  Block 0 is loaded together
+// with the slice heads: bins 0 .. NT-1 of every slice's own frame cover the
+// row's top NT bins whatever the slice's offset.  The row's total mass comes
+// from the slices' totals (heads), so the scan can stop at the cut.
 template <int NT>
 __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, PlanShared<NT>& ps,
                                          Plan* out) {
@@ -504,34 +516,27 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
   const bool greedy = (rp.flags & ROW_GREEDY) != 0;
   const bool topk = (rp.flags & ROW_TOPK) != 0, topp = (rp.flags & ROW_TOPP) != 0;
   const double Td = (double)rp.temperature;
-  // HOLD rows: the first slices' histograms are loaded in the slices' own bin
-  // frames right away, alongside the heads (the row frame needs the heads)
-  constexpr int BPT = (NBINS + NT - 1) / NT;  // bins per thread and slice
-  constexpr int JC = 4;                        // slices per round of loads
+  constexpr int JC = 10;  // slices per round of histogram loads
   const unsigned long long* gh = a.hist + (int64_t)r * P * NBINS;
-  unsigned long long hv[JC][BPT];
-  auto load_hist = [&](int j0) {
+  unsigned long long hv[JC];
+  // slice j's bins that land in row block blk (its bins 0 .. NT-1 for block 0)
+  auto load_block = [&](int j0, int blk) {
 #pragma unroll
-    for (int jj = 0; jj < JC; ++jj)
-#pragma unroll
-      for (int k = 0; k < BPT; ++k) {
-        const int sb = tid + k * NT;
-        hv[jj][k] = (j0 + jj < P && sb < NBINS) ? ld_u64(gh + (int64_t)(j0 + jj) * NBINS + sb) : 0ull;
-      }
-  };
-  if (hist) {
-    load_hist(0);
-    for (int b = tid; b < NBINS; b += NT) {
-      ps.cumc[b] = 0u;
-      ps.md[b] = 0.0;  // as u64 mass sums first
+    for (int jj = 0; jj < JC; ++jj) {
+      const int j = j0 + jj;
+      const int sb = blk == 0 ? tid : blk * NT - (j < P ? ps.shift[j] : 0) + tid;
+      const bool ok = j < P && (blk == 0 || ps.shift[j] >= 0) && sb >= 0 && sb < NBINS;
+      hv[jj] = ok ? ld_u64(gh + (int64_t)j * NBINS + sb) : 0ull;
     }
-  }
+  };
+  if (hist) load_block(0, 0);
   // merge the slice heads: wave 0, lane j holds slice j (P <= 64)
   if (tid < 64) {
     float zm = CDS_NEG_INF;
     int32_t am = INT_MAX;
     uint32_t fl = 0;
     double hs = 0.0;
+    float hk = 0.0f;
     if (tid < P) {
       const SliceHead h = ld_obj(&a.heads[(int64_t)r * P + tid]);
       ps.head[tid] = h;
@@ -539,6 +544,7 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
       am = h.zmax == CDS_NEG_INF ? INT_MAX : h.arg;
       fl = h.flags;
       hs = h.sumexp;
+      hk = h.kmax;
     }
     const float hz = zm;
     struct ZAF {
@@ -554,9 +560,17 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
     zm = hm.z;
     am = hm.a;
     fl = hm.f;
+    // slice masses relative to the slice maxima, moved to the row maximum and
+    // summed in a fixed order (deterministic): token sums, or for HOLD rows
+    // the slices' histogram totals
     const double invTe = greedy ? 1.0 : 1.0 / Td;
-    double Z = (!hist && hz != CDS_NEG_INF) ? hs * exp(((double)hz - (double)zm) * invTe) : 0.0;
+    double Z = (hz != CDS_NEG_INF) ? hs * exp(((double)hz - (double)zm) * invTe) : 0.0;
     Z = wave_allreduce(Z, [](double x, double y) { return x + y; });
+    if (hist && tid < P) {
+      // row bin of the slice's bin 0 (both maxima's bins are exact integers)
+      const float kmax_row = floorf(zm * bin_geom(rp.temperature).inv_delta);
+      ps.shift[tid] = hz == CDS_NEG_INF ? -1 : (int32_t)(kmax_row - hk);
+    }
     if (tid == 0) {
       int mode = PLAN_FAST;
       if (zm == CDS_NEG_INF) {
@@ -575,7 +589,7 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
       ps.zmax = zm;
       ps.arg = am;
       ps.m = (double)zm / Td;
-      ps.log_z = hist ? 0.0 : log(Z);
+      ps.log_z = log(Z);
     }
   }
   __syncthreads();
@@ -614,56 +628,100 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
   }
 
   CDS_TRACE_ROW(5);
-  // merge the slices' histograms: slice j's bin sb is row bin
-  // sb + (row kmax - kmax_j); counts and fixed-point masses are summed into LDS
-  // (integer atomics: exact in any order)
   const BinGeom g = bin_geom(rp.temperature);
   const float kmax = floorf(ps.zmax * g.inv_delta);
-  unsigned long long* mas = reinterpret_cast<unsigned long long*>(ps.md);
-  for (int j0 = 0; j0 < P; j0 += JC) {
-    if (j0) load_hist(j0);
+  const double m = ps.m, mtot = exp(ps.log_z);
+  // the scan must reach the row's cuts: the top_k-th token, the min-p bin,
+  // and (top-p over every token) the bin where the mass reaches top_p of it
+  int rb1_need = -1;
+  if (ps.zcut1 != CDS_NEG_INF) {
+    const float rbf = kmax - floorf(ps.zcut1 * g.inv_delta);
+    rb1_need = rbf >= (float)NBINS ? NBINS : (int)rbf;
+  }
+  const bool p_over_all = topp && !topk && ps.zcut1 == CDS_NEG_INF;
+  const double p_need = (double)rp.top_p * mtot * (1.0 + 1e-9);
+  const int lane = tid & 63, wv = tid >> 6;
+  uint32_t run_c = 0u;
+  double run_m = 0.0;
+  int blk = 0;
+  for (;;) {
+    ps.bc[tid] = 0u;
+    ps.bm[tid] = 0ull;
+    __syncthreads();
+    for (int j0 = 0; j0 < P; j0 += JC) {
+      if (blk > 0 || j0 > 0) load_block(j0, blk);
 #pragma unroll
-    for (int jj = 0; jj < JC; ++jj) {
-      const int j = j0 + jj;
-      if (j >= P || ps.head[j].zmax == CDS_NEG_INF) continue;
-      const int shift = (int)(kmax - ps.head[j].kmax);
-#pragma unroll
-      for (int k = 0; k < BPT; ++k) {
-        const unsigned long long v = hv[jj][k];
-        const int rb = tid + k * NT + shift;
-        if (v && rb < NBINS) {
-          atomicAdd(&ps.cumc[rb], (uint32_t)(v >> kCountShift));
-          atomicAdd(&mas[rb], v & ((1ull << kCountShift) - 1ull));
+      for (int jj = 0; jj < JC; ++jj) {
+        const int j = j0 + jj;
+        if (j >= P) break;
+        const int sh = ps.shift[j];
+        const unsigned long long v = hv[jj];
+        // row bin of this value, relative to the block
+        const int sb = blk == 0 ? tid : blk * NT - sh + tid;
+        const int rb = sb + sh - blk * NT;
+        if (v && sh >= 0 && rb >= 0 && rb < NT) {
+          atomicAdd(&ps.bc[rb], (uint32_t)(v >> kCountShift));
+          atomicAdd(&ps.bm[rb], v & ((1ull << kCountShift) - 1ull));
         }
       }
     }
-  }
-  __syncthreads();
-  {
-    const double m = ps.m;
-    for (int b = tid; b < NBINS; b += NT) {
-      // bin b spans [(kmax-b)*delta, (kmax-b+1)*delta); masses are relative to its top
-      const double top = ((double)kmax + 1.0 - (double)b) * (double)g.delta;
-      ps.md[b] = (double)mas[b] * 0x1p-31 * exp(top / Td - m);
+    __syncthreads();
+    const int B = blk * NT + tid;
+    uint32_t cb = 0u;
+    double mb = 0.0;
+    if (B < NBINS) {
+      cb = ps.bc[tid];
+      const double top = ((double)kmax + 1.0 - (double)B) * (double)g.delta;
+      mb = ps.bm[tid] ? (double)ps.bm[tid] * 0x1p-31 * exp(top / Td - m) : 0.0;
     }
+    // inclusive scan of the block in bin order, then the running totals
+    const uint32_t ic = wave_incl_sum(cb);
+    const double im = wave_incl_sum(mb);
+    if (lane == 63) {
+      ps.wtot_u[wv] = ic;
+      ps.wtot_d[wv] = im;
+    }
+    __syncthreads();
+    uint32_t bc0 = 0u, tc = 0u;
+    double bm0 = 0.0, tm = 0.0;
+#pragma unroll
+    for (int k = 0; k < NT / 64; ++k) {
+      const uint32_t u = ps.wtot_u[k];
+      const double d = ps.wtot_d[k];
+      bc0 += k < wv ? u : 0u;
+      bm0 += k < wv ? d : 0.0;
+      tc += u;
+      tm += d;
+    }
+    if (B < NBINS) {
+      ps.cumc[B] = run_c + bc0 + ic;
+      ps.md[B] = run_m + (bm0 + im);
+    }
+    run_c += tc;
+    run_m += tm;
+    ++blk;
+    if (blk * NT >= NBINS) break;
+    bool more = false;
+    if (topk && run_c < (uint32_t)rp.top_k) more = true;   // the k-th token lies below
+    if (rb1_need >= blk * NT) more = true;                  // the min-p bin lies below
+    if (p_over_all && run_m < p_need) more = true;          // the top-p mass is not reached
+    if (!more) break;
+  }
+  // bins below the scanned part: the totals (their own values are never
+  // searched; the last bin's mass is the row's)
+  for (int B = blk * NT + tid; B < NBINS; B += NT) {
+    ps.cumc[B] = run_c;
+    ps.md[B] = run_m > mtot ? run_m : mtot;
   }
   __syncthreads();
   CDS_TRACE_ROW(6);
-  // cumulative counts and masses from the top: waves 0 and 1
-  constexpr int KB = (NBINS + 63) / 64;
-  wave_scan_inplace<KB>(ps.cumc, NBINS, 0);  // two waves, side by side
-  wave_scan_inplace<KB>(ps.md, NBINS, 1);
-  __syncthreads();
   // the rest is searches over the monotone cumulative arrays: wave 0 only
   if (tid >= 64) return;
+  constexpr int KB = (NBINS + 63) / 64;
   const int rb2 = topk ? wave0_first_ge<KB>(ps.cumc, NBINS, (uint32_t)rp.top_k) : NBINS;
   if (tid == 0) {
-    ps.log_z = log(ps.md[NBINS - 1]);
     int rb1 = NBINS;
-    if (ps.zcut1 != CDS_NEG_INF) {
-      const float rbf = kmax - floorf(ps.zcut1 * g.inv_delta);
-      rb1 = rbf >= (float)NBINS ? NBINS : (int)rbf;
-    }
+    if (ps.zcut1 != CDS_NEG_INF) rb1 = rb1_need;
     int inK = -1, k_rank = 0;
     if (rb2 < NBINS && rb2 <= rb1) {
       inK = rb2;
@@ -1656,6 +1714,7 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
 
   uint32_t flags = nonfin ? SLICE_NONFINITE : 0u;
   const double se = st.s;
+  double hold_mass = 0.0;  // HOLD rows: the slice's mass relative to its maximum
   float kmax = 0.0f;
   if (cls == CLS_HOLD && zm != CDS_NEG_INF) {
     // histogram of the values below the slice maximum, bins aligned to delta
@@ -1685,13 +1744,24 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
                     (1ull << kCountShift) | (unsigned long long)fix);
         }
       __syncthreads();
+      // publish the bins, and the slice's total mass relative to its maximum
+      // (the row's planner reads the slice totals first and only the top
+      // bins of each histogram): bin b spans [(kmax-b)*delta,
+      // (kmax-b+1)*delta) and holds fixed-point masses relative to its top
       unsigned long long* gh = a.hist + slot * NBINS;
+      const double Td = (double)rp.temperature, dd = (double)g.delta;
+      double msum = 0.0;
       for (int b = tid; b < NBINS; b += NT) {
         unsigned long long v = 0ull;
 #pragma unroll
         for (int c = 0; c < kHistCopies; ++c) v += sh.hist[b * kHistCopies + c];
         st_u64(gh + b, v);
+        const unsigned long long mfix = v & ((1ull << kCountShift) - 1ull);
+        if (mfix)
+          msum += (double)mfix * 0x1p-31 *
+                  exp((((double)kmax + 1.0 - (double)b) * dd - (double)zm) / Td);
       }
+      hold_mass = block_sum_f64<NT>(msum, red);
     }
   }
   CDS_TRACE(3);
@@ -1779,7 +1849,7 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
     h.arg = (zm == CDS_NEG_INF) ? -1 : am;
     h.flags = flags;
     h.kmax = kmax;
-    h.sumexp = se;
+    h.sumexp = cls == CLS_HOLD ? hold_mass : se;
     h.pad[0] = h.pad[1] = 0u;
     st_obj(&a.heads[slot], h);
   }

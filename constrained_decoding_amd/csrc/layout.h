@@ -144,7 +144,8 @@ struct SliceHead {
   int32_t arg;          // its lowest index (-1 if none)
   uint32_t flags;       // SliceFlag
   float kmax;           // floor(zmax / delta) (histogram rows)
-  double sumexp;        // sum exp((z - zmax) / T_eff) (rows without histogram)
+  double sumexp;        // sum exp((z - zmax) / T_eff): rows without a histogram
+                        // sum the tokens, HOLD rows their histogram bins
   uint32_t pad[2];
 };
 static_assert(sizeof(SliceHead) == 32, "SliceHead layout");

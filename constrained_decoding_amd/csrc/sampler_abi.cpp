@@ -293,7 +293,7 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   int32_t n_hold = 0;
   while (n_hold < (int32_t)order.size() && rank(order[(size_t)n_hold]) == 0) ++n_hold;
   order.insert(order.end(), greedy_rows.begin(), greedy_rows.end());
-  std::memcpy(p + off_list, order.data(), sizeof(int32_t) * order.size());
+  if (!order.empty()) std::memcpy(p + off_list, order.data(), sizeof(int32_t) * order.size());
   std::memset(p + off_list + sizeof(int32_t) * order.size(), 0,
               list_bytes(B) - sizeof(int32_t) * order.size());
   // the task groups: pass-1 group g, and pass-2 group g - lag after it
@@ -323,9 +323,11 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
     }
   // counted penalty entries, the bias, then the raw history ids in row order
   // (runs of consecutive raw rows are one copy each: their CSR ranges adjoin)
-  std::memcpy(p + off_pen, pen.data(), sizeof(PenEntry) * pen.size());
-  std::memcpy(p + off_pen + sizeof(PenEntry) * (size_t)n_pen, bias.data(),
-              sizeof(BiasEntry) * bias.size());
+  // (memcpy from an empty vector's null data() is undefined even for 0 bytes)
+  if (!pen.empty()) std::memcpy(p + off_pen, pen.data(), sizeof(PenEntry) * pen.size());
+  if (!bias.empty())
+    std::memcpy(p + off_pen + sizeof(PenEntry) * (size_t)n_pen, bias.data(),
+                sizeof(BiasEntry) * bias.size());
   const size_t off_raw = off_pen + sizeof(PenEntry) * (size_t)n_pen +
                          sizeof(BiasEntry) * bias.size();
   int32_t* raw = reinterpret_cast<int32_t*>(p + off_raw);

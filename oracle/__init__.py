@@ -41,10 +41,15 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    path = _build.LIB
-    if not _os.path.exists(path) or \
-            _os.path.getmtime(path) < _os.path.getmtime(_build.SRC):
-        _build.build(force=True)
+    # CDS_ORACLE_SANITIZE=1: the AddressSanitizer / UBSan build (the process
+    # must preload the ASan runtime; tests/test_sanitizers.py does)
+    if _os.environ.get("CDS_ORACLE_SANITIZE") == "1":
+        path = _build.build(force=False, sanitize=True)
+    else:
+        path = _build.LIB
+        if not _os.path.exists(path) or \
+                _os.path.getmtime(path) < _os.path.getmtime(_build.SRC):
+            _build.build(force=True)
     lib = _ct.CDLL(path)
     P = _ct.c_void_p
     lib.cdo_philox4x32_10.argtypes = [P, P, P]
