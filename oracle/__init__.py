@@ -19,6 +19,9 @@ from . import build as _build
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
+# filter orders (see cd_oracle.h): min-p first (default), joint top-k/top-p,
+# min-p last
+ORDER_MINP_FIRST, ORDER_JOINT, ORDER_MINP_LAST = 0, 1, 2
 STATUS_OK, STATUS_OVERFLOW, STATUS_INVALID = 0, 1, 2
 F_TOPP, F_RACE, F_MINP, F_TOPK = 1, 2, 4, 8
 # flags that excuse an id mismatch (F_TOPK is informational: top-k is decided
@@ -67,6 +70,11 @@ def _load():
                                    _ct.c_uint64, P, P]
     lib.cdo_sample_batch.argtypes = [P, _ct.c_int64, _ct.c_int32, _ct.c_int32,
                                      P, P, P, P, P, P, P]
+    lib.cdo_sample_row_order.argtypes = [P, _ct.c_int32, _ct.c_float, _ct.c_int32,
+                                         _ct.c_float, _ct.c_float, _ct.c_uint64,
+                                         _ct.c_uint64, _ct.c_int32, P, P]
+    lib.cdo_sample_batch_order.argtypes = [P, _ct.c_int64, _ct.c_int32, _ct.c_int32,
+                                           P, P, P, P, P, P, _ct.c_int32, P]
     _lib = lib
     return lib
 
@@ -135,20 +143,24 @@ def transform_row(logits, *, hist_ids=None, rep=1.0, freq=0.0, pres=0.0,
 
 
 def sample_row(z, *, T, top_k=0, top_p=1.0, min_p=0.0, seed=0, offset=0,
-               want_sets=False):
+               want_sets=False, order=ORDER_MINP_FIRST):
     """Sample one row of transformed logits; returns a RESULT_DTYPE record
-    (and the V-byte set-membership array if ``want_sets``)."""
+    (and the V-byte set-membership array if ``want_sets``).  ``order``: the
+    filter order (ORDER_*)."""
     zz = _np.ascontiguousarray(z, dtype=_np.float32)
     V = zz.shape[0]
     res = _np.zeros(1, RESULT_DTYPE)
     sets = _np.zeros(V, _np.uint8) if want_sets else None
-    _load().cdo_sample_row(_ptr(zz), V, float(T), int(top_k), float(top_p),
-                           float(min_p), int(seed), int(offset), _ptr(res),
-                           _ptr(sets))
+    rc = _load().cdo_sample_row_order(_ptr(zz), V, float(T), int(top_k), float(top_p),
+                                      float(min_p), int(seed), int(offset), int(order),
+                                      _ptr(res), _ptr(sets))
+    if rc != 0:
+        raise ValueError(f"unknown filter order {order}")
     return (res[0], sets) if want_sets else res[0]
 
 
-def sample_batch(z, *, T, top_k, top_p, min_p, seed, offset, broadcast=False):
+def sample_batch(z, *, T, top_k, top_p, min_p, seed, offset, broadcast=False,
+                 order=ORDER_MINP_FIRST):
     """Row loop; ``z`` is [B, V] (or [V] with ``broadcast=True`` and B given
     by the parameter arrays).  Returns RESULT_DTYPE [B]."""
     zz = _np.ascontiguousarray(z, dtype=_np.float32)
@@ -167,8 +179,10 @@ def sample_batch(z, *, T, top_k, top_p, min_p, seed, offset, broadcast=False):
     for a in (k, p, mp, sd, of):
         assert a.shape[0] == B
     out = _np.zeros(B, RESULT_DTYPE)
-    _load().cdo_sample_batch(_ptr(zz), ld, B, V, _ptr(T), _ptr(k), _ptr(p),
-                             _ptr(mp), _ptr(sd), _ptr(of), _ptr(out))
+    rc = _load().cdo_sample_batch_order(_ptr(zz), ld, B, V, _ptr(T), _ptr(k), _ptr(p),
+                                        _ptr(mp), _ptr(sd), _ptr(of), int(order), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"unknown filter order {order}")
     return out
 
 
@@ -181,7 +195,8 @@ def pipeline(logits, params, *, bf16=False, masks=None, row_has_mask=None,
     optional ``rep, freq, pres`` plus per-row lists ``hist`` (int arrays) and
     ``bias`` (lists of (id, value) pairs, applied in order).  ``masks``:
     [B, W] int32 or None; ``row_has_mask``: [B] bool or None (all rows).
-    ``rows``: subset of row indices to evaluate (default all).
+    ``rows``: subset of row indices to evaluate (default all).  An optional
+    ``params["order"]`` (scalar) selects the filter order (ORDER_*).
     Returns (RESULT_DTYPE records, transformed logits) for the chosen rows.
     """
     B = logits.shape[0]
@@ -208,6 +223,7 @@ def pipeline(logits, params, *, bf16=False, masks=None, row_has_mask=None,
         res.append(sample_row(
             z, T=params["temperature"][r], top_k=params["top_k"][r],
             top_p=params["top_p"][r], min_p=params["min_p"][r],
-            seed=params["seed"][r], offset=params["offset"][r]))
+            seed=params["seed"][r], offset=params["offset"][r],
+            order=params.get("order", ORDER_MINP_FIRST)))
         zs.append(z)
     return _np.array(res, dtype=RESULT_DTYPE), _np.array(zs)

@@ -204,9 +204,57 @@ static int cdo_entry_cmp(const void *a, const void *b) {
   return (x->t < y->t) ? -1 : (x->t > y->t ? 1 : 0);
 }
 
+/* Mass of the top-k set over every finite token (ties at the k-th value all
+ * in), by its definition: a full sort of the finite values, the k-th largest
+ * value, and the sum of w over the tokens at or above it.  Used by the
+ * top-k -> top-p -> min-p order, whose top-p cut is normalised by the mass
+ * the top-k cut leaves [SGL, "后端分支": top_k_renorm_prob, then
+ * top_p_renorm_prob, then min_p_sampling_from_probs]. */
+static int cdo_cmp_desc(const void *a, const void *b) {
+  const double x = *(const double *)a, y = *(const double *)b;
+  return x > y ? -1 : (x < y ? 1 : 0);
+}
+
+static double cdo_topk_mass_all(const double *s, const double *w, int32_t V,
+                                int32_t top_k) {
+  double *v = (double *)malloc((size_t)V * sizeof(double));
+  int64_t n = 0;
+  for (int32_t t = 0; t < V; ++t)
+    if (s[t] != -INFINITY) v[n++] = s[t];
+  qsort(v, (size_t)n, sizeof(double), cdo_cmp_desc); /* full sort */
+  const double tau = v[top_k - 1];
+  double mass = 0.0;
+  for (int32_t t = 0; t < V; ++t)
+    if (s[t] != -INFINITY && s[t] >= tau) mass += w[t];
+  free(v);
+  return mass;
+}
+
+static int cdo_sample_row_impl(const float *z, int32_t V, float T,
+                               int32_t top_k, float top_p, float min_p,
+                               uint64_t seed, uint64_t offset, int32_t order,
+                               cdo_result *out, uint8_t *set_out);
+
 int cdo_sample_row(const float *z, int32_t V, float T, int32_t top_k,
                    float top_p, float min_p, uint64_t seed, uint64_t offset,
                    cdo_result *out, uint8_t *set_out) {
+  return cdo_sample_row_impl(z, V, T, top_k, top_p, min_p, seed, offset,
+                             CDO_ORDER_MINP_FIRST, out, set_out);
+}
+
+int cdo_sample_row_order(const float *z, int32_t V, float T, int32_t top_k,
+                         float top_p, float min_p, uint64_t seed,
+                         uint64_t offset, int32_t order, cdo_result *out,
+                         uint8_t *set_out) {
+  if (order < CDO_ORDER_MINP_FIRST || order > CDO_ORDER_MINP_LAST) return -1;
+  return cdo_sample_row_impl(z, V, T, top_k, top_p, min_p, seed, offset,
+                             order, out, set_out);
+}
+
+static int cdo_sample_row_impl(const float *z, int32_t V, float T,
+                               int32_t top_k, float top_p, float min_p,
+                               uint64_t seed, uint64_t offset, int32_t order,
+                               cdo_result *out, uint8_t *set_out) {
   memset(out, 0, sizeof *out);
   out->id = -1;
   out->zcut = NAN;
@@ -318,11 +366,29 @@ int cdo_sample_row(const float *z, int32_t V, float T, int32_t top_k,
     for (int32_t t = 0; t < V; ++t)
       if (in[t] & 1) in[t] |= 2;
 
-  /* S3: top-p within S2, walked in sorted order one value-group at a time */
+  /* S3: top-p within S2, walked in sorted order one value-group at a time.
+   * The mass the cut is normalised by depends on the filter order: the mass
+   * of S2 when min-p and top-k come first (vLLM's order [GLM, "采样"]); the
+   * mass of the top-k set over every token when min-p comes last (top-k,
+   * renormalise, top-p, renormalise, min-p [SGL, "后端分支"]); the mass of
+   * every token when top-k and top-p are applied jointly to one distribution
+   * and the kept set is their intersection [SGL, "后端分支",
+   * filter_apply_order="joint"].  Every set here is a prefix of the sorted
+   * order, so the mass strictly above t is the same whichever set t is
+   * measured in. */
   int64_t n3 = 0;
   if (topp_on) {
     double M2 = 0.0;
     for (int64_t i = 0; i < n2; ++i) M2 += w[ent[i].t];
+    if (order == CDO_ORDER_JOINT) {
+      M2 = Z;
+    } else if (order == CDO_ORDER_MINP_LAST) {
+      int64_t nfin_all = 0;
+      for (int32_t t = 0; t < V; ++t) nfin_all += (z[t] != -INFINITY);
+      M2 = (top_k > 1 && (int64_t)top_k < nfin_all)
+               ? cdo_topk_mass_all(s, w, V, top_k)
+               : Z;
+    }
     const double target = (double)top_p * M2;
     double cum = 0.0;
     int64_t i = 0;
@@ -392,8 +458,19 @@ int cdo_sample_batch(const float *z, int64_t ld, int32_t B, int32_t V,
                      const float *T, const int32_t *top_k, const float *top_p,
                      const float *min_p, const uint64_t *seed,
                      const uint64_t *offset, cdo_result *out) {
+  return cdo_sample_batch_order(z, ld, B, V, T, top_k, top_p, min_p, seed,
+                                offset, CDO_ORDER_MINP_FIRST, out);
+}
+
+int cdo_sample_batch_order(const float *z, int64_t ld, int32_t B, int32_t V,
+                           const float *T, const int32_t *top_k,
+                           const float *top_p, const float *min_p,
+                           const uint64_t *seed, const uint64_t *offset,
+                           int32_t order, cdo_result *out) {
   for (int32_t r = 0; r < B; ++r)
-    cdo_sample_row(z + (int64_t)r * ld, V, T[r], top_k[r], top_p[r], min_p[r],
-                   seed[r], offset[r], &out[r], NULL);
+    if (cdo_sample_row_order(z + (int64_t)r * ld, V, T[r], top_k[r], top_p[r],
+                             min_p[r], seed[r], offset[r], order, &out[r],
+                             NULL) != 0)
+      return -1;
   return 0;
 }

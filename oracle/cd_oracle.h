@@ -86,12 +86,32 @@ int cdo_transform_row(const void *logits, int dtype, int32_t V,
                       const float *bias_vals, int64_t n_bias,
                       const int32_t *mask, float *out);
 
+/* Filter orders.  MINP_FIRST: temperature -> min-p -> top-k -> top-p, each
+ * cut on what the previous ones left (vLLM's order, [GLM] "采样"; the
+ * default).  JOINT: top-k and top-p applied to one distribution, the kept set
+ * their intersection (with min-p's set) [SGL, "后端分支",
+ * filter_apply_order="joint"].  MINP_LAST: top-k, renormalise, top-p,
+ * renormalise, min-p [SGL, "后端分支" and "概率裁剪的数学"]. */
+#define CDO_ORDER_MINP_FIRST 0
+#define CDO_ORDER_JOINT 1
+#define CDO_ORDER_MINP_LAST 2
+
 /* Sampling for one row of transformed logits z (post penalties, mask and
- * bias).  set_out (optional, V bytes): bit0 = in S1, bit1 = in S2,
- * bit2 = in S3.  Returns 0. */
+ * bias), in the MINP_FIRST order.  set_out (optional, V bytes): bit0 = in
+ * S1 (min-p), bit1 = in S2 (and top-k), bit2 = in S3 (the drawn-from set).
+ * Returns 0. */
 int cdo_sample_row(const float *z, int32_t V, float T, int32_t top_k,
                    float top_p, float min_p, uint64_t seed, uint64_t offset,
                    cdo_result *out, uint8_t *set_out);
+
+/* cdo_sample_row in a given filter order (CDO_ORDER_*); -1 on an unknown
+ * order.  In every order the drawn-from set is S1 & Tk & {t : mass strictly
+ * above t < top_p * M}, where M is the mass of S1 & Tk (MINP_FIRST), of Tk
+ * (MINP_LAST) or of every finite token (JOINT); set_out's bit2 marks it. */
+int cdo_sample_row_order(const float *z, int32_t V, float T, int32_t top_k,
+                         float top_p, float min_p, uint64_t seed,
+                         uint64_t offset, int32_t order, cdo_result *out,
+                         uint8_t *set_out);
 
 /* Row loop over cdo_sample_row; ld is the row stride in elements (0 repeats
  * row 0 for every row, used for many draws of one distribution). */
@@ -99,6 +119,11 @@ int cdo_sample_batch(const float *z, int64_t ld, int32_t B, int32_t V,
                      const float *T, const int32_t *top_k, const float *top_p,
                      const float *min_p, const uint64_t *seed,
                      const uint64_t *offset, cdo_result *out);
+int cdo_sample_batch_order(const float *z, int64_t ld, int32_t B, int32_t V,
+                           const float *T, const int32_t *top_k,
+                           const float *top_p, const float *min_p,
+                           const uint64_t *seed, const uint64_t *offset,
+                           int32_t order, cdo_result *out);
 
 #ifdef __cplusplus
 }
