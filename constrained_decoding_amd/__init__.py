@@ -10,5 +10,5 @@ from ._binding import (  # noqa: F401
     FLAG_NEED_MIN_P, FLAG_NEED_PENALTY, FLAG_NEED_TOP_K, FLAG_NEED_TOP_P, FLAG_SPLIT_PASS2, LIB_PATH,
     STATUS_INVALID, STATUS_OK, STATUS_OVERFLOW, WAIT_NONE, Batch, HostParams, Options,
     PackedBatch, SamplerError, Workspace, apply_bitmask, apply_transforms, bias_from_dict, csr,
-    lib, pack_host, sample, strerror, version,
+    ORDER_JOINT, ORDER_MINP_FIRST, ORDER_MINP_LAST, lib, pack_host, sample, strerror, version,
 )

@@ -21,6 +21,7 @@ FLAG_ALL_GREEDY, FLAG_ANY_GREEDY = 1 << 0, 1 << 1
 FLAG_NEED_TOP_K, FLAG_NEED_TOP_P, FLAG_NEED_MIN_P = 1 << 2, 1 << 3, 1 << 4
 FLAG_NEED_PENALTY, FLAG_HAS_BIAS, FLAG_SPLIT_PASS2 = 1 << 5, 1 << 6, 1 << 7
 ALGO_FAST, ALGO_EXACT = 0, 1
+ORDER_MINP_FIRST, ORDER_JOINT, ORDER_MINP_LAST = 0, 1, 2
 WAIT_NONE = -1
 
 EXPORTS = [
@@ -39,7 +40,7 @@ class HostParams(ct.Structure):
         ("frequency_penalty", ct.c_void_p), ("presence_penalty", ct.c_void_p),
         ("hist_indptr", ct.c_void_p), ("hist_ids", ct.c_void_p),
         ("bias_indptr", ct.c_void_p), ("bias_ids", ct.c_void_p), ("bias_vals", ct.c_void_p),
-        ("seed", ct.c_void_p), ("offset", ct.c_void_p),
+        ("seed", ct.c_void_p), ("offset", ct.c_void_p), ("filter_order", ct.c_int32),
     ]
 
 
@@ -146,7 +147,7 @@ class _HostArrays:
     def __init__(self, B, V, temperature, top_k=None, top_p=None, min_p=None,
                  repetition_penalty=None, frequency_penalty=None, presence_penalty=None,
                  hist_indptr=None, hist_ids=None, bias_indptr=None, bias_ids=None,
-                 bias_vals=None, seed=None, offset=None):
+                 bias_vals=None, seed=None, offset=None, filter_order=ORDER_MINP_FIRST):
         self.a = dict(
             temperature=_arr(temperature, np.float32, B), top_k=_arr(top_k, np.int32, B),
             top_p=_arr(top_p, np.float32, B), min_p=_arr(min_p, np.float32, B),
@@ -158,7 +159,8 @@ class _HostArrays:
             bias_indptr=_arr(bias_indptr, np.int64, None if bias_indptr is None else B + 1),
             bias_ids=_arr(bias_ids, np.int32), bias_vals=_arr(bias_vals, np.float32),
             seed=_arr(seed, np.uint64, B), offset=_arr(offset, np.uint64, B))
-        self.hp = HostParams(B=B, V=V, **{k: _p(v) for k, v in self.a.items()})
+        self.hp = HostParams(B=B, V=V, filter_order=int(filter_order),
+                             **{k: _p(v) for k, v in self.a.items()})
         self.B, self.V = B, V
         self.n_hist = 0 if self.a["hist_ids"] is None else self.a["hist_ids"].shape[0]
         self.n_bias = 0 if self.a["bias_ids"] is None else self.a["bias_ids"].shape[0]

@@ -292,6 +292,7 @@ __device__ __forceinline__ void row_exact(const SampleArgs& a, int r, ExactShare
   }
 
   // top-k: radix select of the k-th largest value (8-bit digits of the order key)
+  float zk = CDS_NEG_INF;
   if ((rp.flags & ROW_TOPK) && rp.top_k < nf) {
     uint32_t prefix = 0, pmask = 0;
     unsigned long long krem = (unsigned long long)rp.top_k;
@@ -313,7 +314,8 @@ __device__ __forceinline__ void row_exact(const SampleArgs& a, int r, ExactShare
       prefix |= (uint32_t)d << shift;
       pmask |= 255u << shift;
     }
-    zcut = fmaxf(zcut, from_okey(prefix));
+    zk = from_okey(prefix);
+    zcut = fmaxf(zcut, zk);
   }
 
   // top-p: mass-weighted radix select on fixed-point masses exp(s - m) * 2^sc
@@ -332,10 +334,26 @@ __device__ __forceinline__ void row_exact(const SampleArgs& a, int r, ExactShare
         if (x[q] != CDS_NEG_INF && x[q] >= zc) msum += wfix(x[q]);
     });
     msum = block_sum_u64<NT>(msum, sh.red);
-    const double need = (double)rp.top_p * (double)msum;
+    // the mass the cut is normalised by: what min-p and top-k left (min-p
+    // first), the top-k set (min-p last), every token (joint)
+    const uint32_t ord = rp.flags & kRowOrderBits;
+    unsigned long long mnorm = msum;
+    if (ord) {
+      const float zn = (ord & ROW_ORDER_MINP_LAST) ? zk : CDS_NEG_INF;
+      mnorm = 0ull;
+      for_row4<NT, BF16, VEC>(rv, V, nonfin, [&](const float* x, int64_t) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (x[q] != CDS_NEG_INF && x[q] >= zn) mnorm += wfix(x[q]);
+      });
+      mnorm = block_sum_u64<NT>(mnorm, sh.red);
+    }
+    const double need = (double)rp.top_p * (double)mnorm;
+    // a target above what min-p and top-k left keeps all of it
+    const bool keep_all = (double)msum < need;
     uint32_t prefix = 0, pmask = 0;
     unsigned long long base = 0;
-    for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int shift = 24; shift >= 0 && !keep_all; shift -= 8) {
       if (threadIdx.x < 256) sh.hist[threadIdx.x] = 0ull;
       __syncthreads();
       for_row4<NT, BF16, VEC>(rv, V, nonfin, [&](const float* x, int64_t) {
@@ -353,7 +371,7 @@ __device__ __forceinline__ void row_exact(const SampleArgs& a, int r, ExactShare
       prefix |= (uint32_t)d << shift;
       pmask |= 255u << shift;
     }
-    zcut = fmaxf(zcut, from_okey(prefix));
+    if (!keep_all) zcut = fmaxf(zcut, from_okey(prefix));
   }
 
   // the race over {z >= zcut}
@@ -584,6 +602,8 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
         mode = PLAN_DONE;
       } else if (fl & SLICE_BINS_LOST) {
         mode = PLAN_SLOW;
+      } else if (hist && (rp.flags & kRowOrderBits)) {
+        mode = PLAN_SLOW;  // a large top-k with top-p in another filter order
       }
       ps.mode = mode;
       ps.zmax = zm;
@@ -1169,6 +1189,7 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
       auto mx = [](uint32_t x, uint32_t y) { return x > y ? x : y; };
       int status = 0;  // 1: the row takes the exact path
       float zc12 = pl.zcut1;
+      float zk = CDS_NEG_INF;  // the k-th largest value
       if (pl.k_rank > 0) {
         bool inK[KW];
         uint32_t c = 0u, lo = 0xFFFFFFFFu, hi = 0u;
@@ -1184,23 +1205,32 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
         lo = wave_allreduce(lo, mn);
         hi = wave_allreduce(hi, mx);
         if (c < (uint32_t)pl.k_rank && !pl.list_mode) status = 1;
-        else if (c >= (uint32_t)pl.k_rank)
-          zc12 = fmaxf(zc12, from_okey(wave_select_count<KW>(u, inK, (uint32_t)pl.k_rank, lo, hi)));
+        else if (c >= (uint32_t)pl.k_rank) {
+          zk = from_okey(wave_select_count<KW>(u, inK, (uint32_t)pl.k_rank, lo, hi));
+          zc12 = fmaxf(zc12, zk);
+        }
       }
       if (pl.list_mode && zc12 < sh.fshare) status = 1;
+      const uint32_t ord = rp.flags & kRowOrderBits;
+      // min-p last: every token of the top-k set must be listed (its mass
+      // normalises the top-p cut)
+      if ((ord & ROW_ORDER_MINP_LAST) && pl.k_rank > 0 && pl.list_mode && zk < sh.fshare)
+        status = 1;
       float zf = zc12;
       if (status == 0 && pl.topp) {
         const float zref = pl.a_hi, a_lo = pl.a_lo, zc = zc12;
         const float c32 = (float)(1.4426950408889634 / Td);
         const double F = exp((double)zref / Td - pl.m);
         constexpr double kFix = 0x1p46;
-        unsigned long long w[KW], wi[KW], mu = 0ull, m_in = 0ull;
+        unsigned long long w[KW], wi[KW], mu = 0ull, m_in = 0ull, mk = 0ull;
         uint32_t lo = 0xFFFFFFFFu, hi = 0u;
 #pragma unroll
         for (int k = 0; k < KW; ++k) {
-          w[k] = z[k] >= zc ? (unsigned long long)((double)__builtin_amdgcn_exp2f((z[k] - zref) * c32) *
-                                                  kFix)
-                            : 0ull;
+          const unsigned long long wz =
+              v[k] ? (unsigned long long)((double)__builtin_amdgcn_exp2f((z[k] - zref) * c32) * kFix)
+                   : 0ull;
+          w[k] = z[k] >= zc ? wz : 0ull;
+          mk += z[k] >= zk ? wz : 0ull;  // the top-k set (min-p last)
           mu += w[k];
           wi[k] = (z[k] >= a_lo) ? w[k] : 0ull;
           m_in += wi[k];
@@ -1214,11 +1244,22 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
         m_in = wave_allreduce(m_in, add);
         lo = wave_allreduce(lo, mn);
         hi = wave_allreduce(hi, mx);
-        const double M2 = pl.m_sure + pl.m_mid + F * ((double)mu / kFix);
+        // the mass top-p is normalised by: what min-p and top-k left (min-p
+        // first), the top-k set (min-p last), every token (joint)
+        double M2 = pl.m_sure + pl.m_mid + F * ((double)mu / kFix);
+        if (ord & ROW_ORDER_JOINT) {
+          M2 = exp(pl.log_z);
+        } else if (ord & ROW_ORDER_MINP_LAST) {
+          mk = wave_allreduce(mk, add);
+          M2 = pl.k_rank > 0 ? F * ((double)mk / kFix) : exp(pl.log_z);
+        }
         const double need = (pl.p * M2 - pl.m_sure) / F * kFix;
-        if (!(need > 0.0) || (double)m_in < need) {
+        // (other orders: a target above the mass of what min-p and top-k left
+        // keeps all of it)
+        const bool keep_all = ord != 0u && need > 0.0 && (double)m_in < need;
+        if (!(need > 0.0) || ((double)m_in < need && !keep_all)) {
           status = 1;
-        } else {
+        } else if (!keep_all) {
           // the cut is the key of a boundary entry (wi > 0): with at most 64
           // such entries, one per lane, each lane sums the weight at or above
           // its own key and the largest key whose sum reaches need wins (the
@@ -1295,6 +1336,7 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
   } else {
   // exact top-k value: the k_rank-th largest list value inside [k_lo, k_hi)
   float zc12 = pl.zcut1;
+  float zk = CDS_NEG_INF;
   if (pl.k_rank > 0) {
     const float k_lo = pl.k_lo, k_hi = pl.k_hi;
     auto inK = [&](unsigned long long e) {
@@ -1322,13 +1364,17 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
       const uint32_t v = list_select<NT>(
           ul, n, inK, [](unsigned long long) { return 1ull; }, (double)pl.k_rank, 0ull, klo, khi,
           sel);
-      zc12 = fmaxf(zc12, from_okey(v));
+      zk = from_okey(v);
+      zc12 = fmaxf(zc12, zk);
     }
   }
   // list mode: the lists hold every token >= their slice's cut, so the set
   // {z >= zc12} is complete only if zc12 is at or above every cut (always so
   // when the slices listed their full top-k; truncated lists may miss it)
   if (pl.list_mode && zc12 < sh.fshare) return false;
+  const uint32_t ord = rp.flags & kRowOrderBits;
+  // min-p last: the whole top-k set must be listed (its mass normalises top-p)
+  if ((ord & ROW_ORDER_MINP_LAST) && pl.k_rank > 0 && pl.list_mode && zk < sh.fshare) return false;
   CDS_TRACE_ROW(2);
   zfin = zc12;
 
@@ -1361,15 +1407,37 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
       }
     }
     block_sums_range<NT>(mu, m_in, plo, phi, red);
-    const double M2 = pl.m_sure + pl.m_mid + F * ((double)mu / kFix);
+    // the mass top-p is normalised by (see the one-wave path)
+    double M2 = pl.m_sure + pl.m_mid + F * ((double)mu / kFix);
+    if (ord & ROW_ORDER_JOINT) {
+      M2 = exp(pl.log_z);
+    } else if ((ord & ROW_ORDER_MINP_LAST) && pl.k_rank > 0) {
+      unsigned long long mk = 0ull;
+      const float zkk = zk;
+#pragma unroll 1
+      for (int i = tid; i < n; i += NT) {
+        const float z = ukey_z(ul[i]);
+        if (z >= zkk)
+          mk += (unsigned long long)((double)__builtin_amdgcn_exp2f((z - zref) * c32) * kFix);
+      }
+      mk = block_sum_u64<NT>(mk, red);
+      M2 = F * ((double)mk / kFix);
+    } else if (ord & ROW_ORDER_MINP_LAST) {
+      M2 = exp(pl.log_z);
+    }
     // the list mass (in fixed units) the cut must reach above the sure region
     const double need = (pl.p * M2 - pl.m_sure) / F * kFix;
     if (!(need > 0.0)) return false;         // the cut lies above the range
-    if ((double)m_in < need) return false;   // ... or below it
-    const uint32_t v = list_select<NT>(
-        ul, n, [=](unsigned long long e) { return ukey_z(e) >= a_lo; },
-        [=](unsigned long long e) { return wfix(ukey_z(e)); }, need, 0ull, plo, phi, sel);
-    zfin = fmaxf(zfin, from_okey(v));
+    if ((double)m_in < need) {
+      // ... or below it: for the joint and min-p-last orders all of what
+      // min-p and top-k left is kept; otherwise the plan was wrong
+      if (!ord) return false;
+    } else {
+      const uint32_t v = list_select<NT>(
+          ul, n, [=](unsigned long long e) { return ukey_z(e) >= a_lo; },
+          [=](unsigned long long e) { return wfix(ukey_z(e)); }, need, 0ull, plo, phi, sel);
+      zfin = fmaxf(zfin, from_okey(v));
+    }
   }
 
   CDS_TRACE_ROW(3);
@@ -1807,7 +1875,9 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
     // at most the min-p bound relative to the slice maximum (min-p rows; the
     // row's bound, relative to the row maximum, is at least as high)
     float cut = (topk_list && st.lb != CDS_POS_INF) ? st.lb : CDS_NEG_INF;
-    if (rp.flags & ROW_MINP) {
+    // (min-p last: the top-p cut is normalised by the whole top-k set's
+    // mass, so a top-k row lists it without the min-p bound)
+    if ((rp.flags & ROW_MINP) && !(topk_list && (rp.flags & ROW_ORDER_MINP_LAST))) {
       const double b = (double)zm + (double)rp.temperature * log((double)rp.min_p);
       const float bm = (float)(b - 1e-5 * (1.0 + fabs(b) + fabs((double)zm)));
       cut = fmaxf(cut, bm);
@@ -1892,7 +1962,9 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
     pl.a_lo = pl.a_hi = pl.k_lo = pl.k_hi = CDS_POS_INF;
     if (rp.flags & ROW_TOPK) {
       pl.k_rank = rp.top_k;
-      pl.k_lo = pl.zcut1;  // the k-th largest within the min-p set
+      // the k-th largest within the min-p set, or over every token when
+      // min-p comes last (the same value when the min-p set holds k tokens)
+      pl.k_lo = (rp.flags & ROW_ORDER_MINP_LAST) ? -FLT_MAX : pl.zcut1;
       pl.k_hi = CDS_POS_INF;
     }
     if (rp.flags & ROW_TOPP) {

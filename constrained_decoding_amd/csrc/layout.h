@@ -17,7 +17,12 @@ enum RowFlag : uint32_t {
   ROW_PEN_RAW = 1u << 6, // its history is raw int32 ids (repeats not merged):
                          // the transforms kernel counts them
   ROW_BIAS = 1u << 5,    // has bias entries
+  // filter order (neither bit: min-p, then top-k, then top-p); set only on
+  // rows where the order changes the kept set (top-p with top-k or min-p)
+  ROW_ORDER_JOINT = 1u << 8,      // top-k and top-p cut one distribution jointly
+  ROW_ORDER_MINP_LAST = 1u << 9,  // top-k, then top-p, then min-p
 };
+constexpr uint32_t kRowOrderBits = ROW_ORDER_JOINT | ROW_ORDER_MINP_LAST;
 
 struct alignas(16) RowParams {
   float temperature;

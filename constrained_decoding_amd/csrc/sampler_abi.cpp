@@ -89,6 +89,11 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   if (B <= 0 || V <= 0) return SAMPLER_EINVAL;
   if (B > kMaxB || V > kMaxV) return SAMPLER_ERANGE;
   if (!h->temperature) return SAMPLER_EINVAL;
+  if (h->filter_order < SAMPLER_ORDER_MINP_FIRST || h->filter_order > SAMPLER_ORDER_MINP_LAST)
+    return SAMPLER_EINVAL;
+  const uint32_t order_bits = h->filter_order == SAMPLER_ORDER_JOINT       ? ROW_ORDER_JOINT
+                              : h->filter_order == SAMPLER_ORDER_MINP_LAST ? ROW_ORDER_MINP_LAST
+                                                                           : 0u;
   if ((h->hist_indptr == nullptr) != (h->hist_ids == nullptr)) return SAMPLER_EINVAL;
   if ((h->bias_indptr == nullptr) != (h->bias_ids == nullptr) ||
       (h->bias_ids == nullptr) != (h->bias_vals == nullptr))
@@ -176,6 +181,8 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
         rp.flags |= ROW_MINP;
         flags |= SAMPLER_FLAG_NEED_MIN_P;
       }
+      // the order matters only where top-p meets another cut
+      if ((rp.flags & ROW_TOPP) && (rp.flags & (ROW_TOPK | ROW_MINP))) rp.flags |= order_bits;
     }
 
     // penalties: the row's history, raw (counted on the device) or as

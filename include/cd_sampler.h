@@ -111,7 +111,27 @@ extern "C" {
  *                the decode position ([SGL] "调用点": positions seed the
  *                draw, so a request's stream does not depend on the batch).
  *                default: the row index.
+ *   filter_order (a scalar for the whole batch) SAMPLER_ORDER_*: how min-p,
+ *                top-k and top-p stack.  Each cut keeps a prefix of the
+ *                tokens by value; the kept set is always S1 & Tk &
+ *                {t : mass strictly above t < top_p * M} (S1 the min-p set,
+ *                Tk the top-k set over every token) and the orders differ in
+ *                the mass M the top-p cut is normalised by:
+ *                  MINP_FIRST (0, default): M = mass of S1 & Tk -- min-p,
+ *                    then top-k, then top-p on what is left ([GLM] "采样",
+ *                    vLLM's order);
+ *                  JOINT (1): M = mass of every allowed token -- top-k and
+ *                    top-p cut one distribution and the intersection is kept
+ *                    ([SGL] "后端分支", filter_apply_order="joint"; min-p, if
+ *                    set, is intersected too);
+ *                  MINP_LAST (2): M = mass of Tk -- top-k, renormalise,
+ *                    top-p, renormalise, min-p ([SGL] "后端分支" and
+ *                    "概率裁剪的数学").
+ *                Any other value -> SAMPLER_EINVAL.
  * -------------------------------------------------------------------------- */
+#define SAMPLER_ORDER_MINP_FIRST 0
+#define SAMPLER_ORDER_JOINT 1
+#define SAMPLER_ORDER_MINP_LAST 2
 typedef struct sampler_host_params {
   int32_t B;
   int32_t V;
@@ -129,6 +149,7 @@ typedef struct sampler_host_params {
   const float *bias_vals;
   const uint64_t *seed;
   const uint64_t *offset;
+  int32_t filter_order;
 } sampler_host_params;
 
 /* ---- packed batch descriptor (plain data, returned by value) ------------- */

@@ -18,7 +18,7 @@ def to_device(batch: workloads.Batch):
 def pack(batch: workloads.Batch, stream=None):
     import constrained_decoding_amd as cds
     kw = dict(top_k=batch.top_k, top_p=batch.top_p, min_p=batch.min_p, seed=batch.seed,
-              offset=batch.offset)
+              offset=batch.offset, filter_order=batch.order)
     if batch.rep is not None:
         kw.update(repetition_penalty=batch.rep, frequency_penalty=batch.freq,
                   presence_penalty=batch.pres)

@@ -124,6 +124,11 @@ int main(int argc, char** argv) {
     h.bias_vals = bid.empty() ? nullptr : bval.data();
     h.seed = seed.data();
     h.offset = I(0, 1) ? off.data() : nullptr;
+    h.filter_order = (int32_t)I(0, 2);
+    if (I(0, 60) == 0) {
+      h.filter_order = I(0, 1) ? 3 : -1;
+      expect_bad = true;
+    }
     const size_t cap = sampler_params_bytes(B, (int64_t)hid.size(), (int64_t)bid.size());
     // an exact-size heap buffer: any write past the bound is an ASan report
     std::vector<unsigned char> buf(cap);

@@ -228,3 +228,20 @@ def test_dispatch_order_by_list_length(cds):
     T2 = np.array([0.5, 1.2, 0.5, 0.9], np.float32)
     buf, b = cds.pack_host(4, 151936, T2, top_k=np.full(4, 50, np.int32))
     assert np.frombuffer(buf[64 * 4:64 * 4 + 16].tobytes(), "<i4").tolist() == [1, 3, 0, 2]
+
+
+def test_filter_order_validated_and_flagged_where_it_matters(cds):
+    T = np.ones(4, np.float32)
+    k = np.array([20, 0, 20, 0], np.int32)
+    p = np.array([0.9, 0.9, 1.0, 0.9], np.float32)
+    mp = np.array([0.0, 0.1, 0.1, 0.0], np.float32)
+    for order, bit in ((0, 0), (1, 1 << 8), (2, 1 << 9)):
+        buf, b = cds.pack_host(4, 1000, T, top_k=k, top_p=p, min_p=mp, filter_order=order)
+        flags = _rowparams(buf, 4)["flags"]
+        # top-p with top-k, top-p with min-p: flagged; top-k + min-p without
+        # top-p, and top-p alone: the orders agree, no flag
+        assert [(f & (3 << 8)) for f in flags] == [bit, bit, 0, 0]
+    for bad in (-1, 3):
+        with pytest.raises(cds.SamplerError) as e:
+            cds.pack_host(4, 1000, T, top_k=k, top_p=p, min_p=mp, filter_order=bad)
+        assert e.value.code == -1

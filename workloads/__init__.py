@@ -64,6 +64,7 @@ class Batch:
     masks: Optional[np.ndarray] = None         # [B, ceil(V/32)] int32
     row_has_mask: Optional[np.ndarray] = None  # [B] uint8
     meta: dict = field(default_factory=dict)
+    order: int = 0                             # filter order (0: min-p first)
 
     @property
     def B(self) -> int:
@@ -87,7 +88,7 @@ class Batch:
     def oracle_params(self) -> dict:
         """Per-row parameters in the dict form ``oracle.pipeline`` takes."""
         p = dict(temperature=self.temperature, top_k=self.top_k, top_p=self.top_p,
-                 min_p=self.min_p, seed=self.seed, offset=self.offset)
+                 min_p=self.min_p, seed=self.seed, offset=self.offset, order=self.order)
         if self.rep is not None:
             p.update(rep=self.rep, freq=self.freq, pres=self.pres)
         if self.hist_indptr is not None:
@@ -119,7 +120,7 @@ class Batch:
                      take(self.min_p), take(self.seed), take(self.offset),
                      take(self.rep), take(self.freq), take(self.pres), hp, hi,
                      bp, bi, bv, take(self.masks), take(self.row_has_mask),
-                     dict(self.meta))
+                     dict(self.meta), self.order)
 
 
 # ---------------------------------------------------------------- pieces ---
