@@ -27,8 +27,8 @@ WAIT_NONE = -1
 EXPORTS = [
     "sampler_strerror", "sampler_version", "sampler_params_bytes", "sampler_pack_params",
     "sampler_pack_host", "sampler_apply_transforms", "sampler_apply_bitmask",
-    "sampler_workspace_bytes", "sampler_workspace_init", "sampler_sample",
-    "sampler_sample_ex",
+    "sampler_workspace_bytes", "sampler_workspace_bytes_batch", "sampler_workspace_init",
+    "sampler_sample", "sampler_sample_ex",
 ]
 
 
@@ -51,6 +51,8 @@ class Batch(ct.Structure):
         ("d_rows", ct.c_void_p), ("d_pen", ct.c_void_p), ("d_bias", ct.c_void_p),
         ("bytes", ct.c_size_t), ("n_sampled", ct.c_int32), ("n_hold", ct.c_int32),
         ("d_sampled", ct.c_void_p), ("n_hist_raw", ct.c_int64), ("d_hist_raw", ct.c_void_p),
+        ("d_slots", ct.c_void_p), ("ws_list_entries", ct.c_uint64), ("ws_records", ct.c_uint64),
+        ("ws_hist_slices", ct.c_uint64),
     ]
 
 
@@ -82,6 +84,7 @@ def _load():
         "sampler_apply_transforms": ([P, P, I64, P], ct.c_int),
         "sampler_apply_bitmask": ([P, ct.c_int, I64, I32, I32, P, I64, P, P], ct.c_int),
         "sampler_workspace_bytes": ([I32, I32], SZ),
+        "sampler_workspace_bytes_batch": ([P], SZ),
         "sampler_workspace_init": ([P, SZ, P], ct.c_int),
         "sampler_sample": ([P, P, ct.c_int, I64, P, I64, P, P, P, P, P, SZ, P], ct.c_int),
         "sampler_sample_ex": ([P, P, ct.c_int, I64, P, I64, P, P, P, P, P, SZ, P, P], ct.c_int),

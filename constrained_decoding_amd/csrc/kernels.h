@@ -11,6 +11,7 @@ namespace cds {
 
 struct SampleArgs {
   const RowParams* rows;
+  const RowSlots* slots;       // per row: where its lists, records and histograms live
   const int32_t* task_row;     // task k: row index | kPass2 (pass-2 task), -1: none
   int32_t n_groups;            // task groups of kXcds tasks (grid: n_groups * kXcds * P)
   const void* logits;
@@ -25,9 +26,9 @@ struct SampleArgs {
   RowSync* sync;
   Plan* plans;
   SliceHead* heads;
-  unsigned long long* hist;  // [B*P][NBINS]: count << kCountShift | mass
-  SliceBest* bests; // [B*P]
-  uint64_t* ulist;  // [B][P][SCAP] boundary tokens: okey(z) << 32 | ~t
+  unsigned long long* hist;  // slice histograms [NBINS]: count << kCountShift | mass
+  SliceBest* bests; // list records (RowSlots::rec)
+  uint64_t* ulist;  // list entries (RowSlots::list64, cap): okey(z) << 32 | ~t
   int32_t P;
   int64_t S;
   uint64_t spin_limit;  // wall-clock ticks a race task waits for its row's plan

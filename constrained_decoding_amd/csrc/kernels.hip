@@ -535,7 +535,7 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
   const bool topk = (rp.flags & ROW_TOPK) != 0, topp = (rp.flags & ROW_TOPP) != 0;
   const double Td = (double)rp.temperature;
   constexpr int JC = 10;  // slices per round of histogram loads
-  const unsigned long long* gh = a.hist + (int64_t)r * P * NBINS;
+  const unsigned long long* gh = a.hist + (int64_t)a.slots[r].hist * NBINS;
   unsigned long long hv[JC];
   // slice j's bins that land in row block blk (its bins 0 .. NT-1 for block 0)
   auto load_block = [&](int j0, int blk) {
@@ -1083,7 +1083,10 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
                                            SelShared& sel, RedScratch<NT>& red) {
   // the row's nl <= 64 lists: list j is number r * 2P + j
   const int tid = threadIdx.x;
-  const int64_t l0 = (int64_t)r * 2 * a.P;
+  const RowSlots rs = a.slots[r];
+  const int64_t l0 = rs.rec;                                    // record of list 0
+  const uint64_t* ulr = a.ulist + (int64_t)rs.list64 * 64;      // list 0
+  const int64_t lcap = rs.cap;                                  // entries per list
   const RowParams rp = a.rows[r];
   const double Td = (double)rp.temperature;
   // the slices' top two and list lengths; list offsets by a prefix sum
@@ -1103,8 +1106,8 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
         b.k1 += sh_k;
         b.k2 += sh_k;
       }
-      // a list past SCAP was not written: the row takes the exact path
-      cnt = sb.ucnt > (uint32_t)SCAP ? (uint32_t)(SCAP * 64 + 1) : sb.ucnt;
+      // a list past its capacity was not written: the row takes the exact path
+      cnt = sb.ucnt > (uint32_t)lcap ? (uint32_t)(lcap * 64 + 1) : sb.ucnt;
       if (pl.list_mode) lcut = __uint_as_float(sb.pad[2]);
     }
     lcut = wave_allreduce(lcut, [](float u, float v) { return fmaxf(u, v); });
@@ -1116,7 +1119,7 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
   __syncthreads();
   CDS_TRACE_ROW(0);
   const int n_all = off[nl];
-  if (n_all > SCAP * nl) return false;
+  if ((int64_t)n_all > lcap * nl) return false;
   // gather the slices' lists into LDS: every load of a round is issued before
   // any result is stored; element i = tid + k*NT of a round increases with k
   // (and over rounds), so its slice j (with off[j] <= i < off[j+1]) is found
@@ -1132,7 +1135,7 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
     for (int k = 0; k < KG; ++k) {
       const int i = tid + k * NT;
       while (j + 1 < nl && off[j + 1] <= i) ++j;
-      v[k] = i < n ? ld_u64(a.ulist + (l0 + j) * SCAP + (i - off[j])) : 0ull;
+      v[k] = i < n ? ld_u64(ulr + j * lcap + (i - off[j])) : 0ull;
     }
 #pragma unroll
     for (int k = 0; k < KG; ++k)
@@ -1148,7 +1151,7 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
       for (int k = 0; k < KG; ++k) {
         const int i = base + tid + k * NT;
         while (j + 1 < nl && off[j + 1] <= i) ++j;
-        v[k] = i < n_all ? ld_u64(a.ulist + (l0 + j) * SCAP + (i - off[j])) : 0ull;
+        v[k] = i < n_all ? ld_u64(ulr + j * lcap + (i - off[j])) : 0ull;
       }
       uint32_t c = 0u;
 #pragma unroll
@@ -1687,8 +1690,10 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
   const int64_t hi = min(lo + a.S, (int64_t)a.V);
   const int32_t tbase = (int32_t)lo + 4 * tid;  // token of chunk i: tbase + 4*NT*i
   const RowView rv = row_view<BF16>(a, r);
-  const int64_t slot = (int64_t)r * P + sl;       // heads and histograms
-  const int64_t lslot = (int64_t)r * 2 * P + sl;  // list and record: list sl of the row
+  const RowSlots rs = a.slots[r];
+  const int64_t slot = (int64_t)r * P + sl;        // head
+  const int64_t hslot = (int64_t)rs.hist + sl;     // histogram (HOLD rows)
+  const int64_t lslot = (int64_t)rs.rec + sl;      // record of list sl of the row
   CDS_TRACE(1);
 
   float x[E4][4];
@@ -1816,7 +1821,7 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
       // (the row's planner reads the slice totals first and only the top
       // bins of each histogram): bin b spans [(kmax-b)*delta,
       // (kmax-b+1)*delta) and holds fixed-point masses relative to its top
-      unsigned long long* gh = a.hist + slot * NBINS;
+      unsigned long long* gh = a.hist + hslot * NBINS;
       const double Td = (double)rp.temperature, dd = (double)g.delta;
       double msum = 0.0;
       for (int b = tid; b < NBINS; b += NT) {
@@ -1883,9 +1888,9 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
       cut = fmaxf(cut, bm);
     }
     const float cutv = sgpr_f(cut);
-    uint64_t* gl = a.ulist + lslot * SCAP;
+    uint64_t* gl = a.ulist + (int64_t)rs.list64 * 64 + (int64_t)sl * rs.cap;
     const uint32_t nst = list_tokens<NT, E4>(
-        x, tbase, (uint32_t)SCAP, sh.sel.wt,
+        x, tbase, rs.cap, sh.sel.wt,
         [&](float v) { return v >= cutv && v != CDS_NEG_INF; },
         [&](uint32_t pos, float v, int32_t t) { st_u64(gl + pos, ulist_entry(v, t)); });
     if (tid == 0) {
@@ -2016,7 +2021,9 @@ __device__ __forceinline__ void hold_race_task(const SampleArgs& a, int r, const
   const int32_t tbase = (int32_t)lo + 4 * tid;  // token of chunk i: tbase + 4*NT*i
   const RowView rv = row_view<BF16>(a, r);
   const int nl = halves * P;                                     // the row's lists
-  const int64_t slot = (int64_t)r * 2 * P + sl * halves + half;  // this task's list
+  const RowSlots rs = a.slots[r];
+  const int64_t li = (int64_t)sl * halves + half;                // this task's list
+  const int64_t slot = (int64_t)rs.rec + li;                     // ... and its record
   RowSync* sy = &a.sync[r];
   if (a.trace && tid == 0)
     a.trace[(size_t)blockIdx.x * 8] = (unsigned long long)r | ((unsigned long long)sl << 20) |
@@ -2074,11 +2081,11 @@ __device__ __forceinline__ void hold_race_task(const SampleArgs& a, int r, const
     // value bits), and the boundary-bin tokens to the slice's global list.
     // Boundary: below zs, at or above zc1, inside [a_lo, a_hi) or [k_lo, k_hi).
     uint2* stage = reinterpret_cast<uint2*>(sh.fin.list);
-    uint64_t* gl = a.ulist + slot * SCAP;
+    uint64_t* gl = a.ulist + (int64_t)rs.list64 * 64 + li * rs.cap;
     const float lo1 = fmaxf(a_lo, zc1), hi1 = fminf(a_hi, zs);
     const float lo2 = fmaxf(k_lo, zc1), hi2 = fminf(k_hi, zs);
     const uint2 nn = list_tokens2<NT, EC>(
-        x, tbase, (uint32_t)UCAP, (uint32_t)SCAP, sh.sel.wt,
+        x, tbase, (uint32_t)UCAP, rs.cap, sh.sel.wt,
         [&](float v) { return !SPLIT && v >= zs; },
         [&](uint32_t pos, float v, int32_t t) {
           stage[pos] = make_uint2((uint32_t)t, __float_as_uint(v));

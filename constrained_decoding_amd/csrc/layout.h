@@ -48,6 +48,21 @@ constexpr int32_t kHalf = 1 << 29;
 constexpr int32_t kSplit = 1 << 28;
 constexpr int32_t kTaskRow = kSplit - 1;  // the row index bits
 
+// Where a row's data lives in the workspace (written by the host pack, one
+// per row): the rows that list candidates (LIST rows: a list per slice; HOLD
+// rows: a boundary list per pass-2 task) get `lists` lists of `cap` entries
+// each, contiguous from entry 64*list64 of the list area, and one SliceBest
+// record per list (RACE rows: records only); HOLD rows get P slice
+// histograms from histogram slot `hist`.  Rows get only what their class
+// uses, so a workspace can be sized for the batch it serves.
+struct RowSlots {
+  uint32_t list64;  // first entry of the row's lists, in units of 64 entries
+  uint32_t cap;     // entries per list (0: the row lists nothing)
+  uint32_t rec;     // first SliceBest record of the row
+  uint32_t hist;    // first slice histogram of the row (HOLD rows)
+};
+static_assert(sizeof(RowSlots) == 16, "RowSlots layout");
+
 struct PenEntry {
   int32_t id;
   int32_t count;
@@ -204,6 +219,15 @@ struct WorkspaceLayout {
   int64_t S;
 };
 
+// Entries per list of a top-k row that lists candidates: room for twice its
+// per-slice share q plus a margin, in whole 64-entry blocks (a slice whose
+// list would pass it overflows, and the row takes the exact path).
+constexpr uint32_t list_cap_topk(int32_t q) {
+  return (uint32_t)((2 * q + 64 + 63) / 64 * 64) < (uint32_t)SCAP
+             ? (uint32_t)((2 * q + 64 + 63) / 64 * 64)
+             : (uint32_t)SCAP;
+}
+
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
 
 // Slices per row: the fewest that keep a slice register-resident.
@@ -222,7 +246,11 @@ constexpr int pass2_halves(int P, int32_t n_hold, int32_t B) {
   return (2 * P <= 64 && 4 * n_hold <= B) ? 2 : 1;
 }
 
-inline WorkspaceLayout workspace_layout(int32_t B, int32_t V) {
+// Workspace layout for B rows of V tokens whose rows take n_hist slice
+// histograms, n_rec list records and n_entries list entries in all (see
+// RowSlots).
+inline WorkspaceLayout workspace_layout(int32_t B, int32_t V, uint64_t n_hist, uint64_t n_rec,
+                                        uint64_t n_entries) {
   WorkspaceLayout L;
   L.P = choose_slices(V);
   L.S = round_up((V + L.P - 1) / L.P, 4);
@@ -239,13 +267,19 @@ inline WorkspaceLayout workspace_layout(int32_t B, int32_t V) {
   L.sync_off = take(sizeof(RowSync) * (size_t)kMaxRows);
   L.plan_off = take(sizeof(Plan) * (size_t)B);
   L.head_off = take(sizeof(SliceHead) * (size_t)B * L.P);
-  L.hist_off = take(sizeof(uint64_t) * NBINS * (size_t)B * L.P);
-  // lists and their records: up to 2P per row (a slice each, or a half slice
-  // each for pass-2 rows); list j of row r is number r * 2P + j
-  L.best_off = take(sizeof(SliceBest) * (size_t)B * 2 * L.P);
-  L.ulist_off = take(sizeof(uint64_t) * SCAP * (size_t)B * 2 * L.P);
+  L.hist_off = take(sizeof(uint64_t) * NBINS * (size_t)n_hist);
+  L.best_off = take(sizeof(SliceBest) * (size_t)n_rec);
+  L.ulist_off = take(sizeof(uint64_t) * (size_t)n_entries);
   L.total = off;
   return L;
+}
+
+// The largest layout any batch of B rows of V tokens can need: every row with
+// P histograms and 2P lists of SCAP entries.
+inline WorkspaceLayout workspace_layout(int32_t B, int32_t V) {
+  const int P = choose_slices(V);
+  return workspace_layout(B, V, (uint64_t)B * P, (uint64_t)B * 2 * P,
+                          (uint64_t)B * 2 * P * SCAP);
 }
 
 }  // namespace cds

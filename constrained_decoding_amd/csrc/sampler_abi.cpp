@@ -43,9 +43,10 @@ inline bool finite_f(float x) { return std::isfinite(x); }
 
 // Device parameter block: RowParams[B] | int32 row order [B] (the dispatch order
 // of sampler_sample) | int32 task rows [tasks_max(B)] (the sampling kernel's
-// tasks, see below) | PenEntry[n_pen] (counted histories) | BiasEntry[n_bias]
-// | int32 raw history ids [n_hist_raw]; the int32 arrays are padded to 16
-// bytes.  (The block stays small: it is copied every step.)
+// tasks, see below) | RowSlots[B] (workspace places) | PenEntry[n_pen]
+// (counted histories) | BiasEntry[n_bias] | int32 raw history ids
+// [n_hist_raw]; the int32 arrays are padded to 16 bytes.  (The block stays
+// small: it is copied every step.)
 //
 // Tasks: the sampling kernel runs groups of 8 tasks (one per XCD), each task
 // a row's P slices.  Task k is row task_row[k] & ~(kPass2 | kHalf) (-1:
@@ -58,8 +59,10 @@ size_t list_bytes(int32_t B) { return ((size_t)B * sizeof(int32_t) + 15) / 16 * 
 int32_t tasks_max(int32_t B) { return 24 * ((B + 7) / 8); }  // pass 1 + two pass-2 halves
 size_t task_bytes(int32_t B) { return list_bytes(tasks_max(B)); }
 
+size_t slots_bytes(int32_t B) { return sizeof(RowSlots) * (size_t)B; }
+
 size_t params_bytes_exact(int32_t B, int64_t n_pen, int64_t n_bias, int64_t n_raw) {
-  return sizeof(RowParams) * (size_t)B + list_bytes(B) + task_bytes(B) +
+  return sizeof(RowParams) * (size_t)B + list_bytes(B) + task_bytes(B) + slots_bytes(B) +
          sizeof(PenEntry) * (size_t)n_pen + sizeof(BiasEntry) * (size_t)n_bias +
          list_bytes((int32_t)n_raw);
 }
@@ -269,7 +272,8 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   }
   const size_t off_list = sizeof(RowParams) * (size_t)B;
   const size_t off_task = off_list + list_bytes(B);
-  const size_t off_pen = off_list + list_bytes(B) + task_bytes(B);
+  const size_t off_slots = off_task + task_bytes(B);
+  const size_t off_pen = off_slots + slots_bytes(B);
   std::memcpy(p, rows.data(), sizeof(RowParams) * rows.size());
   // dispatch order: the rows whose last slice has the longest way to go
   // first -- rows whose slices wait for the row's plan, then top-k rows with
@@ -328,6 +332,37 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
                                 (seq[q].first >= 2 && halves == 2 ? kSplit : 0) |
                                 (seq[q].first == 3 ? kHalf : 0);
     }
+  // workspace places: lists, records and histograms for the rows that use
+  // them (see RowSlots), in dispatch order
+  uint64_t ws_entries = 0, ws_rec = 0, ws_hist = 0;
+  {
+    RowSlots* sl = reinterpret_cast<RowSlots*>(p + off_slots);
+    std::memset(sl, 0, slots_bytes(B));
+    for (size_t q = 0; q < order.size(); ++q) {
+      const int32_t r = order[q];
+      const RowParams& rp = rows[(size_t)r];
+      const RowClass c = row_class_of(rp.flags, rp.top_k, P);
+      RowSlots x = {0u, 0u, 0u, 0u};
+      int lists = 0;
+      if (c == CLS_RACE) {
+        lists = P;  // records only
+      } else if (c == CLS_LIST) {
+        lists = P;
+        x.cap = (rp.flags & ROW_TOPK) ? list_cap_topk(list_q(rp.top_k, P)) : (uint32_t)SCAP;
+      } else if (c == CLS_HOLD) {
+        lists = halves * P;
+        x.cap = SCAP;
+        x.hist = (uint32_t)ws_hist;
+        ws_hist += (uint64_t)P;
+      }
+      x.rec = (uint32_t)ws_rec;
+      x.list64 = (uint32_t)(ws_entries / 64);
+      ws_rec += (uint64_t)lists;
+      ws_entries += (uint64_t)lists * x.cap;
+      sl[r] = x;
+    }
+  }
+
   // counted penalty entries, the bias, then the raw history ids in row order
   // (runs of consecutive raw rows are one copy each: their CSR ranges adjoin)
   // (memcpy from an empty vector's null data() is undefined even for 0 bytes)
@@ -377,15 +412,20 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   out->bytes = bytes;
   out->n_sampled = (int32_t)sampled.size();
   out->n_hold = n_hold;
+  out->ws_list_entries = ws_entries;
+  out->ws_records = ws_rec;
+  out->ws_hist_slices = ws_hist;
   return SAMPLER_OK;
 }
 
 void set_pointers(sampler_batch* out, const void* base) {
   const unsigned char* b = static_cast<const unsigned char*>(base);
   const size_t off_list = sizeof(RowParams) * (size_t)out->B;
-  const size_t off_pen = off_list + list_bytes(out->B) + task_bytes(out->B);
+  const size_t off_slots = off_list + list_bytes(out->B) + task_bytes(out->B);
+  const size_t off_pen = off_slots + slots_bytes(out->B);
   out->d_rows = b;
   out->d_sampled = b + off_list;
+  out->d_slots = b + off_slots;
   out->d_pen = b + off_pen;
   out->d_bias = b + off_pen + sizeof(PenEntry) * (size_t)out->n_pen;
   out->d_hist_raw = b + off_pen + sizeof(PenEntry) * (size_t)out->n_pen +
@@ -393,6 +433,11 @@ void set_pointers(sampler_batch* out, const void* base) {
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// The workspace a packed batch needs (its rows' lists, records, histograms).
+WorkspaceLayout batch_layout(const sampler_batch* b) {
+  return workspace_layout(b->B, b->V, b->ws_hist_slices, b->ws_records, b->ws_list_entries);
+}
 
 }  // namespace
 
@@ -481,6 +526,11 @@ size_t sampler_workspace_bytes(int32_t B, int32_t V) {
   return workspace_layout(B, V).total;
 }
 
+size_t sampler_workspace_bytes_batch(const sampler_batch* b) {
+  if (!b || b->B <= 0 || b->V <= 0 || b->B > kMaxB || b->V > kMaxV) return 0;
+  return batch_layout(b).total;
+}
+
 int sampler_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
   if (!workspace || ws_bytes % 4 != 0) return SAMPLER_EINVAL;
   const hipError_t e = launch_fill_zero(workspace, ws_bytes, static_cast<hipStream_t>(stream));
@@ -508,7 +558,8 @@ int sampler_sample_ex(const sampler_batch* b, const void* logits, int dtype, int
   const bool bf16 = dtype == SAMPLER_DTYPE_BF16;
   if (!aligned(logits, bf16 ? 2 : 4)) return SAMPLER_EINVAL;
   if (bitmask && mask_ld < ((int64_t)V + 31) / 32) return SAMPLER_EINVAL;
-  const WorkspaceLayout L = workspace_layout(B, V);
+  if (!b->d_slots) return SAMPLER_EINVAL;
+  const WorkspaceLayout L = batch_layout(b);
   if (!workspace || ws_bytes < L.total) return SAMPLER_ENOSPC;
   if (!aligned(workspace, 256)) return SAMPLER_EINVAL;
 
@@ -516,6 +567,7 @@ int sampler_sample_ex(const sampler_batch* b, const void* logits, int dtype, int
   SampleArgs a;
   if (b->n_sampled < 0 || b->n_sampled > B || !b->d_sampled) return SAMPLER_EINVAL;
   a.rows = static_cast<const RowParams*>(b->d_rows);
+  a.slots = static_cast<const RowSlots*>(b->d_slots);
   if (b->n_hold < 0 || b->n_hold > b->n_sampled) return SAMPLER_EINVAL;
   {
     const unsigned char* t = static_cast<const unsigned char*>(b->d_sampled) + list_bytes(B);

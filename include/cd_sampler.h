@@ -183,6 +183,10 @@ typedef struct sampler_batch {
   int64_t n_hist_raw;   /* raw history ids (histories of up to 4096 tokens,
                            counted on the device by the transforms kernel)  */
   const void *d_hist_raw; /* dev: int32 raw history ids inside d_buf        */
+  const void *d_slots;  /* dev: per-row workspace places inside d_buf       */
+  uint64_t ws_list_entries; /* workspace the batch's rows need: candidate-  */
+  uint64_t ws_records;      /* list entries, list records and slice         */
+  uint64_t ws_hist_slices;  /* histograms (see sampler_workspace_bytes_batch) */
 } sampler_batch;
 
 /* Message for a SAMPLER_* return code (static storage). */
@@ -244,8 +248,15 @@ int sampler_apply_bitmask(void *logits, int dtype, int64_t ld, int32_t B,
                           int32_t V, const int32_t *bitmask, int64_t mask_ld,
                           const uint8_t *row_has_mask, void *stream);
 
-/* Device workspace bytes sampler_sample needs for B rows of V tokens. */
+/* Device workspace bytes sampler_sample needs for any batch of B rows of V
+ * tokens (every row with room for its largest class). */
 size_t sampler_workspace_bytes(int32_t B, int32_t V);
+
+/* Device workspace bytes sampler_sample needs for this packed batch: only
+ * the rows that list candidates get lists (sized by their class), only rows
+ * whose cut needs the row's histogram get histograms.  At most
+ * sampler_workspace_bytes(b->B, b->V); 0 on an invalid descriptor. */
+size_t sampler_workspace_bytes_batch(const sampler_batch *b);
 
 /* Zero a workspace on `stream` (a fill kernel, safe under graph capture).
  * A workspace must be zero before its first sampler_sample; every
@@ -261,7 +272,8 @@ int sampler_workspace_init(void *workspace, size_t ws_bytes, void *stream);
  *   row_has_mask dev uint8 [B] or NULL.
  *   out_ids     dev int32 [B] (required); out_logprobs dev float [B] or NULL;
  *               out_status dev int32 [B] or NULL.
- *   workspace   dev, >= sampler_workspace_bytes(B, V), zeroed once.
+ *   workspace   dev, >= sampler_workspace_bytes_batch(b) (at most
+ *               sampler_workspace_bytes(B, V)), zeroed once.
  * Per row, on the transformed (and masked) logits z:
  *   greedy rows: id = lowest index of max z; logprob = log_softmax(z)[id]
  *     ([SGL] "贪心路径"; [GLM] "采样": greedy rows use the logits before

@@ -89,8 +89,8 @@ def test_penalty_counts_and_bias_dedup(cds):
     assert b.n_sampled == 3
     assert np.frombuffer(buf[64 * 3:64 * 3 + 12].tobytes(), "<i4").tolist() == [0, 1, 2]
     # the row order (room for B int32, 16-byte padded), then the task table: 24
-    # task rows (int32)
-    pen_off = 64 * 3 + 16 + 96
+    # task rows (int32), then the rows' workspace places (16 bytes each)
+    pen_off = 64 * 3 + 16 + 96 + 16 * 3
     assert b.n_pen == 0 and b.n_hist_raw == 4
     raw_off = pen_off + 8 * b.n_bias
     pen = np.frombuffer(buf[raw_off:raw_off + 4 * b.n_hist_raw].tobytes(), "<i4")
@@ -245,3 +245,29 @@ def test_filter_order_validated_and_flagged_where_it_matters(cds):
         with pytest.raises(cds.SamplerError) as e:
             cds.pack_host(4, 1000, T, top_k=k, top_p=p, min_p=mp, filter_order=bad)
         assert e.value.code == -1
+
+
+def test_workspace_per_batch_smaller_than_bound(cds):
+    """Workspace a packed batch needs: lists only for rows that list
+    candidates (top-k rows at their class's capacity), histograms only for
+    rows whose cut needs the row's histogram; the per-shape bound covers
+    every batch."""
+    V, P = 151936, 10
+    B = 8
+    T = np.ones(B, np.float32)
+    T[0] = 0.0                                              # greedy: nothing
+    k = np.array([0, 20, 0, 0, 50, 0, 1000, 0], np.int32)
+    p = np.array([1, 0.9, 0.9, 1, 1, 1, 0.9, 1], np.float32)
+    mp = np.array([0, 0, 0, 0.05, 0, 0, 0, 0], np.float32)
+    _, b = cds.pack_host(B, V, T, top_k=k, top_p=p, min_p=mp)
+    need = cds.lib.sampler_workspace_bytes_batch(ct.byref(b))
+    bound = cds.lib.sampler_workspace_bytes(B, V)
+    assert 0 < need < bound
+    # row 2 (top-p only) and row 6 (k = 1000 lists) ... row 2 is the only
+    # HOLD row: P histograms
+    assert b.ws_hist_slices == P
+    # lists: rows 1, 3, 4, 6 (LIST) P each, row 2 (HOLD) 2P (half slices),
+    # rows 5, 7 (no cut: RACE) records only
+    assert b.ws_records == P * (4 + 2 + 2)
+    caps = {20: 128, 50: 192, 1000: 640}     # 2q + 64 rounded up to 64 entries
+    assert b.ws_list_entries == P * (caps[20] + 2048 + caps[50] + caps[1000]) + 2 * P * 2048
