@@ -28,7 +28,7 @@ EXPORTS = [
     "sampler_strerror", "sampler_version", "sampler_params_bytes", "sampler_pack_params",
     "sampler_pack_host", "sampler_apply_transforms", "sampler_apply_bitmask",
     "sampler_workspace_bytes", "sampler_workspace_bytes_batch", "sampler_workspace_init",
-    "sampler_sample", "sampler_sample_ex",
+    "sampler_sample", "sampler_sample_ex", "sampler_sample_static",
 ]
 
 
@@ -88,6 +88,7 @@ def _load():
         "sampler_workspace_init": ([P, SZ, P], ct.c_int),
         "sampler_sample": ([P, P, ct.c_int, I64, P, I64, P, P, P, P, P, SZ, P], ct.c_int),
         "sampler_sample_ex": ([P, P, ct.c_int, I64, P, I64, P, P, P, P, P, SZ, P, P], ct.c_int),
+        "sampler_sample_static": ([P, P, ct.c_int, I64, P, I64, P, P, P, P, P], ct.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)

@@ -49,6 +49,11 @@ hipError_t launch_bitmask(void* logits, bool bf16, int64_t ld, int32_t B, int32_
                           const int32_t* mask, int64_t mask_ld, const uint8_t* row_has_mask,
                           hipStream_t stream);
 hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream);
+// Device address of the library's own workspace (kStaticWorkspaceBytes) on
+// the current device; the first call on a device clears its row counters on
+// `stream`.
+hipError_t static_workspace(void** ptr, hipStream_t stream);
+
 // algo 0: the fused fast path; algo 1: the row-serial exact path.
 hipError_t launch_sample(const SampleArgs& a, bool bf16, bool vec, int algo,
                          const KernelEvents* ev, hipStream_t stream);

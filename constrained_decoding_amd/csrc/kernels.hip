@@ -28,6 +28,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
+#include <mutex>
 
 #include "device_common.h"
 #include "kernels.h"
@@ -2251,6 +2252,40 @@ hipError_t launch_fill_zero(void* ptr, size_t bytes, hipStream_t stream) {
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      static_cast<uint32_t*>(ptr), n);
   return hipGetLastError();
+}
+
+// ---- the library's own workspace (sampler_sample_static) ---------------------
+// A file-scope device array, so that callers that cannot allocate (graph
+// capture, allocation-free serving loops) need no workspace of their own.
+// Each device the library runs on holds its copy until the process ends.  In
+// host code `scratch` names a host-side stand-in: its device address comes
+// from hipGetSymbolAddress, once per device, and only that address is used.
+static __device__ __align__(256) unsigned char scratch[kStaticWorkspaceBytes];
+
+namespace {
+constexpr int kMaxStaticDevices = 64;
+std::mutex g_static_mu;
+void* g_static_ptr[kMaxStaticDevices];  // device address of `scratch` per device
+}  // namespace
+
+hipError_t static_workspace(void** ptr, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxStaticDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  if (!g_static_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    // the row counters must start at zero (every call leaves them zero
+    // again); a fill kernel, not a memset, so the call is capturable
+    e = launch_fill_zero(p, workspace_layout(1, 1, 0, 0, 0).plan_off, stream);
+    if (e != hipSuccess) return e;
+    g_static_ptr[dev] = p;
+  }
+  *ptr = g_static_ptr[dev];
+  return hipSuccess;
 }
 
 constexpr int kExactNT = 512;

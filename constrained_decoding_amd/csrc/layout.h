@@ -103,6 +103,8 @@ constexpr int kMaxSlices = 64;
 constexpr int kShortList = 256;   // a row's listed tokens one wave of the finisher resolves
 constexpr int kXcds = 8;          // XCDs of an MI355X (workgroups go round-robin over them)
 constexpr int kMaxRows = 65535;
+// Size of the library's own workspace (sampler_sample_static), per device.
+constexpr size_t kStaticWorkspaceBytes = (size_t)64 << 20;
 
 // How a row's slices work in the sampling kernel.  The host dispatches the rows
 // in the order HOLD, then top-k LIST rows by the length of their lists, then

@@ -624,6 +624,18 @@ int sampler_sample_ex(const sampler_batch* b, const void* logits, int dtype, int
   return e == hipSuccess ? SAMPLER_OK : SAMPLER_EHIP;
 }
 
+int sampler_sample_static(const sampler_batch* b, const void* logits, int dtype, int64_t ld,
+                          const int32_t* bitmask, int64_t mask_ld, const uint8_t* row_has_mask,
+                          int32_t* out_ids, float* out_logprobs, int32_t* out_status,
+                          void* stream) {
+  if (!b || b->B <= 0 || b->V <= 0 || b->B > kMaxB || b->V > kMaxV) return SAMPLER_EINVAL;
+  if (batch_layout(b).total > kStaticWorkspaceBytes) return SAMPLER_ENOSPC;
+  void* ws = nullptr;
+  if (static_workspace(&ws, static_cast<hipStream_t>(stream)) != hipSuccess) return SAMPLER_EHIP;
+  return sampler_sample_ex(b, logits, dtype, ld, bitmask, mask_ld, row_has_mask, out_ids,
+                           out_logprobs, out_status, ws, kStaticWorkspaceBytes, stream, nullptr);
+}
+
 int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_t ld,
                    const int32_t* bitmask, int64_t mask_ld, const uint8_t* row_has_mask,
                    int32_t* out_ids, float* out_logprobs, int32_t* out_status, void* workspace,

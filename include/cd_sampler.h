@@ -298,6 +298,22 @@ int sampler_sample(const sampler_batch *b, const void *logits, int dtype,
                    float *out_logprobs, int32_t *out_status, void *workspace,
                    size_t ws_bytes, void *stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, allocation-free serving loops, harnesses that forbid hipMalloc:
+ * sampler_sample with no workspace argument.  The workspace is the library's
+ * own device array of SAMPLER_STATIC_WORKSPACE_BYTES (64 MiB), one per
+ * device, held until the process ends; the call allocates nothing.  The first
+ * call on a device clears the array's row counters on its stream (a fill
+ * kernel).  Every call on a device shares that array: calls that overlap on
+ * one device race (keep them on one stream).  A batch that needs more than
+ * the array (sampler_workspace_bytes_batch) -> SAMPLER_ENOSPC, nothing
+ * launched.  Other arguments and errors as sampler_sample. */
+#define SAMPLER_STATIC_WORKSPACE_BYTES ((size_t)64 << 20)
+int sampler_sample_static(const sampler_batch *b, const void *logits, int dtype,
+                          int64_t ld, const int32_t *bitmask, int64_t mask_ld,
+                          const uint8_t *row_has_mask, int32_t *out_ids,
+                          float *out_logprobs, int32_t *out_status, void *stream);
+
 /* ---- per-call options -----------------------------------------------------
  * sampler_sample_ex is sampler_sample with a per-call options record; every
  * option belongs to that one call (nothing is kept between calls).

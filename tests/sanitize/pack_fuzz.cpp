@@ -32,6 +32,7 @@ hipError_t launch_bitmask(void*, bool, int64_t, int32_t, int32_t, const int32_t*
   return hipSuccess;
 }
 hipError_t launch_fill_zero(void*, size_t, hipStream_t) { return hipSuccess; }
+hipError_t static_workspace(void**, hipStream_t) { return hipErrorNotSupported; }
 hipError_t launch_sample(const SampleArgs&, bool, bool, int, const KernelEvents*, hipStream_t) {
   return hipSuccess;
 }
