@@ -50,6 +50,11 @@ def parse():
                     help="rows of the workload the oracle is timed on (cpu_baseline)")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--algo", type=int, default=0)
+    ap.add_argument("--upload", choices=["auto", "side", "same"], default="auto",
+                    help="parameter upload on a side stream (overlapping the previous "
+                         "step) or on the compute stream; auto: the side stream for "
+                         "blocks over 64 KB (measured: it pays for c3's 434 KB block, "
+                         "and stalls the host for mid-size blocks such as c5's 41 KB)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (the "
                          "reference point for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -217,9 +222,11 @@ def main():
             torch.empty(B, dtype=torch.float32, device="cuda"),
             torch.empty(B, dtype=torch.int32, device="cuda"))
 
-    # Everything a step needs from the host, prepared once per input set: the
-    # host parameter arrays (what a serving loop would hand over each step),
-    # a device parameter block and a pinned staging buffer.
+    # The host parameter arrays of each input set (what a serving loop hands
+    # over each step), and a ring of parameter slots -- a device block, a
+    # pinned staging buffer and their events -- deep enough that a slot's
+    # previous step has long finished when it comes round again (a copy that
+    # has to wait on unfinished kernels stalls the host inside the enqueue).
     host = []
     for b in sets:
         kw = dict(top_k=b.top_k, top_p=b.top_p, min_p=b.min_p, seed=b.seed, offset=b.offset)
@@ -228,14 +235,15 @@ def main():
                       presence_penalty=b.pres, hist_indptr=b.hist_indptr, hist_ids=b.hist_ids)
         if b.bias_indptr is not None:
             kw.update(bias_indptr=b.bias_indptr, bias_ids=b.bias_ids, bias_vals=b.bias_vals)
-        h = bd._HostArrays(B, V, b.temperature, **kw)
-        nbytes = h.bytes_bound()
-        host.append(dict(h=h, nbytes=nbytes,
-                         d_buf=torch.empty(nbytes, dtype=torch.uint8, device="cuda"),
-                         staging=torch.empty(nbytes, dtype=torch.uint8, pin_memory=True),
-                         batch=bd.Batch(), copied=None, used=None))
+        host.append(bd._HostArrays(B, V, b.temperature, **kw))
+    nbytes = max(h.bytes_bound() for h in host)
+    if args.upload == "auto":
+        args.upload = "side" if nbytes > (64 << 10) else "same"
+    ring = [dict(d_buf=torch.empty(nbytes, dtype=torch.uint8, device="cuda"),
+                 staging=torch.empty(nbytes, dtype=torch.uint8, pin_memory=True),
+                 batch=bd.Batch(), copied=None, used=None) for _ in range(8)]
     compute = torch.cuda.current_stream()
-    copy_s = torch.cuda.Stream()
+    copy_s = torch.cuda.Stream() if args.upload == "side" else compute
     lib = bd.lib
     mask_args = [(None, 0, None) if masks[j] is None else
                  (masks[j].data_ptr(), masks[j].stride(0),
@@ -246,16 +254,16 @@ def main():
 
     def step(i, ev=None, j=None):
         j = i % len(sets) if j is None else j
-        hs = host[j]
+        hs = ring[i % len(ring)]
         # the staging buffer and the device block are reused: the previous copy
         # out of the staging buffer must have run, and the previous kernels that
         # read the device block must be done before the copy overwrites it
         if hs["copied"] is not None:
             hs["copied"].synchronize()
-        if hs["used"] is not None:
+        if hs["used"] is not None and copy_s is not compute:
             copy_s.wait_event(hs["used"])
         t0 = time.perf_counter()
-        rc = lib.sampler_pack_params(ct.byref(hs["h"].hp), hs["d_buf"].data_ptr(), hs["nbytes"],
+        rc = lib.sampler_pack_params(ct.byref(host[j].hp), hs["d_buf"].data_ptr(), nbytes,
                                      hs["staging"].data_ptr(), copy_s.cuda_stream,
                                      ct.byref(hs["batch"]))
         pack_s.append(time.perf_counter() - t0)
@@ -264,7 +272,8 @@ def main():
         copied = torch.cuda.Event()
         copied.record(copy_s)
         hs["copied"] = copied
-        compute.wait_event(copied)
+        if copy_s is not compute:
+            compute.wait_event(copied)
         if transforms:
             rc = lib.sampler_apply_transforms(ct.byref(hs["batch"]), work[j].data_ptr(),
                                               work[j].stride(0), compute.cuda_stream)
@@ -352,6 +361,7 @@ def main():
                    "algo": "fast" if args.algo == 0 else "row-exact"},
         "pipeline_gbs": round(alg / (ms_per_step * 1e-3) / 1e9, 1),
         "host_pack_us": round(host_pack_us, 2),
+        "param_upload": args.upload,
         "roofline": {"bound": "hbm", "kernel": "sample_kernel", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),

@@ -536,7 +536,8 @@ __device__ __forceinline__ void plan_row(const SampleArgs& a, int r, bool hist, 
   const bool topk = (rp.flags & ROW_TOPK) != 0, topp = (rp.flags & ROW_TOPP) != 0;
   const double Td = (double)rp.temperature;
   constexpr int JC = 10;  // slices per round of histogram loads
-  const unsigned long long* gh = a.hist + (int64_t)a.slots[r].hist * NBINS;
+  const unsigned long long* gh =
+      a.hist + (int64_t)(a.slots[r].rec / (2u * (uint32_t)P)) * P * NBINS;
   unsigned long long hv[JC];
   // slice j's bins that land in row block blk (its bins 0 .. NT-1 for block 0)
   auto load_block = [&](int j0, int blk) {
@@ -1085,10 +1086,10 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
   // the row's nl <= 64 lists: list j is number r * 2P + j
   const int tid = threadIdx.x;
   const RowSlots rs = a.slots[r];
+  const RowParams rp = a.rows[r];
   const int64_t l0 = rs.rec;                                    // record of list 0
   const uint64_t* ulr = a.ulist + (int64_t)rs.list64 * 64;      // list 0
-  const int64_t lcap = rs.cap;                                  // entries per list
-  const RowParams rp = a.rows[r];
+  const int64_t lcap = row_list_cap(rp.flags, rp.top_k, a.P);   // entries per list
   const double Td = (double)rp.temperature;
   // the slices' top two and list lengths; list offsets by a prefix sum
   Top2 b = top2_init();
@@ -1692,8 +1693,9 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
   const int32_t tbase = (int32_t)lo + 4 * tid;  // token of chunk i: tbase + 4*NT*i
   const RowView rv = row_view<BF16>(a, r);
   const RowSlots rs = a.slots[r];
-  const int64_t slot = (int64_t)r * P + sl;        // head
-  const int64_t hslot = (int64_t)rs.hist + sl;     // histogram (HOLD rows)
+  const uint32_t lcap = row_list_cap(rp.flags, rp.top_k, P);
+  const int64_t slot = (int64_t)r * P + sl;                              // head
+  const int64_t hslot = (int64_t)(rs.rec / (2u * (uint32_t)P)) * P + sl;  // histogram (HOLD)
   const int64_t lslot = (int64_t)rs.rec + sl;      // record of list sl of the row
   CDS_TRACE(1);
 
@@ -1889,9 +1891,9 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
       cut = fmaxf(cut, bm);
     }
     const float cutv = sgpr_f(cut);
-    uint64_t* gl = a.ulist + (int64_t)rs.list64 * 64 + (int64_t)sl * rs.cap;
+    uint64_t* gl = a.ulist + (int64_t)rs.list64 * 64 + (int64_t)sl * lcap;
     const uint32_t nst = list_tokens<NT, E4>(
-        x, tbase, rs.cap, sh.sel.wt,
+        x, tbase, lcap, sh.sel.wt,
         [&](float v) { return v >= cutv && v != CDS_NEG_INF; },
         [&](uint32_t pos, float v, int32_t t) { st_u64(gl + pos, ulist_entry(v, t)); });
     if (tid == 0) {
@@ -2082,11 +2084,12 @@ __device__ __forceinline__ void hold_race_task(const SampleArgs& a, int r, const
     // value bits), and the boundary-bin tokens to the slice's global list.
     // Boundary: below zs, at or above zc1, inside [a_lo, a_hi) or [k_lo, k_hi).
     uint2* stage = reinterpret_cast<uint2*>(sh.fin.list);
-    uint64_t* gl = a.ulist + (int64_t)rs.list64 * 64 + li * rs.cap;
+    const uint32_t lcap = row_list_cap(rp.flags, rp.top_k, P);
+    uint64_t* gl = a.ulist + (int64_t)rs.list64 * 64 + li * lcap;
     const float lo1 = fmaxf(a_lo, zc1), hi1 = fminf(a_hi, zs);
     const float lo2 = fmaxf(k_lo, zc1), hi2 = fminf(k_hi, zs);
     const uint2 nn = list_tokens2<NT, EC>(
-        x, tbase, (uint32_t)UCAP, rs.cap, sh.sel.wt,
+        x, tbase, (uint32_t)UCAP, lcap, sh.sel.wt,
         [&](float v) { return !SPLIT && v >= zs; },
         [&](uint32_t pos, float v, int32_t t) {
           stage[pos] = make_uint2((uint32_t)t, __float_as_uint(v));

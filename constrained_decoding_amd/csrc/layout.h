@@ -50,18 +50,17 @@ constexpr int32_t kTaskRow = kSplit - 1;  // the row index bits
 
 // Where a row's data lives in the workspace (written by the host pack, one
 // per row): the rows that list candidates (LIST rows: a list per slice; HOLD
-// rows: a boundary list per pass-2 task) get `lists` lists of `cap` entries
+// rows: a boundary list per pass-2 task) get lists of row_list_cap() entries
 // each, contiguous from entry 64*list64 of the list area, and one SliceBest
-// record per list (RACE rows: records only); HOLD rows get P slice
-// histograms from histogram slot `hist`.  Rows get only what their class
-// uses, so a workspace can be sized for the batch it serves.
+// record per list (RACE rows: records only).  HOLD rows come first in the
+// record area with 2P records each, so a HOLD row's P slice histograms start
+// at histogram slot (rec / 2P) * P.  Rows get only what their class uses, so
+// a workspace can be sized for the batch it serves.
 struct RowSlots {
   uint32_t list64;  // first entry of the row's lists, in units of 64 entries
-  uint32_t cap;     // entries per list (0: the row lists nothing)
   uint32_t rec;     // first SliceBest record of the row
-  uint32_t hist;    // first slice histogram of the row (HOLD rows)
 };
-static_assert(sizeof(RowSlots) == 16, "RowSlots layout");
+static_assert(sizeof(RowSlots) == 8, "RowSlots layout");
 
 struct PenEntry {
   int32_t id;
@@ -141,6 +140,12 @@ constexpr RowClass row_class_of(uint32_t flags, int32_t top_k, int32_t P) {
          : (flags & ROW_TOPP)  ? CLS_HOLD
                                : CLS_RACE;
 }
+
+// Entries per list of a row: top-k rows that list candidates hold twice their
+// share and a margin (list_cap_topk), min-p rows and second-pass boundary
+// lists SCAP, rows that list nothing 0.
+constexpr uint32_t list_cap_topk(int32_t q);
+constexpr uint32_t row_list_cap(uint32_t flags, int32_t top_k, int32_t P);
 
 // ---- workspace ------------------------------------------------------------
 // Per-row meeting point of the row's workgroups.  Counters count the slices
@@ -228,6 +233,12 @@ constexpr uint32_t list_cap_topk(int32_t q) {
   return (uint32_t)((2 * q + 64 + 63) / 64 * 64) < (uint32_t)SCAP
              ? (uint32_t)((2 * q + 64 + 63) / 64 * 64)
              : (uint32_t)SCAP;
+}
+constexpr uint32_t row_list_cap(uint32_t flags, int32_t top_k, int32_t P) {
+  return row_class_of(flags, top_k, P) == CLS_HOLD ? (uint32_t)SCAP
+         : row_class_of(flags, top_k, P) == CLS_LIST
+             ? ((flags & ROW_TOPK) ? list_cap_topk(list_q(top_k, P)) : (uint32_t)SCAP)
+             : 0u;
 }
 
 inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }

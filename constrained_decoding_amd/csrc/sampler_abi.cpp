@@ -57,12 +57,17 @@ inline bool finite_f(float x) { return std::isfinite(x); }
 // once the row's plan is out.
 size_t list_bytes(int32_t B) { return ((size_t)B * sizeof(int32_t) + 15) / 16 * 16; }
 int32_t tasks_max(int32_t B) { return 24 * ((B + 7) / 8); }  // pass 1 + two pass-2 halves
-size_t task_bytes(int32_t B) { return list_bytes(tasks_max(B)); }
+// the task table a batch uses: pass-1 groups, and pass-2 groups of its n_hold
+// rows (two per group of rows when their tasks take half slices)
+int32_t tasks_used(int32_t B, int32_t n_hold, bool split) {
+  return 8 * ((B + 7) / 8 + (split ? 2 : 1) * ((n_hold + 7) / 8));
+}
 
 size_t slots_bytes(int32_t B) { return sizeof(RowSlots) * (size_t)B; }
 
-size_t params_bytes_exact(int32_t B, int64_t n_pen, int64_t n_bias, int64_t n_raw) {
-  return sizeof(RowParams) * (size_t)B + list_bytes(B) + task_bytes(B) + slots_bytes(B) +
+size_t params_bytes_exact(int32_t B, int32_t n_tasks, int64_t n_pen, int64_t n_bias,
+                          int64_t n_raw) {
+  return sizeof(RowParams) * (size_t)B + list_bytes(B) + list_bytes(n_tasks) + slots_bytes(B) +
          sizeof(PenEntry) * (size_t)n_pen + sizeof(BiasEntry) * (size_t)n_bias +
          list_bytes((int32_t)n_raw);
 }
@@ -261,20 +266,6 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   }
   if (bias.size() > (size_t)INT32_MAX) return SAMPLER_ERANGE;
 
-  const int64_t n_pen = (int64_t)pen.size();
-  const size_t bytes = params_bytes_exact(B, n_pen, (int64_t)bias.size(), n_raw);
-  unsigned char* p = dst;
-  if (!p) {
-    tmp->resize(bytes);
-    p = tmp->data();
-  } else if (cap < bytes) {
-    return SAMPLER_ENOSPC;
-  }
-  const size_t off_list = sizeof(RowParams) * (size_t)B;
-  const size_t off_task = off_list + list_bytes(B);
-  const size_t off_slots = off_task + task_bytes(B);
-  const size_t off_pen = off_slots + slots_bytes(B);
-  std::memcpy(p, rows.data(), sizeof(RowParams) * rows.size());
   // dispatch order: the rows whose last slice has the longest way to go
   // first -- rows whose slices wait for the row's plan, then top-k rows with
   // long candidate lists, then top-k rows whose lists are too long for the
@@ -304,13 +295,29 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   int32_t n_hold = 0;
   while (n_hold < (int32_t)order.size() && rank(order[(size_t)n_hold]) == 0) ++n_hold;
   order.insert(order.end(), greedy_rows.begin(), greedy_rows.end());
+  const int halves = pass2_halves(P, n_hold, B);
+  if (halves == 2) flags |= SAMPLER_FLAG_SPLIT_PASS2;
+  const int32_t n_tasks = tasks_used(B, n_hold, halves == 2);
+
+  const int64_t n_pen = (int64_t)pen.size();
+  const size_t bytes = params_bytes_exact(B, n_tasks, n_pen, (int64_t)bias.size(), n_raw);
+  unsigned char* p = dst;
+  if (!p) {
+    tmp->resize(bytes);
+    p = tmp->data();
+  } else if (cap < bytes) {
+    return SAMPLER_ENOSPC;
+  }
+  const size_t off_list = sizeof(RowParams) * (size_t)B;
+  const size_t off_task = off_list + list_bytes(B);
+  const size_t off_slots = off_task + list_bytes(n_tasks);
+  const size_t off_pen = off_slots + slots_bytes(B);
+  std::memcpy(p, rows.data(), sizeof(RowParams) * rows.size());
   if (!order.empty()) std::memcpy(p + off_list, order.data(), sizeof(int32_t) * order.size());
   std::memset(p + off_list + sizeof(int32_t) * order.size(), 0,
               list_bytes(B) - sizeof(int32_t) * order.size());
   // the task groups: pass-1 group g, and pass-2 group g - lag after it
-  const int halves = pass2_halves(P, n_hold, B);
   const int32_t G1 = (B + 7) / 8, GH = (n_hold + 7) / 8, lag = pass2_lag(P, halves);
-  if (halves == 2) flags |= SAMPLER_FLAG_SPLIT_PASS2;
   std::vector<std::pair<int, int32_t>> seq;  // (pass: 1, or 2 + half, group)
   auto pass2 = [&](int32_t g) {
     for (int h = 0; h < halves; ++h) seq.push_back({2 + h, g});
@@ -321,8 +328,8 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   }
   for (int32_t g = std::max(0, G1 - lag); g < GH; ++g) pass2(g);
   int32_t* trow = reinterpret_cast<int32_t*>(p + off_task);
-  std::memset(p + off_task, 0, task_bytes(B));
-  for (int32_t k = 0; k < tasks_max(B); ++k) trow[k] = -1;
+  std::memset(p + off_task, 0, list_bytes(n_tasks));
+  for (int32_t k = 0; k < n_tasks; ++k) trow[k] = -1;
   for (size_t q = 0; q < seq.size(); ++q)
     for (int32_t x = 0; x < 8; ++x) {
       const int32_t o = seq[q].second * 8 + x;
@@ -333,33 +340,23 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
                                 (seq[q].first == 3 ? kHalf : 0);
     }
   // workspace places: lists, records and histograms for the rows that use
-  // them (see RowSlots), in dispatch order
-  uint64_t ws_entries = 0, ws_rec = 0, ws_hist = 0;
+  // them (see RowSlots), in dispatch order: the HOLD rows (the first n_hold)
+  // take 2P records each from record 0, so their histogram slot follows
+  uint64_t ws_entries = 0, ws_rec = 0;
+  const uint64_t ws_hist = (uint64_t)n_hold * P;
   {
     RowSlots* sl = reinterpret_cast<RowSlots*>(p + off_slots);
     std::memset(sl, 0, slots_bytes(B));
     for (size_t q = 0; q < order.size(); ++q) {
-      const int32_t r = order[q];
+      const int32_t r = order[(size_t)q];
       const RowParams& rp = rows[(size_t)r];
       const RowClass c = row_class_of(rp.flags, rp.top_k, P);
-      RowSlots x = {0u, 0u, 0u, 0u};
-      int lists = 0;
-      if (c == CLS_RACE) {
-        lists = P;  // records only
-      } else if (c == CLS_LIST) {
-        lists = P;
-        x.cap = (rp.flags & ROW_TOPK) ? list_cap_topk(list_q(rp.top_k, P)) : (uint32_t)SCAP;
-      } else if (c == CLS_HOLD) {
-        lists = halves * P;
-        x.cap = SCAP;
-        x.hist = (uint32_t)ws_hist;
-        ws_hist += (uint64_t)P;
-      }
-      x.rec = (uint32_t)ws_rec;
-      x.list64 = (uint32_t)(ws_entries / 64);
+      const uint32_t lcap = row_list_cap(rp.flags, rp.top_k, P);
+      const int lists = c == CLS_HOLD ? 2 * P : (c == CLS_LIST || c == CLS_RACE) ? P : 0;
+      sl[r].rec = (uint32_t)ws_rec;
+      sl[r].list64 = (uint32_t)(ws_entries / 64);
       ws_rec += (uint64_t)lists;
-      ws_entries += (uint64_t)lists * x.cap;
-      sl[r] = x;
+      ws_entries += (uint64_t)(c == CLS_HOLD ? halves * P : lists) * lcap;
     }
   }
 
@@ -421,7 +418,9 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
 void set_pointers(sampler_batch* out, const void* base) {
   const unsigned char* b = static_cast<const unsigned char*>(base);
   const size_t off_list = sizeof(RowParams) * (size_t)out->B;
-  const size_t off_slots = off_list + list_bytes(out->B) + task_bytes(out->B);
+  const size_t off_slots =
+      off_list + list_bytes(out->B) +
+      list_bytes(tasks_used(out->B, out->n_hold, (out->flags & SAMPLER_FLAG_SPLIT_PASS2) != 0));
   const size_t off_pen = off_slots + slots_bytes(out->B);
   out->d_rows = b;
   out->d_sampled = b + off_list;
@@ -460,7 +459,7 @@ const char* sampler_version(void) { return "cd_sampler 0.1 (gfx950)"; }
 size_t sampler_params_bytes(int32_t B, int64_t n_hist, int64_t n_bias) {
   if (B < 0 || n_hist < 0 || n_bias < 0) return 0;
   // a history id takes 8 bytes at most (a counted entry) and 4 at least
-  return params_bytes_exact(B, n_hist, n_bias, 0) + 16;
+  return params_bytes_exact(B, tasks_max(B), n_hist, n_bias, 0) + 16;
 }
 
 int sampler_pack_host(const sampler_host_params* h, void* host_buf, size_t bytes,

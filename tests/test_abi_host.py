@@ -88,9 +88,10 @@ def test_penalty_counts_and_bias_dedup(cds):
     rows = _rowparams(buf, 3)
     assert b.n_sampled == 3
     assert np.frombuffer(buf[64 * 3:64 * 3 + 12].tobytes(), "<i4").tolist() == [0, 1, 2]
-    # the row order (room for B int32, 16-byte padded), then the task table: 24
-    # task rows (int32), then the rows' workspace places (16 bytes each)
-    pen_off = 64 * 3 + 16 + 96 + 16 * 3
+    # the row order (room for B int32, 16-byte padded), then the task table (one
+    # group of 8 task rows, int32: no row needs a second pass), then the rows'
+    # workspace places (8 bytes each)
+    pen_off = 64 * 3 + 16 + 32 + 8 * 3
     assert b.n_pen == 0 and b.n_hist_raw == 4
     raw_off = pen_off + 8 * b.n_bias
     pen = np.frombuffer(buf[raw_off:raw_off + 4 * b.n_hist_raw].tobytes(), "<i4")
@@ -182,11 +183,12 @@ def test_sampled_row_list(cds):
     assert tasks[:8].tolist() == order + [-1, -1]
     assert tasks[8] == 5 | (1 << 30) | (1 << 28) and (tasks[9:16] == -1).all()
     assert tasks[16] == 5 | (1 << 30) | (1 << 29) | (1 << 28) and (tasks[17:] == -1).all()
-    # when most rows need the second pass, its tasks take whole slices
+    # when most rows need the second pass, its tasks take whole slices (the
+    # table holds the groups in use: one pass-1 and one pass-2 group)
     buf, b = cds.pack_host(4, 1000, np.ones(4, np.float32), top_p=np.full(4, 0.9, np.float32))
     assert b.n_hold == 4 and not b.flags & cds.FLAG_SPLIT_PASS2
-    tasks = np.frombuffer(buf[64 * 4 + 16:64 * 4 + 16 + 96].tobytes(), "<i4")
-    assert tasks[8:12].tolist() == [(1 << 30) | r for r in range(4)] and (tasks[16:] == -1).all()
+    tasks = np.frombuffer(buf[64 * 4 + 16:64 * 4 + 16 + 64].tobytes(), "<i4")
+    assert tasks[8:12].tolist() == [(1 << 30) | r for r in range(4)] and (tasks[12:] == -1).all()
 
     buf, b = cds.pack_host(2, 1000, np.zeros(2, np.float32))
     assert b.n_sampled == 0 and b.flags & cds.FLAG_ALL_GREEDY
