@@ -365,6 +365,40 @@ __device__ __forceinline__ void load_chunks(const RowView& rv, int64_t lo, int64
   typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
   typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
   uint32_t raw[N][4];
+  // every chunk in range and no mask (all slices of an unmasked row but the
+  // last): no clamp, no masking, offsets from one base (uniform branch)
+  if (!rv.mrow && hi32 - lo32 >= 4u * (uint32_t)(NT * (first + N))) {
+    if (BF16) {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const u32x2* src = reinterpret_cast<const u32x2*>(base + tb * 2u) + NT * i;
+        const u32x2 u = STREAM ? __builtin_nontemporal_load(src) : *src;
+        x[i][0] = __uint_as_float(u.x << 16);
+        x[i][1] = __uint_as_float(u.x & 0xFFFF0000u);
+        x[i][2] = __uint_as_float(u.y << 16);
+        x[i][3] = __uint_as_float(u.y & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < N; ++i) {
+        const u32x4* src = reinterpret_cast<const u32x4*>(base + tb * 4u) + NT * i;
+        const u32x4 u = STREAM ? __builtin_nontemporal_load(src) : *src;
+        x[i][0] = __uint_as_float(u.x);
+        x[i][1] = __uint_as_float(u.y);
+        x[i][2] = __uint_as_float(u.z);
+        x[i][3] = __uint_as_float(u.w);
+      }
+    }
+    if (CHECK_NF) {
+      uint32_t nf = 0u;
+#pragma unroll
+      for (int i = 0; i < N; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) nf |= __builtin_amdgcn_class(x[i][q], 0x203) ? 1u : 0u;
+      nonfin |= nf;
+    }
+    return;
+  }
   if (BF16) {
 #pragma unroll
     for (int i = 0; i < N; ++i) {
@@ -419,6 +453,12 @@ __device__ __forceinline__ void load_chunks(const RowView& rv, int64_t lo, int64
     }
   }
   nonfin |= nf;
+}
+
+// Number of set bits of m below the calling lane.
+__device__ __forceinline__ uint32_t lanes_below(unsigned long long m) {
+  return __builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32),
+                                   __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
 }
 
 // ---- wave-level inclusive prefix sums by DPP (no LDS, no barrier) --------------

@@ -180,6 +180,7 @@ struct ExactShared {
   unsigned long long pick_above;
   int32_t pick;
   float fshare;
+  int32_t wrest;  // finish_row: some list is longer than its window
 };
 
 // Visit every token of the row in groups of four (t0 % 4 == 0).
@@ -1091,13 +1092,28 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
   const uint64_t* ulr = a.ulist + (int64_t)rs.list64 * 64;      // list 0
   const int64_t lcap = row_list_cap(rp.flags, rp.top_k, a.P);   // entries per list
   const double Td = (double)rp.temperature;
+  // One round of loads brings the records and a window of the first W
+  // entries of every list (thread t reads list t % nl at positions
+  // t / nl + M*k, M = NT / nl threads per list): most lists fit their window,
+  // and only the entries past it are loaded once the lengths are known.
+  constexpr int KP = 8;
+  const int M = NT / nl;
+  const int wj = tid % nl, wm = tid / nl;
+  const int W = (int)min((int64_t)M * KP, lcap);  // window entries per list
+  SliceBest sb{};
+  if (tid < nl) sb = ld_obj(&a.bests[l0 + tid]);
+  unsigned long long pre[KP];
+#pragma unroll
+  for (int k = 0; k < KP; ++k) {
+    const int pos = wm + M * k;
+    pre[k] = (wm < M && pos < W) ? ld_u64(ulr + wj * lcap + pos) : 0ull;
+  }
   // the slices' top two and list lengths; list offsets by a prefix sum
   Top2 b = top2_init();
   if (tid < 64) {  // nl <= 64: one wave
     uint32_t cnt = 0;
     float lcut = CDS_NEG_INF;  // list mode: the highest slice list cut
     if (tid < nl) {
-      const SliceBest sb = ld_obj(&a.bests[l0 + tid]);
       b.k1 = sb.k1;
       b.t1 = sb.t1;
       b.z1 = sb.z1;
@@ -1113,7 +1129,11 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
       if (pl.list_mode) lcut = __uint_as_float(sb.pad[2]);
     }
     lcut = wave_allreduce(lcut, [](float u, float v) { return fmaxf(u, v); });
-    if (tid == 0) sh.fshare = lcut;
+    const bool over = __ballot(cnt > (uint32_t)W) != 0ull;
+    if (tid == 0) {
+      sh.fshare = lcut;
+      sh.wrest = over ? 1 : 0;
+    }
     const uint32_t incl = wave_incl_sum(cnt);
     off[tid + 1] = (int32_t)incl;
     if (tid == 0) off[0] = 0;
@@ -1131,17 +1151,30 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
   int n = n_all;
   constexpr int KG = UCAP / NT;
   if (__builtin_expect(n_all <= UCAP, 1)) {
-    unsigned long long v[KG];
-    int j = 0;
+    // the windows, then whatever lies past them
+    if (wm < M) {
+      const int cj = off[wj + 1] - off[wj], oj = off[wj];
 #pragma unroll
-    for (int k = 0; k < KG; ++k) {
-      const int i = tid + k * NT;
-      while (j + 1 < nl && off[j + 1] <= i) ++j;
-      v[k] = i < n ? ld_u64(ulr + j * lcap + (i - off[j])) : 0ull;
+      for (int k = 0; k < KP; ++k) {
+        const int pos = wm + M * k;
+        if (pos < W && pos < cj) ul[oj + pos] = pre[k];
+      }
     }
+    if (sh.wrest) {
+      unsigned long long v[KG];
+      bool got[KG];
+      int j = 0;
 #pragma unroll
-    for (int k = 0; k < KG; ++k)
-      if (tid + k * NT < n) ul[tid + k * NT] = v[k];
+      for (int k = 0; k < KG; ++k) {
+        const int i = tid + k * NT;
+        while (j + 1 < nl && off[j + 1] <= i) ++j;
+        got[k] = i < n && i - off[j] >= W;
+        v[k] = got[k] ? ld_u64(ulr + j * lcap + (i - off[j])) : 0ull;
+      }
+#pragma unroll
+      for (int k = 0; k < KG; ++k)
+        if (got[k]) ul[tid + k * NT] = v[k];
+    }
   } else {
     if (!(pl.zcut1 > CDS_NEG_INF)) return false;  // nothing to filter by
     const float zf = pl.zcut1;
@@ -1576,6 +1609,52 @@ __device__ __forceinline__ uint32_t list_tokens(const float (&x)[E4][4], int32_t
   return total;
 }
 
+// list_tokens with one ballot per register instead of a counting pass: each
+// wave appends the entries it keeps (entry(v, t)) to its own region of
+// `stage` (LDS, NT/64 regions of UCAP/(NT/64) entries) in (register, lane)
+// order, skipping registers no lane keeps; one barrier shares the wave counts,
+// then each wave copies its region to list positions after the waves before
+// it, through emit(pos, entry).  Returns the number of tokens kept; when that
+// exceeds cap nothing is emitted.  If a wave keeps more than its region holds
+// (and the total fits cap) nothing is emitted either and *spill is set: the
+// caller lists with list_tokens instead.  wt: LDS scratch of NT/64 words.
+template <int NT, int E4, typename Keep, typename Entry, typename Emit>
+__device__ __forceinline__ uint32_t list_tokens_staged(const float (&x)[E4][4], int32_t tbase,
+                                                       uint32_t cap, uint64_t* stage, uint32_t* wt,
+                                                       bool* spill, Keep keep, Entry entry,
+                                                       Emit emit) {
+  constexpr uint32_t kRegion = (uint32_t)UCAP / (uint32_t)(NT / 64);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  uint64_t* mine = stage + (size_t)w * kRegion;
+  uint32_t n = 0u;  // wave-uniform
+#pragma unroll
+  for (int i = 0; i < E4; ++i)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const bool k = keep(x[i][q]);
+      const unsigned long long m = __ballot(k);
+      if (m) {
+        const uint32_t pos = n + lanes_below(m);
+        if (k && pos < kRegion) mine[pos] = entry(x[i][q], tbase + 4 * NT * i + q);
+        n += (uint32_t)__popcll(m);
+      }
+    }
+  if (lane == 0) wt[w] = n;
+  __syncthreads();
+  uint32_t base = 0u, total = 0u, most = 0u;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) {
+    const uint32_t tk = wt[k];
+    base += k < w ? tk : 0u;
+    total += tk;
+    most = tk > most ? tk : most;
+  }
+  *spill = total <= cap && most > kRegion;
+  if (total <= cap && most <= kRegion)
+    for (uint32_t j = (uint32_t)lane; j < n; j += 64u) emit(base + j, mine[j]);
+  return total;
+}
+
 // list_tokens for two disjoint predicates at once: one counting pass, one
 // barrier, one writing pass; returns (number kept by keep1, by keep2).  wt is
 // LDS scratch of 2*NT/64 words.
@@ -1891,11 +1970,19 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
       cut = fmaxf(cut, bm);
     }
     const float cutv = sgpr_f(cut);
+    const float cutk = fmaxf(cutv, -FLT_MAX);  // v >= cutk keeps no -inf
     uint64_t* gl = a.ulist + (int64_t)rs.list64 * 64 + (int64_t)sl * lcap;
-    const uint32_t nst = list_tokens<NT, E4>(
-        x, tbase, lcap, sh.sel.wt,
-        [&](float v) { return v >= cutv && v != CDS_NEG_INF; },
-        [&](uint32_t pos, float v, int32_t t) { st_u64(gl + pos, ulist_entry(v, t)); });
+    bool spill;
+    uint32_t nst = list_tokens_staged<NT, E4>(
+        x, tbase, lcap, sh.fin.list, sh.sel.wt, &spill, [&](float v) { return v >= cutk; },
+        [](float v, int32_t t) { return ulist_entry(v, t); },
+        [&](uint32_t pos, uint64_t e) { st_u64(gl + pos, e); });
+    if (spill) {
+      __syncthreads();  // sh.sel.wt is written again
+      nst = list_tokens<NT, E4>(
+          x, tbase, lcap, sh.sel.wt, [&](float v) { return v >= cutk; },
+          [&](uint32_t pos, float v, int32_t t) { st_u64(gl + pos, ulist_entry(v, t)); });
+    }
     if (tid == 0) {
       SliceBest sb;
       sb.k1 = CDS_NEG_INF;
