@@ -13,8 +13,10 @@ steps.
 
 Prints one JSON line: metric and value (rows/s over the whole timed region),
 a roofline object for sample_kernel (algorithmic HBM bytes per launch over
-its HIP-event launch time, against 8 TB/s; median, p10 and p90 of the
-per-launch times; a warm figure from steps that reuse one input set) and a
+its HIP-event launch time, taken on every eighth launch of the timed region,
+against 8 TB/s; median, p10 and p90 of the timed launches; a warm figure from
+steps that reuse one input set), the host time of a step and of its
+parameter pack, and a
 cpu_baseline object (the CPU oracle timed on a bounded sample of the same
 workload on all host cores, with the single-thread figure beside it).
 """
@@ -239,9 +241,12 @@ def main():
     nbytes = max(h.bytes_bound() for h in host)
     if args.upload == "auto":
         args.upload = "side" if nbytes > (64 << 10) else "same"
+    # (events are made once per slot and recorded again each time round: the
+    # step allocates nothing)
     ring = [dict(d_buf=torch.empty(nbytes, dtype=torch.uint8, device="cuda"),
                  staging=torch.empty(nbytes, dtype=torch.uint8, pin_memory=True),
-                 batch=bd.Batch(), copied=None, used=None) for _ in range(8)]
+                 batch=bd.Batch(), copied=torch.cuda.Event(), used=torch.cuda.Event(),
+                 fresh=True) for _ in range(8)]
     compute = torch.cuda.current_stream()
     copy_s = torch.cuda.Stream() if args.upload == "side" else compute
     lib = bd.lib
@@ -250,47 +255,54 @@ def main():
                   None if rhm[j] is None else rhm[j].data_ptr()) for j in range(len(sets))]
     dtype = cds.DTYPE_BF16 if b0.bf16 else cds.DTYPE_F32
     out_ptrs = tuple(t.data_ptr() for t in outs)
-    pack_s = []
+    pack_s, step_s = [], []
+    # everything a step passes through ctypes, made once
+    host_refs = [ct.byref(h.hp) for h in host]
+    work_args = [(w.data_ptr(), w.stride(0)) for w in work]
+    copy_h, compute_h = copy_s.cuda_stream, compute.cuda_stream
+    opts = bd.Options(size=ct.sizeof(bd.Options), algo=args.algo)
+    opts_ref = ct.byref(opts)
+    for hs in ring:
+        hs.update(batch_ref=ct.byref(hs["batch"]), d_ptr=hs["d_buf"].data_ptr(),
+                  s_ptr=hs["staging"].data_ptr())
 
     def step(i, ev=None, j=None):
+        t_in = time.perf_counter()
         j = i % len(sets) if j is None else j
         hs = ring[i % len(ring)]
         # the staging buffer and the device block are reused: the previous copy
         # out of the staging buffer must have run, and the previous kernels that
         # read the device block must be done before the copy overwrites it
-        if hs["copied"] is not None:
+        if not hs["fresh"]:
             hs["copied"].synchronize()
-        if hs["used"] is not None and copy_s is not compute:
-            copy_s.wait_event(hs["used"])
+            if copy_s is not compute:
+                copy_s.wait_event(hs["used"])
+        hs["fresh"] = False
         t0 = time.perf_counter()
-        rc = lib.sampler_pack_params(ct.byref(host[j].hp), hs["d_buf"].data_ptr(), nbytes,
-                                     hs["staging"].data_ptr(), copy_s.cuda_stream,
-                                     ct.byref(hs["batch"]))
+        rc = lib.sampler_pack_params(host_refs[j], hs["d_ptr"], nbytes, hs["s_ptr"], copy_h,
+                                     hs["batch_ref"])
         pack_s.append(time.perf_counter() - t0)
         if rc != 0:
             raise cds.SamplerError(rc, "sampler_pack_params")
-        copied = torch.cuda.Event()
-        copied.record(copy_s)
-        hs["copied"] = copied
+        hs["copied"].record(copy_s)
         if copy_s is not compute:
-            compute.wait_event(copied)
+            compute.wait_event(hs["copied"])
+        wp, wld = work_args[j]
         if transforms:
-            rc = lib.sampler_apply_transforms(ct.byref(hs["batch"]), work[j].data_ptr(),
-                                              work[j].stride(0), compute.cuda_stream)
+            rc = lib.sampler_apply_transforms(hs["batch_ref"], wp, wld, compute_h)
             if rc != 0:
                 raise cds.SamplerError(rc, "sampler_apply_transforms")
         mp, mld, rp = mask_args[j]
-        o = bd.Options(size=ct.sizeof(bd.Options), algo=args.algo)
         if ev is not None:
-            o.start_event, o.stop_event = bd._event_ptr(ev[0]), bd._event_ptr(ev[1])
-        rc = lib.sampler_sample_ex(ct.byref(hs["batch"]), work[j].data_ptr(), dtype,
-                                   work[j].stride(0), mp, mld, rp, *out_ptrs, ws.ptr, ws.nbytes,
-                                   compute.cuda_stream, ct.byref(o))
+            opts.start_event, opts.stop_event = ev[0].cuda_event, ev[1].cuda_event
+        else:
+            opts.start_event = opts.stop_event = None
+        rc = lib.sampler_sample_ex(hs["batch_ref"], wp, dtype, wld, mp, mld, rp, *out_ptrs,
+                                   ws.ptr, ws.nbytes, compute_h, opts_ref)
         if rc != 0:
             raise cds.SamplerError(rc, "sampler_sample_ex")
-        used = torch.cuda.Event()
-        used.record(compute)
-        hs["used"] = used
+        hs["used"].record(compute)
+        step_s.append(time.perf_counter() - t_in)
 
     # The transforms write their (few hundred per row) tokens in place, so a
     # step re-applies them to the previous step's output: the same work, on
@@ -299,23 +311,31 @@ def main():
         step(i)
     torch.cuda.synchronize()
     pack_s.clear()
+    step_s.clear()
 
-    # timed region: K whole steps, inputs resident in HBM
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(args.steps)]
-    for e in evs:                      # create the HIP events outside the timed region
+    # timed region: K whole steps, inputs resident in HBM.  The kernel's own
+    # time comes from HIP events the library records right around the launch,
+    # on every TIME_EVERY-th step of the region: a timing event pair costs the
+    # step ~10 us of queue time on this runtime, which timing every launch
+    # would add to the step rate it measures.
+    TIME_EVERY = 8
+    timed = list(range(0, args.steps, TIME_EVERY))
+    evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for i in timed}
+    for e in evs.values():             # create the HIP events outside the timed region
         e[0].record()
         e[1].record()
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(args.steps):
-        step(i, evs[i])
+        step(i, evs.get(i))
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     elapsed = t1 - t0
     ms_per_step = elapsed * 1e3 / args.steps
-    kern = np.array([a.elapsed_time(z) for a, z in evs]) * 1e3   # us
+    kern = np.array([a.elapsed_time(z) for a, z in evs.values()]) * 1e3   # us
     host_pack_us = float(np.mean(pack_s)) * 1e6
+    host_step_us = float(np.mean(step_s)) * 1e6
 
     # warm figure: the same input set every step (its 117 MB can stay in the
     # Infinity Cache); reported beside, never as the value
@@ -323,6 +343,10 @@ def main():
     if args.warm_steps > 0:
         wevs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                 for _ in range(args.warm_steps)]
+        for e in wevs:
+            e[0].record()
+            e[1].record()
+        torch.cuda.synchronize()
         for i in range(args.warm_steps):
             step(i, wevs[i], j=0)
         torch.cuda.synchronize()
@@ -361,12 +385,14 @@ def main():
                    "algo": "fast" if args.algo == 0 else "row-exact"},
         "pipeline_gbs": round(alg / (ms_per_step * 1e-3) / 1e9, 1),
         "host_pack_us": round(host_pack_us, 2),
+        "host_step_us": round(host_step_us, 2),
         "param_upload": args.upload,
         "roofline": {"bound": "hbm", "kernel": "sample_kernel", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(args.config),
                      "kernel_us": round(kern_mean, 2),
+                     "kernel_launches_timed": len(kern),
                      "kernel_us_p10_p50_p90": [round(float(np.percentile(kern, q)), 2)
                                                for q in (10, 50, 90)],
                      "kernel_us_warm_p50": None if warm is None else round(warm, 2),

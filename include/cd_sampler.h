@@ -211,7 +211,9 @@ size_t sampler_params_bytes(int32_t B, int64_t n_hist, int64_t n_bias);
  * [SGL] "后端分支" and vLLM's validate_params ([VLP] "Logits Processor 编程
  * 模型"): any invalid value -> SAMPLER_EINVAL and nothing is copied.
  * d_bytes too small -> SAMPLER_ENOSPC.  On success *out describes the batch;
- * its device pointers point into d_buf. */
+ * its device pointers point into d_buf, which the kernels of every call given
+ * *out read: d_buf must not be packed into again (nor h_staging rewritten)
+ * before those calls and the copy have run on the stream. */
 int sampler_pack_params(const sampler_host_params *h, void *d_buf,
                         size_t d_bytes, void *h_staging, void *stream,
                         sampler_batch *out);
