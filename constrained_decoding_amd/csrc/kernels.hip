@@ -1753,19 +1753,22 @@ __device__ __forceinline__ float minp_cut_wave(float zmax, double Td, float min_
 // sure tokens, list their boundary tokens and take the done ticket; the last
 // one resolves the boundary list.  A wait that times out marks the row, whose
 // finisher then takes the exact path, so results never depend on timing.
-// STREAM: non-temporal loads, for greedy rows (read once).
+// STREAM: non-temporal loads, for rows whose slices are read once (every
+// class but HOLD, whose second pass reads its slices again).
 // Diagnostic phase timestamp k of this workgroup (SAMPLER_OPT_TRACE).
 #define CDS_TRACE(k)                                                             \
   do {                                                                           \
     if (a.trace && threadIdx.x == 0) a.trace[(size_t)blockIdx.x * 8 + (k)] = wall_clock64(); \
   } while (0)
 
-template <int NT, int E4, bool BF16, bool VEC, bool STREAM>
+// CLS >= 0: the row's class, fixed at compile time (the instantiation then
+// holds that class's code only).
+template <int NT, int E4, bool BF16, bool VEC, bool STREAM, int CLS>
 __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const RowParams& rp, int sl,
                                            FusedLds<NT>& sh, RedScratch<NT>& red,
                                            StatScratch<NT>& sst, Plan* s_plan, uint32_t* s_word) {
   const int tid = threadIdx.x, P = a.P;
-  const int cls = row_class(rp, a.P);
+  const int cls = CLS >= 0 ? CLS : row_class(rp, a.P);
   const bool greedy = cls == CLS_GREEDY;
   const int64_t lo = (int64_t)sl * a.S;
   const int64_t hi = min(lo + a.S, (int64_t)a.V);
@@ -2303,10 +2306,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CDS_WAVES_PE
                                             &s_plan, s_word);
   else if (tr & kPass2)
     hold_race_task<NT, E4, false, BF16, VEC>(a, r, rp, sl, 0, sh, red, &s_plan, s_word);
-  else if (rp.flags & ROW_GREEDY)
-    slice_task<NT, E4, BF16, VEC, true>(a, r, rp, sl, sh, red, sst, &s_plan, s_word);
-  else
-    slice_task<NT, E4, BF16, VEC, false>(a, r, rp, sl, sh, red, sst, &s_plan, s_word);
+  else if (rp.flags & ROW_GREEDY)  // read once: non-temporal loads
+    slice_task<NT, E4, BF16, VEC, true, CLS_GREEDY>(a, r, rp, sl, sh, red, sst, &s_plan, s_word);
+  else if (row_class(rp, a.P) == CLS_HOLD)  // its second pass reads the slice again
+    slice_task<NT, E4, BF16, VEC, false, CLS_HOLD>(a, r, rp, sl, sh, red, sst, &s_plan, s_word);
+  else  // LIST and RACE rows, read once
+    slice_task<NT, E4, BF16, VEC, true, -1>(a, r, rp, sl, sh, red, sst, &s_plan, s_word);
 }
 
 // ============================================================================
