@@ -2308,10 +2308,15 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(CDS_WAVES_PE
     hold_race_task<NT, E4, false, BF16, VEC>(a, r, rp, sl, 0, sh, red, &s_plan, s_word);
   else if (rp.flags & ROW_GREEDY)  // read once: non-temporal loads
     slice_task<NT, E4, BF16, VEC, true, CLS_GREEDY>(a, r, rp, sl, sh, red, sst, &s_plan, s_word);
-  else if (row_class(rp, a.P) == CLS_HOLD)  // its second pass reads the slice again
-    slice_task<NT, E4, BF16, VEC, false, CLS_HOLD>(a, r, rp, sl, sh, red, sst, &s_plan, s_word);
-  else  // LIST and RACE rows, read once
-    slice_task<NT, E4, BF16, VEC, true, -1>(a, r, rp, sl, sh, red, sst, &s_plan, s_word);
+  else {
+    const int c = row_class(rp, a.P);
+    if (c == CLS_HOLD)  // its second pass reads the slice again
+      slice_task<NT, E4, BF16, VEC, false, CLS_HOLD>(a, r, rp, sl, sh, red, sst, &s_plan, s_word);
+    else if (c == CLS_LIST)  // LIST and RACE rows, read once
+      slice_task<NT, E4, BF16, VEC, true, CLS_LIST>(a, r, rp, sl, sh, red, sst, &s_plan, s_word);
+    else
+      slice_task<NT, E4, BF16, VEC, true, CLS_RACE>(a, r, rp, sl, sh, red, sst, &s_plan, s_word);
+  }
 }
 
 // ============================================================================
