@@ -368,10 +368,25 @@ __device__ __forceinline__ void load_chunks(const RowView& rv, int64_t lo, int64
   // every chunk in range and no mask (all slices of an unmasked row but the
   // last): no clamp, no masking, offsets from one base (uniform branch)
   if (!rv.mrow && hi32 - lo32 >= 4u * (uint32_t)(NT * (first + N))) {
+    // chunk i: a uniform base (scalar registers) plus the thread's own 32-bit
+    // byte offset, so no address arithmetic per chunk in vector registers
+    // (readfirstlane pins the base to scalar registers: the compiler would
+    // otherwise fold the thread offset into a 64-bit vector address per chunk)
+    const uint32_t toff = tb * (BF16 ? 2u : 4u);
+    typedef const __attribute__((address_space(1))) unsigned char gbyte;
+    auto sbase = [](const unsigned char* q) {
+      const uint64_t v = reinterpret_cast<uint64_t>(q);
+      const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+      const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(v >> 32));
+      return (gbyte*)((hi << 32) | lo);  // global memory: global, not flat, loads
+    };
+    typedef const __attribute__((address_space(1))) u32x2 gu32x2;
+    typedef const __attribute__((address_space(1))) u32x4 gu32x4;
     if (BF16) {
 #pragma unroll
       for (int i = 0; i < N; ++i) {
-        const u32x2* src = reinterpret_cast<const u32x2*>(base + tb * 2u) + NT * i;
+        gbyte* bi = sbase(base + (size_t)i * NT * 8);
+        gu32x2* src = (gu32x2*)(bi + toff);
         const u32x2 u = STREAM ? __builtin_nontemporal_load(src) : *src;
         x[i][0] = __uint_as_float(u.x << 16);
         x[i][1] = __uint_as_float(u.x & 0xFFFF0000u);
@@ -381,7 +396,8 @@ __device__ __forceinline__ void load_chunks(const RowView& rv, int64_t lo, int64
     } else {
 #pragma unroll
       for (int i = 0; i < N; ++i) {
-        const u32x4* src = reinterpret_cast<const u32x4*>(base + tb * 4u) + NT * i;
+        gbyte* bi = sbase(base + (size_t)i * NT * 16);
+        gu32x4* src = (gu32x4*)(bi + toff);
         const u32x4 u = STREAM ? __builtin_nontemporal_load(src) : *src;
         x[i][0] = __uint_as_float(u.x);
         x[i][1] = __uint_as_float(u.y);

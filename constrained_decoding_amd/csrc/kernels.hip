@@ -1835,9 +1835,9 @@ __device__ __forceinline__ void slice_task(const SampleArgs& a, int r, const Row
       const float mt = st.m;
 #pragma unroll
       for (int i = 0; i < E4; ++i) {
-        float part = 0.0f;
+        float part = __builtin_amdgcn_exp2f((x[i][0] - mt) * cexp);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) part += __builtin_amdgcn_exp2f((x[i][q] - mt) * cexp);
+        for (int q = 1; q < 4; ++q) part += __builtin_amdgcn_exp2f((x[i][q] - mt) * cexp);
         st.s += (double)part;
       }
     }
