@@ -23,6 +23,9 @@ DTYPE_BF16 = 1
 # min-p last
 ORDER_MINP_FIRST, ORDER_JOINT, ORDER_MINP_LAST = 0, 1, 2
 STATUS_OK, STATUS_OVERFLOW, STATUS_INVALID = 0, 1, 2
+# logprob basis of the further outputs: the distribution the row is sampled
+# from (z/T; greedy rows z), or the logits before the temperature (z)
+BASIS_SAMPLED, BASIS_ORIGINAL = 0, 1
 F_TOPP, F_RACE, F_MINP, F_TOPK = 1, 2, 4, 8
 # flags that excuse an id mismatch (F_TOPK is informational: top-k is decided
 # on exact fp32 values on both sides)
@@ -75,6 +78,10 @@ def _load():
                                          _ct.c_uint64, _ct.c_int32, P, P]
     lib.cdo_sample_batch_order.argtypes = [P, _ct.c_int64, _ct.c_int32, _ct.c_int32,
                                            P, P, P, P, P, P, _ct.c_int32, P]
+    lib.cdo_set_log_softmax.argtypes = [P, _ct.c_int32, _ct.c_double, P, _ct.c_uint8, P]
+    lib.cdo_set_log_softmax.restype = _ct.c_int64
+    lib.cdo_top_n.argtypes = [P, P, _ct.c_int32, _ct.c_int32, P, P]
+    lib.cdo_top_n.restype = _ct.c_int32
     _lib = lib
     return lib
 
@@ -227,3 +234,107 @@ def pipeline(logits, params, *, bf16=False, masks=None, row_has_mask=None,
             order=params.get("order", ORDER_MINP_FIRST)))
         zs.append(z)
     return _np.array(res, dtype=RESULT_DTYPE), _np.array(zs)
+
+
+# ------------------------------------------------------------ further outputs
+
+def set_log_softmax(z, T=1.0, in_set=None, bit=1):
+    """log_softmax(z/T) over the finite tokens of a set (all tokens when
+    ``in_set`` is None; else those with ``in_set & bit``), -inf elsewhere.
+    Returns (count, float64 [V]); count -1 means a NaN/+inf lay in the set
+    (every value NaN)."""
+    zz = _np.ascontiguousarray(z, dtype=_np.float32)
+    V = zz.shape[0]
+    st = None if in_set is None else _np.ascontiguousarray(in_set, _np.uint8)
+    out = _np.empty(V, _np.float64)
+    n = _load().cdo_set_log_softmax(_ptr(zz), V, float(T), _ptr(st), int(bit), _ptr(out))
+    return int(n), out
+
+
+def top_n(z, lp, N):
+    """The N largest z (lower id first among equal values) with their lp."""
+    zz = _np.ascontiguousarray(z, dtype=_np.float32)
+    ll = _np.ascontiguousarray(lp, dtype=_np.float64)
+    ids = _np.empty(max(N, 1), _np.int32)
+    vals = _np.empty(max(N, 1), _np.float64)
+    _load().cdo_top_n(_ptr(zz), _ptr(ll), zz.shape[0], int(N), _ptr(ids), _ptr(vals))
+    return ids[:N], vals[:N]
+
+
+def row_outputs(z, *, T, top_k=0, top_p=1.0, min_p=0.0, seed=0, offset=0,
+                order=ORDER_MINP_FIRST, basis=BASIS_SAMPLED, n_top=0,
+                token_ids=(), selected=None, support_cap=None):
+    """The further outputs of one row of transformed logits ``z``.
+
+    Basis: the row's sampling distribution (s = z/T; greedy rows z, as for
+    the chosen token's logprob), or with ``basis=BASIS_ORIGINAL`` the logits
+    before the temperature.  Returns a dict with
+      ``top_ids, top_vals``  the ``n_top`` most likely tokens (larger z first,
+                             lower id first among equal values; -1 / -inf past
+                             the allowed tokens; -1 / NaN on an OVERFLOW row);
+      ``tok_vals``           logprobs of ``token_ids`` (NaN for an id outside
+                             [0, V) or on an OVERFLOW row, -inf if masked);
+      ``next``               logprob of token ``selected`` (if given): NaN on
+                             OVERFLOW, -inf on INVALID;
+      and, if ``support_cap`` is given, the support set (the set the row's
+      draw is made from; a greedy row's is its argmax): ``sup_ids`` (ascending,
+      at most ``support_cap``), ``sup_vals`` (logprobs renormalised over the
+      whole support, under the sampling distribution), ``sup_n`` (its true
+      size), ``sup_len``, ``sup_status`` (OK; OVERFLOW: larger than the
+      capacity; INVALID: no distribution -- no finite allowed logit, or a NaN
+      or +inf among them), ``sup_sel`` (renormalised logprob of ``selected``,
+      -inf outside the support, NaN if ``selected`` is not a token id or the
+      row is INVALID).
+    Also ``res``: the row's sampling record (RESULT_DTYPE)."""
+    zz = _np.ascontiguousarray(z, dtype=_np.float32)
+    V = zz.shape[0]
+    T32 = float(_np.float32(T))
+    res, sets = sample_row(zz, T=T32, top_k=top_k, top_p=top_p, min_p=min_p,
+                           seed=seed, offset=offset, want_sets=True, order=order)
+    status = int(res["status"])
+    greedy = bool(res["greedy"])
+    Tb = 1.0 if (basis == BASIS_ORIGINAL or greedy) else T32
+    if status == STATUS_OVERFLOW:
+        lp = _np.full(V, _np.nan)
+    else:
+        _, lp = set_log_softmax(zz, Tb)
+    out = {"res": res}
+    if status == STATUS_OVERFLOW:
+        out["top_ids"] = _np.full(n_top, -1, _np.int32)
+        out["top_vals"] = _np.full(n_top, _np.nan)
+    else:
+        out["top_ids"], out["top_vals"] = top_n(zz, lp, n_top)
+
+    def at(i):
+        return float(lp[i]) if 0 <= i < V else float("nan")
+    out["tok_vals"] = _np.array([at(int(i)) for i in token_ids], _np.float64)
+    if selected is not None:
+        if status == STATUS_OVERFLOW:
+            out["next"] = float("nan")
+        elif status == STATUS_INVALID:
+            out["next"] = float("-inf")
+        else:
+            out["next"] = at(int(selected))
+    if support_cap is not None:
+        sel = None if selected is None else int(selected)
+        if status != STATUS_OK:
+            ids = _np.zeros(0, _np.int64)
+            vals = _np.zeros(0)
+            n_sup, sst, ssel = 0, STATUS_INVALID, float("nan")
+        else:
+            if greedy:
+                member = _np.zeros(V, _np.uint8)
+                member[int(res["id"])] = 1
+                _, slp = set_log_softmax(zz, 1.0, member, 1)
+            else:
+                member = (sets & 4).astype(_np.uint8)
+                _, slp = set_log_softmax(zz, T32, member, 4)
+            allids = _np.flatnonzero(member)
+            n_sup = int(allids.shape[0])
+            ids = allids[:support_cap]
+            vals = slp[ids]
+            sst = STATUS_OVERFLOW if n_sup > support_cap else STATUS_OK
+            ssel = float("nan") if sel is None or not 0 <= sel < V else float(slp[sel])
+        out.update(sup_ids=ids.astype(_np.int32), sup_vals=vals, sup_n=n_sup,
+                   sup_len=int(ids.shape[0]), sup_status=sst, sup_sel=ssel)
+    return out

@@ -474,3 +474,77 @@ int cdo_sample_batch_order(const float *z, int64_t ld, int32_t B, int32_t V,
       return -1;
   return 0;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Further outputs [SGL, "LogitsProcessorOutput 的五段结构": the chosen        */
+/* token's logprob, the top logprobs (the most likely tokens and their      */
+/* logprobs), the logprobs of tokens the request names, and the sampling    */
+/* support set with its logprobs and a severity-ordered status; "logprobs   */
+/* 的数值一致性": an option returns logprobs of the distribution before the   */
+/* temperature; "LogitsProcessor 与 LogitsProcessorOutput": scoring requests */
+/* take logprobs of the same preprocessed logits without a draw].           */
+/* ------------------------------------------------------------------------ */
+
+int64_t cdo_set_log_softmax(const float *z, int32_t V, double T,
+                            const uint8_t *set, uint8_t bit, double *out) {
+  /* the tokens in play: finite z, and in the set when one is given */
+  int64_t n = 0;
+  int bad = 0;
+  double m = -INFINITY;
+  for (int32_t t = 0; t < V; ++t) {
+    out[t] = -INFINITY;
+    if (set && !(set[t] & bit)) continue;
+    if (isnan(z[t]) || z[t] == INFINITY) {
+      bad = 1;
+      continue;
+    }
+    if (z[t] == -INFINITY) continue;
+    ++n;
+    const double s = (double)z[t] / T;
+    if (s > m) m = s;
+  }
+  if (bad) {
+    for (int32_t t = 0; t < V; ++t) out[t] = NAN;
+    return -1;
+  }
+  if (n == 0) return 0;
+  /* log form: s - m - log(sum exp(s - m)) */
+  double sum = 0.0;
+  for (int32_t t = 0; t < V; ++t) {
+    if (set && !(set[t] & bit)) continue;
+    if (z[t] == -INFINITY) continue;
+    sum += exp((double)z[t] / T - m);
+  }
+  const double log_sum = log(sum);
+  for (int32_t t = 0; t < V; ++t) {
+    if (set && !(set[t] & bit)) continue;
+    if (z[t] == -INFINITY) continue;
+    out[t] = (double)z[t] / T - m - log_sum;
+  }
+  return n;
+}
+
+int32_t cdo_top_n(const float *z, const double *lp, int32_t V, int32_t N,
+                  int32_t *ids, double *vals) {
+  cdo_entry *ent = (cdo_entry *)malloc((size_t)(V > 0 ? V : 1) * sizeof(cdo_entry));
+  int64_t n = 0;
+  for (int32_t t = 0; t < V; ++t)
+    if (z[t] != -INFINITY && !isnan(z[t])) {
+      ent[n].s = (double)z[t];
+      ent[n].t = t;
+      ++n;
+    }
+  /* full sort: larger value first, the lower id first among equal values */
+  qsort(ent, (size_t)n, sizeof(cdo_entry), cdo_entry_cmp);
+  int32_t k = 0;
+  for (; k < N && k < n; ++k) {
+    ids[k] = ent[k].t;
+    vals[k] = lp[ent[k].t];
+  }
+  for (int32_t j = k; j < N; ++j) {
+    ids[j] = -1;
+    vals[j] = -INFINITY;
+  }
+  free(ent);
+  return k;
+}

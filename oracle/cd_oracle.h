@@ -125,6 +125,26 @@ int cdo_sample_batch_order(const float *z, int64_t ld, int32_t B, int32_t V,
                            const uint64_t *seed, const uint64_t *offset,
                            int32_t order, cdo_result *out);
 
+
+/* ---- further outputs [SGL, "LogitsProcessorOutput 的五段结构"] ----------- */
+
+/* Log-softmax of s = z/T over a set of tokens, in log form (s - m - log sum
+ * exp(s - m), m the largest s of the set) [SGL, "logprobs 的数值一致性"]:
+ * out[t] for every t in the set with finite z, -inf elsewhere.  The set is
+ * {t : set[t] & bit} (set == NULL: every token).  T = 1 gives the logprobs
+ * of the logits before the temperature.  Returns the number of finite
+ * tokens in the set (0: every out is -inf), or -1 if a NaN or +inf lies in
+ * the set (then every out is NaN). */
+int64_t cdo_set_log_softmax(const float *z, int32_t V, double T,
+                            const uint8_t *set, uint8_t bit, double *out);
+
+/* The N tokens with the largest z (NaN and -inf excluded), larger value
+ * first and the lower id first among equal values, with their lp values;
+ * entries past the number of such tokens get id -1 and -inf.  Returns the
+ * number of real entries. */
+int32_t cdo_top_n(const float *z, const double *lp, int32_t V, int32_t N,
+                  int32_t *ids, double *vals);
+
 #ifdef __cplusplus
 }
 #endif
