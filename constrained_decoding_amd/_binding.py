@@ -23,12 +23,14 @@ FLAG_NEED_PENALTY, FLAG_HAS_BIAS, FLAG_SPLIT_PASS2 = 1 << 5, 1 << 6, 1 << 7
 ALGO_FAST, ALGO_EXACT = 0, 1
 ORDER_MINP_FIRST, ORDER_JOINT, ORDER_MINP_LAST = 0, 1, 2
 WAIT_NONE = -1
+LOGPROB_SAMPLED, LOGPROB_ORIGINAL = 0, 1
+MAX_TOP_N = 256
 
 EXPORTS = [
     "sampler_strerror", "sampler_version", "sampler_params_bytes", "sampler_pack_params",
     "sampler_pack_host", "sampler_apply_transforms", "sampler_apply_bitmask",
     "sampler_workspace_bytes", "sampler_workspace_bytes_batch", "sampler_workspace_init",
-    "sampler_sample", "sampler_sample_ex", "sampler_sample_static",
+    "sampler_sample", "sampler_sample_ex", "sampler_sample_static", "sampler_logprobs",
 ]
 
 
@@ -63,6 +65,26 @@ class Options(ct.Structure):
     ]
 
 
+class LogprobRequest(ct.Structure):
+    _fields_ = [
+        ("size", ct.c_uint32), ("basis", ct.c_int32), ("selected", ct.c_void_p),
+        ("top_n_max", ct.c_int32), ("n_mask_rows", ct.c_int32), ("top_n", ct.c_void_p),
+        ("token_indptr", ct.c_void_p), ("token_ids", ct.c_void_p), ("mask_rows", ct.c_void_p),
+        ("mask_cap", ct.c_int32), ("pad_", ct.c_int32),
+    ]
+
+
+class LogprobOutputs(ct.Structure):
+    _fields_ = [
+        ("size", ct.c_uint32), ("pad_", ct.c_int32),
+        ("next_token_logprobs", ct.c_void_p), ("top_logprobs_idx", ct.c_void_p),
+        ("top_logprobs_val", ct.c_void_p), ("token_ids_logprobs", ct.c_void_p),
+        ("mask_token_ids", ct.c_void_p), ("mask_support_logprobs", ct.c_void_p),
+        ("mask_lengths", ct.c_void_p), ("mask_selected_logprobs", ct.c_void_p),
+        ("mask_statuses", ct.c_void_p),
+    ]
+
+
 class SamplerError(RuntimeError):
     def __init__(self, code, what):
         self.code = code
@@ -89,6 +111,7 @@ def _load():
         "sampler_sample": ([P, P, ct.c_int, I64, P, I64, P, P, P, P, P, SZ, P], ct.c_int),
         "sampler_sample_ex": ([P, P, ct.c_int, I64, P, I64, P, P, P, P, P, SZ, P, P], ct.c_int),
         "sampler_sample_static": ([P, P, ct.c_int, I64, P, I64, P, P, P, P, P], ct.c_int),
+        "sampler_logprobs": ([P, P, ct.c_int, I64, P, I64, P, P, P, P], ct.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -339,3 +362,68 @@ def sample(packed: PackedBatch, logits, *, bitmask=None, row_has_mask=None, work
                     stop_event=None if events is None else _event_ptr(events[1]))
         _check(lib.sampler_sample_ex(*args, ct.byref(o)), "sampler_sample_ex")
     return ids, lp, st
+
+
+def logprobs(packed: PackedBatch, logits, *, selected=None, basis=LOGPROB_SAMPLED, top_n_max=0,
+             top_n=None, token_indptr=None, token_ids=None, mask_rows=None, mask_cap=0,
+             support_logprobs=True, bitmask=None, row_has_mask=None, stream=None):
+    """Further outputs (sampler_logprobs).  Device tensors in, a dict of
+    device tensors out: ``next`` [B] (with ``selected``), ``top_idx`` /
+    ``top_val`` [B, top_n_max], ``token`` [token_indptr[-1]] (named tokens),
+    and for ``mask_rows`` (int32 row indices) ``mask_ids`` [R, mask_cap],
+    ``mask_lp`` [R, mask_cap] (if ``support_logprobs``), ``mask_len``,
+    ``mask_sel`` and ``mask_status`` [R].  ``selected=None``: scoring, no
+    draw."""
+    import torch
+    B, V = logits.shape
+    if (B, V) != (packed.B, packed.V):
+        raise ValueError("logits shape does not match the packed batch")
+    if logits.stride(1) != 1:
+        raise ValueError("logits must have unit column stride")
+    dev = logits.device
+    res = {}
+    ptr = lambda t: None if t is None else t.data_ptr()
+    if selected is not None:
+        res["next"] = torch.empty(B, dtype=torch.float32, device=dev)
+    if top_n_max > 0:
+        res["top_idx"] = torch.empty((B, top_n_max), dtype=torch.int32, device=dev)
+        res["top_val"] = torch.empty((B, top_n_max), dtype=torch.float32, device=dev)
+    n_tok = 0
+    if token_indptr is not None:
+        n_tok = int(token_indptr[-1].item()) if token_indptr.numel() else 0
+        if n_tok == 0:            # nothing named: not asked for
+            token_indptr = token_ids = None
+        else:
+            res["token"] = torch.empty(n_tok, dtype=torch.float32, device=dev)
+    R = 0 if mask_rows is None else int(mask_rows.numel())
+    if R > 0:
+        res["mask_ids"] = torch.empty((R, max(mask_cap, 1)), dtype=torch.int32, device=dev)
+        if support_logprobs:
+            res["mask_lp"] = torch.empty((R, max(mask_cap, 1)), dtype=torch.float32, device=dev)
+        res["mask_len"] = torch.empty(R, dtype=torch.int32, device=dev)
+        res["mask_sel"] = torch.empty(R, dtype=torch.float32, device=dev)
+        res["mask_status"] = torch.empty(R, dtype=torch.int32, device=dev)
+    req = LogprobRequest(size=ct.sizeof(LogprobRequest), basis=int(basis),
+                         selected=ptr(selected), top_n_max=int(top_n_max), n_mask_rows=R,
+                         top_n=ptr(top_n), token_indptr=ptr(token_indptr),
+                         token_ids=ptr(token_ids), mask_rows=ptr(mask_rows) if R else None,
+                         mask_cap=int(mask_cap))
+    out = LogprobOutputs(size=ct.sizeof(LogprobOutputs),
+                         next_token_logprobs=ptr(res.get("next")),
+                         top_logprobs_idx=ptr(res.get("top_idx")),
+                         top_logprobs_val=ptr(res.get("top_val")),
+                         token_ids_logprobs=ptr(res.get("token")),
+                         mask_token_ids=ptr(res.get("mask_ids")) if mask_cap > 0 else None,
+                         mask_support_logprobs=ptr(res.get("mask_lp")) if mask_cap > 0 else None,
+                         mask_lengths=ptr(res.get("mask_len")),
+                         mask_selected_logprobs=ptr(res.get("mask_sel")),
+                         mask_statuses=ptr(res.get("mask_status")))
+    _check(lib.sampler_logprobs(
+        ct.byref(packed.batch), logits.data_ptr(), _dtype_code(logits), logits.stride(0),
+        None if bitmask is None else bitmask.data_ptr(),
+        0 if bitmask is None else bitmask.stride(0),
+        None if row_has_mask is None else row_has_mask.data_ptr(),
+        ct.byref(req), ct.byref(out), _stream_ptr(stream)), "sampler_logprobs")
+    if "token" not in res and n_tok == 0 and token_indptr is None:
+        res["token"] = torch.empty(0, dtype=torch.float32, device=dev)
+    return res

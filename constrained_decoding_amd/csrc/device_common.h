@@ -883,6 +883,25 @@ __device__ __forceinline__ void block_top2(Top2& b, RedScratch<NT>& s) {
 }
 
 // max value, lowest index among equal maxima
+// Exclusive prefix sum of c over the block (thread order) and its total, with
+// one barrier; wt is LDS scratch of NT/64 words.
+template <int NT>
+__device__ __forceinline__ uint32_t block_excl(uint32_t c, uint32_t* wt, uint32_t& total) {
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const uint32_t incl = wave_incl_sum(c);
+  if (lane == 63) wt[w] = incl;
+  __syncthreads();
+  uint32_t base = 0u;
+  total = 0u;
+#pragma unroll
+  for (int k = 0; k < NT / 64; ++k) {
+    const uint32_t tk = wt[k];
+    base += k < w ? tk : 0u;
+    total += tk;
+  }
+  return base + incl - c;
+}
+
 template <int NT>
 __device__ __forceinline__ void block_argmax(float& z, int32_t& t, RedScratch<NT>& s) {
   struct ZT {

@@ -36,6 +36,32 @@ struct SampleArgs {
   unsigned long long* trace;  // 8 words per workgroup of phase timestamps, or nullptr
 };
 
+// Further per-row outputs (logprob-outputs kernel, outputs.hip).  Row blocks:
+// one workgroup per row for the chosen token's logprob, the top-N logprobs
+// and the logprobs of named tokens; support blocks: one workgroup per entry
+// of sup_rows for that row's support set.
+struct OutputArgs {
+  int32_t basis;          // 0: the row's sampling distribution, 1: before the temperature
+  int32_t top_n_max;      // columns of top_ids / top_vals (0: none)
+  const int32_t* top_n;   // [B] per-row N (clamped to [0, top_n_max]) or nullptr
+  const int64_t* tok_off; // [B+1] CSR offsets of named tokens or nullptr
+  const int32_t* tok_ids;
+  const int32_t* sel_ids; // [B] the drawn tokens, or nullptr (scoring: no draw)
+  const int32_t* sup_rows;
+  int32_t n_sup;
+  int32_t sup_cap;
+  int32_t n_row_blocks;   // B, or 0 when no per-row output is asked for
+  float* next_lp;         // [B] or nullptr
+  int32_t* top_ids;       // [B, top_n_max]
+  float* top_vals;
+  float* tok_vals;        // [tok_off[B]]
+  int32_t* sup_ids;       // [n_sup, sup_cap]
+  float* sup_lp;          // [n_sup, sup_cap] or nullptr
+  int32_t* sup_len;       // [n_sup]
+  float* sup_sel;         // [n_sup] or nullptr
+  int32_t* sup_st;        // [n_sup]
+};
+
 // Optional timing events recorded around the sampling kernel.
 struct KernelEvents {
   hipEvent_t start;
@@ -57,5 +83,9 @@ hipError_t static_workspace(void** ptr, hipStream_t stream);
 // algo 0: the fused fast path; algo 1: the row-serial exact path.
 hipError_t launch_sample(const SampleArgs& a, bool bf16, bool vec, int algo,
                          const KernelEvents* ev, hipStream_t stream);
+
+// The logprob-outputs kernel (one launch: n_row_blocks + n_sup workgroups).
+hipError_t launch_outputs(const SampleArgs& a, const OutputArgs& o, bool bf16, bool vec,
+                          const KernelEvents* ev, hipStream_t stream);
 
 }  // namespace cds

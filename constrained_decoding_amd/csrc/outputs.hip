@@ -1,0 +1,335 @@
+// outputs.hip -- further per-row outputs of the sampling step, for gfx950.
+//
+// What the sampler returns beside the drawn token ("SGLang 源码完全拆解(十)",
+// section LogitsProcessorOutput 的五段结构): the chosen token's logprob, the
+// top-N logprobs (the most likely tokens and their logprobs), the logprobs of
+// tokens a request names, and the sampling support set (the tokens the row's
+// draw was made from, with their renormalised logprobs and a status ordered
+// by severity, OK < OVERFLOW < INVALID).  Same page, section logprobs
+// 的数值一致性: an option returns logprobs of the distribution before the
+// temperature; section LogitsProcessor 与 LogitsProcessorOutput: scoring
+// requests take logprobs of the same preprocessed logits with no draw.
+//
+// One launch.  Row blocks (one workgroup per row) compute the row's max and
+// normaliser in the requested basis, then the chosen and named tokens'
+// logprobs by direct reads, and the top-N by an exact radix select on the
+// fp32 order key (ties broken by id with a second select on ~id), then an
+// LDS rank sort of the N winners.  Support blocks (one workgroup per
+// requested row) find the row's value threshold with the exact path's
+// selection (row_cut), sum the kept mass, and write the kept tokens in id
+// order by a block-wide prefix sum per chunk.  Every pass streams the row;
+// after the first, it comes from L2 / the last-level cache.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+
+#include "device_common.h"
+#include "exact_path.h"
+#include "kernels.h"
+
+namespace cds {
+
+constexpr int kOutNT = 512;
+constexpr int kMaxTopN = 256;  // SAMPLER_MAX_TOP_N
+
+template <int NT>
+struct OutShared {
+  ExactShared<NT> ex;
+  uint32_t key[kMaxTopN];
+  int32_t id[kMaxTopN];
+  uint32_t cnt;
+  uint32_t wt[NT / 64];
+};
+
+// z of token t as the sampling kernel sees it: bf16 upcast, mask applied
+// (-inf if disallowed), -0 read as +0.
+template <bool BF16>
+__device__ __forceinline__ float token_z(const RowView& rv, int64_t t) {
+  if (rv.mrow && !(((uint32_t)rv.mrow[t >> 5] >> (uint32_t)(t & 31)) & 1u)) return CDS_NEG_INF;
+  const float v = BF16 ? __uint_as_float((uint32_t)rv.b16[t] << 16) : rv.f32[t];
+  return v + 0.0f;
+}
+
+__device__ __forceinline__ bool finite_f(float x) { return x > CDS_NEG_INF && x < CDS_POS_INF; }
+
+// Radix select over 8-bit digits of a 32-bit key (most significant first):
+// the `need`-th largest key among the tokens `sel` admits, counting with
+// `key`.  Returns the key; *tie_rem = how many tokens with exactly that key
+// the `need` largest hold, *tie_cnt = how many tokens have it.
+template <int NT, bool BF16, bool VEC, typename Sel, typename Key>
+__device__ __forceinline__ uint32_t radix_select(const RowView& rv, int64_t V, uint32_t need, Sel sel,
+                                                 Key key, ExactShared<NT>& sh, uint32_t* tie_rem,
+                                                 uint32_t* tie_cnt) {
+  uint32_t prefix = 0, pmask = 0;
+  unsigned long long krem = need;
+  unsigned long long cnt_d = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    if (threadIdx.x < 256) sh.hist[threadIdx.x] = 0ull;
+    __syncthreads();
+    uint32_t nonfin = 0;
+    for_row4<NT, BF16, VEC>(rv, V, nonfin, [&](const float* x, int64_t t0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (!sel(x[q], t0 + q)) continue;
+        const uint32_t u = key(x[q], t0 + q);
+        if ((u & pmask) == prefix) atomicAdd(&sh.hist[(u >> shift) & 255u], 1ull);
+      }
+    });
+    __syncthreads();
+    unsigned long long above;
+    const int d = pick_digit<NT>(sh, (double)krem, 0ull, &above);
+    if (shift == 0) cnt_d = sh.hist[d];  // no later round clears it
+    krem -= above;
+    prefix |= (uint32_t)d << shift;
+    pmask |= 255u << shift;
+  }
+  __syncthreads();  // every thread has read the last round's count
+  *tie_rem = (uint32_t)krem;
+  *tie_cnt = (uint32_t)cnt_d;
+  return prefix;
+}
+
+// ---- row blocks: chosen-token, named-token and top-N logprobs ----------------
+template <int NT, bool BF16, bool VEC>
+__device__ __forceinline__ void row_outputs(const SampleArgs& a, const OutputArgs& o, int r,
+                                            OutShared<NT>& sh) {
+  const int64_t V = a.V;
+  const int ncol = o.top_ids ? o.top_n_max : 0;
+  int n_top = ncol;
+  if (ncol > 0 && o.top_n) n_top = min(max(o.top_n[r], 0), ncol);
+  const int64_t tlo = o.tok_off ? o.tok_off[r] : 0;
+  const int64_t thi = o.tok_off ? o.tok_off[r + 1] : 0;
+  int32_t* top_ids = ncol > 0 ? o.top_ids + (int64_t)r * ncol : nullptr;
+  float* top_vals = ncol > 0 ? o.top_vals + (int64_t)r * ncol : nullptr;
+  // columns past the row's N
+  for (int j = n_top + (int)threadIdx.x; j < ncol; j += NT) {
+    top_ids[j] = -1;
+    top_vals[j] = CDS_NEG_INF;
+  }
+  if (n_top == 0 && thi <= tlo && !o.next_lp) return;
+
+  const RowParams rp = a.rows[r];
+  const RowView rv = row_view<BF16>(a, r);
+  const RowStats st = row_stats<NT, BF16, VEC>(rv, V, sh.ex);
+  const int status = st.nf == 0 ? 2 : (st.nonfin ? 1 : 0);
+  const bool greedy = (rp.flags & ROW_GREEDY) != 0;
+  // the basis: the row's sampling distribution (greedy rows: the logits
+  // before the temperature, as for the drawn token's logprob), or the logits
+  // before the temperature for every row
+  const double Tb = (o.basis == 1 || greedy) ? 1.0 : (double)rp.temperature;
+  double mb = 0.0, lz = 0.0;
+  if (status == 0) {
+    const double se = row_expsum<NT, BF16, VEC>(rv, V, st.zm, (float)(1.0 / Tb), sh.ex);
+    mb = (double)st.zm / Tb;
+    lz = log(se);
+  }
+  const float qnan = __builtin_nanf("");
+  auto lp_of = [&](float z) -> float {
+    return z == CDS_NEG_INF ? CDS_NEG_INF : (float)((double)z / Tb - mb - lz);
+  };
+  auto named = [&](int64_t t) -> float {
+    if (status == 1 || t < 0 || t >= V) return qnan;
+    return lp_of(token_z<BF16>(rv, t));  // an INVALID row's allowed tokens are all -inf
+  };
+  if (o.next_lp && threadIdx.x == 0) {
+    float v;
+    if (status == 1)
+      v = qnan;
+    else if (status == 2)
+      v = CDS_NEG_INF;
+    else
+      v = named(o.sel_ids[r]);
+    o.next_lp[r] = v;
+  }
+  for (int64_t j = tlo + threadIdx.x; j < thi; j += NT) o.tok_vals[j] = named(o.tok_ids[j]);
+  if (n_top == 0) return;
+
+  int n = 0;  // real entries
+  if (status == 0) {
+    n = min(n_top, st.nf);
+    // the n largest values, the lower id first among equal values: the
+    // token set {key > kthr} + {key == kthr, ~id >= ithr}
+    uint32_t kthr = 0u, ithr = 0u;
+    auto fin = [](float x, int64_t) { return finite_f(x); };
+    if (n < st.nf) {
+      uint32_t rem, cnt;
+      kthr = radix_select<NT, BF16, VEC>(
+          rv, V, (uint32_t)n, fin, [](float x, int64_t) { return okey(x + 0.0f); }, sh.ex, &rem,
+          &cnt);
+      if (cnt > rem) {
+        uint32_t rem2, cnt2;
+        const uint32_t kt = kthr;
+        ithr = radix_select<NT, BF16, VEC>(
+            rv, V, rem, [&](float x, int64_t) { return finite_f(x) && okey(x + 0.0f) == kt; },
+            [](float, int64_t t) { return ~(uint32_t)t; }, sh.ex, &rem2, &cnt2);
+      }
+    }
+    if (threadIdx.x == 0) sh.cnt = 0u;
+    __syncthreads();
+    uint32_t nonfin = 0;
+    const uint32_t kt = kthr, it = ithr;
+    const bool all = n == st.nf;
+    for_row4<NT, BF16, VEC>(rv, V, nonfin, [&](const float* x, int64_t t0) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (!finite_f(x[q])) continue;
+        const uint32_t u = okey(x[q] + 0.0f);
+        const uint32_t iu = ~(uint32_t)(t0 + q);
+        if (all || u > kt || (u == kt && iu >= it)) {
+          const uint32_t slot = atomicAdd(&sh.cnt, 1u);
+          if (slot < (uint32_t)kMaxTopN) {
+            sh.key[slot] = u;
+            sh.id[slot] = (int32_t)(t0 + q);
+          }
+        }
+      }
+    });
+    __syncthreads();
+    n = min(n, (int)min(sh.cnt, (uint32_t)kMaxTopN));
+    // rank sort: larger key first, lower id first among equal keys
+    for (int i = threadIdx.x; i < n; i += NT) {
+      const uint32_t ki = sh.key[i];
+      const int32_t ti = sh.id[i];
+      int rank = 0;
+      for (int j = 0; j < n; ++j) {
+        const uint32_t kj = sh.key[j];
+        rank += (kj > ki || (kj == ki && sh.id[j] < ti)) ? 1 : 0;
+      }
+      top_ids[rank] = ti;
+      top_vals[rank] = lp_of(from_okey(ki));
+    }
+  }
+  const float pad = status == 1 ? qnan : CDS_NEG_INF;
+  for (int j = n + (int)threadIdx.x; j < n_top; j += NT) {
+    top_ids[j] = -1;
+    top_vals[j] = pad;
+  }
+}
+
+// ---- support blocks: the set the row's draw was made from ------------------
+template <int NT, bool BF16, bool VEC>
+__device__ __forceinline__ void support_outputs(const SampleArgs& a, const OutputArgs& o, int j,
+                                                OutShared<NT>& sh) {
+  const int64_t V = a.V;
+  const int cap = o.sup_cap;
+  int32_t* ids_out = o.sup_ids ? o.sup_ids + (int64_t)j * cap : nullptr;
+  float* lp_out = o.sup_lp ? o.sup_lp + (int64_t)j * cap : nullptr;
+  const float qnan = __builtin_nanf("");
+  auto finish = [&](int len, int status, float sel) {
+    if (threadIdx.x == 0) {
+      o.sup_len[j] = len;
+      o.sup_st[j] = status;
+      if (o.sup_sel) o.sup_sel[j] = sel;
+    }
+  };
+  const int r = o.sup_rows[j];
+  if (r < 0 || r >= a.B) {
+    finish(0, 2, qnan);
+    return;
+  }
+  const RowParams rp = a.rows[r];
+  const RowView rv = row_view<BF16>(a, r);
+  const RowStats st = row_stats<NT, BF16, VEC>(rv, V, sh.ex);
+  if (st.nf == 0 || st.nonfin) {  // no distribution
+    finish(0, 2, qnan);
+    return;
+  }
+  const int64_t tsel = o.sel_ids ? (int64_t)o.sel_ids[r] : -1;
+  const bool has_sel = o.sel_ids && tsel >= 0 && tsel < V;
+  if (rp.flags & ROW_GREEDY) {  // the argmax alone
+    if (threadIdx.x == 0 && cap > 0) {
+      if (ids_out) ids_out[0] = st.am;
+      if (lp_out) lp_out[0] = 0.0f;
+    }
+    finish(min(1, cap), cap >= 1 ? 0 : 1, !has_sel ? qnan : (tsel == st.am ? 0.0f : CDS_NEG_INF));
+    return;
+  }
+  const float zm = st.zm;
+  const float zcut = row_cut<NT, BF16, VEC>(rv, V, rp, zm, st.nf, sh.ex);
+  const double Td = (double)rp.temperature;
+  const float invT32 = (float)(1.0 / Td);
+  // size and mass of {allowed z >= zcut}
+  int32_t cnt = 0;
+  double mass = 0.0;
+  uint32_t nonfin = 0;
+  for_row4<NT, BF16, VEC>(rv, V, nonfin, [&](const float* x, int64_t) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      if (x[q] != CDS_NEG_INF && x[q] >= zcut) {
+        ++cnt;
+        mass += (double)exp2f((x[q] - zm) * invT32 * kLog2e);
+      }
+  });
+  cnt = block_sum_i32<NT>(cnt, sh.ex.red);
+  mass = block_sum_f64<NT>(mass, sh.ex.red);
+  const double m = (double)zm / Td;
+  const double lmass = log(mass);
+  auto lp_s = [&](float z) -> float { return (float)((double)z / Td - m - lmass); };
+  // the kept tokens in id order, at most cap: chunk by chunk (thread order
+  // within a chunk is id order), an exclusive prefix sum places each thread's
+  // members after those of lower ids
+  if (cap > 0 && ids_out) {
+    uint32_t written = 0u;
+    for (int g = 0; (int64_t)g * 4 * NT < V && written < (uint32_t)cap; g += 4) {
+      float x[4][4];
+      uint32_t nf2 = 0;
+      load_chunks<NT, 4, BF16, VEC>(rv, 0, V, g, x, nf2);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t t0 = 4 * ((int64_t)(g + i) * NT + threadIdx.x);
+        uint32_t c = 0u;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) c += (x[i][q] != CDS_NEG_INF && x[i][q] >= zcut) ? 1u : 0u;
+        uint32_t total;
+        uint32_t pos = written + block_excl<NT>(c, sh.wt, total);
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (x[i][q] != CDS_NEG_INF && x[i][q] >= zcut) {
+            if (pos < (uint32_t)cap) {
+              ids_out[pos] = (int32_t)(t0 + q);
+              if (lp_out) lp_out[pos] = lp_s(x[i][q]);
+            }
+            ++pos;
+          }
+        written += total;
+        __syncthreads();  // sh.wt is read again by the next chunk's sum
+      }
+    }
+  }
+  float sel = qnan;
+  if (has_sel) {
+    const float z = token_z<BF16>(rv, tsel);
+    sel = (z != CDS_NEG_INF && z >= zcut) ? lp_s(z) : CDS_NEG_INF;
+  }
+  finish(min(cnt, cap), cnt > cap ? 1 : 0, sel);
+}
+
+template <int NT, bool BF16, bool VEC>
+__global__ __launch_bounds__(NT) void outputs_kernel(const SampleArgs a, const OutputArgs o) {
+  __shared__ OutShared<NT> sh;
+  if ((int)blockIdx.x < o.n_row_blocks)
+    row_outputs<NT, BF16, VEC>(a, o, blockIdx.x, sh);
+  else
+    support_outputs<NT, BF16, VEC>(a, o, (int)blockIdx.x - o.n_row_blocks, sh);
+}
+
+template <bool BF16, bool VEC>
+static hipError_t launch_out(const SampleArgs& a, const OutputArgs& o, const KernelEvents* ev,
+                             hipStream_t s) {
+  const unsigned grid = (unsigned)o.n_row_blocks + (unsigned)o.n_sup;
+  if (grid == 0u) return hipSuccess;
+  if (ev && ev->start) (void)hipEventRecord(ev->start, s);
+  hipLaunchKernelGGL((outputs_kernel<kOutNT, BF16, VEC>), dim3(grid), dim3(kOutNT), 0, s, a, o);
+  if (ev && ev->stop) (void)hipEventRecord(ev->stop, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_outputs(const SampleArgs& a, const OutputArgs& o, bool bf16, bool vec,
+                          const KernelEvents* ev, hipStream_t stream) {
+  if (o.top_n_max > kMaxTopN) return hipErrorInvalidValue;
+  if (bf16)
+    return vec ? launch_out<true, true>(a, o, ev, stream) : launch_out<true, false>(a, o, ev, stream);
+  return vec ? launch_out<false, true>(a, o, ev, stream) : launch_out<false, false>(a, o, ev, stream);
+}
+
+}  // namespace cds

@@ -643,4 +643,82 @@ int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_
                            out_logprobs, out_status, workspace, ws_bytes, stream, nullptr);
 }
 
+int sampler_logprobs(const sampler_batch* b, const void* logits, int dtype, int64_t ld,
+                     const int32_t* bitmask, int64_t mask_ld, const uint8_t* row_has_mask,
+                     const sampler_logprob_request* req, const sampler_logprob_outputs* out,
+                     void* stream) {
+  if (!req || !out || req->size != sizeof(sampler_logprob_request) ||
+      out->size != sizeof(sampler_logprob_outputs))
+    return SAMPLER_EINVAL;
+  if (!b || !logits || !b->d_rows) return SAMPLER_EINVAL;
+  const int32_t B = b->B, V = b->V;
+  if (B <= 0 || V <= 0 || ld < V) return SAMPLER_EINVAL;
+  if (B > kMaxB || V > kMaxV) return SAMPLER_ERANGE;
+  if (dtype != SAMPLER_DTYPE_F32 && dtype != SAMPLER_DTYPE_BF16) return SAMPLER_EINVAL;
+  const bool bf16 = dtype == SAMPLER_DTYPE_BF16;
+  if (!aligned(logits, bf16 ? 2 : 4)) return SAMPLER_EINVAL;
+  if (bitmask && mask_ld < ((int64_t)V + 31) / 32) return SAMPLER_EINVAL;
+  if (req->basis != SAMPLER_LOGPROB_SAMPLED && req->basis != SAMPLER_LOGPROB_ORIGINAL)
+    return SAMPLER_EINVAL;
+  if (req->top_n_max < 0 || req->top_n_max > SAMPLER_MAX_TOP_N) return SAMPLER_EINVAL;
+  // each output needs its input, each input its output
+  if (out->next_token_logprobs && !req->selected) return SAMPLER_EINVAL;
+  const bool top = req->top_n_max > 0;
+  if (top != (out->top_logprobs_idx != nullptr) || top != (out->top_logprobs_val != nullptr))
+    return SAMPLER_EINVAL;
+  if (req->top_n && !top) return SAMPLER_EINVAL;
+  const bool named = req->token_indptr != nullptr;
+  if (named != (req->token_ids != nullptr) || named != (out->token_ids_logprobs != nullptr))
+    return SAMPLER_EINVAL;
+  if (req->n_mask_rows < 0 || req->mask_cap < 0) return SAMPLER_EINVAL;
+  const bool mask = req->n_mask_rows > 0;
+  if (mask && (!req->mask_rows || !out->mask_lengths || !out->mask_statuses ||
+               (req->mask_cap > 0 && !out->mask_token_ids)))
+    return SAMPLER_EINVAL;
+  if (!mask && (out->mask_token_ids || out->mask_support_logprobs || out->mask_lengths ||
+                out->mask_selected_logprobs || out->mask_statuses))
+    return SAMPLER_EINVAL;
+  if (out->mask_support_logprobs && !out->mask_token_ids) return SAMPLER_EINVAL;
+  if ((int64_t)req->n_mask_rows * (int64_t)req->mask_cap > ((int64_t)1 << 40)) return SAMPLER_ERANGE;
+
+  SampleArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.rows = static_cast<const RowParams*>(b->d_rows);
+  a.logits = logits;
+  a.ld = ld;
+  a.B = B;
+  a.V = V;
+  a.mask = bitmask;
+  a.mask_ld = mask_ld;
+  a.row_has_mask = row_has_mask;
+
+  OutputArgs o;
+  std::memset(&o, 0, sizeof o);
+  o.basis = req->basis;
+  o.top_n_max = req->top_n_max;
+  o.top_n = req->top_n;
+  o.tok_off = req->token_indptr;
+  o.tok_ids = req->token_ids;
+  o.sel_ids = req->selected;
+  o.sup_rows = mask ? req->mask_rows : nullptr;
+  o.n_sup = mask ? req->n_mask_rows : 0;
+  o.sup_cap = req->mask_cap;
+  o.next_lp = out->next_token_logprobs;
+  o.top_ids = out->top_logprobs_idx;
+  o.top_vals = out->top_logprobs_val;
+  o.tok_vals = out->token_ids_logprobs;
+  o.sup_ids = out->mask_token_ids;
+  o.sup_lp = out->mask_support_logprobs;
+  o.sup_len = out->mask_lengths;
+  o.sup_sel = out->mask_selected_logprobs;
+  o.sup_st = out->mask_statuses;
+  o.n_row_blocks = (top || named || o.next_lp) ? B : 0;
+  if (o.n_row_blocks == 0 && o.n_sup == 0) return SAMPLER_OK;
+
+  const size_t elem = bf16 ? 2 : 4;
+  const bool vec = aligned(logits, 4 * elem) && (ld % 4 == 0) && (V % 4 == 0);
+  const hipError_t e = launch_outputs(a, o, bf16, vec, nullptr, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SAMPLER_OK : SAMPLER_EHIP;
+}
+
 }  // extern "C"

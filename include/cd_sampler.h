@@ -362,6 +362,111 @@ int sampler_sample_ex(const sampler_batch *b, const void *logits, int dtype,
                       void *workspace, size_t ws_bytes, void *stream,
                       const sampler_options *opt);
 
+/* ---- further outputs ------------------------------------------------------
+ * What the sampler returns beside the drawn token ([SGL]
+ * "LogitsProcessorOutput 的五段结构"): the chosen token's logprob, the top-N
+ * logprobs (next_token_top_logprobs_val / _idx), the logprobs of tokens a
+ * request names (next_token_token_ids_logprobs_val), and the sampling support
+ * set (SamplingMaskOutput: token_ids, lengths, selected_logprobs,
+ * support_logprobs, statuses).  sampler_logprobs computes them for a packed
+ * batch from the same logits sampler_sample read (after the transforms, the
+ * bitmask fused or applied), on `stream`, after the draw when `selected` is
+ * given; with `selected` NULL it is the scoring path: logprobs of the same
+ * preprocessed logits with no draw ([SGL] "LogitsProcessor 与
+ * LogitsProcessorOutput": compute_logprobs_only).
+ *
+ * Basis of every logprob but the support set's ([SGL] "logprobs 的数值一致
+ * 性"): SAMPLER_LOGPROB_SAMPLED (0): log_softmax(z/T) over the allowed
+ * tokens, greedy rows log_softmax(z) -- the basis of sampler_sample's
+ * out_logprobs; SAMPLER_LOGPROB_ORIGINAL (1): log_softmax(z) for every row,
+ * the logits before the temperature.
+ *
+ * Request (all device arrays; NULL = not asked for):
+ *   selected        int32 [B]: the drawn tokens (sampler_sample's out_ids).
+ *   top_n_max       columns of the top-N outputs, 0..SAMPLER_MAX_TOP_N.
+ *   top_n           int32 [B]: the row's N (top_logprobs_nums), clamped to
+ *                   [0, top_n_max]; NULL: top_n_max for every row.
+ *   token_indptr    int64 [B+1], token_ids int32: the named tokens per row
+ *                   (token_ids_logprobs, CSR).
+ *   mask_rows       int32 [n_mask_rows]: the rows that return their support
+ *                   set (sampling_mask_batch_indices); a row may appear more
+ *                   than once; an index outside [0, B) gives status INVALID.
+ *   mask_cap        ids kept per support set.
+ * Outputs (device; NULL = not written):
+ *   next_token_logprobs   float [B]: logprob of selected[r] in the basis
+ *                   (needs selected); NaN on an OVERFLOW row or for an id
+ *                   outside [0, V), -inf on an INVALID row or a masked id.
+ *   top_logprobs_idx int32 [B, top_n_max], top_logprobs_val float: the row's
+ *                   N largest z, larger first, the lower id first among equal
+ *                   values, with their logprobs; entries past the allowed
+ *                   tokens and columns past the row's N are -1 / -inf; an
+ *                   OVERFLOW row's N entries are -1 / NaN.  Both or neither;
+ *                   required when top_n_max > 0.
+ *   token_ids_logprobs float [token_indptr[B]]: logprob of each named token
+ *                   (NaN for an id outside [0, V) or on an OVERFLOW row,
+ *                   -inf if masked).  Required with token_indptr.
+ *   mask_token_ids  int32 [n_mask_rows, mask_cap]: the support set in
+ *                   ascending id order, at most mask_cap of it: the tokens the
+ *                   row's draw is made from (the set sampler_sample defines;
+ *                   a greedy row's is its argmax alone).
+ *   mask_support_logprobs float [n_mask_rows, mask_cap]: their logprobs
+ *                   renormalised over the whole support (the distribution the
+ *                   draw used, at the row's temperature, whatever the basis).
+ *   mask_lengths    int32 [n_mask_rows]: ids written, min(|support|, cap).
+ *   mask_selected_logprobs float [n_mask_rows]: the renormalised logprob of
+ *                   selected[row] (-inf outside the support, NaN without
+ *                   selected or for an id outside [0, V)).
+ *   mask_statuses   int32 [n_mask_rows]: SAMPLER_STATUS_OK; OVERFLOW: the
+ *                   support has more than mask_cap tokens; INVALID: the row has
+ *                   no distribution (no finite allowed logit, or a NaN / +inf
+ *                   among them).  Severity-ordered so that a MAX reduction
+ *                   reaches one decision ([SGL] "LogitsProcessorOutput").
+ *   mask_lengths and mask_statuses are required when n_mask_rows > 0, and
+ *   mask_token_ids when mask_cap > 0 as well.
+ * Other arguments as sampler_sample; no workspace.  Errors: an inconsistent
+ * request (an output without its input, a missing required output, a record
+ * of another size, basis or top_n_max out of range) -> SAMPLER_EINVAL;
+ * launch failure -> SAMPLER_EHIP.  Nothing asked for: SAMPLER_OK, no launch.
+ * Cost: one workgroup per row (when a per-row output is asked for) plus one
+ * per support row, each streaming its row several times.
+ * -------------------------------------------------------------------------- */
+#define SAMPLER_LOGPROB_SAMPLED 0
+#define SAMPLER_LOGPROB_ORIGINAL 1
+#define SAMPLER_MAX_TOP_N 256
+typedef struct sampler_logprob_request {
+  uint32_t size; /* sizeof(sampler_logprob_request) as the caller compiled it */
+  int32_t basis;
+  const int32_t *selected;
+  int32_t top_n_max;
+  int32_t n_mask_rows;
+  const int32_t *top_n;
+  const int64_t *token_indptr;
+  const int32_t *token_ids;
+  const int32_t *mask_rows;
+  int32_t mask_cap;
+  int32_t pad_;
+} sampler_logprob_request;
+
+typedef struct sampler_logprob_outputs {
+  uint32_t size; /* sizeof(sampler_logprob_outputs) as the caller compiled it */
+  int32_t pad_;
+  float *next_token_logprobs;
+  int32_t *top_logprobs_idx;
+  float *top_logprobs_val;
+  float *token_ids_logprobs;
+  int32_t *mask_token_ids;
+  float *mask_support_logprobs;
+  int32_t *mask_lengths;
+  float *mask_selected_logprobs;
+  int32_t *mask_statuses;
+} sampler_logprob_outputs;
+
+int sampler_logprobs(const sampler_batch *b, const void *logits, int dtype,
+                     int64_t ld, const int32_t *bitmask, int64_t mask_ld,
+                     const uint8_t *row_has_mask,
+                     const sampler_logprob_request *req,
+                     const sampler_logprob_outputs *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -36,6 +36,10 @@ hipError_t static_workspace(void**, hipStream_t) { return hipErrorNotSupported; 
 hipError_t launch_sample(const SampleArgs&, bool, bool, int, const KernelEvents*, hipStream_t) {
   return hipSuccess;
 }
+hipError_t launch_outputs(const SampleArgs&, const OutputArgs&, bool, bool, const KernelEvents*,
+                          hipStream_t) {
+  return hipSuccess;
+}
 }  // namespace cds
 
 static int fail(const char* what, int it) {

@@ -273,3 +273,51 @@ def test_workspace_per_batch_smaller_than_bound(cds):
     assert b.ws_records == P * (4 + 2 + 2)
     caps = {20: 128, 50: 192, 1000: 640}     # 2q + 64 rounded up to 64 entries
     assert b.ws_list_entries == P * (caps[20] + 2048 + caps[50] + caps[1000]) + 2 * P * 2048
+
+
+def test_logprobs_request_validation(cds):
+    """sampler_logprobs rejects inconsistent requests before any launch, and
+    returns OK without a launch when nothing is asked for (host pointers stand
+    in for device ones: nothing reaches the GPU)."""
+    _, b = cds.pack_host(4, 1000, np.ones(4, np.float32))
+    logits = np.zeros((4, 1000), np.float32)
+    dummy = np.zeros(4096, np.int64)
+    P = dummy.ctypes.data
+
+    def call(req=None, out=None, **kw):
+        r = cds.LogprobRequest(size=ct.sizeof(cds.LogprobRequest))
+        o = cds.LogprobOutputs(size=ct.sizeof(cds.LogprobOutputs))
+        for k, v in (req or {}).items():
+            setattr(r, k, v)
+        for k, v in (out or {}).items():
+            setattr(o, k, v)
+        return cds.lib.sampler_logprobs(ct.byref(b), logits.ctypes.data, 0, 1000, None, 0, None,
+                                        ct.byref(r), ct.byref(o), None)
+
+    assert call() == 0                                        # nothing asked: no launch
+    bad = [
+        ({"size": 8}, {}),
+        ({"basis": 2}, {}),
+        ({"top_n_max": cds.MAX_TOP_N + 1}, {"top_logprobs_idx": P, "top_logprobs_val": P}),
+        ({"top_n_max": 5}, {}),                               # no top-N outputs
+        ({}, {"top_logprobs_idx": P, "top_logprobs_val": P}),  # outputs, top_n_max 0
+        ({"top_n": P}, {}),
+        ({}, {"next_token_logprobs": P}),                     # needs selected
+        ({"token_indptr": P, "token_ids": P}, {}),            # no output
+        ({"token_indptr": P}, {"token_ids_logprobs": P}),     # no ids
+        ({"n_mask_rows": 3, "mask_rows": P, "mask_cap": 4},
+         {"mask_lengths": P, "mask_statuses": P}),            # no ids output
+        ({"n_mask_rows": 3, "mask_rows": P}, {"mask_statuses": P}),
+        ({"n_mask_rows": 3}, {"mask_lengths": P, "mask_statuses": P}),
+        ({}, {"mask_lengths": P}),                            # outputs without rows
+        ({"n_mask_rows": -1}, {}),
+        ({"n_mask_rows": 2, "mask_rows": P, "mask_cap": -1},
+         {"mask_lengths": P, "mask_statuses": P}),
+    ]
+    for req, out in bad:
+        assert call(req, out) == -1, (req, out)
+    # a record of another size
+    r = cds.LogprobRequest(size=ct.sizeof(cds.LogprobRequest))
+    o = cds.LogprobOutputs(size=ct.sizeof(cds.LogprobOutputs) - 8)
+    assert cds.lib.sampler_logprobs(ct.byref(b), logits.ctypes.data, 0, 1000, None, 0, None,
+                                    ct.byref(r), ct.byref(o), None) == -1
