@@ -57,6 +57,10 @@ def parse():
                          "step) or on the compute stream; auto: the side stream for "
                          "blocks over 64 KB (measured: it pays for c3's 434 KB block, "
                          "and stalls the host for mid-size blocks such as c5's 41 KB)")
+    ap.add_argument("--outputs", action="store_true",
+                    help="time the further-outputs call (sampler_logprobs: top-20 and 4 "
+                         "named-token logprobs per row, the support sets of every 12th "
+                         "row) on the workload instead of the sampling step")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (the "
                          "reference point for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -78,29 +82,36 @@ WORKLOAD_FILES = {"c2": "c2_decode", "c3": "c3_penalties", "c4": "c4_grammar",
                   "c5a": "c5a_spec_greedy", "c5b": "c5b_spec_topk"}
 
 
-def kernel_sources_digest():
+KERNEL_SOURCES = {
+    "sample_kernel": ("kernels.hip", "exact_path.h", "device_common.h", "layout.h"),
+    "outputs_kernel": ("outputs.hip", "exact_path.h", "device_common.h", "layout.h", "kernels.h"),
+}
+
+
+def kernel_sources_digest(kernel="sample_kernel"):
     import hashlib
     h = hashlib.sha256()
-    for f in ("kernels.hip", "device_common.h", "layout.h"):
+    for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(ROOT, "constrained_decoding_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
-def measured_traffic(config):
-    """HBM bytes per sample_kernel launch from the committed FETCH_SIZE /
+def measured_traffic(config, kernel="sample_kernel"):
+    """HBM bytes per launch of `kernel` from the committed FETCH_SIZE /
     WRITE_SIZE summary of this workload, or None when that summary is missing
     or was taken on different kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{WORKLOAD_FILES[config]}.md")
+    name = WORKLOAD_FILES[config] + ("" if kernel == "sample_kernel" else "_outputs")
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{name}.md")
     if not os.path.exists(path):
         return None
     fields = {}
     with open(path) as fh:
         for ln in fh:
-            if ln.startswith("sample_kernel ") and ":" in ln:
+            if ln.startswith(kernel + " ") and ":" in ln:
                 k, v = ln.split(":", 1)
                 fields[k.split()[1]] = v.strip()
-    if fields.get("traffic_sources_sha256") != kernel_sources_digest():
+    if fields.get("traffic_sources_sha256") != kernel_sources_digest(kernel):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
@@ -125,6 +136,20 @@ def algorithmic_bytes(batch):
         n += int(batch.bias_indptr[-1]) * (8 + 8)
     n += batch.B * (ROW_PARAM_BYTES + ROW_OUT_BYTES)
     return n
+
+
+WORKLOAD_NAMES = {
+    "c2": "decode B=192 V=151936 fp32, mixed greedy/top-k/top-p/min-p",
+    "c3": "penalties+bias B=192 V=151936 fp32, T=0.8 top_p=0.95",
+    "c4": "grammar bitmask B=192 V=151936 bf16, 96 masked rows, T=0.7 top_p=0.9",
+    "c5a": "spec-verify 64x8=512 rows V=151936 fp32, all greedy",
+    "c5b": "spec-verify 64x8=512 rows V=151936 fp32, T=1 top_k=50"}
+
+# the further-outputs request the --outputs leg times on every input set
+OUT_TOP_N = 20           # top logprobs per row
+OUT_NAMED = 4            # named tokens per row
+OUT_MASK_EVERY = 12      # every 12th row returns its support set ...
+OUT_MASK_CAP = 40000     # ... with room for this many tokens
 
 
 def cpu_model():
@@ -198,6 +223,10 @@ def main():
     torch.cuda.set_device(0)
     if args.copy_calibration:
         copy_calibration(args.copy_calibration)
+        return
+
+    if args.outputs:
+        bench_outputs(args)
         return
 
     import constrained_decoding_amd as cds
@@ -363,11 +392,7 @@ def main():
 
     cpu = None if args.no_cpu else cpu_baseline(sets, args.cpu_rows)
 
-    names = {"c2": "decode B=192 V=151936 fp32, mixed greedy/top-k/top-p/min-p",
-             "c3": "penalties+bias B=192 V=151936 fp32, T=0.8 top_p=0.95",
-             "c4": "grammar bitmask B=192 V=151936 bf16, 96 masked rows, T=0.7 top_p=0.9",
-             "c5a": "spec-verify 64x8=512 rows V=151936 fp32, all greedy",
-             "c5b": "spec-verify 64x8=512 rows V=151936 fp32, T=1 top_k=50"}
+    names = WORKLOAD_NAMES
     line = {
         "metric": METRIC,
         "value": round(rows_per_s, 1),
@@ -400,6 +425,238 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(line), flush=True)
+
+
+def bench_outputs(args):
+    """The further-outputs call (sampler_logprobs) on the workload, two
+    requests timed apart: every row asks for its top-20 logprobs, the
+    logprobs of 4 named tokens and the chosen token's logprob (the value and
+    the roofline); every 12th row returns its support set with room for 40000
+    tokens, from the thresholds the sampling call returned (the "support"
+    object).  The sampling step runs once per input set before the timed
+    region (its ids are the chosen tokens, its thresholds the support sets').  One JSON line in
+    the form of the sampling step's, for outputs_kernel."""
+    import torch
+
+    import constrained_decoding_amd as cds
+    from constrained_decoding_amd import _binding as bd
+    import workloads
+
+    sets = [workloads.input_set(args.config, s) for s in range(args.sets)]
+    b0 = sets[0]
+    B, V = b0.B, b0.V
+    rng = np.random.default_rng(20261202)
+    named = [[rng.integers(0, V, OUT_NAMED) for _ in range(B)] for _ in sets]
+    mask_rows = np.arange(0, B, OUT_MASK_EVERY, dtype=np.int32)
+    R = len(mask_rows)
+    d_mask_rows = torch.from_numpy(mask_rows).cuda()
+    top_n = torch.full((B,), OUT_TOP_N, dtype=torch.int32, device="cuda")
+    # outputs, shared by the input sets
+    o_next = torch.empty(B, dtype=torch.float32, device="cuda")
+    o_tidx = torch.empty((B, OUT_TOP_N), dtype=torch.int32, device="cuda")
+    o_tval = torch.empty((B, OUT_TOP_N), dtype=torch.float32, device="cuda")
+    o_tok = torch.empty(B * OUT_NAMED, dtype=torch.float32, device="cuda")
+    o_mids = torch.empty((R, OUT_MASK_CAP), dtype=torch.int32, device="cuda")
+    o_mlp = torch.empty((R, OUT_MASK_CAP), dtype=torch.float32, device="cuda")
+    o_mlen = torch.empty(R, dtype=torch.int32, device="cuda")
+    o_msel = torch.empty(R, dtype=torch.float32, device="cuda")
+    o_mst = torch.empty(R, dtype=torch.int32, device="cuda")
+    out_rows = bd.LogprobOutputs(
+        size=ct.sizeof(bd.LogprobOutputs), next_token_logprobs=o_next.data_ptr(),
+        top_logprobs_idx=o_tidx.data_ptr(), top_logprobs_val=o_tval.data_ptr(),
+        token_ids_logprobs=o_tok.data_ptr())
+    out_sup = bd.LogprobOutputs(
+        size=ct.sizeof(bd.LogprobOutputs), mask_token_ids=o_mids.data_ptr(),
+        mask_support_logprobs=o_mlp.data_ptr(), mask_lengths=o_mlen.data_ptr(),
+        mask_selected_logprobs=o_msel.data_ptr(), mask_statuses=o_mst.data_ptr())
+    keep, calls = [], {"rows": [], "support": []}
+    for j, b in enumerate(sets):
+        if b.bf16:
+            x = torch.from_numpy(np.ascontiguousarray(b.logits).view(np.int16)) \
+                .view(torch.bfloat16).cuda()
+        else:
+            x = torch.from_numpy(b.logits).cuda()
+        kw = dict(top_k=b.top_k, top_p=b.top_p, min_p=b.min_p, seed=b.seed, offset=b.offset)
+        if b.rep is not None:
+            kw.update(repetition_penalty=b.rep, frequency_penalty=b.freq,
+                      presence_penalty=b.pres, hist_indptr=b.hist_indptr, hist_ids=b.hist_ids)
+        if b.bias_indptr is not None:
+            kw.update(bias_indptr=b.bias_indptr, bias_ids=b.bias_ids, bias_vals=b.bias_vals)
+        pk = cds.PackedBatch(B, V, b.temperature, **kw)
+        if b.rep is not None or b.bias_indptr is not None:
+            cds.apply_transforms(pk, x)
+        m = None if b.masks is None else torch.from_numpy(b.masks).cuda()
+        rh = None if b.row_has_mask is None else torch.from_numpy(b.row_has_mask).cuda()
+        cut = torch.empty(B, dtype=torch.float32, device="cuda")
+        ids, _, _ = cds.sample(pk, x, bitmask=m, row_has_mask=rh, cut=cut)
+        indptr, flat = cds.csr(named[j])
+        d_ind = torch.from_numpy(indptr).cuda()
+        d_tok = torch.from_numpy(flat.astype(np.int32)).cuda()
+        req_rows = bd.LogprobRequest(size=ct.sizeof(bd.LogprobRequest), basis=cds.LOGPROB_SAMPLED,
+                                     selected=ids.data_ptr(), top_n_max=OUT_TOP_N,
+                                     top_n=top_n.data_ptr(), token_indptr=d_ind.data_ptr(),
+                                     token_ids=d_tok.data_ptr())
+        req_sup = bd.LogprobRequest(size=ct.sizeof(bd.LogprobRequest), basis=cds.LOGPROB_SAMPLED,
+                                    selected=ids.data_ptr(), n_mask_rows=R,
+                                    mask_rows=d_mask_rows.data_ptr(), mask_cap=OUT_MASK_CAP,
+                                    cuts=cut.data_ptr())
+        keep.append((x, pk, m, rh, ids, cut, d_ind, d_tok, req_rows, req_sup))
+        base = (ct.byref(pk.batch), x.data_ptr(), x.stride(0),
+                None if m is None else m.data_ptr(), 0 if m is None else m.stride(0),
+                None if rh is None else rh.data_ptr())
+        calls["rows"].append(base + (ct.byref(req_rows), ct.byref(out_rows)))
+        calls["support"].append(base + (ct.byref(req_sup), ct.byref(out_sup)))
+    dtype = cds.DTYPE_BF16 if b0.bf16 else cds.DTYPE_F32
+    compute_h = torch.cuda.current_stream().cuda_stream
+    lib = bd.lib
+
+    def launch(kind, j):
+        br, xp, ld, mp, mld, rp, rq, oq = calls[kind][j]
+        rc = lib.sampler_logprobs(br, xp, dtype, ld, mp, mld, rp, rq, oq, compute_h)
+        if rc != 0:
+            raise cds.SamplerError(rc, "sampler_logprobs")
+
+    # support entries written per launch (for the algorithmic bytes)
+    sup_entries = []
+    for j in range(len(sets)):
+        launch("support", j)
+        torch.cuda.synchronize()
+        sup_entries.append(int(o_mlen.sum().item()))
+
+    def timed(kind):
+        for i in range(args.warmup):
+            launch(kind, i % len(sets))
+        torch.cuda.synchronize()
+        every = 4
+        evs = {i: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for i in range(0, args.steps, every)}
+        for e in evs.values():
+            e[0].record()
+            e[1].record()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            ev = evs.get(i)
+            if ev:
+                ev[0].record()
+            launch(kind, i % len(sets))
+            if ev:
+                ev[1].record()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        kern = np.array([a.elapsed_time(z) for a, z in evs.values()]) * 1e3   # us
+        return elapsed, kern
+
+    elapsed, kern = timed("rows")
+    s_elapsed, s_kern = timed("support")
+
+    elem = 2 if b0.bf16 else 4
+    mwords = (V + 31) // 32 * 4
+    mrows = 0 if b0.masks is None else (B if b0.row_has_mask is None else int(b0.row_has_mask.sum()))
+    # per-row request: each row read once, its params, chosen id, named ids
+    # and offsets in; chosen, top-N (id + value) and named logprobs out
+    alg = B * V * elem + mrows * mwords + B * (ROW_PARAM_BYTES + 4) + B * OUT_NAMED * 4 + \
+        (B + 1) * 8 + B * 4 + B * OUT_TOP_N * 8 + B * OUT_NAMED * 4
+    # support request: each support row read once; ids and logprobs of the
+    # support entries plus length, status and selected logprob out
+    sup_mrows = 0 if b0.masks is None else int(
+        (np.ones(B, bool) if b0.row_has_mask is None else b0.row_has_mask.astype(bool))[mask_rows].sum())
+    s_alg = R * V * elem + sup_mrows * mwords + R * (ROW_PARAM_BYTES + 8) + R * 12 + \
+        int(np.mean(sup_entries)) * 8
+    kern_mean, s_mean = float(np.mean(kern)), float(np.mean(s_kern))
+    achieved = alg / (kern_mean * 1e-6) / 1e9
+    s_achieved = s_alg / (s_mean * 1e-6) / 1e9
+
+    cpu = None if args.no_cpu else cpu_baseline_outputs(sets, named, args.cpu_rows // 4)
+    line = {
+        "metric": "rows/sec with further outputs (top-20 and 4 named-token logprobs and the "
+                  "chosen token's logprob per row) at B=192, V=151936 (1 GPU)",
+        "value": round(B * args.steps / elapsed, 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(elapsed * 1e3 / args.steps, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if b0.bf16 else "f32",
+        "data": "synthetic (seeded; stands in for GLM-5.3 decode logits)",
+        "config": {"workload": WORKLOAD_NAMES[args.config] + "; further outputs",
+                   "B": B, "V": V, "input_sets": len(sets), "top_n": OUT_TOP_N,
+                   "named_tokens_per_row": OUT_NAMED},
+        "roofline": {"bound": "hbm", "kernel": "outputs_kernel", "achieved": round(achieved, 1),
+                     "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(args.config, "outputs_kernel"),
+                     "kernel_us": round(kern_mean, 2),
+                     "kernel_launches_timed": len(kern),
+                     "kernel_us_p10_p50_p90": [round(float(np.percentile(kern, q)), 2)
+                                               for q in (10, 50, 90)],
+                     "bytes_per_launch": alg},
+        "support": {"rows": R, "cap": OUT_MASK_CAP, "kernel_us": round(s_mean, 2),
+                    "kernel_us_p10_p50_p90": [round(float(np.percentile(s_kern, q)), 2)
+                                              for q in (10, 50, 90)],
+                    "entries_per_launch": int(np.mean(sup_entries)),
+                    "bytes_per_launch": s_alg, "achieved": round(s_achieved, 1),
+                    "frac": round(s_achieved / PEAK_HBM_GBS, 4),
+                    "rows_per_s": round(R * args.steps / s_elapsed, 1)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def cpu_baseline_outputs(sets, named, n_rows):
+    """The oracle's per-row further outputs (top-20, named tokens, chosen
+    token) on a bounded sample of rows (in order, rotating the input sets),
+    row-parallel over the host cores."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    import oracle
+
+    B = sets[0].B
+    work = []
+    k = 0
+    while len(work) < n_rows:
+        j = k % len(sets)
+        for r in range(min(B, n_rows - len(work))):
+            work.append((j, r))
+        k += 1
+    params = [b.oracle_params() for b in sets]
+
+    def one(jr):
+        j, r = jr
+        b, pr = sets[j], params[j]
+        hist = pr.get("hist")
+        bias = pr.get("bias")
+        mk = None
+        if b.masks is not None and (b.row_has_mask is None or b.row_has_mask[r]):
+            mk = b.masks[r]
+        z = oracle.transform_row(
+            b.logits[r], hist_ids=None if hist is None or hist[r] is None or not len(hist[r])
+            else np.asarray(hist[r], np.int32),
+            rep=float(pr["rep"][r]) if "rep" in pr else 1.0,
+            freq=float(pr["freq"][r]) if "freq" in pr else 0.0,
+            pres=float(pr["pres"][r]) if "pres" in pr else 0.0,
+            bias_ids=np.asarray([q[0] for q in bias[r]], np.int32) if bias and bias[r] else None,
+            bias_vals=np.asarray([q[1] for q in bias[r]], np.float32) if bias and bias[r] else None,
+            mask=mk, bf16=b.bf16)
+        oracle.row_outputs(z, T=float(b.temperature[r]), top_k=int(b.top_k[r]),
+                           top_p=float(b.top_p[r]), min_p=float(b.min_p[r]),
+                           seed=int(b.seed[r]), offset=int(b.offset[r]), order=b.order,
+                           n_top=OUT_TOP_N, token_ids=named[j][r], selected=0)
+
+    oracle.sample_row(np.zeros(4, np.float32), T=1.0)   # load the library first
+    workers = max(1, min(MAX_CPU_WORKERS, len(os.sched_getaffinity(0))))
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(workers) as ex:
+        list(ex.map(one, work))
+    tn = time.perf_counter() - t0
+    return {"value": round(len(work) / tn, 3), "unit": "rows/s", "cores": workers,
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "sample": f"transforms and further outputs of {len(work)} rows of the same "
+                      f"workload (rotating the {len(sets)} input sets), row-parallel over "
+                      f"{workers} threads, {tn:.1f} s"}
 
 
 if __name__ == "__main__":

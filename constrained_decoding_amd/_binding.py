@@ -62,6 +62,7 @@ class Options(ct.Structure):
     _fields_ = [
         ("size", ct.c_uint32), ("algo", ct.c_int32), ("wait_ns", ct.c_int64),
         ("trace", ct.c_void_p), ("start_event", ct.c_void_p), ("stop_event", ct.c_void_p),
+        ("cut", ct.c_void_p),
     ]
 
 
@@ -70,7 +71,7 @@ class LogprobRequest(ct.Structure):
         ("size", ct.c_uint32), ("basis", ct.c_int32), ("selected", ct.c_void_p),
         ("top_n_max", ct.c_int32), ("n_mask_rows", ct.c_int32), ("top_n", ct.c_void_p),
         ("token_indptr", ct.c_void_p), ("token_ids", ct.c_void_p), ("mask_rows", ct.c_void_p),
-        ("mask_cap", ct.c_int32), ("pad_", ct.c_int32),
+        ("mask_cap", ct.c_int32), ("pad_", ct.c_int32), ("cuts", ct.c_void_p),
     ]
 
 
@@ -324,14 +325,16 @@ def _event_ptr(e):
 
 
 def sample(packed: PackedBatch, logits, *, bitmask=None, row_has_mask=None, workspace=None,
-           out=None, stream=None, algo=ALGO_FAST, wait_ns=0, trace=None, events=None):
+           out=None, stream=None, algo=ALGO_FAST, wait_ns=0, trace=None, events=None, cut=None):
     """The sampling step.  Returns (ids int32 [B], logprobs float32 [B],
     status int32 [B]) as device tensors (``out`` may supply them).
 
     Per-call options (sampler_sample_ex): ``algo`` ALGO_FAST or ALGO_EXACT;
     ``wait_ns`` 0 (default wait), WAIT_NONE or nanoseconds; ``trace`` a
     device int64 tensor for phase timestamps; ``events`` a pair of
-    torch.cuda.Event recorded right around the sampling kernel."""
+    torch.cuda.Event recorded right around the sampling kernel; ``cut`` a
+    device float32 [B] tensor that receives each sampled row's kept-set
+    threshold (for logprobs(..., cuts=cut))."""
     import torch
     B, V = logits.shape
     if (B, V) != (packed.B, packed.V):
@@ -353,27 +356,29 @@ def sample(packed: PackedBatch, logits, *, bitmask=None, row_has_mask=None, work
             ids.data_ptr(), None if lp is None else lp.data_ptr(),
             None if st is None else st.data_ptr(), workspace.ptr, workspace.nbytes,
             _stream_ptr(stream))
-    if algo == ALGO_FAST and wait_ns == 0 and trace is None and events is None:
+    if algo == ALGO_FAST and wait_ns == 0 and trace is None and events is None and cut is None:
         _check(lib.sampler_sample(*args), "sampler_sample")
     else:
         o = Options(size=ct.sizeof(Options), algo=int(algo), wait_ns=int(wait_ns),
                     trace=None if trace is None else trace.data_ptr(),
                     start_event=None if events is None else _event_ptr(events[0]),
-                    stop_event=None if events is None else _event_ptr(events[1]))
+                    stop_event=None if events is None else _event_ptr(events[1]),
+                    cut=None if cut is None else cut.data_ptr())
         _check(lib.sampler_sample_ex(*args, ct.byref(o)), "sampler_sample_ex")
     return ids, lp, st
 
 
 def logprobs(packed: PackedBatch, logits, *, selected=None, basis=LOGPROB_SAMPLED, top_n_max=0,
              top_n=None, token_indptr=None, token_ids=None, mask_rows=None, mask_cap=0,
-             support_logprobs=True, bitmask=None, row_has_mask=None, stream=None):
+             support_logprobs=True, cuts=None, bitmask=None, row_has_mask=None, stream=None):
     """Further outputs (sampler_logprobs).  Device tensors in, a dict of
     device tensors out: ``next`` [B] (with ``selected``), ``top_idx`` /
     ``top_val`` [B, top_n_max], ``token`` [token_indptr[-1]] (named tokens),
     and for ``mask_rows`` (int32 row indices) ``mask_ids`` [R, mask_cap],
     ``mask_lp`` [R, mask_cap] (if ``support_logprobs``), ``mask_len``,
     ``mask_sel`` and ``mask_status`` [R].  ``selected=None``: scoring, no
-    draw."""
+    draw.  ``cuts``: the kept-set thresholds sample(..., cut=) returned for
+    the same batch (support sets then skip selecting them again)."""
     import torch
     B, V = logits.shape
     if (B, V) != (packed.B, packed.V):
@@ -407,7 +412,7 @@ def logprobs(packed: PackedBatch, logits, *, selected=None, basis=LOGPROB_SAMPLE
                          selected=ptr(selected), top_n_max=int(top_n_max), n_mask_rows=R,
                          top_n=ptr(top_n), token_indptr=ptr(token_indptr),
                          token_ids=ptr(token_ids), mask_rows=ptr(mask_rows) if R else None,
-                         mask_cap=int(mask_cap))
+                         mask_cap=int(mask_cap), cuts=ptr(cuts))
     out = LogprobOutputs(size=ct.sizeof(LogprobOutputs),
                          next_token_logprobs=ptr(res.get("next")),
                          top_logprobs_idx=ptr(res.get("top_idx")),

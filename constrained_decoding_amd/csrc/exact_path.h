@@ -63,8 +63,9 @@ struct ExactShared {
 };
 
 // Visit every token of the row in groups of four (t0 % 4 == 0).
-// K chunks per thread are loaded per round, all loads in flight at once.
-template <int NT, bool BF16, bool VEC, typename F, int K = 4>
+// K chunks per thread are loaded per round, all loads in flight at once (one
+// workgroup per row: the bytes in flight set the pass's speed).
+template <int NT, bool BF16, bool VEC, int K = 4, typename F>
 __device__ __forceinline__ void for_row4(const RowView& rv, int64_t V, uint32_t& nonfin, F f) {
 #pragma unroll 1
   for (int g = 0; (int64_t)g * 4 * NT < V; g += K) {
@@ -124,13 +125,13 @@ struct RowStats {
   uint32_t nonfin;
 };
 
-template <int NT, bool BF16, bool VEC>
+template <int NT, bool BF16, bool VEC, int K = 4>
 __device__ __forceinline__ RowStats row_stats(const RowView& rv, int64_t V, ExactShared<NT>& sh) {
   uint32_t nonfin = 0;
   float zm = CDS_NEG_INF;
   int32_t am = INT_MAX;
   int32_t nf = 0;
-  for_row4<NT, BF16, VEC>(rv, V, nonfin, [&](const float* x, int64_t t0) {
+  for_row4<NT, BF16, VEC, K>(rv, V, nonfin, [&](const float* x, int64_t t0) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if (x[q] > zm) {
@@ -152,12 +153,12 @@ __device__ __forceinline__ RowStats row_stats(const RowView& rv, int64_t V, Exac
 
 // sum over the finite allowed tokens of exp((z - zm) * invT), accumulated in
 // fp64 (each term an fp32 exp2 of an fp32 exponent)
-template <int NT, bool BF16, bool VEC>
+template <int NT, bool BF16, bool VEC, int K = 4>
 __device__ __forceinline__ double row_expsum(const RowView& rv, int64_t V, float zm, float invT32,
                                              ExactShared<NT>& sh) {
   uint32_t nonfin = 0;
   double se = 0.0;
-  for_row4<NT, BF16, VEC>(rv, V, nonfin, [&](const float* x, int64_t) {
+  for_row4<NT, BF16, VEC, K>(rv, V, nonfin, [&](const float* x, int64_t) {
 #pragma unroll
     for (int q = 0; q < 4; ++q)
       if (x[q] != CDS_NEG_INF) se += (double)exp2f((x[q] - zm) * invT32 * kLog2e);
@@ -168,7 +169,7 @@ __device__ __forceinline__ double row_expsum(const RowView& rv, int64_t V, float
 // The value threshold of a sampled row (finite allowed values, nonempty): the
 // kept set is {allowed z >= returned value} (-inf: no cut).  zm: the row's
 // max z; nf: its number of finite allowed tokens.
-template <int NT, bool BF16, bool VEC>
+template <int NT, bool BF16, bool VEC, int K = 4>
 __device__ __forceinline__ float row_cut(const RowView& rv, int64_t V, const RowParams& rp, float zm,
                                          int32_t nf, ExactShared<NT>& sh) {
   uint32_t nonfin = 0;
@@ -191,7 +192,7 @@ __device__ __forceinline__ float row_cut(const RowView& rv, int64_t V, const Row
     for (int shift = 24; shift >= 0; shift -= 8) {
       if (threadIdx.x < 256) sh.hist[threadIdx.x] = 0ull;
       __syncthreads();
-      for_row4<NT, BF16, VEC>(rv, V, nonfin, [&](const float* x, int64_t) {
+      for_row4<NT, BF16, VEC, K>(rv, V, nonfin, [&](const float* x, int64_t) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           if (x[q] == CDS_NEG_INF) continue;
@@ -220,7 +221,7 @@ __device__ __forceinline__ float row_cut(const RowView& rv, int64_t V, const Row
       return (unsigned long long)(exp((double)v / Td - m) * scale + 0.5);
     };
     unsigned long long msum = 0;
-    for_row4<NT, BF16, VEC>(rv, V, nonfin, [&](const float* x, int64_t) {
+    for_row4<NT, BF16, VEC, K>(rv, V, nonfin, [&](const float* x, int64_t) {
 #pragma unroll
       for (int q = 0; q < 4; ++q)
         if (x[q] != CDS_NEG_INF && x[q] >= zc) msum += wfix(x[q]);
@@ -233,7 +234,7 @@ __device__ __forceinline__ float row_cut(const RowView& rv, int64_t V, const Row
     if (ord) {
       const float zn = (ord & ROW_ORDER_MINP_LAST) ? zk : CDS_NEG_INF;
       mnorm = 0ull;
-      for_row4<NT, BF16, VEC>(rv, V, nonfin, [&](const float* x, int64_t) {
+      for_row4<NT, BF16, VEC, K>(rv, V, nonfin, [&](const float* x, int64_t) {
 #pragma unroll
         for (int q = 0; q < 4; ++q)
           if (x[q] != CDS_NEG_INF && x[q] >= zn) mnorm += wfix(x[q]);
@@ -248,7 +249,7 @@ __device__ __forceinline__ float row_cut(const RowView& rv, int64_t V, const Row
     for (int shift = 24; shift >= 0 && !keep_all; shift -= 8) {
       if (threadIdx.x < 256) sh.hist[threadIdx.x] = 0ull;
       __syncthreads();
-      for_row4<NT, BF16, VEC>(rv, V, nonfin, [&](const float* x, int64_t) {
+      for_row4<NT, BF16, VEC, K>(rv, V, nonfin, [&](const float* x, int64_t) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
           if (x[q] == CDS_NEG_INF || x[q] < zc) continue;

@@ -23,6 +23,7 @@ struct SampleArgs {
   int32_t* out_ids;
   float* out_lp;
   int32_t* out_st;
+  float* out_cut;       // per sampled row the smallest kept value, or nullptr
   RowSync* sync;
   Plan* plans;
   SliceHead* heads;
@@ -47,6 +48,7 @@ struct OutputArgs {
   const int64_t* tok_off; // [B+1] CSR offsets of named tokens or nullptr
   const int32_t* tok_ids;
   const int32_t* sel_ids; // [B] the drawn tokens, or nullptr (scoring: no draw)
+  const float* cuts;      // [B] the sampling call's kept-set thresholds, or nullptr
   const int32_t* sup_rows;
   int32_t n_sup;
   int32_t sup_cap;

@@ -186,7 +186,10 @@ __device__ __forceinline__ void row_exact(const SampleArgs& a, int r, ExactShare
       if (x[q] != CDS_NEG_INF && x[q] >= zf) race_consider(b, x[q], (int32_t)(t0 + q), xs[q], c);
   });
   block_best<NT>(b, sh.red);
-  if (threadIdx.x == 0) write_out(a, r, b.t, (float)((double)b.z / Td - m - log_z), 0);
+  if (threadIdx.x == 0) {
+    write_out(a, r, b.t, (float)((double)b.z / Td - m - log_z), 0);
+    if (a.out_cut) a.out_cut[r] = zcut;
+  }
 }
 
 template <int NT, bool BF16, bool VEC>
@@ -1289,19 +1292,22 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
   }
   CDS_TRACE_ROW(4);
   if (b.t1 == INT_MAX) return false;
+  // the drawn-from set is {allowed z >= zfinal}
+  const float zs = fmaxf(pl.z_sure, pl.zcut1);
+  const float zfinal = (pl.topp || pl.k_rank > 0) ? zfin : zs;
   if (b.k1 - b.k2 > 2.0f * kRaceEps) {
     if (tid == 0) {
       write_out(a, r, b.t1, (float)((double)b.z1 / Td - pl.m - pl.log_z), 0);
+      if (a.out_cut) a.out_cut[r] = zfinal;
       a.plans[r].path = PATH_FAST;
     }
     return true;
   }
   // fp32 top two too close: decide in fp64 over the final set
-  const float zs = fmaxf(pl.z_sure, pl.zcut1);
-  const float zfinal = (pl.topp || pl.k_rank > 0) ? zfin : zs;
   const Best e = exact_rerace<NT, BF16, VEC>(a, r, pl, zfinal, b.k1 - 2.0f * kRaceEps, red);
   if (tid == 0) {
     write_out(a, r, e.t, (float)((double)e.z / Td - pl.m - pl.log_z), 0);
+    if (a.out_cut) a.out_cut[r] = zfinal;
     a.plans[r].path = PATH_RERACE;
   }
   return true;

@@ -11,10 +11,12 @@
 // requests take logprobs of the same preprocessed logits with no draw.
 //
 // One launch.  Row blocks (one workgroup per row) compute the row's max and
-// normaliser in the requested basis, then the chosen and named tokens'
-// logprobs by direct reads, and the top-N by an exact radix select on the
-// fp32 order key (ties broken by id with a second select on ~id), then an
-// LDS rank sort of the N winners.  Support blocks (one workgroup per
+// normaliser in the requested basis in one pass (a running sum per thread),
+// the chosen and named tokens' logprobs by direct reads, and the top-N in a
+// second pass: every token at or above the N-th largest of the threads'
+// maxima goes to an LDS candidate list, which a bitonic sort orders (an exact
+// radix select on the fp32 order key, ties broken by id, if the list would
+// overflow).  Support blocks (one workgroup per
 // requested row) find the row's value threshold with the exact path's
 // selection (row_cut), sum the kept mass, and write the kept tokens in id
 // order by a block-wide prefix sum per chunk.  Every pass streams the row;
@@ -30,13 +32,15 @@
 namespace cds {
 
 constexpr int kOutNT = 512;
+constexpr int kOutK = 16;      // chunks of 4 tokens in flight per thread and pass
 constexpr int kMaxTopN = 256;  // SAMPLER_MAX_TOP_N
+constexpr int kCandCap = 2048; // top-N candidates held in LDS
 
 template <int NT>
 struct OutShared {
   ExactShared<NT> ex;
-  uint32_t key[kMaxTopN];
-  int32_t id[kMaxTopN];
+  unsigned long long cand[kCandCap];  // okey(z) << 32 | ~id: larger = earlier in the order
+  float tmax[NT];
   uint32_t cnt;
   uint32_t wt[NT / 64];
 };
@@ -56,7 +60,7 @@ __device__ __forceinline__ bool finite_f(float x) { return x > CDS_NEG_INF && x 
 // the `need`-th largest key among the tokens `sel` admits, counting with
 // `key`.  Returns the key; *tie_rem = how many tokens with exactly that key
 // the `need` largest hold, *tie_cnt = how many tokens have it.
-template <int NT, bool BF16, bool VEC, typename Sel, typename Key>
+template <int NT, bool BF16, bool VEC, int K, typename Sel, typename Key>
 __device__ __forceinline__ uint32_t radix_select(const RowView& rv, int64_t V, uint32_t need, Sel sel,
                                                  Key key, ExactShared<NT>& sh, uint32_t* tie_rem,
                                                  uint32_t* tie_cnt) {
@@ -67,7 +71,7 @@ __device__ __forceinline__ uint32_t radix_select(const RowView& rv, int64_t V, u
     if (threadIdx.x < 256) sh.hist[threadIdx.x] = 0ull;
     __syncthreads();
     uint32_t nonfin = 0;
-    for_row4<NT, BF16, VEC>(rv, V, nonfin, [&](const float* x, int64_t t0) {
+    for_row4<NT, BF16, VEC, K>(rv, V, nonfin, [&](const float* x, int64_t t0) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
         if (!sel(x[q], t0 + q)) continue;
@@ -89,10 +93,134 @@ __device__ __forceinline__ uint32_t radix_select(const RowView& rv, int64_t V, u
   return prefix;
 }
 
+// One pass: max z (lowest index on ties), finite count, non-finite flag and
+// sum over finite tokens of exp((z - zm) * invT), the last kept per thread
+// against the thread's running maximum (rescaled when it grows) and brought
+// to the row maximum in fp64 at the end.  Also returns the thread's maximum.
+struct RowLse {
+  float zm;
+  int32_t am;
+  int32_t nf;
+  uint32_t nonfin;
+  double se;
+  float tmax;
+};
+
+template <int NT, bool BF16, bool VEC, int K>
+__device__ __forceinline__ RowLse row_stats_lse(const RowView& rv, int64_t V, float invT32,
+                                                ExactShared<NT>& sh) {
+  uint32_t nonfin = 0;
+  float mt = CDS_NEG_INF;
+  int32_t am = INT_MAX;
+  int32_t nf = 0;
+  double st = 0.0;
+  const float c = invT32 * kLog2e;
+  for_row4<NT, BF16, VEC, K>(rv, V, nonfin, [&](const float* x, int64_t t0) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float v = x[q];
+      if (!finite_f(v)) continue;
+      ++nf;
+      if (v > mt) {  // exp2(-inf) = 0 on the first one
+        st = st * (double)exp2f((mt - v) * c) + 1.0;
+        mt = v;
+        am = (int32_t)(t0 + q);
+      } else {
+        st += (double)exp2f((v - mt) * c);
+      }
+    }
+  });
+  RowLse r;
+  r.tmax = mt;
+  float zm = mt;
+  int32_t a = am;
+  block_argmax<NT>(zm, a, sh.red);
+  r.zm = zm;
+  r.am = a;
+  r.nf = block_sum_i32<NT>(nf, sh.red);
+  r.nonfin = block_or_u32<NT>(nonfin, sh.red);
+  const double part = mt > CDS_NEG_INF ? st * exp(((double)mt - (double)zm) * (double)invT32) : 0.0;
+  r.se = block_sum_f64<NT>(part, sh.red);
+  return r;
+}
+
+// With the kept-set threshold given: one pass for the row's max, finite
+// count, non-finite flag, and the size and mass (sum of exp((z - zm) * invT))
+// of {allowed z >= cut}, the mass kept per thread against the thread's
+// running maximum and brought to the row maximum in fp64 at the end.
+struct CutStats {
+  float zm;
+  int32_t nf;
+  uint32_t nonfin;
+  int32_t cnt;
+  double mass;
+};
+
+template <int NT, bool BF16, bool VEC, int K>
+__device__ __forceinline__ CutStats row_stats_cut(const RowView& rv, int64_t V, float cut,
+                                                  float invT32, ExactShared<NT>& sh) {
+  uint32_t nonfin = 0;
+  float mt = CDS_NEG_INF;
+  int32_t nf = 0, cnt = 0;
+  double st = 0.0;
+  const float c = invT32 * kLog2e;
+  for_row4<NT, BF16, VEC, K>(rv, V, nonfin, [&](const float* x, int64_t) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float v = x[q];
+      if (!finite_f(v)) continue;
+      ++nf;
+      const bool kept = v >= cut;
+      cnt += kept ? 1 : 0;
+      if (v > mt) {  // exp2(-inf) = 0 on the first one
+        st = st * (double)exp2f((mt - v) * c) + (kept ? 1.0 : 0.0);
+        mt = v;
+      } else if (kept) {
+        st += (double)exp2f((v - mt) * c);
+      }
+    }
+  });
+  CutStats r;
+  r.zm = block_max_f32<NT>(mt, sh.red);
+  r.nf = block_sum_i32<NT>(nf, sh.red);
+  r.nonfin = block_or_u32<NT>(nonfin, sh.red);
+  r.cnt = block_sum_i32<NT>(cnt, sh.red);
+  const double part = mt > CDS_NEG_INF ? st * exp(((double)mt - (double)r.zm) * (double)invT32) : 0.0;
+  r.mass = block_sum_f64<NT>(part, sh.red);
+  return r;
+}
+
+// Sort the first n entries of sh.cand in descending order (bitonic network
+// over the next power of two, padded with zeros, which sort last).
+template <int NT>
+__device__ __forceinline__ void sort_desc(unsigned long long* cand, int n) {
+  int P = 1;
+  while (P < n) P <<= 1;
+  for (int i = n + (int)threadIdx.x; i < P; i += NT) cand[i] = 0ull;
+  __syncthreads();
+  for (int k = 2; k <= P; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = threadIdx.x; i < P; i += NT) {
+        const int l = i ^ j;
+        if (l > i) {
+          const unsigned long long x = cand[i], y = cand[l];
+          // descending runs where (i & k) == 0, ascending elsewhere
+          if (((i & k) == 0) ? (x < y) : (x > y)) {
+            cand[i] = y;
+            cand[l] = x;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
 // ---- row blocks: chosen-token, named-token and top-N logprobs ----------------
 template <int NT, bool BF16, bool VEC>
 __device__ __forceinline__ void row_outputs(const SampleArgs& a, const OutputArgs& o, int r,
                                             OutShared<NT>& sh) {
+  constexpr int K = kOutK;
   const int64_t V = a.V;
   const int ncol = o.top_ids ? o.top_n_max : 0;
   int n_top = ncol;
@@ -110,18 +238,17 @@ __device__ __forceinline__ void row_outputs(const SampleArgs& a, const OutputArg
 
   const RowParams rp = a.rows[r];
   const RowView rv = row_view<BF16>(a, r);
-  const RowStats st = row_stats<NT, BF16, VEC>(rv, V, sh.ex);
-  const int status = st.nf == 0 ? 2 : (st.nonfin ? 1 : 0);
   const bool greedy = (rp.flags & ROW_GREEDY) != 0;
   // the basis: the row's sampling distribution (greedy rows: the logits
   // before the temperature, as for the drawn token's logprob), or the logits
   // before the temperature for every row
   const double Tb = (o.basis == 1 || greedy) ? 1.0 : (double)rp.temperature;
+  const RowLse st = row_stats_lse<NT, BF16, VEC, K>(rv, V, (float)(1.0 / Tb), sh.ex);
+  const int status = st.nf == 0 ? 2 : (st.nonfin ? 1 : 0);
   double mb = 0.0, lz = 0.0;
   if (status == 0) {
-    const double se = row_expsum<NT, BF16, VEC>(rv, V, st.zm, (float)(1.0 / Tb), sh.ex);
     mb = (double)st.zm / Tb;
-    lz = log(se);
+    lz = log(st.se);
   }
   const float qnan = __builtin_nanf("");
   auto lp_of = [&](float z) -> float {
@@ -147,56 +274,70 @@ __device__ __forceinline__ void row_outputs(const SampleArgs& a, const OutputArg
   int n = 0;  // real entries
   if (status == 0) {
     n = min(n_top, st.nf);
-    // the n largest values, the lower id first among equal values: the
-    // token set {key > kthr} + {key == kthr, ~id >= ithr}
-    uint32_t kthr = 0u, ithr = 0u;
-    auto fin = [](float x, int64_t) { return finite_f(x); };
+    // Candidates: every finite z >= tau, where tau is the n-th largest of the
+    // threads' maxima (those n maxima are distinct tokens, so at least n
+    // tokens reach tau, and every one of the n largest does).
+    float tau = CDS_NEG_INF;
     if (n < st.nf) {
-      uint32_t rem, cnt;
-      kthr = radix_select<NT, BF16, VEC>(
-          rv, V, (uint32_t)n, fin, [](float x, int64_t) { return okey(x + 0.0f); }, sh.ex, &rem,
-          &cnt);
-      if (cnt > rem) {
-        uint32_t rem2, cnt2;
-        const uint32_t kt = kthr;
-        ithr = radix_select<NT, BF16, VEC>(
-            rv, V, rem, [&](float x, int64_t) { return finite_f(x) && okey(x + 0.0f) == kt; },
-            [](float, int64_t t) { return ~(uint32_t)t; }, sh.ex, &rem2, &cnt2);
-      }
+      sh.tmax[threadIdx.x] = st.tmax;
+      __syncthreads();
+      int c = 0;
+      for (int j = 0; j < NT; ++j) c += sh.tmax[j] >= st.tmax ? 1 : 0;
+      tau = block_max_f32<NT>(st.tmax > CDS_NEG_INF && c >= n ? st.tmax : CDS_NEG_INF, sh.ex.red);
     }
     if (threadIdx.x == 0) sh.cnt = 0u;
     __syncthreads();
     uint32_t nonfin = 0;
-    const uint32_t kt = kthr, it = ithr;
-    const bool all = n == st.nf;
-    for_row4<NT, BF16, VEC>(rv, V, nonfin, [&](const float* x, int64_t t0) {
+    const float tf = tau;
+    for_row4<NT, BF16, VEC, K>(rv, V, nonfin, [&](const float* x, int64_t t0) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if (!finite_f(x[q])) continue;
-        const uint32_t u = okey(x[q] + 0.0f);
-        const uint32_t iu = ~(uint32_t)(t0 + q);
-        if (all || u > kt || (u == kt && iu >= it)) {
-          const uint32_t slot = atomicAdd(&sh.cnt, 1u);
-          if (slot < (uint32_t)kMaxTopN) {
-            sh.key[slot] = u;
-            sh.id[slot] = (int32_t)(t0 + q);
-          }
-        }
+        if (!finite_f(x[q]) || x[q] < tf) continue;
+        const uint32_t slot = atomicAdd(&sh.cnt, 1u);
+        if (slot < (uint32_t)kCandCap)
+          sh.cand[slot] = ((unsigned long long)okey(x[q] + 0.0f) << 32) | (uint32_t)~(uint32_t)(t0 + q);
       }
     });
     __syncthreads();
-    n = min(n, (int)min(sh.cnt, (uint32_t)kMaxTopN));
-    // rank sort: larger key first, lower id first among equal keys
-    for (int i = threadIdx.x; i < n; i += NT) {
-      const uint32_t ki = sh.key[i];
-      const int32_t ti = sh.id[i];
-      int rank = 0;
-      for (int j = 0; j < n; ++j) {
-        const uint32_t kj = sh.key[j];
-        rank += (kj > ki || (kj == ki && sh.id[j] < ti)) ? 1 : 0;
+    int nc = (int)sh.cnt;
+    if (nc > kCandCap) {
+      // too many candidates (values concentrated in few threads): exact radix
+      // select of the n-th largest key, then of the id among its ties; the
+      // token set {key > kthr} + {key == kthr, ~id >= ithr} has n members
+      uint32_t rem, cnt;
+      const uint32_t kthr = radix_select<NT, BF16, VEC, K>(
+          rv, V, (uint32_t)n, [](float x, int64_t) { return finite_f(x); },
+          [](float x, int64_t) { return okey(x + 0.0f); }, sh.ex, &rem, &cnt);
+      uint32_t ithr = 0u;
+      if (cnt > rem) {
+        uint32_t rem2, cnt2;
+        ithr = radix_select<NT, BF16, VEC, K>(
+            rv, V, rem, [&](float x, int64_t) { return finite_f(x) && okey(x + 0.0f) == kthr; },
+            [](float, int64_t t) { return ~(uint32_t)t; }, sh.ex, &rem2, &cnt2);
       }
-      top_ids[rank] = ti;
-      top_vals[rank] = lp_of(from_okey(ki));
+      if (threadIdx.x == 0) sh.cnt = 0u;
+      __syncthreads();
+      for_row4<NT, BF16, VEC, K>(rv, V, nonfin, [&](const float* x, int64_t t0) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (!finite_f(x[q])) continue;
+          const uint32_t u = okey(x[q] + 0.0f);
+          const uint32_t iu = ~(uint32_t)(t0 + q);
+          if (u > kthr || (u == kthr && iu >= ithr)) {
+            const uint32_t slot = atomicAdd(&sh.cnt, 1u);
+            if (slot < (uint32_t)kCandCap) sh.cand[slot] = ((unsigned long long)u << 32) | iu;
+          }
+        }
+      });
+      __syncthreads();
+      nc = min((int)sh.cnt, kCandCap);
+    }
+    sort_desc<NT>(sh.cand, nc);
+    n = min(n, nc);
+    for (int i = threadIdx.x; i < n; i += NT) {
+      const unsigned long long e = sh.cand[i];
+      top_ids[i] = (int32_t)~(uint32_t)e;
+      top_vals[i] = lp_of(from_okey((uint32_t)(e >> 32)));
     }
   }
   const float pad = status == 1 ? qnan : CDS_NEG_INF;
@@ -229,39 +370,59 @@ __device__ __forceinline__ void support_outputs(const SampleArgs& a, const Outpu
   }
   const RowParams rp = a.rows[r];
   const RowView rv = row_view<BF16>(a, r);
-  const RowStats st = row_stats<NT, BF16, VEC>(rv, V, sh.ex);
-  if (st.nf == 0 || st.nonfin) {  // no distribution
-    finish(0, 2, qnan);
-    return;
-  }
-  const int64_t tsel = o.sel_ids ? (int64_t)o.sel_ids[r] : -1;
-  const bool has_sel = o.sel_ids && tsel >= 0 && tsel < V;
-  if (rp.flags & ROW_GREEDY) {  // the argmax alone
-    if (threadIdx.x == 0 && cap > 0) {
-      if (ids_out) ids_out[0] = st.am;
-      if (lp_out) lp_out[0] = 0.0f;
-    }
-    finish(min(1, cap), cap >= 1 ? 0 : 1, !has_sel ? qnan : (tsel == st.am ? 0.0f : CDS_NEG_INF));
-    return;
-  }
-  const float zm = st.zm;
-  const float zcut = row_cut<NT, BF16, VEC>(rv, V, rp, zm, st.nf, sh.ex);
+  constexpr int K = kOutK;
+  const bool greedy = (rp.flags & ROW_GREEDY) != 0;
   const double Td = (double)rp.temperature;
   const float invT32 = (float)(1.0 / Td);
-  // size and mass of {allowed z >= zcut}
-  int32_t cnt = 0;
-  double mass = 0.0;
-  uint32_t nonfin = 0;
-  for_row4<NT, BF16, VEC>(rv, V, nonfin, [&](const float* x, int64_t) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      if (x[q] != CDS_NEG_INF && x[q] >= zcut) {
-        ++cnt;
-        mass += (double)exp2f((x[q] - zm) * invT32 * kLog2e);
+  const int64_t tsel = o.sel_ids ? (int64_t)o.sel_ids[r] : -1;
+  const bool has_sel = o.sel_ids && tsel >= 0 && tsel < V;
+  float zm, zcut;
+  int32_t cnt;
+  double mass;
+  if (o.cuts && !greedy) {
+    // the sampling call's threshold: one pass for the row's status and the
+    // size and mass of {allowed z >= cut}
+    zcut = o.cuts[r];
+    const CutStats cs = row_stats_cut<NT, BF16, VEC, K>(rv, V, zcut, invT32, sh.ex);
+    if (cs.nf == 0 || cs.nonfin) {  // no distribution
+      finish(0, 2, qnan);
+      return;
+    }
+    zm = cs.zm;
+    cnt = cs.cnt;
+    mass = cs.mass;
+  } else {
+    const RowStats st = row_stats<NT, BF16, VEC, K>(rv, V, sh.ex);
+    if (st.nf == 0 || st.nonfin) {  // no distribution
+      finish(0, 2, qnan);
+      return;
+    }
+    if (greedy) {  // the argmax alone
+      if (threadIdx.x == 0 && cap > 0) {
+        if (ids_out) ids_out[0] = st.am;
+        if (lp_out) lp_out[0] = 0.0f;
       }
-  });
-  cnt = block_sum_i32<NT>(cnt, sh.ex.red);
-  mass = block_sum_f64<NT>(mass, sh.ex.red);
+      finish(min(1, cap), cap >= 1 ? 0 : 1, !has_sel ? qnan : (tsel == st.am ? 0.0f : CDS_NEG_INF));
+      return;
+    }
+    zm = st.zm;
+    zcut = row_cut<NT, BF16, VEC, K>(rv, V, rp, zm, st.nf, sh.ex);
+    // size and mass of {allowed z >= zcut}
+    cnt = 0;
+    mass = 0.0;
+    uint32_t nonfin = 0;
+    const float zc = zcut, zmax = zm;
+    for_row4<NT, BF16, VEC, K>(rv, V, nonfin, [&](const float* x, int64_t) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (x[q] != CDS_NEG_INF && x[q] >= zc) {
+          ++cnt;
+          mass += (double)exp2f((x[q] - zmax) * invT32 * kLog2e);
+        }
+    });
+    cnt = block_sum_i32<NT>(cnt, sh.ex.red);
+    mass = block_sum_f64<NT>(mass, sh.ex.red);
+  }
   const double m = (double)zm / Td;
   const double lmass = log(mass);
   auto lp_s = [&](float z) -> float { return (float)((double)z / Td - m - lmass); };
@@ -270,12 +431,13 @@ __device__ __forceinline__ void support_outputs(const SampleArgs& a, const Outpu
   // members after those of lower ids
   if (cap > 0 && ids_out) {
     uint32_t written = 0u;
-    for (int g = 0; (int64_t)g * 4 * NT < V && written < (uint32_t)cap; g += 4) {
-      float x[4][4];
+    constexpr int KW = 8;
+    for (int g = 0; (int64_t)g * 4 * NT < V && written < (uint32_t)cap; g += KW) {
+      float x[KW][4];
       uint32_t nf2 = 0;
-      load_chunks<NT, 4, BF16, VEC>(rv, 0, V, g, x, nf2);
+      load_chunks<NT, KW, BF16, VEC>(rv, 0, V, g, x, nf2);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = 0; i < KW; ++i) {
         const int64_t t0 = 4 * ((int64_t)(g + i) * NT + threadIdx.x);
         uint32_t c = 0u;
 #pragma unroll

@@ -583,6 +583,7 @@ int sampler_sample_ex(const sampler_batch* b, const void* logits, int dtype, int
   a.out_ids = out_ids;
   a.out_lp = out_logprobs;
   a.out_st = out_status;
+  a.out_cut = static_cast<float*>(o.cut);
   a.sync = reinterpret_cast<RowSync*>(ws + L.sync_off);
   a.plans = reinterpret_cast<Plan*>(ws + L.plan_off);
   a.heads = reinterpret_cast<SliceHead*>(ws + L.head_off);
@@ -700,6 +701,7 @@ int sampler_logprobs(const sampler_batch* b, const void* logits, int dtype, int6
   o.tok_off = req->token_indptr;
   o.tok_ids = req->token_ids;
   o.sel_ids = req->selected;
+  o.cuts = req->cuts;
   o.sup_rows = mask ? req->mask_rows : nullptr;
   o.n_sup = mask ? req->n_mask_rows : 0;
   o.sup_cap = req->mask_cap;

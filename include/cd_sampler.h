@@ -342,6 +342,11 @@ int sampler_sample_static(const sampler_batch *b, const void *logits, int dtype,
  *               the wait for it), and at the end.
  *   start_event, stop_event  hipEvent_t (as void*) or NULL: recorded on the
  *               call's stream right before and after the sampling kernel.
+ *   cut         dev float [B] or NULL: for each sampled row with status OK the
+ *               value threshold of the set its token was drawn from (that
+ *               set is {allowed z >= cut}); other rows are not written.
+ *               sampler_logprobs takes it to return support sets without
+ *               selecting the cut again.
  * -------------------------------------------------------------------------- */
 #define SAMPLER_ALGO_FAST 0
 #define SAMPLER_ALGO_EXACT 1
@@ -353,6 +358,7 @@ typedef struct sampler_options {
   void *trace;
   void *start_event;
   void *stop_event;
+  void *cut;
 } sampler_options;
 
 int sampler_sample_ex(const sampler_batch *b, const void *logits, int dtype,
@@ -388,6 +394,10 @@ int sampler_sample_ex(const sampler_batch *b, const void *logits, int dtype,
  *                   [0, top_n_max]; NULL: top_n_max for every row.
  *   token_indptr    int64 [B+1], token_ids int32: the named tokens per row
  *                   (token_ids_logprobs, CSR).
+ *   cuts            float [B]: the thresholds sampler_sample_ex returned
+ *                   (option `cut`) for the same batch and logits: support
+ *                   sets then take two passes over their row; NULL: the
+ *                   threshold is selected again (several more passes).
  *   mask_rows       int32 [n_mask_rows]: the rows that return their support
  *                   set (sampling_mask_batch_indices); a row may appear more
  *                   than once; an index outside [0, B) gives status INVALID.
@@ -445,6 +455,7 @@ typedef struct sampler_logprob_request {
   const int32_t *mask_rows;
   int32_t mask_cap;
   int32_t pad_;
+  const float *cuts;
 } sampler_logprob_request;
 
 typedef struct sampler_logprob_outputs {

@@ -44,9 +44,11 @@ def _close(a, b, tol=LP_TOL):
     return bool(ok.all()), np.flatnonzero(~ok)
 
 
-def _run(batch, *, basis, top_n, tok_rows, mask_rows, cap, with_selected=True):
+def _run(batch, *, basis, top_n, tok_rows, mask_rows, cap, with_selected=True, use_cuts=True):
     """Pack, transform, sample (fused mask), then sampler_logprobs; returns
-    (ids, status, dict of host arrays)."""
+    (ids, status, logprobs, dict of host arrays).  use_cuts: the support sets
+    take the sampling call's kept-set thresholds (else they select them
+    again)."""
     import torch
     import constrained_decoding_amd as cds
     x = to_device(batch)
@@ -58,7 +60,8 @@ def _run(batch, *, basis, top_n, tok_rows, mask_rows, cap, with_selected=True):
         mask = torch.from_numpy(batch.masks).cuda()
         rhm = None if batch.row_has_mask is None else \
             torch.from_numpy(batch.row_has_mask.astype(np.uint8)).cuda()
-    ids, lp, st = cds.sample(pk, x, bitmask=mask, row_has_mask=rhm)
+    cut = torch.full((batch.B,), float("nan"), dtype=torch.float32, device="cuda")
+    ids, lp, st = cds.sample(pk, x, bitmask=mask, row_has_mask=rhm, cut=cut)
     indptr, flat = cds.csr(tok_rows)
     top_n_max = int(max(top_n)) if len(top_n) else 0
     res = cds.logprobs(
@@ -67,7 +70,7 @@ def _run(batch, *, basis, top_n, tok_rows, mask_rows, cap, with_selected=True):
         token_indptr=torch.from_numpy(indptr).cuda(),
         token_ids=torch.from_numpy(flat.astype(np.int32)).cuda(),
         mask_rows=torch.from_numpy(np.asarray(mask_rows, np.int32)).cuda() if len(mask_rows) else None,
-        mask_cap=cap, bitmask=mask, row_has_mask=rhm)
+        mask_cap=cap, cuts=cut if use_cuts else None, bitmask=mask, row_has_mask=rhm)
     torch.cuda.synchronize()
     host = {k: v.cpu().numpy() for k, v in res.items()}
     return ids.cpu().numpy(), st.cpu().numpy(), lp.cpu().numpy(), host
@@ -176,11 +179,12 @@ def _oracle_member(batch, zs, r):
     return (sets & 4) > 0
 
 
-def _case(batch, *, basis, top_n, tok_rows, mask_rows, cap, with_selected=True, label=""):
+def _case(batch, *, basis, top_n, tok_rows, mask_rows, cap, with_selected=True, use_cuts=True,
+          label=""):
     print(f"[case] {label} B={batch.B} V={batch.V} bf16={batch.bf16} basis={basis} "
-          f"cap={cap} selected={with_selected}", flush=True)
+          f"cap={cap} selected={with_selected} cuts={use_cuts}", flush=True)
     gpu = _run(batch, basis=basis, top_n=top_n, tok_rows=tok_rows, mask_rows=mask_rows, cap=cap,
-               with_selected=with_selected)
+               with_selected=with_selected, use_cuts=use_cuts)
     ids = gpu[0]
     _, zs = run_oracle(batch)
     want = np.zeros(batch.B, bool)
@@ -242,9 +246,11 @@ def test_outputs_small_parity(V, bf16):
     batch = _mixed_batch(rng, B, V, bf16=bf16)
     top_n, tok_rows = _requests(rng, B, V)
     mask_rows = list(range(B)) + [B, -3, 5]
-    for basis in (oracle.BASIS_SAMPLED, oracle.BASIS_ORIGINAL):
+    # support sets from the sampling call's thresholds, and selected again
+    for basis, cuts in ((oracle.BASIS_SAMPLED, True), (oracle.BASIS_ORIGINAL, False)):
         _case(batch, basis=basis, top_n=top_n, tok_rows=tok_rows, mask_rows=mask_rows,
-              cap=V if basis == oracle.BASIS_SAMPLED else 64, label=f"small V={V} bf16={bf16}")
+              cap=V if basis == oracle.BASIS_SAMPLED else 64, use_cuts=cuts,
+              label=f"small V={V} bf16={bf16}")
 
 
 def test_outputs_scoring_without_draw():
@@ -255,7 +261,8 @@ def test_outputs_scoring_without_draw():
     batch = _mixed_batch(rng, B, V)
     top_n, tok_rows = _requests(rng, B, V, n_max=256)
     gpu, refs = _case(batch, basis=oracle.BASIS_SAMPLED, top_n=top_n, tok_rows=tok_rows,
-                      mask_rows=list(range(B)), cap=300, with_selected=False, label="scoring")
+                      mask_rows=list(range(B)), cap=300, with_selected=False, use_cuts=False,
+                      label="scoring")
     assert "next" not in gpu[3]
     ok = gpu[3]["mask_status"] == oracle.STATUS_INVALID
     assert np.all(np.isnan(gpu[3]["mask_sel"][~ok]))
@@ -286,6 +293,10 @@ def test_outputs_full_size(cfg):
     mask_rows = list(range(0, B, 12))
     _case(batch, basis=oracle.BASIS_SAMPLED, top_n=top_n, tok_rows=tok_rows, mask_rows=mask_rows,
           cap=40000, label=f"full {cfg}")
+    # the same support sets with the thresholds selected again
+    _case(batch, basis=oracle.BASIS_SAMPLED, top_n=np.zeros(B, np.int32),
+          tok_rows=[np.zeros(0, np.int64)] * B, mask_rows=mask_rows, cap=40000, use_cuts=False,
+          label=f"full {cfg} reselected")
 
 
 def test_outputs_original_basis_full_size():
@@ -295,3 +306,27 @@ def test_outputs_original_basis_full_size():
     B = batch.B
     _case(batch, basis=oracle.BASIS_ORIGINAL, top_n=np.full(B, 5, np.int32),
           tok_rows=[np.zeros(0, np.int64)] * B, mask_rows=[], cap=0, label="original basis")
+
+
+def test_outputs_top_n_candidate_overflow_and_ties():
+    """Rows whose candidate list (tokens at or above the N-th largest
+    thread maximum) overflows LDS: all-equal values, two values, and the
+    large values packed into a few threads; top-N then takes the exact radix
+    select with the id tie-break.  V = 151936, N up to 256."""
+    rng = np.random.default_rng(714)
+    B, V = 8, 151936
+    z = (rng.standard_normal((B, V)) * 2.0).astype(np.float32)
+    z[0, :] = 0.25                                   # all equal
+    z[1, :] = np.where(rng.random(V) < 0.5, 1.0, 2.0).astype(np.float32)
+    idx = np.arange(V)
+    z[2, (idx % 2048) < 4] += 30.0                   # every large value in thread 0's groups
+    z[3, :] = np.round(z[3] * 4) / 4                 # many ties
+    z[4, :] = np.float32(-3.0)
+    z[4, rng.choice(V, 300, replace=False)] = 5.0     # 300 tied maxima
+    T = np.array([0.7, 1.0, 0.5, 0.9, 1.2, 0.0, 0.8, 1.0], np.float32)
+    batch = workloads.Batch("ties", z, False, T, np.zeros(B, np.int32),
+                            np.full(B, 0.9, np.float32), np.zeros(B, np.float32),
+                            workloads.seeds(rng, B), np.arange(B, dtype=np.uint64))
+    top_n = np.array([256, 256, 40, 256, 256, 20, 1, 256], np.int32)
+    _case(batch, basis=oracle.BASIS_SAMPLED, top_n=top_n, tok_rows=[np.array([0, 5])] * B,
+          mask_rows=[0, 1, 4], cap=V, label="candidate overflow")
