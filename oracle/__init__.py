@@ -82,6 +82,9 @@ def _load():
     lib.cdo_set_log_softmax.restype = _ct.c_int64
     lib.cdo_top_n.argtypes = [P, P, _ct.c_int32, _ct.c_int32, P, P]
     lib.cdo_top_n.restype = _ct.c_int32
+    lib.cdo_race_best.argtypes = [P, _ct.c_int32, _ct.c_float, _ct.c_double, _ct.c_uint64,
+                                  _ct.c_uint64, _ct.c_int32, _ct.c_int32, P, _ct.c_uint8, P]
+    lib.cdo_race_best.restype = _ct.c_int32
     _lib = lib
     return lib
 
@@ -338,3 +341,16 @@ def row_outputs(z, *, T, top_k=0, top_p=1.0, min_p=0.0, seed=0, offset=0,
         out.update(sup_ids=ids.astype(_np.int32), sup_vals=vals, sup_n=n_sup,
                    sup_len=int(ids.shape[0]), sup_status=sst, sup_sel=ssel)
     return out
+
+
+# ------------------------------------------------------------ vocabulary shards
+
+def race_best(z, in_set, *, T, m, seed, offset, v0, width, bit=4):
+    """The race over the set's tokens in [v0, v0 + width), global ids: returns
+    (token or -1, key)."""
+    zz = _np.ascontiguousarray(z, dtype=_np.float32)
+    st = _np.ascontiguousarray(in_set, _np.uint8)
+    key = _np.zeros(1, _np.float64)
+    t = _load().cdo_race_best(_ptr(zz), zz.shape[0], float(T), float(m), int(seed), int(offset),
+                              int(v0), int(width), _ptr(st), int(bit), _ptr(key))
+    return int(t), float(key[0])

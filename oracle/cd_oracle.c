@@ -548,3 +548,31 @@ int32_t cdo_top_n(const float *z, const double *lp, int32_t V, int32_t N,
   free(ent);
   return k;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Vocabulary shards [GLM, "输出侧的通信与开销账本": sampling after a gather of */
+/* per-shard results instead of the full logits; "从最后一层 hidden 到 token  */
+/* id": the LM head's output is split along the vocabulary under TP].  The  */
+/* race key of token t depends only on (seed, offset, t) and s_t - m, so the */
+/* row's winner is the best of the shards' winners when every shard uses   */
+/* global token ids.                                                         */
+/* ------------------------------------------------------------------------ */
+int32_t cdo_race_best(const float *z, int32_t V, float T, double m,
+                      uint64_t seed, uint64_t offset, int32_t v0,
+                      int32_t width, const uint8_t *set, uint8_t bit,
+                      double *best_key) {
+  const double Td = (double)T;
+  double best = -INFINITY;
+  int32_t best_t = -1;
+  for (int32_t t = v0; t < v0 + width && t < V; ++t) {
+    if (!(set[t] & bit)) continue;
+    const double u = cdo_uniform24(cdo_race_bits(seed, offset, t));
+    const double key = ((double)z[t] / Td - m) - log(-log(u));
+    if (key > best) { /* strict: the lowest id wins an exact tie */
+      best = key;
+      best_t = t;
+    }
+  }
+  *best_key = best;
+  return best_t;
+}

@@ -145,6 +145,18 @@ int64_t cdo_set_log_softmax(const float *z, int32_t V, double T,
 int32_t cdo_top_n(const float *z, const double *lp, int32_t V, int32_t N,
                   int32_t *ids, double *vals);
 
+/* ---- vocabulary shards [GLM, "输出侧的通信与开销账本"] --------------------- */
+
+/* The race over the tokens of [v0, v0 + width) that are in a set
+ * ({t : set[t] & bit}), with global token ids: the largest key
+ * (z_t/T - m) - ln(-ln U_t) (U_t as in cdo_race_bits / cdo_uniform24), the
+ * lowest id on an exact tie.  Returns its token (-1 if none) and sets
+ * *best_key (-inf if none).  z and set are the whole row (V entries). */
+int32_t cdo_race_best(const float *z, int32_t V, float T, double m,
+                      uint64_t seed, uint64_t offset, int32_t v0,
+                      int32_t width, const uint8_t *set, uint8_t bit,
+                      double *best_key);
+
 #ifdef __cplusplus
 }
 #endif
