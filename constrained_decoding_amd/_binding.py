@@ -25,12 +25,15 @@ ORDER_MINP_FIRST, ORDER_JOINT, ORDER_MINP_LAST = 0, 1, 2
 WAIT_NONE = -1
 LOGPROB_SAMPLED, LOGPROB_ORIGINAL = 0, 1
 MAX_TOP_N = 256
+SHARD_PHASES = 11
 
 EXPORTS = [
     "sampler_strerror", "sampler_version", "sampler_params_bytes", "sampler_pack_params",
     "sampler_pack_host", "sampler_apply_transforms", "sampler_apply_bitmask",
     "sampler_workspace_bytes", "sampler_workspace_bytes_batch", "sampler_workspace_init",
     "sampler_sample", "sampler_sample_ex", "sampler_sample_static", "sampler_logprobs",
+    "sampler_shard_state_bytes", "sampler_shard_partial_bytes", "sampler_shard_phases",
+    "sampler_shard_pass", "sampler_shard_merge",
 ]
 
 
@@ -113,6 +116,11 @@ def _load():
         "sampler_sample_ex": ([P, P, ct.c_int, I64, P, I64, P, P, P, P, P, SZ, P, P], ct.c_int),
         "sampler_sample_static": ([P, P, ct.c_int, I64, P, I64, P, P, P, P, P], ct.c_int),
         "sampler_logprobs": ([P, P, ct.c_int, I64, P, I64, P, P, P, P], ct.c_int),
+        "sampler_shard_state_bytes": ([I32], SZ),
+        "sampler_shard_partial_bytes": ([I32], SZ),
+        "sampler_shard_phases": ([P], ct.c_uint32),
+        "sampler_shard_pass": ([P, I32, P, ct.c_int, I64, I32, I32, P, I64, P, P, P, P], ct.c_int),
+        "sampler_shard_merge": ([P, I32, P, P, I32, P, P, P, P], ct.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -432,3 +440,62 @@ def logprobs(packed: PackedBatch, logits, *, selected=None, basis=LOGPROB_SAMPLE
     if "token" not in res and n_tok == 0 and token_indptr is None:
         res["token"] = torch.empty(0, dtype=torch.float32, device=dev)
     return res
+
+
+def _aligned_buffer(nbytes, device, align=256):
+    import torch
+    buf = torch.empty(nbytes + align, dtype=torch.uint8, device=device)
+    return buf, buf.data_ptr() + (-buf.data_ptr()) % align
+
+
+class ShardBuffers:
+    """The per-rank state and the partial records of n_parts shards (the
+    records side by side, as an all-gather delivers them)."""
+
+    def __init__(self, B, n_parts, *, device="cuda"):
+        self.state_bytes = int(lib.sampler_shard_state_bytes(B))
+        self.part_bytes = int(lib.sampler_shard_partial_bytes(B))
+        if not self.state_bytes or not self.part_bytes:
+            raise SamplerError(ERANGE, "sampler_shard_state_bytes")
+        self._s, self.state = _aligned_buffer(self.state_bytes, device)
+        self._p, self.parts = _aligned_buffer(self.part_bytes * n_parts, device)
+        self.B, self.n_parts = B, n_parts
+
+
+def shard_sample(packed: PackedBatch, shards, *, row_has_mask=None, buffers=None, out=None,
+                 stream=None):
+    """Vocabulary-parallel sampling with every shard on this device: the
+    phases sampler_shard_phases names, each a pass over every shard (writing
+    its slot of the partial records) and a merge.  ``shards``: list of
+    (logits [B, width] tensor, v0, bitmask [B, words] tensor or None) in any
+    order.  Returns (ids, logprobs, status) device tensors."""
+    import torch
+    B = packed.B
+    dev = shards[0][0].device
+    if buffers is None:
+        buffers = ShardBuffers(B, len(shards), device=dev)
+    if out is None:
+        ids = torch.empty(B, dtype=torch.int32, device=dev)
+        lp = torch.empty(B, dtype=torch.float32, device=dev)
+        st = torch.empty(B, dtype=torch.int32, device=dev)
+    else:
+        ids, lp, st = out
+    sp = _stream_ptr(stream)
+    br = ct.byref(packed.batch)
+    phases = int(lib.sampler_shard_phases(br))
+    rhm = None if row_has_mask is None else row_has_mask.data_ptr()
+    for ph in range(SHARD_PHASES):
+        if not (phases >> ph) & 1:
+            continue
+        for p, (x, v0, mask) in enumerate(shards):
+            if x.stride(1) != 1:
+                raise ValueError("shard logits must have unit column stride")
+            _check(lib.sampler_shard_pass(
+                br, ph, x.data_ptr(), _dtype_code(x), x.stride(0), int(v0), x.shape[1],
+                None if mask is None else mask.data_ptr(), 0 if mask is None else mask.stride(0),
+                rhm, buffers.state, buffers.parts + p * buffers.part_bytes, sp),
+                "sampler_shard_pass")
+        _check(lib.sampler_shard_merge(br, ph, buffers.state, buffers.parts, len(shards),
+                                       ids.data_ptr(), lp.data_ptr(), st.data_ptr(), sp),
+               "sampler_shard_merge")
+    return ids, lp, st

@@ -64,6 +64,74 @@ struct OutputArgs {
   int32_t* sup_st;        // [n_sup]
 };
 
+// ---- vocabulary-parallel protocol (shard.hip) ----------------------------------
+// Phases, run in order: the row statistics, four radix rounds of the top-k
+// threshold, the top-p mass sums, four radix rounds of the top-p threshold,
+// the race.  Each phase is a pass over every shard (partials) and a merge of
+// the shards' partials into the row state.
+enum ShardPhase : int32_t {
+  SHARD_STATS = 0,
+  SHARD_TOPK0 = 1,       // 1..4: digits at shifts 24, 16, 8, 0
+  SHARD_TOPP_SUMS = 5,
+  SHARD_TOPP0 = 6,       // 6..9
+  SHARD_RACE = 10,
+  SHARD_PHASES = 11,
+};
+
+// Per-row state of the protocol, written by the merges (device).
+struct alignas(16) ShardState {
+  float zm;               // row max z
+  int32_t am;             // its lowest global id
+  int32_t nf;             // finite allowed tokens
+  int32_t active;         // sampled row with status OK: later phases run
+  double m;               // zm / T
+  double log_z;           // log sum exp(s - m)
+  float zcut;             // kept-set threshold so far
+  float zk;               // top-k threshold (-inf: none)
+  uint32_t prefix, pmask; // radix select digits so far
+  unsigned long long krem; // top-k: tokens still to take at the current prefix
+  unsigned long long base; // top-p: mass above the current prefix
+  double need;            // top-p: the mass the cut must reach
+  int32_t topk_on, topp_on;
+};
+static_assert(sizeof(ShardState) == 80, "ShardState layout");
+
+// One shard's contribution to one phase, per row (device).
+struct alignas(16) ShardPartial {
+  float zm;             // stats: shard max, its lowest global id, finite
+  int32_t am;           // count, non-finite flag, exp-sum against the
+  int32_t nf;           // shard max
+  uint32_t nonfin;
+  double se;
+  unsigned long long s0, s1;  // top-p sums: kept mass, normalising mass
+  double key;           // race: best key, its global id and z
+  int32_t t;
+  float z;
+  unsigned long long hist[256];  // radix rounds: counts or fixed-point masses
+};
+static_assert(sizeof(ShardPartial) == 2112, "ShardPartial layout");
+
+struct ShardArgs {
+  const RowParams* rows;
+  const void* logits;   // the shard: [B, ld], tokens v0 .. v0 + width - 1
+  int64_t ld;
+  int32_t B, V;         // V: the whole vocabulary
+  int32_t v0, width;
+  const int32_t* mask;  // the shard's bitmask words (bit j: token v0 + j), or nullptr
+  int64_t mask_ld;
+  const uint8_t* row_has_mask;
+  ShardState* state;
+  ShardPartial* part;   // pass: this shard's [B]; merge: [n_parts][B]
+  int32_t n_parts;
+  int32_t phase;
+  int32_t* out_ids;
+  float* out_lp;
+  int32_t* out_st;
+};
+
+hipError_t launch_shard_pass(const ShardArgs& a, bool bf16, bool vec, hipStream_t stream);
+hipError_t launch_shard_merge(const ShardArgs& a, hipStream_t stream);
+
 // Optional timing events recorded around the sampling kernel.
 struct KernelEvents {
   hipEvent_t start;

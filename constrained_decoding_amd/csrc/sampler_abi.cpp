@@ -723,4 +723,92 @@ int sampler_logprobs(const sampler_batch* b, const void* logits, int dtype, int6
   return e == hipSuccess ? SAMPLER_OK : SAMPLER_EHIP;
 }
 
+size_t sampler_shard_state_bytes(int32_t B) {
+  if (B <= 0 || B > kMaxB) return 0;
+  return sizeof(ShardState) * (size_t)B;
+}
+
+size_t sampler_shard_partial_bytes(int32_t B) {
+  if (B <= 0 || B > kMaxB) return 0;
+  return sizeof(ShardPartial) * (size_t)B;
+}
+
+uint32_t sampler_shard_phases(const sampler_batch* b) {
+  if (!b || b->B <= 0) return 0u;
+  uint32_t ph = 1u << SHARD_STATS;
+  if (b->flags & SAMPLER_FLAG_NEED_TOP_K)
+    for (int i = 0; i < 4; ++i) ph |= 1u << (SHARD_TOPK0 + i);
+  if (b->flags & SAMPLER_FLAG_NEED_TOP_P) {
+    ph |= 1u << SHARD_TOPP_SUMS;
+    for (int i = 0; i < 4; ++i) ph |= 1u << (SHARD_TOPP0 + i);
+  }
+  if (b->n_sampled > 0) ph |= 1u << SHARD_RACE;
+  return ph;
+}
+
+int sampler_shard_pass(const sampler_batch* b, int32_t phase, const void* logits, int dtype,
+                       int64_t ld, int32_t v0, int32_t width, const int32_t* bitmask,
+                       int64_t mask_ld, const uint8_t* row_has_mask, const void* state,
+                       void* partial, void* stream) {
+  if (!b || !logits || !b->d_rows || !partial) return SAMPLER_EINVAL;
+  const int32_t B = b->B, V = b->V;
+  if (B <= 0 || V <= 0) return SAMPLER_EINVAL;
+  if (B > kMaxB || V > kMaxV) return SAMPLER_ERANGE;
+  if (phase < 0 || phase >= SHARD_PHASES) return SAMPLER_EINVAL;
+  if (phase > SHARD_STATS && !state) return SAMPLER_EINVAL;
+  if (v0 < 0 || v0 % 4 != 0 || width <= 0 || (int64_t)v0 + width > V || ld < width)
+    return SAMPLER_EINVAL;
+  if (dtype != SAMPLER_DTYPE_F32 && dtype != SAMPLER_DTYPE_BF16) return SAMPLER_EINVAL;
+  const bool bf16 = dtype == SAMPLER_DTYPE_BF16;
+  if (!aligned(logits, bf16 ? 2 : 4)) return SAMPLER_EINVAL;
+  if (bitmask && mask_ld < ((int64_t)width + 31) / 32) return SAMPLER_EINVAL;
+  if (!aligned(partial, 16) || (state && !aligned(state, 16))) return SAMPLER_EINVAL;
+  ShardArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.rows = static_cast<const RowParams*>(b->d_rows);
+  a.logits = logits;
+  a.ld = ld;
+  a.B = B;
+  a.V = V;
+  a.v0 = v0;
+  a.width = width;
+  a.mask = bitmask;
+  a.mask_ld = mask_ld;
+  a.row_has_mask = row_has_mask;
+  a.state = static_cast<ShardState*>(const_cast<void*>(state));
+  a.part = static_cast<ShardPartial*>(partial);
+  a.n_parts = 1;
+  a.phase = phase;
+  const size_t elem = bf16 ? 2 : 4;
+  const bool vec = aligned(logits, 4 * elem) && (ld % 4 == 0) && (width % 4 == 0);
+  const hipError_t e = launch_shard_pass(a, bf16, vec, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SAMPLER_OK : SAMPLER_EHIP;
+}
+
+int sampler_shard_merge(const sampler_batch* b, int32_t phase, void* state, const void* partials,
+                        int32_t n_parts, int32_t* out_ids, float* out_logprobs,
+                        int32_t* out_status, void* stream) {
+  if (!b || !b->d_rows || !state || !partials || !out_ids) return SAMPLER_EINVAL;
+  const int32_t B = b->B, V = b->V;
+  if (B <= 0 || V <= 0) return SAMPLER_EINVAL;
+  if (B > kMaxB || V > kMaxV) return SAMPLER_ERANGE;
+  if (phase < 0 || phase >= SHARD_PHASES) return SAMPLER_EINVAL;
+  if (n_parts < 1 || n_parts > V / 4 + 1) return SAMPLER_EINVAL;
+  if (!aligned(state, 16) || !aligned(partials, 16)) return SAMPLER_EINVAL;
+  ShardArgs a;
+  std::memset(&a, 0, sizeof a);
+  a.rows = static_cast<const RowParams*>(b->d_rows);
+  a.B = B;
+  a.V = V;
+  a.state = static_cast<ShardState*>(state);
+  a.part = static_cast<ShardPartial*>(const_cast<void*>(partials));
+  a.n_parts = n_parts;
+  a.phase = phase;
+  a.out_ids = out_ids;
+  a.out_lp = out_logprobs;
+  a.out_st = out_status;
+  const hipError_t e = launch_shard_merge(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SAMPLER_OK : SAMPLER_EHIP;
+}
+
 }  // extern "C"

@@ -1,0 +1,361 @@
+// shard.hip -- one rank's share of vocabulary-parallel sampling, for gfx950.
+//
+// Under tensor parallelism the LM head's output is split along the
+// vocabulary: each rank holds [B, V/TP] logits ("GLM-5.3 推理全链路(七)",
+// section 从最后一层 hidden 到 token id: 输出边界在哪里).  Instead of
+// gathering the full logits before sampling, each rank works on its shard
+// and the ranks exchange per-row partial results (same page, section
+// 输出侧的通信与开销账本, sampling after a gather of per-shard candidates;
+// the grammar bitmask split by vocabulary shard, section 结构化输出).
+//
+// The protocol is the exact path's sequence of passes (exact_path.h), each
+// split over the shards:
+//   stats      shard max (lowest global id), finite count, non-finite flag,
+//              exp-sum against the shard max -> row max, status, normaliser,
+//              the min-p threshold;
+//   top-k      four radix rounds on the fp32 order key: per-shard 256-bin
+//              counts, summed -> the next digit;
+//   top-p      the kept and normalising fixed-point masses, then four radix
+//              rounds of fixed-point masses, summed -> the next digit;
+//   race       the shard's best race key over the kept set, with global token
+//              ids in the Philox counter -> the row's winner is the best of
+//              the shards' winners.
+// Every shard uses the row's global maximum and the same fixed-point scale,
+// so the sums are exact integers and the thresholds, hence the drawn ids, are
+// those of the exact path on the whole row.
+//
+// On several GPUs each rank runs the pass over its shard, the partials are
+// all-gathered, and every rank runs the same merge (so every rank holds the
+// same state).  On one GPU the passes of all shards write their slots of one
+// partials buffer and one merge follows.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+
+#include "device_common.h"
+#include "exact_path.h"
+#include "kernels.h"
+
+namespace cds {
+
+constexpr int kShardNT = 512;
+constexpr int kShardK = 8;
+constexpr int kMergeNT = 256;
+
+template <bool BF16>
+__device__ __forceinline__ RowView shard_view(const ShardArgs& a, int r) {
+  RowView v;
+  if (BF16) {
+    v.b16 = static_cast<const uint16_t*>(a.logits) + (int64_t)r * a.ld;
+    v.f32 = nullptr;
+  } else {
+    v.f32 = static_cast<const float*>(a.logits) + (int64_t)r * a.ld;
+    v.b16 = nullptr;
+  }
+  v.mrow = (a.mask && (!a.row_has_mask || a.row_has_mask[r])) ? a.mask + (int64_t)r * a.mask_ld
+                                                              : nullptr;
+  return v;
+}
+
+// fixed-point scale of the top-p masses: 2^(62 - ceil(log2 V)) for the whole
+// vocabulary, so that no sum over the row overflows
+__device__ __forceinline__ double mass_scale(int64_t V) {
+  int lg = 0;
+  while ((1ll << lg) < V) ++lg;
+  return ldexp(1.0, 62 - lg);
+}
+
+template <int NT, bool BF16, bool VEC>
+__global__ __launch_bounds__(NT) void shard_pass_kernel(const ShardArgs a) {
+  constexpr int K = kShardK;
+  __shared__ ExactShared<NT> sh;
+  const int r = blockIdx.x;
+  const RowParams rp = a.rows[r];
+  const RowView rv = shard_view<BF16>(a, r);
+  const int64_t W = a.width;
+  ShardPartial* P = a.part + r;
+  const int tid = threadIdx.x;
+  uint32_t nonfin = 0;
+
+  if (a.phase == SHARD_STATS) {
+    const bool greedy = (rp.flags & ROW_GREEDY) != 0;
+    const RowStats st = row_stats<NT, BF16, VEC, K>(rv, W, sh);
+    double se = 0.0;
+    if (st.nf > 0 && !st.nonfin)
+      se = row_expsum<NT, BF16, VEC, K>(
+          rv, W, st.zm, (float)(greedy ? 1.0 : 1.0 / (double)rp.temperature), sh);
+    if (tid == 0) {
+      P->zm = st.zm;
+      P->am = st.nf > 0 ? a.v0 + st.am : INT_MAX;
+      P->nf = st.nf;
+      P->nonfin = st.nonfin;
+      P->se = se;
+    }
+    return;
+  }
+
+  const ShardState S = a.state[r];
+  if (!S.active) return;  // greedy, INVALID and OVERFLOW rows end with the stats
+  const double Td = (double)rp.temperature;
+
+  if (a.phase >= SHARD_TOPK0 && a.phase < SHARD_TOPK0 + 4) {
+    if (!S.topk_on) return;
+    const int shift = 24 - 8 * (a.phase - SHARD_TOPK0);
+    if (tid < 256) sh.hist[tid] = 0ull;
+    __syncthreads();
+    for_row4<NT, BF16, VEC, K>(rv, W, nonfin, [&](const float* x, int64_t) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (x[q] == CDS_NEG_INF) continue;
+        const uint32_t u = okey(x[q]);
+        if ((u & S.pmask) == S.prefix) atomicAdd(&sh.hist[(u >> shift) & 255u], 1ull);
+      }
+    });
+    __syncthreads();
+    if (tid < 256) P->hist[tid] = sh.hist[tid];
+    return;
+  }
+
+  if (rp.flags & ROW_TOPP) {
+    const double scale = mass_scale(a.V);
+    const double m = S.m;
+    auto wfix = [&](float v) -> unsigned long long {
+      return (unsigned long long)(exp((double)v / Td - m) * scale + 0.5);
+    };
+    const float zc = S.zcut;
+    if (a.phase == SHARD_TOPP_SUMS) {
+      // the mass of what min-p and top-k left, and the mass the cut is
+      // normalised by (the top-k set for min-p last, every token for joint)
+      const uint32_t ord = rp.flags & kRowOrderBits;
+      const float zn = (ord & ROW_ORDER_MINP_LAST) ? S.zk : CDS_NEG_INF;
+      unsigned long long s0 = 0, s1 = 0;
+      for_row4<NT, BF16, VEC, K>(rv, W, nonfin, [&](const float* x, int64_t) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (x[q] == CDS_NEG_INF) continue;
+          if (x[q] >= zc) s0 += wfix(x[q]);
+          if (ord && x[q] >= zn) s1 += wfix(x[q]);
+        }
+      });
+      s0 = block_sum_u64<NT>(s0, sh.red);
+      s1 = block_sum_u64<NT>(s1, sh.red);
+      if (tid == 0) {
+        P->s0 = s0;
+        P->s1 = s1;
+      }
+      return;
+    }
+    if (a.phase >= SHARD_TOPP0 && a.phase < SHARD_TOPP0 + 4) {
+      if (!S.topp_on) return;
+      const int shift = 24 - 8 * (a.phase - SHARD_TOPP0);
+      if (tid < 256) sh.hist[tid] = 0ull;
+      __syncthreads();
+      for_row4<NT, BF16, VEC, K>(rv, W, nonfin, [&](const float* x, int64_t) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (x[q] == CDS_NEG_INF || x[q] < zc) continue;
+          const uint32_t u = okey(x[q]);
+          if ((u & S.pmask) == S.prefix) atomicAdd(&sh.hist[(u >> shift) & 255u], wfix(x[q]));
+        }
+      });
+      __syncthreads();
+      if (tid < 256) P->hist[tid] = sh.hist[tid];
+      return;
+    }
+  }
+
+  if (a.phase == SHARD_RACE) {
+    // the race over {z >= zcut} with global ids: t0 + v0 is a multiple of
+    // four (the host checks v0), so one Philox block serves each group
+    const RaceCtx c = make_race_ctx(rp, S.zm);
+    Best b = best_init();
+    const float zf = S.zcut;
+    const int64_t v0 = a.v0;
+    for_row4<NT, BF16, VEC, K>(rv, W, nonfin, [&](const float* x, int64_t t0) {
+      bool need = false;
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        need |= (x[q] != CDS_NEG_INF && x[q] >= zf && race_hopeful(b, x[q], c));
+      if (!need) return;
+      const uint4 blk = race_block(c, v0 + t0);
+      const uint32_t xs[4] = {blk.x, blk.y, blk.z, blk.w};
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (x[q] != CDS_NEG_INF && x[q] >= zf)
+          race_consider(b, x[q], (int32_t)(v0 + t0 + q), xs[q], c);
+    });
+    block_best<NT>(b, sh.red);
+    if (tid == 0) {
+      P->key = b.key;
+      P->t = b.t;
+      P->z = b.z;
+    }
+  }
+}
+
+// One workgroup per row: fold the shards' partials of one phase into the
+// row state (and write the row's outputs when the phase ends it).
+template <int NT>
+__global__ __launch_bounds__(NT) void shard_merge_kernel(const ShardArgs a) {
+  __shared__ ExactShared<NT> sh;
+  const int r = blockIdx.x;
+  const int B = a.B;
+  const int tid = threadIdx.x;
+  const RowParams rp = a.rows[r];
+  ShardState* S = a.state + r;
+  const ShardPartial* part = a.part;
+  const int np = a.n_parts;
+  auto out = [&](int32_t id, float lp, int32_t st) {
+    a.out_ids[r] = id;
+    if (a.out_lp) a.out_lp[r] = lp;
+    if (a.out_st) a.out_st[r] = st;
+  };
+
+  if (a.phase == SHARD_STATS) {
+    if (tid != 0) return;
+    const bool greedy = (rp.flags & ROW_GREEDY) != 0;
+    float zm = CDS_NEG_INF;
+    int32_t am = INT_MAX, nf = 0;
+    uint32_t nonfin = 0;
+    for (int p = 0; p < np; ++p) {
+      const ShardPartial& q = part[(int64_t)p * B + r];
+      nf += q.nf;
+      nonfin |= q.nonfin;
+      if (q.nf > 0 && (q.zm > zm || (q.zm == zm && q.am < am))) {
+        zm = q.zm;
+        am = q.am;
+      }
+    }
+    S->active = 0;
+    if (nf == 0) {
+      out(-1, CDS_NEG_INF, 2);
+      return;
+    }
+    if (nonfin) {
+      out(-1, __builtin_nanf(""), 1);
+      return;
+    }
+    const double invTe = greedy ? 1.0 : 1.0 / (double)rp.temperature;
+    double se = 0.0;
+    for (int p = 0; p < np; ++p) {
+      const ShardPartial& q = part[(int64_t)p * B + r];
+      if (q.nf > 0) se += q.se * exp(((double)q.zm - (double)zm) * (double)(float)invTe);
+    }
+    if (greedy) {
+      out(am, (float)(-log(se)), 0);
+      return;
+    }
+    const double Td = (double)rp.temperature;
+    ShardState s;
+    s.zm = zm;
+    s.am = am;
+    s.nf = nf;
+    s.active = 1;
+    s.m = (double)zm / Td;
+    s.log_z = log(se);
+    s.zcut = (rp.flags & ROW_MINP) ? minp_cut(zm, Td, s.m, rp.min_p) : CDS_NEG_INF;
+    s.zk = CDS_NEG_INF;
+    s.prefix = s.pmask = 0u;
+    s.krem = (unsigned long long)rp.top_k;
+    s.base = 0ull;
+    s.need = 0.0;
+    s.topk_on = (rp.flags & ROW_TOPK) && rp.top_k < nf;
+    s.topp_on = 0;
+    *S = s;
+    return;
+  }
+
+  const ShardState s = *S;  // every thread: the branches below are uniform
+  if (!s.active) return;
+
+  const bool topk_round = a.phase >= SHARD_TOPK0 && a.phase < SHARD_TOPK0 + 4;
+  const bool topp_round = a.phase >= SHARD_TOPP0 && a.phase < SHARD_TOPP0 + 4;
+  if ((topk_round && s.topk_on) || (topp_round && s.topp_on)) {
+    // the shards' histograms summed, then the digit: as the exact path's
+    // radix rounds on the whole row
+    const int i = a.phase - (topk_round ? SHARD_TOPK0 : SHARD_TOPP0);
+    const int shift = 24 - 8 * i;
+    if (tid < 256) {
+      unsigned long long h = 0;
+      for (int p = 0; p < np; ++p) h += part[(int64_t)p * B + r].hist[tid];
+      sh.hist[tid] = h;
+    }
+    __syncthreads();
+    unsigned long long above;
+    const int d = topk_round ? pick_digit<NT>(sh, (double)s.krem, 0ull, &above)
+                             : pick_digit<NT>(sh, s.need, s.base, &above);
+    if (tid == 0) {
+      ShardState n = s;
+      if (topk_round)
+        n.krem -= above;
+      else
+        n.base = above;
+      n.prefix |= (uint32_t)d << shift;
+      n.pmask |= 255u << shift;
+      if (i == 3) {
+        const float v = from_okey(n.prefix);
+        if (topk_round) n.zk = v;
+        n.zcut = fmaxf(n.zcut, v);
+        n.prefix = n.pmask = 0u;
+      }
+      *S = n;
+    }
+    return;
+  }
+
+  if (tid != 0) return;
+  if (a.phase == SHARD_TOPP_SUMS && (rp.flags & ROW_TOPP)) {
+    unsigned long long msum = 0, mnorm = 0;
+    for (int p = 0; p < np; ++p) {
+      msum += part[(int64_t)p * B + r].s0;
+      mnorm += part[(int64_t)p * B + r].s1;
+    }
+    if (!(rp.flags & kRowOrderBits)) mnorm = msum;
+    ShardState n = s;
+    n.need = (double)rp.top_p * (double)mnorm;
+    // a target above what min-p and top-k left keeps all of it
+    n.topp_on = !((double)msum < n.need);
+    n.prefix = n.pmask = 0u;
+    n.base = 0ull;
+    *S = n;
+    return;
+  }
+  if (a.phase == SHARD_RACE) {
+    double key = -HUGE_VAL;
+    int32_t t = INT_MAX;
+    float z = CDS_NEG_INF;
+    for (int p = 0; p < np; ++p) {
+      const ShardPartial& q = part[(int64_t)p * B + r];
+      if (better(q.key, q.t, key, t)) {
+        key = q.key;
+        t = q.t;
+        z = q.z;
+      }
+    }
+    const double Td = (double)rp.temperature;
+    if (t == INT_MAX)
+      out(-1, CDS_NEG_INF, 2);
+    else
+      out(t, (float)((double)z / Td - s.m - s.log_z), 0);
+  }
+}
+
+template <bool BF16, bool VEC>
+static hipError_t launch_pass(const ShardArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((shard_pass_kernel<kShardNT, BF16, VEC>), dim3((unsigned)a.B), dim3(kShardNT),
+                     0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_shard_pass(const ShardArgs& a, bool bf16, bool vec, hipStream_t stream) {
+  if (bf16) return vec ? launch_pass<true, true>(a, stream) : launch_pass<true, false>(a, stream);
+  return vec ? launch_pass<false, true>(a, stream) : launch_pass<false, false>(a, stream);
+}
+
+hipError_t launch_shard_merge(const ShardArgs& a, hipStream_t stream) {
+  hipLaunchKernelGGL((shard_merge_kernel<kMergeNT>), dim3((unsigned)a.B), dim3(kMergeNT), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace cds

@@ -478,6 +478,62 @@ int sampler_logprobs(const sampler_batch *b, const void *logits, int dtype,
                      const sampler_logprob_request *req,
                      const sampler_logprob_outputs *out, void *stream);
 
+/* ---- vocabulary-parallel sampling: one rank's share ------------------------
+ * Under tensor parallelism each rank holds the logits of a slice of the
+ * vocabulary ([GLM] "从最后一层 hidden 到 token id": the LM head's output is
+ * split along the vocabulary and normally all-gathered before sampling).
+ * These calls sample from the shards without gathering the logits ([GLM]
+ * "输出侧的通信与开销账本": sample on per-shard results, exchange only what
+ * the draw needs): the row's draw is the exact path's (SAMPLER_ALGO_EXACT)
+ * decomposed into phases; in each phase every shard makes a small partial
+ * record per row (sampler_shard_pass), the ranks all-gather the records, and
+ * every rank folds them into the same per-row state (sampler_shard_merge).
+ * The race uses global token ids in the Philox counter, so the winner is the
+ * best of the shards' winners, and every threshold is summed from exact
+ * per-shard integer counts and fixed-point masses: the results are those of
+ * sampler_sample_ex with SAMPLER_ALGO_EXACT on the gathered logits (ids and
+ * statuses bit for bit; logprobs within rounding).
+ *
+ * A step: sampler_shard_phases(b) gives the phases the batch needs (bit p
+ * set: run phase p); for each p in 0 .. SAMPLER_SHARD_PHASES-1 with its bit
+ * set, in order on one stream: sampler_shard_pass on every shard, writing
+ * its record block (sampler_shard_partial_bytes(B) bytes), then the blocks of
+ * all shards side by side ([n_parts][B] records, in any order: ties are
+ * broken by global id; what an all-gather of the blocks delivers), then
+ * sampler_shard_merge.  The merges
+ * write out_ids / out_logprobs / out_status (greedy, INVALID and OVERFLOW
+ * rows after phase 0, sampled rows after the last phase).
+ *
+ *   b         the packed batch of the whole vocabulary (b->V = every shard's
+ *             width summed); every rank packs the same parameters.
+ *   logits    dev [B, ld]: the shard, tokens v0 .. v0 + width - 1 (after the
+ *             transforms, which touch only the shard's own tokens).
+ *   v0        global id of the shard's first token: a multiple of 4 (four
+ *             tokens share a Philox block), 0 <= v0, v0 + width <= b->V.
+ *   bitmask   dev int32 [B, mask_ld] or NULL: the shard's own bitmask, bit j
+ *             of the shard's row (bit j&31 of word j>>5) for token v0 + j --
+ *             the mask split by vocabulary shard ([GLM] "结构化输出"); mask_ld
+ *             >= ceil(width/32).  row_has_mask as sampler_sample.
+ *   state     dev, sampler_shard_state_bytes(B), 16-byte aligned: written by
+ *             the merges, read by the passes; one per rank.
+ * Errors: bad phase, v0, width, strides or sizes -> SAMPLER_EINVAL; launch
+ * failure -> SAMPLER_EHIP.  Phases run out of order, or records from other
+ * steps, give unspecified results (never out-of-bounds accesses).
+ * -------------------------------------------------------------------------- */
+#define SAMPLER_SHARD_PHASES 11
+size_t sampler_shard_state_bytes(int32_t B);
+size_t sampler_shard_partial_bytes(int32_t B);
+uint32_t sampler_shard_phases(const sampler_batch *b);
+int sampler_shard_pass(const sampler_batch *b, int32_t phase, const void *logits,
+                       int dtype, int64_t ld, int32_t v0, int32_t width,
+                       const int32_t *bitmask, int64_t mask_ld,
+                       const uint8_t *row_has_mask, const void *state,
+                       void *partial, void *stream);
+int sampler_shard_merge(const sampler_batch *b, int32_t phase, void *state,
+                        const void *partials, int32_t n_parts,
+                        int32_t *out_ids, float *out_logprobs,
+                        int32_t *out_status, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

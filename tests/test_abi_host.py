@@ -321,3 +321,31 @@ def test_logprobs_request_validation(cds):
     o = cds.LogprobOutputs(size=ct.sizeof(cds.LogprobOutputs) - 8)
     assert cds.lib.sampler_logprobs(ct.byref(b), logits.ctypes.data, 0, 1000, None, 0, None,
                                     ct.byref(r), ct.byref(o), None) == -1
+
+
+def test_shard_calls_validated_without_launch(cds):
+    """The vocabulary-parallel calls: sizes, the phase set of a batch, and
+    rejected arguments (host pointers stand in: nothing is launched)."""
+    assert cds.lib.sampler_shard_state_bytes(192) == 80 * 192
+    assert cds.lib.sampler_shard_partial_bytes(192) == 2112 * 192
+    assert cds.lib.sampler_shard_state_bytes(0) == 0
+    T = np.array([0.0, 0.0], np.float32)
+    _, b = cds.pack_host(2, 1000, T)
+    assert cds.lib.sampler_shard_phases(ct.byref(b)) == 1            # all greedy: stats only
+    T = np.array([0.7, 0.0], np.float32)
+    _, b = cds.pack_host(2, 1000, T, top_k=np.array([5, 0], np.int32),
+                         top_p=np.array([0.9, 1.0], np.float32))
+    assert cds.lib.sampler_shard_phases(ct.byref(b)) == (1 << 11) - 1  # every phase
+    _, b = cds.pack_host(2, 1000, T)
+    assert cds.lib.sampler_shard_phases(ct.byref(b)) == 1 | (1 << 10)  # stats and race
+    x = np.zeros((2, 1000), np.float32)
+    buf = np.zeros(8192, np.uint8)
+    p = buf.ctypes.data + (-buf.ctypes.data) % 256
+    pas = lambda **kw: cds.lib.sampler_shard_pass(
+        ct.byref(b), kw.get("phase", 0), x.ctypes.data, 0, kw.get("ld", 1000), kw.get("v0", 0),
+        kw.get("width", 500), None, 0, None, p, p, None)
+    for bad in ({"phase": -1}, {"phase": 11}, {"v0": 2}, {"v0": -4}, {"width": 0},
+                {"v0": 600, "width": 500}, {"ld": 400}):
+        assert pas(**bad) == -1, bad
+    mer = lambda ph, n: cds.lib.sampler_shard_merge(ct.byref(b), ph, p, p, n, p, None, None, None)
+    assert mer(0, 0) == -1 and mer(11, 2) == -1
