@@ -61,6 +61,9 @@ def parse():
                     help="time the further-outputs call (sampler_logprobs: top-20 and 4 "
                          "named-token logprobs per row, the support sets of every 12th "
                          "row) on the workload instead of the sampling step")
+    ap.add_argument("--shards", type=int, default=0, metavar="TP",
+                    help="time vocabulary-parallel sampling (sampler_shard_pass / merge) "
+                         "with the vocabulary split into TP shards, every shard on this GPU")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB a few times (the "
                          "reference point for the FETCH_SIZE / WRITE_SIZE counters)")
@@ -85,6 +88,7 @@ WORKLOAD_FILES = {"c2": "c2_decode", "c3": "c3_penalties", "c4": "c4_grammar",
 KERNEL_SOURCES = {
     "sample_kernel": ("kernels.hip", "exact_path.h", "device_common.h", "layout.h"),
     "outputs_kernel": ("outputs.hip", "exact_path.h", "device_common.h", "layout.h", "kernels.h"),
+    "shard_pass_kernel": ("shard.hip", "exact_path.h", "device_common.h", "layout.h", "kernels.h"),
 }
 
 
@@ -101,7 +105,8 @@ def measured_traffic(config, kernel="sample_kernel"):
     """HBM bytes per launch of `kernel` from the committed FETCH_SIZE /
     WRITE_SIZE summary of this workload, or None when that summary is missing
     or was taken on different kernel sources."""
-    name = WORKLOAD_FILES[config] + ("" if kernel == "sample_kernel" else "_outputs")
+    name = WORKLOAD_FILES[config] + {"sample_kernel": "", "outputs_kernel": "_outputs",
+                                     "shard_pass_kernel": "_shards"}[kernel]
     path = os.path.join(ROOT, "profiles", f"hbm_traffic_{name}.md")
     if not os.path.exists(path):
         return None
@@ -227,6 +232,9 @@ def main():
 
     if args.outputs:
         bench_outputs(args)
+        return
+    if args.shards:
+        bench_shards(args)
         return
 
     import constrained_decoding_amd as cds
@@ -657,6 +665,161 @@ def cpu_baseline_outputs(sets, named, n_rows):
             "sample": f"transforms and further outputs of {len(work)} rows of the same "
                       f"workload (rotating the {len(sets)} input sets), row-parallel over "
                       f"{workers} threads, {tn:.1f} s"}
+
+
+SHARD_PHASE_NAMES = ["stats", "top-k 1", "top-k 2", "top-k 3", "top-k 4", "top-p sums",
+                     "top-p 1", "top-p 2", "top-p 3", "top-p 4", "race"]
+SHARD_RECORD_BYTES = {"stats": 24, "top-p sums": 16, "race": 16}   # per row; histograms 2048
+
+
+def bench_shards(args):
+    """Vocabulary-parallel sampling on the workload with the vocabulary split
+    into TP shards (multiples of 4 tokens) and every shard on this GPU: each
+    step runs the phases the batch needs, each phase a pass over every shard
+    and one merge.  HIP events around each whole step (the value) and around
+    the stats phase's TP passes (the roofline: one pass over one shard).  A
+    rank's own share (one shard's passes and the merges) is read from a
+    kernel trace."""
+    import torch
+
+    import constrained_decoding_amd as cds
+    from constrained_decoding_amd import _binding as bd
+    import workloads
+
+    TP = args.shards
+    sets = [workloads.input_set(args.config, s) for s in range(args.sets)]
+    b0 = sets[0]
+    B, V = b0.B, b0.V
+    step_w = (V // TP + 3) // 4 * 4
+    bounds = [min(i * step_w, V) for i in range(TP)] + [V]
+    prep = []
+    for b in sets:
+        if b.bf16:
+            x = torch.from_numpy(np.ascontiguousarray(b.logits).view(np.int16)) \
+                .view(torch.bfloat16).cuda()
+        else:
+            x = torch.from_numpy(b.logits).cuda()
+        kw = dict(top_k=b.top_k, top_p=b.top_p, min_p=b.min_p, seed=b.seed, offset=b.offset,
+                  filter_order=b.order)
+        if b.rep is not None:
+            kw.update(repetition_penalty=b.rep, frequency_penalty=b.freq,
+                      presence_penalty=b.pres, hist_indptr=b.hist_indptr, hist_ids=b.hist_ids)
+        if b.bias_indptr is not None:
+            kw.update(bias_indptr=b.bias_indptr, bias_ids=b.bias_ids, bias_vals=b.bias_vals)
+        pk = cds.PackedBatch(B, V, b.temperature, **kw)
+        if b.rep is not None or b.bias_indptr is not None:
+            cds.apply_transforms(pk, x)
+        bits = None
+        if b.masks is not None:
+            w = b.masks.view(np.uint32)
+            bits = ((w[:, :, None] >> np.arange(32, dtype=np.uint32)) & 1) \
+                .reshape(B, -1)[:, :V].astype(bool)
+        shards = []
+        for a0, a1 in zip(bounds[:-1], bounds[1:]):
+            m = None
+            if bits is not None:
+                m = torch.from_numpy(workloads.pack_bitmask(
+                    [np.flatnonzero(bits[r, a0:a1]) for r in range(B)], a1 - a0)).cuda()
+            shards.append((x[:, a0:a1].contiguous(), a0, m))
+        rhm = None if b.row_has_mask is None else torch.from_numpy(b.row_has_mask).cuda()
+        prep.append((pk, shards, rhm))
+        del x
+    bufs = bd.ShardBuffers(B, [a1 - a0 for a0, a1 in zip(bounds[:-1], bounds[1:])])
+    ids = torch.empty(B, dtype=torch.int32, device="cuda")
+    lp = torch.empty(B, dtype=torch.float32, device="cuda")
+    st = torch.empty(B, dtype=torch.int32, device="cuda")
+    lib = bd.lib
+    sp = torch.cuda.current_stream().cuda_stream
+    phases = [int(lib.sampler_shard_phases(ct.byref(p[0].batch))) for p in prep]
+    run = [ph for ph in range(bd.SHARD_PHASES) if (phases[0] >> ph) & 1]
+    calls = []
+    for pk, shards, rhm in prep:
+        br = ct.byref(pk.batch)
+        per = []
+        for ph in run:
+            passes = [(br, ph, xs.data_ptr(), cds.DTYPE_BF16 if b0.bf16 else cds.DTYPE_F32,
+                       xs.stride(0), v0, xs.shape[1], None if m is None else m.data_ptr(),
+                       0 if m is None else m.stride(0), None if rhm is None else rhm.data_ptr(),
+                       bufs.state, bufs.offsets[p], sp)
+                      for p, (xs, v0, m) in enumerate(shards)]
+            merge = (br, ph, bufs.state, bufs.parts, bufs.n_records, ids.data_ptr(),
+                     lp.data_ptr(), st.data_ptr(), sp)
+            per.append((passes, merge))
+        calls.append(per)
+
+    def step(j, ev_step=None, ev_stats=None):
+        if ev_step is not None:
+            ev_step[0].record()
+        for k, (passes, merge) in enumerate(calls[j]):
+            if k == 0 and ev_stats is not None:
+                ev_stats[0].record()
+            for c in passes:
+                rc = lib.sampler_shard_pass(*c)
+                if rc != 0:
+                    raise cds.SamplerError(rc, "sampler_shard_pass")
+            if k == 0 and ev_stats is not None:
+                ev_stats[1].record()
+            rc = lib.sampler_shard_merge(*merge)
+            if rc != 0:
+                raise cds.SamplerError(rc, "sampler_shard_merge")
+        if ev_step is not None:
+            ev_step[1].record()
+
+    for i in range(args.warmup):
+        step(i % len(sets))
+    torch.cuda.synchronize()
+    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    evs = [(mk(), mk()) for _ in range(args.steps)]
+    for a, z in evs:                   # create the HIP events outside the timed region
+        for e in (*a, *z):
+            e.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i % len(sets), *evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    step_us = np.array([a[0].elapsed_time(a[1]) for a, _ in evs]) * 1e3
+    stats_us = np.array([z[0].elapsed_time(z[1]) for _, z in evs]) * 1e3 / TP
+    elem = 2 if b0.bf16 else 4
+    width = bounds[1] - bounds[0]
+    shard_bytes = B * width * elem + B * ROW_PARAM_BYTES
+    if b0.masks is not None:
+        rows = B if b0.row_has_mask is None else int(b0.row_has_mask.sum())
+        shard_bytes += rows * ((width + 31) // 32) * 4
+    st_us = float(np.mean(stats_us))
+    achieved = shard_bytes / (st_us * 1e-6) / 1e9
+    exchange = sum(SHARD_RECORD_BYTES.get(SHARD_PHASE_NAMES[ph], 2048) for ph in run) * B * \
+        bufs.n_records
+    cpu = None if args.no_cpu else cpu_baseline(sets, args.cpu_rows)
+    line = {
+        "metric": f"rows/sec of vocabulary-parallel sampling with the vocabulary split "
+                  f"{TP} ways and every shard on one GPU, B={B}, V={V}",
+        "value": round(B / (float(np.mean(step_us)) * 1e-6), 1),
+        "unit": "rows/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(float(np.mean(step_us)) * 1e-3, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if b0.bf16 else "f32",
+        "data": "synthetic (seeded; stands in for GLM-5.3 decode logits)",
+        "config": {"workload": WORKLOAD_NAMES[args.config] + f"; vocabulary split {TP} ways",
+                   "B": B, "V": V, "tp": TP, "shard_width": width, "input_sets": len(sets),
+                   "phases": [SHARD_PHASE_NAMES[ph] for ph in run]},
+        "step_us_p10_p50_p90": [round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)],
+        "wall_ms_per_step": round(elapsed * 1e3 / args.steps, 3),
+        "exchange_bytes_per_step": exchange,
+        "roofline": {"bound": "hbm", "kernel": "shard_pass_kernel (stats phase)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBS, 4),
+                     "traffic": measured_traffic(args.config, "shard_pass_kernel"),
+                     "kernel_us": round(st_us, 2), "bytes_per_launch": shard_bytes},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":

@@ -32,7 +32,8 @@ EXPORTS = [
     "sampler_pack_host", "sampler_apply_transforms", "sampler_apply_bitmask",
     "sampler_workspace_bytes", "sampler_workspace_bytes_batch", "sampler_workspace_init",
     "sampler_sample", "sampler_sample_ex", "sampler_sample_static", "sampler_logprobs",
-    "sampler_shard_state_bytes", "sampler_shard_partial_bytes", "sampler_shard_phases",
+    "sampler_shard_state_bytes", "sampler_shard_records", "sampler_shard_partial_bytes",
+    "sampler_shard_phases",
     "sampler_shard_pass", "sampler_shard_merge",
 ]
 
@@ -117,7 +118,8 @@ def _load():
         "sampler_sample_static": ([P, P, ct.c_int, I64, P, I64, P, P, P, P, P], ct.c_int),
         "sampler_logprobs": ([P, P, ct.c_int, I64, P, I64, P, P, P, P], ct.c_int),
         "sampler_shard_state_bytes": ([I32], SZ),
-        "sampler_shard_partial_bytes": ([I32], SZ),
+        "sampler_shard_records": ([I32], I32),
+        "sampler_shard_partial_bytes": ([I32, I32], SZ),
         "sampler_shard_phases": ([P], ct.c_uint32),
         "sampler_shard_pass": ([P, I32, P, ct.c_int, I64, I32, I32, P, I64, P, P, P, P], ct.c_int),
         "sampler_shard_merge": ([P, I32, P, P, I32, P, P, P, P], ct.c_int),
@@ -449,17 +451,19 @@ def _aligned_buffer(nbytes, device, align=256):
 
 
 class ShardBuffers:
-    """The per-rank state and the partial records of n_parts shards (the
-    records side by side, as an all-gather delivers them)."""
+    """The per-rank state and the partial records of a set of shards (their
+    record blocks side by side, as an all-gather delivers them)."""
 
-    def __init__(self, B, n_parts, *, device="cuda"):
+    def __init__(self, B, widths, *, device="cuda"):
         self.state_bytes = int(lib.sampler_shard_state_bytes(B))
-        self.part_bytes = int(lib.sampler_shard_partial_bytes(B))
-        if not self.state_bytes or not self.part_bytes:
-            raise SamplerError(ERANGE, "sampler_shard_state_bytes")
+        self.block_bytes = [int(lib.sampler_shard_partial_bytes(B, int(w))) for w in widths]
+        if not self.state_bytes or not all(self.block_bytes):
+            raise SamplerError(ERANGE, "sampler_shard_partial_bytes")
+        self.n_records = sum(int(lib.sampler_shard_records(int(w))) for w in widths)
         self._s, self.state = _aligned_buffer(self.state_bytes, device)
-        self._p, self.parts = _aligned_buffer(self.part_bytes * n_parts, device)
-        self.B, self.n_parts = B, n_parts
+        self._p, self.parts = _aligned_buffer(sum(self.block_bytes), device)
+        self.offsets = [self.parts + int(o) for o in np.cumsum([0] + self.block_bytes[:-1])]
+        self.B = B
 
 
 def shard_sample(packed: PackedBatch, shards, *, row_has_mask=None, buffers=None, out=None,
@@ -473,7 +477,7 @@ def shard_sample(packed: PackedBatch, shards, *, row_has_mask=None, buffers=None
     B = packed.B
     dev = shards[0][0].device
     if buffers is None:
-        buffers = ShardBuffers(B, len(shards), device=dev)
+        buffers = ShardBuffers(B, [x.shape[1] for x, _, _ in shards], device=dev)
     if out is None:
         ids = torch.empty(B, dtype=torch.int32, device=dev)
         lp = torch.empty(B, dtype=torch.float32, device=dev)
@@ -493,9 +497,9 @@ def shard_sample(packed: PackedBatch, shards, *, row_has_mask=None, buffers=None
             _check(lib.sampler_shard_pass(
                 br, ph, x.data_ptr(), _dtype_code(x), x.stride(0), int(v0), x.shape[1],
                 None if mask is None else mask.data_ptr(), 0 if mask is None else mask.stride(0),
-                rhm, buffers.state, buffers.parts + p * buffers.part_bytes, sp),
+                rhm, buffers.state, buffers.offsets[p], sp),
                 "sampler_shard_pass")
-        _check(lib.sampler_shard_merge(br, ph, buffers.state, buffers.parts, len(shards),
+        _check(lib.sampler_shard_merge(br, ph, buffers.state, buffers.parts, buffers.n_records,
                                        ids.data_ptr(), lp.data_ptr(), st.data_ptr(), sp),
                "sampler_shard_merge")
     return ids, lp, st

@@ -111,6 +111,12 @@ struct alignas(16) ShardPartial {
 };
 static_assert(sizeof(ShardPartial) == 2112, "ShardPartial layout");
 
+// A shard's pass splits each row into sub-slices of kShardSub tokens (a
+// multiple of 32, so that a sub-slice starts on a mask word), one workgroup
+// and one record each: a shard of width w makes ceil(w / kShardSub) records
+// per row, laid out [sub-slice][B].
+constexpr int kShardSub = 4096;
+
 struct ShardArgs {
   const RowParams* rows;
   const void* logits;   // the shard: [B, ld], tokens v0 .. v0 + width - 1
@@ -121,8 +127,8 @@ struct ShardArgs {
   int64_t mask_ld;
   const uint8_t* row_has_mask;
   ShardState* state;
-  ShardPartial* part;   // pass: this shard's [B]; merge: [n_parts][B]
-  int32_t n_parts;
+  ShardPartial* part;   // pass: this shard's [subs][B]; merge: [n_parts][B]
+  int32_t n_parts;      // merge: records per row over every shard
   int32_t phase;
   int32_t* out_ids;
   float* out_lp;

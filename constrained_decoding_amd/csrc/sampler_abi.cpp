@@ -728,9 +728,14 @@ size_t sampler_shard_state_bytes(int32_t B) {
   return sizeof(ShardState) * (size_t)B;
 }
 
-size_t sampler_shard_partial_bytes(int32_t B) {
-  if (B <= 0 || B > kMaxB) return 0;
-  return sizeof(ShardPartial) * (size_t)B;
+int32_t sampler_shard_records(int32_t width) {
+  if (width <= 0) return 0;
+  return (int32_t)(((int64_t)width + kShardSub - 1) / kShardSub);
+}
+
+size_t sampler_shard_partial_bytes(int32_t B, int32_t width) {
+  if (B <= 0 || B > kMaxB || width <= 0) return 0;
+  return sizeof(ShardPartial) * (size_t)B * (size_t)sampler_shard_records(width);
 }
 
 uint32_t sampler_shard_phases(const sampler_batch* b) {
@@ -786,14 +791,14 @@ int sampler_shard_pass(const sampler_batch* b, int32_t phase, const void* logits
 }
 
 int sampler_shard_merge(const sampler_batch* b, int32_t phase, void* state, const void* partials,
-                        int32_t n_parts, int32_t* out_ids, float* out_logprobs,
+                        int32_t n_records, int32_t* out_ids, float* out_logprobs,
                         int32_t* out_status, void* stream) {
   if (!b || !b->d_rows || !state || !partials || !out_ids) return SAMPLER_EINVAL;
   const int32_t B = b->B, V = b->V;
   if (B <= 0 || V <= 0) return SAMPLER_EINVAL;
   if (B > kMaxB || V > kMaxV) return SAMPLER_ERANGE;
   if (phase < 0 || phase >= SHARD_PHASES) return SAMPLER_EINVAL;
-  if (n_parts < 1 || n_parts > V / 4 + 1) return SAMPLER_EINVAL;
+  if (n_records < 1 || n_records > V / 4 + 1) return SAMPLER_EINVAL;
   if (!aligned(state, 16) || !aligned(partials, 16)) return SAMPLER_EINVAL;
   ShardArgs a;
   std::memset(&a, 0, sizeof a);
@@ -802,7 +807,7 @@ int sampler_shard_merge(const sampler_batch* b, int32_t phase, void* state, cons
   a.V = V;
   a.state = static_cast<ShardState*>(state);
   a.part = static_cast<ShardPartial*>(const_cast<void*>(partials));
-  a.n_parts = n_parts;
+  a.n_parts = n_records;
   a.phase = phase;
   a.out_ids = out_ids;
   a.out_lp = out_logprobs;

@@ -38,22 +38,26 @@
 
 namespace cds {
 
-constexpr int kShardNT = 512;
-constexpr int kShardK = 8;
+constexpr int kShardNT = 256;
+constexpr int kShardK = 4;
 constexpr int kMergeNT = 256;
 
+// Sub-slice s of row r of the shard: tokens s * kShardSub .. (whole mask
+// words: kShardSub is a multiple of 32).
 template <bool BF16>
-__device__ __forceinline__ RowView shard_view(const ShardArgs& a, int r) {
+__device__ __forceinline__ RowView shard_view(const ShardArgs& a, int r, int s) {
   RowView v;
+  const int64_t o = (int64_t)r * a.ld + (int64_t)s * kShardSub;
   if (BF16) {
-    v.b16 = static_cast<const uint16_t*>(a.logits) + (int64_t)r * a.ld;
+    v.b16 = static_cast<const uint16_t*>(a.logits) + o;
     v.f32 = nullptr;
   } else {
-    v.f32 = static_cast<const float*>(a.logits) + (int64_t)r * a.ld;
+    v.f32 = static_cast<const float*>(a.logits) + o;
     v.b16 = nullptr;
   }
-  v.mrow = (a.mask && (!a.row_has_mask || a.row_has_mask[r])) ? a.mask + (int64_t)r * a.mask_ld
-                                                              : nullptr;
+  v.mrow = (a.mask && (!a.row_has_mask || a.row_has_mask[r]))
+               ? a.mask + (int64_t)r * a.mask_ld + (int64_t)s * (kShardSub / 32)
+               : nullptr;
   return v;
 }
 
@@ -69,11 +73,14 @@ template <int NT, bool BF16, bool VEC>
 __global__ __launch_bounds__(NT) void shard_pass_kernel(const ShardArgs a) {
   constexpr int K = kShardK;
   __shared__ ExactShared<NT> sh;
-  const int r = blockIdx.x;
+  // workgroup k: row k % B, sub-slice k / B (its record sits at k)
+  const int r = (int)(blockIdx.x % (unsigned)a.B);
+  const int sub = (int)(blockIdx.x / (unsigned)a.B);
   const RowParams rp = a.rows[r];
-  const RowView rv = shard_view<BF16>(a, r);
-  const int64_t W = a.width;
-  ShardPartial* P = a.part + r;
+  const RowView rv = shard_view<BF16>(a, r, sub);
+  const int64_t W = min((int64_t)kShardSub, (int64_t)a.width - (int64_t)sub * kShardSub);
+  const int64_t v0 = (int64_t)a.v0 + (int64_t)sub * kShardSub;
+  ShardPartial* P = a.part + blockIdx.x;
   const int tid = threadIdx.x;
   uint32_t nonfin = 0;
 
@@ -86,7 +93,7 @@ __global__ __launch_bounds__(NT) void shard_pass_kernel(const ShardArgs a) {
           rv, W, st.zm, (float)(greedy ? 1.0 : 1.0 / (double)rp.temperature), sh);
     if (tid == 0) {
       P->zm = st.zm;
-      P->am = st.nf > 0 ? a.v0 + st.am : INT_MAX;
+      P->am = st.nf > 0 ? (int32_t)(v0 + st.am) : INT_MAX;
       P->nf = st.nf;
       P->nonfin = st.nonfin;
       P->se = se;
@@ -166,11 +173,11 @@ __global__ __launch_bounds__(NT) void shard_pass_kernel(const ShardArgs a) {
 
   if (a.phase == SHARD_RACE) {
     // the race over {z >= zcut} with global ids: t0 + v0 is a multiple of
-    // four (the host checks v0), so one Philox block serves each group
+    // four (the host checks the shard's v0), so one Philox block serves
+    // each group
     const RaceCtx c = make_race_ctx(rp, S.zm);
     Best b = best_init();
     const float zf = S.zcut;
-    const int64_t v0 = a.v0;
     for_row4<NT, BF16, VEC, K>(rv, W, nonfin, [&](const float* x, int64_t t0) {
       bool need = false;
 #pragma unroll
@@ -212,12 +219,12 @@ __global__ __launch_bounds__(NT) void shard_merge_kernel(const ShardArgs a) {
   };
 
   if (a.phase == SHARD_STATS) {
-    if (tid != 0) return;
+    if (tid >= 64) return;  // one wave: lane p folds records p, p + 64, ...
     const bool greedy = (rp.flags & ROW_GREEDY) != 0;
     float zm = CDS_NEG_INF;
     int32_t am = INT_MAX, nf = 0;
     uint32_t nonfin = 0;
-    for (int p = 0; p < np; ++p) {
+    for (int p = tid; p < np; p += 64) {
       const ShardPartial& q = part[(int64_t)p * B + r];
       nf += q.nf;
       nonfin |= q.nonfin;
@@ -226,6 +233,26 @@ __global__ __launch_bounds__(NT) void shard_merge_kernel(const ShardArgs a) {
         am = q.am;
       }
     }
+    struct ZA {
+      float z;
+      int32_t t;
+    };
+    const ZA za = wave_allreduce(ZA{zm, am}, [](const ZA& x, const ZA& y) {
+      return (y.z > x.z || (y.z == x.z && y.t < x.t)) ? y : x;
+    });
+    zm = za.z;
+    am = za.t;
+    nf = wave_allreduce(nf, [](int32_t x, int32_t y) { return x + y; });
+    nonfin = wave_allreduce(nonfin, [](uint32_t x, uint32_t y) { return x | y; });
+    const double invTe = greedy ? 1.0 : 1.0 / (double)rp.temperature;
+    double se = 0.0;
+    if (nf > 0 && !nonfin)
+      for (int p = tid; p < np; p += 64) {
+        const ShardPartial& q = part[(int64_t)p * B + r];
+        if (q.nf > 0) se += q.se * exp(((double)q.zm - (double)zm) * (double)(float)invTe);
+      }
+    se = wave_allreduce(se, [](double x, double y) { return x + y; });
+    if (tid != 0) return;
     S->active = 0;
     if (nf == 0) {
       out(-1, CDS_NEG_INF, 2);
@@ -235,33 +262,27 @@ __global__ __launch_bounds__(NT) void shard_merge_kernel(const ShardArgs a) {
       out(-1, __builtin_nanf(""), 1);
       return;
     }
-    const double invTe = greedy ? 1.0 : 1.0 / (double)rp.temperature;
-    double se = 0.0;
-    for (int p = 0; p < np; ++p) {
-      const ShardPartial& q = part[(int64_t)p * B + r];
-      if (q.nf > 0) se += q.se * exp(((double)q.zm - (double)zm) * (double)(float)invTe);
-    }
     if (greedy) {
       out(am, (float)(-log(se)), 0);
       return;
     }
     const double Td = (double)rp.temperature;
-    ShardState s;
-    s.zm = zm;
-    s.am = am;
-    s.nf = nf;
-    s.active = 1;
-    s.m = (double)zm / Td;
-    s.log_z = log(se);
-    s.zcut = (rp.flags & ROW_MINP) ? minp_cut(zm, Td, s.m, rp.min_p) : CDS_NEG_INF;
-    s.zk = CDS_NEG_INF;
-    s.prefix = s.pmask = 0u;
-    s.krem = (unsigned long long)rp.top_k;
-    s.base = 0ull;
-    s.need = 0.0;
-    s.topk_on = (rp.flags & ROW_TOPK) && rp.top_k < nf;
-    s.topp_on = 0;
-    *S = s;
+    ShardState st;
+    st.zm = zm;
+    st.am = am;
+    st.nf = nf;
+    st.active = 1;
+    st.m = (double)zm / Td;
+    st.log_z = log(se);
+    st.zcut = (rp.flags & ROW_MINP) ? minp_cut(zm, Td, st.m, rp.min_p) : CDS_NEG_INF;
+    st.zk = CDS_NEG_INF;
+    st.prefix = st.pmask = 0u;
+    st.krem = (unsigned long long)rp.top_k;
+    st.base = 0ull;
+    st.need = 0.0;
+    st.topk_on = (rp.flags & ROW_TOPK) && rp.top_k < nf;
+    st.topp_on = 0;
+    *S = st;
     return;
   }
 
@@ -277,6 +298,7 @@ __global__ __launch_bounds__(NT) void shard_merge_kernel(const ShardArgs a) {
     const int shift = 24 - 8 * i;
     if (tid < 256) {
       unsigned long long h = 0;
+#pragma unroll 8
       for (int p = 0; p < np; ++p) h += part[(int64_t)p * B + r].hist[tid];
       sh.hist[tid] = h;
     }
@@ -303,13 +325,17 @@ __global__ __launch_bounds__(NT) void shard_merge_kernel(const ShardArgs a) {
     return;
   }
 
-  if (tid != 0) return;
+  if (tid >= 64) return;  // one wave: lane p folds records p, p + 64, ...
   if (a.phase == SHARD_TOPP_SUMS && (rp.flags & ROW_TOPP)) {
     unsigned long long msum = 0, mnorm = 0;
-    for (int p = 0; p < np; ++p) {
+    for (int p = tid; p < np; p += 64) {
       msum += part[(int64_t)p * B + r].s0;
       mnorm += part[(int64_t)p * B + r].s1;
     }
+    auto add = [](unsigned long long x, unsigned long long y) { return x + y; };
+    msum = wave_allreduce(msum, add);
+    mnorm = wave_allreduce(mnorm, add);
+    if (tid != 0) return;
     if (!(rp.flags & kRowOrderBits)) mnorm = msum;
     ShardState n = s;
     n.need = (double)rp.top_p * (double)mnorm;
@@ -321,29 +347,31 @@ __global__ __launch_bounds__(NT) void shard_merge_kernel(const ShardArgs a) {
     return;
   }
   if (a.phase == SHARD_RACE) {
-    double key = -HUGE_VAL;
-    int32_t t = INT_MAX;
-    float z = CDS_NEG_INF;
-    for (int p = 0; p < np; ++p) {
+    struct KT {
+      double key;
+      int32_t t;
+      float z;
+    };
+    KT b{-HUGE_VAL, INT_MAX, CDS_NEG_INF};
+    for (int p = tid; p < np; p += 64) {
       const ShardPartial& q = part[(int64_t)p * B + r];
-      if (better(q.key, q.t, key, t)) {
-        key = q.key;
-        t = q.t;
-        z = q.z;
-      }
+      if (better(q.key, q.t, b.key, b.t)) b = KT{q.key, q.t, q.z};
     }
+    b = wave_allreduce(b, [](const KT& x, const KT& y) { return better(y.key, y.t, x.key, x.t) ? y : x; });
+    if (tid != 0) return;
     const double Td = (double)rp.temperature;
-    if (t == INT_MAX)
+    if (b.t == INT_MAX)
       out(-1, CDS_NEG_INF, 2);
     else
-      out(t, (float)((double)z / Td - s.m - s.log_z), 0);
+      out(b.t, (float)((double)b.z / Td - s.m - s.log_z), 0);
   }
 }
 
 template <bool BF16, bool VEC>
 static hipError_t launch_pass(const ShardArgs& a, hipStream_t s) {
-  hipLaunchKernelGGL((shard_pass_kernel<kShardNT, BF16, VEC>), dim3((unsigned)a.B), dim3(kShardNT),
-                     0, s, a);
+  const unsigned subs = (unsigned)((a.width + kShardSub - 1) / kShardSub);
+  hipLaunchKernelGGL((shard_pass_kernel<kShardNT, BF16, VEC>), dim3((unsigned)a.B * subs),
+                     dim3(kShardNT), 0, s, a);
   return hipGetLastError();
 }
 

@@ -497,8 +497,11 @@ int sampler_logprobs(const sampler_batch *b, const void *logits, int dtype,
  * A step: sampler_shard_phases(b) gives the phases the batch needs (bit p
  * set: run phase p); for each p in 0 .. SAMPLER_SHARD_PHASES-1 with its bit
  * set, in order on one stream: sampler_shard_pass on every shard, writing
- * its record block (sampler_shard_partial_bytes(B) bytes), then the blocks of
- * all shards side by side ([n_parts][B] records, in any order: ties are
+ * its record block (sampler_shard_partial_bytes(B, width) bytes: the pass
+ * splits each row of its shard into slices of 4096 tokens and makes one
+ * record per slice, sampler_shard_records(width) per row), then the blocks
+ * of all shards side by side (records of n_records = the shards'
+ * sampler_shard_records summed, [n_records][B], in any order: ties are
  * broken by global id; what an all-gather of the blocks delivers), then
  * sampler_shard_merge.  The merges
  * write out_ids / out_logprobs / out_status (greedy, INVALID and OVERFLOW
@@ -522,7 +525,8 @@ int sampler_logprobs(const sampler_batch *b, const void *logits, int dtype,
  * -------------------------------------------------------------------------- */
 #define SAMPLER_SHARD_PHASES 11
 size_t sampler_shard_state_bytes(int32_t B);
-size_t sampler_shard_partial_bytes(int32_t B);
+int32_t sampler_shard_records(int32_t width);
+size_t sampler_shard_partial_bytes(int32_t B, int32_t width);
 uint32_t sampler_shard_phases(const sampler_batch *b);
 int sampler_shard_pass(const sampler_batch *b, int32_t phase, const void *logits,
                        int dtype, int64_t ld, int32_t v0, int32_t width,
@@ -530,7 +534,7 @@ int sampler_shard_pass(const sampler_batch *b, int32_t phase, const void *logits
                        const uint8_t *row_has_mask, const void *state,
                        void *partial, void *stream);
 int sampler_shard_merge(const sampler_batch *b, int32_t phase, void *state,
-                        const void *partials, int32_t n_parts,
+                        const void *partials, int32_t n_records,
                         int32_t *out_ids, float *out_logprobs,
                         int32_t *out_status, void *stream);
 

@@ -327,7 +327,8 @@ def test_shard_calls_validated_without_launch(cds):
     """The vocabulary-parallel calls: sizes, the phase set of a batch, and
     rejected arguments (host pointers stand in: nothing is launched)."""
     assert cds.lib.sampler_shard_state_bytes(192) == 80 * 192
-    assert cds.lib.sampler_shard_partial_bytes(192) == 2112 * 192
+    assert cds.lib.sampler_shard_records(18992) == 5 and cds.lib.sampler_shard_records(4096) == 1
+    assert cds.lib.sampler_shard_partial_bytes(192, 18992) == 2112 * 192 * 5
     assert cds.lib.sampler_shard_state_bytes(0) == 0
     T = np.array([0.0, 0.0], np.float32)
     _, b = cds.pack_host(2, 1000, T)
