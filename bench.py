@@ -789,8 +789,12 @@ def bench_shards(args):
         shard_bytes += rows * ((width + 31) // 32) * 4
     st_us = float(np.mean(stats_us))
     achieved = shard_bytes / (st_us * 1e-6) / 1e9
-    exchange = sum(SHARD_RECORD_BYTES.get(SHARD_PHASE_NAMES[ph], 2048) for ph in run) * B * \
-        bufs.n_records
+    # what the ranks would exchange per step if each folded its slices'
+    # records into one per row first: an all-gather of those, or all-reduces
+    # (sums) for the histogram rounds
+    rec = [SHARD_RECORD_BYTES.get(SHARD_PHASE_NAMES[ph], 2048) for ph in run]
+    exchange = sum(rec) * B * TP
+    exchange_ar = sum(r for r in rec if r != 2048) * B * TP + sum(r for r in rec if r == 2048) * B
     cpu = None if args.no_cpu else cpu_baseline(sets, args.cpu_rows)
     line = {
         "metric": f"rows/sec of vocabulary-parallel sampling with the vocabulary split "
@@ -811,7 +815,8 @@ def bench_shards(args):
                    "phases": [SHARD_PHASE_NAMES[ph] for ph in run]},
         "step_us_p10_p50_p90": [round(float(np.percentile(step_us, q)), 2) for q in (10, 50, 90)],
         "wall_ms_per_step": round(elapsed * 1e3 / args.steps, 3),
-        "exchange_bytes_per_step": exchange,
+        "exchange_allgather_bytes_per_step": exchange,
+        "exchange_allreduce_hist_bytes_per_step": exchange_ar,
         "roofline": {"bound": "hbm", "kernel": "shard_pass_kernel (stats phase)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
