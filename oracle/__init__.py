@@ -85,6 +85,8 @@ def _load():
     lib.cdo_race_best.argtypes = [P, _ct.c_int32, _ct.c_float, _ct.c_double, _ct.c_uint64,
                                   _ct.c_uint64, _ct.c_int32, _ct.c_int32, P, _ct.c_uint8, P]
     lib.cdo_race_best.restype = _ct.c_int32
+    lib.cdo_spec_accept.argtypes = [P, P, _ct.c_int32, P, _ct.c_int32, P, P]
+    lib.cdo_spec_accept.restype = _ct.c_int32
     _lib = lib
     return lib
 
@@ -354,3 +356,19 @@ def race_best(z, in_set, *, T, m, seed, offset, v0, width, bit=4):
     t = _load().cdo_race_best(_ptr(zz), zz.shape[0], float(T), float(m), int(seed), int(offset),
                               int(v0), int(width), _ptr(st), int(bit), _ptr(key))
     return int(t), float(key[0])
+
+
+# --------------------------------------------------------- speculative verify
+
+def spec_accept(sampled, draft, status=None, eos=-1):
+    """One request's k+1 sampled rows against its k drafts: returns
+    (emitted tokens [count], count, rollback)."""
+    sm = _np.ascontiguousarray(sampled, _np.int32)
+    k = sm.shape[0] - 1
+    dr = _np.ascontiguousarray(draft, _np.int32)
+    assert dr.shape[0] == k
+    st = None if status is None else _np.ascontiguousarray(status, _np.int32)
+    tok = _np.empty(k + 1, _np.int32)
+    rb = _np.zeros(1, _np.int32)
+    n = _load().cdo_spec_accept(_ptr(sm), _ptr(st), k, _ptr(dr), int(eos), _ptr(tok), _ptr(rb))
+    return tok[:n], int(n), int(rb[0])

@@ -576,3 +576,31 @@ int32_t cdo_race_best(const float *z, int32_t V, float T, double m,
   *best_key = best;
   return best_t;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Speculative verification [GLM, "投机解码的输出行: 一次前向里的 k+1 个      */
+/* token": one verification forward gives k+1 rows per request (the token    */
+/* after the committed prefix, then after each of the k draft tokens); each  */
+/* row is sampled; the accepted tokens are kept and the rejected suffix's KV */
+/* rolled back; SGL, "逐 token 推进: accept_token、rollback 与跳步": the draft */
+/* is rolled back from the first position that does not match; the tail      */
+/* past a terminator is dropped].  Row j's sample y_j is compared with draft */
+/* token j+1: the first n drafts are accepted while y_j equals them, and the */
+/* request emits y_0 .. y_n (the accepted drafts and the row's own token at  */
+/* the first mismatch).  A row without a token (status not OK) ends the     */
+/* emission before it; a terminator ends it after itself.                    */
+/* ------------------------------------------------------------------------ */
+int32_t cdo_spec_accept(const int32_t *sampled, const int32_t *status,
+                        int32_t k, const int32_t *draft, int32_t eos,
+                        int32_t *tokens, int32_t *rollback) {
+  int32_t count = 0;
+  for (int32_t j = 0; j <= k; ++j) {
+    if (status && status[j] != CDO_STATUS_OK) break; /* no token here   */
+    tokens[count++] = sampled[j];
+    if (eos >= 0 && sampled[j] == eos) break;        /* terminator       */
+    if (j == k || sampled[j] != draft[j]) break;     /* first mismatch   */
+  }
+  for (int32_t j = count; j <= k; ++j) tokens[j] = -1;
+  *rollback = k + 1 - count; /* positions written by the verification but not kept */
+  return count;
+}

@@ -157,6 +157,18 @@ int32_t cdo_race_best(const float *z, int32_t V, float T, double m,
                       int32_t width, const uint8_t *set, uint8_t bit,
                       double *best_key);
 
+/* ---- speculative verification [GLM, "投机解码的输出行"] ------------------- */
+
+/* One request's k+1 sampled rows (sampled[j], status[j] or NULL) against its
+ * k draft tokens: the emitted tokens y_0 .. y_n (n = the number of leading
+ * drafts equal to the rows' samples, draft[j] compared with sampled[j]),
+ * cut before a row whose status is not OK and after the terminator `eos`
+ * (-1: none).  tokens [k+1] gets the emitted tokens then -1; *rollback =
+ * k + 1 - count.  Returns count. */
+int32_t cdo_spec_accept(const int32_t *sampled, const int32_t *status,
+                        int32_t k, const int32_t *draft, int32_t eos,
+                        int32_t *tokens, int32_t *rollback);
+
 #ifdef __cplusplus
 }
 #endif
