@@ -61,6 +61,10 @@ def parse():
                     help="time the further-outputs call (sampler_logprobs: top-20 and 4 "
                          "named-token logprobs per row, the support sets of every 12th "
                          "row) on the workload instead of the sampling step")
+    ap.add_argument("--spec", action="store_true",
+                    help="spec-verify workloads (c5a, c5b): add speculative verification "
+                         "(sampler_spec_accept, drafts = each row's most likely token) to "
+                         "the step and report emitted tokens/s")
     ap.add_argument("--shards", type=int, default=0, metavar="TP",
                     help="time vocabulary-parallel sampling (sampler_shard_pass / merge) "
                          "with the vocabulary split into TP shards, every shard on this GPU")
@@ -260,6 +264,19 @@ def main():
     outs = (torch.empty(B, dtype=torch.int32, device="cuda"),
             torch.empty(B, dtype=torch.float32, device="cuda"),
             torch.empty(B, dtype=torch.int32, device="cuda"))
+    spec = None
+    if args.spec:
+        if args.config not in ("c5a", "c5b"):
+            raise SystemExit("--spec needs a spec-verify workload (c5a or c5b)")
+        n_pos = 8
+        n_req = B // n_pos
+        drafts = [torch.from_numpy(workloads.spec_drafts(b, n_pos)).cuda() for b in sets]
+        spec = dict(n_req=n_req, k=n_pos - 1, drafts=drafts,
+                    tokens=torch.empty((n_req, n_pos), dtype=torch.int32, device="cuda"),
+                    count=torch.empty(n_req, dtype=torch.int32, device="cuda"),
+                    rollback=torch.empty(n_req, dtype=torch.int32, device="cuda"),
+                    ev=(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)),
+                    emitted=[])
 
     # The host parameter arrays of each input set (what a serving loop hands
     # over each step), and a ring of parameter slots -- a device block, a
@@ -338,6 +355,13 @@ def main():
                                    ws.ptr, ws.nbytes, compute_h, opts_ref)
         if rc != 0:
             raise cds.SamplerError(rc, "sampler_sample_ex")
+        if spec is not None:
+            rc = lib.sampler_spec_accept(spec["n_req"], spec["k"], out_ptrs[0], out_ptrs[2],
+                                         spec["drafts"][j].data_ptr(), None,
+                                         spec["tokens"].data_ptr(), spec["count"].data_ptr(),
+                                         spec["rollback"].data_ptr(), compute_h)
+            if rc != 0:
+                raise cds.SamplerError(rc, "sampler_spec_accept")
         hs["used"].record(compute)
         step_s.append(time.perf_counter() - t_in)
 
@@ -347,6 +371,24 @@ def main():
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    if spec is not None:
+        # tokens each input set emits (the draws are deterministic), and the
+        # verification kernel's own time
+        for j in range(len(sets)):
+            step(j, j=j)
+            torch.cuda.synchronize()
+            spec["emitted"].append(int(spec["count"].sum().item()))
+        acc = []
+        for _ in range(20):
+            spec["ev"][0].record()
+            rc = lib.sampler_spec_accept(spec["n_req"], spec["k"], out_ptrs[0], out_ptrs[2],
+                                         spec["drafts"][0].data_ptr(), None,
+                                         spec["tokens"].data_ptr(), spec["count"].data_ptr(),
+                                         spec["rollback"].data_ptr(), compute_h)
+            spec["ev"][1].record()
+            torch.cuda.synchronize()
+            acc.append(spec["ev"][0].elapsed_time(spec["ev"][1]) * 1e3)
+        spec["accept_us"] = float(np.median(acc))
     pack_s.clear()
     step_s.clear()
 
@@ -432,6 +474,18 @@ def main():
                      "bytes_per_launch": scan_bytes},
         "cpu_baseline": cpu,
     }
+    if spec is not None:
+        emitted = float(np.mean([spec["emitted"][i % len(sets)] for i in range(args.steps)]))
+        line["metric"] = (f"emitted tokens/sec of the spec-verify step ({spec['n_req']} requests x "
+                          f"{spec['k'] + 1} rows, V={V}, 1 GPU)")
+        line["value"] = round(emitted * args.steps / elapsed, 1)
+        line["unit"] = "tokens/s"
+        line["config"]["workload"] += "; speculative verification, drafts = rows' modes"
+        line["spec"] = {"requests": spec["n_req"], "drafts_per_request": spec["k"],
+                        "emitted_per_step": emitted,
+                        "emitted_per_set": spec["emitted"],
+                        "rows_per_s": round(rows_per_s, 1),
+                        "accept_kernel_us": round(spec["accept_us"], 2)}
     print(json.dumps(line), flush=True)
 
 

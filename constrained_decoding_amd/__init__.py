@@ -12,6 +12,6 @@ from ._binding import (  # noqa: F401
     FLAG_SPLIT_PASS2, LIB_PATH, LOGPROB_ORIGINAL, LOGPROB_SAMPLED, MAX_TOP_N, STATUS_INVALID,
     STATUS_OK, STATUS_OVERFLOW, WAIT_NONE, Batch, HostParams, LogprobOutputs, LogprobRequest,
     Options, PackedBatch, SamplerError, Workspace, apply_bitmask, apply_transforms,
-    bias_from_dict, csr, logprobs, SHARD_PHASES, ShardBuffers, shard_sample,
+    bias_from_dict, csr, logprobs, SHARD_PHASES, ShardBuffers, shard_sample, spec_accept,
     ORDER_JOINT, ORDER_MINP_FIRST, ORDER_MINP_LAST, lib, pack_host, sample, strerror, version,
 )

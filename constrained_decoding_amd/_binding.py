@@ -34,7 +34,7 @@ EXPORTS = [
     "sampler_sample", "sampler_sample_ex", "sampler_sample_static", "sampler_logprobs",
     "sampler_shard_state_bytes", "sampler_shard_records", "sampler_shard_partial_bytes",
     "sampler_shard_phases",
-    "sampler_shard_pass", "sampler_shard_merge",
+    "sampler_shard_pass", "sampler_shard_merge", "sampler_spec_accept",
 ]
 
 
@@ -123,6 +123,7 @@ def _load():
         "sampler_shard_phases": ([P], ct.c_uint32),
         "sampler_shard_pass": ([P, I32, P, ct.c_int, I64, I32, I32, P, I64, P, P, P, P], ct.c_int),
         "sampler_shard_merge": ([P, I32, P, P, I32, P, P, P, P], ct.c_int),
+        "sampler_spec_accept": ([I32, I32, P, P, P, P, P, P, P, P], ct.c_int),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -503,3 +504,24 @@ def shard_sample(packed: PackedBatch, shards, *, row_has_mask=None, buffers=None
                                        ids.data_ptr(), lp.data_ptr(), st.data_ptr(), sp),
                "sampler_shard_merge")
     return ids, lp, st
+
+
+def spec_accept(sampled, draft, *, status=None, eos=None, stream=None):
+    """Speculative verification (sampler_spec_accept): ``sampled`` int32
+    [n_req, k+1] (the drawn rows), ``draft`` int32 [n_req, k]; returns
+    (tokens [n_req, k+1], count [n_req], rollback [n_req]) device tensors."""
+    import torch
+    n_req, k1 = sampled.shape
+    k = k1 - 1
+    if draft.shape != (n_req, k):
+        raise ValueError("draft must be [n_req, k]")
+    dev = sampled.device
+    tokens = torch.empty((n_req, k1), dtype=torch.int32, device=dev)
+    count = torch.empty(n_req, dtype=torch.int32, device=dev)
+    rollback = torch.empty(n_req, dtype=torch.int32, device=dev)
+    ptr = lambda t: None if t is None else t.data_ptr()
+    _check(lib.sampler_spec_accept(n_req, k, sampled.data_ptr(), ptr(status),
+                                   ptr(draft) if k > 0 else None, ptr(eos), tokens.data_ptr(),
+                                   count.data_ptr(), rollback.data_ptr(), _stream_ptr(stream)),
+           "sampler_spec_accept")
+    return tokens, count, rollback

@@ -138,6 +138,20 @@ struct ShardArgs {
 hipError_t launch_shard_pass(const ShardArgs& a, bool bf16, bool vec, hipStream_t stream);
 hipError_t launch_shard_merge(const ShardArgs& a, hipStream_t stream);
 
+// ---- speculative verification (spec.hip) -----------------------------------------
+struct SpecArgs {
+  int32_t n_req, k;         // requests, drafts per request (k+1 rows each)
+  const int32_t* sampled;   // [n_req, k+1] the rows' drawn tokens
+  const int32_t* status;    // [n_req, k+1] or nullptr
+  const int32_t* draft;     // [n_req, k]
+  const int32_t* eos;       // [n_req] terminator per request (-1: none) or nullptr
+  int32_t* tokens;          // [n_req, k+1] emitted tokens, then -1
+  int32_t* count;           // [n_req] tokens emitted
+  int32_t* rollback;        // [n_req] positions to roll back, or nullptr
+};
+
+hipError_t launch_spec_accept(const SpecArgs& a, hipStream_t stream);
+
 // Optional timing events recorded around the sampling kernel.
 struct KernelEvents {
   hipEvent_t start;

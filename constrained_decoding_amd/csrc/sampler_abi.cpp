@@ -816,4 +816,25 @@ int sampler_shard_merge(const sampler_batch* b, int32_t phase, void* state, cons
   return e == hipSuccess ? SAMPLER_OK : SAMPLER_EHIP;
 }
 
+int sampler_spec_accept(int32_t n_req, int32_t k, const int32_t* sampled, const int32_t* status,
+                        const int32_t* draft, const int32_t* eos, int32_t* tokens, int32_t* count,
+                        int32_t* rollback, void* stream) {
+  if (n_req < 0 || k < 0 || n_req > kMaxB) return SAMPLER_EINVAL;
+  if (n_req == 0) return SAMPLER_OK;
+  if (!sampled || !tokens || !count || (k > 0 && !draft)) return SAMPLER_EINVAL;
+  if ((int64_t)n_req * (k + 1) > kMaxB) return SAMPLER_ERANGE;
+  SpecArgs a;
+  a.n_req = n_req;
+  a.k = k;
+  a.sampled = sampled;
+  a.status = status;
+  a.draft = draft;
+  a.eos = eos;
+  a.tokens = tokens;
+  a.count = count;
+  a.rollback = rollback;
+  const hipError_t e = launch_spec_accept(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? SAMPLER_OK : SAMPLER_EHIP;
+}
+
 }  // extern "C"

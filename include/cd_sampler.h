@@ -538,6 +538,37 @@ int sampler_shard_merge(const sampler_batch *b, int32_t phase, void *state,
                         int32_t *out_ids, float *out_logprobs,
                         int32_t *out_status, void *stream);
 
+/* ---- speculative verification -----------------------------------------------
+ * One verification forward of a linear draft gives k+1 rows per request
+ * ([GLM] "投机解码的输出行"): row j of request i (row i*(k+1) + j of the
+ * batch) is the distribution after the committed prefix and the first j
+ * draft tokens.  After sampler_sample has drawn y_j from every row, draft
+ * token j+1 (draft[i*k + j]) is accepted while y_j equals it; the request
+ * emits y_0 .. y_n -- the n accepted drafts, then the row's own token at the
+ * first mismatch (the bonus token when all k are accepted) -- and the KV the
+ * verification wrote past what is kept is rolled back ([SGL] "逐 token 推进":
+ * rollback from the first mismatching position).  Emission also stops after
+ * the request's terminator token (the tail past it is dropped: [SO] 4.4
+ * "推进与终止") and before a row whose status is not OK.
+ * Every emitted token is a draw from the target's own distribution given the
+ * tokens before it: the rule changes how many tokens a step yields, not
+ * their distribution.  Greedy rows verify greedily.
+ *   sampled   dev int32 [n_req, k+1] (sampler_sample's out_ids)
+ *   status    dev int32 [n_req, k+1] or NULL (sampler_sample's out_status)
+ *   draft     dev int32 [n_req, k]
+ *   eos       dev int32 [n_req] or NULL: terminator per request, -1 = none
+ *   tokens    dev int32 [n_req, k+1]: emitted tokens, then -1
+ *   count     dev int32 [n_req]: tokens emitted, 0 .. k+1 (0: row 0 of the
+ *             request had no token)
+ *   rollback  dev int32 [n_req] or NULL: k + 1 - count, the verified
+ *             positions whose KV is not kept
+ * Errors: n_req < 0, k < 0, or a required pointer NULL -> SAMPLER_EINVAL;
+ * launch failure -> SAMPLER_EHIP.  n_req = 0: SAMPLER_OK, no launch. */
+int sampler_spec_accept(int32_t n_req, int32_t k, const int32_t *sampled,
+                        const int32_t *status, const int32_t *draft,
+                        const int32_t *eos, int32_t *tokens, int32_t *count,
+                        int32_t *rollback, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

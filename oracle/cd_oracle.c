@@ -583,8 +583,8 @@ int32_t cdo_race_best(const float *z, int32_t V, float T, double m,
 /* after the committed prefix, then after each of the k draft tokens); each  */
 /* row is sampled; the accepted tokens are kept and the rejected suffix's KV */
 /* rolled back; SGL, "逐 token 推进: accept_token、rollback 与跳步": the draft */
-/* is rolled back from the first position that does not match; the tail      */
-/* past a terminator is dropped].  Row j's sample y_j is compared with draft */
+/* is rolled back from the first position that does not match; SO, 4.4     */
+/* "推进与终止": the tail past a terminator is dropped].  Row j's sample y_j is compared with draft */
 /* token j+1: the first n drafts are accepted while y_j equals them, and the */
 /* request emits y_0 .. y_n (the accepted drafts and the row's own token at  */
 /* the first mismatch).  A row without a token (status not OK) ends the     */

@@ -42,6 +42,7 @@ hipError_t launch_outputs(const SampleArgs&, const OutputArgs&, bool, bool, cons
 }
 hipError_t launch_shard_pass(const ShardArgs&, bool, bool, hipStream_t) { return hipSuccess; }
 hipError_t launch_shard_merge(const ShardArgs&, hipStream_t) { return hipSuccess; }
+hipError_t launch_spec_accept(const SpecArgs&, hipStream_t) { return hipSuccess; }
 }  // namespace cds
 
 static int fail(const char* what, int it) {

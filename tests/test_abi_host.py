@@ -350,3 +350,14 @@ def test_shard_calls_validated_without_launch(cds):
         assert pas(**bad) == -1, bad
     mer = lambda ph, n: cds.lib.sampler_shard_merge(ct.byref(b), ph, p, p, n, p, None, None, None)
     assert mer(0, 0) == -1 and mer(11, 2) == -1
+
+
+def test_spec_accept_validated_without_launch(cds):
+    P = np.zeros(64, np.int32).ctypes.data
+    f = cds.lib.sampler_spec_accept
+    assert f(0, 7, None, None, None, None, None, None, None, None) == 0   # nothing to do
+    assert f(-1, 7, P, None, P, None, P, P, None, None) == -1
+    assert f(4, -1, P, None, P, None, P, P, None, None) == -1
+    assert f(4, 7, None, None, P, None, P, P, None, None) == -1
+    assert f(4, 7, P, None, None, None, P, P, None, None) == -1         # drafts required
+    assert f(4, 7, P, None, P, None, P, None, None, None) == -1         # counts required

@@ -1,8 +1,8 @@
 """Pins of the oracle's speculative-verification rule ("GLM-5.3 推理全链路
 (七)", section 投机解码的输出行: k+1 sampled rows per request, accepted
 tokens kept and the rejected suffix rolled back; "SGLang 源码完全拆解(十)",
-section 逐 token 推进: rollback from the first mismatching position, the tail
-past a terminator dropped).
+section 逐 token 推进: rollback from the first mismatching position; "04 · 结构
+化输出", 4.4 推进与终止: the tail past a terminator dropped).
 
 The rule is pinned by what it must preserve: the emitted tokens are
 distributed as the target model's own samples, whatever the drafts (the

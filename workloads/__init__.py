@@ -259,6 +259,19 @@ def c5_spec(variant="b", n_req=64, n_pos=8, V=151936):
                  seed, offset)
 
 
+def spec_drafts(batch, n_pos=8):
+    """Draft tokens for a spec-verify batch (rows request-major, n_pos rows per
+    request): draft token j+1 of a request is the most likely token of its row
+    j (a draft model that agrees with the target's greedy choice), so greedy
+    rows accept every draft and sampled rows accept while their draws hit the
+    mode.  [n_req, n_pos - 1] int32."""
+    z = batch.logits
+    if batch.bf16:
+        z = (z.astype(np.uint32) << 16).view(np.float32)
+    am = np.argmax(z, axis=1).astype(np.int32).reshape(-1, n_pos)
+    return np.ascontiguousarray(am[:, :n_pos - 1])
+
+
 CONFIGS = {
     "c1": c1_tiny, "c2": c2_decode, "c3": c3_penalties, "c4": c4_grammar,
     "c5a": lambda **kw: c5_spec("a", **kw), "c5b": lambda **kw: c5_spec("b", **kw),
