@@ -531,6 +531,9 @@ def bench_outputs(args):
         size=ct.sizeof(bd.LogprobOutputs), mask_token_ids=o_mids.data_ptr(),
         mask_support_logprobs=o_mlp.data_ptr(), mask_lengths=o_mlen.data_ptr(),
         mask_selected_logprobs=o_msel.data_ptr(), mask_statuses=o_mst.data_ptr())
+    ws_need = int(bd.lib.sampler_logprobs_workspace_bytes(B, V, OUT_TOP_N))
+    ws_buf = torch.empty(ws_need + 256, dtype=torch.uint8, device="cuda")
+    ws_ptr = ws_buf.data_ptr() + (-ws_buf.data_ptr()) % 256
     keep, calls = [], {"rows": [], "support": []}
     for j, b in enumerate(sets):
         if b.bf16:
@@ -557,7 +560,8 @@ def bench_outputs(args):
         req_rows = bd.LogprobRequest(size=ct.sizeof(bd.LogprobRequest), basis=cds.LOGPROB_SAMPLED,
                                      selected=ids.data_ptr(), top_n_max=OUT_TOP_N,
                                      top_n=top_n.data_ptr(), token_indptr=d_ind.data_ptr(),
-                                     token_ids=d_tok.data_ptr())
+                                     token_ids=d_tok.data_ptr(), workspace=ws_ptr,
+                                     workspace_bytes=ws_need)
         req_sup = bd.LogprobRequest(size=ct.sizeof(bd.LogprobRequest), basis=cds.LOGPROB_SAMPLED,
                                     selected=ids.data_ptr(), n_mask_rows=R,
                                     mask_rows=d_mask_rows.data_ptr(), mask_cap=OUT_MASK_CAP,

@@ -35,6 +35,7 @@ EXPORTS = [
     "sampler_shard_state_bytes", "sampler_shard_records", "sampler_shard_partial_bytes",
     "sampler_shard_phases",
     "sampler_shard_pass", "sampler_shard_merge", "sampler_spec_accept",
+    "sampler_logprobs_workspace_bytes",
 ]
 
 
@@ -76,6 +77,7 @@ class LogprobRequest(ct.Structure):
         ("top_n_max", ct.c_int32), ("n_mask_rows", ct.c_int32), ("top_n", ct.c_void_p),
         ("token_indptr", ct.c_void_p), ("token_ids", ct.c_void_p), ("mask_rows", ct.c_void_p),
         ("mask_cap", ct.c_int32), ("pad_", ct.c_int32), ("cuts", ct.c_void_p),
+        ("workspace", ct.c_void_p), ("workspace_bytes", ct.c_size_t),
     ]
 
 
@@ -124,6 +126,7 @@ def _load():
         "sampler_shard_pass": ([P, I32, P, ct.c_int, I64, I32, I32, P, I64, P, P, P, P], ct.c_int),
         "sampler_shard_merge": ([P, I32, P, P, I32, P, P, P, P], ct.c_int),
         "sampler_spec_accept": ([I32, I32, P, P, P, P, P, P, P, P], ct.c_int),
+        "sampler_logprobs_workspace_bytes": ([I32, I32, I32], SZ),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -381,7 +384,8 @@ def sample(packed: PackedBatch, logits, *, bitmask=None, row_has_mask=None, work
 
 def logprobs(packed: PackedBatch, logits, *, selected=None, basis=LOGPROB_SAMPLED, top_n_max=0,
              top_n=None, token_indptr=None, token_ids=None, mask_rows=None, mask_cap=0,
-             support_logprobs=True, cuts=None, bitmask=None, row_has_mask=None, stream=None):
+             support_logprobs=True, cuts=None, bitmask=None, row_has_mask=None, stream=None,
+             workspace=True):
     """Further outputs (sampler_logprobs).  Device tensors in, a dict of
     device tensors out: ``next`` [B] (with ``selected``), ``top_idx`` /
     ``top_val`` [B, top_n_max], ``token`` [token_indptr[-1]] (named tokens),
@@ -389,7 +393,9 @@ def logprobs(packed: PackedBatch, logits, *, selected=None, basis=LOGPROB_SAMPLE
     ``mask_lp`` [R, mask_cap] (if ``support_logprobs``), ``mask_len``,
     ``mask_sel`` and ``mask_status`` [R].  ``selected=None``: scoring, no
     draw.  ``cuts``: the kept-set thresholds sample(..., cut=) returned for
-    the same batch (support sets then skip selecting them again)."""
+    the same batch (support sets then skip selecting them again).
+    ``workspace``: True (allocate the slice pass's workspace), a device
+    uint8 tensor, or None/False (one workgroup per row streams the row)."""
     import torch
     B, V = logits.shape
     if (B, V) != (packed.B, packed.V):
@@ -419,11 +425,19 @@ def logprobs(packed: PackedBatch, logits, *, selected=None, basis=LOGPROB_SAMPLE
         res["mask_len"] = torch.empty(R, dtype=torch.int32, device=dev)
         res["mask_sel"] = torch.empty(R, dtype=torch.float32, device=dev)
         res["mask_status"] = torch.empty(R, dtype=torch.int32, device=dev)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None and workspace is not False:
+        need = int(lib.sampler_logprobs_workspace_bytes(B, V, int(top_n_max)))
+        if workspace is True:
+            workspace = torch.empty(need + 16, dtype=torch.uint8, device=dev)
+        ws_ptr = workspace.data_ptr() + (-workspace.data_ptr()) % 16
+        ws_bytes = workspace.numel() - (ws_ptr - workspace.data_ptr())
     req = LogprobRequest(size=ct.sizeof(LogprobRequest), basis=int(basis),
                          selected=ptr(selected), top_n_max=int(top_n_max), n_mask_rows=R,
                          top_n=ptr(top_n), token_indptr=ptr(token_indptr),
                          token_ids=ptr(token_ids), mask_rows=ptr(mask_rows) if R else None,
-                         mask_cap=int(mask_cap), cuts=ptr(cuts))
+                         mask_cap=int(mask_cap), cuts=ptr(cuts), workspace=ws_ptr,
+                         workspace_bytes=ws_bytes)
     out = LogprobOutputs(size=ct.sizeof(LogprobOutputs),
                          next_token_logprobs=ptr(res.get("next")),
                          top_logprobs_idx=ptr(res.get("top_idx")),

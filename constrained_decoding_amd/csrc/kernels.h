@@ -37,6 +37,23 @@ struct SampleArgs {
   unsigned long long* trace;  // 8 words per workgroup of phase timestamps, or nullptr
 };
 
+// Per row and slice of the further outputs' slice pass: the slice's max
+// (lowest id), finite count, flags (1: a NaN or +inf; 2: candidate list
+// overflow), exp-sum against its max in the requested basis, and how many
+// top-N keys it kept.
+struct alignas(16) OutSliceStat {
+  float zm;
+  int32_t am;
+  int32_t nf;
+  uint32_t flags;
+  double se;
+  int32_t nc;
+  int32_t pad;
+};
+static_assert(sizeof(OutSliceStat) == 32, "OutSliceStat layout");
+// tokens per slice of the further outputs' slice pass (whole mask words)
+constexpr int kOutSlice = 16384;
+
 // Further per-row outputs (logprob-outputs kernel, outputs.hip).  Row blocks:
 // one workgroup per row for the chosen token's logprob, the top-N logprobs
 // and the logprobs of named tokens; support blocks: one workgroup per entry
@@ -62,7 +79,13 @@ struct OutputArgs {
   int32_t* sup_len;       // [n_sup]
   float* sup_sel;         // [n_sup] or nullptr
   int32_t* sup_st;        // [n_sup]
+  // slice records (workspace) for the row blocks, or nullptr: the row blocks
+  // then stream their rows themselves
+  OutSliceStat* sl_stat;    // [B][n_slices]
+  unsigned long long* sl_keys;   // [B][n_slices][top_n_max]
+  int32_t n_slices;
 };
+
 
 // ---- vocabulary-parallel protocol (shard.hip) ----------------------------------
 // Phases, run in order: the row statistics, four radix rounds of the top-k
@@ -174,7 +197,8 @@ hipError_t static_workspace(void** ptr, hipStream_t stream);
 hipError_t launch_sample(const SampleArgs& a, bool bf16, bool vec, int algo,
                          const KernelEvents* ev, hipStream_t stream);
 
-// The logprob-outputs kernel (one launch: n_row_blocks + n_sup workgroups).
+// The logprob-outputs kernels: with slice records, the slice pass (B *
+// n_slices workgroups) first; then n_row_blocks + n_sup workgroups.
 hipError_t launch_outputs(const SampleArgs& a, const OutputArgs& o, bool bf16, bool vec,
                           const KernelEvents* ev, hipStream_t stream);
 

@@ -36,6 +36,10 @@ constexpr int kOutK = 16;      // chunks of 4 tokens in flight per thread and pa
 constexpr int kMaxTopN = 256;  // SAMPLER_MAX_TOP_N
 constexpr int kCandCap = 2048; // top-N candidates held in LDS
 
+constexpr int kSliceNT = 256;                                // slice pass workgroup
+constexpr int kSliceChunks = kOutSlice / (4 * kSliceNT);      // 16 chunks of 4 per thread
+constexpr int kMergeCap = 8192;  // slice top-N keys the merge holds in LDS
+
 template <int NT>
 struct OutShared {
   ExactShared<NT> ex;
@@ -43,6 +47,7 @@ struct OutShared {
   float tmax[NT];
   uint32_t cnt;
   uint32_t wt[NT / 64];
+  unsigned long long mlist[kMergeCap];  // the slices' top-N keys, N slots per slice
 };
 
 // z of token t as the sampling kernel sees it: bf16 upcast, mask applied
@@ -216,6 +221,139 @@ __device__ __forceinline__ void sort_desc(unsigned long long* cand, int n) {
   }
 }
 
+// ---- slice pass: per row and 16384-token slice, its statistics and top-N ----
+// One workgroup per slice with the slice in registers: max (lowest id),
+// finite count, exp-sum against the slice max in the requested basis, and
+// the slice's N largest keys: every token at or above the smallest of the
+// waves' ceil(N/W)-th largest thread maxima is a candidate (at least N thread
+// maxima, distinct tokens, reach it), sorted in LDS.  A candidate list over the LDS capacity flags the slice and its row
+// falls back to the row-serial passes.
+template <int NT>
+struct SliceShared {
+  RedScratch<NT> red;
+  unsigned long long cand[kCandCap];
+  uint32_t cnt;
+  float wk[NT / 64];
+};
+
+__device__ __forceinline__ int row_top_n(const OutputArgs& o, int r) {
+  const int ncol = o.top_ids ? o.top_n_max : 0;
+  return (ncol > 0 && o.top_n) ? min(max(o.top_n[r], 0), ncol) : ncol;
+}
+
+template <int NT, bool BF16, bool VEC>
+__global__ __launch_bounds__(NT) void outputs_slice_kernel(const SampleArgs a, const OutputArgs o) {
+  constexpr int KS = kSliceChunks;
+  __shared__ SliceShared<NT> sh;
+  const int Q = o.n_slices;
+  const int r = (int)blockIdx.x / Q, q = (int)blockIdx.x % Q;
+  const int tid = threadIdx.x;
+  const int n_top = row_top_n(o, r);
+  const bool named = o.tok_off && o.tok_off[r + 1] > o.tok_off[r];
+  if (n_top == 0 && !named && !o.next_lp) return;  // nothing asked of this row
+  const RowParams rp = a.rows[r];
+  RowView rv = row_view<BF16>(a, r);
+  const int64_t s0 = (int64_t)q * kOutSlice;
+  if (BF16)
+    rv.b16 += s0;
+  else
+    rv.f32 += s0;
+  if (rv.mrow) rv.mrow += s0 / 32;
+  const int64_t W = min((int64_t)kOutSlice, (int64_t)a.V - s0);
+  float x[KS][4];
+  uint32_t nonfin = 0;
+  load_chunks<NT, KS, BF16, VEC>(rv, 0, W, 0, x, nonfin);
+  // (a NaN or +inf sets nonfin, and such a row's outputs ignore every sum
+  // and list, so the sums and lists below only test against -inf)
+  float zm = CDS_NEG_INF;
+  int32_t am = INT_MAX, nf = 0;
+#pragma unroll
+  for (int i = 0; i < KS; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float v = x[i][k];
+      nf += finite_f(v) ? 1 : 0;
+      if (v > zm) {  // tokens in increasing order per thread: the lowest id wins ties
+        zm = v;
+        am = 4 * (i * NT + tid) + k;
+      }
+    }
+  const float zt = zm;  // the thread's own maximum
+  const bool greedy = (rp.flags & ROW_GREEDY) != 0;
+  const double Tb = (o.basis == 1 || greedy) ? 1.0 : (double)rp.temperature;
+  const float c = (float)(1.0 / Tb) * kLog2e;
+  // exp-sum against the thread's maximum, four terms in fp32 then fp64
+  double st = 0.0;
+  if (zt > CDS_NEG_INF) {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      float p = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        p += x[i][k] > CDS_NEG_INF ? __builtin_amdgcn_exp2f((x[i][k] - zt) * c) : 0.0f;
+      st += (double)p;
+    }
+  }
+  block_argmax<NT>(zm, am, sh.red);
+  nf = block_sum_i32<NT>(nf, sh.red);
+  nonfin = block_or_u32<NT>(nonfin, sh.red);
+  double se = zt > CDS_NEG_INF && zm < CDS_POS_INF
+                  ? st * exp(((double)zt - (double)zm) * (double)(float)(1.0 / Tb))
+                  : 0.0;
+  se = block_sum_f64<NT>(se, sh.red);
+  uint32_t flags = nonfin ? 1u : 0u;
+  int nc = 0;
+  const int n = min(n_top, nf);
+  if (n > 0 && !nonfin) {
+    auto key = [&](float v, int i, int k) -> unsigned long long {
+      return ((unsigned long long)okey(v + 0.0f) << 32) |
+             (uint32_t)~(uint32_t)(s0 + 4 * (i * NT + tid) + k);
+    };
+    // a value bound: each wave's ceil(n/W)-th largest thread maximum (W
+    // waves), the smallest of them -- at least n thread maxima, distinct
+    // tokens, reach it
+    constexpr int NW = NT / 64;
+    const float wk = wave_kth_largest(zt, (n + NW - 1) / NW);
+    if ((tid & 63) == 0) sh.wk[tid >> 6] = wk;
+    __syncthreads();
+    float tz = sh.wk[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) tz = fminf(tz, sh.wk[w]);
+    if (tid == 0) sh.cnt = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < KS; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float v = x[i][k];
+        if (!(v > CDS_NEG_INF && v >= tz)) continue;
+        const uint32_t slot = atomicAdd(&sh.cnt, 1u);
+        if (slot < (uint32_t)kCandCap) sh.cand[slot] = key(v, i, k);
+      }
+    __syncthreads();
+    const int cnt = (int)sh.cnt;
+    if (cnt > kCandCap) {
+      flags |= 2u;
+    } else {
+      sort_desc<NT>(sh.cand, cnt);
+      nc = min(n, cnt);
+      unsigned long long* out = o.sl_keys + ((int64_t)r * Q + q) * o.top_n_max;
+      for (int j = tid; j < nc; j += NT) out[j] = sh.cand[j];
+    }
+  }
+  if (tid == 0) {
+    OutSliceStat st;
+    st.zm = zm;
+    st.am = nf > 0 ? (int32_t)(s0 + am) : INT_MAX;
+    st.nf = nf;
+    st.flags = flags;
+    st.se = se;
+    st.nc = nc;
+    st.pad = 0;
+    o.sl_stat[(int64_t)r * Q + q] = st;
+  }
+}
+
 // ---- row blocks: chosen-token, named-token and top-N logprobs ----------------
 template <int NT, bool BF16, bool VEC>
 __device__ __forceinline__ void row_outputs(const SampleArgs& a, const OutputArgs& o, int r,
@@ -243,7 +381,35 @@ __device__ __forceinline__ void row_outputs(const SampleArgs& a, const OutputArg
   // before the temperature, as for the drawn token's logprob), or the logits
   // before the temperature for every row
   const double Tb = (o.basis == 1 || greedy) ? 1.0 : (double)rp.temperature;
-  const RowLse st = row_stats_lse<NT, BF16, VEC, K>(rv, V, (float)(1.0 / Tb), sh.ex);
+  RowLse st;
+  bool slices = o.sl_stat != nullptr;  // the slice pass summarised the row
+  bool ovf = false;
+  if (slices) {
+    // fold the slices' records: max (lowest id), finite count, flags, and the
+    // exp-sums brought to the row max in fp64
+    const int Q = o.n_slices;
+    const OutSliceStat* S = o.sl_stat + (int64_t)r * Q;
+    float zm = CDS_NEG_INF;
+    int32_t nf = 0;
+    uint32_t fl = 0;
+    for (int q = 0; q < Q; ++q) {
+      zm = S[q].nf > 0 ? fmaxf(zm, S[q].zm) : zm;
+      nf += S[q].nf;
+      fl |= S[q].flags;
+    }
+    double se = 0.0;
+    for (int q = 0; q < Q; ++q)
+      if (S[q].nf > 0) se += S[q].se * exp(((double)S[q].zm - (double)zm) / Tb);
+    st.zm = zm;
+    st.nf = nf;
+    st.nonfin = fl & 1u;
+    st.se = se;
+    st.tmax = CDS_NEG_INF;
+    st.am = INT_MAX;
+    ovf = (fl & 2u) != 0 || (int64_t)Q * o.top_n_max > kMergeCap;
+  } else {
+    st = row_stats_lse<NT, BF16, VEC, K>(rv, V, (float)(1.0 / Tb), sh.ex);
+  }
   const int status = st.nf == 0 ? 2 : (st.nonfin ? 1 : 0);
   double mb = 0.0, lz = 0.0;
   if (status == 0) {
@@ -272,7 +438,45 @@ __device__ __forceinline__ void row_outputs(const SampleArgs& a, const OutputArg
   if (n_top == 0) return;
 
   int n = 0;  // real entries
-  if (status == 0) {
+  if (status == 0 && slices && !ovf) {
+    // the slices' sorted top-N lists, N slots each (zero keys pad them and
+    // sort last); a key's rank in the row is its index in its own list plus
+    // the keys above it in the other lists (binary search), and every key of
+    // the row's top n is in its slice's top n
+    n = min(n_top, st.nf);
+    const int Q = o.n_slices, N = o.top_n_max;
+    const OutSliceStat* S = o.sl_stat + (int64_t)r * Q;
+    const unsigned long long* K0 = o.sl_keys + (int64_t)r * Q * N;
+    for (int j = threadIdx.x; j < Q * N; j += NT) {
+      const int q = j / N, i = j % N;
+      sh.mlist[j] = i < S[q].nc ? K0[j] : 0ull;
+    }
+    __syncthreads();
+    for (int j = threadIdx.x; j < Q * N; j += NT) {
+      const unsigned long long e = sh.mlist[j];
+      if (e == 0ull) continue;
+      const int q = j / N;
+      int rank = j % N;
+      for (int p = 0; p < Q && rank < n; ++p) {
+        if (p == q) continue;
+        const unsigned long long* L = sh.mlist + p * N;
+        int lo = 0, hi = N;  // count of entries > e: the first index with L[i] < e
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (L[mid] > e)
+            lo = mid + 1;
+          else
+            hi = mid;
+        }
+        rank += lo;
+      }
+      if (rank < n) {
+        top_ids[rank] = (int32_t)~(uint32_t)e;
+        top_vals[rank] = lp_of(from_okey((uint32_t)(e >> 32)));
+      }
+    }
+  } else if (status == 0) {
+    if (slices) st = row_stats_lse<NT, BF16, VEC, K>(rv, V, (float)(1.0 / Tb), sh.ex);
     n = min(n_top, st.nf);
     // Candidates: every finite z >= tau, where tau is the n-th largest of the
     // threads' maxima (those n maxima are distinct tokens, so at least n
@@ -481,6 +685,9 @@ static hipError_t launch_out(const SampleArgs& a, const OutputArgs& o, const Ker
   const unsigned grid = (unsigned)o.n_row_blocks + (unsigned)o.n_sup;
   if (grid == 0u) return hipSuccess;
   if (ev && ev->start) (void)hipEventRecord(ev->start, s);
+  if (o.sl_stat && o.n_row_blocks > 0)
+    hipLaunchKernelGGL((outputs_slice_kernel<kSliceNT, BF16, VEC>),
+                       dim3((unsigned)a.B * (unsigned)o.n_slices), dim3(kSliceNT), 0, s, a, o);
   hipLaunchKernelGGL((outputs_kernel<kOutNT, BF16, VEC>), dim3(grid), dim3(kOutNT), 0, s, a, o);
   if (ev && ev->stop) (void)hipEventRecord(ev->stop, s);
   return hipGetLastError();

@@ -644,6 +644,14 @@ int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_
                            out_logprobs, out_status, workspace, ws_bytes, stream, nullptr);
 }
 
+size_t sampler_logprobs_workspace_bytes(int32_t B, int32_t V, int32_t top_n_max) {
+  if (B <= 0 || V <= 0 || B > kMaxB || V > kMaxV || top_n_max < 0 ||
+      top_n_max > SAMPLER_MAX_TOP_N)
+    return 0;
+  const size_t Q = ((size_t)V + kOutSlice - 1) / kOutSlice;
+  return (size_t)B * Q * (sizeof(OutSliceStat) + sizeof(uint64_t) * (size_t)top_n_max);
+}
+
 int sampler_logprobs(const sampler_batch* b, const void* logits, int dtype, int64_t ld,
                      const int32_t* bitmask, int64_t mask_ld, const uint8_t* row_has_mask,
                      const sampler_logprob_request* req, const sampler_logprob_outputs* out,
@@ -716,6 +724,14 @@ int sampler_logprobs(const sampler_batch* b, const void* logits, int dtype, int6
   o.sup_st = out->mask_statuses;
   o.n_row_blocks = (top || named || o.next_lp) ? B : 0;
   if (o.n_row_blocks == 0 && o.n_sup == 0) return SAMPLER_OK;
+  if (req->workspace) {
+    const size_t need = sampler_logprobs_workspace_bytes(B, V, req->top_n_max);
+    if (req->workspace_bytes < need) return SAMPLER_ENOSPC;
+    if (!aligned(req->workspace, 16)) return SAMPLER_EINVAL;
+    o.n_slices = (int32_t)(((int64_t)V + kOutSlice - 1) / kOutSlice);
+    o.sl_stat = static_cast<OutSliceStat*>(req->workspace);
+    o.sl_keys = reinterpret_cast<unsigned long long*>(o.sl_stat + (size_t)B * o.n_slices);
+  }
 
   const size_t elem = bf16 ? 2 : 4;
   const bool vec = aligned(logits, 4 * elem) && (ld % 4 == 0) && (V % 4 == 0);

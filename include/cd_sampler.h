@@ -402,6 +402,14 @@ int sampler_sample_ex(const sampler_batch *b, const void *logits, int dtype,
  *                   set (sampling_mask_batch_indices); a row may appear more
  *                   than once; an index outside [0, B) gives status INVALID.
  *   mask_cap        ids kept per support set.
+ *   workspace       dev, >= sampler_logprobs_workspace_bytes(B, V, top_n_max)
+ *                   bytes, 16-byte aligned, or NULL.  With it the rows are
+ *                   first summarised by 8192-token slices (one workgroup
+ *                   each: statistics and the slice's top-N) and the per-row
+ *                   outputs fold the slices' records; without it one
+ *                   workgroup per row streams the row (slower).  Same results
+ *                   either way (logprobs within rounding).  Not kept between
+ *                   calls; calls that share it must not overlap.
  * Outputs (device; NULL = not written):
  *   next_token_logprobs   float [B]: logprob of selected[r] in the basis
  *                   (needs selected); NaN on an OVERFLOW row or for an id
@@ -456,7 +464,13 @@ typedef struct sampler_logprob_request {
   int32_t mask_cap;
   int32_t pad_;
   const float *cuts;
+  void *workspace;
+  size_t workspace_bytes;
 } sampler_logprob_request;
+
+/* Workspace bytes of sampler_logprobs's slice pass for B rows of V tokens
+ * and top_n_max columns (0 on an invalid size). */
+size_t sampler_logprobs_workspace_bytes(int32_t B, int32_t V, int32_t top_n_max);
 
 typedef struct sampler_logprob_outputs {
   uint32_t size; /* sizeof(sampler_logprob_outputs) as the caller compiled it */

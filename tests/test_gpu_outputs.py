@@ -44,7 +44,8 @@ def _close(a, b, tol=LP_TOL):
     return bool(ok.all()), np.flatnonzero(~ok)
 
 
-def _run(batch, *, basis, top_n, tok_rows, mask_rows, cap, with_selected=True, use_cuts=True):
+def _run(batch, *, basis, top_n, tok_rows, mask_rows, cap, with_selected=True, use_cuts=True,
+         use_ws=True):
     """Pack, transform, sample (fused mask), then sampler_logprobs; returns
     (ids, status, logprobs, dict of host arrays).  use_cuts: the support sets
     take the sampling call's kept-set thresholds (else they select them
@@ -70,7 +71,8 @@ def _run(batch, *, basis, top_n, tok_rows, mask_rows, cap, with_selected=True, u
         token_indptr=torch.from_numpy(indptr).cuda(),
         token_ids=torch.from_numpy(flat.astype(np.int32)).cuda(),
         mask_rows=torch.from_numpy(np.asarray(mask_rows, np.int32)).cuda() if len(mask_rows) else None,
-        mask_cap=cap, cuts=cut if use_cuts else None, bitmask=mask, row_has_mask=rhm)
+        mask_cap=cap, cuts=cut if use_cuts else None, bitmask=mask, row_has_mask=rhm,
+        workspace=use_ws)
     torch.cuda.synchronize()
     host = {k: v.cpu().numpy() for k, v in res.items()}
     return ids.cpu().numpy(), st.cpu().numpy(), lp.cpu().numpy(), host
@@ -180,11 +182,11 @@ def _oracle_member(batch, zs, r):
 
 
 def _case(batch, *, basis, top_n, tok_rows, mask_rows, cap, with_selected=True, use_cuts=True,
-          label=""):
+          use_ws=True, label=""):
     print(f"[case] {label} B={batch.B} V={batch.V} bf16={batch.bf16} basis={basis} "
-          f"cap={cap} selected={with_selected} cuts={use_cuts}", flush=True)
+          f"cap={cap} selected={with_selected} cuts={use_cuts} slices={use_ws}", flush=True)
     gpu = _run(batch, basis=basis, top_n=top_n, tok_rows=tok_rows, mask_rows=mask_rows, cap=cap,
-               with_selected=with_selected, use_cuts=use_cuts)
+               with_selected=with_selected, use_cuts=use_cuts, use_ws=use_ws)
     ids = gpu[0]
     _, zs = run_oracle(batch)
     want = np.zeros(batch.B, bool)
@@ -235,12 +237,14 @@ def _requests(rng, B, V, n_max=40):
     return top_n, tok_rows
 
 
+@pytest.mark.parametrize("use_ws", [True, False])
 @pytest.mark.parametrize("V,bf16", [(5003, False), (20000, False), (20000, True), (7001, True)])
-def test_outputs_small_parity(V, bf16):
+def test_outputs_small_parity(V, bf16, use_ws):
     """Mixed rows (greedy, low T, top-k, top-p, min-p, masks allowing 1 to
     V/2 tokens), ragged V (scalar loads) and V % 4 == 0 (vector loads), fp32
     and bf16 (many ties); both bases; a support set per row plus an index out
-    of range and a repeated row."""
+    of range and a repeated row; the per-row outputs from the slice pass's
+    records and from the row-serial passes."""
     rng = np.random.default_rng(700 + V + bf16)
     B = 24
     batch = _mixed_batch(rng, B, V, bf16=bf16)
@@ -249,7 +253,7 @@ def test_outputs_small_parity(V, bf16):
     # support sets from the sampling call's thresholds, and selected again
     for basis, cuts in ((oracle.BASIS_SAMPLED, True), (oracle.BASIS_ORIGINAL, False)):
         _case(batch, basis=basis, top_n=top_n, tok_rows=tok_rows, mask_rows=mask_rows,
-              cap=V if basis == oracle.BASIS_SAMPLED else 64, use_cuts=cuts,
+              cap=V if basis == oracle.BASIS_SAMPLED else 64, use_cuts=cuts, use_ws=use_ws,
               label=f"small V={V} bf16={bf16}")
 
 
@@ -328,5 +332,6 @@ def test_outputs_top_n_candidate_overflow_and_ties():
                             np.full(B, 0.9, np.float32), np.zeros(B, np.float32),
                             workloads.seeds(rng, B), np.arange(B, dtype=np.uint64))
     top_n = np.array([256, 256, 40, 256, 256, 20, 1, 256], np.int32)
-    _case(batch, basis=oracle.BASIS_SAMPLED, top_n=top_n, tok_rows=[np.array([0, 5])] * B,
-          mask_rows=[0, 1, 4], cap=V, label="candidate overflow")
+    for ws in (True, False):
+        _case(batch, basis=oracle.BASIS_SAMPLED, top_n=top_n, tok_rows=[np.array([0, 5])] * B,
+              mask_rows=[0, 1, 4], cap=V, use_ws=ws, label="candidate overflow")
