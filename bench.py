@@ -531,7 +531,7 @@ def bench_outputs(args):
         size=ct.sizeof(bd.LogprobOutputs), mask_token_ids=o_mids.data_ptr(),
         mask_support_logprobs=o_mlp.data_ptr(), mask_lengths=o_mlen.data_ptr(),
         mask_selected_logprobs=o_msel.data_ptr(), mask_statuses=o_mst.data_ptr())
-    ws_need = int(bd.lib.sampler_logprobs_workspace_bytes(B, V, OUT_TOP_N))
+    ws_need = int(bd.lib.sampler_logprobs_workspace_bytes(B, V, OUT_TOP_N, R))
     ws_buf = torch.empty(ws_need + 256, dtype=torch.uint8, device="cuda")
     ws_ptr = ws_buf.data_ptr() + (-ws_buf.data_ptr()) % 256
     keep, calls = [], {"rows": [], "support": []}
@@ -565,7 +565,8 @@ def bench_outputs(args):
         req_sup = bd.LogprobRequest(size=ct.sizeof(bd.LogprobRequest), basis=cds.LOGPROB_SAMPLED,
                                     selected=ids.data_ptr(), n_mask_rows=R,
                                     mask_rows=d_mask_rows.data_ptr(), mask_cap=OUT_MASK_CAP,
-                                    cuts=cut.data_ptr())
+                                    cuts=cut.data_ptr(), workspace=ws_ptr,
+                                    workspace_bytes=ws_need)
         keep.append((x, pk, m, rh, ids, cut, d_ind, d_tok, req_rows, req_sup))
         base = (ct.byref(pk.batch), x.data_ptr(), x.stride(0),
                 None if m is None else m.data_ptr(), 0 if m is None else m.stride(0),
@@ -651,7 +652,7 @@ def bench_outputs(args):
         "config": {"workload": WORKLOAD_NAMES[args.config] + "; further outputs",
                    "B": B, "V": V, "input_sets": len(sets), "top_n": OUT_TOP_N,
                    "named_tokens_per_row": OUT_NAMED},
-        "roofline": {"bound": "hbm", "kernel": "outputs_kernel", "achieved": round(achieved, 1),
+        "roofline": {"bound": "hbm", "kernel": "outputs_slice_kernel+outputs_kernel", "achieved": round(achieved, 1),
                      "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBS, 4),
                      "traffic": measured_traffic(args.config, "outputs_kernel"),

@@ -126,7 +126,7 @@ def _load():
         "sampler_shard_pass": ([P, I32, P, ct.c_int, I64, I32, I32, P, I64, P, P, P, P], ct.c_int),
         "sampler_shard_merge": ([P, I32, P, P, I32, P, P, P, P], ct.c_int),
         "sampler_spec_accept": ([I32, I32, P, P, P, P, P, P, P, P], ct.c_int),
-        "sampler_logprobs_workspace_bytes": ([I32, I32, I32], SZ),
+        "sampler_logprobs_workspace_bytes": ([I32, I32, I32, I32], SZ),
     }
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -394,8 +394,9 @@ def logprobs(packed: PackedBatch, logits, *, selected=None, basis=LOGPROB_SAMPLE
     ``mask_sel`` and ``mask_status`` [R].  ``selected=None``: scoring, no
     draw.  ``cuts``: the kept-set thresholds sample(..., cut=) returned for
     the same batch (support sets then skip selecting them again).
-    ``workspace``: True (allocate the slice pass's workspace), a device
-    uint8 tensor, or None/False (one workgroup per row streams the row)."""
+    ``workspace``: True (allocate the slice passes' workspace), a device
+    uint8 tensor, or None/False (one workgroup per row, or per support row,
+    streams the row)."""
     import torch
     B, V = logits.shape
     if (B, V) != (packed.B, packed.V):
@@ -427,7 +428,7 @@ def logprobs(packed: PackedBatch, logits, *, selected=None, basis=LOGPROB_SAMPLE
         res["mask_status"] = torch.empty(R, dtype=torch.int32, device=dev)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None and workspace is not False:
-        need = int(lib.sampler_logprobs_workspace_bytes(B, V, int(top_n_max)))
+        need = int(lib.sampler_logprobs_workspace_bytes(B, V, int(top_n_max), R))
         if workspace is True:
             workspace = torch.empty(need + 16, dtype=torch.uint8, device=dev)
         ws_ptr = workspace.data_ptr() + (-workspace.data_ptr()) % 16

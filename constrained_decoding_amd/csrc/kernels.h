@@ -54,6 +54,23 @@ static_assert(sizeof(OutSliceStat) == 32, "OutSliceStat layout");
 // tokens per slice of the further outputs' slice pass (whole mask words)
 constexpr int kOutSlice = 16384;
 
+// Record of one slice of a support row (support sets from the sampling
+// call's thresholds, by slices): the slice's largest finite z and the lowest
+// id holding it, its finite and kept (z >= threshold) token counts, the kept
+// tokens' sum of exp((z - zm) / T), and whether a NaN or +inf was seen.
+struct alignas(16) SupSliceStat {
+  float zm;
+  int32_t am;
+  int32_t nf;
+  int32_t cnt;
+  double st;
+  uint32_t nonfin;
+  uint32_t pad;
+};
+static_assert(sizeof(SupSliceStat) == 32, "SupSliceStat layout");
+// tokens per support slice (whole mask words)
+constexpr int kSupSlice = 4096;
+
 // Further per-row outputs (logprob-outputs kernel, outputs.hip).  Row blocks:
 // one workgroup per row for the chosen token's logprob, the top-N logprobs
 // and the logprobs of named tokens; support blocks: one workgroup per entry
@@ -84,6 +101,10 @@ struct OutputArgs {
   OutSliceStat* sl_stat;    // [B][n_slices]
   unsigned long long* sl_keys;   // [B][n_slices][top_n_max]
   int32_t n_slices;
+  // support slice records (workspace; needs cuts), or nullptr: one
+  // workgroup per support row then streams the row itself
+  int32_t n_sup_slices;
+  SupSliceStat* sup_stat;   // [n_sup][n_sup_slices]
 };
 
 

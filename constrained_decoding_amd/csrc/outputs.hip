@@ -10,17 +10,20 @@
 // temperature; section LogitsProcessor 与 LogitsProcessorOutput: scoring
 // requests take logprobs of the same preprocessed logits with no draw.
 //
-// One launch.  Row blocks (one workgroup per row) compute the row's max and
-// normaliser in the requested basis in one pass (a running sum per thread),
-// the chosen and named tokens' logprobs by direct reads, and the top-N in a
-// second pass: every token at or above the N-th largest of the threads'
-// maxima goes to an LDS candidate list, which a bitonic sort orders (an exact
-// radix select on the fp32 order key, ties broken by id, if the list would
-// overflow).  Support blocks (one workgroup per
-// requested row) find the row's value threshold with the exact path's
-// selection (row_cut), sum the kept mass, and write the kept tokens in id
-// order by a block-wide prefix sum per chunk.  Every pass streams the row;
-// after the first, it comes from L2 / the last-level cache.
+// Row blocks (one workgroup per row) give the chosen and named tokens'
+// logprobs and the top-N.  With a workspace, a slice pass first summarises
+// every 16384-token slice (maximum, normaliser in the requested basis, the
+// slice's top-N keys) and the row blocks fold those records; without one, a
+// row block streams its row: maximum and normaliser in one pass, then the
+// top-N from an LDS candidate list of every token at or above the N-th
+// largest of the threads' maxima, sorted by a bitonic network (an exact radix
+// select on the fp32 order key, ties broken by id, if the list would
+// overflow).  Support sets: with the sampling call's thresholds and a
+// workspace, one pass over 4096-token slices records counts and kept mass
+// and a second writes each slice's kept tokens in id order at its offset;
+// otherwise one workgroup per support row finds the threshold with the exact
+// path's selection (row_cut) when none was given, sums the kept mass, and
+// writes the kept tokens by a block-wide prefix sum per chunk.
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -670,6 +673,209 @@ __device__ __forceinline__ void support_outputs(const SampleArgs& a, const Outpu
   finish(min(cnt, cap), cnt > cap ? 1 : 0, sel);
 }
 
+// ---- support sets by slices ----------------------------------------------------
+// With the sampling call's thresholds and a workspace, a support request is
+// two launches over (support row, 4096-token slice) workgroups instead of one
+// workgroup per row: the first records each slice's statistics
+// (SupSliceStat); the second folds its row's records -- every wave of every
+// workgroup of the row in the same fixed order, so all agree bit for bit on
+// the row's maximum, counts and kept mass -- and writes the slice's kept
+// tokens in id order after the kept tokens of the slices before it.
+constexpr int kSupNT = 256;
+constexpr int kSupChunks = kSupSlice / (4 * kSupNT);  // chunks of 4 tokens per thread
+
+template <int NT, bool BF16, bool VEC>
+__global__ __launch_bounds__(NT) void support_stats_kernel(const SampleArgs a, const OutputArgs o) {
+  __shared__ RedScratch<NT> red;
+  const int Qs = o.n_sup_slices;
+  const int j = (int)(blockIdx.x / (unsigned)Qs), q = (int)(blockIdx.x % (unsigned)Qs);
+  const int r = o.sup_rows[j];
+  if (r < 0 || r >= a.B) return;  // the write pass reports it
+  const RowParams rp = a.rows[r];
+  const RowView rv = row_view<BF16>(a, r);
+  const int64_t s0 = (int64_t)q * kSupSlice, s1 = min(s0 + (int64_t)kSupSlice, (int64_t)a.V);
+  float x[kSupChunks][4];
+  uint32_t nonfin = 0u;
+  load_chunks<NT, kSupChunks, BF16, VEC>(rv, s0, s1, 0, x, nonfin);
+  const bool greedy = (rp.flags & ROW_GREEDY) != 0;
+  const float cut = greedy ? CDS_POS_INF : o.cuts[r];
+  // thread: largest finite z and its lowest id, finite and kept counts
+  float mt = CDS_NEG_INF;
+  int32_t at = INT_MAX, nf = 0, cnt = 0;
+#pragma unroll
+  for (int i = 0; i < kSupChunks; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float v = x[i][k];
+      const bool fin = finite_f(v);
+      nf += fin ? 1 : 0;
+      cnt += (fin && v >= cut) ? 1 : 0;
+      if (fin && v > mt) {  // ids increase along (i, k): the first one stays
+        mt = v;
+        at = (int32_t)(s0 + 4 * ((int64_t)i * NT + threadIdx.x) + k);
+      }
+    }
+  float zm = mt;
+  int32_t am = at;
+  block_argmax<NT>(zm, am, red);
+  const uint64_t counts = block_sum_u64<NT>((uint64_t)(uint32_t)nf | ((uint64_t)(uint32_t)cnt << 32), red);
+  const uint32_t nonf = block_or_u32<NT>(nonfin, red);
+  // kept mass relative to the slice's largest z (which is kept if anything is)
+  double st = 0.0;
+  if (!greedy && zm > CDS_NEG_INF) {
+    const float c = (float)(1.0 / (double)rp.temperature) * kLog2e;
+#pragma unroll
+    for (int i = 0; i < kSupChunks; ++i) {
+      float part = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        part += (finite_f(x[i][k]) && x[i][k] >= cut) ? exp2f((x[i][k] - zm) * c) : 0.0f;
+      st += (double)part;
+    }
+  }
+  st = block_sum_f64<NT>(st, red);
+  if (threadIdx.x == 0) {
+    SupSliceStat rec;
+    rec.zm = zm;
+    rec.am = am;
+    rec.nf = (int32_t)(uint32_t)counts;
+    rec.cnt = (int32_t)(uint32_t)(counts >> 32);
+    rec.st = st;
+    rec.nonfin = nonf;
+    rec.pad = 0u;
+    o.sup_stat[(size_t)j * (size_t)Qs + (size_t)q] = rec;
+  }
+}
+
+template <int NT, bool BF16, bool VEC>
+__global__ __launch_bounds__(NT) void support_write_kernel(const SampleArgs a, const OutputArgs o) {
+  __shared__ uint32_t wt[kSupChunks][NT / 64];
+  const int Qs = o.n_sup_slices;
+  const int j = (int)(blockIdx.x / (unsigned)Qs), q = (int)(blockIdx.x % (unsigned)Qs);
+  const int cap = o.sup_cap;
+  const float qnan = __builtin_nanf("");
+  const bool lead = q == 0 && threadIdx.x == 0;  // reports the row
+  auto finish = [&](int len, int status, float sel) {
+    if (lead) {
+      o.sup_len[j] = len;
+      o.sup_st[j] = status;
+      if (o.sup_sel) o.sup_sel[j] = sel;
+    }
+  };
+  const int r = o.sup_rows[j];
+  if (r < 0 || r >= a.B) {
+    finish(0, 2, qnan);
+    return;
+  }
+  const RowParams rp = a.rows[r];
+  const RowView rv = row_view<BF16>(a, r);
+  // fold the row's records, each wave on its own (no barrier)
+  const SupSliceStat* rec = o.sup_stat + (size_t)j * (size_t)Qs;
+  const int lane = threadIdx.x & 63;
+  struct ZA {
+    float z;
+    int32_t a;
+  };
+  ZA za{CDS_NEG_INF, INT_MAX};
+  int32_t nf = 0, cnt = 0, before = 0;
+  uint32_t nonfin = 0u;
+  for (int k = lane; k < Qs; k += 64) {
+    const SupSliceStat sr = rec[k];
+    if (sr.zm > za.z || (sr.zm == za.z && sr.am < za.a)) za = ZA{sr.zm, sr.am};
+    nf += sr.nf;
+    cnt += sr.cnt;
+    before += k < q ? sr.cnt : 0;
+    nonfin |= sr.nonfin;
+  }
+  za = wave_allreduce(za, [](const ZA& p, const ZA& u) {
+    return (u.z > p.z || (u.z == p.z && u.a < p.a)) ? u : p;
+  });
+  nf = wave_allreduce(nf, [](int32_t u, int32_t v) { return u + v; });
+  cnt = wave_allreduce(cnt, [](int32_t u, int32_t v) { return u + v; });
+  before = wave_allreduce(before, [](int32_t u, int32_t v) { return u + v; });
+  nonfin = wave_allreduce(nonfin, [](uint32_t u, uint32_t v) { return u | v; });
+  if (nf == 0 || nonfin) {  // no distribution
+    finish(0, 2, qnan);
+    return;
+  }
+  const int64_t tsel = o.sel_ids ? (int64_t)o.sel_ids[r] : -1;
+  const bool has_sel = o.sel_ids && tsel >= 0 && tsel < a.V;
+  if ((rp.flags & ROW_GREEDY) != 0) {  // the argmax alone
+    if (lead && cap > 0) {
+      if (o.sup_ids) o.sup_ids[(int64_t)j * cap] = za.a;
+      if (o.sup_lp) o.sup_lp[(int64_t)j * cap] = 0.0f;
+    }
+    finish(min(1, cap), cap >= 1 ? 0 : 1,
+           !has_sel ? qnan : (tsel == (int64_t)za.a ? 0.0f : CDS_NEG_INF));
+    return;
+  }
+  const double Td = (double)rp.temperature;
+  const double invT = 1.0 / Td;
+  double mass = 0.0;
+  for (int k = lane; k < Qs; k += 64) {
+    const SupSliceStat sr = rec[k];
+    if (sr.zm > CDS_NEG_INF) mass += sr.st * exp(((double)sr.zm - (double)za.z) * invT);
+  }
+  mass = wave_allreduce(mass, [](double u, double v) { return u + v; });
+  const double m = (double)za.z / Td;
+  const double lmass = log(mass);
+  const float zcut = o.cuts[r];
+  auto lp_s = [&](float z) -> float { return (float)((double)z / Td - m - lmass); };
+  if (lead) {
+    float sel = qnan;
+    if (has_sel) {
+      const float z = token_z<BF16>(rv, tsel);
+      sel = (z != CDS_NEG_INF && z >= zcut) ? lp_s(z) : CDS_NEG_INF;
+    }
+    o.sup_len[j] = min(cnt, cap);
+    o.sup_st[j] = cnt > cap ? 1 : 0;
+    if (o.sup_sel) o.sup_sel[j] = sel;
+  }
+  if (cap == 0 || !o.sup_ids || before >= cap) return;  // uniform over the workgroup
+  // this slice's kept tokens, in id order: chunk, then thread, then token
+  const int64_t s0 = (int64_t)q * kSupSlice, s1 = min(s0 + (int64_t)kSupSlice, (int64_t)a.V);
+  float x[kSupChunks][4];
+  uint32_t nf2 = 0u;
+  load_chunks<NT, kSupChunks, BF16, VEC>(rv, s0, s1, 0, x, nf2);
+  const int w = threadIdx.x >> 6;
+  uint32_t excl[kSupChunks];
+#pragma unroll
+  for (int i = 0; i < kSupChunks; ++i) {
+    uint32_t e = 0u, tot = 0u;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const unsigned long long bal = __ballot(x[i][k] != CDS_NEG_INF && x[i][k] >= zcut);
+      e += __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+      tot += (uint32_t)__popcll(bal);
+    }
+    excl[i] = e;
+    if (lane == 0) wt[i][w] = tot;
+  }
+  __syncthreads();
+  uint32_t base = (uint32_t)before;
+  int32_t* ids_out = o.sup_ids + (int64_t)j * cap;
+  float* lp_out = o.sup_lp ? o.sup_lp + (int64_t)j * cap : nullptr;
+#pragma unroll
+  for (int i = 0; i < kSupChunks; ++i) {
+    uint32_t pos = base + excl[i];
+#pragma unroll
+    for (int w2 = 0; w2 < NT / 64; ++w2) {
+      const uint32_t tw = wt[i][w2];
+      pos += w2 < w ? tw : 0u;
+      base += tw;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (x[i][k] != CDS_NEG_INF && x[i][k] >= zcut) {
+        if (pos < (uint32_t)cap) {
+          ids_out[pos] = (int32_t)(s0 + 4 * ((int64_t)i * NT + threadIdx.x) + k);
+          if (lp_out) lp_out[pos] = lp_s(x[i][k]);
+        }
+        ++pos;
+      }
+  }
+}
+
 template <int NT, bool BF16, bool VEC>
 __global__ __launch_bounds__(NT) void outputs_kernel(const SampleArgs a, const OutputArgs o) {
   __shared__ OutShared<NT> sh;
@@ -682,13 +888,23 @@ __global__ __launch_bounds__(NT) void outputs_kernel(const SampleArgs a, const O
 template <bool BF16, bool VEC>
 static hipError_t launch_out(const SampleArgs& a, const OutputArgs& o, const KernelEvents* ev,
                              hipStream_t s) {
-  const unsigned grid = (unsigned)o.n_row_blocks + (unsigned)o.n_sup;
-  if (grid == 0u) return hipSuccess;
+  // support rows by slices (their own launches) or one block each here
+  const bool sup_sliced = o.sup_stat && o.n_sup > 0;
+  const unsigned grid = (unsigned)o.n_row_blocks + (sup_sliced ? 0u : (unsigned)o.n_sup);
+  if (grid == 0u && !sup_sliced) return hipSuccess;
   if (ev && ev->start) (void)hipEventRecord(ev->start, s);
   if (o.sl_stat && o.n_row_blocks > 0)
     hipLaunchKernelGGL((outputs_slice_kernel<kSliceNT, BF16, VEC>),
                        dim3((unsigned)a.B * (unsigned)o.n_slices), dim3(kSliceNT), 0, s, a, o);
-  hipLaunchKernelGGL((outputs_kernel<kOutNT, BF16, VEC>), dim3(grid), dim3(kOutNT), 0, s, a, o);
+  if (grid > 0u)
+    hipLaunchKernelGGL((outputs_kernel<kOutNT, BF16, VEC>), dim3(grid), dim3(kOutNT), 0, s, a, o);
+  if (sup_sliced) {
+    const unsigned sgrid = (unsigned)o.n_sup * (unsigned)o.n_sup_slices;
+    hipLaunchKernelGGL((support_stats_kernel<kSupNT, BF16, VEC>), dim3(sgrid), dim3(kSupNT), 0, s,
+                       a, o);
+    hipLaunchKernelGGL((support_write_kernel<kSupNT, BF16, VEC>), dim3(sgrid), dim3(kSupNT), 0, s,
+                       a, o);
+  }
   if (ev && ev->stop) (void)hipEventRecord(ev->stop, s);
   return hipGetLastError();
 }

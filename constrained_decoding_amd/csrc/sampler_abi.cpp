@@ -644,12 +644,25 @@ int sampler_sample(const sampler_batch* b, const void* logits, int dtype, int64_
                            out_logprobs, out_status, workspace, ws_bytes, stream, nullptr);
 }
 
-size_t sampler_logprobs_workspace_bytes(int32_t B, int32_t V, int32_t top_n_max) {
-  if (B <= 0 || V <= 0 || B > kMaxB || V > kMaxV || top_n_max < 0 ||
-      top_n_max > SAMPLER_MAX_TOP_N)
-    return 0;
+namespace {
+// sampler_logprobs workspace: the row slice records and keys, then (16-byte
+// aligned) the support slice records
+size_t logprobs_rows_bytes(int32_t B, int32_t V, int32_t top_n_max) {
   const size_t Q = ((size_t)V + kOutSlice - 1) / kOutSlice;
-  return (size_t)B * Q * (sizeof(OutSliceStat) + sizeof(uint64_t) * (size_t)top_n_max);
+  const size_t n = (size_t)B * Q * (sizeof(OutSliceStat) + sizeof(uint64_t) * (size_t)top_n_max);
+  return (n + 15) / 16 * 16;
+}
+int32_t support_slices(int32_t V) { return (int32_t)(((int64_t)V + kSupSlice - 1) / kSupSlice); }
+}  // namespace
+
+size_t sampler_logprobs_workspace_bytes(int32_t B, int32_t V, int32_t top_n_max,
+                                        int32_t n_mask_rows) {
+  if (B <= 0 || V <= 0 || B > kMaxB || V > kMaxV || top_n_max < 0 ||
+      top_n_max > SAMPLER_MAX_TOP_N || n_mask_rows < 0 ||
+      (int64_t)n_mask_rows * support_slices(V) > (int64_t)INT32_MAX)
+    return 0;
+  return logprobs_rows_bytes(B, V, top_n_max) +
+         (size_t)n_mask_rows * (size_t)support_slices(V) * sizeof(SupSliceStat);
 }
 
 int sampler_logprobs(const sampler_batch* b, const void* logits, int dtype, int64_t ld,
@@ -725,12 +738,19 @@ int sampler_logprobs(const sampler_batch* b, const void* logits, int dtype, int6
   o.n_row_blocks = (top || named || o.next_lp) ? B : 0;
   if (o.n_row_blocks == 0 && o.n_sup == 0) return SAMPLER_OK;
   if (req->workspace) {
-    const size_t need = sampler_logprobs_workspace_bytes(B, V, req->top_n_max);
+    const size_t need =
+        sampler_logprobs_workspace_bytes(B, V, req->top_n_max, mask ? req->n_mask_rows : 0);
+    if (need == 0) return SAMPLER_ERANGE;
     if (req->workspace_bytes < need) return SAMPLER_ENOSPC;
     if (!aligned(req->workspace, 16)) return SAMPLER_EINVAL;
     o.n_slices = (int32_t)(((int64_t)V + kOutSlice - 1) / kOutSlice);
     o.sl_stat = static_cast<OutSliceStat*>(req->workspace);
     o.sl_keys = reinterpret_cast<unsigned long long*>(o.sl_stat + (size_t)B * o.n_slices);
+    if (mask && req->cuts) {  // support sets by slices need the thresholds
+      o.n_sup_slices = support_slices(V);
+      o.sup_stat = reinterpret_cast<SupSliceStat*>(static_cast<unsigned char*>(req->workspace) +
+                                                   logprobs_rows_bytes(B, V, req->top_n_max));
+    }
   }
 
   const size_t elem = bf16 ? 2 : 4;

@@ -396,20 +396,23 @@ int sampler_sample_ex(const sampler_batch *b, const void *logits, int dtype,
  *                   (token_ids_logprobs, CSR).
  *   cuts            float [B]: the thresholds sampler_sample_ex returned
  *                   (option `cut`) for the same batch and logits: support
- *                   sets then take two passes over their row; NULL: the
- *                   threshold is selected again (several more passes).
+ *                   sets then take two passes over their row (with a
+ *                   workspace, by 4096-token slices, one workgroup each);
+ *                   NULL: the threshold is selected again (several more
+ *                   passes, one workgroup per support row).
  *   mask_rows       int32 [n_mask_rows]: the rows that return their support
  *                   set (sampling_mask_batch_indices); a row may appear more
  *                   than once; an index outside [0, B) gives status INVALID.
  *   mask_cap        ids kept per support set.
- *   workspace       dev, >= sampler_logprobs_workspace_bytes(B, V, top_n_max)
- *                   bytes, 16-byte aligned, or NULL.  With it the rows are
- *                   first summarised by 8192-token slices (one workgroup
- *                   each: statistics and the slice's top-N) and the per-row
- *                   outputs fold the slices' records; without it one
- *                   workgroup per row streams the row (slower).  Same results
- *                   either way (logprobs within rounding).  Not kept between
- *                   calls; calls that share it must not overlap.
+ *   workspace       dev, >= sampler_logprobs_workspace_bytes(B, V,
+ *                   top_n_max, n_mask_rows) bytes, 16-byte aligned, or NULL.
+ *                   With it the rows are first summarised by 16384-token
+ *                   slices (one workgroup each: statistics and the slice's
+ *                   top-N) and the per-row outputs fold the slices' records,
+ *                   and support sets with `cuts` are made by slices; without
+ *                   it one workgroup per row streams the row (slower).  Same
+ *                   results either way (logprobs within rounding).  Not kept
+ *                   between calls; calls that share it must not overlap.
  * Outputs (device; NULL = not written):
  *   next_token_logprobs   float [B]: logprob of selected[r] in the basis
  *                   (needs selected); NaN on an OVERFLOW row or for an id
@@ -441,12 +444,13 @@ int sampler_sample_ex(const sampler_batch *b, const void *logits, int dtype,
  *                   reaches one decision ([SGL] "LogitsProcessorOutput").
  *   mask_lengths and mask_statuses are required when n_mask_rows > 0, and
  *   mask_token_ids when mask_cap > 0 as well.
- * Other arguments as sampler_sample; no workspace.  Errors: an inconsistent
- * request (an output without its input, a missing required output, a record
- * of another size, basis or top_n_max out of range) -> SAMPLER_EINVAL;
- * launch failure -> SAMPLER_EHIP.  Nothing asked for: SAMPLER_OK, no launch.
- * Cost: one workgroup per row (when a per-row output is asked for) plus one
- * per support row, each streaming its row several times.
+ * Other arguments as sampler_sample.  Errors: an inconsistent request (an
+ * output without its input, a missing required output, a record of another
+ * size, basis or top_n_max out of range, a misaligned workspace) ->
+ * SAMPLER_EINVAL; a workspace below the size query -> SAMPLER_ENOSPC;
+ * n_mask_rows times the 4096-token slices of a row beyond 2^31 - 1 with a
+ * workspace -> SAMPLER_ERANGE; launch failure -> SAMPLER_EHIP.  Nothing asked
+ * for: SAMPLER_OK, no launch.
  * -------------------------------------------------------------------------- */
 #define SAMPLER_LOGPROB_SAMPLED 0
 #define SAMPLER_LOGPROB_ORIGINAL 1
@@ -468,9 +472,11 @@ typedef struct sampler_logprob_request {
   size_t workspace_bytes;
 } sampler_logprob_request;
 
-/* Workspace bytes of sampler_logprobs's slice pass for B rows of V tokens
- * and top_n_max columns (0 on an invalid size). */
-size_t sampler_logprobs_workspace_bytes(int32_t B, int32_t V, int32_t top_n_max);
+/* Workspace bytes of sampler_logprobs's slice passes for B rows of V
+ * tokens, top_n_max columns and n_mask_rows support rows (0 on an invalid
+ * size). */
+size_t sampler_logprobs_workspace_bytes(int32_t B, int32_t V, int32_t top_n_max,
+                                        int32_t n_mask_rows);
 
 typedef struct sampler_logprob_outputs {
   uint32_t size; /* sizeof(sampler_logprob_outputs) as the caller compiled it */

@@ -316,6 +316,20 @@ def test_logprobs_request_validation(cds):
     ]
     for req, out in bad:
         assert call(req, out) == -1, (req, out)
+    # the workspace: row slice records and keys (16384-token slices), then
+    # the support slice records (4096-token slices), 16-byte aligned
+    rows = -(-4 * 1 * (32 + 8 * 5) // 16) * 16
+    ws = cds.lib.sampler_logprobs_workspace_bytes
+    assert ws(4, 1000, 5, 0) == rows
+    assert ws(4, 1000, 5, 3) == rows + 3 * 1 * 32
+    assert ws(4, 151936, 0, 16) == -(-4 * 10 * 32 // 16) * 16 + 16 * 38 * 32
+    assert ws(4, 1000, 5, -1) == 0 and ws(4, 1000, cds.MAX_TOP_N + 1, 0) == 0
+    assert ws(0, 1000, 5, 0) == 0
+    sup_req = {"n_mask_rows": 3, "mask_rows": P, "mask_cap": 4, "cuts": P, "workspace": P}
+    sup_out = {"mask_token_ids": P, "mask_lengths": P, "mask_statuses": P}
+    need = ws(4, 1000, 0, 3)
+    assert call(dict(sup_req, workspace_bytes=need - 16), sup_out) == -3   # too small
+    assert call(dict(sup_req, workspace=P + 8, workspace_bytes=need), sup_out) == -1  # misaligned
     # a record of another size
     r = cds.LogprobRequest(size=ct.sizeof(cds.LogprobRequest))
     o = cds.LogprobOutputs(size=ct.sizeof(cds.LogprobOutputs) - 8)

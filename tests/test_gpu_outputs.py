@@ -250,11 +250,13 @@ def test_outputs_small_parity(V, bf16, use_ws):
     batch = _mixed_batch(rng, B, V, bf16=bf16)
     top_n, tok_rows = _requests(rng, B, V)
     mask_rows = list(range(B)) + [B, -3, 5]
-    # support sets from the sampling call's thresholds, and selected again
-    for basis, cuts in ((oracle.BASIS_SAMPLED, True), (oracle.BASIS_ORIGINAL, False)):
+    # support sets from the sampling call's thresholds (by slices with the
+    # workspace: whole, and cut at 64 ids across slice boundaries), and with
+    # the thresholds selected again
+    for basis, cuts, cap in ((oracle.BASIS_SAMPLED, True, V), (oracle.BASIS_SAMPLED, True, 64),
+                             (oracle.BASIS_ORIGINAL, False, 64)):
         _case(batch, basis=basis, top_n=top_n, tok_rows=tok_rows, mask_rows=mask_rows,
-              cap=V if basis == oracle.BASIS_SAMPLED else 64, use_cuts=cuts, use_ws=use_ws,
-              label=f"small V={V} bf16={bf16}")
+              cap=cap, use_cuts=cuts, use_ws=use_ws, label=f"small V={V} bf16={bf16}")
 
 
 def test_outputs_scoring_without_draw():
