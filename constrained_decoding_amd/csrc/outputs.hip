@@ -231,9 +231,35 @@ __device__ __forceinline__ void sort_desc(unsigned long long* cand, int n) {
 // waves' ceil(N/W)-th largest thread maxima is a candidate (at least N thread
 // maxima, distinct tokens, reach it), sorted in LDS.  A candidate list over the LDS capacity flags the slice and its row
 // falls back to the row-serial passes.
+// A slice's running statistics: largest value, the lowest index holding it,
+// the exp-sum relative to that value, the non-finite flag, the finite count.
+struct OutStat {
+  float m;
+  int32_t a;
+  double s;
+  uint32_t nonfin;
+  int32_t nf;
+};
+
+__device__ __forceinline__ OutStat out_stat_merge(const OutStat& x, const OutStat& y, float c) {
+  OutStat r;
+  r.m = fmaxf(x.m, y.m);
+  r.a = x.m > y.m ? x.a : (y.m > x.m ? y.a : min(x.a, y.a));
+  const double sx = x.m == CDS_NEG_INF ? 0.0 : x.s * (double)__builtin_amdgcn_exp2f((x.m - r.m) * c);
+  const double sy = y.m == CDS_NEG_INF ? 0.0 : y.s * (double)__builtin_amdgcn_exp2f((y.m - r.m) * c);
+  r.s = sx + sy;
+  r.nonfin = x.nonfin | y.nonfin;
+  r.nf = x.nf + y.nf;
+  return r;
+}
+
 template <int NT>
 struct SliceShared {
-  RedScratch<NT> red;
+  float m[NT / 64];
+  int32_t a[NT / 64];
+  double s[NT / 64];
+  uint32_t nonfin[NT / 64];
+  int32_t nf[NT / 64];
   unsigned long long cand[kCandCap];
   uint32_t cnt;
   float wk[NT / 64];
@@ -244,13 +270,130 @@ __device__ __forceinline__ int row_top_n(const OutputArgs& o, int r) {
   return (ncol > 0 && o.top_n) ? min(max(o.top_n[r], 0), ncol) : ncol;
 }
 
+// The records of row r, slice q (tokens s0 ..), from the slice's values:
+// thread chunk i holds tokens s0 + 4*(i*NT + tid) .. +3 (disallowed and
+// out-of-range tokens -inf; nonfin: a NaN or +inf among the allowed ones).
+// Statistics and the slice's n_top largest keys.
+template <int NT, int KS>
+__device__ __forceinline__ void slice_summary(const OutputArgs& o, int r, int q, int64_t s0,
+                                              const float (&x)[KS][4], uint32_t nonfin,
+                                              int n_top, bool greedy, float temperature,
+                                              SliceShared<NT>& sh) {
+  const int Q = o.n_slices;
+  const int tid = threadIdx.x;
+  // (a NaN or +inf sets nonfin, and such a row's outputs ignore every sum
+  // and list, so the sums and lists below only test against -inf)
+  OutStat t{CDS_NEG_INF, INT_MAX, 0.0, nonfin, 0};
+#pragma unroll
+  for (int i = 0; i < KS; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const float v = x[i][k];
+      t.nf += finite_f(v) ? 1 : 0;
+      if (v > t.m) {  // tokens in increasing order per thread: the lowest id wins ties
+        t.m = v;
+        t.a = 4 * (i * NT + tid) + k;
+      }
+    }
+  const float zt = t.m;  // the thread's own maximum
+  const double Tb = (o.basis == 1 || greedy) ? 1.0 : (double)temperature;
+  const float c = (float)(1.0 / Tb) * kLog2e;
+  // exp-sum against the thread's maximum, four terms in fp32 then fp64
+  if (zt > CDS_NEG_INF) {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      float p = 0.0f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k)
+        p += x[i][k] > CDS_NEG_INF ? __builtin_amdgcn_exp2f((x[i][k] - zt) * c) : 0.0f;
+      t.s += (double)p;
+    }
+  }
+  // one workgroup merge (a fixed tree: deterministic), one barrier
+  t = wave_allreduce(t, [c](const OutStat& u, const OutStat& v) { return out_stat_merge(u, v, c); });
+  if ((tid & 63) == 0) {
+    const int w = tid >> 6;
+    sh.m[w] = t.m;
+    sh.a[w] = t.a;
+    sh.s[w] = t.s;
+    sh.nonfin[w] = t.nonfin;
+    sh.nf[w] = t.nf;
+  }
+  __syncthreads();
+  OutStat bs{sh.m[0], sh.a[0], sh.s[0], sh.nonfin[0], sh.nf[0]};
+#pragma unroll
+  for (int w = 1; w < NT / 64; ++w)
+    bs = out_stat_merge(bs, OutStat{sh.m[w], sh.a[w], sh.s[w], sh.nonfin[w], sh.nf[w]}, c);
+  const float zm = bs.m;
+  const int32_t am = bs.a, nf = bs.nf;
+  const double se = zm < CDS_POS_INF ? bs.s : 0.0;
+  uint32_t flags = bs.nonfin ? 1u : 0u;
+  int nc = 0;
+  const int n = min(n_top, nf);
+  if (n > 0 && !bs.nonfin) {
+    auto key = [&](float v, int i, int k) -> unsigned long long {
+      return ((unsigned long long)okey(v + 0.0f) << 32) |
+             (uint32_t)~(uint32_t)(s0 + 4 * (i * NT + tid) + k);
+    };
+    // a value bound: each wave's ceil(n/W)-th largest thread maximum (W
+    // waves), the smallest of them -- at least n thread maxima, distinct
+    // tokens, reach it
+    constexpr int NW = NT / 64;
+    const float wk = wave_kth_largest(zt, (n + NW - 1) / NW);
+    if ((tid & 63) == 0) sh.wk[tid >> 6] = wk;
+    if (tid == 0) sh.cnt = 0u;
+    __syncthreads();
+    float tz = sh.wk[0];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) tz = fminf(tz, sh.wk[w]);
+#pragma unroll
+    for (int i = 0; i < KS; ++i)
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const float v = x[i][k];
+        if (!(v > CDS_NEG_INF && v >= tz)) continue;
+        const uint32_t slot = atomicAdd(&sh.cnt, 1u);
+        if (slot < (uint32_t)kCandCap) sh.cand[slot] = key(v, i, k);
+      }
+    __syncthreads();
+    const int cnt = (int)sh.cnt;
+    unsigned long long* out = o.sl_keys + ((int64_t)r * Q + q) * o.top_n_max;
+    if (cnt > kCandCap) {
+      flags |= 2u;
+    } else if (cnt <= NT) {
+      // each candidate's rank is the number of larger keys (keys are
+      // distinct): no sort, no further barrier
+      nc = min(n, cnt);
+      const unsigned long long mine = tid < cnt ? sh.cand[tid] : 0ull;
+      uint32_t rank = 0u;
+      for (int j = 0; j < cnt; ++j) rank += sh.cand[j] > mine ? 1u : 0u;
+      if (tid < cnt && rank < (uint32_t)nc) out[rank] = mine;
+    } else {
+      sort_desc<NT>(sh.cand, cnt);
+      nc = min(n, cnt);
+      for (int j = tid; j < nc; j += NT) out[j] = sh.cand[j];
+    }
+  }
+  if (tid == 0) {
+    OutSliceStat rec;
+    rec.zm = zm;
+    rec.am = nf > 0 ? (int32_t)(s0 + am) : INT_MAX;
+    rec.nf = nf;
+    rec.flags = flags;
+    rec.se = se;
+    rec.nc = nc;
+    rec.pad = 0;
+    o.sl_stat[(int64_t)r * Q + q] = rec;
+  }
+}
+
+// One workgroup per (row, slice).
 template <int NT, bool BF16, bool VEC>
 __global__ __launch_bounds__(NT) void outputs_slice_kernel(const SampleArgs a, const OutputArgs o) {
   constexpr int KS = kSliceChunks;
   __shared__ SliceShared<NT> sh;
   const int Q = o.n_slices;
   const int r = (int)blockIdx.x / Q, q = (int)blockIdx.x % Q;
-  const int tid = threadIdx.x;
   const int n_top = row_top_n(o, r);
   const bool named = o.tok_off && o.tok_off[r + 1] > o.tok_off[r];
   if (n_top == 0 && !named && !o.next_lp) return;  // nothing asked of this row
@@ -266,95 +409,8 @@ __global__ __launch_bounds__(NT) void outputs_slice_kernel(const SampleArgs a, c
   float x[KS][4];
   uint32_t nonfin = 0;
   load_chunks<NT, KS, BF16, VEC>(rv, 0, W, 0, x, nonfin);
-  // (a NaN or +inf sets nonfin, and such a row's outputs ignore every sum
-  // and list, so the sums and lists below only test against -inf)
-  float zm = CDS_NEG_INF;
-  int32_t am = INT_MAX, nf = 0;
-#pragma unroll
-  for (int i = 0; i < KS; ++i)
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const float v = x[i][k];
-      nf += finite_f(v) ? 1 : 0;
-      if (v > zm) {  // tokens in increasing order per thread: the lowest id wins ties
-        zm = v;
-        am = 4 * (i * NT + tid) + k;
-      }
-    }
-  const float zt = zm;  // the thread's own maximum
-  const bool greedy = (rp.flags & ROW_GREEDY) != 0;
-  const double Tb = (o.basis == 1 || greedy) ? 1.0 : (double)rp.temperature;
-  const float c = (float)(1.0 / Tb) * kLog2e;
-  // exp-sum against the thread's maximum, four terms in fp32 then fp64
-  double st = 0.0;
-  if (zt > CDS_NEG_INF) {
-#pragma unroll
-    for (int i = 0; i < KS; ++i) {
-      float p = 0.0f;
-#pragma unroll
-      for (int k = 0; k < 4; ++k)
-        p += x[i][k] > CDS_NEG_INF ? __builtin_amdgcn_exp2f((x[i][k] - zt) * c) : 0.0f;
-      st += (double)p;
-    }
-  }
-  block_argmax<NT>(zm, am, sh.red);
-  nf = block_sum_i32<NT>(nf, sh.red);
-  nonfin = block_or_u32<NT>(nonfin, sh.red);
-  double se = zt > CDS_NEG_INF && zm < CDS_POS_INF
-                  ? st * exp(((double)zt - (double)zm) * (double)(float)(1.0 / Tb))
-                  : 0.0;
-  se = block_sum_f64<NT>(se, sh.red);
-  uint32_t flags = nonfin ? 1u : 0u;
-  int nc = 0;
-  const int n = min(n_top, nf);
-  if (n > 0 && !nonfin) {
-    auto key = [&](float v, int i, int k) -> unsigned long long {
-      return ((unsigned long long)okey(v + 0.0f) << 32) |
-             (uint32_t)~(uint32_t)(s0 + 4 * (i * NT + tid) + k);
-    };
-    // a value bound: each wave's ceil(n/W)-th largest thread maximum (W
-    // waves), the smallest of them -- at least n thread maxima, distinct
-    // tokens, reach it
-    constexpr int NW = NT / 64;
-    const float wk = wave_kth_largest(zt, (n + NW - 1) / NW);
-    if ((tid & 63) == 0) sh.wk[tid >> 6] = wk;
-    __syncthreads();
-    float tz = sh.wk[0];
-#pragma unroll
-    for (int w = 1; w < NW; ++w) tz = fminf(tz, sh.wk[w]);
-    if (tid == 0) sh.cnt = 0u;
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < KS; ++i)
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const float v = x[i][k];
-        if (!(v > CDS_NEG_INF && v >= tz)) continue;
-        const uint32_t slot = atomicAdd(&sh.cnt, 1u);
-        if (slot < (uint32_t)kCandCap) sh.cand[slot] = key(v, i, k);
-      }
-    __syncthreads();
-    const int cnt = (int)sh.cnt;
-    if (cnt > kCandCap) {
-      flags |= 2u;
-    } else {
-      sort_desc<NT>(sh.cand, cnt);
-      nc = min(n, cnt);
-      unsigned long long* out = o.sl_keys + ((int64_t)r * Q + q) * o.top_n_max;
-      for (int j = tid; j < nc; j += NT) out[j] = sh.cand[j];
-    }
-  }
-  if (tid == 0) {
-    OutSliceStat st;
-    st.zm = zm;
-    st.am = nf > 0 ? (int32_t)(s0 + am) : INT_MAX;
-    st.nf = nf;
-    st.flags = flags;
-    st.se = se;
-    st.nc = nc;
-    st.pad = 0;
-    o.sl_stat[(int64_t)r * Q + q] = st;
-  }
+  slice_summary<NT, KS>(o, r, q, s0, x, nonfin, n_top, (rp.flags & ROW_GREEDY) != 0,
+                        rp.temperature, sh);
 }
 
 // ---- row blocks: chosen-token, named-token and top-N logprobs ----------------
@@ -390,19 +446,29 @@ __device__ __forceinline__ void row_outputs(const SampleArgs& a, const OutputArg
   if (slices) {
     // fold the slices' records: max (lowest id), finite count, flags, and the
     // exp-sums brought to the row max in fp64
+    // (every wave on its own, lane k taking records k, k + 64, ...: one
+    // round of loads, a fixed reduction tree, the same result in each wave)
     const int Q = o.n_slices;
     const OutSliceStat* S = o.sl_stat + (int64_t)r * Q;
+    const int lane = threadIdx.x & 63;
     float zm = CDS_NEG_INF;
     int32_t nf = 0;
     uint32_t fl = 0;
-    for (int q = 0; q < Q; ++q) {
-      zm = S[q].nf > 0 ? fmaxf(zm, S[q].zm) : zm;
-      nf += S[q].nf;
-      fl |= S[q].flags;
+    for (int q = lane; q < Q; q += 64) {
+      const OutSliceStat sq = S[q];
+      zm = sq.nf > 0 ? fmaxf(zm, sq.zm) : zm;
+      nf += sq.nf;
+      fl |= sq.flags;
     }
+    zm = wave_allreduce(zm, [](float u, float v) { return fmaxf(u, v); });
+    nf = wave_allreduce(nf, [](int32_t u, int32_t v) { return u + v; });
+    fl = wave_allreduce(fl, [](uint32_t u, uint32_t v) { return u | v; });
     double se = 0.0;
-    for (int q = 0; q < Q; ++q)
-      if (S[q].nf > 0) se += S[q].se * exp(((double)S[q].zm - (double)zm) / Tb);
+    for (int q = lane; q < Q; q += 64) {
+      const OutSliceStat sq = S[q];
+      if (sq.nf > 0) se += sq.se * exp(((double)sq.zm - (double)zm) / Tb);
+    }
+    se = wave_allreduce(se, [](double u, double v) { return u + v; });
     st.zm = zm;
     st.nf = nf;
     st.nonfin = fl & 1u;

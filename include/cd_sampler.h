@@ -407,8 +407,8 @@ int sampler_sample_ex(const sampler_batch *b, const void *logits, int dtype,
  *   workspace       dev, >= sampler_logprobs_workspace_bytes(B, V,
  *                   top_n_max, n_mask_rows) bytes, 16-byte aligned, or NULL.
  *                   With it the rows are first summarised by 16384-token
- *                   slices (one workgroup each: statistics and the slice's
- *                   top-N) and the per-row outputs fold the slices' records,
+ *                   slices (each slice's statistics and top-N) and the
+ *                   per-row outputs fold the slices' records,
  *                   and support sets with `cuts` are made by slices; without
  *                   it one workgroup per row streams the row (slower).  Same
  *                   results either way (logprobs within rounding).  Not kept
