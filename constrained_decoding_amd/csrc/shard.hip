@@ -40,7 +40,7 @@ namespace cds {
 
 constexpr int kShardNT = 256;
 constexpr int kShardK = 4;
-constexpr int kMergeNT = 256;
+constexpr int kMergeNT = 1024;
 
 // Sub-slice s of row r of the shard: tokens s * kShardSub .. (whole mask
 // words: kShardSub is a multiple of 32).
@@ -204,7 +204,9 @@ __global__ __launch_bounds__(NT) void shard_pass_kernel(const ShardArgs a) {
 // row state (and write the row's outputs when the phase ends it).
 template <int NT>
 __global__ __launch_bounds__(NT) void shard_merge_kernel(const ShardArgs a) {
+  static_assert(NT % 256 == 0, "whole groups of 256 histogram bins");
   __shared__ ExactShared<NT> sh;
+  __shared__ unsigned long long hgrp[NT / 256 > 1 ? NT / 256 - 1 : 1][256];
   const int r = blockIdx.x;
   const int B = a.B;
   const int tid = threadIdx.x;
@@ -296,11 +298,20 @@ __global__ __launch_bounds__(NT) void shard_merge_kernel(const ShardArgs a) {
     // radix rounds on the whole row
     const int i = a.phase - (topk_round ? SHARD_TOPK0 : SHARD_TOPP0);
     const int shift = 24 - 8 * i;
-    if (tid < 256) {
-      unsigned long long h = 0;
-#pragma unroll 8
-      for (int p = 0; p < np; ++p) h += part[(int64_t)p * B + r].hist[tid];
-      sh.hist[tid] = h;
+    // NT / 256 groups of 256 threads, group g summing records g, g + NT/256,
+    // ...: a row's records (up to 64 per group) are loaded in one round;
+    // integer sums, exact in any order
+    constexpr int NG = NT / 256;
+    const int bin = tid & 255, g = tid >> 8;
+    unsigned long long h = 0;
+#pragma unroll 16
+    for (int p = g; p < np; p += NG) h += part[(int64_t)p * B + r].hist[bin];
+    if (g > 0) hgrp[g - 1][bin] = h;
+    __syncthreads();
+    if (g == 0) {
+#pragma unroll
+      for (int k = 0; k < NG - 1; ++k) h += hgrp[k][bin];
+      sh.hist[bin] = h;
     }
     __syncthreads();
     unsigned long long above;
