@@ -84,18 +84,18 @@ __device__ __forceinline__ uint4 race_block(const RaceCtx& c, int64_t t0) {
   return philox4x32_10(make_uint4((uint32_t)(t0 >> 2), c.off_lo, c.off_hi, 0u), c.k0, c.k1);
 }
 
-// fp32 estimate of -ln(-ln U); |error| < 1e-5 (used only to prune).
-__device__ __forceinline__ float gumbel32(uint32_t x) {
-  const uint32_t j = x >> 9;
-  const uint32_t n = 2u * j + 1u;  // odd, < 2^24: exact in fp32
-  float e;
-  if (j >= (1u << 22)) {  // U > 1/2: -ln U = -log1p(-(1-U)), 1-U exact
-    const float d = (float)((1u << 24) - n) * 0x1p-24f;
-    e = -log1pf(-d);
-  } else {
-    e = -logf((float)n * 0x1p-24f);
-  }
-  return -logf(e);
+// -ln(-ln U) in fp32, branch-free: E2 = -log2 U by a degree-5 series in
+// d = 1-U when d < 1/16 (relative error < 2e-7; U near 1 would lose -log2 U to
+// cancellation in a log), by the hardware log2 otherwise; then
+// -ln(-ln U) = -ln(E2 ln 2) = -ln 2 log2(E2) - ln ln 2.  Both logs take normal
+// arguments (U >= 2^-24, E2 > 8e-8), where the hardware log2 is within 1 ulp.
+__device__ __forceinline__ float gumbel_fast(uint32_t x) {
+  const float u = fmaf((float)(x >> 9), 0x1p-23f, 0x1p-24f);  // (2 (x>>9) + 1) 2^-24, exact
+  const float d = 1.0f - u;                                   // exact
+  constexpr float L = 1.4426950408889634f;                    // 1 / ln 2
+  const float ser = d * fmaf(d, fmaf(d, fmaf(d, fmaf(d, L / 5, L / 4), L / 3), L / 2), L);
+  const float e2 = d < 0.0625f ? ser : -__builtin_amdgcn_logf(u);
+  return fmaf(-0.6931471805599453f, __builtin_amdgcn_logf(e2), 0.36651292058166435f);
 }
 
 // The exact key, in fp64 with the same operation order as the definition.
@@ -135,7 +135,9 @@ __device__ __forceinline__ void race_consider(Best& b, float z, int32_t t, uint3
                                               const RaceCtx& c) {
   const float sd = (z - c.zmax) * c.invT32;
   if (sd < -19.5f || sd + 16.7f < b.key32) return;
-  const float k32 = sd + gumbel32(x);
+  // (for a token that can win, k32 is within 1e-5 of the exact key, as in
+  // the fp32 race below: far inside the 1e-3 margin)
+  const float k32 = sd + gumbel_fast(x);
   if (k32 + 1e-3f < b.key32) return;
   const double k64 = race_key64(z, c, x);
   if (better(k64, t, b.key, b.t)) {
@@ -153,20 +155,6 @@ __device__ __forceinline__ void race_consider(Best& b, float z, int32_t t, uint3
 // 2 * kRaceEps the fp32 winner is the exact winner.  Otherwise the row is
 // re-raced in fp64 by the row's finisher.
 constexpr float kRaceEps = 2e-5f;
-
-// -ln(-ln U) in fp32, branch-free: E2 = -log2 U by a degree-5 series in
-// d = 1-U when d < 1/16 (relative error < 2e-7; U near 1 would lose -log2 U to
-// cancellation in a log), by the hardware log2 otherwise; then
-// -ln(-ln U) = -ln(E2 ln 2) = -ln 2 log2(E2) - ln ln 2.  Both logs take normal
-// arguments (U >= 2^-24, E2 > 8e-8), where the hardware log2 is within 1 ulp.
-__device__ __forceinline__ float gumbel_fast(uint32_t x) {
-  const float u = fmaf((float)(x >> 9), 0x1p-23f, 0x1p-24f);  // (2 (x>>9) + 1) 2^-24, exact
-  const float d = 1.0f - u;                                   // exact
-  constexpr float L = 1.4426950408889634f;                    // 1 / ln 2
-  const float ser = d * fmaf(d, fmaf(d, fmaf(d, fmaf(d, L / 5, L / 4), L / 3), L / 2), L);
-  const float e2 = d < 0.0625f ? ser : -__builtin_amdgcn_logf(u);
-  return fmaf(-0.6931471805599453f, __builtin_amdgcn_logf(e2), 0.36651292058166435f);
-}
 
 struct Top2 {
   float k1;    // best key
