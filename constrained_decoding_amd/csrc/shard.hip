@@ -174,23 +174,82 @@ __global__ __launch_bounds__(NT) void shard_pass_kernel(const ShardArgs a) {
   if (a.phase == SHARD_RACE) {
     // the race over {z >= zcut} with global ids: t0 + v0 is a multiple of
     // four (the host checks the shard's v0), so one Philox block serves
-    // each group
+    // each group.  Keys are ranked in fp32 first (within 1e-5 of the exact
+    // key for any token that can win): each thread keeps its best two tokens
+    // and its third-best key; only tokens within kNear of the sub-slice's
+    // best fp32 key can hold the exact best, and those get fp64 keys.  A
+    // thread with three such tokens sends the sub-slice to the fp64 race
+    // over every token.
     const RaceCtx c = make_race_ctx(rp, S.zm);
-    Best b = best_init();
     const float zf = S.zcut;
+    constexpr float kNear = 1e-4f;
+    float k1 = CDS_NEG_INF, k2 = CDS_NEG_INF, k3 = CDS_NEG_INF;
+    float z1 = CDS_NEG_INF, z2 = CDS_NEG_INF;
+    int32_t t1 = INT_MAX, t2 = INT_MAX;
+    uint32_t x1 = 0u, x2 = 0u;
     for_row4<NT, BF16, VEC, K>(rv, W, nonfin, [&](const float* x, int64_t t0) {
       bool need = false;
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        need |= (x[q] != CDS_NEG_INF && x[q] >= zf && race_hopeful(b, x[q], c));
+      for (int q = 0; q < 4; ++q) {
+        const float sd = (x[q] - c.zmax) * c.invT32;
+        need |= x[q] != CDS_NEG_INF && x[q] >= zf && sd >= -19.5f && sd + 16.7f >= k3;
+      }
       if (!need) return;
       const uint4 blk = race_block(c, v0 + t0);
       const uint32_t xs[4] = {blk.x, blk.y, blk.z, blk.w};
 #pragma unroll
-      for (int q = 0; q < 4; ++q)
-        if (x[q] != CDS_NEG_INF && x[q] >= zf)
-          race_consider(b, x[q], (int32_t)(v0 + t0 + q), xs[q], c);
+      for (int q = 0; q < 4; ++q) {
+        const float sd = (x[q] - c.zmax) * c.invT32;
+        if (!(x[q] != CDS_NEG_INF && x[q] >= zf && sd >= -19.5f)) continue;
+        const float k = sd + gumbel_fast(xs[q]);
+        const int32_t t = (int32_t)(v0 + t0 + q);
+        if (k > k1) {
+          k3 = k2;
+          k2 = k1, t2 = t1, z2 = z1, x2 = x1;
+          k1 = k, t1 = t, z1 = x[q], x1 = xs[q];
+        } else if (k > k2) {
+          k3 = k2;
+          k2 = k, t2 = t, z2 = x[q], x2 = xs[q];
+        } else {
+          k3 = fmaxf(k3, k);
+        }
+      }
     });
+    const float kb = block_max_f32<NT>(k1, sh.red);  // -inf: nothing kept here
+    const bool crowded =
+        block_or_u32<NT>(kb != CDS_NEG_INF && k3 >= kb - kNear ? 1u : 0u, sh.red) != 0u;
+    Best b = best_init();
+    if (kb == CDS_NEG_INF) {
+      // no candidate in this sub-slice
+    } else if (!crowded) {
+      if (k1 >= kb - kNear) {
+        b.key = race_key64(z1, c, x1);
+        b.t = t1;
+        b.z = z1;
+      }
+      if (k2 >= kb - kNear) {
+        const double key = race_key64(z2, c, x2);
+        if (better(key, t2, b.key, b.t)) {
+          b.key = key;
+          b.t = t2;
+          b.z = z2;
+        }
+      }
+    } else {
+      for_row4<NT, BF16, VEC, K>(rv, W, nonfin, [&](const float* x, int64_t t0) {
+        bool need = false;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          need |= (x[q] != CDS_NEG_INF && x[q] >= zf && race_hopeful(b, x[q], c));
+        if (!need) return;
+        const uint4 blk = race_block(c, v0 + t0);
+        const uint32_t xs[4] = {blk.x, blk.y, blk.z, blk.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (x[q] != CDS_NEG_INF && x[q] >= zf)
+            race_consider(b, x[q], (int32_t)(v0 + t0 + q), xs[q], c);
+      });
+    }
     block_best<NT>(b, sh.red);
     if (tid == 0) {
       P->key = b.key;
