@@ -36,7 +36,7 @@ METRIC = "sampled rows/sec and achieved HBM GB/s at B=192, V=151936 fp32 (1 GPU)
 PEAK_HBM_GBS = 8000.0
 ROW_PARAM_BYTES = 64   # packed per-row record read by the sampling kernel
 ROW_OUT_BYTES = 12     # id + logprob + status written per row
-MAX_CPU_WORKERS = 16   # the machine's CPU share for one GPU
+MAX_CPU_WORKERS = 16   # host threads for the oracle baseline: one GPU's share of the host
 
 
 def parse():
