@@ -314,6 +314,49 @@ def test_outputs_original_basis_full_size():
           tok_rows=[np.zeros(0, np.int64)] * B, mask_rows=[], cap=0, label="original basis")
 
 
+@pytest.mark.parametrize("use_ws", [True, False])
+@pytest.mark.parametrize("V", [20000, 20003])
+def test_outputs_edge_rows(V, use_ws):
+    """Rows without a distribution and other edges, through the per-row
+    outputs and the support sets from the sampling call's thresholds (by
+    slices with the workspace, row by row without): a NaN and a +inf among
+    the allowed tokens (statuses OVERFLOW / INVALID), a row with nothing
+    allowed, one allowed token, a masked greedy row, a NaN on a masked token
+    (ignored), ties under top-k, and a support cut at 3 ids; V % 4 == 0 (vector
+    loads) and ragged."""
+    rng = np.random.default_rng(716 + V)
+    B = 8
+    z = (rng.standard_normal((B, V)) * 2.0).astype(np.float32)
+    z[0, 1234] = np.nan
+    z[1, V - 7] = np.inf
+    z[6, 17] = np.nan                       # masked below
+    z[7, :] = np.round(z[7] * 2) / 2        # ties
+    allowed = [np.arange(V)] * B
+    allowed = list(allowed)
+    allowed[2] = np.zeros(0, np.int64)      # nothing allowed
+    allowed[3] = np.array([V - 1])          # one token
+    allowed[4] = rng.choice(V, 500, replace=False)
+    allowed[6] = np.setdiff1d(np.arange(V), [17])
+    masks = workloads.pack_bitmask(allowed, V)
+    rhm = np.array([0, 0, 1, 1, 1, 0, 1, 0], np.uint8)
+    T = np.array([0.8, 1.0, 0.9, 0.7, 0.0, 1.1, 0.6, 1.0], np.float32)
+    k = np.array([0, 0, 0, 0, 0, 40, 0, 5], np.int32)
+    p = np.array([0.9, 0.9, 1.0, 0.5, 1.0, 0.95, 0.8, 1.0], np.float32)
+    mp = np.array([0.0, 0.0, 0.0, 0.0, 0.0, 0.05, 0.0, 0.0], np.float32)
+    batch = workloads.Batch("outputs-edge", z, False, T, k, p, mp, workloads.seeds(rng, B),
+                            np.arange(B, dtype=np.uint64), masks=masks, row_has_mask=rhm)
+    top_n = np.array([20, 20, 20, 20, 20, 20, 20, 20], np.int32)
+    tok_rows = [np.array([0, 17, 1234, V - 1, V - 7], np.int64)] * B
+    for cap in (V, 3):
+        gpu, refs = _case(batch, basis=oracle.BASIS_SAMPLED, top_n=top_n, tok_rows=tok_rows,
+                          mask_rows=list(range(B)) + [3], cap=cap, use_ws=use_ws,
+                          label=f"edge rows V={V} cap={cap}")
+        st = gpu[3]["mask_status"]
+        assert st[0] == oracle.STATUS_INVALID and st[1] == oracle.STATUS_INVALID
+        assert st[2] == oracle.STATUS_INVALID and gpu[3]["mask_len"][2] == 0
+        assert gpu[3]["mask_len"][3] == 1 and gpu[3]["mask_ids"][3, 0] == V - 1
+
+
 def test_outputs_top_n_candidate_overflow_and_ties():
     """Rows whose candidate list (tokens at or above the N-th largest
     thread maximum) overflows LDS: all-equal values, two values, and the
