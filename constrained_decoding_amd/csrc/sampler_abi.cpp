@@ -119,11 +119,13 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
     if (h->bias_indptr[0] != 0) return SAMPLER_EINVAL;
     for (int32_t r = 0; r < B; ++r)
       if (h->bias_indptr[r + 1] < h->bias_indptr[r]) return SAMPLER_EINVAL;
-    for (int64_t i = 0; i < h->bias_indptr[B]; ++i) {
-      if (h->bias_ids[i] < 0 || h->bias_ids[i] >= V) return SAMPLER_EINVAL;
-      const float v = h->bias_vals[i];
-      if (std::isnan(v) || v == INFINITY) return SAMPLER_EINVAL;
-    }
+    const int64_t nb = h->bias_indptr[B];
+    const int32_t* ids = h->bias_ids;
+    const float* vals = h->bias_vals;
+    int bad = 0;
+    for (int64_t i = 0; i < nb; ++i)  // (branch-free: vectorised)
+      bad |= (ids[i] < 0) | (ids[i] >= V) | !(vals[i] < INFINITY);  // NaN or +inf
+    if (bad) return SAMPLER_EINVAL;
   }
 
   std::vector<RowParams> rows((size_t)B);
@@ -133,8 +135,11 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
   // kernel counts them); only longer rows are counted here, into `pen`.
   std::vector<PenEntry> pen;
   int64_t n_raw = 0;
-  std::vector<BiasEntry> bias;
-  if (h->bias_indptr) bias.reserve((size_t)h->bias_indptr[B]);
+  // bias entries, written by index into room for all of them (a push_back per
+  // entry reloads the vector's end from memory around every other store)
+  std::vector<BiasEntry> bias(h->bias_indptr ? (size_t)h->bias_indptr[B] : 0u);
+  BiasEntry* const bout = bias.data();
+  size_t n_bias_out = 0;
   uint32_t flags = SAMPLER_FLAG_ALL_GREEDY;
   bool all_nongreedy_have_k = true;
   int32_t max_k = 0;
@@ -199,12 +204,10 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
     if (h->hist_indptr && !pen_active) {
       // an unused history is still checked: any id outside [0, V) is rejected
       const int64_t lo = h->hist_indptr[r], hi = h->hist_indptr[r + 1];
-      int32_t mn = 0, mx = 0;
-      for (int64_t i = lo; i < hi; ++i) {
-        mn = std::min(mn, h->hist_ids[i]);
-        mx = std::max(mx, h->hist_ids[i]);
-      }
-      if (mn < 0 || mx >= V) return SAMPLER_EINVAL;
+      const int32_t* ids = h->hist_ids;
+      int bad = 0;
+      for (int64_t i = lo; i < hi; ++i) bad |= (ids[i] < 0) | (ids[i] >= V);
+      if (bad) return SAMPLER_EINVAL;
     }
     if (h->hist_indptr && pen_active) {
       const int64_t lo = h->hist_indptr[r], hi = h->hist_indptr[r + 1];
@@ -234,19 +237,27 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
       }
     }
     // bias: duplicates of a token keep the later entry
-    rp.bias_lo = rp.bias_hi = (int32_t)bias.size();
+    rp.bias_lo = rp.bias_hi = (int32_t)n_bias_out;
     if (h->bias_indptr) {
       const int64_t lo = h->bias_indptr[r], hi = h->bias_indptr[r + 1];
       if (hi > lo) {
         if (hi - lo <= 32) {
           // short rows (the usual case): an entry survives unless a later one
           // names the same token; survivors keep their order
-          for (int64_t i = lo; i < hi; ++i) {
-            const int32_t id = h->bias_ids[i];
-            bool later = false;
-            for (int64_t j = i + 1; j < hi; ++j) later |= h->bias_ids[j] == id;
-            if (!later) bias.push_back(BiasEntry{id, h->bias_vals[i]});
+          // (from the last entry back: a token seen before, i.e. later in the
+          // row, drops the entry; one pass over the row's few entries each)
+          const int32_t* ids = h->bias_ids + lo;
+          const float* vals = h->bias_vals + lo;
+          const int n = (int)(hi - lo);
+          uint32_t keep = 0u;
+          for (int i = n - 1; i >= 0; --i) {
+            const int32_t id = ids[i];
+            int seen = 0;
+            for (int j = i + 1; j < n; ++j) seen |= ids[j] == id;
+            keep |= seen ? 0u : (1u << i);
           }
+          for (int i = 0; i < n; ++i)
+            if ((keep >> i) & 1u) bout[n_bias_out++] = BiasEntry{ids[i], vals[i]};
         } else {
           scratch_bias.clear();
           for (int64_t i = lo; i < hi; ++i) scratch_bias.emplace_back(h->bias_ids[i], i);
@@ -254,16 +265,18 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
           for (size_t i = 0; i < scratch_bias.size(); ++i) {
             if (i + 1 < scratch_bias.size() && scratch_bias[i + 1].first == scratch_bias[i].first)
               continue;  // a later duplicate follows
-            bias.push_back(BiasEntry{scratch_bias[i].first, h->bias_vals[scratch_bias[i].second]});
+            bout[n_bias_out++] =
+                BiasEntry{scratch_bias[i].first, h->bias_vals[scratch_bias[i].second]};
           }
         }
-        rp.bias_hi = (int32_t)bias.size();
+        rp.bias_hi = (int32_t)n_bias_out;
         rp.flags |= ROW_BIAS;
         flags |= SAMPLER_FLAG_HAS_BIAS;
       }
     }
     rows[(size_t)r] = rp;
   }
+  bias.resize(n_bias_out);
   if (bias.size() > (size_t)INT32_MAX) return SAMPLER_ERANGE;
 
   // dispatch order: the rows whose last slice has the longest way to go
@@ -381,18 +394,15 @@ int pack_into(const sampler_host_params* h, unsigned char* dst, size_t cap,
            h->hist_indptr[e] == h->hist_indptr[e - 1] + (rows[(size_t)(e - 1)].pen_hi -
                                                          rows[(size_t)(e - 1)].pen_lo))
       ++e;
-    // copy and range-check in one pass (min / max, no branch per id)
+    // one block copy (the destination may be pinned staging memory, where
+    // the library copy writes fastest), then the range check on the source
     const int32_t n = rows[(size_t)(e - 1)].pen_hi - rows[(size_t)r].pen_lo;
     const int32_t* src = h->hist_ids + h->hist_indptr[r];
     int32_t* dstp = raw + rows[(size_t)r].pen_lo;
-    int32_t mn = src[0], mx = src[0];
-    for (int32_t i = 0; i < n; ++i) {
-      const int32_t v = src[i];
-      dstp[i] = v;
-      mn = std::min(mn, v);
-      mx = std::max(mx, v);
-    }
-    if (mn < 0 || mx >= V) return SAMPLER_EINVAL;
+    std::memcpy(dstp, src, sizeof(int32_t) * (size_t)n);
+    int bad = 0;
+    for (int32_t i = 0; i < n; ++i) bad |= (src[i] < 0) | (src[i] >= V);
+    if (bad) return SAMPLER_EINVAL;
     r = e;
   }
   std::memset(reinterpret_cast<unsigned char*>(raw + n_raw), 0,
