@@ -128,7 +128,9 @@ def compare(batch, gpu, ref, rows=None, *, lp_tol=1e-5, label=""):
                        f"n3={o['n3']}, flags={o['flags']}, keys={o['best_key']:.9f}/"
                        f"{o['second_key']:.9f})")
             continue
-        if not abs(float(lp[r]) - o["logprob"]) <= lp_tol:
+        # within lp_tol, or one fp32 spacing where that is coarser (|lp| >= 128)
+        tol = max(lp_tol, float(np.spacing(np.float32(abs(o["logprob"])))))
+        if not abs(float(lp[r]) - o["logprob"]) <= tol:
             bad.append(f"row {r}: logprob gpu={lp[r]!r} oracle={o['logprob']!r}")
     assert not bad, f"{label}: {len(bad)} unexplained rows:\n" + "\n".join(bad[:20])
     return len(rows), n_flag, n_flag_mm

@@ -35,12 +35,17 @@ def _need_gpu():
 
 
 def _close(a, b, tol=LP_TOL):
+    """a: the GPU's fp32 logprobs, b: the oracle's fp64 values; within tol,
+    or within one fp32 spacing of b where that spacing is coarser than tol
+    (|b| >= 128: the outputs' own precision)."""
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     same_nan = np.isnan(a) & np.isnan(b)
     same_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
     fin = np.isfinite(a) & np.isfinite(b)
-    ok = same_nan | same_inf | (fin & (np.abs(a - b) <= tol))
+    with np.errstate(invalid="ignore"):
+        ulp = np.spacing(np.abs(np.where(fin, b, 0.0)).astype(np.float32)).astype(np.float64)
+    ok = same_nan | same_inf | (fin & (np.abs(a - b) <= np.maximum(tol, ulp)))
     return bool(ok.all()), np.flatnonzero(~ok)
 
 
