@@ -869,6 +869,15 @@ __device__ __forceinline__ bool finish_row(const SampleArgs& a, int r, int nl, c
   const uint64_t* ulr = a.ulist + (int64_t)rs.list64 * 64;      // list 0
   const int64_t lcap = row_list_cap(rp.flags, rp.top_k, a.P);   // entries per list
   const double Td = (double)rp.temperature;
+  // A top-k row whose k-th token lies below the histogram window (no boundary
+  // bin inside it, and min-p cuts nothing above the window's bottom): the
+  // draw is exact (tokens below the window cannot win the race), but the kept
+  // set reaches below the window's bottom, which the sure region stops at.  A
+  // caller that asks for the kept-set threshold gets it from the exact path,
+  // which selects the k-th value over the whole row.
+  if (a.out_cut && !pl.list_mode && (rp.flags & ROW_TOPK) && !pl.topp && pl.k_rank == 0 &&
+      pl.z_sure > pl.zcut1)
+    return false;
   // One round of loads brings the records and a window of the first W
   // entries of every list (thread t reads list t % nl at positions
   // t / nl + M*k, M = NT / nl threads per list): most lists fit their window,

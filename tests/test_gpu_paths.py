@@ -14,7 +14,10 @@ C ABI, against the CPU oracle (same bar as test_gpu_parity.py):
   - logprobs at low temperature with large logits (the exp-sum must not
     carry the rounding of max / T);
   - a NaN among the few tokens a mask allows, on the vector-load path (the
-    NaN's thread sees no other allowed token).
+    NaN's thread sees no other allowed token);
+  - the kept-set threshold of top-k rows whose k-th token lies below the
+    histogram window (large k at low temperature): the threshold a caller
+    asks for is the k-th value itself, not the window's bottom.
 """
 import numpy as np
 import pytest
@@ -178,3 +181,71 @@ def test_nan_among_masked_tokens_vector_path():
     compare(b, gpu, ref, label="nan-masked")
     assert (gpu[2][:9] == oracle.STATUS_OVERFLOW).all()
     assert (gpu[2][9:] == oracle.STATUS_OK).all()
+
+
+def _kept_sets(b, zs, rows):
+    """The oracle's kept set of each row (bool [V]), "SGLang 源码完全拆解(十)",
+    section LogitsProcessor 与 LogitsProcessorOutput: the support the draw is
+    made from."""
+    out = {}
+    for r in rows:
+        _, sets = oracle.sample_row(zs[r], T=float(b.temperature[r]), top_k=int(b.top_k[r]),
+                                    top_p=float(b.top_p[r]), min_p=float(b.min_p[r]),
+                                    seed=int(b.seed[r]), offset=int(b.offset[r]),
+                                    want_sets=True, order=b.order)
+        out[r] = (sets & 4) > 0
+    return out
+
+
+@pytest.mark.parametrize("V", [151936, 5003])
+def test_cut_of_topk_below_histogram_window(V):
+    """Top-k rows too large for the slices' lists, at T = 0.05, where the
+    k-th largest value lies more than the histogram window (1120 bins of
+    width 2^-9, about 2.2 in z) below the maximum, with min-p below or
+    inside the window, with top-p, and with a mask allowing fewer tokens
+    than k; control rows at T = 0.3 and 1.  On the fast and the exact path
+    the returned threshold keeps exactly the oracle's kept set; asking for
+    it changes no id, logprob or status."""
+    import torch
+    import constrained_decoding_amd as cds
+    from gpu_harness import pack, to_device
+    rng = np.random.default_rng(57)
+    B = 16
+    z = workloads.decode_logits(rng, B, V)
+    k = np.full(B, 3000 if V > 100000 else 1000, np.int32)
+    T = np.full(B, 0.05, np.float32)
+    T[8:10] = 1.0
+    T[12:14] = 0.3
+    mp = np.zeros(B, np.float32)
+    mp[4:6] = 1e-20                    # min-p cut below the window
+    mp[6:8] = 1e-6                     # ... inside it (about 14 units of z/T)
+    p = np.ones(B, np.float32)
+    p[10:12] = 0.9
+    allowed = [np.arange(V)] * B
+    allowed = list(allowed)
+    allowed[14] = rng.choice(V, int(k[14]) // 2, replace=False)   # fewer tokens than k
+    allowed[15] = rng.choice(V, V // 2, replace=False)
+    rhm = np.zeros(B, np.uint8)
+    rhm[14:] = 1
+    b = _batch(z, T, k=k, p=p, mp=mp, masks=workloads.pack_bitmask(allowed, V), rhm=rhm)
+    print(f"[case] cut below window V={V}", flush=True)
+    ref, zs = run_oracle(b)
+    kept = _kept_sets(b, zs, range(B))
+    plain = run_gpu(b)
+    record_parity(f"cut-below-window-{V}", compare(b, plain, ref, label="cut-below-window"))
+    for algo in (cds.ALGO_FAST, cds.ALGO_EXACT):
+        x = to_device(b)
+        mask = torch.from_numpy(b.masks).cuda()
+        rh = torch.from_numpy(b.row_has_mask).cuda()
+        cut = torch.full((B,), float("nan"), dtype=torch.float32, device="cuda")
+        ids, lp, st = cds.sample(pack(b), x, bitmask=mask, row_has_mask=rh, cut=cut, algo=algo)
+        torch.cuda.synchronize()
+        ids, lp, st, c = (t.cpu().numpy() for t in (ids, lp, st, cut))
+        np.testing.assert_array_equal(ids, plain[0])
+        np.testing.assert_array_equal(st, plain[2])
+        assert np.max(np.abs(lp - plain[1])) <= 1e-5
+        for r in range(B):
+            fin = np.isfinite(zs[r])
+            got = fin & (zs[r] >= c[r])
+            assert np.array_equal(got, kept[r]), \
+                f"algo {algo} row {r}: cut {c[r]} keeps {got.sum()} tokens, the oracle {kept[r].sum()}"
